@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Throughput of the Flux MMDiT block forward under rectified-flow training on
+one MI355X, through the libflux C ABI.
+
+One step = the whole hot path over one synthetic batch at the Flux-12B block
+shapes (batch 1, 512 text + 64x64 image tokens = 4608 joint tokens, hidden
+3072, 24 x 128 heads, MLP 12288, bf16 operands with fp32 accumulation):
+rf noising of the [1, 64, 64, 64] latents -> image embedding + conditioning
+vector -> one double block -> one single block -> output head -> velocity
+MSE.  Inputs and weights (N(0, 0.02)) are resident in HBM before timing.
+
+Prints ONE JSON line with tokens/s, the per-kernel roofline of the dominant
+kernel (durations from HIP events recorded on the launch stream inside the
+timed region), the joint-attention TFLOP/s and a CPU baseline (the fp64
+oracle timed on this host on a bounded sample, scaled by algorithmic FLOPs).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MMDiT block fwd tokens/s & joint-attn TFLOP/s (512 txt+4096 img, bf16)"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_work(wl):
+    """FLOPs (and bytes) the method must do per step, per kernel class."""
+    B, L, Li, D, F, H, dh, C = wl.batch, wl.seq, wl.l_img, wl.hidden, wl.mlp_hidden, wl.heads, wl.head_dim, wl.latent_ch
+    T = B * L
+    gemm_double = 2 * T * D * (3 * D + D + F + F)         # qkv, proj, fc1, fc2 over both streams
+    gemm_single = 2 * T * D * (3 * D + F) + 2 * T * (D + F) * D
+    attn = 4 * B * H * L * L * dh                         # QK^T and PV, no mask
+    small_gemm = 2 * B * Li * C * D + 2 * B * Li * D * C  # image embedding, output linear
+    gemv_bytes = 2 * (2 * 6 * D * D + 3 * D * D + 2 * D * D + 256 * D + D * D)
+    ln_bytes = (3 * T + B * Li) * (4 * D + 2 * D)
+    return {
+        "gemm_bf16_256x256": {"flops": gemm_double + gemm_single, "launches": 6},
+        "attention": {"flops": 2 * attn, "launches": 2},
+        "gemm_bf16_128x128": {"flops": small_gemm, "launches": 2},
+        "gemv": {"bytes": gemv_bytes},
+        "ln_modulate": {"bytes": ln_bytes},
+        "total_flops": gemm_double + gemm_single + 2 * attn + small_gemm,
+        "double_block_flops": gemm_double + attn,
+    }
+
+
+def cpu_baseline(wl, w2, inp, ids, work):
+    """The fp64 oracle's double block on the full bench input (all 4608
+    tokens), timed on this host and scaled by algorithmic FLOPs to one step."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    ang = O.rope_angles(ids, wl.axes_dim, wl.theta)
+    t0 = time.perf_counter()
+    oi, ot = O.double_block(inp["x_img"], inp["x_txt"], inp["vec"], ang, w2, wl.heads, wl.eps)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(oi).all() and np.isfinite(ot).all()
+    flops_s = work["double_block_flops"] / dt
+    value = wl.tokens * flops_s / work["total_flops"]
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, one double block over the full {wl.l_txt}+{wl.l_img}-token input "
+                       f"({dt:.1f} s, {flops_s / 1e9:.1f} GFLOP/s), scaled by algorithmic FLOPs to one step"),
+            "seconds": round(dt, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for {max(args.gpus, world)}); "
+              "multi-GPU sharding is described in the design notes, not implemented", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from flow_matching_diffusion_amd import flux as FX
+    from flow_matching_diffusion_amd import synth
+    from flow_matching_diffusion_amd.model import FluxModel, device_array
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    FX.lib()
+    wl = synth.WORKLOADS["flux12b_blocks"]
+    print(f"[bench] generating weights for {wl.name}", file=sys.stderr, flush=True)
+    emb = synth.embed_weights(wl)
+    w2 = synth.double_block_weights(wl, 0)
+    w1 = synth.single_block_weights(wl, 1)
+    mi = synth.model_inputs(wl)
+    inp = synth.block_inputs(wl)
+    m = FluxModel(wl, emb, [w2], [w1])
+    dev = lambda a, bf=False: device_array(a, bf)
+    z0, z1, t, ids = dev(mi["z0"]), dev(mi["z1"]), dev(mi["t"]), dev(mi["ids"])
+    txt = dev(mi["txt"], True)
+    out: dict = {}
+
+    def step():
+        m.forward_loss(z0, z1, t, txt, None, ids, out)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    FX.flux_timing_read()                       # discard anything recorded so far
+    FX.flux_timing_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    FX.flux_timing_enable(False)
+    kernels = FX.flux_timing_read()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    loss = float(out["loss"].item())
+    assert np.isfinite(loss), "non-finite loss"
+
+    work = algorithmic_work(wl)
+    kt = {k: {"ms_per_launch": (v[0] / v[1]) if v[1] else 0.0, "launches_per_step": v[1] / args.steps,
+              "ms_per_step": v[0] / args.steps} for k, v in kernels.items() if v[1]}
+    dom = max(kt, key=lambda k: kt[k]["ms_per_step"])
+    roof = None
+    if "flops" in work.get(dom, {}):
+        per_launch = work[dom]["flops"] / work[dom]["launches"]
+        achieved = per_launch / (kt[dom]["ms_per_launch"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": per_launch, "ms_per_launch": round(kt[dom]["ms_per_launch"], 5)}
+    elif "bytes" in work.get(dom, {}):
+        achieved = work[dom]["bytes"] / (kt[dom]["ms_per_step"] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    attn = kt.get("attention")
+    attn_tflops = (work["attention"]["flops"] / work["attention"]["launches"] / (attn["ms_per_launch"] * 1e-3) / 1e12
+                   if attn else None)
+    gemm = kt.get("gemm_bf16_256x256")
+    gemm_tflops = (work["gemm_bf16_256x256"]["flops"] / (gemm["ms_per_step"] * 1e-3) / 1e12 if gemm else None)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(wl.tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "flux12b_block_pair_rf_step", "batch": wl.batch, "l_txt": wl.l_txt,
+                   "l_img": wl.l_img, "hidden": wl.hidden, "heads": wl.heads, "head_dim": wl.head_dim,
+                   "mlp_hidden": wl.mlp_hidden, "double_blocks": 1, "single_blocks": 1,
+                   "step": "rf noise + image embed + vec + double block + single block + head + velocity MSE"},
+        "roofline": roof,
+        "attention_tflops": round(attn_tflops, 2) if attn_tflops else None,
+        "attention_frac_of_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
+        "block_gemm_tflops": round(gemm_tflops, 2) if gemm_tflops else None,
+        "step_tflops": round(work["total_flops"] / (ms_step * 1e-3) / 1e12, 2),
+        "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in kt.items()},
+        "wall_s": round(wall, 3),
+        "loss": loss,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle double block)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(wl, w2, inp, synth.joint_ids(wl), work)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,706 @@
+// libflux C ABI: argument validation, workspace layout and launch sequences
+// of the Flux double block, single block, embeddings, output head and the
+// rectified-flow objective.  Every check runs on the host before anything is
+// enqueued; the library never allocates, frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/flux.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace flux;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+flux_status fail(flux_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+flux_status hip_fail(hipError_t e, const char* what) {
+  return fail(FLUX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FLUX_HIP(call, what)                  \
+  do {                                        \
+    hipError_t e_ = (call);                   \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+#define REQUIRE(cond, ...)                                                  \
+  do {                                                                      \
+    if (!(cond)) return fail(FLUX_ERR_INVALID_ARGUMENT, __VA_ARGS__);       \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int esize(int prec) { return prec == FLUX_PREC_BF16 ? 2 : 4; }
+int64_t seq_pad_of(int64_t seq) { return round_up(seq, 128); }
+
+// Bump allocator over the caller's workspace (256-byte aligned regions).
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = (size_t)round_up((int64_t)off, 256);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+flux_status check_dims(const flux_dims* d) {
+  REQUIRE(d, "dims is NULL");
+  REQUIRE(d->precision == FLUX_PREC_F32 || d->precision == FLUX_PREC_BF16, "precision %d unknown", d->precision);
+  REQUIRE(d->batch >= 1, "batch must be >= 1 (got %d)", d->batch);
+  REQUIRE(d->l_img >= 1, "l_img must be >= 1 (got %d)", d->l_img);
+  REQUIRE(d->l_txt >= 0, "l_txt must be >= 0 (got %d)", d->l_txt);
+  REQUIRE(d->heads >= 1 && d->head_dim >= 1, "heads and head_dim must be >= 1");
+  REQUIRE((int64_t)d->heads * d->head_dim == d->hidden, "hidden (%d) != heads (%d) * head_dim (%d)", d->hidden,
+          d->heads, d->head_dim);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(FLUX_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
+  if (d->hidden % 256 != 0 || d->hidden > 4096)
+    return fail(FLUX_ERR_UNSUPPORTED, "hidden %d unsupported (a multiple of 256, at most 4096)", d->hidden);
+  if (d->mlp_hidden < 64 || d->mlp_hidden % 64 != 0)
+    return fail(FLUX_ERR_UNSUPPORTED, "mlp_hidden %d unsupported (a positive multiple of 64)", d->mlp_hidden);
+  int sum = 0;
+  for (int i = 0; i < 3; ++i) {
+    REQUIRE(d->axes_dim[i] >= 0 && d->axes_dim[i] % 2 == 0, "axes_dim[%d] = %d must be even and >= 0", i,
+            d->axes_dim[i]);
+    sum += d->axes_dim[i];
+  }
+  REQUIRE(sum == d->head_dim, "axes_dim sum %d != head_dim %d", sum, d->head_dim);
+  REQUIRE(d->theta > 0.f && isfinite(d->theta), "theta must be positive");
+  REQUIRE(d->eps > 0.f && isfinite(d->eps), "eps must be positive");
+  const int64_t L = (int64_t)d->l_img + d->l_txt;
+  REQUIRE(L * d->batch < (int64_t)1 << 31 && (int64_t)d->batch * L * (3 * d->hidden + d->mlp_hidden) < (int64_t)1 << 40,
+          "problem too large");
+  return FLUX_OK;
+}
+
+// ------------------------------ workspace layouts ------------------------------
+struct BlockWs {
+  float* mod[2];
+  void* h;
+  void* big;
+  void* o;
+  void* qh;
+  void* kh;
+  void* vt;
+  size_t bytes;
+};
+
+BlockWs block_ws(const flux_dims* d, void* base) {
+  Carve c(base);
+  BlockWs w{};
+  const int64_t B = d->batch, L = (int64_t)d->l_img + d->l_txt, D = d->hidden, F = d->mlp_hidden;
+  const int64_t Lp = seq_pad_of(L), es = esize(d->precision);
+  w.mod[0] = static_cast<float*>(c.take(B * 6 * D * 4));
+  w.mod[1] = static_cast<float*>(c.take(B * 6 * D * 4));
+  w.h = c.take(B * L * D * es);
+  w.big = c.take(B * L * (3 * D > F ? 3 * D : F) * es);
+  w.o = c.take(B * L * D * es);
+  w.qh = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.kh = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.vt = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.bytes = (size_t)round_up((int64_t)c.off, 256);
+  return w;
+}
+
+struct SingleWs {
+  float* mod;
+  void* h;
+  void* qkv;
+  void* cat;
+  void* qh;
+  void* kh;
+  void* vt;
+  size_t bytes;
+};
+
+SingleWs single_ws(const flux_dims* d, void* base) {
+  Carve c(base);
+  SingleWs w{};
+  const int64_t B = d->batch, L = (int64_t)d->l_img + d->l_txt, D = d->hidden, F = d->mlp_hidden;
+  const int64_t Lp = seq_pad_of(L), es = esize(d->precision);
+  w.mod = static_cast<float*>(c.take(B * 3 * D * 4));
+  w.h = c.take(B * L * D * es);
+  w.qkv = c.take(B * L * 3 * D * es);
+  w.cat = c.take(B * L * (D + F) * es);
+  w.qh = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.kh = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.vt = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.bytes = (size_t)round_up((int64_t)c.off, 256);
+  return w;
+}
+
+flux_status check_workspace(void* ws, size_t have, size_t need) {
+  REQUIRE(ws, "workspace is NULL");
+  REQUIRE((reinterpret_cast<uintptr_t>(ws) & 255u) == 0, "workspace must be 256-byte aligned");
+  if (have < need)
+    return fail(FLUX_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", have, need);
+  return FLUX_OK;
+}
+
+RowMap rmap(int64_t bstride, int64_t ld, int64_t seg) { return RowMap{bstride, ld, (int32_t)seg}; }
+
+// ------------------------------ launch helpers ------------------------------
+hipError_t run_gemv(GemvBatch g, int batch, int dtype, hipStream_t st) {
+  for (int b0 = 0; b0 < batch; b0 += 4) {
+    GemvBatch c = g;
+    c.batch = batch - b0 < 4 ? batch - b0 : 4;
+    for (int i = 0; i < c.count; ++i) {
+      c.p[i].x += (int64_t)b0 * c.p[i].x_bstride;
+      c.p[i].y += (int64_t)b0 * c.p[i].y_bstride;
+    }
+    hipError_t e = launch_gemv(c, dtype, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+GemvProblem gemv_problem(const void* W, const void* b, int N, int K, const float* x, int64_t xbs, float* y,
+                         int64_t ybs, int silu, int acc) {
+  GemvProblem p{};
+  p.W = W; p.bias = b; p.N = N; p.K = K; p.x = x; p.x_bstride = xbs; p.y = y; p.y_bstride = ybs;
+  p.act_silu = silu; p.accumulate = acc;
+  return p;
+}
+
+GemmProblem gemm_problem(const void* A, RowMap am, const void* W, const void* bias, int M, int N, int K, int epi,
+                         void* out0, RowMap om0) {
+  GemmProblem p{};
+  p.A = A; p.amap = am; p.W = W; p.ldw = K; p.bias = bias; p.M = M; p.N = N; p.K = K; p.epi = epi;
+  p.out0 = out0; p.omap0 = om0; p.col_stride0 = 1;
+  p.omap1 = rmap(0, 1, 1);
+  return p;
+}
+
+const char* elem_ptr(const void* p, int64_t elems, int es) { return static_cast<const char*>(p) + elems * es; }
+char* elem_ptr(void* p, int64_t elems, int es) { return static_cast<char*>(p) + elems * es; }
+
+flux_status check_stream_weights(const flux_stream_weights* w, const char* name) {
+  REQUIRE(w, "%s weights are NULL", name);
+  REQUIRE(w->mod_w && w->mod_b && w->qkv_w && w->qkv_b && w->q_norm && w->k_norm && w->proj_w && w->proj_b &&
+              w->fc1_w && w->fc1_b && w->fc2_w && w->fc2_b,
+          "%s weights: a pointer is NULL", name);
+  const void* ps[] = {w->mod_w, w->mod_b, w->qkv_w, w->qkv_b, w->proj_w, w->proj_b,
+                      w->fc1_w, w->fc1_b, w->fc2_w, w->fc2_b, w->q_norm, w->k_norm};
+  for (const void* p : ps) REQUIRE(aligned16(p), "%s weights: pointers must be 16-byte aligned", name);
+  return FLUX_OK;
+}
+
+}  // namespace
+
+// ================================ public API ================================
+extern "C" {
+
+const char* flux_status_string(flux_status s) {
+  switch (s) {
+    case FLUX_OK: return "ok";
+    case FLUX_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FLUX_ERR_UNSUPPORTED: return "unsupported";
+    case FLUX_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FLUX_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* flux_last_error(void) { return g_err; }
+
+size_t flux_workspace_bytes(const flux_dims* d, int32_t op) {
+  if (check_dims(d) != FLUX_OK) return 0;
+  if (op == 0) return block_ws(d, nullptr).bytes;
+  if (op == 1) return single_ws(d, nullptr).bytes;
+  return 0;
+}
+
+// --------------------------------- double block --------------------------------
+flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, const flux_stream_weights* tw,
+                           float* img, int64_t img_bstride, float* txt, int64_t txt_bstride, const float* vec,
+                           const float* rope, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  flux_status s = check_dims(d);
+  if (s != FLUX_OK) return s;
+  const int64_t B = d->batch, Li = d->l_img, Lt = d->l_txt, L = Li + Lt, D = d->hidden, F = d->mlp_hidden;
+  const int dt = d->precision == FLUX_PREC_BF16 ? kBF16 : kF32, es = esize(d->precision);
+  if ((s = check_stream_weights(iw, "image")) != FLUX_OK) return s;
+  if (Lt > 0 && (s = check_stream_weights(tw, "text")) != FLUX_OK) return s;
+  REQUIRE(img && aligned16(img), "img must be a non-NULL 16-byte aligned pointer");
+  REQUIRE(img_bstride >= Li * D && img_bstride % 4 == 0, "img_bstride must be >= l_img*hidden and a multiple of 4");
+  if (Lt > 0) {
+    REQUIRE(txt && aligned16(txt), "txt must be a non-NULL 16-byte aligned pointer");
+    REQUIRE(txt_bstride >= Lt * D && txt_bstride % 4 == 0,
+            "txt_bstride must be >= l_txt*hidden and a multiple of 4");
+  }
+  REQUIRE(vec && aligned16(vec), "vec must be a non-NULL 16-byte aligned pointer");
+  REQUIRE(rope && aligned16(rope), "rope must be a non-NULL 16-byte aligned pointer");
+  const BlockWs need = block_ws(d, nullptr);
+  if ((s = check_workspace(workspace, workspace_bytes, need.bytes)) != FLUX_OK) return s;
+  const BlockWs w = block_ws(d, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ns = Lt > 0 ? 2 : 1;
+  const flux_stream_weights* sw[2] = {iw, tw};
+  float* xs[2] = {img, txt};
+  const int64_t xbs[2] = {img_bstride, txt_bstride};
+  const int64_t seg[2] = {Li, Lt};
+  const int64_t off[2] = {0, Li};   // first joint row of each stream
+
+  // 1. adaLN modulation of both streams: Linear(SiLU(vec)) -> 6 chunks
+  GemvBatch gv{};
+  gv.count = ns;
+  for (int i = 0; i < ns; ++i)
+    gv.p[i] = gemv_problem(sw[i]->mod_w, sw[i]->mod_b, (int)(6 * D), (int)D, vec, D, w.mod[i], 6 * D, 1, 0);
+  FLUX_HIP(run_gemv(gv, (int)B, dt, st), "modulation GEMV");
+
+  auto ln_mod = [&](int chunk_shift) -> hipError_t {
+    LnArgs a{};
+    a.count = ns;
+    a.dim = (int)D;
+    a.eps = d->eps;
+    for (int i = 0; i < ns; ++i) {
+      a.s[i].x = xs[i];
+      a.s[i].xmap = rmap(xbs[i], D, seg[i]);
+      a.s[i].out = elem_ptr(w.h, off[i] * D, es);
+      a.s[i].omap = rmap(L * D, D, seg[i]);
+      a.s[i].shift = w.mod[i] + chunk_shift * D;
+      a.s[i].scale = w.mod[i] + (chunk_shift + 1) * D;
+      a.s[i].mod_bstride = 6 * D;
+      a.s[i].rows = (int32_t)(B * seg[i]);
+    }
+    return launch_ln_mod(a, dt, st);
+  };
+  // 2. h = LN(x)(1 + scale1) + shift1
+  FLUX_HIP(ln_mod(0), "LayerNorm-modulate (attention)");
+
+  // 3. q|k|v = Linear_qkv(h) per stream, one grouped launch
+  GemmBatch g{};
+  g.count = ns;
+  for (int i = 0; i < ns; ++i)
+    g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->qkv_w, sw[i]->qkv_b,
+                          (int)(B * seg[i]), (int)(3 * D), (int)D, kEpiStore, elem_ptr(w.big, off[i] * 3 * D, es),
+                          rmap(L * 3 * D, 3 * D, seg[i]));
+  FLUX_HIP(launch_gemm(g, dt, st), "qkv GEMM");
+
+  // 4. RMSNorm(q), RMSNorm(k), RoPE, head-major layout
+  const int64_t Lp = seq_pad_of(L);
+  PrepArgs pa{};
+  pa.src_q = w.big;
+  pa.src_k = elem_ptr(w.big, D, es);
+  pa.src_v = elem_ptr(w.big, 2 * D, es);
+  pa.src_bstride = L * 3 * D;
+  pa.src_ld = 3 * D;
+  pa.batch = (int)B; pa.seq = (int)L; pa.seq_pad = (int)Lp; pa.heads = d->heads; pa.head_dim = d->head_dim;
+  pa.l_img = (int)Li;
+  pa.gq_img = iw->q_norm; pa.gk_img = iw->k_norm;
+  pa.gq_txt = Lt > 0 ? tw->q_norm : iw->q_norm;
+  pa.gk_txt = Lt > 0 ? tw->k_norm : iw->k_norm;
+  pa.rope = rope; pa.eps = d->eps;
+  pa.qh = w.qh; pa.kh = w.kh; pa.vt = w.vt;
+  FLUX_HIP(launch_prep(pa, dt, st), "q/k norm + RoPE");
+
+  // 5. joint attention over image|text rows
+  AttnArgs aa{};
+  aa.qh = w.qh; aa.kh = w.kh; aa.vt = w.vt;
+  aa.out = w.o; aa.out_bstride = L * D; aa.out_ld = D;
+  aa.batch = (int)B; aa.seq = (int)L; aa.seq_pad = (int)Lp; aa.heads = d->heads; aa.head_dim = d->head_dim;
+  aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d->head_dim));
+  FLUX_HIP(launch_attention(aa, dt, st), "joint attention");
+
+  // 6. x += gate1 * Linear_proj(O)
+  for (int i = 0; i < ns; ++i) {
+    g.p[i] = gemm_problem(elem_ptr(w.o, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->proj_w, sw[i]->proj_b,
+                          (int)(B * seg[i]), (int)D, (int)D, kEpiResid, xs[i], rmap(xbs[i], D, seg[i]));
+    g.p[i].gate = w.mod[i] + 2 * D;
+    g.p[i].gate_bstride = 6 * D;
+  }
+  FLUX_HIP(launch_gemm(g, dt, st), "output projection GEMM");
+
+  // 7. h = LN(x)(1 + scale2) + shift2
+  FLUX_HIP(ln_mod(3), "LayerNorm-modulate (MLP)");
+
+  // 8. u = GELU(fc1(h))
+  for (int i = 0; i < ns; ++i)
+    g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->fc1_w, sw[i]->fc1_b,
+                          (int)(B * seg[i]), (int)F, (int)D, kEpiGelu, elem_ptr(w.big, off[i] * F, es),
+                          rmap(L * F, F, seg[i]));
+  FLUX_HIP(launch_gemm(g, dt, st), "fc1 GEMM");
+
+  // 9. x += gate2 * fc2(u)
+  for (int i = 0; i < ns; ++i) {
+    g.p[i] = gemm_problem(elem_ptr(w.big, off[i] * F, es), rmap(L * F, F, seg[i]), sw[i]->fc2_w, sw[i]->fc2_b,
+                          (int)(B * seg[i]), (int)D, (int)F, kEpiResid, xs[i], rmap(xbs[i], D, seg[i]));
+    g.p[i].gate = w.mod[i] + 5 * D;
+    g.p[i].gate_bstride = 6 * D;
+  }
+  FLUX_HIP(launch_gemm(g, dt, st), "fc2 GEMM");
+  return FLUX_OK;
+}
+
+// --------------------------------- single block --------------------------------
+flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, float* x, int64_t x_bstride,
+                            const float* vec, const float* rope, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_err[0] = 0;
+  flux_status s = check_dims(d);
+  if (s != FLUX_OK) return s;
+  const int64_t B = d->batch, L = (int64_t)d->l_img + d->l_txt, D = d->hidden, F = d->mlp_hidden;
+  const int dt = d->precision == FLUX_PREC_BF16 ? kBF16 : kF32, es = esize(d->precision);
+  REQUIRE(sw, "single-block weights are NULL");
+  REQUIRE(sw->mod_w && sw->mod_b && sw->lin1_w && sw->lin1_b && sw->q_norm && sw->k_norm && sw->lin2_w &&
+              sw->lin2_b,
+          "single-block weights: a pointer is NULL");
+  {
+    const void* ps[] = {sw->mod_w, sw->mod_b, sw->lin1_w, sw->lin1_b, sw->q_norm, sw->k_norm, sw->lin2_w, sw->lin2_b};
+    for (const void* p : ps) REQUIRE(aligned16(p), "single-block weights: pointers must be 16-byte aligned");
+  }
+  REQUIRE(x && aligned16(x), "x must be a non-NULL 16-byte aligned pointer");
+  REQUIRE(x_bstride >= L * D && x_bstride % 4 == 0, "x_bstride must be >= L*hidden and a multiple of 4");
+  REQUIRE(vec && aligned16(vec), "vec must be a non-NULL 16-byte aligned pointer");
+  REQUIRE(rope && aligned16(rope), "rope must be a non-NULL 16-byte aligned pointer");
+  const SingleWs need = single_ws(d, nullptr);
+  if ((s = check_workspace(workspace, workspace_bytes, need.bytes)) != FLUX_OK) return s;
+  const SingleWs w = single_ws(d, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // 1. (shift, scale, gate) = Linear(SiLU(vec))
+  GemvBatch gv{};
+  gv.count = 1;
+  gv.p[0] = gemv_problem(sw->mod_w, sw->mod_b, (int)(3 * D), (int)D, vec, D, w.mod, 3 * D, 1, 0);
+  FLUX_HIP(run_gemv(gv, (int)B, dt, st), "modulation GEMV");
+
+  // 2. h = LN(x)(1 + scale) + shift
+  LnArgs la{};
+  la.count = 1;
+  la.dim = (int)D;
+  la.eps = d->eps;
+  la.s[0].x = x; la.s[0].xmap = rmap(x_bstride, D, L);
+  la.s[0].out = w.h; la.s[0].omap = rmap(L * D, D, L);
+  la.s[0].shift = w.mod; la.s[0].scale = w.mod + D; la.s[0].mod_bstride = 3 * D;
+  la.s[0].rows = (int32_t)(B * L);
+  FLUX_HIP(launch_ln_mod(la, dt, st), "LayerNorm-modulate");
+
+  // 3. q|k|v -> qkv buffer; GELU(mlp_in) -> columns D.. of the linear2 input
+  GemmBatch g{};
+  g.count = 1;
+  g.p[0] = gemm_problem(w.h, rmap(L * D, D, L), sw->lin1_w, sw->lin1_b, (int)(B * L), (int)(3 * D + F), (int)D,
+                        kEpiSplitGelu, w.qkv, rmap(L * 3 * D, 3 * D, L));
+  g.p[0].out1 = elem_ptr(w.cat, D, es);
+  g.p[0].omap1 = rmap(L * (D + F), D + F, L);
+  g.p[0].n_split = (int)(3 * D);
+  FLUX_HIP(launch_gemm(g, dt, st), "linear1 GEMM");
+
+  // 4. RMSNorm(q), RMSNorm(k), RoPE
+  const int64_t Lp = seq_pad_of(L);
+  PrepArgs pa{};
+  pa.src_q = w.qkv;
+  pa.src_k = elem_ptr(w.qkv, D, es);
+  pa.src_v = elem_ptr(w.qkv, 2 * D, es);
+  pa.src_bstride = L * 3 * D;
+  pa.src_ld = 3 * D;
+  pa.batch = (int)B; pa.seq = (int)L; pa.seq_pad = (int)Lp; pa.heads = d->heads; pa.head_dim = d->head_dim;
+  pa.l_img = (int)L;
+  pa.gq_img = pa.gq_txt = sw->q_norm;
+  pa.gk_img = pa.gk_txt = sw->k_norm;
+  pa.rope = rope; pa.eps = d->eps;
+  pa.qh = w.qh; pa.kh = w.kh; pa.vt = w.vt;
+  FLUX_HIP(launch_prep(pa, dt, st), "q/k norm + RoPE");
+
+  // 5. attention -> columns 0..D of the linear2 input
+  AttnArgs aa{};
+  aa.qh = w.qh; aa.kh = w.kh; aa.vt = w.vt;
+  aa.out = w.cat; aa.out_bstride = L * (D + F); aa.out_ld = D + F;
+  aa.batch = (int)B; aa.seq = (int)L; aa.seq_pad = (int)Lp; aa.heads = d->heads; aa.head_dim = d->head_dim;
+  aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d->head_dim));
+  FLUX_HIP(launch_attention(aa, dt, st), "attention");
+
+  // 6. x += gate * Linear2([O | GELU(m)])
+  g.p[0] = gemm_problem(w.cat, rmap(L * (D + F), D + F, L), sw->lin2_w, sw->lin2_b, (int)(B * L), (int)D,
+                        (int)(D + F), kEpiResid, x, rmap(x_bstride, D, L));
+  g.p[0].gate = w.mod + 2 * D;
+  g.p[0].gate_bstride = 3 * D;
+  FLUX_HIP(launch_gemm(g, dt, st), "linear2 GEMM");
+  return FLUX_OK;
+}
+
+// ------------------------------ rectified flow ------------------------------
+size_t flux_rf_workspace_bytes(int32_t batch, int64_t n) {
+  if (batch < 1 || n < 1) return 0;
+  return (size_t)round_up((int64_t)batch * rf_parts_per_sample(n) * 8, 256);
+}
+
+static bool overlap(const void* a, const void* b, int64_t bytes) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + bytes && y < x + bytes;
+}
+
+flux_status rf_noise_loss(const rf_args* a, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(a, "args is NULL");
+  REQUIRE(a->batch >= 1, "batch must be >= 1 (got %d)", a->batch);
+  REQUIRE(a->n_per_sample >= 1, "n_per_sample must be >= 1");
+  REQUIRE((int64_t)a->batch * a->n_per_sample < ((int64_t)1 << 40), "problem too large");
+  REQUIRE(a->z0 && a->z1 && a->t, "z0, z1 and t are required");
+  const float* ptrs[] = {a->z0, a->z1, a->t, a->z_t, a->v_target, a->v_pred, a->loss, a->loss_per_sample};
+  for (const float* p : ptrs) REQUIRE(!p || aligned16(p), "tensor pointers must be 16-byte aligned");
+  const int64_t bytes = (int64_t)a->batch * a->n_per_sample * 4;
+  const float* outs[] = {a->z_t, a->v_target};
+  for (const float* o : outs) {
+    if (!o) continue;
+    REQUIRE(!overlap(o, a->z0, bytes) && !overlap(o, a->z1, bytes), "z_t / v_target must not alias z0 or z1");
+  }
+  if (a->z_t && a->v_target) REQUIRE(!overlap(a->z_t, a->v_target, bytes), "z_t and v_target must not alias");
+  const bool want_loss = a->loss || a->loss_per_sample;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (want_loss) {
+    REQUIRE(a->v_pred, "a loss output needs v_pred");
+    flux_status s = check_workspace(a->workspace, a->workspace_bytes,
+                                    flux_rf_workspace_bytes(a->batch, a->n_per_sample));
+    if (s != FLUX_OK) return s;
+  }
+  if (a->z_t || a->v_target)
+    FLUX_HIP(launch_rf_noise(a->batch, a->n_per_sample, a->z0, a->z1, a->t, a->z_t, a->v_target, st), "rf noise");
+  if (want_loss)
+    FLUX_HIP(launch_rf_loss(a->batch, a->n_per_sample, a->z0, a->z1, a->v_pred, a->loss, a->loss_per_sample,
+                            static_cast<double*>(a->workspace), rf_parts_per_sample(a->n_per_sample), st),
+             "rf loss");
+  return FLUX_OK;
+}
+
+// -------------------------------- RoPE table --------------------------------
+flux_status flux_rope_table(const float* ids, int32_t batch, int32_t seq, const int32_t axes_dim[3], float theta,
+                            float* table, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(ids && table && axes_dim, "ids, table and axes_dim are required");
+  REQUIRE(aligned16(table), "table must be 16-byte aligned");
+  REQUIRE(batch >= 1 && seq >= 1, "batch and seq must be >= 1");
+  for (int i = 0; i < 3; ++i) REQUIRE(axes_dim[i] >= 0 && axes_dim[i] % 2 == 0, "axes_dim must be even and >= 0");
+  REQUIRE(axes_dim[0] + axes_dim[1] + axes_dim[2] >= 2, "axes_dim sum must be >= 2");
+  REQUIRE(theta > 0.f && isfinite(theta), "theta must be positive");
+  FLUX_HIP(launch_rope_table(ids, batch, seq, axes_dim, theta, table, static_cast<hipStream_t>(stream)),
+           "RoPE table");
+  return FLUX_OK;
+}
+
+// -------------------------------- embeddings --------------------------------
+size_t flux_embed_workspace_bytes(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
+                                  int32_t hidden) {
+  if (batch < 1 || channels < 1 || height < 1 || width < 1 || hidden < 1) return 0;
+  Carve c(nullptr);
+  c.take((size_t)batch * height * width * channels * esize(precision));   // patchified latents
+  c.take((size_t)batch * 256 * 4);                                         // sinusoid, time_dim <= 256
+  c.take((size_t)batch * hidden * 4 * 2);                                  // two hidden activations
+  return (size_t)round_up((int64_t)c.off, 256);
+}
+
+flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
+                           int32_t l_txt, int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
+                           const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
+                           const float* y, float* x_img, int64_t img_bstride, float* x_txt, int64_t txt_bstride,
+                           float* vec, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(precision == FLUX_PREC_F32 || precision == FLUX_PREC_BF16, "precision %d unknown", precision);
+  REQUIRE(batch >= 1 && channels >= 1 && height >= 1 && width >= 1 && hidden >= 1, "sizes must be >= 1");
+  REQUIRE(w && w->img_in_w && w->img_in_b && w->time_in1_w && w->time_in1_b && w->time_in2_w && w->time_in2_b,
+          "image and time embedder weights are required");
+  REQUIRE(z_t && t && x_img && vec, "z_t, t, x_img and vec are required");
+  REQUIRE(time_dim >= 2 && time_dim % 2 == 0 && time_dim <= 256, "time_dim must be even, in [2, 256]");
+  const bool bf = precision == FLUX_PREC_BF16;
+  const int dt = bf ? kBF16 : kF32, es = esize(precision);
+  const int kq = bf ? 8 : 4;
+  if (bf && channels % 64 != 0)
+    return fail(FLUX_ERR_UNSUPPORTED, "bf16 image input needs channels %% 64 == 0 (got %d)", channels);
+  REQUIRE(hidden % 4 == 0 && hidden % kq == 0 && time_dim % kq == 0, "hidden and time_dim must be multiples of %d",
+          kq);
+  REQUIRE(hidden <= 4096, "hidden must be <= 4096");
+  const int64_t HW = (int64_t)height * width;
+  REQUIRE(img_bstride >= HW * hidden && img_bstride % 4 == 0, "img_bstride too small or not a multiple of 4");
+  REQUIRE(aligned16(x_img) && aligned16(vec) && aligned16(z_t), "pointers must be 16-byte aligned");
+  const bool has_txt = w->txt_in_w != nullptr;
+  if (has_txt) {
+    REQUIRE(w->txt_in_b && txt && x_txt && l_txt >= 1 && ctx_dim >= 1, "txt_in needs txt, x_txt, l_txt and ctx_dim");
+    if (bf && ctx_dim % 64 != 0) return fail(FLUX_ERR_UNSUPPORTED, "bf16 txt_in needs ctx_dim %% 64 == 0");
+    REQUIRE(txt_bstride >= (int64_t)l_txt * hidden && txt_bstride % 4 == 0, "txt_bstride too small");
+    REQUIRE(aligned16(x_txt) && aligned16(txt), "pointers must be 16-byte aligned");
+  }
+  const bool has_y = w->vector_in1_w != nullptr;
+  if (has_y) {
+    REQUIRE(w->vector_in1_b && w->vector_in2_w && w->vector_in2_b && y && y_dim >= 1 && y_dim % kq == 0,
+            "vector_in needs both layers, y and y_dim (a multiple of %d)", kq);
+  }
+  flux_status s = check_workspace(workspace, workspace_bytes,
+                                  flux_embed_workspace_bytes(precision, batch, channels, height, width, hidden));
+  if (s != FLUX_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carve c(workspace);
+  void* tok = c.take((size_t)batch * HW * channels * es);
+  float* emb = static_cast<float*>(c.take((size_t)batch * 256 * 4));
+  float* a1 = static_cast<float*>(c.take((size_t)batch * hidden * 4));
+  float* a2 = static_cast<float*>(c.take((size_t)batch * hidden * 4));
+
+  // image tokens and (optionally) text tokens: one grouped GEMM into fp32 residual streams
+  FLUX_HIP(launch_patchify(z_t, batch, channels, (int)HW, tok, dt, st), "patchify");
+  GemmBatch g{};
+  g.count = has_txt ? 2 : 1;
+  g.p[0] = gemm_problem(tok, rmap(HW * channels, channels, HW), w->img_in_w, w->img_in_b, (int)(batch * HW), hidden,
+                        channels, kEpiStoreF32, x_img, rmap(img_bstride, hidden, HW));
+  if (has_txt)
+    g.p[1] = gemm_problem(txt, rmap((int64_t)l_txt * ctx_dim, ctx_dim, l_txt), w->txt_in_w, w->txt_in_b,
+                          batch * l_txt, hidden, ctx_dim, kEpiStoreF32, x_txt, rmap(txt_bstride, hidden, l_txt));
+  FLUX_HIP(launch_gemm(g, dt, st), "input projection GEMM");
+
+  // conditioning vector
+  FLUX_HIP(launch_timestep_embed(t, batch, time_dim, 1000.f, 10000.f, emb, st), "timestep sinusoid");
+  GemvBatch gv{};
+  gv.count = has_y ? 2 : 1;
+  gv.p[0] = gemv_problem(w->time_in1_w, w->time_in1_b, hidden, time_dim, emb, time_dim, a1, hidden, 0, 0);
+  if (has_y) gv.p[1] = gemv_problem(w->vector_in1_w, w->vector_in1_b, hidden, y_dim, y, y_dim, a2, hidden, 0, 0);
+  FLUX_HIP(run_gemv(gv, batch, dt, st), "embedder layer 1");
+  GemvBatch g2{};
+  g2.count = 1;
+  g2.p[0] = gemv_problem(w->time_in2_w, w->time_in2_b, hidden, hidden, a1, hidden, vec, hidden, 1, 0);
+  FLUX_HIP(run_gemv(g2, batch, dt, st), "time embedder layer 2");
+  if (has_y) {
+    g2.p[0] = gemv_problem(w->vector_in2_w, w->vector_in2_b, hidden, hidden, a2, hidden, vec, hidden, 1, 1);
+    FLUX_HIP(run_gemv(g2, batch, dt, st), "vector embedder layer 2");
+  }
+  return FLUX_OK;
+}
+
+// -------------------------------- output head --------------------------------
+size_t flux_final_workspace_bytes(int32_t precision, int32_t batch, int32_t height, int32_t width, int32_t hidden) {
+  if (batch < 1 || height < 1 || width < 1 || hidden < 1) return 0;
+  Carve c(nullptr);
+  c.take((size_t)batch * 2 * hidden * 4);
+  c.take((size_t)batch * height * width * hidden * esize(precision));
+  return (size_t)round_up((int64_t)c.off, 256);
+}
+
+flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
+                           int32_t hidden, float eps, const void* mod_w, const void* mod_b, const void* out_w,
+                           const void* out_b, const float* x_img, int64_t bstride, const float* vec, float* v_pred,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(precision == FLUX_PREC_F32 || precision == FLUX_PREC_BF16, "precision %d unknown", precision);
+  REQUIRE(batch >= 1 && channels >= 1 && height >= 1 && width >= 1, "sizes must be >= 1");
+  if (hidden % 256 != 0 || hidden > 4096)
+    return fail(FLUX_ERR_UNSUPPORTED, "hidden %d unsupported (a multiple of 256, at most 4096)", hidden);
+  if (channels % 4 != 0) return fail(FLUX_ERR_UNSUPPORTED, "channels must be a multiple of 4");
+  REQUIRE(eps > 0.f, "eps must be positive");
+  REQUIRE(mod_w && mod_b && out_w && out_b && x_img && vec && v_pred, "a required pointer is NULL");
+  REQUIRE(aligned16(x_img) && aligned16(vec) && aligned16(v_pred), "pointers must be 16-byte aligned");
+  const int64_t HW = (int64_t)height * width;
+  REQUIRE(bstride >= HW * hidden && bstride % 4 == 0, "bstride too small or not a multiple of 4");
+  flux_status s =
+      check_workspace(workspace, workspace_bytes, flux_final_workspace_bytes(precision, batch, height, width, hidden));
+  if (s != FLUX_OK) return s;
+  const int dt = precision == FLUX_PREC_BF16 ? kBF16 : kF32;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carve c(workspace);
+  float* mod = static_cast<float*>(c.take((size_t)batch * 2 * hidden * 4));
+  void* h = c.take((size_t)batch * HW * hidden * esize(precision));
+  GemvBatch gv{};
+  gv.count = 1;
+  gv.p[0] = gemv_problem(mod_w, mod_b, 2 * hidden, hidden, vec, hidden, mod, 2 * hidden, 1, 0);
+  FLUX_HIP(run_gemv(gv, batch, dt, st), "final modulation GEMV");
+  LnArgs la{};
+  la.count = 1;
+  la.dim = hidden;
+  la.eps = eps;
+  la.s[0].x = x_img; la.s[0].xmap = rmap(bstride, hidden, HW);
+  la.s[0].out = h; la.s[0].omap = rmap(HW * hidden, hidden, HW);
+  la.s[0].shift = mod; la.s[0].scale = mod + hidden; la.s[0].mod_bstride = 2 * hidden;
+  la.s[0].rows = (int32_t)(batch * HW);
+  FLUX_HIP(launch_ln_mod(la, dt, st), "final LayerNorm-modulate");
+  // tok[b, l, c] lands at v_pred[b, c, l]: row l -> +l, column c -> +c*HW
+  GemmBatch g{};
+  g.count = 1;
+  g.p[0] = gemm_problem(h, rmap(HW * hidden, hidden, HW), out_w, out_b, (int)(batch * HW), channels, hidden,
+                        kEpiStoreF32, v_pred, rmap(channels * HW, 1, HW));
+  g.p[0].col_stride0 = HW;
+  FLUX_HIP(launch_gemm(g, dt, st), "output GEMM");
+  return FLUX_OK;
+}
+
+// ------------------------------ standalone ops ------------------------------
+flux_status flux_linear_fwd(int32_t precision, int32_t m, int32_t n, int32_t k, const void* x, int64_t lda,
+                            const void* w, const void* b, float* y, int64_t ldy, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(precision == FLUX_PREC_F32 || precision == FLUX_PREC_BF16, "precision %d unknown", precision);
+  REQUIRE(m >= 1 && n >= 1 && k >= 1, "m, n, k must be >= 1");
+  REQUIRE(x && w && y, "x, w and y are required");
+  REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && (!b || aligned16(b)), "pointers must be 16-byte aligned");
+  REQUIRE(lda >= k && ldy >= n, "lda >= k and ldy >= n required");
+  if (precision == FLUX_PREC_BF16) {
+    if (k % 64 != 0) return fail(FLUX_ERR_UNSUPPORTED, "bf16 linear needs k %% 64 == 0 (got %d)", k);
+    REQUIRE(lda % 8 == 0, "bf16 lda must be a multiple of 8");
+  }
+  if (n % 4 != 0) return fail(FLUX_ERR_UNSUPPORTED, "n must be a multiple of 4 (got %d)", n);
+  REQUIRE(ldy % 4 == 0, "ldy must be a multiple of 4");
+  GemmBatch g{};
+  g.count = 1;
+  g.p[0] = gemm_problem(x, rmap((int64_t)m * lda, lda, m), w, b, m, n, k, kEpiStoreF32, y, rmap((int64_t)m * ldy, ldy, m));
+  FLUX_HIP(launch_gemm(g, precision == FLUX_PREC_BF16 ? kBF16 : kF32, static_cast<hipStream_t>(stream)),
+           "linear GEMM");
+  return FLUX_OK;
+}
+
+size_t flux_attention_workspace_bytes(int32_t precision, int32_t batch, int32_t seq, int32_t heads,
+                                      int32_t head_dim) {
+  if (batch < 1 || seq < 1 || heads < 1 || head_dim < 1) return 0;
+  Carve c(nullptr);
+  const int64_t per = (int64_t)batch * heads * seq_pad_of(seq) * head_dim * esize(precision);
+  c.take(per);
+  c.take(per);
+  c.take(per);
+  return (size_t)round_up((int64_t)c.off, 256);
+}
+
+flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, int32_t heads, int32_t head_dim,
+                               const void* q, const void* k, const void* v, int64_t ld_in, void* o, int64_t ld_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(precision == FLUX_PREC_F32 || precision == FLUX_PREC_BF16, "precision %d unknown", precision);
+  REQUIRE(batch >= 1 && seq >= 1 && heads >= 1, "batch, seq and heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FLUX_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  REQUIRE(q && k && v && o, "q, k, v and o are required");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o), "pointers must be 16-byte aligned");
+  const int64_t D = (int64_t)heads * head_dim;
+  REQUIRE(ld_in >= D && ld_out >= D && ld_in % 8 == 0 && ld_out % 8 == 0,
+          "row strides must be >= heads*head_dim and multiples of 8");
+  flux_status s = check_workspace(workspace, workspace_bytes,
+                                  flux_attention_workspace_bytes(precision, batch, seq, heads, head_dim));
+  if (s != FLUX_OK) return s;
+  const int dt = precision == FLUX_PREC_BF16 ? kBF16 : kF32;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t Lp = seq_pad_of(seq), es = esize(precision);
+  Carve c(workspace);
+  const int64_t per = (int64_t)batch * heads * Lp * head_dim * es;
+  PrepArgs pa{};
+  pa.src_q = q; pa.src_k = k; pa.src_v = v;
+  pa.src_bstride = (int64_t)seq * ld_in; pa.src_ld = ld_in;
+  pa.batch = batch; pa.seq = seq; pa.seq_pad = (int)Lp; pa.heads = heads; pa.head_dim = head_dim; pa.l_img = seq;
+  pa.eps = 1e-6f;
+  pa.qh = c.take(per); pa.kh = c.take(per); pa.vt = c.take(per);
+  FLUX_HIP(launch_prep(pa, dt, st), "attention layout");
+  AttnArgs aa{};
+  aa.qh = pa.qh; aa.kh = pa.kh; aa.vt = pa.vt;
+  aa.out = o; aa.out_bstride = (int64_t)seq * ld_out; aa.out_ld = ld_out;
+  aa.batch = batch; aa.seq = seq; aa.seq_pad = (int)Lp; aa.heads = heads; aa.head_dim = head_dim;
+  aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  FLUX_HIP(launch_attention(aa, dt, st), "attention");
+  return FLUX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,244 @@
+// Joint softmax attention O = softmax(Q K^T / sqrt(Dh)) V, no mask, over the
+// concatenated image|text sequence ("Flux architecture deep dive",
+// Implementation details / Attention implementation and the joint attention
+// trick; Mathematical formulation).  Exact attention evaluated flash-style:
+// K / V tiles streamed through LDS, running max and sum in registers, no
+// L x L buffer.
+//
+// bf16 kernel (CDNA4, wave64, v_mfma_f32_32x32x16_bf16): a block owns 128
+// queries of one (batch, head); each of its 4 waves owns 32 queries.  Per
+// 64-key tile a wave computes S^T = K Q^T (keys on MFMA rows, its queries on
+// MFMA columns), so lane l holds 32 scores of query l % 32 and the row max /
+// sum need a single exchange with lane l ^ 32.  The probabilities then feed
+// O^T = V^T P^T directly from registers: K rows are stored in LDS in a
+// permuted order (bits 2 and 3 of the row index swapped within each 32-row
+// half) so that the accumulator registers of each lane hold 8 consecutive
+// keys per 16-key MFMA step, matching 8 consecutive keys of a V^T row.
+// Inputs come from launch_prep: Q, K head-major [B, H, Lp, Dh] and V
+// transposed [B, H, Dh, Lp], Lp = seq rounded up to 128, zero padded.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "timing.h"
+
+namespace flux {
+
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int DH>
+__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
+  constexpr int KT = 64;          // keys per tile
+  constexpr int QW = 32;          // queries per wave
+  constexpr int QB = 4 * QW;      // queries per block
+  constexpr int DCH = DH / 8;     // 16-byte chunks per K row
+  constexpr int KS = DH / 16;     // MFMA k-steps of S^T
+  constexpr int DT = DH / 32;     // 32-row tiles of O^T
+  constexpr int LK = KT * DCH / 256;
+  constexpr int LV = DH * 8 / 256;
+  // LDS rows padded by 16 bytes: a 16-byte read by 16 consecutive rows then
+  // hits 16 distinct 4-bank groups (conflict-free for 32 or 64 banks), and
+  // every read address is a per-lane base plus an immediate offset
+  constexpr int KLD = DH + 8;     // K tile row stride (elements)
+  constexpr int VLD = KT + 8;     // V^T tile row stride (elements)
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KLD];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][DH * VLD];
+
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int64_t bh = (int64_t)b * a.heads + h;
+  const bf16_t* Qh = reinterpret_cast<const bf16_t*>(a.qh) + bh * a.seq_pad * DH;
+  const bf16_t* Kh = reinterpret_cast<const bf16_t*>(a.kh) + bh * a.seq_pad * DH;
+  const bf16_t* Vt = reinterpret_cast<const bf16_t*>(a.vt) + bh * DH * a.seq_pad;
+
+  const int q = qb * QB + wave * QW + l32;
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(Qh + (int64_t)q * DH + ks * 16 + half * 8);
+
+  u32x4_t rk[LK], rv[LV];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int g = tid + 256 * i, kr = g / DCH, c = g % DCH;
+      rk[i] = *reinterpret_cast<const u32x4_t*>(Kh + (int64_t)(k0 + kr) * DH + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int g = tid + 256 * i, d = g >> 3, c = g & 7;
+      rv[i] = *reinterpret_cast<const u32x4_t*>(Vt + (int64_t)d * a.seq_pad + k0 + c * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int g = tid + 256 * i, kr = g / DCH, c = g % DCH;
+      const int rho = (kr & 32) | swap23(kr & 31);
+      *reinterpret_cast<u32x4_t*>(&Ks[buf][rho * KLD + c * 8]) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int g = tid + 256 * i, d = g >> 3, c = g & 7;
+      *reinterpret_cast<u32x4_t*>(&Vs[buf][d * VLD + c * 8]) = rv[i];
+    }
+  };
+
+  f32x16_t o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2;
+
+  const int ntiles = (a.seq + KT - 1) / KT;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < ntiles) gload((t + 1) * KT);
+    // S^T for 64 keys x 32 queries: two 32 x 32 tiles
+    f32x16_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
+      const int rho = u * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[cur][rho * KLD + (ks * 2 + half) * 8]);
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[u], 0, 0, 0);
+      }
+    }
+    // s[u][e] is the score of key t*64 + (2u + e/8)*16 + half*8 + e%8 for query l32
+    if ((t + 1) * KT > a.seq) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = t * KT + (2 * u + (e >> 3)) * 16 + half * 8 + (e & 7);
+          if (key >= a.seq) s[u][e] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * sc);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.f;
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2], sc, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2 + 1], sc, -m_new));
+          psum += p0 + p1;
+          w[e2] = pack_bf16x2(p0, p1);
+        }
+        u32x4_t wv = {w[0], w[1], w[2], w[3]};
+        pf[2 * u + hh] = __builtin_bit_cast(bf16x8_t, wv);
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+    // O^T += V^T P^T over the 4 16-key steps of the tile
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      const int d = i * 32 + l32;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vs[cur][d * VLD + (kb * 2 + half) * 8]);
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb], o[i], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntiles) lstore(cur ^ 1);
+    __syncthreads();
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (q < a.seq) {
+    bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + (int64_t)b * a.out_bstride + (int64_t)q * a.out_ld + h * DH;
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = i * 32 + 8 * g + 4 * half;
+        uint2 v;
+        v.x = pack_bf16x2(o[i][4 * g] * inv, o[i][4 * g + 1] * inv);
+        v.y = pack_bf16x2(o[i][4 * g + 2] * inv, o[i][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(out + d0) = v;
+      }
+  }
+}
+
+// fp32 kernel for the fp32 workloads: one thread per query, online softmax,
+// keys and values read as broadcasts (every thread of the block walks the
+// same key).
+template <int DH>
+__global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int q = blockIdx.x * 64 + threadIdx.x;
+  const int64_t bh = (int64_t)b * a.heads + h;
+  const float* Qh = reinterpret_cast<const float*>(a.qh) + bh * a.seq_pad * DH;
+  const float* Kh = reinterpret_cast<const float*>(a.kh) + bh * a.seq_pad * DH;
+  const float* Vt = reinterpret_cast<const float*>(a.vt) + bh * DH * a.seq_pad;
+  float qv[DH], o[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    qv[d] = Qh[(int64_t)q * DH + d];
+    o[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < a.seq; ++j) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) s += qv[d] * Kh[(int64_t)j * DH + d];
+    s *= a.scale_log2;
+    const float m_new = fmaxf(m, s);
+    const float alpha = exp2f(m - m_new);
+    const float p = exp2f(s - m_new);
+    l = l * alpha + p;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) o[d] = o[d] * alpha + p * Vt[(int64_t)d * a.seq_pad + j];
+    m = m_new;
+  }
+  if (q < a.seq) {
+    float* out = reinterpret_cast<float*>(a.out) + (int64_t)b * a.out_bstride + (int64_t)q * a.out_ld + h * DH;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) out[d] = o[d] * inv;
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream) {
+  TimingScope ts(kKcAttn, stream);
+  if (dtype == kBF16) {
+    const dim3 grid(a.seq_pad / 128, a.heads, a.batch);
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
+  } else {
+    const dim3 grid(a.seq_pad / 64, a.heads, a.batch);
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace flux

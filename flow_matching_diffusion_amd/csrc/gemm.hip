@@ -1,0 +1,393 @@
+// GEMM C = A W^T (+ bias, fused epilogues) for the Flux block linears
+// ("Flux architecture deep dive", MMDiT layer / Flux single block: the qkv,
+// output-projection and MLP linears; "Flux model API reference", add_qkv_bias).
+//
+// bf16 path: 4 waves (2 x 2), block tile BM x BN x 64, v_mfma_f32_32x32x16_bf16,
+// A and W both K-contiguous (torch Linear layout), tiles staged through LDS in
+// two buffers with rows padded against bank conflicts, fp32 accumulation.  Several
+// problems (the image and text streams of a double block) share one grid; the
+// block -> tile map keeps each XCD on a contiguous tile range and walks tiles
+// in groups of 8 tile rows so A and W panels are reused from L2.
+// fp32 path (fp32 workloads only): LDS-tiled FMA kernel with the same epilogues.
+#include "common.h"
+#include "kernels.h"
+#include "timing.h"
+
+namespace flux {
+
+// ---------------------------------------------------------------------------
+// epilogue
+// ---------------------------------------------------------------------------
+struct EpiRow {
+  char* o0;
+  char* o1;
+  const float* gate;
+  bool valid;
+};
+
+__device__ __forceinline__ EpiRow epi_row(const GemmProblem& p, int row, int elem_bytes) {
+  EpiRow r;
+  r.valid = row < p.M;
+  const int rr = r.valid ? row : 0;
+  const int64_t b = rr / p.omap0.seg, l = rr % p.omap0.seg;
+  const int ob = (p.epi == kEpiResid || p.epi == kEpiStoreF32) ? 4 : elem_bytes;
+  r.o0 = reinterpret_cast<char*>(p.out0) + (b * p.omap0.bstride + l * p.omap0.ld) * ob;
+  r.gate = p.gate ? p.gate + b * p.gate_bstride : nullptr;
+  r.o1 = nullptr;
+  if (p.epi == kEpiSplitGelu) {
+    const int64_t b1 = rr / p.omap1.seg, l1 = rr % p.omap1.seg;
+    r.o1 = reinterpret_cast<char*>(p.out1) + (b1 * p.omap1.bstride + l1 * p.omap1.ld) * elem_bytes;
+  }
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_apply(const GemmProblem& p, const EpiRow& r, int col, float v) {
+  switch (p.epi) {
+    case kEpiStore:
+      reinterpret_cast<T*>(r.o0)[col] = from_f32<T>(v);
+      break;
+    case kEpiGelu:
+      reinterpret_cast<T*>(r.o0)[col] = from_f32<T>(gelu_f(v));
+      break;
+    case kEpiResid: {
+      float* x = reinterpret_cast<float*>(r.o0) + col;
+      *x = *x + r.gate[col] * v;
+      break;
+    }
+    case kEpiStoreF32:
+      reinterpret_cast<float*>(r.o0)[(int64_t)col * p.col_stride0] = v;
+      break;
+    case kEpiSplitGelu:
+      if (col < p.n_split)
+        reinterpret_cast<T*>(r.o0)[col] = from_f32<T>(v);
+      else
+        reinterpret_cast<T*>(r.o1)[col - p.n_split] = from_f32<T>(gelu_f(v));
+      break;
+    default:
+      break;
+  }
+}
+
+// Four consecutive columns col..col+3 of one row (bf16 operands).  N is a
+// multiple of 4, so the four columns are all in range together; for the
+// split epilogue n_split is a multiple of 4, so they fall on one side.
+__device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int col, float4 v) {
+  if (p.bias) {
+    const uint2 bb = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.bias) + col);
+    v.x += __uint_as_float(bb.x << 16);
+    v.y += __uint_as_float(bb.x & 0xffff0000u);
+    v.z += __uint_as_float(bb.y << 16);
+    v.w += __uint_as_float(bb.y & 0xffff0000u);
+  }
+  const int64_t b = row / p.omap0.seg, l = row % p.omap0.seg;
+  const int64_t off0 = b * p.omap0.bstride + l * p.omap0.ld;
+  switch (p.epi) {
+    case kEpiStore:
+    case kEpiGelu: {
+      if (p.epi == kEpiGelu) {
+        v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
+      }
+      uint2 o;
+      o.x = pack_bf16x2(v.x, v.y);
+      o.y = pack_bf16x2(v.z, v.w);
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = o;
+      break;
+    }
+    case kEpiResid: {
+      float4* x = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out0) + off0 + col);
+      const float4 g = *reinterpret_cast<const float4*>(p.gate + b * p.gate_bstride + col);
+      float4 r = *x;
+      r.x += g.x * v.x; r.y += g.y * v.y; r.z += g.z * v.z; r.w += g.w * v.w;
+      *x = r;
+      break;
+    }
+    case kEpiStoreF32: {
+      float* o = reinterpret_cast<float*>(p.out0) + off0;
+      if (p.col_stride0 == 1) {
+        *reinterpret_cast<float4*>(o + col) = v;
+      } else {
+        o[(int64_t)col * p.col_stride0] = v.x;
+        o[(int64_t)(col + 1) * p.col_stride0] = v.y;
+        o[(int64_t)(col + 2) * p.col_stride0] = v.z;
+        o[(int64_t)(col + 3) * p.col_stride0] = v.w;
+      }
+      break;
+    }
+    case kEpiSplitGelu: {
+      uint2 o;
+      if (col < p.n_split) {
+        o.x = pack_bf16x2(v.x, v.y);
+        o.y = pack_bf16x2(v.z, v.w);
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = o;
+      } else {
+        const int64_t b1 = row / p.omap1.seg, l1 = row % p.omap1.seg;
+        o.x = pack_bf16x2(gelu_f(v.x), gelu_f(v.y));
+        o.y = pack_bf16x2(gelu_f(v.z), gelu_f(v.w));
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out1) + b1 * p.omap1.bstride + l1 * p.omap1.ld +
+                                  (col - p.n_split)) = o;
+      }
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tile scheduling shared by both paths
+// ---------------------------------------------------------------------------
+struct TileCoord {
+  int prob, tm, tn;
+};
+
+__device__ __forceinline__ TileCoord decode_tile(const GemmBatch& bt, int BM, int BN) {
+  // Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8);
+  // give XCD x the contiguous tile range [x*q + min(x, r), ...).
+  const int total = bt.total_tiles;
+  const int bid = blockIdx.x;
+  const int q = total / 8, rem = total % 8;
+  const int x = bid % 8, i = bid / 8;
+  const int id = x * q + (x < rem ? x : rem) + i;
+  TileCoord c;
+  c.prob = (bt.count > 1 && id >= bt.p[1].tile_begin) ? 1 : 0;
+  const int local = id - (c.prob ? bt.p[1].tile_begin : bt.p[0].tile_begin);
+  const int tiles_m = (int)ceil_div(c.prob ? bt.p[1].M : bt.p[0].M, BM);
+  const int tiles_n = c.prob ? bt.p[1].tiles_n : bt.p[0].tiles_n;
+  constexpr int kGroupM = 8;
+  const int group = kGroupM * tiles_n;
+  const int g = local / group;
+  const int first_m = g * kGroupM;
+  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int in = local % group;
+  c.tm = first_m + in % gm;
+  c.tn = in / gm;
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel
+// ---------------------------------------------------------------------------
+constexpr int kBK = 64;   // K per stage: 64 bf16 = 128 bytes = 8 chunks of 16 bytes per row
+// LDS rows padded to 144 bytes: 16 consecutive rows read at one chunk hit 16
+// distinct 4-bank groups (conflict-free for 32 or 64 banks) and all fragment
+// addresses are a per-lane base plus immediates.
+constexpr int kLdsLd = kBK + 8;
+
+// LDS element offset of chunk `c` (0..7) of tile row `row`.
+__device__ __forceinline__ int lds_off(int row, int c) { return row * kLdsLd + (c << 3); }
+
+template <int BM, int BN>
+__global__ void __launch_bounds__(256, 1) gemm_bf16_kernel(GemmBatch bt) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int LA = BM / 32, LB = BN / 32;      // 16-byte loads per thread per stage
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * kLdsLd];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * kLdsLd];
+
+  const TileCoord tc = decode_tile(bt, BM, BN);
+  // select by value: a dynamically indexed kernel-argument array would be
+  // copied to scratch memory
+  GemmProblem p = bt.p[0];
+  if (tc.prob) p = bt.p[1];
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global row pointers of this thread's loads (rows clamped into range)
+  const bf16_t* arow[LA];
+  const bf16_t* brow[LB];
+  const int lrow = tid >> 3, lchunk = tid & 7;
+  {
+    const bf16_t* A = reinterpret_cast<const bf16_t*>(p.A);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      int r = m0 + i * 32 + lrow;
+      r = r < p.M ? r : p.M - 1;
+      arow[i] = A + (int64_t)(r / p.amap.seg) * p.amap.bstride + (int64_t)(r % p.amap.seg) * p.amap.ld + lchunk * 8;
+    }
+    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      int r = n0 + i * 32 + lrow;
+      r = r < p.N ? r : p.N - 1;
+      brow[i] = W + (int64_t)r * p.ldw + lchunk * 8;
+    }
+  }
+  u32x4_t ra[LA], rb[LB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(brow[i] + k0);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4_t*>(&As[buf][lds_off(i * 32 + lrow, lchunk)]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4_t*>(&Bs[buf][lds_off(i * 32 + lrow, lchunk)]) = rb[i];
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int KT = p.K / kBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int frow = lane & 31, fhalf = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * kBK);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 32 + frow;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&As[cur][lds_off(r, kk * 2 + fhalf)]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WN + j * 32 + frow;
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[cur][lds_off(r, kk * 2 + fhalf)]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  Accumulator element e of lane l sits at row 8*(e/4) + 4*(l/32)
+  // + e%4, column l%32 of its 32 x 32 tile.  Each 32-row slab of a wave's
+  // tile goes through LDS (reusing the operand buffers) so the fused epilogue
+  // then runs on 4 consecutive columns per lane with vector loads and stores.
+  constexpr int CLD = WN + 4;
+  float* cs = reinterpret_cast<float*>(&As[0][0]) + wave * 32 * CLD;
+  static_assert(4 * 32 * CLD * 4 <= 2 * BM * kLdsLd * 2, "epilogue staging must fit in the A buffers");
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * CLD + j * 32 + frow] = acc[i][j][e];
+    __syncthreads();
+    constexpr int LPR = WN / 4;              // lanes per slab row
+    constexpr int RPI = 64 / LPR;            // slab rows per wave step
+    const int c4 = (lane % LPR) * 4;
+    const int col = n0 + wn * WN + c4;
+#pragma unroll 2
+    for (int rr = lane / LPR; rr < 32; rr += RPI) {
+      const int row = m0 + wm * WM + i * 32 + rr;
+      if (row < p.M && col < p.N) {
+        const float4 v = *reinterpret_cast<const float4*>(&cs[rr * CLD + c4]);
+        epi_apply4(p, row, col, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: 64 x 64 tile, 16 x 16 threads with 4 x 4 outputs each
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) gemm_f32_kernel(GemmBatch bt) {
+  constexpr int BM = 64, BN = 64, BKF = 16;
+  __shared__ float As[BKF][BM + 4];
+  __shared__ float Bs[BKF][BN + 4];
+  const TileCoord tc = decode_tile(bt, BM, BN);
+  // select by value: a dynamically indexed kernel-argument array would be
+  // copied to scratch memory
+  GemmProblem p = bt.p[0];
+  if (tc.prob) p = bt.p[1];
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const float* A = reinterpret_cast<const float*>(p.A);
+  const float* W = reinterpret_cast<const float*>(p.W);
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < p.K; k0 += BKF) {
+    for (int i = threadIdx.x; i < BM * BKF; i += 256) {
+      const int r = i / BKF, kk = i % BKF;
+      int gr = m0 + r;
+      gr = gr < p.M ? gr : p.M - 1;
+      const int k = k0 + kk;
+      As[kk][r] = k < p.K ? A[(int64_t)(gr / p.amap.seg) * p.amap.bstride + (int64_t)(gr % p.amap.seg) * p.amap.ld + k]
+                          : 0.f;
+      int gn = n0 + r;
+      gn = gn < p.N ? gn : p.N - 1;
+      Bs[kk][r] = k < p.K ? W[(int64_t)gn * p.ldw + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BKF; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+  const float* bias = reinterpret_cast<const float*>(p.bias);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty + 16 * i;
+    const EpiRow er = epi_row(p, row, 4);
+    if (!er.valid) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx + 16 * j;
+      if (col < p.N) epi_apply<float>(p, er, col, acc[i][j] + (bias ? bias[col] : 0.f));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+static int assign_tiles(GemmBatch& bt, int BM, int BN) {
+  int t = 0;
+  for (int i = 0; i < bt.count; ++i) {
+    bt.p[i].tile_begin = t;
+    bt.p[i].tiles_n = (int)ceil_div(bt.p[i].N, BN);
+    t += (int)ceil_div(bt.p[i].M, BM) * bt.p[i].tiles_n;
+  }
+  bt.total_tiles = t;
+  return t;
+}
+
+hipError_t launch_gemm(GemmBatch bt, int dtype, hipStream_t stream) {
+  if (dtype == kF32) {
+    const int tiles = assign_tiles(bt, 64, 64);
+    TimingScope ts(kKcGemmF32, stream);
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, bt);
+    return hipGetLastError();
+  }
+  // big tiles when they still give every CU at least one tile
+  GemmBatch big = bt;
+  const int tiles_big = assign_tiles(big, 256, 256);
+  if (tiles_big >= 256) {
+    TimingScope ts(kKcGemm256, stream);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256>), dim3(tiles_big), dim3(256), 0, stream, big);
+  } else {
+    const int tiles = assign_tiles(bt, 128, 128);
+    TimingScope ts(kKcGemm128, stream);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128>), dim3(tiles), dim3(256), 0, stream, bt);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace flux

@@ -1,0 +1,123 @@
+// Internal launch interface of libflux: argument structs and host launchers.
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flux {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+// ---------------------------------------------------------------------------
+// Row addressing shared by the token-wise kernels.  A logical row r of a
+// segment with `seg` rows per sample lives at
+//     base + (r / seg) * bstride + (r % seg) * ld      (elements)
+// which covers contiguous [B*L, ld] buffers, per-sample strided residual
+// streams and the image / text halves of a joint [B, L, ld] buffer.
+// ---------------------------------------------------------------------------
+struct RowMap {
+  int64_t bstride;
+  int64_t ld;
+  int32_t seg;
+};
+
+// ---------------------------- GEMM (C = A W^T) -----------------------------
+enum EpiKind : int {
+  kEpiStore = 0,      // out0 = T(acc + bias)                   (T = operand type)
+  kEpiGelu = 1,       // out0 = T(GELU(acc + bias))
+  kEpiResid = 2,      // out0 (float) += gate[b, col] * (acc + bias)
+  kEpiStoreF32 = 3,   // out0 (float) = acc + bias            (column stride col_stride)
+  kEpiSplitGelu = 4,  // col < n_split: out0 = T(acc + bias); else out1[col - n_split] = T(GELU(acc + bias))
+};
+
+struct GemmProblem {
+  const void* A;  RowMap amap;          // [M, K] rows
+  const void* W;  int64_t ldw;          // [N, K]
+  const void* bias;                     // [N] or null (operand type)
+  int32_t M, N, K;
+  int32_t epi;
+  void* out0;     RowMap omap0;  int64_t col_stride0;
+  void* out1;     RowMap omap1;  int32_t n_split;
+  const float* gate; int64_t gate_bstride;   // gate[(r / omap0.seg) * gate_bstride + col]
+  int32_t tile_begin;                   // filled by the launcher
+  int32_t tiles_n;                      // filled by the launcher
+};
+
+constexpr int kMaxGemmProblems = 2;
+struct GemmBatch {
+  GemmProblem p[kMaxGemmProblems];
+  int32_t count;
+  int32_t total_tiles;
+};
+
+hipError_t launch_gemm(GemmBatch batch, int dtype, hipStream_t stream);
+
+// ------------------------------ LN + modulate ------------------------------
+struct LnSeg {
+  const float* x;  RowMap xmap;         // fp32 residual rows
+  void* out;       RowMap omap;         // T rows
+  const float* shift; const float* scale; int64_t mod_bstride;   // [b * mod_bstride + col]
+  int32_t rows;                         // B * seg
+};
+struct LnArgs {
+  LnSeg s[2];
+  int32_t count;
+  int32_t dim;
+  float eps;
+};
+hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream);
+
+// ------------------------------- GEMV (M = B) -------------------------------
+struct GemvProblem {
+  const void* W; const void* bias;      // [N, K], [N] (operand type)
+  int32_t N, K;
+  const float* x; int64_t x_bstride;    // input [B, K] float
+  float* y; int64_t y_bstride;          // output [B, N] float
+  int32_t act_silu;                     // apply SiLU to x first
+  int32_t accumulate;                   // y += instead of y =
+};
+struct GemvBatch {
+  GemvProblem p[2];
+  int32_t count;
+  int32_t batch;
+};
+hipError_t launch_gemv(const GemvBatch& a, int dtype, hipStream_t stream);
+
+// ------------------ q/k RMSNorm + RoPE + head-major layout ------------------
+struct PrepArgs {
+  const void* src_q; const void* src_k; const void* src_v; // token rows (operand type)
+  int64_t src_bstride; int64_t src_ld;
+  int32_t batch, seq, seq_pad, heads, head_dim, l_img;
+  const float* gq_img; const float* gk_img;               // RMSNorm scales (null -> no norm)
+  const float* gq_txt; const float* gk_txt;               // rows >= l_img use these
+  const float* rope;                                      // [B, seq, head_dim/2, 2] or null
+  float eps;
+  void* qh; void* kh;                                     // [B, H, seq_pad, head_dim]
+  void* vt;                                               // [B, H, head_dim, seq_pad]
+};
+hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream);
+
+// -------------------------------- attention --------------------------------
+struct AttnArgs {
+  const void* qh; const void* kh; const void* vt;         // as written by launch_prep
+  void* out; int64_t out_bstride; int64_t out_ld;         // [B, seq, ...], head h at column h*head_dim
+  int32_t batch, seq, seq_pad, heads, head_dim;
+  float scale_log2;                                       // log2(e) / sqrt(head_dim)
+};
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
+
+// ------------------------------ small kernels ------------------------------
+hipError_t launch_rope_table(const float* ids, int batch, int seq, const int32_t axes[3], float theta,
+                             float* table, hipStream_t stream);
+hipError_t launch_timestep_embed(const float* t, int batch, int dim, float time_factor, float max_period,
+                                 float* out, hipStream_t stream);
+hipError_t launch_patchify(const float* z, int batch, int channels, int hw, void* out, int dtype,
+                           hipStream_t stream);
+hipError_t launch_rf_noise(int batch, int64_t n, const float* z0, const float* z1, const float* t,
+                           float* zt, float* vt, hipStream_t stream);
+hipError_t launch_rf_loss(int batch, int64_t n, const float* z0, const float* z1, const float* vpred,
+                          float* loss, float* loss_ps, double* partials, int parts_per_sample,
+                          hipStream_t stream);
+int rf_parts_per_sample(int64_t n);
+
+}  // namespace flux

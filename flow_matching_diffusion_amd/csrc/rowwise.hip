@@ -1,0 +1,522 @@
+// Row-wise and elementwise kernels of the Flux block forward (gfx950, wave64):
+// rectified-flow noising and loss, timestep sinusoid, 3D RoPE table,
+// patchify, LayerNorm + adaLN modulate, modulation GEMV, q/k RMSNorm + RoPE.
+#include "common.h"
+#include "kernels.h"
+#include "timing.h"
+
+namespace flux {
+
+// ===========================================================================
+// Rectified flow ("Flux architecture deep dive", Flow matching framework and
+// Mathematical formulation / Flow matching objective).
+// ===========================================================================
+// z_t = (1 - t) z0 + t z1 as two rounded products and one rounded sum;
+// v* = z1 - z0.  Contraction into an FMA is switched off for this kernel, so
+// the result is the same rounding sequence on every build.
+__global__ void __launch_bounds__(256) rf_noise_kernel(int64_t n, const float* __restrict__ z0,
+                                                       const float* __restrict__ z1, const float* __restrict__ t,
+                                                       float* __restrict__ zt, float* __restrict__ vt) {
+#pragma clang fp contract(off)
+  const int b = blockIdx.y;
+  const float tb = t[b];
+  const float omt = 1.0f - tb;
+  const int64_t base = (int64_t)b * n;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool vec4 = ((n & 3) == 0);
+  if (vec4) {
+    const int64_t n4 = n >> 2;
+    const float4* a4 = reinterpret_cast<const float4*>(z0 + base);
+    const float4* b4 = reinterpret_cast<const float4*>(z1 + base);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      float4 a = a4[i], c = b4[i];
+      if (zt) {
+        float4 r;
+        r.x = omt * a.x + tb * c.x;
+        r.y = omt * a.y + tb * c.y;
+        r.z = omt * a.z + tb * c.z;
+        r.w = omt * a.w + tb * c.w;
+        reinterpret_cast<float4*>(zt + base)[i] = r;
+      }
+      if (vt) {
+        float4 v;
+        v.x = c.x - a.x; v.y = c.y - a.y;
+        v.z = c.z - a.z; v.w = c.w - a.w;
+        reinterpret_cast<float4*>(vt + base)[i] = v;
+      }
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+      const float a = z0[base + i], c = z1[base + i];
+      if (zt) zt[base + i] = omt * a + tb * c;
+      if (vt) vt[base + i] = c - a;
+    }
+  }
+}
+
+hipError_t launch_rf_noise(int batch, int64_t n, const float* z0, const float* z1, const float* t, float* zt,
+                           float* vt, hipStream_t stream) {
+  const int64_t work = (n & 3) == 0 ? n / 4 : n;
+  int gx = (int)ceil_div(work, 256);
+  if (gx > 1024) gx = 1024;
+  TimingScope ts(kKcRf, stream);
+  hipLaunchKernelGGL(rf_noise_kernel, dim3(gx, batch), dim3(256), 0, stream, n, z0, z1, t, zt, vt);
+  return hipGetLastError();
+}
+
+// Velocity MSE, stage 1: block (g, b) sums (v_pred - (z1 - z0))^2 over its
+// slice of sample b in fp64.  Each thread walks a fixed strided set, then a
+// fixed butterfly/tree -> the same bits on every run.
+constexpr int kRfLossThreads = 256;
+int rf_parts_per_sample(int64_t n) {
+  int64_t p = ceil_div(n, (int64_t)kRfLossThreads * 16);
+  if (p < 1) p = 1;
+  if (p > 256) p = 256;
+  return (int)p;
+}
+
+__global__ void __launch_bounds__(kRfLossThreads) rf_loss_partial_kernel(int64_t n, const float* __restrict__ z0,
+                                                                         const float* __restrict__ z1,
+                                                                         const float* __restrict__ vp,
+                                                                         double* __restrict__ partials) {
+  const int b = blockIdx.y, g = blockIdx.x, parts = gridDim.x;
+  const int64_t per = ceil_div(n, parts);
+  const int64_t lo = (int64_t)g * per;
+  const int64_t hi = lo + per < n ? lo + per : n;
+  const int64_t base = (int64_t)b * n;
+  double acc = 0.0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kRfLossThreads) {
+    const float v = __fsub_rn(z1[base + i], z0[base + i]);
+    const float d = __fsub_rn(vp[base + i], v);
+    acc += (double)d * (double)d;
+  }
+  acc = wave_sum_f64(acc);
+  __shared__ double red[kRfLossThreads / kWave];
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int i = 0; i < kRfLossThreads / kWave; ++i) s += red[i];
+    partials[(int64_t)b * parts + g] = s;
+  }
+}
+
+// Stage 2: one block; per-sample sums in fixed order, then the total.
+__global__ void __launch_bounds__(256) rf_loss_final_kernel(int batch, int64_t n, int parts,
+                                                            const double* __restrict__ partials,
+                                                            float* __restrict__ loss, float* __restrict__ loss_ps) {
+  __shared__ double ps[256];
+  for (int b = threadIdx.x; b < batch; b += blockDim.x) {
+    double s = 0.0;
+    for (int g = 0; g < parts; ++g) s += partials[(int64_t)b * parts + g];
+    if (b < 256) ps[b] = s;
+    if (loss_ps) loss_ps[b] = (float)(s / (double)n);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && loss) {
+    double s = 0.0;
+    if (batch <= 256) {
+      for (int b = 0; b < batch; ++b) s += ps[b];
+    } else {
+      for (int b = 0; b < batch; ++b)
+        for (int g = 0; g < parts; ++g) s += partials[(int64_t)b * parts + g];
+    }
+    *loss = (float)(s / ((double)n * (double)batch));
+  }
+}
+
+hipError_t launch_rf_loss(int batch, int64_t n, const float* z0, const float* z1, const float* vpred, float* loss,
+                          float* loss_ps, double* partials, int parts, hipStream_t stream) {
+  TimingScope ts(kKcRf, stream);
+  hipLaunchKernelGGL(rf_loss_partial_kernel, dim3(parts, batch), dim3(kRfLossThreads), 0, stream, n, z0, z1, vpred,
+                     partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rf_loss_final_kernel, dim3(1), dim3(256), 0, stream, batch, n, parts, partials, loss, loss_ps);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// Timestep sinusoid ("Flux architecture deep dive", Conditioning; "Flux model
+// API reference", TimeStepEmbedder): tau = time_factor * t,
+// out = [cos(tau f_j) | sin(tau f_j)], f_j = max_period^(-j/half).  fp64.
+// ===========================================================================
+__global__ void timestep_embed_kernel(const float* __restrict__ t, int batch, int dim, double time_factor,
+                                      double log_max_period, float* __restrict__ out) {
+  const int half = dim / 2;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= batch * half) return;
+  const int b = i / half, j = i % half;
+  const double tau = time_factor * (double)t[b];
+  const double f = exp(-log_max_period * (double)j / (double)half);
+  double s, c;
+  sincos(tau * f, &s, &c);
+  out[(int64_t)b * dim + j] = (float)c;
+  out[(int64_t)b * dim + half + j] = (float)s;
+}
+
+hipError_t launch_timestep_embed(const float* t, int batch, int dim, float time_factor, float max_period, float* out,
+                                 hipStream_t stream) {
+  const int n = batch * (dim / 2);
+  TimingScope ts(kKcMisc, stream);
+  hipLaunchKernelGGL(timestep_embed_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, t, batch, dim,
+                     (double)time_factor, log((double)max_period), out);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// 3D RoPE table ("Flux architecture deep dive", 3D RoPE mathematics; "Flux
+// model API reference", EmbedND).  Pair m of the head belongs to axis a with
+// local index j; angle = p_a * theta^(-2j/d_a) in fp64; stored (cos, sin).
+// ===========================================================================
+__global__ void rope_table_kernel(const float* __restrict__ ids, int n_tok, int a0, int a1, int a2, double log_theta,
+                                  float2* __restrict__ table) {
+  const int pairs = (a0 + a1 + a2) / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_tok * pairs) return;
+  const int64_t tok = i / pairs;
+  int m = (int)(i % pairs);
+  int axis, d;
+  if (m < a0 / 2) { axis = 0; d = a0; }
+  else if (m < (a0 + a1) / 2) { axis = 1; d = a1; m -= a0 / 2; }
+  else { axis = 2; d = a2; m -= (a0 + a1) / 2; }
+  const double p = (double)ids[tok * 3 + axis];
+  const double ang = p * exp(-log_theta * (2.0 * (double)m) / (double)d);
+  double s, c;
+  sincos(ang, &s, &c);
+  table[i] = make_float2((float)c, (float)s);
+}
+
+hipError_t launch_rope_table(const float* ids, int batch, int seq, const int32_t axes[3], float theta, float* table,
+                             hipStream_t stream) {
+  const int n_tok = batch * seq;
+  const int pairs = (axes[0] + axes[1] + axes[2]) / 2;
+  const int64_t n = (int64_t)n_tok * pairs;
+  TimingScope ts(kKcMisc, stream);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, ids, n_tok, axes[0],
+                     axes[1], axes[2], log((double)theta), reinterpret_cast<float2*>(table));
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// patchify ("Flux architecture deep dive", Implementation details / Memory
+// layout): [B, C, H*W] float -> [B, H*W, C] operand type.
+// ===========================================================================
+template <typename T>
+__global__ void patchify_kernel(const float* __restrict__ z, int channels, int hw, T* __restrict__ out) {
+  const int b = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over hw * C, channel fastest
+  if (i >= (int64_t)hw * channels) return;
+  const int c = (int)(i % channels);
+  const int64_t l = i / channels;
+  out[(int64_t)b * hw * channels + i] = from_f32<T>(z[((int64_t)b * channels + c) * hw + l]);
+}
+
+hipError_t launch_patchify(const float* z, int batch, int channels, int hw, void* out, int dtype,
+                           hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div((int64_t)hw * channels, 256), batch);
+  TimingScope ts(kKcMisc, stream);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(patchify_kernel<bf16_t>, grid, dim3(256), 0, stream, z, channels, hw, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL(patchify_kernel<float>, grid, dim3(256), 0, stream, z, channels, hw, (float*)out);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// LayerNorm (no affine, biased variance) + adaLN modulate ("Flux architecture
+// deep dive", Implementation details / Adaptive layer normalization):
+// h = (x - mean) / sqrt(var + eps) * (1 + scale[b]) + shift[b].
+// One wave per token row; the row stays in registers (two-pass variance).
+// ===========================================================================
+constexpr int kLnMaxVec = 16;   // float4 per lane: D <= 64 * 4 * 16 = 4096
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = pack_bf16x2(a, b);
+  v.y = pack_bf16x2(c, d);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row_g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int si = 0;
+  int64_t r = row_g;
+  if (r >= a.s[0].rows) {
+    if (a.count < 2) return;
+    r -= a.s[0].rows;
+    si = 1;
+    if (r >= a.s[1].rows) return;
+  }
+  const LnSeg& s = a.s[si];
+  const int D = a.dim;
+  const int64_t b = r / s.xmap.seg, l = r % s.xmap.seg;
+  const float* x = s.x + b * s.xmap.bstride + l * s.xmap.ld;
+  T* out = reinterpret_cast<T*>(s.out) + b * s.omap.bstride + l * s.omap.ld;
+  const float* sh = s.shift + b * s.mod_bstride;
+  const float* sc = s.scale + b * s.mod_bstride;
+  const int nv = D / 256;
+  float4 v[kLnMaxVec];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i) {
+    if (i < nv) {
+      v[i] = reinterpret_cast<const float4*>(x)[lane + 64 * i];
+      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float mean = wave_sum(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i) {
+    if (i < nv) {
+      const float dx = v[i].x - mean, dy = v[i].y - mean, dz = v[i].z - mean, dw = v[i].w - mean;
+      sq += (dx * dx + dy * dy) + (dz * dz + dw * dw);
+    }
+  }
+  const float var = wave_sum(sq) / (float)D;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+#pragma unroll
+  for (int i = 0; i < kLnMaxVec; ++i) {
+    if (i < nv) {
+      const int c = (lane + 64 * i) * 4;
+      const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
+      const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
+      store4<T>(out + c, (v[i].x - mean) * rstd * (1.f + s4.x) + h4.x, (v[i].y - mean) * rstd * (1.f + s4.y) + h4.y,
+                (v[i].z - mean) * rstd * (1.f + s4.z) + h4.z, (v[i].w - mean) * rstd * (1.f + s4.w) + h4.w);
+    }
+  }
+}
+
+hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {
+  int64_t rows = a.s[0].rows + (a.count > 1 ? a.s[1].rows : 0);
+  const dim3 grid((unsigned)ceil_div(rows, 4));
+  TimingScope ts(kKcLnMod, stream);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(ln_mod_kernel<bf16_t>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(ln_mod_kernel<float>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// Modulation GEMV (M = batch <= 4 per launch): y[b, n] (+)= sum_k W[n, k]
+// act(x[b, k]) + bias[n] ("Flux model API reference", AdaLN: Linear over
+// SiLU(vec); also the timestep / pooled-vector embedders).  Weight-bandwidth
+// bound: each wave streams whole W rows with 16-byte loads; act(x) is staged
+// in LDS once per block.
+// ===========================================================================
+constexpr int kGemvMaxB = 4;
+
+template <typename T>
+struct Vec16;  // 16 bytes of operand elements
+template <>
+struct Vec16<bf16_t> { static constexpr int n = 8; };
+template <>
+struct Vec16<float> { static constexpr int n = 4; };
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const u32x4_t& r, float* w);
+template <>
+__device__ __forceinline__ void unpack16<bf16_t>(const u32x4_t& r, float* w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[2 * i] = __uint_as_float(r[i] << 16);
+    w[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const u32x4_t& r, float* w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = __uint_as_float(r[i]);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) gemv_kernel(GemvBatch a) {
+  extern __shared__ float xs[];   // [batch][K]
+  const GemvProblem& p = a.p[blockIdx.y];
+  const int K = p.K, B = a.batch;
+  for (int i = threadIdx.x; i < B * K; i += blockDim.x) {
+    const int b = i / K, k = i % K;
+    const float v = p.x[(int64_t)b * p.x_bstride + k];
+    xs[i] = p.act_silu ? silu_f(v) : v;
+  }
+  __syncthreads();
+  constexpr int E = Vec16<T>::n;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const T* W = reinterpret_cast<const T*>(p.W);
+  const T* bias = reinterpret_cast<const T*>(p.bias);
+  for (int n = blockIdx.x * 4 + wave; n < p.N; n += gridDim.x * 4) {
+    const T* wr = W + (int64_t)n * K;
+    float acc[kGemvMaxB] = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = lane * E; k0 < K; k0 += 64 * E) {
+      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(wr + k0);
+      float w[E];
+      unpack16<T>(raw, w);
+#pragma unroll
+      for (int b = 0; b < kGemvMaxB; ++b) {
+        if (b < B) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[b] += w[e] * xs[b * K + k0 + e];
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kGemvMaxB; ++b) {
+      if (b < B) {
+        const float s = wave_sum(acc[b]);
+        if (lane == 0) {
+          float v = s + (bias ? load_f32<T>(bias + n) : 0.f);
+          float* y = p.y + (int64_t)b * p.y_bstride + n;
+          *y = p.accumulate ? *y + v : v;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemv(const GemvBatch& a, int dtype, hipStream_t stream) {
+  int maxn = 0, maxk = 0;
+  for (int i = 0; i < a.count; ++i) {
+    maxn = a.p[i].N > maxn ? a.p[i].N : maxn;
+    maxk = a.p[i].K > maxk ? a.p[i].K : maxk;
+  }
+  int gx = (int)ceil_div(maxn, 4);
+  if (gx > 512) gx = 512;
+  const size_t lds = (size_t)a.batch * maxk * sizeof(float);
+  const dim3 grid(gx, a.count);
+  TimingScope ts(kKcGemv, stream);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(gemv_kernel<bf16_t>, grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL(gemv_kernel<float>, grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// q/k preparation for attention: per token and head, RMSNorm over head_dim
+// with the stream's scale ("Flux model API reference", RMSNorm), then the 3D
+// RoPE rotation of interleaved pairs ("Flux architecture deep dive", 3D RoPE
+// mathematics), written head-major [B, H, seq_pad, Dh]; v is written
+// transposed [B, H, Dh, seq_pad] so that attention reads it K-contiguous.
+// Rows seq .. seq_pad-1 are written as zeros.
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void load_pair(const T* p, float& u, float& w);
+template <>
+__device__ __forceinline__ void load_pair<float>(const float* p, float& u, float& w) {
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  u = v.x;
+  w = v.y;
+}
+template <>
+__device__ __forceinline__ void load_pair<bf16_t>(const bf16_t* p, float& u, float& w) {
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+  u = __uint_as_float(v << 16);
+  w = __uint_as_float(v & 0xffff0000u);
+}
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, float u, float w);
+template <>
+__device__ __forceinline__ void store_pair<float>(float* p, float u, float w) {
+  *reinterpret_cast<float2*>(p) = make_float2(u, w);
+}
+template <>
+__device__ __forceinline__ void store_pair<bf16_t>(bf16_t* p, float u, float w) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(u, w);
+}
+
+template <typename T, int DH>
+__global__ void __launch_bounds__(256) qk_prep_kernel(PrepArgs a) {
+  constexpr int PAIRS = DH / 2;               // one pair per lane
+  constexpr int PER_WAVE = 64 / PAIRS;        // (token, head) items per wave step
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / PAIRS, m = lane % PAIRS;
+  const int H = a.heads;
+  const bool valid = j < a.seq;
+  const bool txt = j >= a.l_img;
+  const int64_t row_off = (int64_t)b * a.src_bstride + (int64_t)j * a.src_ld;
+  float c = 1.f, s = 0.f;
+  if (valid && a.rope) {
+    const float2 cs = reinterpret_cast<const float2*>(a.rope)[((int64_t)b * a.seq + j) * PAIRS + m];
+    c = cs.x;
+    s = cs.y;
+  }
+  // items: (which in {q, k}) x heads
+  for (int it = wave * PER_WAVE + sub; it < 2 * H; it += 4 * PER_WAVE) {
+    const int which = it / H, h = it % H;
+    float u = 0.f, w = 0.f;
+    if (valid) {
+      const T* src = reinterpret_cast<const T*>(which == 0 ? a.src_q : a.src_k) + row_off;
+      load_pair<T>(src + h * DH + 2 * m, u, w);
+      const float* g = which == 0 ? (txt ? a.gq_txt : a.gq_img) : (txt ? a.gk_txt : a.gk_img);
+      if (g) {
+        const float ms = wave_sum<PAIRS>(u * u + w * w) / (float)DH;
+        const float r = 1.0f / sqrtf(ms + a.eps);
+        u = u * r * g[2 * m];
+        w = w * r * g[2 * m + 1];
+      }
+      const float u2 = u * c - w * s;
+      const float w2 = u * s + w * c;
+      u = u2;
+      w = w2;
+    }
+    T* dst = reinterpret_cast<T*>(which == 0 ? a.qh : a.kh) + (((int64_t)b * H + h) * a.seq_pad + j) * DH + 2 * m;
+    store_pair<T>(dst, u, w);
+  }
+}
+
+// v [rows j0..j0+63 of one head] -> vt[d][j0..j0+63] through LDS.
+template <typename T, int DH>
+__global__ void __launch_bounds__(256) v_transpose_kernel(PrepArgs a) {
+  __shared__ T tile[64][DH + 2];
+  const int j0 = blockIdx.x * 64, h = blockIdx.y % a.heads, b = blockIdx.y / a.heads;
+  const T* src = reinterpret_cast<const T*>(a.src_v) + (int64_t)b * a.src_bstride + h * DH;
+  for (int i = threadIdx.x; i < 64 * DH; i += 256) {
+    const int r = i / DH, d = i % DH;
+    const int j = j0 + r;
+    tile[r][d] = j < a.seq ? src[(int64_t)j * a.src_ld + d] : from_f32<T>(0.f);
+  }
+  __syncthreads();
+  T* dst = reinterpret_cast<T*>(a.vt) + ((int64_t)b * a.heads + h) * DH * a.seq_pad + j0;
+  for (int i = threadIdx.x; i < 64 * DH; i += 256) {
+    const int d = i / 64, r = i % 64;
+    dst[(int64_t)d * a.seq_pad + r] = tile[r][d];
+  }
+}
+
+template <typename T>
+static hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
+  const dim3 g1(a.seq_pad, a.batch), g2(a.seq_pad / 64, a.batch * a.heads);
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL((qk_prep_kernel<T, 128>), g1, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((v_transpose_kernel<T, 128>), g2, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((qk_prep_kernel<T, 64>), g1, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((v_transpose_kernel<T, 64>), g2, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream) {
+  TimingScope ts(kKcPrep, stream);
+  return dtype == kBF16 ? launch_prep_t<bf16_t>(a, stream) : launch_prep_t<float>(a, stream);
+}
+
+}  // namespace flux

@@ -1,0 +1,35 @@
+// Kernel classes and the RAII launch bracket used by the opt-in timing hook.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace flux {
+
+enum KernelClass : int {
+  kKcGemm256 = 0,
+  kKcGemm128,
+  kKcGemmF32,
+  kKcAttn,
+  kKcLnMod,
+  kKcGemv,
+  kKcPrep,
+  kKcRf,
+  kKcMisc,
+  kKcCount
+};
+
+// Records a start event on `s` at construction and a stop event at
+// destruction when timing is enabled; does nothing otherwise.
+class TimingScope {
+ public:
+  TimingScope(int cls, hipStream_t s);
+  ~TimingScope();
+  TimingScope(const TimingScope&) = delete;
+  TimingScope& operator=(const TimingScope&) = delete;
+
+ private:
+  int cls_;
+  hipStream_t stream_;
+  hipEvent_t start_;
+};
+
+}  // namespace flux

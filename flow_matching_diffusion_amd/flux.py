@@ -1,0 +1,295 @@
+"""ctypes binding of libflux (include/flux.h).  Argument marshalling only:
+every step of the computation runs in the HIP library.  Loading fails loudly
+when the library has not been built; there is no fallback implementation.
+
+Tensors are passed as torch tensors on the GPU (their data_ptr() is handed to
+the library) or as raw integer device addresses; the stream defaults to
+torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflux.so")
+
+FLUX_OK = 0
+FLUX_ERR_INVALID_ARGUMENT = 1
+FLUX_ERR_UNSUPPORTED = 2
+FLUX_ERR_WORKSPACE_TOO_SMALL = 3
+FLUX_ERR_HIP = 4
+FLUX_PREC_F32 = 0
+FLUX_PREC_BF16 = 1
+
+# every symbol include/flux.h declares
+EXPORTED = (
+    "flux_block_fwd", "flux_single_fwd", "rf_noise_loss", "flux_rope_table", "flux_embed_fwd",
+    "flux_final_fwd", "flux_linear_fwd", "flux_attention_fwd", "flux_workspace_bytes",
+    "flux_rf_workspace_bytes", "flux_embed_workspace_bytes", "flux_final_workspace_bytes",
+    "flux_attention_workspace_bytes", "flux_status_string", "flux_last_error", "flux_timing_enable",
+    "flux_timing_classes", "flux_timing_class_name", "flux_timing_read",
+)
+
+
+class FluxError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({_status_name(status)}): {detail}")
+        self.status = status
+
+
+def _status_name(s: int) -> str:
+    return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}.get(s, "?")
+
+
+# --------------------------------------------------------------------------- #
+# C structs (mirror include/flux.h)
+# --------------------------------------------------------------------------- #
+class flux_dims(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("l_img", C.c_int32), ("l_txt", C.c_int32), ("hidden", C.c_int32),
+                ("heads", C.c_int32), ("head_dim", C.c_int32), ("mlp_hidden", C.c_int32),
+                ("axes_dim", C.c_int32 * 3), ("theta", C.c_float), ("eps", C.c_float), ("precision", C.c_int32)]
+
+
+class flux_stream_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "qkv_w", "qkv_b", "q_norm", "k_norm", "proj_w",
+                                          "proj_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+
+
+class flux_single_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "lin1_w", "lin1_b", "q_norm", "k_norm", "lin2_w",
+                                          "lin2_b")]
+
+
+class rf_args(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("n_per_sample", C.c_int64), ("z0", C.c_void_p), ("z1", C.c_void_p),
+                ("t", C.c_void_p), ("z_t", C.c_void_p), ("v_target", C.c_void_p), ("v_pred", C.c_void_p),
+                ("loss", C.c_void_p), ("loss_per_sample", C.c_void_p), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_size_t)]
+
+
+class flux_embed_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("img_in_w", "img_in_b", "txt_in_w", "txt_in_b", "time_in1_w",
+                                          "time_in1_b", "time_in2_w", "time_in2_b", "vector_in1_w",
+                                          "vector_in1_b", "vector_in2_w", "vector_in2_b")]
+
+
+# --------------------------------------------------------------------------- #
+# library loading
+# --------------------------------------------------------------------------- #
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m flow_matching_diffusion_amd.build` "
+                           "(there is no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+    P = C.POINTER
+    sig = {
+        "flux_block_fwd": [P(flux_dims), P(flux_stream_weights), P(flux_stream_weights), vp, i64, vp, i64, vp, vp,
+                           vp, sz, vp],
+        "flux_single_fwd": [P(flux_dims), P(flux_single_weights), vp, i64, vp, vp, vp, sz, vp],
+        "rf_noise_loss": [P(rf_args), vp],
+        "flux_rope_table": [vp, i32, i32, P(C.c_int32), f32, vp, vp],
+        "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
+                           vp, i64, vp, i64, vp, vp, sz, vp],
+        "flux_final_fwd": [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp],
+        "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
+        "flux_attention_fwd": [i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, sz, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = C.c_int
+    L.flux_workspace_bytes.argtypes = [P(flux_dims), i32]
+    L.flux_workspace_bytes.restype = sz
+    L.flux_rf_workspace_bytes.argtypes = [i32, i64]
+    L.flux_rf_workspace_bytes.restype = sz
+    L.flux_embed_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.flux_embed_workspace_bytes.restype = sz
+    L.flux_final_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.flux_final_workspace_bytes.restype = sz
+    L.flux_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.flux_attention_workspace_bytes.restype = sz
+    L.flux_status_string.argtypes = [C.c_int]
+    L.flux_status_string.restype = C.c_char_p
+    L.flux_last_error.argtypes = []
+    L.flux_last_error.restype = C.c_char_p
+    L.flux_timing_enable.argtypes = [i32]
+    L.flux_timing_enable.restype = C.c_int
+    L.flux_timing_classes.argtypes = []
+    L.flux_timing_classes.restype = i32
+    L.flux_timing_class_name.argtypes = [i32]
+    L.flux_timing_class_name.restype = C.c_char_p
+    L.flux_timing_read.argtypes = [P(C.c_double), P(C.c_int64), i32]
+    L.flux_timing_read.restype = C.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != FLUX_OK:
+        raise FluxError(status, where, lib().flux_last_error().decode())
+
+
+def ptr(x) -> Optional[int]:
+    """Device address of a tensor (or pass-through int / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# --------------------------------------------------------------------------- #
+# marshalling helpers
+# --------------------------------------------------------------------------- #
+def make_dims(batch, l_img, l_txt, hidden, heads, head_dim, mlp_hidden, axes_dim=(16, 56, 56), theta=10000.0,
+              eps=1e-6, precision=FLUX_PREC_BF16) -> flux_dims:
+    d = flux_dims()
+    d.batch, d.l_img, d.l_txt, d.hidden, d.heads, d.head_dim, d.mlp_hidden = (
+        batch, l_img, l_txt, hidden, heads, head_dim, mlp_hidden)
+    d.axes_dim[:] = list(axes_dim)
+    d.theta, d.eps, d.precision = theta, eps, precision
+    return d
+
+
+def dims_for(wl, batch: Optional[int] = None) -> flux_dims:
+    """flux_dims of a synth.Workload."""
+    return make_dims(batch or wl.batch, wl.l_img, wl.l_txt, wl.hidden, wl.heads, wl.head_dim, wl.mlp_hidden,
+                     wl.axes_dim, wl.theta, wl.eps, FLUX_PREC_F32 if wl.precision == "f32" else FLUX_PREC_BF16)
+
+
+def stream_weights(w: Dict[str, object], prefix: str) -> flux_stream_weights:
+    s = flux_stream_weights()
+    for f in ("mod", "qkv", "proj", "fc1", "fc2"):
+        setattr(s, f + "_w", ptr(w[f"{prefix}_{f}.w"]))
+        setattr(s, f + "_b", ptr(w[f"{prefix}_{f}.b"]))
+    s.q_norm = ptr(w[f"{prefix}_q_norm"])
+    s.k_norm = ptr(w[f"{prefix}_k_norm"])
+    return s
+
+
+def single_weights(w: Dict[str, object]) -> flux_single_weights:
+    s = flux_single_weights()
+    for f in ("mod", "lin1", "lin2"):
+        setattr(s, f + "_w", ptr(w[f + ".w"]))
+        setattr(s, f + "_b", ptr(w[f + ".b"]))
+    s.q_norm = ptr(w["q_norm"])
+    s.k_norm = ptr(w["k_norm"])
+    return s
+
+
+def embed_weights(w: Dict[str, object]) -> flux_embed_weights:
+    s = flux_embed_weights()
+    for f in ("img_in", "txt_in", "time_in1", "time_in2", "vector_in1", "vector_in2"):
+        setattr(s, f + "_w", ptr(w.get(f + ".w")))
+        setattr(s, f + "_b", ptr(w.get(f + ".b")))
+    return s
+
+
+# --------------------------------------------------------------------------- #
+# entry points (names of include/flux.h)
+# --------------------------------------------------------------------------- #
+def flux_workspace_bytes(dims: flux_dims, op: int) -> int:
+    return lib().flux_workspace_bytes(C.byref(dims), op)
+
+
+def flux_block_fwd(dims: flux_dims, img_w: flux_stream_weights, txt_w: flux_stream_weights, img, img_bstride: int,
+                   txt, txt_bstride: int, vec, rope, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_block_fwd(C.byref(dims), C.byref(img_w), C.byref(txt_w), ptr(img), img_bstride, ptr(txt),
+                                txt_bstride, ptr(vec), ptr(rope), ptr(workspace), workspace_bytes,
+                                _stream(stream)), "flux_block_fwd")
+
+
+def flux_single_fwd(dims: flux_dims, w: flux_single_weights, x, x_bstride: int, vec, rope, workspace,
+                    workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_single_fwd(C.byref(dims), C.byref(w), ptr(x), x_bstride, ptr(vec), ptr(rope), ptr(workspace),
+                                 workspace_bytes, _stream(stream)), "flux_single_fwd")
+
+
+def flux_rf_workspace_bytes(batch: int, n_per_sample: int) -> int:
+    return lib().flux_rf_workspace_bytes(batch, n_per_sample)
+
+
+def rf_noise_loss(batch: int, n_per_sample: int, z0, z1, t, z_t=None, v_target=None, v_pred=None, loss=None,
+                  loss_per_sample=None, workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    a = rf_args()
+    a.batch, a.n_per_sample = batch, n_per_sample
+    a.z0, a.z1, a.t, a.z_t, a.v_target, a.v_pred = map(ptr, (z0, z1, t, z_t, v_target, v_pred))
+    a.loss, a.loss_per_sample, a.workspace = map(ptr, (loss, loss_per_sample, workspace))
+    a.workspace_bytes = workspace_bytes
+    _check(lib().rf_noise_loss(C.byref(a), _stream(stream)), "rf_noise_loss")
+
+
+def flux_rope_table(ids, batch: int, seq: int, axes_dim, theta: float, table, stream=None) -> None:
+    ax = (C.c_int32 * 3)(*axes_dim)
+    _check(lib().flux_rope_table(ptr(ids), batch, seq, ax, theta, ptr(table), _stream(stream)), "flux_rope_table")
+
+
+def flux_embed_workspace_bytes(precision, batch, channels, height, width, hidden) -> int:
+    return lib().flux_embed_workspace_bytes(precision, batch, channels, height, width, hidden)
+
+
+def flux_embed_fwd(precision, batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim,
+                   w: flux_embed_weights, z_t, txt, t, y, x_img, img_bstride, x_txt, txt_bstride, vec, workspace,
+                   workspace_bytes, stream=None) -> None:
+    _check(lib().flux_embed_fwd(precision, batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim,
+                                C.byref(w), ptr(z_t), ptr(txt), ptr(t), ptr(y), ptr(x_img), img_bstride, ptr(x_txt),
+                                txt_bstride, ptr(vec), ptr(workspace), workspace_bytes, _stream(stream)),
+           "flux_embed_fwd")
+
+
+def flux_final_workspace_bytes(precision, batch, height, width, hidden) -> int:
+    return lib().flux_final_workspace_bytes(precision, batch, height, width, hidden)
+
+
+def flux_final_fwd(precision, batch, channels, height, width, hidden, eps, mod_w, mod_b, out_w, out_b, x_img,
+                   bstride, vec, v_pred, workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().flux_final_fwd(precision, batch, channels, height, width, hidden, eps, ptr(mod_w), ptr(mod_b),
+                                ptr(out_w), ptr(out_b), ptr(x_img), bstride, ptr(vec), ptr(v_pred), ptr(workspace),
+                                workspace_bytes, _stream(stream)), "flux_final_fwd")
+
+
+def flux_linear_fwd(precision, m, n, k, x, lda, w, b, y, ldy, stream=None) -> None:
+    _check(lib().flux_linear_fwd(precision, m, n, k, ptr(x), lda, ptr(w), ptr(b), ptr(y), ldy, _stream(stream)),
+           "flux_linear_fwd")
+
+
+def flux_attention_workspace_bytes(precision, batch, seq, heads, head_dim) -> int:
+    return lib().flux_attention_workspace_bytes(precision, batch, seq, heads, head_dim)
+
+
+def flux_attention_fwd(precision, batch, seq, heads, head_dim, q, k, v, ld_in, o, ld_out, workspace,
+                       workspace_bytes, stream=None) -> None:
+    _check(lib().flux_attention_fwd(precision, batch, seq, heads, head_dim, ptr(q), ptr(k), ptr(v), ld_in, ptr(o),
+                                    ld_out, ptr(workspace), workspace_bytes, _stream(stream)), "flux_attention_fwd")
+
+
+def flux_timing_enable(on: bool) -> None:
+    _check(lib().flux_timing_enable(1 if on else 0), "flux_timing_enable")
+
+
+def flux_timing_read() -> Dict[str, tuple]:
+    """{class name: (total ms, launches)} of the launches since the last read."""
+    L = lib()
+    n = L.flux_timing_classes()
+    ms = (C.c_double * n)()
+    cnt = (C.c_int64 * n)()
+    _check(L.flux_timing_read(ms, cnt, n), "flux_timing_read")
+    return {L.flux_timing_class_name(i).decode(): (ms[i], cnt[i]) for i in range(n)}

@@ -1,0 +1,143 @@
+"""Device-side composition of the Flux forward over the libflux C ABI.
+
+This module only uploads arrays, allocates device buffers with torch and calls
+the library in order ("Flux architecture deep dive", Data flow / Complete
+forward pass and Training data flow): rf noising -> input embeddings and
+conditioning vector -> double blocks -> single blocks over the joint sequence
+-> output head -> velocity MSE.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import flux as F
+from . import synth
+
+
+def device_array(a: np.ndarray, bf16: bool, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    t = t.to(device)
+    return t.to(torch.bfloat16) if bf16 else t
+
+
+def upload_weights(w: Dict[str, np.ndarray], bf16: bool, device="cuda") -> Dict[str, torch.Tensor]:
+    """Linear weights/biases in the operand type; RMSNorm scales stay float."""
+    out = {}
+    for k, v in w.items():
+        is_norm = k.endswith("_norm") or k in ("q_norm", "k_norm")
+        out[k] = device_array(v, bf16 and not is_norm, device)
+    return out
+
+
+def precision_of(wl: synth.Workload) -> int:
+    return F.FLUX_PREC_F32 if wl.precision == "f32" else F.FLUX_PREC_BF16
+
+
+class Workspace:
+    """One device scratch buffer, grown on demand (256-byte aligned)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+class BlockStack:
+    """Double and single blocks of one workload, weights resident on the GPU."""
+
+    def __init__(self, wl: synth.Workload, double_ws: List[Dict[str, np.ndarray]],
+                 single_ws: List[Dict[str, np.ndarray]], device="cuda"):
+        self.wl = wl
+        self.bf16 = wl.precision != "f32"
+        self.dims = F.dims_for(wl)
+        self.double = [upload_weights(w, self.bf16, device) for w in double_ws]
+        self.single = [upload_weights(w, self.bf16, device) for w in single_ws]
+        self._dstructs = [(F.stream_weights(w, "img"), F.stream_weights(w, "txt")) for w in self.double]
+        self._sstructs = [F.single_weights(w) for w in self.single]
+        self.ws = Workspace(device)
+        self.ws_bytes = max(F.flux_workspace_bytes(self.dims, 0), F.flux_workspace_bytes(self.dims, 1))
+        self.device = device
+
+    def rope_table(self, ids: torch.Tensor) -> torch.Tensor:
+        wl = self.wl
+        B, L = ids.shape[0], ids.shape[1]
+        table = torch.empty((B, L, wl.head_dim // 2, 2), dtype=torch.float32, device=self.device)
+        F.flux_rope_table(ids, B, L, wl.axes_dim, wl.theta, table)
+        return table
+
+    def double_fwd(self, i: int, x: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor) -> None:
+        """x: joint [B, L, D] float residual (image rows then text rows), in place."""
+        wl = self.wl
+        L = wl.seq
+        iw, tw = self._dstructs[i]
+        ws = self.ws.get(self.ws_bytes)
+        txt = x[:, wl.l_img:] if wl.l_txt > 0 else None
+        F.flux_block_fwd(self.dims, iw, tw, x, L * wl.hidden, txt, L * wl.hidden, vec, rope, ws, ws.numel())
+
+    def single_fwd(self, i: int, x: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor) -> None:
+        wl = self.wl
+        ws = self.ws.get(self.ws_bytes)
+        F.flux_single_fwd(self.dims, self._sstructs[i], x, wl.seq * wl.hidden, vec, rope, ws, ws.numel())
+
+    def blocks_fwd(self, x: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor) -> None:
+        for i in range(len(self.double)):
+            self.double_fwd(i, x, vec, rope)
+        for i in range(len(self.single)):
+            self.single_fwd(i, x, vec, rope)
+
+
+class FluxModel(BlockStack):
+    """Whole forward + rectified-flow loss of a workload."""
+
+    def __init__(self, wl: synth.Workload, emb_w: Dict[str, np.ndarray], double_ws, single_ws, device="cuda"):
+        super().__init__(wl, double_ws, single_ws, device)
+        self.emb = upload_weights(emb_w, self.bf16, device)
+        self._estruct = F.embed_weights(self.emb)
+        p = precision_of(wl)
+        self.ws_bytes = max(self.ws_bytes,
+                            F.flux_embed_workspace_bytes(p, wl.batch, wl.latent_ch, wl.img_h, wl.img_w, wl.hidden),
+                            F.flux_final_workspace_bytes(p, wl.batch, wl.img_h, wl.img_w, wl.hidden),
+                            F.flux_rf_workspace_bytes(wl.batch, wl.latent_ch * wl.l_img))
+
+    def forward_loss(self, z0, z1, t, txt, y, ids, out: Optional[Dict[str, torch.Tensor]] = None):
+        """Noise, forward, loss.  Returns a dict of device tensors: z_t, v_target,
+        x (joint residual after the blocks), vec, v_pred, loss, loss_per_sample."""
+        wl, dev = self.wl, self.device
+        B, C, D = wl.batch, wl.latent_ch, wl.hidden
+        n = C * wl.l_img
+        p = precision_of(wl)
+        o = out if out is not None else {}
+        if not o:
+            f32 = dict(dtype=torch.float32, device=dev)
+            o["z_t"] = torch.empty((B, C, wl.img_h, wl.img_w), **f32)
+            o["v_target"] = torch.empty_like(o["z_t"])
+            o["x"] = torch.empty((B, wl.seq, D), **f32)
+            o["vec"] = torch.empty((B, D), **f32)
+            o["v_pred"] = torch.empty_like(o["z_t"])
+            o["loss"] = torch.empty((1,), **f32)
+            o["loss_per_sample"] = torch.empty((B,), **f32)
+            o["rope"] = self.rope_table(ids)
+        ws = self.ws.get(self.ws_bytes)
+        F.rf_noise_loss(B, n, z0, z1, t, z_t=o["z_t"], v_target=o["v_target"])
+        x = o["x"]
+        has_txt_in = "txt_in.w" in self.emb
+        if not has_txt_in:
+            x[:, wl.l_img:].copy_(txt)   # text enters at hidden width: a copy into the joint buffer
+        F.flux_embed_fwd(p, B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
+                         wl.vec_in_dim or 0, self._estruct, o["z_t"], txt if has_txt_in else None, t,
+                         y, x, wl.seq * D, x[:, wl.l_img:] if has_txt_in else None, wl.seq * D, o["vec"], ws,
+                         ws.numel())
+        self.blocks_fwd(x, o["vec"], o["rope"])
+        F.flux_final_fwd(p, B, C, wl.img_h, wl.img_w, D, wl.eps, self.emb["final_mod.w"], self.emb["final_mod.b"],
+                         self.emb["final_out.w"], self.emb["final_out.b"], x, wl.seq * D, o["vec"], o["v_pred"], ws,
+                         ws.numel())
+        F.rf_noise_loss(B, n, z0, z1, t, v_pred=o["v_pred"], loss=o["loss"], loss_per_sample=o["loss_per_sample"],
+                        workspace=ws, workspace_bytes=ws.numel())
+        return o

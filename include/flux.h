@@ -1,0 +1,275 @@
+/*
+ * libflux -- Flux MMDiT block forward and rectified-flow objective on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI.
+ *
+ * What the library computes is defined by two pages:
+ *   "Flux architecture deep dive" (sections Flow matching framework, Model
+ *     components, Mathematical formulation, Implementation details), and
+ *   "Flux model API reference" (FluxConfig key parameters, AdaLN, RMSNorm,
+ *     EmbedND, JointSelfAttention, MMDiTLayer, FluxSingleTransformerBlock,
+ *     apply_flow_matching_noise, compute_flow_matching_loss).
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers unless stated otherwise; the
+ *    caller allocates and owns every buffer (the library never allocates,
+ *    frees or synchronises).  Struct arguments themselves live in host memory
+ *    and are read before the call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it in order; results are ready when the stream is.
+ *  - Token layout is batch-major [B, L, D]; within a projection the feature
+ *    index is head * head_dim + d.  The joint sequence is image rows first,
+ *    then text rows.
+ *  - Element types: with FLUX_PREC_F32 every weight and activation operand is
+ *    float; with FLUX_PREC_BF16 weights and biases are bf16 (raw 16-bit
+ *    patterns) and the GEMM/attention operands are bf16 with fp32
+ *    accumulation.  Residual streams, modulation vectors, RMSNorm scales,
+ *    RoPE tables, latents and losses are always float.
+ *  - Errors: every argument is validated on the host BEFORE anything is
+ *    enqueued.  A failed check returns a non-zero flux_status and enqueues
+ *    nothing; flux_last_error() then returns a thread-local message.  A HIP
+ *    launch error returns FLUX_ERR_HIP.  Faults inside kernels surface at the
+ *    caller's next synchronisation.
+ *  - Pointers passed as tensors must be 16-byte aligned; row strides are in
+ *    elements.
+ */
+#ifndef FLUX_H
+#define FLUX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLUX_OK = 0,
+  FLUX_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment, aliasing */
+  FLUX_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. head_dim not 64/128) */
+  FLUX_ERR_WORKSPACE_TOO_SMALL = 3,
+  FLUX_ERR_HIP = 4                 /* a HIP runtime call failed */
+} flux_status;
+
+typedef enum {
+  FLUX_PREC_F32 = 0,
+  FLUX_PREC_BF16 = 1
+} flux_precision;
+
+/* Shapes of one block call ("Flux model API reference", FluxConfig). */
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t l_img;          /* image tokens per sample (H*W of the latent), >= 1 */
+  int32_t l_txt;          /* text tokens per sample, >= 0; joint L = l_img + l_txt */
+  int32_t hidden;         /* D == heads * head_dim, a multiple of 256, at most 4096 */
+  int32_t heads;
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t mlp_hidden;     /* F (4 * D for Flux), multiple of 64 */
+  int32_t axes_dim[3];    /* 3D RoPE widths, even, sum == head_dim; Flux: 16, 56, 56 */
+  float theta;            /* RoPE base, 10000 */
+  float eps;              /* LayerNorm and RMSNorm epsilon, 1e-6 */
+  int32_t precision;      /* flux_precision */
+} flux_dims;
+
+/* Weights of one stream of a double block (torch Linear layout W [out, in]).
+ * Element type of W and b follows dims.precision; q_norm / k_norm are float. */
+typedef struct {
+  const void* mod_w;  const void* mod_b;    /* [6D, D], [6D]: shift1|scale1|gate1|shift2|scale2|gate2 */
+  const void* qkv_w;  const void* qkv_b;    /* [3D, D], [3D]: rows q|k|v */
+  const float* q_norm; const float* k_norm; /* [head_dim] RMSNorm scales, shared by the heads */
+  const void* proj_w; const void* proj_b;   /* [D, D], [D] */
+  const void* fc1_w;  const void* fc1_b;    /* [F, D], [F] */
+  const void* fc2_w;  const void* fc2_b;    /* [D, F], [D] */
+} flux_stream_weights;
+
+/* Weights of a single block, fused parallel form. */
+typedef struct {
+  const void* mod_w;  const void* mod_b;    /* [3D, D], [3D]: shift|scale|gate */
+  const void* lin1_w; const void* lin1_b;   /* [3D+F, D], [3D+F]: rows q|k|v|mlp_in */
+  const float* q_norm; const float* k_norm; /* [head_dim] */
+  const void* lin2_w; const void* lin2_b;   /* [D, D+F], [D]: input columns attn|gelu(mlp_in) */
+} flux_single_weights;
+
+/*
+ * flux_block_fwd -- one MMDiT double block ("Flux architecture deep dive",
+ * Model components / MMDiT layer (double block); "Flux model API reference",
+ * MMDiTLayer and JointSelfAttention).
+ *
+ * Per stream s (image, text): (shift1, scale1, gate1, shift2, scale2, gate2) =
+ * Linear_mod,s(SiLU(vec)); h = LayerNorm(x_s)(1 + scale1) + shift1 (no affine,
+ * eps); q|k|v = Linear_qkv,s(h); q, k <- RMSNorm over head_dim with the
+ * stream's scales.  Joint softmax attention over the image rows followed by
+ * the text rows, 3D RoPE applied to q and k, scale 1/sqrt(head_dim), no mask.
+ * x_s += gate1 * Linear_proj,s(O_s); x_s += gate2 * fc2_s(GELU(fc1_s(
+ * LayerNorm(x_s)(1 + scale2) + shift2))).
+ *
+ *  img   [B, l_img, D] float, sample b at img + b*img_bstride; updated in place.
+ *  txt   [B, l_txt, D] float, sample b at txt + b*txt_bstride; updated in place
+ *        (may be NULL when l_txt == 0).  img and txt rows must not overlap.
+ *  vec   [B, D] float conditioning vector.
+ *  rope  [B, L, head_dim/2, 2] float (cos, sin) per token and pair, image
+ *        rows first, as written by flux_rope_table.
+ *  workspace  device scratch of at least flux_workspace_bytes(dims, 0) bytes,
+ *        256-byte aligned; its content on entry is ignored.
+ */
+flux_status flux_block_fwd(const flux_dims* dims, const flux_stream_weights* img_w,
+                           const flux_stream_weights* txt_w, float* img, int64_t img_bstride,
+                           float* txt, int64_t txt_bstride, const float* vec, const float* rope,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * flux_single_fwd -- one single-stream block over the joint sequence
+ * ("Flux architecture deep dive", Model components / Flux single block, in the
+ * fused parallel form: one adaLN, one linear D -> 3D+F, attention and GELU
+ * side by side, one linear D+F -> D, one gated residual).
+ *
+ * (shift, scale, gate) = Linear_mod(SiLU(vec)); h = LayerNorm(x)(1+scale)+shift;
+ * q|k|v|m = Linear1(h); q, k <- RMSNorm, RoPE; O = softmax attention;
+ * x += gate * Linear2([O | GELU(m)]).
+ *
+ *  x     [B, L, D] float (image rows then text rows), sample b at x + b*x_bstride;
+ *        updated in place.
+ *  vec, rope, workspace as for flux_block_fwd (workspace op 1).
+ */
+flux_status flux_single_fwd(const flux_dims* dims, const flux_single_weights* w, float* x,
+                            int64_t x_bstride, const float* vec, const float* rope,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rf_noise_loss -- rectified-flow noising and velocity MSE ("Flux architecture
+ * deep dive", Flow matching framework and Mathematical formulation / Flow
+ * matching objective; "Flux model API reference", apply_flow_matching_noise
+ * and compute_flow_matching_loss).
+ *
+ *  z_t = (1 - t_b) z0 + t_b z1, evaluated as two rounded fp32 products and one
+ *        rounded sum (so t = 0 and t = 1 reproduce z0 and z1 exactly);
+ *  v_target = z1 - z0;
+ *  loss = mean over all B*n elements of (v_pred - (z1 - z0))^2, accumulated in
+ *        fp64 in a fixed order (bitwise reproducible), stored as float;
+ *  loss_per_sample[b] = the same mean over sample b.
+ * Outputs that are NULL are skipped; the loss outputs need v_pred.  z_t and
+ * v_target must not alias z0, z1 or each other.
+ */
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int64_t n_per_sample;       /* C*H*W >= 1 */
+  const float* z0;            /* [B, n] clean latents */
+  const float* z1;            /* [B, n] noise */
+  const float* t;             /* [B] flow time in [0, 1] (not checked on the device) */
+  float* z_t;                 /* [B, n] out, nullable */
+  float* v_target;            /* [B, n] out, nullable */
+  const float* v_pred;        /* [B, n] in, nullable (needed for the loss) */
+  float* loss;                /* [1] out, nullable */
+  float* loss_per_sample;     /* [B] out, nullable */
+  void* workspace;            /* >= flux_rf_workspace_bytes(batch, n) bytes when a loss is asked */
+  size_t workspace_bytes;
+} rf_args;
+
+flux_status rf_noise_loss(const rf_args* args, void* stream);
+
+/*
+ * flux_rope_table -- 3D RoPE angles ("Flux architecture deep dive", 3D RoPE
+ * mathematics; "Flux model API reference", EmbedND with rotary_interleaved).
+ * For token position ids (p0, p1, p2) and axis a of width d_a (axes in order,
+ * contiguous head-dim slices), pair j < d_a/2 turns by p_a * theta^(-2j/d_a);
+ * interleaved pairs (2m, 2m+1).  Angles are evaluated in fp64 and stored as
+ * float cos/sin.
+ *  ids   [B, L, 3] float position ids;  table [B, L, head_dim/2, 2] float out.
+ */
+flux_status flux_rope_table(const float* ids, int32_t batch, int32_t seq, const int32_t axes_dim[3],
+                            float theta, float* table, void* stream);
+
+/*
+ * flux_embed_fwd -- inputs of the transformer ("Flux architecture deep dive",
+ * Model components / Input embeddings and Conditioning; Implementation
+ * details / Memory layout):
+ *   x_img = Linear_img_in(patchify(z_t)), patchify [B,C,H,W] -> [B,H*W,C];
+ *   x_txt = Linear_txt_in(txt) if txt_in_w is not NULL, else not written;
+ *   vec   = Linear(SiLU(Linear(sinusoid(t)))) [+ Linear(SiLU(Linear(y)))],
+ *   sinusoid(t) = [cos(1000 t f_j) | sin(1000 t f_j)], f_j = 1e4^(-j/half),
+ *   j < half = time_dim/2.
+ * Element type of the weights and of txt follows `precision`.
+ */
+typedef struct {
+  const void* img_in_w;  const void* img_in_b;     /* [D, C], [D] */
+  const void* txt_in_w;  const void* txt_in_b;     /* [D, ctx], [D] or NULL */
+  const void* time_in1_w; const void* time_in1_b;  /* [D, time_dim], [D] */
+  const void* time_in2_w; const void* time_in2_b;  /* [D, D], [D] */
+  const void* vector_in1_w; const void* vector_in1_b;  /* [D, y_dim], [D] or NULL */
+  const void* vector_in2_w; const void* vector_in2_b;  /* [D, D], [D] or NULL */
+} flux_embed_weights;
+
+flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
+                           int32_t l_txt, int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
+                           const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
+                           const float* y, float* x_img, int64_t img_bstride, float* x_txt,
+                           int64_t txt_bstride, float* vec, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * flux_final_fwd -- output head ("Flux architecture deep dive", Model
+ * components / Output processing): (shift, scale) = Linear_mod(SiLU(vec));
+ * tok = Linear_out(LayerNorm(x_img)(1 + scale) + shift) [B, H*W, C];
+ * v_pred[b, c, h, w] = tok[b, h*W + w, c].
+ *  x_img [B, H*W, D] float, sample b at x_img + b*bstride;  v_pred [B, C, H, W] float out.
+ */
+flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
+                           int32_t hidden, float eps, const void* mod_w, const void* mod_b,
+                           const void* out_w, const void* out_b, const float* x_img, int64_t bstride,
+                           const float* vec, float* v_pred, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * flux_linear_fwd -- y = x W^T + b, the linear layer used throughout the
+ * blocks, exposed on its own.  x [M, K] (row stride lda), W [N, K], b [N] or
+ * NULL, all of element type `precision`; y [M, N] float (row stride ldy).
+ * K must be a multiple of 64 for bf16.
+ */
+flux_status flux_linear_fwd(int32_t precision, int32_t m, int32_t n, int32_t k, const void* x, int64_t lda,
+                            const void* w, const void* b, float* y, int64_t ldy, void* stream);
+
+/*
+ * flux_attention_fwd -- softmax(q k^T / sqrt(head_dim)) v per head, no mask
+ * ("Flux architecture deep dive", Implementation details / Attention
+ * implementation), exposed on its own (no RMSNorm, no RoPE).
+ *  q, k, v [B, L, heads*head_dim] of element type `precision`, row stride ld_in;
+ *  o [B, L, heads*head_dim] same type, row stride ld_out.
+ *  workspace >= flux_attention_workspace_bytes(...) bytes.
+ */
+flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, int32_t heads, int32_t head_dim,
+                               const void* q, const void* k, const void* v, int64_t ld_in, void* o,
+                               int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace sizes (bytes).  op: 0 double block, 1 single block. */
+size_t flux_workspace_bytes(const flux_dims* dims, int32_t op);
+size_t flux_rf_workspace_bytes(int32_t batch, int64_t n_per_sample);
+size_t flux_embed_workspace_bytes(int32_t precision, int32_t batch, int32_t channels, int32_t height,
+                                  int32_t width, int32_t hidden);
+size_t flux_final_workspace_bytes(int32_t precision, int32_t batch, int32_t height, int32_t width,
+                                  int32_t hidden);
+size_t flux_attention_workspace_bytes(int32_t precision, int32_t batch, int32_t seq, int32_t heads,
+                                      int32_t head_dim);
+
+/*
+ * Kernel timing (diagnostics, off by default).  While enabled, each kernel
+ * launch made by the library is bracketed by two hipEvents recorded on that
+ * launch's stream.  flux_timing_read waits for the recorded events, writes
+ * the summed milliseconds and launch counts of the first n kernel classes
+ * (n <= flux_timing_classes(); either array may be NULL) and forgets them.
+ * flux_timing_class_name names a class ("" when out of range).  The hook is
+ * process-wide and serialised by a lock.
+ */
+flux_status flux_timing_enable(int32_t on);
+int32_t flux_timing_classes(void);
+const char* flux_timing_class_name(int32_t cls);
+flux_status flux_timing_read(double* ms, int64_t* launches, int32_t n);
+
+/* Static text for a status code; thread-local detail of the last failure on
+ * this thread ("" when none). */
+const char* flux_status_string(flux_status s);
+const char* flux_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLUX_H */

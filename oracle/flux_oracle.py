@@ -192,7 +192,7 @@ def attention_probs(q, k) -> np.ndarray:
     -> [B, H, Lq, Lk]."""
     q, k = f64(q), f64(k)
     dh = q.shape[-1]
-    s = np.einsum("bqhd,bkhd->bhqk", q, k) / np.sqrt(dh)
+    s = np.matmul(q.transpose(0, 2, 1, 3), k.transpose(0, 2, 3, 1)) / np.sqrt(dh)
     s = s - s.max(axis=-1, keepdims=True)
     e = np.exp(s)
     return e / e.sum(axis=-1, keepdims=True)
@@ -201,9 +201,9 @@ def attention_probs(q, k) -> np.ndarray:
 def attention(q, k, v) -> np.ndarray:
     """softmax(q k^T / sqrt(Dh)) v, heads merged back: -> [B, Lq, H * Dh]."""
     a = attention_probs(q, k)
-    o = np.einsum("bhqk,bkhd->bqhd", a, f64(v))
+    o = np.matmul(a, f64(v).transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)
     b_, lq, h, dh = o.shape
-    return o.reshape(b_, lq, h * dh)
+    return np.ascontiguousarray(o).reshape(b_, lq, h * dh)
 
 
 def _heads(y: np.ndarray, heads: int) -> np.ndarray:

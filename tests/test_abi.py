@@ -1,0 +1,139 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every symbol
+include/flux.h declares, and rejects bad arguments on the host with the
+documented status codes before anything is enqueued (no GPU is touched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from flow_matching_diffusion_amd import flux as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flux.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(F.LIB_PATH), reason="libflux.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:flux_status|size_t|int32_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 15
+    L = F.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(F.EXPORTED)
+
+
+def test_status_strings():
+    L = F.lib()
+    assert L.flux_status_string(0) == b"ok"
+    assert L.flux_status_string(3) == b"workspace too small"
+
+
+def _dims(**kw):
+    base = dict(batch=1, l_img=64, l_txt=16, hidden=256, heads=4, head_dim=64, mlp_hidden=1024, axes_dim=(8, 28, 28),
+                precision=F.FLUX_PREC_BF16)
+    base.update(kw)
+    return F.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=256, heads=8, head_dim=32, axes_dim=(8, 12, 12)), F.FLUX_ERR_UNSUPPORTED),
+    (dict(hidden=300, heads=4, head_dim=75), F.FLUX_ERR_UNSUPPORTED),
+    (dict(hidden=256, heads=2, head_dim=64), F.FLUX_ERR_INVALID_ARGUMENT),
+    (dict(axes_dim=(8, 28, 30)), F.FLUX_ERR_INVALID_ARGUMENT),
+    (dict(axes_dim=(7, 29, 28)), F.FLUX_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), F.FLUX_ERR_INVALID_ARGUMENT),
+    (dict(l_img=0), F.FLUX_ERR_INVALID_ARGUMENT),
+    (dict(mlp_hidden=100), F.FLUX_ERR_UNSUPPORTED),
+    (dict(precision=7), F.FLUX_ERR_INVALID_ARGUMENT),
+])
+def test_bad_dims_rejected(kw, status):
+    L = F.lib()
+    d = _dims(**kw)
+    assert L.flux_block_fwd(C.byref(d), None, None, None, 0, None, 0, None, None, None, 0, None) == status
+    assert L.flux_last_error()
+    assert L.flux_single_fwd(C.byref(d), None, None, 0, None, None, None, 0, None) == status
+    assert F.flux_workspace_bytes(d, 0) == 0
+
+
+def test_null_and_misaligned_pointers_rejected():
+    L = F.lib()
+    d = _dims()
+    fake = 1 << 40                          # never dereferenced: validation fails first
+    w = F.flux_stream_weights(*([fake] * 12))
+    ws_need = F.flux_workspace_bytes(d, 0)
+    assert ws_need > 0
+    # missing residual pointer
+    s = L.flux_block_fwd(C.byref(d), C.byref(w), C.byref(w), None, 64 * 256, fake, 16 * 256, fake, fake, fake,
+                         ws_need, None)
+    assert s == F.FLUX_ERR_INVALID_ARGUMENT
+    # misaligned residual
+    s = L.flux_block_fwd(C.byref(d), C.byref(w), C.byref(w), fake + 4, 64 * 256, fake, 16 * 256, fake, fake, fake,
+                         ws_need, None)
+    assert s == F.FLUX_ERR_INVALID_ARGUMENT and b"aligned" in L.flux_last_error()
+    # batch stride smaller than a sample
+    s = L.flux_block_fwd(C.byref(d), C.byref(w), C.byref(w), fake, 10, fake, 16 * 256, fake, fake, fake, ws_need,
+                         None)
+    assert s == F.FLUX_ERR_INVALID_ARGUMENT
+    # a NULL weight
+    w2 = F.flux_stream_weights(*([fake] * 12))
+    w2.fc2_b = None
+    s = L.flux_block_fwd(C.byref(d), C.byref(w2), C.byref(w), fake, 64 * 256, fake, 16 * 256, fake, fake, fake,
+                         ws_need, None)
+    assert s == F.FLUX_ERR_INVALID_ARGUMENT and b"NULL" in L.flux_last_error()
+    # workspace too small / misaligned
+    s = L.flux_block_fwd(C.byref(d), C.byref(w), C.byref(w), fake, 64 * 256, fake, 16 * 256, fake, fake, fake,
+                         ws_need - 1, None)
+    assert s == F.FLUX_ERR_WORKSPACE_TOO_SMALL
+    s = L.flux_block_fwd(C.byref(d), C.byref(w), C.byref(w), fake, 64 * 256, fake, 16 * 256, fake, fake, fake + 16,
+                         ws_need, None)
+    assert s == F.FLUX_ERR_INVALID_ARGUMENT
+
+
+def test_rf_argument_checks():
+    L = F.lib()
+    fake = 1 << 40
+    a = F.rf_args()
+    a.batch, a.n_per_sample = 2, 1000
+    assert L.rf_noise_loss(C.byref(a), None) == F.FLUX_ERR_INVALID_ARGUMENT      # z0/z1/t missing
+    a.z0, a.z1, a.t = fake, fake + 8000, fake + 16000
+    a.z_t = fake + 4000                                                         # overlaps z0
+    assert L.rf_noise_loss(C.byref(a), None) == F.FLUX_ERR_INVALID_ARGUMENT
+    a.z_t = None
+    a.loss = fake + 1 << 20                                                     # loss without v_pred
+    assert L.rf_noise_loss(C.byref(a), None) == F.FLUX_ERR_INVALID_ARGUMENT
+    a.v_pred = fake + (2 << 20)
+    a.workspace, a.workspace_bytes = fake + (4 << 20), 8
+    assert L.rf_noise_loss(C.byref(a), None) == F.FLUX_ERR_WORKSPACE_TOO_SMALL
+    a.batch = 0
+    assert L.rf_noise_loss(C.byref(a), None) == F.FLUX_ERR_INVALID_ARGUMENT
+
+
+def test_linear_and_attention_argument_checks():
+    L = F.lib()
+    fake = 1 << 40
+    assert L.flux_linear_fwd(F.FLUX_PREC_BF16, 16, 64, 100, fake, 100, fake, None, fake, 64, None) == \
+        F.FLUX_ERR_UNSUPPORTED                                                  # bf16 K % 64
+    assert L.flux_linear_fwd(F.FLUX_PREC_BF16, 16, 66, 64, fake, 64, fake, None, fake, 68, None) == \
+        F.FLUX_ERR_UNSUPPORTED                                                  # N % 4
+    assert L.flux_attention_fwd(F.FLUX_PREC_BF16, 1, 80, 4, 96, fake, fake, fake, 384, fake, 384, fake, 1 << 30,
+                                None) == F.FLUX_ERR_UNSUPPORTED                # head_dim 96
+    need = F.flux_attention_workspace_bytes(F.FLUX_PREC_BF16, 1, 80, 4, 64)
+    assert L.flux_attention_fwd(F.FLUX_PREC_BF16, 1, 80, 4, 64, fake, fake, fake, 256, fake, 256, fake, need - 1,
+                                None) == F.FLUX_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_sizes_grow_with_problem():
+    small = F.flux_workspace_bytes(_dims(), 0)
+    big = F.flux_workspace_bytes(_dims(batch=4), 0)
+    assert 0 < small < big
+    assert F.flux_workspace_bytes(_dims(), 1) > 0
+    assert F.flux_workspace_bytes(_dims(), 2) == 0
+    assert F.flux_rf_workspace_bytes(2, 1 << 20) >= 2 * 8
