@@ -34,22 +34,18 @@ PEAK_HBM_GBS = 8000.0
 
 
 def algorithmic_work(wl):
-    """FLOPs (and bytes) the method must do per step, per kernel class."""
+    """FLOPs the method must do per step ("Flux architecture deep dive", MMDiT
+    layer and Flux single block): every linear 2*M*N*K, attention 4*B*H*L^2*Dh."""
     B, L, Li, D, F, H, dh, C = wl.batch, wl.seq, wl.l_img, wl.hidden, wl.mlp_hidden, wl.heads, wl.head_dim, wl.latent_ch
     T = B * L
     gemm_double = 2 * T * D * (3 * D + D + F + F)         # qkv, proj, fc1, fc2 over both streams
     gemm_single = 2 * T * D * (3 * D + F) + 2 * T * (D + F) * D
     attn = 4 * B * H * L * L * dh                         # QK^T and PV, no mask
     small_gemm = 2 * B * Li * C * D + 2 * B * Li * D * C  # image embedding, output linear
-    gemv_bytes = 2 * (2 * 6 * D * D + 3 * D * D + 2 * D * D + 256 * D + D * D)
-    ln_bytes = (3 * T + B * Li) * (4 * D + 2 * D)
     return {
-        "gemm_bf16_256x256": {"flops": gemm_double + gemm_single, "launches": 6},
-        "attention": {"flops": 2 * attn, "launches": 2},
-        "gemm_bf16_128x128": {"flops": small_gemm, "launches": 2},
-        "gemv": {"bytes": gemv_bytes},
-        "ln_modulate": {"bytes": ln_bytes},
-        "total_flops": gemm_double + gemm_single + 2 * attn + small_gemm,
+        "gemm": gemm_double + gemm_single + small_gemm,
+        "attention": 2 * attn,
+        "total_flops": gemm_double + gemm_single + small_gemm + 2 * attn,
         "double_block_flops": gemm_double + attn,
     }
 
@@ -142,25 +138,33 @@ def main() -> int:
     assert np.isfinite(loss), "non-finite loss"
 
     work = algorithmic_work(wl)
-    kt = {k: {"ms_per_launch": (v[0] / v[1]) if v[1] else 0.0, "launches_per_step": v[1] / args.steps,
-              "ms_per_step": v[0] / args.steps} for k, v in kernels.items() if v[1]}
+    kt = {}
+    for k, (ms, n, w) in kernels.items():
+        if not n:
+            continue
+        compute = k.startswith("gemm") or k == "attention"
+        kt[k] = {"ms_per_launch": ms / n, "launches_per_step": n / args.steps, "ms_per_step": ms / args.steps,
+                 ("tflops" if compute else "gbs"): (w / (ms * 1e-3) / (1e12 if compute else 1e9)) if ms > 0 else 0.0,
+                 ("flops_per_launch" if compute else "bytes_per_launch"): w / n}
+    # the launch-reported work must add up to the method's algorithmic FLOPs
+    gemm_w = sum(v[2] for k, v in kernels.items() if k.startswith("gemm")) / args.steps
+    attn_w = kernels.get("attention", (0, 0, 0.0))[2] / args.steps
+    assert abs(gemm_w - work["gemm"]) <= 1e-6 * work["gemm"], (gemm_w, work["gemm"])
+    assert abs(attn_w - work["attention"]) <= 1e-6 * work["attention"], (attn_w, work["attention"])
     dom = max(kt, key=lambda k: kt[k]["ms_per_step"])
-    roof = None
-    if "flops" in work.get(dom, {}):
-        per_launch = work[dom]["flops"] / work[dom]["launches"]
-        achieved = per_launch / (kt[dom]["ms_per_launch"] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "flops_per_launch": per_launch, "ms_per_launch": round(kt[dom]["ms_per_launch"], 5)}
-    elif "bytes" in work.get(dom, {}):
-        achieved = work[dom]["bytes"] / (kt[dom]["ms_per_step"] * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    d = kt[dom]
+    if "tflops" in d:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(d["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": d["flops_per_launch"], "ms_per_launch": round(d["ms_per_launch"], 5)}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(d["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                "bytes_per_launch": d["bytes_per_launch"], "ms_per_launch": round(d["ms_per_launch"], 5)}
     attn = kt.get("attention")
-    attn_tflops = (work["attention"]["flops"] / work["attention"]["launches"] / (attn["ms_per_launch"] * 1e-3) / 1e12
-                   if attn else None)
-    gemm = kt.get("gemm_bf16_256x256")
-    gemm_tflops = (work["gemm_bf16_256x256"]["flops"] / (gemm["ms_per_step"] * 1e-3) / 1e12 if gemm else None)
+    attn_tflops = attn["tflops"] if attn else None
+    gemm_ms = sum(v["ms_per_step"] for k, v in kt.items() if k.startswith("gemm"))
+    gemm_tflops = work["gemm"] / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
 
     rec = {
         "metric": METRIC,
@@ -182,9 +186,9 @@ def main() -> int:
         "roofline": roof,
         "attention_tflops": round(attn_tflops, 2) if attn_tflops else None,
         "attention_frac_of_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
-        "block_gemm_tflops": round(gemm_tflops, 2) if gemm_tflops else None,
+        "gemm_tflops": round(gemm_tflops, 2) if gemm_tflops else None,
         "step_tflops": round(work["total_flops"] / (ms_step * 1e-3) / 1e12, 2),
-        "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in kt.items()},
+        "kernels": {k: {kk: (round(vv, 5) if vv < 1e6 else vv) for kk, vv in v.items()} for k, v in kt.items()},
         "wall_s": round(wall, 3),
         "loss": loss,
     }

@@ -248,6 +248,11 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   if ((s = check_workspace(workspace, workspace_bytes, need.bytes)) != FLUX_OK) return s;
   const BlockWs w = block_ws(d, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // element types: fp32 workloads use float everywhere; bf16 workloads run the
+  // linears on fp16 activations (bf16 weights converted in LDS) and attention
+  // on bf16 q, k, v
+  const bool bf = dt == kBF16;
+  const int act = bf ? kF16 : kF32, qkv_t = bf ? kBF16 : kF32;
   const int ns = Lt > 0 ? 2 : 1;
   const flux_stream_weights* sw[2] = {iw, tw};
   float* xs[2] = {img, txt};
@@ -277,7 +282,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
       a.s[i].mod_bstride = 6 * D;
       a.s[i].rows = (int32_t)(B * seg[i]);
     }
-    return launch_ln_mod(a, dt, st);
+    return launch_ln_mod(a, act, st);
   };
   // 2. h = LN(x)(1 + scale1) + shift1
   FLUX_HIP(ln_mod(0), "LayerNorm-modulate (attention)");
@@ -289,7 +294,8 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->qkv_w, sw[i]->qkv_b,
                           (int)(B * seg[i]), (int)(3 * D), (int)D, kEpiStore, elem_ptr(w.big, off[i] * 3 * D, es),
                           rmap(L * 3 * D, 3 * D, seg[i]));
-  FLUX_HIP(launch_gemm(g, dt, st), "qkv GEMM");
+  for (int i = 0; i < ns; ++i) g.p[i].out0_dt = qkv_t;
+  FLUX_HIP(launch_gemm(g, act, st), "qkv GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE, head-major layout
   const int64_t Lp = seq_pad_of(L);
@@ -306,7 +312,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   pa.gk_txt = Lt > 0 ? tw->k_norm : iw->k_norm;
   pa.rope = rope; pa.eps = d->eps;
   pa.qh = w.qh; pa.kh = w.kh; pa.vt = w.vt;
-  FLUX_HIP(launch_prep(pa, dt, st), "q/k norm + RoPE");
+  FLUX_HIP(launch_prep(pa, qkv_t, st), "q/k norm + RoPE");
 
   // 5. joint attention over image|text rows
   AttnArgs aa{};
@@ -314,7 +320,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   aa.out = w.o; aa.out_bstride = L * D; aa.out_ld = D;
   aa.batch = (int)B; aa.seq = (int)L; aa.seq_pad = (int)Lp; aa.heads = d->heads; aa.head_dim = d->head_dim;
   aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d->head_dim));
-  FLUX_HIP(launch_attention(aa, dt, st), "joint attention");
+  FLUX_HIP(launch_attention(aa, qkv_t, act, st), "joint attention");
 
   // 6. x += gate1 * Linear_proj(O)
   for (int i = 0; i < ns; ++i) {
@@ -323,7 +329,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i].gate = w.mod[i] + 2 * D;
     g.p[i].gate_bstride = 6 * D;
   }
-  FLUX_HIP(launch_gemm(g, dt, st), "output projection GEMM");
+  FLUX_HIP(launch_gemm(g, act, st), "output projection GEMM");
 
   // 7. h = LN(x)(1 + scale2) + shift2
   FLUX_HIP(ln_mod(3), "LayerNorm-modulate (MLP)");
@@ -333,7 +339,8 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->fc1_w, sw[i]->fc1_b,
                           (int)(B * seg[i]), (int)F, (int)D, kEpiGelu, elem_ptr(w.big, off[i] * F, es),
                           rmap(L * F, F, seg[i]));
-  FLUX_HIP(launch_gemm(g, dt, st), "fc1 GEMM");
+  for (int i = 0; i < ns; ++i) g.p[i].out0_dt = act;
+  FLUX_HIP(launch_gemm(g, act, st), "fc1 GEMM");
 
   // 9. x += gate2 * fc2(u)
   for (int i = 0; i < ns; ++i) {
@@ -342,7 +349,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i].gate = w.mod[i] + 5 * D;
     g.p[i].gate_bstride = 6 * D;
   }
-  FLUX_HIP(launch_gemm(g, dt, st), "fc2 GEMM");
+  FLUX_HIP(launch_gemm(g, act, st), "fc2 GEMM");
   return FLUX_OK;
 }
 
@@ -371,6 +378,8 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   if ((s = check_workspace(workspace, workspace_bytes, need.bytes)) != FLUX_OK) return s;
   const SingleWs w = single_ws(d, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = dt == kBF16;
+  const int act = bf ? kF16 : kF32, qkv_t = bf ? kBF16 : kF32;
 
   // 1. (shift, scale, gate) = Linear(SiLU(vec))
   GemvBatch gv{};
@@ -387,7 +396,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   la.s[0].out = w.h; la.s[0].omap = rmap(L * D, D, L);
   la.s[0].shift = w.mod; la.s[0].scale = w.mod + D; la.s[0].mod_bstride = 3 * D;
   la.s[0].rows = (int32_t)(B * L);
-  FLUX_HIP(launch_ln_mod(la, dt, st), "LayerNorm-modulate");
+  FLUX_HIP(launch_ln_mod(la, act, st), "LayerNorm-modulate");
 
   // 3. q|k|v -> qkv buffer; GELU(mlp_in) -> columns D.. of the linear2 input
   GemmBatch g{};
@@ -397,7 +406,9 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   g.p[0].out1 = elem_ptr(w.cat, D, es);
   g.p[0].omap1 = rmap(L * (D + F), D + F, L);
   g.p[0].n_split = (int)(3 * D);
-  FLUX_HIP(launch_gemm(g, dt, st), "linear1 GEMM");
+  g.p[0].out0_dt = qkv_t;
+  g.p[0].out1_dt = act;
+  FLUX_HIP(launch_gemm(g, act, st), "linear1 GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE
   const int64_t Lp = seq_pad_of(L);
@@ -413,7 +424,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   pa.gk_img = pa.gk_txt = sw->k_norm;
   pa.rope = rope; pa.eps = d->eps;
   pa.qh = w.qh; pa.kh = w.kh; pa.vt = w.vt;
-  FLUX_HIP(launch_prep(pa, dt, st), "q/k norm + RoPE");
+  FLUX_HIP(launch_prep(pa, qkv_t, st), "q/k norm + RoPE");
 
   // 5. attention -> columns 0..D of the linear2 input
   AttnArgs aa{};
@@ -421,14 +432,14 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   aa.out = w.cat; aa.out_bstride = L * (D + F); aa.out_ld = D + F;
   aa.batch = (int)B; aa.seq = (int)L; aa.seq_pad = (int)Lp; aa.heads = d->heads; aa.head_dim = d->head_dim;
   aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d->head_dim));
-  FLUX_HIP(launch_attention(aa, dt, st), "attention");
+  FLUX_HIP(launch_attention(aa, qkv_t, act, st), "attention");
 
   // 6. x += gate * Linear2([O | GELU(m)])
   g.p[0] = gemm_problem(w.cat, rmap(L * (D + F), D + F, L), sw->lin2_w, sw->lin2_b, (int)(B * L), (int)D,
                         (int)(D + F), kEpiResid, x, rmap(x_bstride, D, L));
   g.p[0].gate = w.mod + 2 * D;
   g.p[0].gate_bstride = 3 * D;
-  FLUX_HIP(launch_gemm(g, dt, st), "linear2 GEMM");
+  FLUX_HIP(launch_gemm(g, act, st), "linear2 GEMM");
   return FLUX_OK;
 }
 
@@ -621,14 +632,15 @@ flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, i
   la.s[0].out = h; la.s[0].omap = rmap(HW * hidden, hidden, HW);
   la.s[0].shift = mod; la.s[0].scale = mod + hidden; la.s[0].mod_bstride = 2 * hidden;
   la.s[0].rows = (int32_t)(batch * HW);
-  FLUX_HIP(launch_ln_mod(la, dt, st), "final LayerNorm-modulate");
+  const int act = dt == kBF16 ? kF16 : kF32;
+  FLUX_HIP(launch_ln_mod(la, act, st), "final LayerNorm-modulate");
   // tok[b, l, c] lands at v_pred[b, c, l]: row l -> +l, column c -> +c*HW
   GemmBatch g{};
   g.count = 1;
   g.p[0] = gemm_problem(h, rmap(HW * hidden, hidden, HW), out_w, out_b, (int)(batch * HW), channels, hidden,
                         kEpiStoreF32, v_pred, rmap(channels * HW, 1, HW));
   g.p[0].col_stride0 = HW;
-  FLUX_HIP(launch_gemm(g, dt, st), "output GEMM");
+  FLUX_HIP(launch_gemm(g, act, st), "output GEMM");
   return FLUX_OK;
 }
 
@@ -699,7 +711,7 @@ flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, in
   aa.out = o; aa.out_bstride = (int64_t)seq * ld_out; aa.out_ld = ld_out;
   aa.batch = batch; aa.seq = seq; aa.seq_pad = (int)Lp; aa.heads = heads; aa.head_dim = head_dim;
   aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
-  FLUX_HIP(launch_attention(aa, dt, st), "attention");
+  FLUX_HIP(launch_attention(aa, dt, dt, st), "attention");
   return FLUX_OK;
 }
 

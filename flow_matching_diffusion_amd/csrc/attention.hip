@@ -15,7 +15,8 @@
 // half) so that the accumulator registers of each lane hold 8 consecutive
 // keys per 16-key MFMA step, matching 8 consecutive keys of a V^T row.
 // Inputs come from launch_prep: Q, K head-major [B, H, Lp, Dh] and V
-// transposed [B, H, Dh, Lp], Lp = seq rounded up to 128, zero padded.
+// transposed [B, H, Dh, Lp], Lp = seq rounded up to 128, zero padded.  The
+// output is written as bf16 or fp16 (the operand type of the next linear).
 #include <math.h>
 
 #include "common.h"
@@ -26,7 +27,7 @@ namespace flux {
 
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-template <int DH>
+template <int DH, int OUT>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   constexpr int KT = 64;          // keys per tile
   constexpr int QW = 32;          // queries per wave
@@ -177,8 +178,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = i * 32 + 8 * g + 4 * half;
         uint2 v;
-        v.x = pack_bf16x2(o[i][4 * g] * inv, o[i][4 * g + 1] * inv);
-        v.y = pack_bf16x2(o[i][4 * g + 2] * inv, o[i][4 * g + 3] * inv);
+        if constexpr (OUT == kF16) {
+          v.x = pack_f16x2(o[i][4 * g] * inv, o[i][4 * g + 1] * inv);
+          v.y = pack_f16x2(o[i][4 * g + 2] * inv, o[i][4 * g + 3] * inv);
+        } else {
+          v.x = pack_bf16x2(o[i][4 * g] * inv, o[i][4 * g + 1] * inv);
+          v.y = pack_bf16x2(o[i][4 * g + 2] * inv, o[i][4 * g + 3] * inv);
+        }
         *reinterpret_cast<uint2*>(out + d0) = v;
       }
   }
@@ -223,14 +229,21 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream) {
-  TimingScope ts(kKcAttn, stream);
+hipError_t launch_attention(const AttnArgs& a, int dtype, int out_dtype, hipStream_t stream) {
+  TimingScope ts(kKcAttn, stream, 4.0 * a.batch * a.heads * (double)a.seq * a.seq * a.head_dim);
   if (dtype == kBF16) {
     const dim3 grid(a.seq_pad / 128, a.heads, a.batch);
-    if (a.head_dim == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
+    if (a.head_dim == 128) {
+      if (out_dtype == kF16)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, kF16>), grid, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<128, kBF16>), grid, dim3(256), 0, stream, a);
+    } else {
+      if (out_dtype == kF16)
+        hipLaunchKernelGGL((attn_bf16_kernel<64, kF16>), grid, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<64, kBF16>), grid, dim3(256), 0, stream, a);
+    }
   } else {
     const dim3 grid(a.seq_pad / 64, a.heads, a.batch);
     if (a.head_dim == 128)

@@ -7,6 +7,7 @@ namespace flux {
 
 typedef uint16_t bf16_t;                                            // storage: raw bf16 bits
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));        // MFMA operand (8 x bf16)
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));       // MFMA operand (8 x fp16)
 typedef float f32x16_t __attribute__((ext_vector_type(16)));        // 32x32 MFMA accumulator
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));       // 16-byte raw vector
@@ -27,14 +28,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// Storage-type adapters: T is float (fp32 workloads) or bf16_t.
+// fp32 -> fp16 (round to nearest even), two values packed low | high
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+// Eight bf16 (a 16-byte word) to eight fp16.  Exact for magnitudes in fp16's
+// normal range [2^-14, 65504]; smaller magnitudes lose at most 2^-24 (round
+// toward zero on the few bits fp16 subnormals cannot hold).
+__device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t w) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return r;
+}
+
+// Storage-type adapters: T is float (fp32 workloads), bf16_t or _Float16.
 template <typename T> __device__ __forceinline__ float load_f32(const T* p);
 template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+template <> __device__ __forceinline__ float load_f32<_Float16>(const _Float16* p) { return (float)*p; }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
 
 // ---- wave reductions (fixed butterfly order -> deterministic) ---------------
 template <int WIDTH = kWave>

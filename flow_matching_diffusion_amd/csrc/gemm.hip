@@ -2,7 +2,9 @@
 // ("Flux architecture deep dive", MMDiT layer / Flux single block: the qkv,
 // output-projection and MLP linears; "Flux model API reference", add_qkv_bias).
 //
-// bf16 path: 4 waves (2 x 2), block tile BM x BN x 64, v_mfma_f32_32x32x16_bf16,
+// 16-bit path: 4 waves (2 x 2), block tile BM x BN x 64, 32x32x16 MFMA with fp32
+// accumulation; operands bf16 x bf16, or fp16 activations x bf16 weights that
+// are converted to fp16 on their way into LDS (exact in fp16's normal range).
 // A and W both K-contiguous (torch Linear layout), tiles staged through LDS in
 // two buffers with rows padded against bank conflicts, fp32 accumulation.  Several
 // problems (the image and text streams of a double block) share one grid; the
@@ -69,7 +71,20 @@ __device__ __forceinline__ void epi_apply(const GemmProblem& p, const EpiRow& r,
   }
 }
 
-// Four consecutive columns col..col+3 of one row (bf16 operands).  N is a
+// Four values as 16-bit elements of type dt (kBF16 or kF16), packed.
+__device__ __forceinline__ uint2 pack4(float4 v, int dt) {
+  uint2 o;
+  if (dt == kF16) {
+    o.x = pack_f16x2(v.x, v.y);
+    o.y = pack_f16x2(v.z, v.w);
+  } else {
+    o.x = pack_bf16x2(v.x, v.y);
+    o.y = pack_bf16x2(v.z, v.w);
+  }
+  return o;
+}
+
+// Four consecutive columns col..col+3 of one row (16-bit operand kernels).  N is a
 // multiple of 4, so the four columns are all in range together; for the
 // split epilogue n_split is a multiple of 4, so they fall on one side.
 __device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int col, float4 v) {
@@ -88,10 +103,7 @@ __device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int co
       if (p.epi == kEpiGelu) {
         v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
       }
-      uint2 o;
-      o.x = pack_bf16x2(v.x, v.y);
-      o.y = pack_bf16x2(v.z, v.w);
-      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = o;
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = pack4(v, p.out0_dt);
       break;
     }
     case kEpiResid: {
@@ -115,17 +127,13 @@ __device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int co
       break;
     }
     case kEpiSplitGelu: {
-      uint2 o;
       if (col < p.n_split) {
-        o.x = pack_bf16x2(v.x, v.y);
-        o.y = pack_bf16x2(v.z, v.w);
-        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = o;
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = pack4(v, p.out0_dt);
       } else {
         const int64_t b1 = row / p.omap1.seg, l1 = row % p.omap1.seg;
-        o.x = pack_bf16x2(gelu_f(v.x), gelu_f(v.y));
-        o.y = pack_bf16x2(gelu_f(v.z), gelu_f(v.w));
+        v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
         *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out1) + b1 * p.omap1.bstride + l1 * p.omap1.ld +
-                                  (col - p.n_split)) = o;
+                                  (col - p.n_split)) = pack4(v, p.out1_dt);
       }
       break;
     }
@@ -166,7 +174,7 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmBatch& bt, int BM, in
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel
+// 16-bit MFMA kernel
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;   // K per stage: 64 bf16 = 128 bytes = 8 chunks of 16 bytes per row
 // LDS rows padded to 144 bytes: 16 consecutive rows read at one chunk hit 16
@@ -177,8 +185,8 @@ constexpr int kLdsLd = kBK + 8;
 // LDS element offset of chunk `c` (0..7) of tile row `row`.
 __device__ __forceinline__ int lds_off(int row, int c) { return row * kLdsLd + (c << 3); }
 
-template <int BM, int BN>
-__global__ void __launch_bounds__(256, 1) gemm_bf16_kernel(GemmBatch bt) {
+template <int BM, int BN, int OP>
+__global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int LA = BM / 32, LB = BN / 32;      // 16-byte loads per thread per stage
@@ -225,7 +233,9 @@ __global__ void __launch_bounds__(256, 1) gemm_bf16_kernel(GemmBatch bt) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4_t*>(&As[buf][lds_off(i * 32 + lrow, lchunk)]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4_t*>(&Bs[buf][lds_off(i * 32 + lrow, lchunk)]) = rb[i];
+    for (int i = 0; i < LB; ++i)
+      *reinterpret_cast<u32x4_t*>(&Bs[buf][lds_off(i * 32 + lrow, lchunk)]) =
+          OP == kF16 ? bf16x8_to_f16x8(rb[i]) : rb[i];
   };
 
   f32x16_t acc[TM][TN];
@@ -236,34 +246,60 @@ __global__ void __launch_bounds__(256, 1) gemm_bf16_kernel(GemmBatch bt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // Pipeline: tile k+1 sits in registers (loaded during iteration k-1) and is
+  // written to the idle LDS buffer at the start of iteration k, then the
+  // global loads of tile k+2 are issued; the MFMAs of tile k read the other
+  // buffer with their 16-wide k slices double-buffered in registers, so the
+  // LDS reads of slice kk+1 overlap the MFMAs of slice kk.  One barrier per
+  // iteration separates the buffer swap.
   const int KT = p.K / kBK;
+  const int frow = lane & 31, fhalf = lane >> 5;
   gload(0);
   lstore(0);
+  if (KT > 1) gload(kBK);
   __syncthreads();
-  const int frow = lane & 31, fhalf = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * kBK);
+  u32x4_t af[2][TM], bfr[2][TN];
+  auto lfrag = [&](int buf, int s, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8_t af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i)
+      af[s][i] = *reinterpret_cast<const u32x4_t*>(&As[buf][lds_off(wm * WM + i * 32 + frow, kk * 2 + fhalf)]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + frow;
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&As[cur][lds_off(r, kk * 2 + fhalf)]);
-      }
+    for (int j = 0; j < TN; ++j)
+      bfr[s][j] = *reinterpret_cast<const u32x4_t*>(&Bs[buf][lds_off(wn * WN + j * 32 + frow, kk * 2 + fhalf)]);
+  };
+  auto mma = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + j * 32 + frow;
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[cur][lds_off(r, kk * 2 + fhalf)]);
+        if constexpr (OP == kF16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s][i]),
+                                                            __builtin_bit_cast(f16x8_t, bfr[s][j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[s][i]),
+                                                             __builtin_bit_cast(bf16x8_t, bfr[s][j]), acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+  };
+  // sched_barrier(0) fences keep the compiler from sinking the fragment
+  // prefetches back next to their MFMAs
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
     if (kt + 1 < KT) lstore(cur ^ 1);
+    if (kt + 2 < KT) gload((kt + 2) * kBK);
+    lfrag(cur, 0, 0);
+    lfrag(cur, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    lfrag(cur, 0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+    lfrag(cur, 1, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
     __syncthreads();
   }
 
@@ -369,24 +405,39 @@ static int assign_tiles(GemmBatch& bt, int BM, int BN) {
   return t;
 }
 
-hipError_t launch_gemm(GemmBatch bt, int dtype, hipStream_t stream) {
-  if (dtype == kF32) {
-    const int tiles = assign_tiles(bt, 64, 64);
-    TimingScope ts(kKcGemmF32, stream);
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, bt);
-    return hipGetLastError();
-  }
+static double gemm_flops(const GemmBatch& bt) {
+  double f = 0.0;
+  for (int i = 0; i < bt.count; ++i) f += 2.0 * bt.p[i].M * (double)bt.p[i].N * bt.p[i].K;
+  return f;
+}
+
+template <int OP>
+static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   // big tiles when they still give every CU at least one tile
   GemmBatch big = bt;
   const int tiles_big = assign_tiles(big, 256, 256);
   if (tiles_big >= 256) {
-    TimingScope ts(kKcGemm256, stream);
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256>), dim3(tiles_big), dim3(256), 0, stream, big);
+    TimingScope ts(kKcGemm256, stream, flops);
+    hipLaunchKernelGGL((gemm_mfma_kernel<256, 256, OP>), dim3(tiles_big), dim3(256), 0, stream, big);
   } else {
     const int tiles = assign_tiles(bt, 128, 128);
-    TimingScope ts(kKcGemm128, stream);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128>), dim3(tiles), dim3(256), 0, stream, bt);
+    TimingScope ts(kKcGemm128, stream, flops);
+    hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, OP>), dim3(tiles), dim3(256), 0, stream, bt);
   }
+}
+
+hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
+  const double flops = gemm_flops(bt);
+  if (op == kF32) {
+    const int tiles = assign_tiles(bt, 64, 64);
+    TimingScope ts(kKcGemmF32, stream, flops);
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, bt);
+    return hipGetLastError();
+  }
+  if (op == kF16)
+    launch_mfma<kF16>(bt, stream, flops);
+  else
+    launch_mfma<kBF16>(bt, stream, flops);
   return hipGetLastError();
 }
 

@@ -6,7 +6,10 @@
 
 namespace flux {
 
-enum Dtype : int { kF32 = 0, kBF16 = 1 };
+// Element types.  GEMM "operand type": kF32 = fp32 FMA kernel; kBF16 = bf16 A
+// times bf16 W on bf16 MFMA; kF16 = fp16 A times bf16 W converted to fp16 in
+// the LDS staging, on fp16 MFMA.
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 // ---------------------------------------------------------------------------
 // Row addressing shared by the token-wise kernels.  A logical row r of a
@@ -23,11 +26,11 @@ struct RowMap {
 
 // ---------------------------- GEMM (C = A W^T) -----------------------------
 enum EpiKind : int {
-  kEpiStore = 0,      // out0 = T(acc + bias)                   (T = operand type)
-  kEpiGelu = 1,       // out0 = T(GELU(acc + bias))
+  kEpiStore = 0,      // out0 = T0(acc + bias)                  (T0 = out0_dt)
+  kEpiGelu = 1,       // out0 = T0(GELU(acc + bias))
   kEpiResid = 2,      // out0 (float) += gate[b, col] * (acc + bias)
   kEpiStoreF32 = 3,   // out0 (float) = acc + bias            (column stride col_stride)
-  kEpiSplitGelu = 4,  // col < n_split: out0 = T(acc + bias); else out1[col - n_split] = T(GELU(acc + bias))
+  kEpiSplitGelu = 4,  // col < n_split: out0 = T0(acc + bias); else out1[col - n_split] = T1(GELU(acc + bias))
 };
 
 struct GemmProblem {
@@ -39,6 +42,7 @@ struct GemmProblem {
   void* out0;     RowMap omap0;  int64_t col_stride0;
   void* out1;     RowMap omap1;  int32_t n_split;
   const float* gate; int64_t gate_bstride;   // gate[(r / omap0.seg) * gate_bstride + col]
+  int32_t out0_dt, out1_dt;             // Dtype of out0 / out1 for the store epilogues
   int32_t tile_begin;                   // filled by the launcher
   int32_t tiles_n;                      // filled by the launcher
 };
@@ -50,7 +54,7 @@ struct GemmBatch {
   int32_t total_tiles;
 };
 
-hipError_t launch_gemm(GemmBatch batch, int dtype, hipStream_t stream);
+hipError_t launch_gemm(GemmBatch batch, int op, hipStream_t stream);
 
 // ------------------------------ LN + modulate ------------------------------
 struct LnSeg {
@@ -65,7 +69,7 @@ struct LnArgs {
   int32_t dim;
   float eps;
 };
-hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_ln_mod(const LnArgs& a, int out_dtype, hipStream_t stream);
 
 // ------------------------------- GEMV (M = B) -------------------------------
 struct GemvProblem {
@@ -104,7 +108,9 @@ struct AttnArgs {
   int32_t batch, seq, seq_pad, heads, head_dim;
   float scale_log2;                                       // log2(e) / sqrt(head_dim)
 };
-hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
+// in_dtype kBF16 (bf16 MFMA) or kF32; out_dtype kBF16 / kF16 with bf16 inputs,
+// kF32 with fp32 inputs
+hipError_t launch_attention(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
 
 // ------------------------------ small kernels ------------------------------
 hipError_t launch_rope_table(const float* ids, int batch, int seq, const int32_t axes[3], float theta,

@@ -59,7 +59,7 @@ hipError_t launch_rf_noise(int batch, int64_t n, const float* z0, const float* z
   const int64_t work = (n & 3) == 0 ? n / 4 : n;
   int gx = (int)ceil_div(work, 256);
   if (gx > 1024) gx = 1024;
-  TimingScope ts(kKcRf, stream);
+  TimingScope ts(kKcRf, stream, (double)batch * n * (8.0 + (zt ? 4.0 : 0.0) + (vt ? 4.0 : 0.0)));
   hipLaunchKernelGGL(rf_noise_kernel, dim3(gx, batch), dim3(256), 0, stream, n, z0, z1, t, zt, vt);
   return hipGetLastError();
 }
@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(256) rf_loss_final_kernel(int batch, int64_t n
 
 hipError_t launch_rf_loss(int batch, int64_t n, const float* z0, const float* z1, const float* vpred, float* loss,
                           float* loss_ps, double* partials, int parts, hipStream_t stream) {
-  TimingScope ts(kKcRf, stream);
+  TimingScope ts(kKcRf, stream, (double)batch * n * 12.0);
   hipLaunchKernelGGL(rf_loss_partial_kernel, dim3(parts, batch), dim3(kRfLossThreads), 0, stream, n, z0, z1, vpred,
                      partials);
   hipError_t e = hipGetLastError();
@@ -245,6 +245,13 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, floa
   v.y = pack_bf16x2(c, d);
   *reinterpret_cast<uint2*>(p) = v;
 }
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = pack_f16x2(a, b);
+  v.y = pack_f16x2(c, d);
+  *reinterpret_cast<uint2*>(p) = v;
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
@@ -298,12 +305,14 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
   }
 }
 
-hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {
+hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {  // dtype: output element type
   int64_t rows = a.s[0].rows + (a.count > 1 ? a.s[1].rows : 0);
   const dim3 grid((unsigned)ceil_div(rows, 4));
-  TimingScope ts(kKcLnMod, stream);
+  TimingScope ts(kKcLnMod, stream, (double)rows * a.dim * (4.0 + (dtype == kF32 ? 4.0 : 2.0)));
   if (dtype == kBF16)
     hipLaunchKernelGGL(ln_mod_kernel<bf16_t>, grid, dim3(256), 0, stream, a);
+  else if (dtype == kF16)
+    hipLaunchKernelGGL(ln_mod_kernel<_Float16>, grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(ln_mod_kernel<float>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -396,7 +405,9 @@ hipError_t launch_gemv(const GemvBatch& a, int dtype, hipStream_t stream) {
   if (gx > 512) gx = 512;
   const size_t lds = (size_t)a.batch * maxk * sizeof(float);
   const dim3 grid(gx, a.count);
-  TimingScope ts(kKcGemv, stream);
+  double wbytes = 0.0;
+  for (int i = 0; i < a.count; ++i) wbytes += (double)a.p[i].N * a.p[i].K * (dtype == kBF16 ? 2.0 : 4.0);
+  TimingScope ts(kKcGemv, stream, wbytes);
   if (dtype == kBF16)
     hipLaunchKernelGGL(gemv_kernel<bf16_t>, grid, dim3(256), lds, stream, a);
   else
@@ -515,7 +526,8 @@ static hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream) {
-  TimingScope ts(kKcPrep, stream);
+  const double es = dtype == kBF16 ? 2.0 : 4.0, D = (double)a.heads * a.head_dim;
+  TimingScope ts(kKcPrep, stream, es * a.batch * D * (3.0 * a.seq + 3.0 * a.seq_pad));
   return dtype == kBF16 ? launch_prep_t<bf16_t>(a, stream) : launch_prep_t<float>(a, stream);
 }
 

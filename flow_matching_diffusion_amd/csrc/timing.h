@@ -18,16 +18,19 @@ enum KernelClass : int {
 };
 
 // Records a start event on `s` at construction and a stop event at
-// destruction when timing is enabled; does nothing otherwise.
+// destruction when timing is enabled; does nothing otherwise.  `work` is the
+// launch's algorithmic work: FLOPs for the GEMM and attention classes, bytes
+// that must cross HBM for the others.
 class TimingScope {
  public:
-  TimingScope(int cls, hipStream_t s);
+  TimingScope(int cls, hipStream_t s, double work = 0.0);
   ~TimingScope();
   TimingScope(const TimingScope&) = delete;
   TimingScope& operator=(const TimingScope&) = delete;
 
  private:
   int cls_;
+  double work_;
   hipStream_t stream_;
   hipEvent_t start_;
 };

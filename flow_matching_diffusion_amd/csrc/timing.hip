@@ -15,6 +15,7 @@ namespace flux {
 namespace {
 struct Record {
   int cls;
+  double work;
   hipEvent_t start, stop;
 };
 std::atomic<bool> g_on{false};
@@ -38,7 +39,7 @@ const char* kNames[kKcCount] = {"gemm_bf16_256x256", "gemm_bf16_128x128", "gemm_
                                 "misc"};
 }  // namespace
 
-TimingScope::TimingScope(int cls, hipStream_t s) : cls_(cls), stream_(s), start_(nullptr) {
+TimingScope::TimingScope(int cls, hipStream_t s, double work) : cls_(cls), work_(work), stream_(s), start_(nullptr) {
   if (!g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
   start_ = take_event();
@@ -57,7 +58,7 @@ TimingScope::~TimingScope() {
     if (stop) g_pool.push_back(stop);
     return;
   }
-  g_records.push_back(Record{cls_, start_, stop});
+  g_records.push_back(Record{cls_, work_, start_, stop});
 }
 
 }  // namespace flux
@@ -75,11 +76,12 @@ int32_t flux_timing_classes(void) { return kKcCount; }
 
 const char* flux_timing_class_name(int32_t cls) { return (cls >= 0 && cls < kKcCount) ? kNames[cls] : ""; }
 
-flux_status flux_timing_read(double* ms, int64_t* launches, int32_t n) {
+flux_status flux_timing_read(double* ms, int64_t* launches, double* work, int32_t n) {
   std::lock_guard<std::mutex> lk(g_mu);
   for (int i = 0; i < n; ++i) {
     if (ms) ms[i] = 0.0;
     if (launches) launches[i] = 0;
+    if (work) work[i] = 0.0;
   }
   flux_status st = FLUX_OK;
   for (const Record& r : g_records) {
@@ -89,6 +91,7 @@ flux_status flux_timing_read(double* ms, int64_t* launches, int32_t n) {
     if (r.cls < n) {
       if (ms) ms[r.cls] += t;
       if (launches) launches[r.cls] += 1;
+      if (work) work[r.cls] += r.work;
     }
     g_pool.push_back(r.start);
     g_pool.push_back(r.stop);

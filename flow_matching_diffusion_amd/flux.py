@@ -127,7 +127,7 @@ def lib() -> C.CDLL:
     L.flux_timing_classes.restype = i32
     L.flux_timing_class_name.argtypes = [i32]
     L.flux_timing_class_name.restype = C.c_char_p
-    L.flux_timing_read.argtypes = [P(C.c_double), P(C.c_int64), i32]
+    L.flux_timing_read.argtypes = [P(C.c_double), P(C.c_int64), P(C.c_double), i32]
     L.flux_timing_read.restype = C.c_int
     _lib = L
     return L
@@ -286,10 +286,12 @@ def flux_timing_enable(on: bool) -> None:
 
 
 def flux_timing_read() -> Dict[str, tuple]:
-    """{class name: (total ms, launches)} of the launches since the last read."""
+    """{class name: (total ms, launches, algorithmic work)} of the launches
+    since the last read (work in FLOPs for GEMM / attention, bytes otherwise)."""
     L = lib()
     n = L.flux_timing_classes()
     ms = (C.c_double * n)()
     cnt = (C.c_int64 * n)()
-    _check(L.flux_timing_read(ms, cnt, n), "flux_timing_read")
-    return {L.flux_timing_class_name(i).decode(): (ms[i], cnt[i]) for i in range(n)}
+    work = (C.c_double * n)()
+    _check(L.flux_timing_read(ms, cnt, work, n), "flux_timing_read")
+    return {L.flux_timing_class_name(i).decode(): (ms[i], cnt[i], work[i]) for i in range(n)}

@@ -21,10 +21,15 @@
  *    index is head * head_dim + d.  The joint sequence is image rows first,
  *    then text rows.
  *  - Element types: with FLUX_PREC_F32 every weight and activation operand is
- *    float; with FLUX_PREC_BF16 weights and biases are bf16 (raw 16-bit
- *    patterns) and the GEMM/attention operands are bf16 with fp32
- *    accumulation.  Residual streams, modulation vectors, RMSNorm scales,
- *    RoPE tables, latents and losses are always float.
+ *    float.  With FLUX_PREC_BF16 weights and biases are bf16 (raw 16-bit
+ *    patterns); attention runs on bf16 q, k, v with fp32 softmax and
+ *    accumulation; the block linears multiply fp16 activations by the bf16
+ *    weights, converted to fp16 inside the kernel (exact for magnitudes in
+ *    fp16's normal range, error below 2^-24 under it), with fp32
+ *    accumulation.  fp16 activations keep 3 more mantissa bits than bf16 at
+ *    the same matrix-core rate, which the max-abs error bound of the block
+ *    outputs needs at Flux-12B widths.  Residual streams, modulation vectors,
+ *    RMSNorm scales, RoPE tables, latents and losses are always float.
  *  - Errors: every argument is validated on the host BEFORE anything is
  *    enqueued.  A failed check returns a non-zero flux_status and enqueues
  *    nothing; flux_last_error() then returns a thread-local message.  A HIP
@@ -254,15 +259,18 @@ size_t flux_attention_workspace_bytes(int32_t precision, int32_t batch, int32_t 
  * Kernel timing (diagnostics, off by default).  While enabled, each kernel
  * launch made by the library is bracketed by two hipEvents recorded on that
  * launch's stream.  flux_timing_read waits for the recorded events, writes
- * the summed milliseconds and launch counts of the first n kernel classes
- * (n <= flux_timing_classes(); either array may be NULL) and forgets them.
+ * per kernel class (the first n classes, n <= flux_timing_classes(); any
+ * array may be NULL) the summed milliseconds, the launch count and the summed
+ * algorithmic work of those launches -- FLOPs (2*M*N*K per GEMM problem,
+ * 4*B*H*L*L*head_dim per attention call) for the GEMM and attention classes,
+ * bytes that must cross HBM for the other classes -- and forgets them.
  * flux_timing_class_name names a class ("" when out of range).  The hook is
  * process-wide and serialised by a lock.
  */
 flux_status flux_timing_enable(int32_t on);
 int32_t flux_timing_classes(void);
 const char* flux_timing_class_name(int32_t cls);
-flux_status flux_timing_read(double* ms, int64_t* launches, int32_t n);
+flux_status flux_timing_read(double* ms, int64_t* launches, double* work, int32_t n);
 
 /* Static text for a status code; thread-local detail of the last failure on
  * this thread ("" when none). */
