@@ -2,14 +2,19 @@
 // ("Flux architecture deep dive", MMDiT layer / Flux single block: the qkv,
 // output-projection and MLP linears; "Flux model API reference", add_qkv_bias).
 //
-// 16-bit path: 4 waves (2 x 2), block tile BM x BN x 64, 32x32x16 MFMA with fp32
-// accumulation; operands bf16 x bf16, or fp16 activations x bf16 weights that
-// are converted to fp16 on their way into LDS (exact in fp16's normal range).
-// A and W both K-contiguous (torch Linear layout), tiles staged through LDS in
-// two buffers with rows padded against bank conflicts, fp32 accumulation.  Several
-// problems (the image and text streams of a double block) share one grid; the
-// block -> tile map keeps each XCD on a contiguous tile range and walks tiles
-// in groups of 8 tile rows so A and W panels are reused from L2.
+// 16-bit operand paths, fp32 accumulation on 32x32x16 MFMA; operands bf16 x
+// bf16, or fp16 activations x bf16 weights converted to fp16 in the kernel
+// (exact in fp16's normal range).  A and W are both K-contiguous (torch
+// Linear layout).  Several problems (the image and text streams of a double
+// block) share one grid; the tile order keeps each XCD on a contiguous tile
+// range and walks tiles in groups of 8 tile rows so A and W panels are reused
+// from L2.
+//  * large problems: gemm_pk_kernel, persistent (one 256-thread block per CU),
+//    256 x 256 tiles, 5-stage LDS ring of 32-wide k steps filled by direct
+//    global->LDS loads three steps ahead, MFMA fragment reads interleaved with
+//    the MFMAs, next tile's loads overlapping the current epilogue;
+//  * small problems: gemm_mfma_kernel, 128 x 128 tiles, register-staged
+//    double buffer.
 // fp32 path (fp32 workloads only): LDS-tiled FMA kernel with the same epilogues.
 #include "common.h"
 #include "kernels.h"
@@ -149,11 +154,10 @@ struct TileCoord {
   int prob, tm, tn;
 };
 
-__device__ __forceinline__ TileCoord decode_tile(const GemmBatch& bt, int BM, int BN) {
+__device__ __forceinline__ TileCoord decode_tile_id(const GemmBatch& bt, int bid, int BM, int BN) {
   // Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8);
   // give XCD x the contiguous tile range [x*q + min(x, r), ...).
   const int total = bt.total_tiles;
-  const int bid = blockIdx.x;
   const int q = total / 8, rem = total % 8;
   const int x = bid % 8, i = bid / 8;
   const int id = x * q + (x < rem ? x : rem) + i;
@@ -171,6 +175,10 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmBatch& bt, int BM, in
   c.tm = first_m + in % gm;
   c.tn = in / gm;
   return c;
+}
+
+__device__ __forceinline__ TileCoord decode_tile(const GemmBatch& bt, int BM, int BN) {
+  return decode_tile_id(bt, blockIdx.x, BM, BN);
 }
 
 // ---------------------------------------------------------------------------
@@ -334,6 +342,221 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
 }
 
 // ---------------------------------------------------------------------------
+// 256 x 256 tile, 4-stage LDS ring fed by direct global->LDS loads
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+constexpr int kDlBK = 32;                 // k per stage
+constexpr int kDlStages = 5;
+constexpr int kDlRows = 256;              // BM = BN
+constexpr int kDlStageBytes = 2 * kDlRows * kDlBK * 2;   // A + B, 32 KB
+
+// Stage layout: rows of 64 bytes (4 chunks of 16 B), A rows 0..255 then B rows
+// 0..255.  Logical chunk c of row r sits at physical chunk c ^ swz(r): a
+// 16-byte read of one chunk by 16 consecutive rows then touches 16 distinct
+// 4-bank groups with 64 banks, 8 consecutive rows with 32 banks.
+__device__ __forceinline__ int dl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt vmcnt(n) leaving expcnt / lgkmcnt unconstrained (gfx9 encoding)
+#define DL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// Persistent kernel: one block per CU walks the tiles t = blockIdx.x,
+// blockIdx.x + gridDim.x, ...  The first four stages of the next tile are
+// issued as soon as every wave has finished reading the current tile, so
+// their latency overlaps the epilogue, which writes straight from the
+// accumulator registers and leaves LDS to the prefetch.
+template <int OP>
+__global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
+  constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
+  __shared__ __attribute__((aligned(1024))) char smem[kDlStages * kDlStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 31, fhalf = lane >> 5;
+
+  int aoff[TM][2], boff[TN][2];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * WM + i * 32 + frow;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) aoff[i][kk] = r * 64 + (((2 * kk + fhalf) ^ dl_swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int r = wn * WN + j * 32 + frow;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) boff[j][kk] = (kDlRows + r) * 64 + (((2 * kk + fhalf) ^ dl_swz(r)) << 4);
+  }
+
+  // tile state (the problem descriptor itself is re-read from the kernel
+  // arguments where needed, so only these scalars stay live)
+  int prob = 0, m0 = 0, n0 = 0, KT = 0;
+  const char* src[8];
+  auto setup = [&](int t) {
+    const TileCoord tc = decode_tile_id(bt, t, BM, BN);
+    GemmProblem p = bt.p[0];
+    if (tc.prob) p = bt.p[1];
+    prob = tc.prob;
+    m0 = tc.tm * BM;
+    n0 = tc.tn * BN;
+    KT = p.K / kDlBK;
+    const bf16_t* A = reinterpret_cast<const bf16_t*>(p.A);
+    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ins = wave + 4 * u;
+      const int r = (ins & 15) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ dl_swz(r);
+      if (ins < 16) {
+        int gr = m0 + r;
+        gr = gr < p.M ? gr : p.M - 1;
+        src[u] = reinterpret_cast<const char*>(A + (int64_t)(gr / p.amap.seg) * p.amap.bstride +
+                                               (int64_t)(gr % p.amap.seg) * p.amap.ld + c * 8);
+      } else {
+        int gr = n0 + r;
+        gr = gr < p.N ? gr : p.N - 1;
+        src[u] = reinterpret_cast<const char*>(W + (int64_t)gr * p.ldw + c * 8);
+      }
+    }
+  };
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % kDlStages) * kDlStageBytes;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ins = wave + 4 * u;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[u] + (int64_t)kt * kDlBK * 2),
+                                       (lds_void_t*)(st + ins * 1024), 16, 0, 0);
+    }
+  };
+  auto prologue_issue = [&]() {
+    const int pre = KT < 4 ? KT : 4;
+    for (int t = 0; t < pre; ++t) issue(t);
+  };
+
+  f32x16_t acc[TM][TN];
+  u32x4_t af[2][TM], bfr[2][TN];
+  auto lfrag = [&](int kt, int s, int kk) {
+    const char* st = smem + (kt % kDlStages) * kDlStageBytes;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[s][i] = *reinterpret_cast<const u32x4_t*>(st + aoff[i][kk]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[s][j] = *reinterpret_cast<const u32x4_t*>(st + boff[j][kk]);
+  };
+  auto mma = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      u32x4_t b = bfr[s][j];
+      if constexpr (OP == kF16) b = bf16x8_to_f16x8(b);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (OP == kF16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s][i]),
+                                                            __builtin_bit_cast(f16x8_t, b), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[s][i]),
+                                                             __builtin_bit_cast(bf16x8_t, b), acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  auto body = [&](int kt, int vm_wait, bool next, bool refill) {
+    mma(0);
+    lfrag(kt, 1, 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) {
+      if (vm_wait == 16) DL_WAIT_VM(16); else if (vm_wait == 8) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+      __syncthreads();
+      mma(1);
+      if (refill) issue(kt + 4);
+      lfrag(kt + 1, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+    } else {
+      mma(1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int t = blockIdx.x;
+  if (t >= bt.total_tiles) return;
+  setup(t);
+  prologue_issue();
+  for (; t < bt.total_tiles; t += gridDim.x) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    {
+      const int pre = KT < 4 ? KT : 4;   // stages of this tile already issued
+      if (pre == 4) DL_WAIT_VM(24); else if (pre == 3) DL_WAIT_VM(16); else if (pre == 2) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+    }
+    __syncthreads();
+    lfrag(0, 0, 0);
+    int kt = 0;
+    for (; kt + 4 < KT; ++kt) body(kt, 16, true, true);
+    if (kt + 3 < KT) { body(kt, 16, true, false); ++kt; }
+    if (kt + 2 < KT) { body(kt, 8, true, false); ++kt; }
+    if (kt + 1 < KT) { body(kt, 0, true, false); ++kt; }
+    body(kt, 0, false, false);
+
+    // tile done: every wave has read its last fragments once it passes this
+    // barrier, so the stages may be refilled for the next tile
+    const int cprob = prob, cm0 = m0, cn0 = n0;
+    __syncthreads();
+    if (t + (int)gridDim.x < bt.total_tiles) {
+      setup(t + gridDim.x);
+      prologue_issue();
+    }
+
+    // Epilogue through stage 4, which the next tile's prologue leaves alone:
+    // each wave stages a 32 x 64 quarter of its 128 x 128 accumulator block
+    // (element e of lane l in a 32x32 MFMA tile is row 8*(e/4) + 4*(l/32) +
+    // e%4, column l%32), then applies the fused epilogue to 4 consecutive
+    // columns per lane.  Only the wave itself reads its region.
+    GemmProblem pc = bt.p[0];
+    if (cprob) pc = bt.p[1];
+    float* cs = reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[i][2 * h + jj][e];
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
+        __builtin_amdgcn_sched_barrier(0);
+        const int c4 = (lane & 15) * 4;
+        const int col = cn0 + wn * WN + h * 64 + c4;
+#pragma unroll 1
+        for (int rr = lane >> 4; rr < 32; rr += 4) {
+          const int row = cm0 + wm * WM + i * 32 + rr;
+          if (row < pc.M && col < pc.N) {
+            const float4 v = *reinterpret_cast<const float4*>(&cs[rr * 64 + c4]);
+            epi_apply4(pc, row, col, v);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: 64 x 64 tile, 16 x 16 threads with 4 x 4 outputs each
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmBatch bt) {
@@ -413,12 +636,14 @@ static double gemm_flops(const GemmBatch& bt) {
 
 template <int OP>
 static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
-  // big tiles when they still give every CU at least one tile
   GemmBatch big = bt;
   const int tiles_big = assign_tiles(big, 256, 256);
-  if (tiles_big >= 256) {
+  bool seg_ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
+  for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].omap0.seg >= 32;
+  if (tiles_big >= 128 && seg_ok) {   // at least half the CUs get a 256 x 256 tile
     TimingScope ts(kKcGemm256, stream, flops);
-    hipLaunchKernelGGL((gemm_mfma_kernel<256, 256, OP>), dim3(tiles_big), dim3(256), 0, stream, big);
+    const int grid = tiles_big < 256 ? tiles_big : 256;
+    hipLaunchKernelGGL((gemm_pk_kernel<OP>), dim3(grid), dim3(256), 0, stream, big);
   } else {
     const int tiles = assign_tiles(bt, 128, 128);
     TimingScope ts(kKcGemm128, stream, flops);
