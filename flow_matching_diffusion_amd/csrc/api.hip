@@ -81,6 +81,8 @@ flux_status check_dims(const flux_dims* d) {
   REQUIRE(sum == d->head_dim, "axes_dim sum %d != head_dim %d", sum, d->head_dim);
   REQUIRE(d->theta > 0.f && isfinite(d->theta), "theta must be positive");
   REQUIRE(d->eps > 0.f && isfinite(d->eps), "eps must be positive");
+  REQUIRE(d->weights_f16 == 0 || (d->weights_f16 == 1 && d->precision == FLUX_PREC_BF16),
+          "weights_f16 must be 0, or 1 with FLUX_PREC_BF16");
   const int64_t L = (int64_t)d->l_img + d->l_txt;
   REQUIRE(L * d->batch < (int64_t)1 << 31 && (int64_t)d->batch * L * (3 * d->hidden + d->mlp_hidden) < (int64_t)1 << 40,
           "problem too large");
@@ -253,6 +255,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   // on bf16 q, k, v
   const bool bf = dt == kBF16;
   const int act = bf ? kF16 : kF32, qkv_t = bf ? kBF16 : kF32;
+  const int lin = bf ? (d->weights_f16 ? kF16W : kF16) : kF32;   // GEMM operand type of the block linears
   const int ns = Lt > 0 ? 2 : 1;
   const flux_stream_weights* sw[2] = {iw, tw};
   float* xs[2] = {img, txt};
@@ -295,7 +298,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
                           (int)(B * seg[i]), (int)(3 * D), (int)D, kEpiStore, elem_ptr(w.big, off[i] * 3 * D, es),
                           rmap(L * 3 * D, 3 * D, seg[i]));
   for (int i = 0; i < ns; ++i) g.p[i].out0_dt = qkv_t;
-  FLUX_HIP(launch_gemm(g, act, st), "qkv GEMM");
+  FLUX_HIP(launch_gemm(g, lin, st), "qkv GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE, head-major layout
   const int64_t Lp = seq_pad_of(L);
@@ -329,7 +332,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i].gate = w.mod[i] + 2 * D;
     g.p[i].gate_bstride = 6 * D;
   }
-  FLUX_HIP(launch_gemm(g, act, st), "output projection GEMM");
+  FLUX_HIP(launch_gemm(g, lin, st), "output projection GEMM");
 
   // 7. h = LN(x)(1 + scale2) + shift2
   FLUX_HIP(ln_mod(3), "LayerNorm-modulate (MLP)");
@@ -340,7 +343,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
                           (int)(B * seg[i]), (int)F, (int)D, kEpiGelu, elem_ptr(w.big, off[i] * F, es),
                           rmap(L * F, F, seg[i]));
   for (int i = 0; i < ns; ++i) g.p[i].out0_dt = act;
-  FLUX_HIP(launch_gemm(g, act, st), "fc1 GEMM");
+  FLUX_HIP(launch_gemm(g, lin, st), "fc1 GEMM");
 
   // 9. x += gate2 * fc2(u)
   for (int i = 0; i < ns; ++i) {
@@ -349,7 +352,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i].gate = w.mod[i] + 5 * D;
     g.p[i].gate_bstride = 6 * D;
   }
-  FLUX_HIP(launch_gemm(g, act, st), "fc2 GEMM");
+  FLUX_HIP(launch_gemm(g, lin, st), "fc2 GEMM");
   return FLUX_OK;
 }
 
@@ -380,6 +383,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = dt == kBF16;
   const int act = bf ? kF16 : kF32, qkv_t = bf ? kBF16 : kF32;
+  const int lin = bf ? (d->weights_f16 ? kF16W : kF16) : kF32;   // GEMM operand type of the block linears
 
   // 1. (shift, scale, gate) = Linear(SiLU(vec))
   GemvBatch gv{};
@@ -408,7 +412,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   g.p[0].n_split = (int)(3 * D);
   g.p[0].out0_dt = qkv_t;
   g.p[0].out1_dt = act;
-  FLUX_HIP(launch_gemm(g, act, st), "linear1 GEMM");
+  FLUX_HIP(launch_gemm(g, lin, st), "linear1 GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE
   const int64_t Lp = seq_pad_of(L);
@@ -439,7 +443,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
                         (int)(D + F), kEpiResid, x, rmap(x_bstride, D, L));
   g.p[0].gate = w.mod + 2 * D;
   g.p[0].gate_bstride = 3 * D;
-  FLUX_HIP(launch_gemm(g, act, st), "linear2 GEMM");
+  FLUX_HIP(launch_gemm(g, lin, st), "linear2 GEMM");
   return FLUX_OK;
 }
 
@@ -641,6 +645,17 @@ flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, i
                         kEpiStoreF32, v_pred, rmap(channels * HW, 1, HW));
   g.p[0].col_stride0 = HW;
   FLUX_HIP(launch_gemm(g, act, st), "output GEMM");
+  return FLUX_OK;
+}
+
+// ------------------------------ weight conversion ------------------------------
+flux_status flux_convert_bf16_to_f16(const void* src, void* dst, int64_t n, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(src && dst, "src and dst are required");
+  REQUIRE(aligned16(src) && aligned16(dst), "src and dst must be 16-byte aligned");
+  REQUIRE(n >= 1, "n must be >= 1");
+  REQUIRE(!overlap(src, dst, n * 2), "src and dst must not overlap");
+  FLUX_HIP(launch_convert_bf16_f16(src, dst, n, static_cast<hipStream_t>(stream)), "bf16 -> fp16 conversion");
   return FLUX_OK;
 }
 

@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       *reinterpret_cast<u32x4_t*>(&Bs[buf][lds_off(i * 32 + lrow, lchunk)]) =
-          OP == kF16 ? bf16x8_to_f16x8(rb[i]) : rb[i];
+          OP == kF16 ? bf16x8_to_f16x8(rb[i]) : rb[i];   // kF16W: already fp16
   };
 
   f32x16_t acc[TM][TN];
@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if constexpr (OP == kF16)
+        if constexpr (OP == kF16 || OP == kF16W)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s][i]),
                                                             __builtin_bit_cast(f16x8_t, bfr[s][j]), acc[i][j], 0, 0, 0);
         else
@@ -446,10 +446,10 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       u32x4_t b = bfr[s][j];
-      if constexpr (OP == kF16) b = bf16x8_to_f16x8(b);
+      if constexpr (OP == kF16) b = bf16x8_to_f16x8(b);   // kF16W: already fp16
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        if constexpr (OP == kF16)
+        if constexpr (OP == kF16 || OP == kF16W)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s][i]),
                                                             __builtin_bit_cast(f16x8_t, b), acc[i][j], 0, 0, 0);
         else
@@ -641,7 +641,7 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   bool seg_ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
   for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].omap0.seg >= 32;
   if (tiles_big >= 128 && seg_ok) {   // at least half the CUs get a 256 x 256 tile
-    TimingScope ts(kKcGemm256, stream, flops);
+    TimingScope ts(OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
     const int grid = tiles_big < 256 ? tiles_big : 256;
     hipLaunchKernelGGL((gemm_pk_kernel<OP>), dim3(grid), dim3(256), 0, stream, big);
   } else {
@@ -659,7 +659,9 @@ hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, bt);
     return hipGetLastError();
   }
-  if (op == kF16)
+  if (op == kF16W)
+    launch_mfma<kF16W>(bt, stream, flops);
+  else if (op == kF16)
     launch_mfma<kF16>(bt, stream, flops);
   else
     launch_mfma<kBF16>(bt, stream, flops);

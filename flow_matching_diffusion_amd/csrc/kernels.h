@@ -10,6 +10,8 @@ namespace flux {
 // times bf16 W on bf16 MFMA; kF16 = fp16 A times bf16 W converted to fp16 in
 // the LDS staging, on fp16 MFMA.
 enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+// GEMM operand type with fp16 weights already in memory (fp16 x fp16 MFMA)
+constexpr int kF16W = 3;
 
 // ---------------------------------------------------------------------------
 // Row addressing shared by the token-wise kernels.  A logical row r of a
@@ -125,5 +127,6 @@ hipError_t launch_rf_loss(int batch, int64_t n, const float* z0, const float* z1
                           float* loss, float* loss_ps, double* partials, int parts_per_sample,
                           hipStream_t stream);
 int rf_parts_per_sample(int64_t n);
+hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStream_t stream);
 
 }  // namespace flux

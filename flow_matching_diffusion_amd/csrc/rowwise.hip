@@ -531,4 +531,35 @@ hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream) {
   return dtype == kBF16 ? launch_prep_t<bf16_t>(a, stream) : launch_prep_t<float>(a, stream);
 }
 
+// ===========================================================================
+// One-time bf16 -> fp16 conversion of static weights (round to nearest even)
+// ===========================================================================
+__global__ void __launch_bounds__(256) convert_bf16_f16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                               int64_t n8, const bf16_t* __restrict__ src_tail,
+                                                               _Float16* __restrict__ dst_tail, int tail) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 v = src[i];
+    uint4 o;
+    o.x = pack_f16x2(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u));
+    o.y = pack_f16x2(__uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    o.z = pack_f16x2(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u));
+    o.w = pack_f16x2(__uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+    dst[i] = o;
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < tail) dst_tail[threadIdx.x] = (_Float16)bf16_to_f32(src_tail[threadIdx.x]);
+}
+
+hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  const int tail = (int)(n - n8 * 8);
+  int64_t blocks = ceil_div(n8 > 0 ? n8 : 1, 256);
+  if (blocks > 4096) blocks = 4096;
+  TimingScope ts(kKcMisc, stream, 4.0 * (double)n);
+  hipLaunchKernelGGL(convert_bf16_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), n8,
+                     reinterpret_cast<const bf16_t*>(src) + n8 * 8, reinterpret_cast<_Float16*>(dst) + n8 * 8, tail);
+  return hipGetLastError();
+}
+
 }  // namespace flux

@@ -5,8 +5,9 @@
 namespace flux {
 
 enum KernelClass : int {
-  kKcGemm256 = 0,
-  kKcGemm128,
+  kKcGemmPkF16 = 0,   // gemm_pk_kernel, fp16 activations
+  kKcGemmPkBf16,      // gemm_pk_kernel, bf16 activations
+  kKcGemm128,         // gemm_mfma_kernel (128 x 128 tiles)
   kKcGemmF32,
   kKcAttn,
   kKcLnMod,

@@ -34,7 +34,7 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* kNames[kKcCount] = {"gemm_256x256", "gemm_128x128", "gemm_f32", "attention",
+const char* kNames[kKcCount] = {"gemm_pk_f16", "gemm_pk_bf16", "gemm_128x128", "gemm_f32", "attention",
                                 "ln_modulate",       "gemv",              "qk_prep",  "rf_noise_loss",
                                 "misc"};
 }  // namespace

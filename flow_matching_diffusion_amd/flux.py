@@ -29,7 +29,7 @@ EXPORTED = (
     "flux_final_fwd", "flux_linear_fwd", "flux_attention_fwd", "flux_workspace_bytes",
     "flux_rf_workspace_bytes", "flux_embed_workspace_bytes", "flux_final_workspace_bytes",
     "flux_attention_workspace_bytes", "flux_status_string", "flux_last_error", "flux_timing_enable",
-    "flux_timing_classes", "flux_timing_class_name", "flux_timing_read",
+    "flux_timing_classes", "flux_timing_class_name", "flux_timing_read", "flux_convert_bf16_to_f16",
 )
 
 
@@ -49,7 +49,8 @@ def _status_name(s: int) -> str:
 class flux_dims(C.Structure):
     _fields_ = [("batch", C.c_int32), ("l_img", C.c_int32), ("l_txt", C.c_int32), ("hidden", C.c_int32),
                 ("heads", C.c_int32), ("head_dim", C.c_int32), ("mlp_hidden", C.c_int32),
-                ("axes_dim", C.c_int32 * 3), ("theta", C.c_float), ("eps", C.c_float), ("precision", C.c_int32)]
+                ("axes_dim", C.c_int32 * 3), ("theta", C.c_float), ("eps", C.c_float), ("precision", C.c_int32),
+                ("weights_f16", C.c_int32)]
 
 
 class flux_stream_weights(C.Structure):
@@ -102,6 +103,7 @@ def lib() -> C.CDLL:
         "flux_final_fwd": [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
         "flux_attention_fwd": [i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, sz, vp],
+        "flux_convert_bf16_to_f16": [vp, vp, i64, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -160,19 +162,20 @@ def _stream(stream):
 # marshalling helpers
 # --------------------------------------------------------------------------- #
 def make_dims(batch, l_img, l_txt, hidden, heads, head_dim, mlp_hidden, axes_dim=(16, 56, 56), theta=10000.0,
-              eps=1e-6, precision=FLUX_PREC_BF16) -> flux_dims:
+              eps=1e-6, precision=FLUX_PREC_BF16, weights_f16=0) -> flux_dims:
     d = flux_dims()
     d.batch, d.l_img, d.l_txt, d.hidden, d.heads, d.head_dim, d.mlp_hidden = (
         batch, l_img, l_txt, hidden, heads, head_dim, mlp_hidden)
     d.axes_dim[:] = list(axes_dim)
-    d.theta, d.eps, d.precision = theta, eps, precision
+    d.theta, d.eps, d.precision, d.weights_f16 = theta, eps, precision, int(weights_f16)
     return d
 
 
-def dims_for(wl, batch: Optional[int] = None) -> flux_dims:
+def dims_for(wl, batch: Optional[int] = None, weights_f16: bool = False) -> flux_dims:
     """flux_dims of a synth.Workload."""
     return make_dims(batch or wl.batch, wl.l_img, wl.l_txt, wl.hidden, wl.heads, wl.head_dim, wl.mlp_hidden,
-                     wl.axes_dim, wl.theta, wl.eps, FLUX_PREC_F32 if wl.precision == "f32" else FLUX_PREC_BF16)
+                     wl.axes_dim, wl.theta, wl.eps, FLUX_PREC_F32 if wl.precision == "f32" else FLUX_PREC_BF16,
+                     weights_f16)
 
 
 def stream_weights(w: Dict[str, object], prefix: str) -> flux_stream_weights:
@@ -295,3 +298,7 @@ def flux_timing_read() -> Dict[str, tuple]:
     work = (C.c_double * n)()
     _check(L.flux_timing_read(ms, cnt, work, n), "flux_timing_read")
     return {L.flux_timing_class_name(i).decode(): (ms[i], cnt[i], work[i]) for i in range(n)}
+
+
+def flux_convert_bf16_to_f16(src, dst, n: int, stream=None) -> None:
+    _check(lib().flux_convert_bf16_to_f16(ptr(src), ptr(dst), n, _stream(stream)), "flux_convert_bf16_to_f16")

@@ -49,16 +49,40 @@ class Workspace:
         return self.buf
 
 
+# the block linears whose weights may be held in fp16 (not the modulation GEMVs)
+LINEARS = ("img_qkv.w", "img_proj.w", "img_fc1.w", "img_fc2.w", "txt_qkv.w", "txt_proj.w", "txt_fc1.w", "txt_fc2.w",
+           "lin1.w", "lin2.w")
+
+
+def to_f16_weights(w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+    """One-time device conversion of the block linears' bf16 weights to fp16
+    (flux_convert_bf16_to_f16); everything else is kept as is."""
+    out = dict(w)
+    for k in LINEARS:
+        if k in w:
+            dst = torch.empty(w[k].shape, dtype=torch.float16, device=w[k].device)
+            F.flux_convert_bf16_to_f16(w[k], dst, w[k].numel())
+            out[k] = dst
+    return out
+
+
 class BlockStack:
-    """Double and single blocks of one workload, weights resident on the GPU."""
+    """Double and single blocks of one workload, weights resident on the GPU.
+
+    weights_f16: hold the block linears' weights in fp16, converted once here,
+    instead of converting bf16 tiles inside every GEMM (bf16 workloads only)."""
 
     def __init__(self, wl: synth.Workload, double_ws: List[Dict[str, np.ndarray]],
-                 single_ws: List[Dict[str, np.ndarray]], device="cuda"):
+                 single_ws: List[Dict[str, np.ndarray]], device="cuda", weights_f16: bool = False):
         self.wl = wl
         self.bf16 = wl.precision != "f32"
-        self.dims = F.dims_for(wl)
+        weights_f16 = weights_f16 and self.bf16
+        self.dims = F.dims_for(wl, weights_f16=weights_f16)
         self.double = [upload_weights(w, self.bf16, device) for w in double_ws]
         self.single = [upload_weights(w, self.bf16, device) for w in single_ws]
+        if weights_f16:
+            self.double = [to_f16_weights(w) for w in self.double]
+            self.single = [to_f16_weights(w) for w in self.single]
         self._dstructs = [(F.stream_weights(w, "img"), F.stream_weights(w, "txt")) for w in self.double]
         self._sstructs = [F.single_weights(w) for w in self.single]
         self.ws = Workspace(device)
@@ -96,8 +120,9 @@ class BlockStack:
 class FluxModel(BlockStack):
     """Whole forward + rectified-flow loss of a workload."""
 
-    def __init__(self, wl: synth.Workload, emb_w: Dict[str, np.ndarray], double_ws, single_ws, device="cuda"):
-        super().__init__(wl, double_ws, single_ws, device)
+    def __init__(self, wl: synth.Workload, emb_w: Dict[str, np.ndarray], double_ws, single_ws, device="cuda",
+                 weights_f16: bool = False):
+        super().__init__(wl, double_ws, single_ws, device, weights_f16)
         self.emb = upload_weights(emb_w, self.bf16, device)
         self._estruct = F.embed_weights(self.emb)
         p = precision_of(wl)

@@ -74,6 +74,10 @@ typedef struct {
   float theta;            /* RoPE base, 10000 */
   float eps;              /* LayerNorm and RMSNorm epsilon, 1e-6 */
   int32_t precision;      /* flux_precision */
+  int32_t weights_f16;    /* FLUX_PREC_BF16 only.  0: the block linears' weights (qkv, proj, fc1,
+                             fc2; lin1, lin2) are bf16 and are converted to fp16 inside the GEMM.
+                             1: those weights were converted once to fp16 with
+                             flux_convert_bf16_to_f16 (biases and modulation weights stay bf16). */
 } flux_dims;
 
 /* Weights of one stream of a double block (torch Linear layout W [out, in]).
@@ -244,6 +248,15 @@ flux_status flux_linear_fwd(int32_t precision, int32_t m, int32_t n, int32_t k, 
 flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, int32_t heads, int32_t head_dim,
                                const void* q, const void* k, const void* v, int64_t ld_in, void* o,
                                int64_t ld_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * flux_convert_bf16_to_f16 -- dst[i] = fp16(src[i]) for n elements, rounded
+ * to nearest even (exact for magnitudes in [2^-14, 65504]; a weight under
+ * 2^-14 keeps an error below 2^-25).  For the one-time conversion of static
+ * linear weights used with flux_dims.weights_f16 = 1.  src and dst are device
+ * pointers, 16-byte aligned, not overlapping.
+ */
+flux_status flux_convert_bf16_to_f16(const void* src, void* dst, int64_t n, void* stream);
 
 /* Workspace sizes (bytes).  op: 0 double block, 1 single block. */
 size_t flux_workspace_bytes(const flux_dims* dims, int32_t op);

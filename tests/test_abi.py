@@ -137,3 +137,14 @@ def test_workspace_sizes_grow_with_problem():
     assert F.flux_workspace_bytes(_dims(), 1) > 0
     assert F.flux_workspace_bytes(_dims(), 2) == 0
     assert F.flux_rf_workspace_bytes(2, 1 << 20) >= 2 * 8
+
+
+def test_convert_and_weights_f16_checks():
+    L = F.lib()
+    fake = 1 << 40
+    assert L.flux_convert_bf16_to_f16(fake, fake + 8, 100, None) == F.FLUX_ERR_INVALID_ARGUMENT   # misaligned
+    assert L.flux_convert_bf16_to_f16(fake, fake + 64, 100, None) == F.FLUX_ERR_INVALID_ARGUMENT  # overlap
+    assert L.flux_convert_bf16_to_f16(fake, fake + 4096, 0, None) == F.FLUX_ERR_INVALID_ARGUMENT
+    d = _dims(precision=F.FLUX_PREC_F32, weights_f16=1)
+    assert F.flux_workspace_bytes(d, 0) == 0      # fp16-held weights need FLUX_PREC_BF16
+    assert F.flux_workspace_bytes(_dims(weights_f16=1), 0) > 0

@@ -185,10 +185,11 @@ def _block_fixture(wl):
     return w2, w1, inp, ids
 
 
-def _run_pair(wl, w2, w1, inp, ids, which):
+def _run_pair(wl, w2, w1, inp, ids, which, weights_f16=False):
     """Run the double block (which='double') or the single block on the joint
     buffer [x_img | x_txt] and return the joint result."""
-    stack = M().BlockStack(wl, [w2] if which == "double" else [], [w1] if which == "single" else [])
+    stack = M().BlockStack(wl, [w2] if which == "double" else [], [w1] if which == "single" else [],
+                           weights_f16=weights_f16)
     x = dev(np.concatenate([inp["x_img"], inp["x_txt"]], axis=1))
     vec = dev(inp["vec"])
     rope = stack.rope_table(dev(ids))
@@ -231,22 +232,43 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_double_block_small(name):
+SMALL_CASES = [(n, False) for n in SMALL] + [(n, True) for n in SMALL if SMALL[n].precision == "bf16"]
+
+
+@pytest.mark.parametrize("name,wf16", SMALL_CASES)
+def test_double_block_small(name, wf16):
     wl = SMALL[name]
-    _say(f"double block {name}")
+    _say(f"double block {name} weights_f16={wf16}")
     w2, w1, inp, ids = _block_fixture(wl)
-    g = _run_pair(wl, w2, w1, inp, ids, "double")
+    g = _run_pair(wl, w2, w1, inp, ids, "double", wf16)
     _check_double(wl, w2, inp, ids, g)
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_single_block_small(name):
+@pytest.mark.parametrize("name,wf16", SMALL_CASES)
+def test_single_block_small(name, wf16):
     wl = SMALL[name]
-    _say(f"single block {name}")
+    _say(f"single block {name} weights_f16={wf16}")
     w2, w1, inp, ids = _block_fixture(wl)
-    g = _run_pair(wl, w2, w1, inp, ids, "single")
+    g = _run_pair(wl, w2, w1, inp, ids, "single", wf16)
     _check_single(wl, w1, inp, ids, g)
+
+
+def test_convert_bf16_to_f16_matches_rne():
+    _say("bf16 -> fp16 weight conversion")
+    rng = np.random.default_rng(5)
+    a = (0.02 * rng.standard_normal(100003)).astype(np.float32)
+    a[:40] = np.float32(2.0) ** -np.arange(10, 50, dtype=np.float32)      # down through fp16 subnormals
+    a[40:60] = rng.standard_normal(20).astype(np.float32) * 1000.0         # large magnitudes
+    a = synth.round_to_bf16(a)
+    src = dev(a, True)
+    dst = torch.empty(a.shape, dtype=torch.float16, device="cuda")
+    F().flux_convert_bf16_to_f16(src, dst, a.size)
+    torch.cuda.synchronize()
+    ref = a.astype(np.float16)                                             # numpy: round to nearest even
+    assert np.array_equal(dst.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+    # exact wherever the magnitude is in fp16's normal range
+    normal = np.abs(a) >= 2.0 ** -14
+    assert np.array_equal(ref[normal].astype(np.float32), a[normal])
 
 
 def test_block_no_text_tokens():
@@ -278,16 +300,16 @@ def _sample_rows(wl, seed):
 @pytest.mark.slow
 def test_double_block_flux12b_shapes_sampled(big_case):
     wl, w2, w1, inp, ids = big_case
-    _say("double block flux12b_blocks (L=4608) sampled rows")
-    g = _run_pair(wl, w2, w1, inp, ids, "double")
+    _say("double block flux12b_blocks (L=4608) sampled rows, fp16-held linear weights")
+    g = _run_pair(wl, w2, w1, inp, ids, "double", True)
     _check_double(wl, w2, inp, ids, g, rows=_sample_rows(wl, 1))
 
 
 @pytest.mark.slow
 def test_single_block_flux12b_shapes_sampled(big_case):
     wl, w2, w1, inp, ids = big_case
-    _say("single block flux12b_blocks (L=4608) sampled rows")
-    g = _run_pair(wl, w2, w1, inp, ids, "single")
+    _say("single block flux12b_blocks (L=4608) sampled rows, fp16-held linear weights")
+    g = _run_pair(wl, w2, w1, inp, ids, "single", True)
     ri, rt = _sample_rows(wl, 2)
     _check_single(wl, w1, inp, ids, g, rows=np.r_[ri, wl.l_img + rt])
 
@@ -312,12 +334,12 @@ def test_adaln_zero_identity_and_determinism():
 # --------------------------------------------------------------------------- #
 # whole forward + loss
 # --------------------------------------------------------------------------- #
-def _forward_case(wl, rows=None):
+def _forward_case(wl, weights_f16=False):
     emb = synth.embed_weights(wl)
     w2s = [synth.double_block_weights(wl, i) for i in range(wl.n_double)]
     w1s = [synth.single_block_weights(wl, 100 + i) for i in range(wl.n_single)]
     mi = synth.model_inputs(wl)
-    m = M().FluxModel(wl, emb, w2s, w1s)
+    m = M().FluxModel(wl, emb, w2s, w1s, weights_f16=weights_f16)
     bf = wl.precision != "f32"
     out = m.forward_loss(dev(mi["z0"]), dev(mi["z1"]), dev(mi["t"]), dev(mi["txt"], bf),
                          dev(mi["y"]) if "y" in mi else None, dev(mi["ids"]))
@@ -347,5 +369,5 @@ def test_forward_tiny_bf16_with_pooled_vector():
 
 @pytest.mark.slow
 def test_forward_flux535m():
-    _say("whole forward + loss flux535m (L=1536)")
-    _forward_case(synth.WORKLOADS["flux535m"])
+    _say("whole forward + loss flux535m (L=1536), fp16-held linear weights")
+    _forward_case(synth.WORKLOADS["flux535m"], weights_f16=True)
