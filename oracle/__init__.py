@@ -12,6 +12,8 @@ an exp, an erf are library primitives), following the Flux pages:
     Implementation details (Adaptive layer normalization, Attention).
   * "Flux model API reference" -- FluxConfig key parameters, AdaLN, RMSNorm,
     EmbedND, apply_flow_matching_noise, compute_flow_matching_loss.
+  * "FP8 training for Flux models" -- Configuration (E4M3, delayed scaling),
+    in fp8_oracle.
 Where the pages leave a step open the oracle takes one stated reading; the
 readings are listed in the design notes and repeated next to the code.
 
@@ -20,3 +22,4 @@ tests/test_oracle_pins.py (closed forms, invariants, page-printed constants and
 a pure-Python brute force on tiny inputs).
 """
 from .flux_oracle import *  # noqa: F401,F403
+from . import fp8_oracle  # noqa: F401

@@ -216,9 +216,13 @@ def _heads(y: np.ndarray, heads: int) -> np.ndarray:
 # single block; "Flux model API reference", MMDiTLayer, JointSelfAttention,
 # FluxSingleTransformerBlock)
 # --------------------------------------------------------------------------- #
+def _plain_linear(name, x, w, b):
+    return linear(x, w, b)
+
+
 def double_block(x_img, x_txt, vec, angles, w: Dict[str, np.ndarray], heads: int,
                  eps: float = 1e-6, rows: Optional[Dict[str, np.ndarray]] = None,
-                 taps: Optional[dict] = None):
+                 taps: Optional[dict] = None, lin=None):
     """One MMDiT double block.
 
     Per stream s: (shift1, scale1, gate1, shift2, scale2, gate2) = adaLN(vec);
@@ -232,7 +236,11 @@ def double_block(x_img, x_txt, vec, angles, w: Dict[str, np.ndarray], heads: int
     rows: optional {"img": idx, "txt": idx}; when given only those token rows
     of the outputs are evaluated (keys and values still cover every token) and
     the returned arrays hold just those rows.
+    lin: optional hook lin(name, x, W, b) for the token-path linears, named
+    "<stream>_qkv", "<stream>_proj", "<stream>_fc1", "<stream>_fc2" (the fp8
+    linears plug in here); plain linear() when omitted.
     """
+    lin = lin or _plain_linear
     xs = {"img": f64(x_img), "txt": f64(x_txt)}
     l_img = xs["img"].shape[1]
     seg = {"img": slice(0, l_img), "txt": slice(l_img, l_img + xs["txt"].shape[1])}
@@ -243,7 +251,7 @@ def double_block(x_img, x_txt, vec, angles, w: Dict[str, np.ndarray], heads: int
         m = adaln(vec, w[s + "_mod.w"], w[s + "_mod.b"], 6)
         mods[s] = m
         h = modulate(xs[s], m[0], m[1], eps)
-        qkv = linear(h, w[s + "_qkv.w"], w[s + "_qkv.b"])
+        qkv = lin(s + "_qkv", h, w[s + "_qkv.w"], w[s + "_qkv.b"])
         q, k, v = qkv[..., :D], qkv[..., D:2 * D], qkv[..., 2 * D:]
         qs[s] = rmsnorm(_heads(q[:, sel[s]], heads), w[s + "_q_norm"], eps)
         ks[s] = rmsnorm(_heads(k, heads), w[s + "_k_norm"], eps)
@@ -261,15 +269,15 @@ def double_block(x_img, x_txt, vec, angles, w: Dict[str, np.ndarray], heads: int
         if taps is not None:
             taps[s + "_attn"] = o
         m = mods[s]
-        x = xs[s][:, sel[s]] + m[2][:, None, :] * linear(o, w[s + "_proj.w"], w[s + "_proj.b"])
+        x = xs[s][:, sel[s]] + m[2][:, None, :] * lin(s + "_proj", o, w[s + "_proj.w"], w[s + "_proj.b"])
         h2 = modulate(x, m[3], m[4], eps)
-        u = gelu(linear(h2, w[s + "_fc1.w"], w[s + "_fc1.b"]))
-        out[s] = x + m[5][:, None, :] * linear(u, w[s + "_fc2.w"], w[s + "_fc2.b"])
+        u = gelu(lin(s + "_fc1", h2, w[s + "_fc1.w"], w[s + "_fc1.b"]))
+        out[s] = x + m[5][:, None, :] * lin(s + "_fc2", u, w[s + "_fc2.w"], w[s + "_fc2.b"])
     return out["img"], out["txt"]
 
 
 def single_block(x, vec, angles, w: Dict[str, np.ndarray], heads: int, eps: float = 1e-6,
-                 rows: Optional[np.ndarray] = None, taps: Optional[dict] = None) -> np.ndarray:
+                 rows: Optional[np.ndarray] = None, taps: Optional[dict] = None, lin=None) -> np.ndarray:
     """One single-stream block in the fused parallel form (reading R1).
 
     (shift, scale, gate) = adaLN(vec); h = LN(x)(1 + scale) + shift;
@@ -277,13 +285,16 @@ def single_block(x, vec, angles, w: Dict[str, np.ndarray], heads: int, eps: floa
     O = attention(q, k, v); x += gate * Linear2([O | GELU(m)]).
     x covers the whole joint sequence (image rows then text rows).
     rows: optional token indices; only those output rows are evaluated.
+    lin: optional hook lin(name, x, W, b) for the two token-path linears,
+    named "lin1" and "lin2"; plain linear() when omitted.
     """
+    lin = lin or _plain_linear
     x = f64(x)
     D = x.shape[-1]
     sel = rows if rows is not None else np.arange(x.shape[1])
     shift, scale, gate = adaln(vec, w["mod.w"], w["mod.b"], 3)
     h = modulate(x, shift, scale, eps)
-    y = linear(h, w["lin1.w"], w["lin1.b"])
+    y = lin("lin1", h, w["lin1.w"], w["lin1.b"])
     q = rmsnorm(_heads(y[:, sel, :D], heads), w["q_norm"], eps)
     k = rmsnorm(_heads(y[..., D:2 * D], heads), w["k_norm"], eps)
     v = _heads(y[..., 2 * D:3 * D], heads)
@@ -294,7 +305,7 @@ def single_block(x, vec, angles, w: Dict[str, np.ndarray], heads: int, eps: floa
         taps["h"] = h
         taps["attn"] = o
     cat = np.concatenate([o, gelu(y[:, sel, 3 * D:])], axis=-1)
-    return x[:, sel] + gate[:, None, :] * linear(cat, w["lin2.w"], w["lin2.b"])
+    return x[:, sel] + gate[:, None, :] * lin("lin2", cat, w["lin2.w"], w["lin2.b"])
 
 
 # --------------------------------------------------------------------------- #
