@@ -41,7 +41,10 @@ flux_status hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-int esize(int prec) { return prec == FLUX_PREC_BF16 ? 2 : 4; }
+// bytes of a q/k/v or attention element (bf16 unless fp32)
+int esize(int prec) { return prec == FLUX_PREC_F32 ? 4 : 2; }
+// bytes of a block-linear activation operand: fp32, fp16 (bf16 workloads) or E4M3
+int act_esize(int prec) { return prec == FLUX_PREC_F32 ? 4 : prec == FLUX_PREC_FP8_E4M3 ? 1 : 2; }
 int64_t seq_pad_of(int64_t seq) { return round_up(seq, 128); }
 
 // Bump allocator over the caller's workspace (256-byte aligned regions).
@@ -59,7 +62,8 @@ struct Carve {
 
 flux_status check_dims(const flux_dims* d) {
   REQUIRE(d, "dims is NULL");
-  REQUIRE(d->precision == FLUX_PREC_F32 || d->precision == FLUX_PREC_BF16, "precision %d unknown", d->precision);
+  REQUIRE(d->precision == FLUX_PREC_F32 || d->precision == FLUX_PREC_BF16 || d->precision == FLUX_PREC_FP8_E4M3,
+          "precision %d unknown", d->precision);
   REQUIRE(d->batch >= 1, "batch must be >= 1 (got %d)", d->batch);
   REQUIRE(d->l_img >= 1, "l_img must be >= 1 (got %d)", d->l_img);
   REQUIRE(d->l_txt >= 0, "l_txt must be >= 0 (got %d)", d->l_txt);
@@ -105,12 +109,12 @@ BlockWs block_ws(const flux_dims* d, void* base) {
   Carve c(base);
   BlockWs w{};
   const int64_t B = d->batch, L = (int64_t)d->l_img + d->l_txt, D = d->hidden, F = d->mlp_hidden;
-  const int64_t Lp = seq_pad_of(L), es = esize(d->precision);
+  const int64_t Lp = seq_pad_of(L), es = esize(d->precision), aes = act_esize(d->precision);
   w.mod[0] = static_cast<float*>(c.take(B * 6 * D * 4));
   w.mod[1] = static_cast<float*>(c.take(B * 6 * D * 4));
-  w.h = c.take(B * L * D * es);
-  w.big = c.take(B * L * (3 * D > F ? 3 * D : F) * es);
-  w.o = c.take(B * L * D * es);
+  w.h = c.take(B * L * D * aes);
+  w.big = c.take(B * L * (3 * D * es > F * aes ? 3 * D * es : F * aes));   // q|k|v, later GELU(fc1)
+  w.o = c.take(B * L * D * aes);
   w.qh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.kh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.vt = c.take(B * d->heads * Lp * d->head_dim * es);
@@ -133,11 +137,11 @@ SingleWs single_ws(const flux_dims* d, void* base) {
   Carve c(base);
   SingleWs w{};
   const int64_t B = d->batch, L = (int64_t)d->l_img + d->l_txt, D = d->hidden, F = d->mlp_hidden;
-  const int64_t Lp = seq_pad_of(L), es = esize(d->precision);
+  const int64_t Lp = seq_pad_of(L), es = esize(d->precision), aes = act_esize(d->precision);
   w.mod = static_cast<float*>(c.take(B * 3 * D * 4));
-  w.h = c.take(B * L * D * es);
+  w.h = c.take(B * L * D * aes);
   w.qkv = c.take(B * L * 3 * D * es);
-  w.cat = c.take(B * L * (D + F) * es);
+  w.cat = c.take(B * L * (D + F) * aes);
   w.qh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.kh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.vt = c.take(B * d->heads * Lp * d->head_dim * es);
@@ -201,6 +205,11 @@ flux_status check_stream_weights(const flux_stream_weights* w, const char* name)
   return FLUX_OK;
 }
 
+flux_status check_fp8_records(const flux_fp8_tensor* r, const char* name) {
+  REQUIRE(r && aligned16(r), "%s: fp8 state records are required (16-byte aligned) with FLUX_PREC_FP8_E4M3", name);
+  return FLUX_OK;
+}
+
 }  // namespace
 
 // ================================ public API ================================
@@ -234,9 +243,12 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   flux_status s = check_dims(d);
   if (s != FLUX_OK) return s;
   const int64_t B = d->batch, Li = d->l_img, Lt = d->l_txt, L = Li + Lt, D = d->hidden, F = d->mlp_hidden;
-  const int dt = d->precision == FLUX_PREC_BF16 ? kBF16 : kF32, es = esize(d->precision);
+  const bool f32 = d->precision == FLUX_PREC_F32, fp8 = d->precision == FLUX_PREC_FP8_E4M3;
+  const int dt = f32 ? kF32 : kBF16, es = esize(d->precision), aes = act_esize(d->precision);
   if ((s = check_stream_weights(iw, "image")) != FLUX_OK) return s;
   if (Lt > 0 && (s = check_stream_weights(tw, "text")) != FLUX_OK) return s;
+  if (fp8 && (s = check_fp8_records(iw->fp8, "image weights")) != FLUX_OK) return s;
+  if (fp8 && Lt > 0 && (s = check_fp8_records(tw->fp8, "text weights")) != FLUX_OK) return s;
   REQUIRE(img && aligned16(img), "img must be a non-NULL 16-byte aligned pointer");
   REQUIRE(img_bstride >= Li * D && img_bstride % 4 == 0, "img_bstride must be >= l_img*hidden and a multiple of 4");
   if (Lt > 0) {
@@ -251,13 +263,15 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   const BlockWs w = block_ws(d, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // element types: fp32 workloads use float everywhere; bf16 workloads run the
-  // linears on fp16 activations (bf16 weights converted in LDS) and attention
-  // on bf16 q, k, v
-  const bool bf = dt == kBF16;
-  const int act = bf ? kF16 : kF32, qkv_t = bf ? kBF16 : kF32;
-  const int lin = bf ? (d->weights_f16 ? kF16W : kF16) : kF32;   // GEMM operand type of the block linears
+  // linears on fp16 activations (bf16 weights converted in LDS, or fp16
+  // weights) and attention on bf16 q, k, v; fp8 workloads run the linears on
+  // E4M3 activations and weights, attention on bf16
+  const int act = f32 ? kF32 : fp8 ? kFP8 : kF16, qkv_t = f32 ? kF32 : kBF16;
+  const int lin = f32 ? kF32 : fp8 ? kFP8 : (d->weights_f16 ? kF16W : kF16);   // GEMM operand type
   const int ns = Lt > 0 ? 2 : 1;
   const flux_stream_weights* sw[2] = {iw, tw};
+  // fp8 state records of a stream (null unless fp8)
+  auto rec = [&](int i, int slot) -> flux_fp8_tensor* { return fp8 ? sw[i]->fp8 + slot : nullptr; };
   float* xs[2] = {img, txt};
   const int64_t xbs[2] = {img_bstride, txt_bstride};
   const int64_t seg[2] = {Li, Lt};
@@ -278,8 +292,9 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     for (int i = 0; i < ns; ++i) {
       a.s[i].x = xs[i];
       a.s[i].xmap = rmap(xbs[i], D, seg[i]);
-      a.s[i].out = elem_ptr(w.h, off[i] * D, es);
+      a.s[i].out = elem_ptr(w.h, off[i] * D, aes);
       a.s[i].omap = rmap(L * D, D, seg[i]);
+      a.s[i].q = rec(i, chunk_shift == 0 ? FLUX_FP8_QKV_X : FLUX_FP8_FC1_X);
       a.s[i].shift = w.mod[i] + chunk_shift * D;
       a.s[i].scale = w.mod[i] + (chunk_shift + 1) * D;
       a.s[i].mod_bstride = 6 * D;
@@ -294,10 +309,14 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   GemmBatch g{};
   g.count = ns;
   for (int i = 0; i < ns; ++i)
-    g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->qkv_w, sw[i]->qkv_b,
+    g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, aes), rmap(L * D, D, seg[i]), sw[i]->qkv_w, sw[i]->qkv_b,
                           (int)(B * seg[i]), (int)(3 * D), (int)D, kEpiStore, elem_ptr(w.big, off[i] * 3 * D, es),
                           rmap(L * 3 * D, 3 * D, seg[i]));
-  for (int i = 0; i < ns; ++i) g.p[i].out0_dt = qkv_t;
+  for (int i = 0; i < ns; ++i) {
+    g.p[i].out0_dt = qkv_t;
+    g.p[i].qa = rec(i, FLUX_FP8_QKV_X);
+    g.p[i].qw = rec(i, FLUX_FP8_QKV_W);
+  }
   FLUX_HIP(launch_gemm(g, lin, st), "qkv GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE, head-major layout
@@ -323,14 +342,19 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   aa.out = w.o; aa.out_bstride = L * D; aa.out_ld = D;
   aa.batch = (int)B; aa.seq = (int)L; aa.seq_pad = (int)Lp; aa.heads = d->heads; aa.head_dim = d->head_dim;
   aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d->head_dim));
+  aa.oq[0] = rec(0, FLUX_FP8_PROJ_X);
+  aa.oq[1] = ns > 1 ? rec(1, FLUX_FP8_PROJ_X) : nullptr;
+  aa.l_img = (int)Li;
   FLUX_HIP(launch_attention(aa, qkv_t, act, st), "joint attention");
 
   // 6. x += gate1 * Linear_proj(O)
   for (int i = 0; i < ns; ++i) {
-    g.p[i] = gemm_problem(elem_ptr(w.o, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->proj_w, sw[i]->proj_b,
+    g.p[i] = gemm_problem(elem_ptr(w.o, off[i] * D, aes), rmap(L * D, D, seg[i]), sw[i]->proj_w, sw[i]->proj_b,
                           (int)(B * seg[i]), (int)D, (int)D, kEpiResid, xs[i], rmap(xbs[i], D, seg[i]));
     g.p[i].gate = w.mod[i] + 2 * D;
     g.p[i].gate_bstride = 6 * D;
+    g.p[i].qa = rec(i, FLUX_FP8_PROJ_X);
+    g.p[i].qw = rec(i, FLUX_FP8_PROJ_W);
   }
   FLUX_HIP(launch_gemm(g, lin, st), "output projection GEMM");
 
@@ -339,18 +363,25 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
 
   // 8. u = GELU(fc1(h))
   for (int i = 0; i < ns; ++i)
-    g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, es), rmap(L * D, D, seg[i]), sw[i]->fc1_w, sw[i]->fc1_b,
-                          (int)(B * seg[i]), (int)F, (int)D, kEpiGelu, elem_ptr(w.big, off[i] * F, es),
+    g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, aes), rmap(L * D, D, seg[i]), sw[i]->fc1_w, sw[i]->fc1_b,
+                          (int)(B * seg[i]), (int)F, (int)D, kEpiGelu, elem_ptr(w.big, off[i] * F, aes),
                           rmap(L * F, F, seg[i]));
-  for (int i = 0; i < ns; ++i) g.p[i].out0_dt = act;
+  for (int i = 0; i < ns; ++i) {
+    g.p[i].out0_dt = act;
+    g.p[i].qa = rec(i, FLUX_FP8_FC1_X);
+    g.p[i].qw = rec(i, FLUX_FP8_FC1_W);
+    g.p[i].qo = rec(i, FLUX_FP8_FC2_X);
+  }
   FLUX_HIP(launch_gemm(g, lin, st), "fc1 GEMM");
 
   // 9. x += gate2 * fc2(u)
   for (int i = 0; i < ns; ++i) {
-    g.p[i] = gemm_problem(elem_ptr(w.big, off[i] * F, es), rmap(L * F, F, seg[i]), sw[i]->fc2_w, sw[i]->fc2_b,
+    g.p[i] = gemm_problem(elem_ptr(w.big, off[i] * F, aes), rmap(L * F, F, seg[i]), sw[i]->fc2_w, sw[i]->fc2_b,
                           (int)(B * seg[i]), (int)D, (int)F, kEpiResid, xs[i], rmap(xbs[i], D, seg[i]));
     g.p[i].gate = w.mod[i] + 5 * D;
     g.p[i].gate_bstride = 6 * D;
+    g.p[i].qa = rec(i, FLUX_FP8_FC2_X);
+    g.p[i].qw = rec(i, FLUX_FP8_FC2_W);
   }
   FLUX_HIP(launch_gemm(g, lin, st), "fc2 GEMM");
   return FLUX_OK;
@@ -364,7 +395,8 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   flux_status s = check_dims(d);
   if (s != FLUX_OK) return s;
   const int64_t B = d->batch, L = (int64_t)d->l_img + d->l_txt, D = d->hidden, F = d->mlp_hidden;
-  const int dt = d->precision == FLUX_PREC_BF16 ? kBF16 : kF32, es = esize(d->precision);
+  const bool f32 = d->precision == FLUX_PREC_F32, fp8 = d->precision == FLUX_PREC_FP8_E4M3;
+  const int dt = f32 ? kF32 : kBF16, es = esize(d->precision), aes = act_esize(d->precision);
   REQUIRE(sw, "single-block weights are NULL");
   REQUIRE(sw->mod_w && sw->mod_b && sw->lin1_w && sw->lin1_b && sw->q_norm && sw->k_norm && sw->lin2_w &&
               sw->lin2_b,
@@ -373,6 +405,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
     const void* ps[] = {sw->mod_w, sw->mod_b, sw->lin1_w, sw->lin1_b, sw->q_norm, sw->k_norm, sw->lin2_w, sw->lin2_b};
     for (const void* p : ps) REQUIRE(aligned16(p), "single-block weights: pointers must be 16-byte aligned");
   }
+  if (fp8 && (s = check_fp8_records(sw->fp8, "single-block weights")) != FLUX_OK) return s;
   REQUIRE(x && aligned16(x), "x must be a non-NULL 16-byte aligned pointer");
   REQUIRE(x_bstride >= L * D && x_bstride % 4 == 0, "x_bstride must be >= L*hidden and a multiple of 4");
   REQUIRE(vec && aligned16(vec), "vec must be a non-NULL 16-byte aligned pointer");
@@ -381,9 +414,9 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   if ((s = check_workspace(workspace, workspace_bytes, need.bytes)) != FLUX_OK) return s;
   const SingleWs w = single_ws(d, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf = dt == kBF16;
-  const int act = bf ? kF16 : kF32, qkv_t = bf ? kBF16 : kF32;
-  const int lin = bf ? (d->weights_f16 ? kF16W : kF16) : kF32;   // GEMM operand type of the block linears
+  const int act = f32 ? kF32 : fp8 ? kFP8 : kF16, qkv_t = f32 ? kF32 : kBF16;
+  const int lin = f32 ? kF32 : fp8 ? kFP8 : (d->weights_f16 ? kF16W : kF16);   // GEMM operand type
+  auto rec = [&](int slot) -> flux_fp8_tensor* { return fp8 ? sw->fp8 + slot : nullptr; };
 
   // 1. (shift, scale, gate) = Linear(SiLU(vec))
   GemvBatch gv{};
@@ -399,6 +432,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   la.s[0].x = x; la.s[0].xmap = rmap(x_bstride, D, L);
   la.s[0].out = w.h; la.s[0].omap = rmap(L * D, D, L);
   la.s[0].shift = w.mod; la.s[0].scale = w.mod + D; la.s[0].mod_bstride = 3 * D;
+  la.s[0].q = rec(FLUX_FP8_LIN1_X);
   la.s[0].rows = (int32_t)(B * L);
   FLUX_HIP(launch_ln_mod(la, act, st), "LayerNorm-modulate");
 
@@ -407,11 +441,14 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   g.count = 1;
   g.p[0] = gemm_problem(w.h, rmap(L * D, D, L), sw->lin1_w, sw->lin1_b, (int)(B * L), (int)(3 * D + F), (int)D,
                         kEpiSplitGelu, w.qkv, rmap(L * 3 * D, 3 * D, L));
-  g.p[0].out1 = elem_ptr(w.cat, D, es);
+  g.p[0].out1 = elem_ptr(w.cat, D, aes);
   g.p[0].omap1 = rmap(L * (D + F), D + F, L);
   g.p[0].n_split = (int)(3 * D);
   g.p[0].out0_dt = qkv_t;
   g.p[0].out1_dt = act;
+  g.p[0].qa = rec(FLUX_FP8_LIN1_X);
+  g.p[0].qw = rec(FLUX_FP8_LIN1_W);
+  g.p[0].qo = rec(FLUX_FP8_LIN2_X);
   FLUX_HIP(launch_gemm(g, lin, st), "linear1 GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE
@@ -436,6 +473,8 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   aa.out = w.cat; aa.out_bstride = L * (D + F); aa.out_ld = D + F;
   aa.batch = (int)B; aa.seq = (int)L; aa.seq_pad = (int)Lp; aa.heads = d->heads; aa.head_dim = d->head_dim;
   aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d->head_dim));
+  aa.oq[0] = aa.oq[1] = rec(FLUX_FP8_LIN2_X);   // O and GELU(m) form one quantized tensor
+  aa.l_img = (int)L;
   FLUX_HIP(launch_attention(aa, qkv_t, act, st), "attention");
 
   // 6. x += gate * Linear2([O | GELU(m)])
@@ -443,6 +482,8 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
                         (int)(D + F), kEpiResid, x, rmap(x_bstride, D, L));
   g.p[0].gate = w.mod + 2 * D;
   g.p[0].gate_bstride = 3 * D;
+  g.p[0].qa = rec(FLUX_FP8_LIN2_X);
+  g.p[0].qw = rec(FLUX_FP8_LIN2_W);
   FLUX_HIP(launch_gemm(g, lin, st), "linear2 GEMM");
   return FLUX_OK;
 }
@@ -679,6 +720,62 @@ flux_status flux_linear_fwd(int32_t precision, int32_t m, int32_t n, int32_t k, 
   g.p[0] = gemm_problem(x, rmap((int64_t)m * lda, lda, m), w, b, m, n, k, kEpiStoreF32, y, rmap((int64_t)m * ldy, ldy, m));
   FLUX_HIP(launch_gemm(g, precision == FLUX_PREC_BF16 ? kBF16 : kF32, static_cast<hipStream_t>(stream)),
            "linear GEMM");
+  return FLUX_OK;
+}
+
+// ------------------------------------ fp8 ------------------------------------
+size_t flux_fp8_state_bytes(int32_t n_tensors) {
+  return n_tensors >= 1 ? (size_t)n_tensors * sizeof(flux_fp8_tensor) : 0;
+}
+
+flux_status flux_fp8_quantize(int32_t src_precision, const void* src, int64_t n, flux_fp8_tensor* rec, uint8_t* dst,
+                              void* stream) {
+  g_err[0] = 0;
+  REQUIRE(src_precision == FLUX_PREC_F32 || src_precision == FLUX_PREC_BF16,
+          "src_precision must be FLUX_PREC_F32 or FLUX_PREC_BF16 (got %d)", src_precision);
+  REQUIRE(n >= 1 && n < ((int64_t)1 << 40), "n must be in [1, 2^40)");
+  REQUIRE(src && dst && rec, "src, rec and dst are required");
+  REQUIRE(aligned16(src) && aligned16(dst) && aligned16(rec), "pointers must be 16-byte aligned");
+  const int64_t sbytes = n * (src_precision == FLUX_PREC_F32 ? 4 : 2);
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = reinterpret_cast<const char*>(dst);
+  REQUIRE(!(s0 < d0 + n && d0 < s0 + sbytes), "src and dst must not overlap");
+  FLUX_HIP(launch_fp8_quantize(src, src_precision == FLUX_PREC_F32 ? kF32 : kBF16, n, rec, dst,
+                               static_cast<hipStream_t>(stream)),
+           "fp8 quantize");
+  return FLUX_OK;
+}
+
+flux_status flux_fp8_update(flux_fp8_tensor* recs, int32_t n_tensors, int32_t algo, int32_t margin, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(recs && aligned16(recs), "recs must be a non-NULL 16-byte aligned pointer");
+  REQUIRE(n_tensors >= 1, "n_tensors must be >= 1");
+  REQUIRE(algo == 0 || algo == 1, "algo must be 0 (most_recent) or 1 (max)");
+  REQUIRE(margin >= 0 && margin <= 32, "margin must be in [0, 32]");
+  FLUX_HIP(launch_fp8_update(recs, n_tensors, algo, margin, static_cast<hipStream_t>(stream)), "fp8 scale update");
+  return FLUX_OK;
+}
+
+flux_status flux_fp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* x, int64_t ldx, const uint8_t* w,
+                                int64_t ldw, const flux_fp8_tensor* rx, const flux_fp8_tensor* rw, const void* b,
+                                float* y, int64_t ldy, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(m >= 1 && n >= 1 && k >= 1, "m, n, k must be >= 1");
+  REQUIRE(x && w && rx && rw && y, "x, w, rx, rw and y are required");
+  REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(rx) && aligned16(rw) && (!b || aligned16(b)),
+          "pointers must be 16-byte aligned");
+  if (k % 64 != 0) return fail(FLUX_ERR_UNSUPPORTED, "fp8 linear needs k %% 64 == 0 (got %d)", k);
+  if (n % 4 != 0) return fail(FLUX_ERR_UNSUPPORTED, "n must be a multiple of 4 (got %d)", n);
+  REQUIRE(ldx >= k && ldw >= k && ldx % 16 == 0 && ldw % 16 == 0, "ldx, ldw must be >= k and multiples of 16");
+  REQUIRE(ldy >= n && ldy % 4 == 0, "ldy must be >= n and a multiple of 4");
+  GemmBatch g{};
+  g.count = 1;
+  g.p[0] = gemm_problem(x, rmap((int64_t)m * ldx, ldx, m), w, b, m, n, k, kEpiStoreF32, y,
+                        rmap((int64_t)m * ldy, ldy, m));
+  g.p[0].ldw = ldw;
+  g.p[0].qa = rx;
+  g.p[0].qw = rw;
+  FLUX_HIP(launch_gemm(g, kFP8, static_cast<hipStream_t>(stream)), "fp8 linear GEMM");
   return FLUX_OK;
 }
 

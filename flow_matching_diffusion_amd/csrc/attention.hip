@@ -16,7 +16,8 @@
 // keys per 16-key MFMA step, matching 8 consecutive keys of a V^T row.
 // Inputs come from launch_prep: Q, K head-major [B, H, Lp, Dh] and V
 // transposed [B, H, Dh, Lp], Lp = seq rounded up to 128, zero padded.  The
-// output is written as bf16 or fp16 (the operand type of the next linear).
+// output is written as bf16, fp16 or E4M3 (the operand type of the next
+// linear; E4M3 with the delayed scale of the row's stream).
 #include <math.h>
 
 #include "common.h"
@@ -170,7 +171,37 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
-  if (q < a.seq) {
+  if constexpr (OUT == kFP8) {
+    // E4M3 output with the delayed scale of the row's stream (image rows
+    // oq[0], text rows oq[1]); each stream's amax is raised once per wave
+    const bool img_row = q < a.l_img;
+    flux_fp8_tensor* rec = img_row ? a.oq[0] : a.oq[1];
+    uint32_t mx = 0;
+    if (q < a.seq) {
+      const float qs = fp8_scale(rec);
+      uint8_t* out = reinterpret_cast<uint8_t*>(a.out) + (int64_t)b * a.out_bstride + (int64_t)q * a.out_ld + h * DH;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = i * 32 + 8 * g + 4 * half;
+          uint32_t w = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float y = o[i][4 * g + e] * inv;
+            mx = max(mx, abs_bits(y));
+            w |= f32_to_e4m3(y * qs) << (8 * e);
+          }
+          *reinterpret_cast<uint32_t*>(out + d0) = w;
+        }
+    }
+    const uint32_t m_img = wave_max_u32(img_row ? mx : 0u);
+    const uint32_t m_txt = wave_max_u32(img_row ? 0u : mx);
+    if (lane == 0) {
+      if (m_img) fp8_amax_raise(a.oq[0], __uint_as_float(m_img));
+      if (m_txt && a.oq[1]) fp8_amax_raise(a.oq[1], __uint_as_float(m_txt));
+    }
+  } else if (q < a.seq) {
     bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + (int64_t)b * a.out_bstride + (int64_t)q * a.out_ld + h * DH;
 #pragma unroll
     for (int i = 0; i < DT; ++i)
@@ -236,11 +267,15 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int out_dtype, hipStre
     if (a.head_dim == 128) {
       if (out_dtype == kF16)
         hipLaunchKernelGGL((attn_bf16_kernel<128, kF16>), grid, dim3(256), 0, stream, a);
+      else if (out_dtype == kFP8)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, kFP8>), grid, dim3(256), 0, stream, a);
       else
         hipLaunchKernelGGL((attn_bf16_kernel<128, kBF16>), grid, dim3(256), 0, stream, a);
     } else {
       if (out_dtype == kF16)
         hipLaunchKernelGGL((attn_bf16_kernel<64, kF16>), grid, dim3(256), 0, stream, a);
+      else if (out_dtype == kFP8)
+        hipLaunchKernelGGL((attn_bf16_kernel<64, kFP8>), grid, dim3(256), 0, stream, a);
       else
         hipLaunchKernelGGL((attn_bf16_kernel<64, kBF16>), grid, dim3(256), 0, stream, a);
     }

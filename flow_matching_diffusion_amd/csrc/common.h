@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/flux.h"
+
 namespace flux {
 
 typedef uint16_t bf16_t;                                            // storage: raw bf16 bits
@@ -71,6 +73,14 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WIDTH));
   return v;
 }
+// max of unsigned values over the wave (used on |x| bit patterns for amax)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+// bit pattern of |x|: orders like |x| for non-negative values, NaN above all
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -81,6 +91,67 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 // GELU, erf form: x * Phi(x), with the device library's erff.
 __device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// ---- OCP E4M3FN ("FP8 training for Flux models", Configuration: fp8 e4m3) ----
+// Byte of the nearest E4M3FN value to x, ties to the even code; |x| > 448
+// (infinities included) saturates to +-448; NaN stays NaN (0x7F | sign).
+// Written from the format: 4 exponent bits with bias 7, 3 mantissa bits,
+// subnormals m * 2^-9 under 2^-6.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a > 0x7f800000u) {
+    code = 0x7fu;                                           // NaN
+  } else if (a > 0x43e00000u) {
+    code = 0x7eu;                                           // above 448: saturate
+  } else if (a >= 0x3c800000u) {
+    // normal: keep 3 of fp32's 23 mantissa bits, round half to even; a carry
+    // out of the mantissa moves into the exponent by itself
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);                         // exponent bias 127 -> 7
+  } else {
+    // subnormal range: nearest multiple of 2^-9 (the product is exact), ties to even
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float fp8_scale(const flux_fp8_tensor* r) {
+  return (r->flags & FLUX_FP8_SCALE_SET) ? r->scale : 1.0f;
+}
+__device__ __forceinline__ float fp8_scale_inv(const flux_fp8_tensor* r) {
+  return (r->flags & FLUX_FP8_SCALE_SET) ? r->scale_inv : 1.0f;
+}
+// Raise the record's amax to m (m >= 0 or NaN): fp32 bit patterns of
+// non-negative values order like unsigned integers, and a NaN's pattern is
+// above every finite one, so the update sees it.  Vector-memory atomic.
+__device__ __forceinline__ void fp8_amax_raise(flux_fp8_tensor* r, float m) {
+  atomicMax(&r->amax_bits, __float_as_uint(m) & 0x7fffffffu);
+}
+
+// Eight E4M3 bytes to eight fp16 (exact: every E4M3 value is an fp16 value).
+// Placing the byte's exponent and mantissa fields at fp16's exponent and
+// mantissa positions gives the value times 2^-8 (for subnormals too), so one
+// multiply by 256 restores it.  NaN bytes are not expected here.
+__device__ __forceinline__ u32x4_t e4m3x8_to_f16x8(uint2 w) {
+  u32x4_t r;
+  const uint32_t in[2] = {w.x, w.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t b0 = (in[i] >> (16 * j)) & 0xffu, b1 = (in[i] >> (16 * j + 8)) & 0xffu;
+      const uint16_t h0 = (uint16_t)(((b0 & 0x7fu) << 7) | ((b0 & 0x80u) << 8));
+      const uint16_t h1 = (uint16_t)(((b1 & 0x7fu) << 7) | ((b1 & 0x80u) << 8));
+      const _Float16 f0 = __builtin_bit_cast(_Float16, h0) * (_Float16)256.0f;
+      const _Float16 f1 = __builtin_bit_cast(_Float16, h1) * (_Float16)256.0f;
+      r[2 * i + j] = (uint32_t)__builtin_bit_cast(uint16_t, f0) | ((uint32_t)__builtin_bit_cast(uint16_t, f1) << 16);
+    }
+  }
+  return r;
+}
 
 // ---- integer helpers ---------------------------------------------------------
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -3,8 +3,10 @@
 // output-projection and MLP linears; "Flux model API reference", add_qkv_bias).
 //
 // 16-bit operand paths, fp32 accumulation on 32x32x16 MFMA; operands bf16 x
-// bf16, or fp16 activations x bf16 weights converted to fp16 in the kernel
-// (exact in fp16's normal range).  A and W are both K-contiguous (torch
+// bf16, fp16 activations x bf16 weights converted to fp16 in the kernel (exact
+// in fp16's normal range), or fp16 x fp16.  E4M3 x E4M3 operands run on the
+// 32x32x64 fp8 MFMA (gemm_fp8_kernel), small E4M3 problems on the 128 x 128
+// kernel after an exact widening to fp16.  A and W are both K-contiguous (torch
 // Linear layout).  Several problems (the image and text streams of a double
 // block) share one grid; the tile order keeps each XCD on a contiguous tile
 // range and walks tiles in groups of 8 tile rows so A and W panels are reused
@@ -16,6 +18,8 @@
 //  * small problems: gemm_mfma_kernel, 128 x 128 tiles, register-staged
 //    double buffer.
 // fp32 path (fp32 workloads only): LDS-tiled FMA kernel with the same epilogues.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -89,10 +93,30 @@ __device__ __forceinline__ uint2 pack4(float4 v, int dt) {
   return o;
 }
 
-// Four consecutive columns col..col+3 of one row (16-bit operand kernels).  N is a
+// Four values as E4M3 bytes (scale qs), and their largest magnitude into mx.
+__device__ __forceinline__ uint32_t pack4_e4m3(float4 v, float qs, uint32_t& mx) {
+  mx = max(mx, max(max(abs_bits(v.x), abs_bits(v.y)), max(abs_bits(v.z), abs_bits(v.w))));
+  return f32_to_e4m3(v.x * qs) | (f32_to_e4m3(v.y * qs) << 8) | (f32_to_e4m3(v.z * qs) << 16) |
+         (f32_to_e4m3(v.w * qs) << 24);
+}
+
+// Store four values of a 16-bit or E4M3 output whose element offset is off.
+__device__ __forceinline__ void store4_dt(void* base, int64_t off, int dt, float4 v, float qs, uint32_t& mx) {
+  if (dt == kFP8)
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(base) + off) = pack4_e4m3(v, qs, mx);
+  else
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(base) + off) = pack4(v, dt);
+}
+
+// Four consecutive columns col..col+3 of one row (MFMA kernels).  N is a
 // multiple of 4, so the four columns are all in range together; for the
 // split epilogue n_split is a multiple of 4, so they fall on one side.
-__device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int col, float4 v) {
+// dq multiplies the accumulator first (the product of the two operand
+// scale_inv for E4M3 operands, else 1); qs is the E4M3 output scale and mx
+// collects the largest magnitude written as E4M3.
+__device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int col, float4 v, float dq, float qs,
+                                           uint32_t& mx) {
+  v.x *= dq; v.y *= dq; v.z *= dq; v.w *= dq;
   if (p.bias) {
     const uint2 bb = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.bias) + col);
     v.x += __uint_as_float(bb.x << 16);
@@ -108,7 +132,7 @@ __device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int co
       if (p.epi == kEpiGelu) {
         v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
       }
-      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = pack4(v, p.out0_dt);
+      store4_dt(p.out0, off0 + col, p.out0_dt, v, qs, mx);
       break;
     }
     case kEpiResid: {
@@ -133,12 +157,11 @@ __device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int co
     }
     case kEpiSplitGelu: {
       if (col < p.n_split) {
-        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + off0 + col) = pack4(v, p.out0_dt);
+        store4_dt(p.out0, off0 + col, p.out0_dt, v, qs, mx);
       } else {
         const int64_t b1 = row / p.omap1.seg, l1 = row % p.omap1.seg;
         v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
-        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out1) + b1 * p.omap1.bstride + l1 * p.omap1.ld +
-                                  (col - p.n_split)) = pack4(v, p.out1_dt);
+        store4_dt(p.out1, b1 * p.omap1.bstride + l1 * p.omap1.ld + (col - p.n_split), p.out1_dt, v, qs, mx);
       }
       break;
     }
@@ -181,8 +204,21 @@ __device__ __forceinline__ TileCoord decode_tile(const GemmBatch& bt, int BM, in
   return decode_tile_id(bt, blockIdx.x, BM, BN);
 }
 
+// Accumulator multiplier of a problem: scale_inv of both E4M3 operand records,
+// 1 for 16-bit operands.
+__device__ __forceinline__ float epi_dequant(const GemmProblem& p) {
+  return p.qa ? fp8_scale_inv(p.qa) * fp8_scale_inv(p.qw) : 1.0f;
+}
+__device__ __forceinline__ float epi_out_scale(const GemmProblem& p) { return p.qo ? fp8_scale(p.qo) : 1.0f; }
+// Raise the output record's amax once per wave (every lane calls).
+__device__ __forceinline__ void epi_amax_flush(const GemmProblem& p, uint32_t mx) {
+  mx = wave_max_u32(mx);
+  if (p.qo && (threadIdx.x & 63) == 0 && mx) fp8_amax_raise(p.qo, __uint_as_float(mx));
+}
+
 // ---------------------------------------------------------------------------
-// 16-bit MFMA kernel
+// 16-bit MFMA kernel (also the small-problem path of E4M3 operands, widened
+// exactly to fp16 on their way into LDS)
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;   // K per stage: 64 bf16 = 128 bytes = 8 chunks of 16 bytes per row
 // LDS rows padded to 144 bytes: 16 consecutive rows read at one chunk hit 16
@@ -210,32 +246,41 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // global row pointers of this thread's loads (rows clamped into range)
-  const bf16_t* arow[LA];
-  const bf16_t* brow[LB];
+  // global row pointers of this thread's loads (rows clamped into range);
+  // each thread moves 8 elements (one 16-byte LDS chunk) per row and stage
+  constexpr int ES = OP == kFP8 ? 1 : 2;          // operand bytes per element in memory
+  const char* arow[LA];
+  const char* brow[LB];
   const int lrow = tid >> 3, lchunk = tid & 7;
   {
-    const bf16_t* A = reinterpret_cast<const bf16_t*>(p.A);
+    const char* A = reinterpret_cast<const char*>(p.A);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       int r = m0 + i * 32 + lrow;
       r = r < p.M ? r : p.M - 1;
-      arow[i] = A + (int64_t)(r / p.amap.seg) * p.amap.bstride + (int64_t)(r % p.amap.seg) * p.amap.ld + lchunk * 8;
+      arow[i] = A + ((int64_t)(r / p.amap.seg) * p.amap.bstride + (int64_t)(r % p.amap.seg) * p.amap.ld + lchunk * 8) * ES;
     }
-    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
+    const char* W = reinterpret_cast<const char*>(p.W);
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       int r = n0 + i * 32 + lrow;
       r = r < p.N ? r : p.N - 1;
-      brow[i] = W + (int64_t)r * p.ldw + lchunk * 8;
+      brow[i] = W + ((int64_t)r * p.ldw + lchunk * 8) * ES;
     }
   }
   u32x4_t ra[LA], rb[LB];
   auto gload = [&](int k0) {
+    if constexpr (OP == kFP8) {
 #pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + k0);
+      for (int i = 0; i < LA; ++i) ra[i] = e4m3x8_to_f16x8(*reinterpret_cast<const uint2*>(arow[i] + k0));
 #pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(brow[i] + k0);
+      for (int i = 0; i < LB; ++i) rb[i] = e4m3x8_to_f16x8(*reinterpret_cast<const uint2*>(brow[i] + k0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + (int64_t)k0 * 2);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(brow[i] + (int64_t)k0 * 2);
+    }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -243,7 +288,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       *reinterpret_cast<u32x4_t*>(&Bs[buf][lds_off(i * 32 + lrow, lchunk)]) =
-          OP == kF16 ? bf16x8_to_f16x8(rb[i]) : rb[i];   // kF16W: already fp16
+          OP == kF16 ? bf16x8_to_f16x8(rb[i]) : rb[i];   // kF16W, kFP8: already fp16
   };
 
   f32x16_t acc[TM][TN];
@@ -280,7 +325,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if constexpr (OP == kF16 || OP == kF16W)
+        if constexpr (OP == kF16 || OP == kF16W || OP == kFP8)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s][i]),
                                                             __builtin_bit_cast(f16x8_t, bfr[s][j]), acc[i][j], 0, 0, 0);
         else
@@ -317,6 +362,8 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
   // then runs on 4 consecutive columns per lane with vector loads and stores.
   constexpr int CLD = WN + 4;
   float* cs = reinterpret_cast<float*>(&As[0][0]) + wave * 32 * CLD;
+  const float dq = epi_dequant(p), qs = epi_out_scale(p);
+  uint32_t mx = 0;
   static_assert(4 * 32 * CLD * 4 <= 2 * BM * kLdsLd * 2, "epilogue staging must fit in the A buffers");
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -334,11 +381,12 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
       const int row = m0 + wm * WM + i * 32 + rr;
       if (row < p.M && col < p.N) {
         const float4 v = *reinterpret_cast<const float4*>(&cs[rr * CLD + c4]);
-        epi_apply4(p, row, col, v);
+        epi_apply4(p, row, col, v, dq, qs, mx);
       }
     }
     __syncthreads();
   }
+  epi_amax_flush(p, mx);
 }
 
 // ---------------------------------------------------------------------------
@@ -364,8 +412,8 @@ __device__ __forceinline__ int dl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3;
 // Persistent kernel: one block per CU walks the tiles t = blockIdx.x,
 // blockIdx.x + gridDim.x, ...  The first four stages of the next tile are
 // issued as soon as every wave has finished reading the current tile, so
-// their latency overlaps the epilogue, which writes straight from the
-// accumulator registers and leaves LDS to the prefetch.
+// their latency overlaps the epilogue, which stages the accumulators through
+// the fifth stage (left alone by that prefetch).
 template <int OP>
 __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
@@ -528,6 +576,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
     GemmProblem pc = bt.p[0];
     if (cprob) pc = bt.p[1];
     float* cs = reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64;
+    uint32_t mx = 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -546,13 +595,225 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
           const int row = cm0 + wm * WM + i * 32 + rr;
           if (row < pc.M && col < pc.N) {
             const float4 v = *reinterpret_cast<const float4*>(&cs[rr * 64 + c4]);
-            epi_apply4(pc, row, col, v);
+            epi_apply4(pc, row, col, v, 1.0f, 1.0f, mx);
           }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 operands ("FP8 training for Flux models", Configuration): persistent
+// 256 x 256 kernel on v_mfma_f32_32x32x64_f8f6f4 (no block scales).  Same LDS
+// ring, swizzle, prologue and epilogue as gemm_pk_kernel; a 64-byte stage row
+// now holds 64 k values, i.e. one MFMA k-step.  Lane half h of a fragment
+// takes row chunks h and 2 + h (32 bytes); A and B use the same split, so each
+// MFMA sums over all 64 k of the stage.  The 16 fragment reads of stage kt+1
+// run under the 16 MFMAs of stage kt, into the other of two register sets.
+// ---------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+template <int S> using SetTag = std::integral_constant<int, S>;
+
+__global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
+  constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
+  constexpr int BK8 = 64;   // k values (bytes) per stage row
+  __shared__ __attribute__((aligned(1024))) char smem[kDlStages * kDlStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 31, fhalf = lane >> 5;
+
+  int aoff[TM][2], boff[TN][2];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * WM + i * 32 + frow;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) aoff[i][kk] = r * 64 + (((2 * kk + fhalf) ^ dl_swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int r = wn * WN + j * 32 + frow;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) boff[j][kk] = (kDlRows + r) * 64 + (((2 * kk + fhalf) ^ dl_swz(r)) << 4);
+  }
+
+  int prob = 0, m0 = 0, n0 = 0, KT = 0;
+  const char* src[8];
+  auto setup = [&](int t) {
+    const TileCoord tc = decode_tile_id(bt, t, BM, BN);
+    GemmProblem p = bt.p[0];
+    if (tc.prob) p = bt.p[1];
+    prob = tc.prob;
+    m0 = tc.tm * BM;
+    n0 = tc.tn * BN;
+    KT = p.K / BK8;
+    const char* A = reinterpret_cast<const char*>(p.A);
+    const char* W = reinterpret_cast<const char*>(p.W);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ins = wave + 4 * u;
+      const int r = (ins & 15) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ dl_swz(r);
+      if (ins < 16) {
+        int gr = m0 + r;
+        gr = gr < p.M ? gr : p.M - 1;
+        src[u] = A + (int64_t)(gr / p.amap.seg) * p.amap.bstride + (int64_t)(gr % p.amap.seg) * p.amap.ld + c * 16;
+      } else {
+        int gr = n0 + r;
+        gr = gr < p.N ? gr : p.N - 1;
+        src[u] = W + (int64_t)gr * p.ldw + c * 16;
+      }
+    }
+  };
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % kDlStages) * kDlStageBytes;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ins = wave + 4 * u;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[u] + (int64_t)kt * BK8),
+                                       (lds_void_t*)(st + ins * 1024), 16, 0, 0);
+    }
+  };
+  auto prologue_issue = [&]() {
+    const int pre = KT < 4 ? KT : 4;
+    for (int t = 0; t < pre; ++t) issue(t);
+  };
+
+  f32x16_t acc[TM][TN];
+  u32x4_t fa[2][TM][2], fb[2][TN][2];   // [set][tile][chunk h or 2 + h]
+  auto lfrag = [&](int kt, auto set) {
+    constexpr int S = decltype(set)::value;
+    const char* st = smem + (kt % kDlStages) * kDlStageBytes;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) fa[S][i][kk] = *reinterpret_cast<const u32x4_t*>(st + aoff[i][kk]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) fb[S][j][kk] = *reinterpret_cast<const u32x4_t*>(st + boff[j][kk]);
+  };
+  auto mma = [&](auto set) {
+    constexpr int S = decltype(set)::value;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[S][j][0], fb[S][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[S][i][0], fa[S][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+      }
+    }
+  };
+  // Stage kt's fragments are in set S.  Wait until stage kt+1 has landed for
+  // every wave (VM: loads allowed to stay outstanding, i.e. those of the
+  // stages issued beyond kt+1), refill the stage freed two steps ago with
+  // kt+4, read stage kt+1 into the other set while the MFMAs of stage kt run.
+  // All flags are compile-time so the k loop carries no branches.
+  auto body = [&](int kt, auto set, auto vm, auto next, auto refill) {
+    constexpr int S = decltype(set)::value;
+    if constexpr (decltype(next)::value) {
+      constexpr int VM = decltype(vm)::value;
+      if constexpr (VM == 16) DL_WAIT_VM(16); else if constexpr (VM == 8) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+      __syncthreads();
+      if constexpr (decltype(refill)::value) issue(kt + 4);
+      lfrag(kt + 1, SetTag<1 - S>{});
+      mma(SetTag<S>{});
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    } else {
+      mma(SetTag<S>{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using V16 = std::integral_constant<int, 16>;
+  using V8 = std::integral_constant<int, 8>;
+  using V0 = std::integral_constant<int, 0>;
+
+  int t = blockIdx.x;
+  if (t >= bt.total_tiles) return;
+  setup(t);
+  prologue_issue();
+  for (; t < bt.total_tiles; t += gridDim.x) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    {
+      const int pre = KT < 4 ? KT : 4;   // stages of this tile already issued
+      if (pre == 4) DL_WAIT_VM(24); else if (pre == 3) DL_WAIT_VM(16); else if (pre == 2) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+    }
+    __syncthreads();
+    lfrag(0, SetTag<0>{});
+    // KT is even (the launcher sends K % 128 != 0 elsewhere).  Steady state:
+    // both steps of a pair refill; then 4 or 2 steps remain.
+    int kt = 0;
+    for (; kt + 5 < KT; kt += 2) {
+      body(kt, SetTag<0>{}, V16{}, T_{}, T_{});
+      body(kt + 1, SetTag<1>{}, V16{}, T_{}, T_{});
+    }
+    if (KT - kt == 4) {
+      body(kt, SetTag<0>{}, V16{}, T_{}, F_{});
+      body(kt + 1, SetTag<1>{}, V8{}, T_{}, F_{});
+      body(kt + 2, SetTag<0>{}, V0{}, T_{}, F_{});
+      body(kt + 3, SetTag<1>{}, V0{}, F_{}, F_{});
+    } else {
+      body(kt, SetTag<0>{}, V0{}, T_{}, F_{});
+      body(kt + 1, SetTag<1>{}, V0{}, F_{}, F_{});
+    }
+
+    // tile done: every wave has read its last fragments once it passes this
+    // barrier, so the stages may be refilled for the next tile
+    const int cprob = prob, cm0 = m0, cn0 = n0;
+    __syncthreads();
+    if (t + (int)gridDim.x < bt.total_tiles) {
+      setup(t + gridDim.x);
+      prologue_issue();
+    }
+
+    // epilogue through stage 4, as in gemm_pk_kernel
+    GemmProblem pc = bt.p[0];
+    if (cprob) pc = bt.p[1];
+    const float dq = epi_dequant(pc), qs = epi_out_scale(pc);
+    uint32_t mx = 0;
+    float* cs = reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[i][2 * h + jj][e];
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
+        __builtin_amdgcn_sched_barrier(0);
+        const int c4 = (lane & 15) * 4;
+        const int col = cn0 + wn * WN + h * 64 + c4;
+#pragma unroll 1
+        for (int rr = lane >> 4; rr < 32; rr += 4) {
+          const int row = cm0 + wm * WM + i * 32 + rr;
+          if (row < pc.M && col < pc.N) {
+            const float4 v = *reinterpret_cast<const float4*>(&cs[rr * 64 + c4]);
+            epi_apply4(pc, row, col, v, dq, qs, mx);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    epi_amax_flush(pc, mx);
   }
 }
 
@@ -640,10 +901,17 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   const int tiles_big = assign_tiles(big, 256, 256);
   bool seg_ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
   for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].omap0.seg >= 32;
+  if constexpr (OP == kFP8)   // gemm_fp8_kernel walks k in pairs of 64-wide steps
+    for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K % 128 == 0;
   if (tiles_big >= 128 && seg_ok) {   // at least half the CUs get a 256 x 256 tile
-    TimingScope ts(OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
     const int grid = tiles_big < 256 ? tiles_big : 256;
-    hipLaunchKernelGGL((gemm_pk_kernel<OP>), dim3(grid), dim3(256), 0, stream, big);
+    if constexpr (OP == kFP8) {
+      TimingScope ts(kKcGemmPkFp8, stream, flops);
+      hipLaunchKernelGGL(gemm_fp8_kernel, dim3(grid), dim3(256), 0, stream, big);
+    } else {
+      TimingScope ts(OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
+      hipLaunchKernelGGL((gemm_pk_kernel<OP>), dim3(grid), dim3(256), 0, stream, big);
+    }
   } else {
     const int tiles = assign_tiles(bt, 128, 128);
     TimingScope ts(kKcGemm128, stream, flops);
@@ -659,7 +927,9 @@ hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, bt);
     return hipGetLastError();
   }
-  if (op == kF16W)
+  if (op == kFP8)
+    launch_mfma<kFP8>(bt, stream, flops);
+  else if (op == kF16W)
     launch_mfma<kF16W>(bt, stream, flops);
   else if (op == kF16)
     launch_mfma<kF16>(bt, stream, flops);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/flux.h"
+
 namespace flux {
 
 // Element types.  GEMM "operand type": kF32 = fp32 FMA kernel; kBF16 = bf16 A
@@ -12,6 +14,10 @@ namespace flux {
 enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 // GEMM operand type with fp16 weights already in memory (fp16 x fp16 MFMA)
 constexpr int kF16W = 3;
+// OCP E4M3FN bytes: as a GEMM operand type, e4m3 activations times e4m3
+// weights on the fp8 MFMA; as an output type, values quantized with the
+// scale of an flux_fp8_tensor record whose amax they raise.
+constexpr int kFP8 = 4;
 
 // ---------------------------------------------------------------------------
 // Row addressing shared by the token-wise kernels.  A logical row r of a
@@ -45,6 +51,9 @@ struct GemmProblem {
   void* out1;     RowMap omap1;  int32_t n_split;
   const float* gate; int64_t gate_bstride;   // gate[(r / omap0.seg) * gate_bstride + col]
   int32_t out0_dt, out1_dt;             // Dtype of out0 / out1 for the store epilogues
+  const flux_fp8_tensor* qa;            // kFP8 operands: records A and W were quantized with;
+  const flux_fp8_tensor* qw;            //   the accumulator is multiplied by both scale_inv
+  flux_fp8_tensor* qo;                  // kFP8 output (out0 of kEpiGelu, out1 of kEpiSplitGelu)
   int32_t tile_begin;                   // filled by the launcher
   int32_t tiles_n;                      // filled by the launcher
 };
@@ -63,6 +72,7 @@ struct LnSeg {
   const float* x;  RowMap xmap;         // fp32 residual rows
   void* out;       RowMap omap;         // T rows
   const float* shift; const float* scale; int64_t mod_bstride;   // [b * mod_bstride + col]
+  flux_fp8_tensor* q;                   // kFP8 output: scale source and amax destination
   int32_t rows;                         // B * seg
 };
 struct LnArgs {
@@ -109,9 +119,11 @@ struct AttnArgs {
   void* out; int64_t out_bstride; int64_t out_ld;         // [B, seq, ...], head h at column h*head_dim
   int32_t batch, seq, seq_pad, heads, head_dim;
   float scale_log2;                                       // log2(e) / sqrt(head_dim)
+  flux_fp8_tensor* oq[2];                                 // kFP8 output: rows < l_img use oq[0], others oq[1]
+  int32_t l_img;
 };
-// in_dtype kBF16 (bf16 MFMA) or kF32; out_dtype kBF16 / kF16 with bf16 inputs,
-// kF32 with fp32 inputs
+// in_dtype kBF16 (bf16 MFMA) or kF32; out_dtype kBF16 / kF16 / kFP8 with bf16
+// inputs, kF32 with fp32 inputs
 hipError_t launch_attention(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
 
 // ------------------------------ small kernels ------------------------------
@@ -128,5 +140,12 @@ hipError_t launch_rf_loss(int batch, int64_t n, const float* z0, const float* z1
                           hipStream_t stream);
 int rf_parts_per_sample(int64_t n);
 hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStream_t stream);
+
+// ---------------------------------- fp8 ------------------------------------
+// dst = e4m3(src * scale(rec)); rec->amax_bits raised to max |src|.  src_dtype kF32 or kBF16.
+hipError_t launch_fp8_quantize(const void* src, int src_dtype, int64_t n, flux_fp8_tensor* rec, uint8_t* dst,
+                               hipStream_t stream);
+// delayed-scaling update of n records (algo 0 most_recent, 1 max)
+hipError_t launch_fp8_update(flux_fp8_tensor* rec, int n, int algo, int margin, hipStream_t stream);
 
 }  // namespace flux

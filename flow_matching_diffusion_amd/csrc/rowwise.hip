@@ -293,14 +293,37 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
   }
   const float var = wave_sum(sq) / (float)D;
   const float rstd = 1.0f / sqrtf(var + a.eps);
+  if constexpr (sizeof(T) == 1) {
+    // E4M3 output with the record's delayed scale; the row's amax raises the record's
+    const float qs = fp8_scale(s.q);
+    uint32_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < kLnMaxVec; ++i) {
-    if (i < nv) {
-      const int c = (lane + 64 * i) * 4;
-      const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
-      const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
-      store4<T>(out + c, (v[i].x - mean) * rstd * (1.f + s4.x) + h4.x, (v[i].y - mean) * rstd * (1.f + s4.y) + h4.y,
-                (v[i].z - mean) * rstd * (1.f + s4.z) + h4.z, (v[i].w - mean) * rstd * (1.f + s4.w) + h4.w);
+    for (int i = 0; i < kLnMaxVec; ++i) {
+      if (i < nv) {
+        const int c = (lane + 64 * i) * 4;
+        const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
+        const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
+        const float y0 = (v[i].x - mean) * rstd * (1.f + s4.x) + h4.x;
+        const float y1 = (v[i].y - mean) * rstd * (1.f + s4.y) + h4.y;
+        const float y2 = (v[i].z - mean) * rstd * (1.f + s4.z) + h4.z;
+        const float y3 = (v[i].w - mean) * rstd * (1.f + s4.w) + h4.w;
+        mx = max(mx, max(max(abs_bits(y0), abs_bits(y1)), max(abs_bits(y2), abs_bits(y3))));
+        *reinterpret_cast<uint32_t*>(out + c) = f32_to_e4m3(y0 * qs) | (f32_to_e4m3(y1 * qs) << 8) |
+                                                (f32_to_e4m3(y2 * qs) << 16) | (f32_to_e4m3(y3 * qs) << 24);
+      }
+    }
+    mx = wave_max_u32(mx);
+    if (lane == 0) fp8_amax_raise(s.q, __uint_as_float(mx));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kLnMaxVec; ++i) {
+      if (i < nv) {
+        const int c = (lane + 64 * i) * 4;
+        const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
+        const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
+        store4<T>(out + c, (v[i].x - mean) * rstd * (1.f + s4.x) + h4.x, (v[i].y - mean) * rstd * (1.f + s4.y) + h4.y,
+                  (v[i].z - mean) * rstd * (1.f + s4.z) + h4.z, (v[i].w - mean) * rstd * (1.f + s4.w) + h4.w);
+      }
     }
   }
 }
@@ -308,8 +331,10 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
 hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {  // dtype: output element type
   int64_t rows = a.s[0].rows + (a.count > 1 ? a.s[1].rows : 0);
   const dim3 grid((unsigned)ceil_div(rows, 4));
-  TimingScope ts(kKcLnMod, stream, (double)rows * a.dim * (4.0 + (dtype == kF32 ? 4.0 : 2.0)));
-  if (dtype == kBF16)
+  TimingScope ts(kKcLnMod, stream, (double)rows * a.dim * (4.0 + (dtype == kF32 ? 4.0 : dtype == kFP8 ? 1.0 : 2.0)));
+  if (dtype == kFP8)
+    hipLaunchKernelGGL(ln_mod_kernel<uint8_t>, grid, dim3(256), 0, stream, a);
+  else if (dtype == kBF16)
     hipLaunchKernelGGL(ln_mod_kernel<bf16_t>, grid, dim3(256), 0, stream, a);
   else if (dtype == kF16)
     hipLaunchKernelGGL(ln_mod_kernel<_Float16>, grid, dim3(256), 0, stream, a);
@@ -559,6 +584,120 @@ hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStr
   hipLaunchKernelGGL(convert_bf16_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), n8,
                      reinterpret_cast<const bf16_t*>(src) + n8 * 8, reinterpret_cast<_Float16*>(dst) + n8 * 8, tail);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// FP8 (E4M3) delayed scaling ("FP8 training for Flux models", Configuration).
+// ===========================================================================
+// dst = e4m3(src * scale(rec)) over a whole tensor (the weight cast of a
+// forward); each thread converts 16 consecutive elements per step, and one
+// atomic per wave raises the record's amax.
+template <typename T>
+__global__ void __launch_bounds__(256) fp8_quantize_kernel(const T* __restrict__ src, int64_t n,
+                                                           flux_fp8_tensor* rec, uint8_t* __restrict__ dst) {
+  const float qs = fp8_scale(rec);
+  const int64_t n16 = n / 16;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t mx = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    float v[16];
+    if constexpr (sizeof(T) == 4) {
+      const float4* p = reinterpret_cast<const float4*>(src) + 4 * i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 f = p[j];
+        v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(src) + 2 * i;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 w = p[j];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * j + 2 * e] = __uint_as_float(ws[e] << 16);
+          v[8 * j + 2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
+        }
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mx = max(mx, abs_bits(v[4 * j + e]));
+        o[j] |= f32_to_e4m3(v[4 * j + e] * qs) << (8 * e);
+      }
+    }
+    reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (blockIdx.x == 0 && (int64_t)threadIdx.x < n - n16 * 16) {
+    const int64_t k = n16 * 16 + threadIdx.x;
+    const float x = load_f32<T>(src + k);
+    mx = max(mx, abs_bits(x));
+    dst[k] = (uint8_t)f32_to_e4m3(x * qs);
+  }
+  mx = wave_max_u32(mx);
+  if ((threadIdx.x & 63) == 0) fp8_amax_raise(rec, __uint_as_float(mx));
+}
+
+hipError_t launch_fp8_quantize(const void* src, int src_dtype, int64_t n, flux_fp8_tensor* rec, uint8_t* dst,
+                               hipStream_t stream) {
+  int64_t blocks = ceil_div(n / 16 > 0 ? n / 16 : 1, 256);
+  if (blocks > 4096) blocks = 4096;
+  TimingScope ts(kKcFp8Cast, stream, (double)n * ((src_dtype == kF32 ? 4.0 : 2.0) + 1.0));
+  if (src_dtype == kF32)
+    hipLaunchKernelGGL(fp8_quantize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const float*>(src), n, rec, dst);
+  else
+    hipLaunchKernelGGL(fp8_quantize_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const bf16_t*>(src), n, rec, dst);
+  return hipGetLastError();
+}
+
+// One thread per record: the amax recorded since the last update enters the
+// history ring, the selected amax (newest entry, or the history maximum with
+// NaN propagating) gives scale = (448 / amax) * 2^-margin when it is finite
+// and positive; the amax is then cleared for the next forward.
+__global__ void fp8_update_kernel(flux_fp8_tensor* recs, int n, int algo, int margin) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  flux_fp8_tensor* t = recs + i;
+  const float a = __uint_as_float(t->amax_bits);
+  const uint32_t pos = t->hist_pos % FLUX_FP8_HISTORY;
+  t->amax_history[pos] = a;
+  t->hist_pos = (pos + 1) % FLUX_FP8_HISTORY;
+  const uint32_t len = t->hist_len < FLUX_FP8_HISTORY ? t->hist_len + 1 : FLUX_FP8_HISTORY;
+  t->hist_len = len;
+  float sel = a;
+  if (algo == 1) {
+    bool nan = false;
+    float m = 0.f;
+    for (uint32_t j = 0; j < len; ++j) {
+      const float h = t->amax_history[j];
+      nan = nan || (h != h);
+      m = h > m ? h : m;
+    }
+    sel = nan ? __uint_as_float(0x7fc00000u) : m;
+  }
+  uint32_t flags = t->flags;
+  if (!(__builtin_isfinite(a))) flags |= FLUX_FP8_NONFINITE;
+  if (__builtin_isfinite(sel) && sel > 0.f) {
+    const float s = ldexpf(448.0f / sel, -margin);
+    t->scale = s;
+    t->scale_inv = 1.0f / s;
+    flags |= FLUX_FP8_SCALE_SET;
+  }
+  t->flags = flags;
+  t->amax_bits = 0u;
+}
+
+hipError_t launch_fp8_update(flux_fp8_tensor* rec, int n, int algo, int margin, hipStream_t stream) {
+  TimingScope ts(kKcMisc, stream);
+  hipLaunchKernelGGL(fp8_update_kernel, dim3((unsigned)ceil_div(n, 64)), dim3(64), 0, stream, rec, n, algo, margin);
   return hipGetLastError();
 }
 

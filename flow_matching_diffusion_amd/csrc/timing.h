@@ -15,6 +15,8 @@ enum KernelClass : int {
   kKcPrep,
   kKcRf,
   kKcMisc,
+  kKcGemmPkFp8,       // gemm_fp8_kernel (E4M3 operands)
+  kKcFp8Cast,         // fp8 quantization of a whole tensor (weight cast)
   kKcCount
 };
 

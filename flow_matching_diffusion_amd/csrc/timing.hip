@@ -36,7 +36,7 @@ hipEvent_t take_event() {
 
 const char* kNames[kKcCount] = {"gemm_pk_f16", "gemm_pk_bf16", "gemm_128x128", "gemm_f32", "attention",
                                 "ln_modulate",       "gemv",              "qk_prep",  "rf_noise_loss",
-                                "misc"};
+                                "misc",        "gemm_pk_fp8",       "fp8_quantize"};
 }  // namespace
 
 TimingScope::TimingScope(int cls, hipStream_t s, double work) : cls_(cls), work_(work), stream_(s), start_(nullptr) {

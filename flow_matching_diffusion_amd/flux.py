@@ -22,6 +22,15 @@ FLUX_ERR_WORKSPACE_TOO_SMALL = 3
 FLUX_ERR_HIP = 4
 FLUX_PREC_F32 = 0
 FLUX_PREC_BF16 = 1
+FLUX_PREC_FP8_E4M3 = 2
+
+# flux_fp8_tensor: 8 words of state then the 1024-entry amax history
+FLUX_FP8_HISTORY = 1024
+FLUX_FP8_SCALE_SET = 1
+FLUX_FP8_NONFINITE = 2
+FP8_TENSOR_BYTES = 32 + 4 * FLUX_FP8_HISTORY
+FP8_STREAM_SLOTS = ("qkv_x", "qkv_w", "proj_x", "proj_w", "fc1_x", "fc1_w", "fc2_x", "fc2_w")
+FP8_SINGLE_SLOTS = ("lin1_x", "lin1_w", "lin2_x", "lin2_w")
 
 # every symbol include/flux.h declares
 EXPORTED = (
@@ -30,6 +39,7 @@ EXPORTED = (
     "flux_rf_workspace_bytes", "flux_embed_workspace_bytes", "flux_final_workspace_bytes",
     "flux_attention_workspace_bytes", "flux_status_string", "flux_last_error", "flux_timing_enable",
     "flux_timing_classes", "flux_timing_class_name", "flux_timing_read", "flux_convert_bf16_to_f16",
+    "flux_fp8_state_bytes", "flux_fp8_quantize", "flux_fp8_update", "flux_fp8_linear_fwd",
 )
 
 
@@ -55,12 +65,12 @@ class flux_dims(C.Structure):
 
 class flux_stream_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "qkv_w", "qkv_b", "q_norm", "k_norm", "proj_w",
-                                          "proj_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+                                          "proj_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b", "fp8")]
 
 
 class flux_single_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "lin1_w", "lin1_b", "q_norm", "k_norm", "lin2_w",
-                                          "lin2_b")]
+                                          "lin2_b", "fp8")]
 
 
 class rf_args(C.Structure):
@@ -104,12 +114,17 @@ def lib() -> C.CDLL:
         "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
         "flux_attention_fwd": [i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, sz, vp],
         "flux_convert_bf16_to_f16": [vp, vp, i64, vp],
+        "flux_fp8_quantize": [i32, vp, i64, vp, vp, vp],
+        "flux_fp8_update": [vp, i32, i32, i32, vp],
+        "flux_fp8_linear_fwd": [i32, i32, i32, vp, i64, vp, i64, vp, vp, vp, vp, i64, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = C.c_int
     L.flux_workspace_bytes.argtypes = [P(flux_dims), i32]
+    L.flux_fp8_state_bytes.argtypes = [i32]
+    L.flux_fp8_state_bytes.restype = sz
     L.flux_workspace_bytes.restype = sz
     L.flux_rf_workspace_bytes.argtypes = [i32, i64]
     L.flux_rf_workspace_bytes.restype = sz
@@ -171,30 +186,37 @@ def make_dims(batch, l_img, l_txt, hidden, heads, head_dim, mlp_hidden, axes_dim
     return d
 
 
+def precision_code(name: str) -> int:
+    return {"f32": FLUX_PREC_F32, "bf16": FLUX_PREC_BF16, "fp8": FLUX_PREC_FP8_E4M3}[name]
+
+
 def dims_for(wl, batch: Optional[int] = None, weights_f16: bool = False) -> flux_dims:
     """flux_dims of a synth.Workload."""
     return make_dims(batch or wl.batch, wl.l_img, wl.l_txt, wl.hidden, wl.heads, wl.head_dim, wl.mlp_hidden,
-                     wl.axes_dim, wl.theta, wl.eps, FLUX_PREC_F32 if wl.precision == "f32" else FLUX_PREC_BF16,
-                     weights_f16)
+                     wl.axes_dim, wl.theta, wl.eps, precision_code(wl.precision), weights_f16)
 
 
-def stream_weights(w: Dict[str, object], prefix: str) -> flux_stream_weights:
+def stream_weights(w: Dict[str, object], prefix: str, fp8=None) -> flux_stream_weights:
+    """fp8: device address of the stream's 8 flux_fp8_tensor records (fp8 dims only)."""
     s = flux_stream_weights()
     for f in ("mod", "qkv", "proj", "fc1", "fc2"):
         setattr(s, f + "_w", ptr(w[f"{prefix}_{f}.w"]))
         setattr(s, f + "_b", ptr(w[f"{prefix}_{f}.b"]))
     s.q_norm = ptr(w[f"{prefix}_q_norm"])
     s.k_norm = ptr(w[f"{prefix}_k_norm"])
+    s.fp8 = ptr(fp8)
     return s
 
 
-def single_weights(w: Dict[str, object]) -> flux_single_weights:
+def single_weights(w: Dict[str, object], fp8=None) -> flux_single_weights:
+    """fp8: device address of the block's 4 flux_fp8_tensor records (fp8 dims only)."""
     s = flux_single_weights()
     for f in ("mod", "lin1", "lin2"):
         setattr(s, f + "_w", ptr(w[f + ".w"]))
         setattr(s, f + "_b", ptr(w[f + ".b"]))
     s.q_norm = ptr(w["q_norm"])
     s.k_norm = ptr(w["k_norm"])
+    s.fp8 = ptr(fp8)
     return s
 
 
@@ -302,3 +324,34 @@ def flux_timing_read() -> Dict[str, tuple]:
 
 def flux_convert_bf16_to_f16(src, dst, n: int, stream=None) -> None:
     _check(lib().flux_convert_bf16_to_f16(ptr(src), ptr(dst), n, _stream(stream)), "flux_convert_bf16_to_f16")
+
+
+# --------------------------------------------------------------------------- #
+# fp8 (E4M3) delayed scaling
+# --------------------------------------------------------------------------- #
+def flux_fp8_state_bytes(n_tensors: int) -> int:
+    return lib().flux_fp8_state_bytes(n_tensors)
+
+
+def flux_fp8_quantize(src_precision: int, src, n: int, rec, dst, stream=None) -> None:
+    _check(lib().flux_fp8_quantize(src_precision, ptr(src), n, ptr(rec), ptr(dst), _stream(stream)),
+           "flux_fp8_quantize")
+
+
+def flux_fp8_update(recs, n_tensors: int, algo: int = 0, margin: int = 0, stream=None) -> None:
+    _check(lib().flux_fp8_update(ptr(recs), n_tensors, algo, margin, _stream(stream)), "flux_fp8_update")
+
+
+def flux_fp8_linear_fwd(m, n, k, x, ldx, w, ldw, rx, rw, b, y, ldy, stream=None) -> None:
+    _check(lib().flux_fp8_linear_fwd(m, n, k, ptr(x), ldx, ptr(w), ldw, ptr(rx), ptr(rw), ptr(b), ptr(y), ldy,
+                                     _stream(stream)), "flux_fp8_linear_fwd")
+
+
+def fp8_record_fields(raw: bytes) -> dict:
+    """Decode one flux_fp8_tensor record copied to the host (for tests and
+    diagnostics): scale, scale_inv, amax, flags, hist_len, hist_pos, history."""
+    import struct
+    scale, scale_inv, amax_bits, flags, hist_len, hist_pos = struct.unpack_from("<ffIIII", raw, 0)
+    hist = struct.unpack_from(f"<{FLUX_FP8_HISTORY}f", raw, 32)
+    return {"scale": scale, "scale_inv": scale_inv, "amax": struct.unpack("<f", struct.pack("<I", amax_bits))[0],
+            "flags": flags, "hist_len": hist_len, "hist_pos": hist_pos, "history": hist}

@@ -33,6 +33,7 @@ def upload_weights(w: Dict[str, np.ndarray], bf16: bool, device="cuda") -> Dict[
 
 
 def precision_of(wl: synth.Workload) -> int:
+    """Precision of the embedding / head calls (fp8 workloads keep those in bf16)."""
     return F.FLUX_PREC_F32 if wl.precision == "f32" else F.FLUX_PREC_BF16
 
 
@@ -66,28 +67,89 @@ def to_f16_weights(w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
     return out
 
 
+# token-path linears of a double-block stream and of a single block, in the
+# order of their fp8 state slots (input X then weight W of each)
+FP8_DOUBLE = ("qkv", "proj", "fc1", "fc2")
+FP8_SINGLE = ("lin1", "lin2")
+
+
 class BlockStack:
     """Double and single blocks of one workload, weights resident on the GPU.
 
     weights_f16: hold the block linears' weights in fp16, converted once here,
-    instead of converting bf16 tiles inside every GEMM (bf16 workloads only)."""
+    instead of converting bf16 tiles inside every GEMM (bf16 workloads only).
+
+    fp8 workloads keep bf16 master weights and E4M3 copies of the token-path
+    linears, plus one zero-initialised delayed-scaling state buffer: 8 records
+    per double-block stream (image then text), 4 per single block.  A forward
+    under the recipe is fp8_cast_weights() -> blocks -> fp8_update()."""
 
     def __init__(self, wl: synth.Workload, double_ws: List[Dict[str, np.ndarray]],
                  single_ws: List[Dict[str, np.ndarray]], device="cuda", weights_f16: bool = False):
         self.wl = wl
         self.bf16 = wl.precision != "f32"
-        weights_f16 = weights_f16 and self.bf16
+        self.fp8 = wl.precision == "fp8"
+        weights_f16 = weights_f16 and wl.precision == "bf16"
         self.dims = F.dims_for(wl, weights_f16=weights_f16)
         self.double = [upload_weights(w, self.bf16, device) for w in double_ws]
         self.single = [upload_weights(w, self.bf16, device) for w in single_ws]
         if weights_f16:
             self.double = [to_f16_weights(w) for w in self.double]
             self.single = [to_f16_weights(w) for w in self.single]
-        self._dstructs = [(F.stream_weights(w, "img"), F.stream_weights(w, "txt")) for w in self.double]
-        self._sstructs = [F.single_weights(w) for w in self.single]
+        self.fp8_state = None
+        if self.fp8:
+            n = len(self.double) * 2 * len(F.FP8_STREAM_SLOTS) + len(self.single) * len(F.FP8_SINGLE_SLOTS)
+            self.fp8_tensors = n
+            self.fp8_state = torch.zeros(F.flux_fp8_state_bytes(n), dtype=torch.uint8, device=device)
+            self._fp8_casts = []           # (master bf16, e4m3 copy, W record address)
+            self._dq = [self._fp8_copies(w, ("img", "txt"), FP8_DOUBLE, 2 * 8 * i, 8)
+                        for i, w in enumerate(self.double)]
+            base = len(self.double) * 16
+            self._sq = [self._fp8_copies(w, (None,), FP8_SINGLE, base + 4 * i, 4) for i, w in enumerate(self.single)]
+            self._dstructs = [(F.stream_weights(q, "img", self.fp8_record(2 * 8 * i)),
+                               F.stream_weights(q, "txt", self.fp8_record(2 * 8 * i + 8)))
+                              for i, q in enumerate(self._dq)]
+            self._sstructs = [F.single_weights(q, self.fp8_record(base + 4 * i)) for i, q in enumerate(self._sq)]
+        else:
+            self._dstructs = [(F.stream_weights(w, "img"), F.stream_weights(w, "txt")) for w in self.double]
+            self._sstructs = [F.single_weights(w) for w in self.single]
         self.ws = Workspace(device)
         self.ws_bytes = max(F.flux_workspace_bytes(self.dims, 0), F.flux_workspace_bytes(self.dims, 1))
         self.device = device
+
+    # ------------------------------------------------------------------ fp8
+    def fp8_record(self, index: int) -> int:
+        """Device address of state record `index`."""
+        return self.fp8_state.data_ptr() + index * F.FP8_TENSOR_BYTES
+
+    def _fp8_copies(self, w, prefixes, names, first, per_prefix):
+        """Dict like w with the token-path linear weights replaced by E4M3
+        copies (filled by fp8_cast_weights)."""
+        out = dict(w)
+        for pi, pre in enumerate(prefixes):
+            for li, n in enumerate(names):
+                key = f"{pre}_{n}.w" if pre else f"{n}.w"
+                if key not in w:
+                    continue
+                q = torch.empty(w[key].shape, dtype=torch.uint8, device=w[key].device)
+                out[key] = q
+                self._fp8_casts.append((w[key], q, self.fp8_record(first + pi * per_prefix + 2 * li + 1)))
+        return out
+
+    def fp8_cast_weights(self) -> None:
+        """Quantize every token-path weight with its record's current scale
+        (and record its amax): the weight cast of a forward."""
+        for src, dst, rec in self._fp8_casts:
+            F.flux_fp8_quantize(F.FLUX_PREC_BF16, src, src.numel(), rec, dst)
+
+    def fp8_update(self, algo: int = 0, margin: int = 0) -> None:
+        """Delayed-scaling update of every record after a forward."""
+        F.flux_fp8_update(self.fp8_state, self.fp8_tensors, algo, margin)
+
+    def fp8_records(self) -> List[dict]:
+        raw = self.fp8_state.cpu().numpy().tobytes()
+        return [F.fp8_record_fields(raw[i * F.FP8_TENSOR_BYTES:(i + 1) * F.FP8_TENSOR_BYTES])
+                for i in range(self.fp8_tensors)]
 
     def rope_table(self, ids: torch.Tensor) -> torch.Tensor:
         wl = self.wl
@@ -111,10 +173,16 @@ class BlockStack:
         F.flux_single_fwd(self.dims, self._sstructs[i], x, wl.seq * wl.hidden, vec, rope, ws, ws.numel())
 
     def blocks_fwd(self, x: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor) -> None:
+        """All blocks in order; fp8 workloads cast the weights first and
+        update the scales after."""
+        if self.fp8:
+            self.fp8_cast_weights()
         for i in range(len(self.double)):
             self.double_fwd(i, x, vec, rope)
         for i in range(len(self.single)):
             self.single_fwd(i, x, vec, rope)
+        if self.fp8:
+            self.fp8_update()
 
 
 class FluxModel(BlockStack):

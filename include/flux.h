@@ -2,12 +2,14 @@
  * libflux -- Flux MMDiT block forward and rectified-flow objective on
  * AMD Instinct MI355X (gfx950).  Plain C ABI.
  *
- * What the library computes is defined by two pages:
+ * What the library computes is defined by three pages:
  *   "Flux architecture deep dive" (sections Flow matching framework, Model
- *     components, Mathematical formulation, Implementation details), and
+ *     components, Mathematical formulation, Implementation details),
  *   "Flux model API reference" (FluxConfig key parameters, AdaLN, RMSNorm,
  *     EmbedND, JointSelfAttention, MMDiTLayer, FluxSingleTransformerBlock,
- *     apply_flow_matching_noise, compute_flow_matching_loss).
+ *     apply_flow_matching_noise, compute_flow_matching_loss), and
+ *   "FP8 training for Flux models" (Configuration: E4M3 linears with delayed
+ *     scaling) for FLUX_PREC_FP8_E4M3.
  *
  * Conventions common to every entry point
  * ---------------------------------------
@@ -28,7 +30,11 @@
  *    fp16's normal range, error below 2^-24 under it), with fp32
  *    accumulation.  fp16 activations keep 3 more mantissa bits than bf16 at
  *    the same matrix-core rate, which the max-abs error bound of the block
- *    outputs needs at Flux-12B widths.  Residual streams, modulation vectors,
+ *    outputs needs at Flux-12B widths.  With FLUX_PREC_FP8_E4M3 the token-path
+ *    linears of the blocks (qkv, proj, fc1, fc2; lin1, lin2) take OCP E4M3FN
+ *    operands (bytes) quantized with per-tensor delayed scales (see
+ *    flux_fp8_tensor); their biases, the modulation linears and attention
+ *    stay bf16.  Residual streams, modulation vectors,
  *    RMSNorm scales, RoPE tables, latents and losses are always float.
  *  - Errors: every argument is validated on the host BEFORE anything is
  *    enqueued.  A failed check returns a non-zero flux_status and enqueues
@@ -58,8 +64,50 @@ typedef enum {
 
 typedef enum {
   FLUX_PREC_F32 = 0,
-  FLUX_PREC_BF16 = 1
+  FLUX_PREC_BF16 = 1,
+  FLUX_PREC_FP8_E4M3 = 2          /* block token-path linears in E4M3, everything else as BF16 */
 } flux_precision;
+
+/*
+ * Delayed-scaling state of one fp8 tensor ("FP8 training for Flux models",
+ * Configuration: fp8 "e4m3", recipe "delayed", margin, amax history length
+ * 1024, amax compute algorithm "most_recent" or "max").  Caller-allocated
+ * device memory; an all-zero record is valid and means scale 1 with an empty
+ * history.
+ *
+ * Quantization of a value v: q = e4m3(fp32(v * scale)), rounded to the nearest
+ * E4M3FN value with ties to even, magnitudes above 448 (infinities included)
+ * saturated to +-448, NaN kept.  Every kernel that quantizes a tensor raises
+ * amax_bits to the largest |v| it saw.  flux_fp8_update then appends that
+ * amax to the history, selects the amax (the new entry, or the history
+ * maximum), sets scale = fp32(448 / amax) * 2^-margin when that amax is finite
+ * and positive (otherwise the scale is kept and FLUX_FP8_NONFINITE is set when
+ * the entry was not finite), and clears amax_bits.  The scale a forward uses
+ * is therefore derived from the amaxes of earlier forwards.
+ */
+#define FLUX_FP8_HISTORY 1024
+#define FLUX_FP8_SCALE_SET 1u     /* flags: scale holds an updated value (else 1 is used) */
+#define FLUX_FP8_NONFINITE 2u     /* flags: a non-finite amax was seen (sticky) */
+typedef struct {
+  float scale;                    /* multiplier applied before rounding; 1 until FLUX_FP8_SCALE_SET */
+  float scale_inv;                /* 1 / scale */
+  uint32_t amax_bits;             /* fp32 bit pattern of the amax since the last update */
+  uint32_t flags;
+  uint32_t hist_len;              /* valid entries of amax_history (<= FLUX_FP8_HISTORY) */
+  uint32_t hist_pos;              /* slot the next entry goes to (ring) */
+  uint32_t reserved[2];
+  float amax_history[FLUX_FP8_HISTORY];
+} flux_fp8_tensor;
+
+/* Record slots.  A double-block stream uses 8 consecutive records, a single
+ * block 4: the input (X) and the weight (W) of each token-path linear. */
+enum {
+  FLUX_FP8_QKV_X = 0, FLUX_FP8_QKV_W = 1, FLUX_FP8_PROJ_X = 2, FLUX_FP8_PROJ_W = 3,
+  FLUX_FP8_FC1_X = 4, FLUX_FP8_FC1_W = 5, FLUX_FP8_FC2_X = 6, FLUX_FP8_FC2_W = 7,
+  FLUX_FP8_STREAM_TENSORS = 8,
+  FLUX_FP8_LIN1_X = 0, FLUX_FP8_LIN1_W = 1, FLUX_FP8_LIN2_X = 2, FLUX_FP8_LIN2_W = 3,
+  FLUX_FP8_SINGLE_TENSORS = 4
+};
 
 /* Shapes of one block call ("Flux model API reference", FluxConfig). */
 typedef struct {
@@ -89,6 +137,10 @@ typedef struct {
   const void* proj_w; const void* proj_b;   /* [D, D], [D] */
   const void* fc1_w;  const void* fc1_b;    /* [F, D], [F] */
   const void* fc2_w;  const void* fc2_b;    /* [D, F], [D] */
+  flux_fp8_tensor* fp8;                     /* FLUX_PREC_FP8_E4M3: FLUX_FP8_STREAM_TENSORS records of
+                                               this stream, and qkv_w, proj_w, fc1_w, fc2_w are E4M3
+                                               bytes quantized (flux_fp8_quantize) with the W records'
+                                               current scales; NULL otherwise */
 } flux_stream_weights;
 
 /* Weights of a single block, fused parallel form. */
@@ -97,6 +149,10 @@ typedef struct {
   const void* lin1_w; const void* lin1_b;   /* [3D+F, D], [3D+F]: rows q|k|v|mlp_in */
   const float* q_norm; const float* k_norm; /* [head_dim] */
   const void* lin2_w; const void* lin2_b;   /* [D, D+F], [D]: input columns attn|gelu(mlp_in) */
+  flux_fp8_tensor* fp8;                     /* FLUX_PREC_FP8_E4M3: FLUX_FP8_SINGLE_TENSORS records,
+                                               lin1_w / lin2_w are E4M3 bytes; NULL otherwise.  The
+                                               attention output and GELU(mlp_in) are one tensor (the
+                                               input of lin2) with one scale. */
 } flux_single_weights;
 
 /*
@@ -257,6 +313,35 @@ flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, in
  * pointers, 16-byte aligned, not overlapping.
  */
 flux_status flux_convert_bf16_to_f16(const void* src, void* dst, int64_t n, void* stream);
+
+/*
+ * FP8 (E4M3) delayed scaling ("FP8 training for Flux models", Configuration).
+ *
+ * flux_fp8_state_bytes -- bytes of n consecutive flux_fp8_tensor records.
+ *
+ * flux_fp8_quantize -- dst[i] = e4m3(src[i] * scale(rec)) for n elements and
+ *   rec->amax_bits raised to max |src[i]| (the weight cast of a forward).
+ *   src_precision FLUX_PREC_F32 (float) or FLUX_PREC_BF16; src, dst 16-byte
+ *   aligned, not overlapping; n >= 1.
+ *
+ * flux_fp8_update -- the update described at flux_fp8_tensor for n
+ *   consecutive records; algo 0 = most_recent, 1 = max; 0 <= margin <= 32.
+ *   Run it after a forward, on the same stream.
+ *
+ * flux_fp8_linear_fwd -- y = (x_q w_q^T) * scale_inv(rx) * scale_inv(rw) + b:
+ *   x_q [M, K] E4M3 bytes (row stride ldx), w_q [N, K] E4M3 bytes (row stride
+ *   ldw), quantized with the records rx and rw; b [N] bf16 or NULL; y [M, N]
+ *   float (row stride ldy).  K a multiple of 64, N a multiple of 4.
+ */
+size_t flux_fp8_state_bytes(int32_t n_tensors);
+flux_status flux_fp8_quantize(int32_t src_precision, const void* src, int64_t n, flux_fp8_tensor* rec,
+                              uint8_t* dst, void* stream);
+flux_status flux_fp8_update(flux_fp8_tensor* recs, int32_t n_tensors, int32_t algo, int32_t margin,
+                            void* stream);
+flux_status flux_fp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* x, int64_t ldx,
+                                const uint8_t* w, int64_t ldw, const flux_fp8_tensor* rx,
+                                const flux_fp8_tensor* rw, const void* b, float* y, int64_t ldy,
+                                void* stream);
 
 /* Workspace sizes (bytes).  op: 0 double block, 1 single block. */
 size_t flux_workspace_bytes(const flux_dims* dims, int32_t op);
