@@ -113,7 +113,9 @@ __device__ __forceinline__ void store4_dt(void* base, int64_t off, int dt, float
 // split epilogue n_split is a multiple of 4, so they fall on one side.
 // dq multiplies the accumulator first (the product of the two operand
 // scale_inv for E4M3 operands, else 1); qs is the E4M3 output scale and mx
-// collects the largest magnitude written as E4M3.
+// collects the largest magnitude written as E4M3.  EPI is the epilogue kind,
+// fixed at compile time so a kernel carries the code of one kind only.
+template <int EPI>
 __device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int col, float4 v, float dq, float qs,
                                            uint32_t& mx) {
   v.x *= dq; v.y *= dq; v.z *= dq; v.w *= dq;
@@ -126,47 +128,48 @@ __device__ __forceinline__ void epi_apply4(const GemmProblem& p, int row, int co
   }
   const int64_t b = row / p.omap0.seg, l = row % p.omap0.seg;
   const int64_t off0 = b * p.omap0.bstride + l * p.omap0.ld;
-  switch (p.epi) {
-    case kEpiStore:
-    case kEpiGelu: {
-      if (p.epi == kEpiGelu) {
-        v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
-      }
+  if constexpr (EPI == kEpiStore || EPI == kEpiGelu) {
+    if constexpr (EPI == kEpiGelu) {
+      v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
+    }
+    store4_dt(p.out0, off0 + col, p.out0_dt, v, qs, mx);
+  } else if constexpr (EPI == kEpiResid) {
+    float4* x = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out0) + off0 + col);
+    const float4 g = *reinterpret_cast<const float4*>(p.gate + b * p.gate_bstride + col);
+    float4 r = *x;
+    r.x += g.x * v.x; r.y += g.y * v.y; r.z += g.z * v.z; r.w += g.w * v.w;
+    *x = r;
+  } else if constexpr (EPI == kEpiStoreF32) {
+    float* o = reinterpret_cast<float*>(p.out0) + off0;
+    if (p.col_stride0 == 1) {
+      *reinterpret_cast<float4*>(o + col) = v;
+    } else {
+      o[(int64_t)col * p.col_stride0] = v.x;
+      o[(int64_t)(col + 1) * p.col_stride0] = v.y;
+      o[(int64_t)(col + 2) * p.col_stride0] = v.z;
+      o[(int64_t)(col + 3) * p.col_stride0] = v.w;
+    }
+  } else if constexpr (EPI == kEpiSplitGelu) {
+    if (col < p.n_split) {
       store4_dt(p.out0, off0 + col, p.out0_dt, v, qs, mx);
-      break;
+    } else {
+      const int64_t b1 = row / p.omap1.seg, l1 = row % p.omap1.seg;
+      v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
+      store4_dt(p.out1, b1 * p.omap1.bstride + l1 * p.omap1.ld + (col - p.n_split), p.out1_dt, v, qs, mx);
     }
-    case kEpiResid: {
-      float4* x = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out0) + off0 + col);
-      const float4 g = *reinterpret_cast<const float4*>(p.gate + b * p.gate_bstride + col);
-      float4 r = *x;
-      r.x += g.x * v.x; r.y += g.y * v.y; r.z += g.z * v.z; r.w += g.w * v.w;
-      *x = r;
-      break;
-    }
-    case kEpiStoreF32: {
-      float* o = reinterpret_cast<float*>(p.out0) + off0;
-      if (p.col_stride0 == 1) {
-        *reinterpret_cast<float4*>(o + col) = v;
-      } else {
-        o[(int64_t)col * p.col_stride0] = v.x;
-        o[(int64_t)(col + 1) * p.col_stride0] = v.y;
-        o[(int64_t)(col + 2) * p.col_stride0] = v.z;
-        o[(int64_t)(col + 3) * p.col_stride0] = v.w;
-      }
-      break;
-    }
-    case kEpiSplitGelu: {
-      if (col < p.n_split) {
-        store4_dt(p.out0, off0 + col, p.out0_dt, v, qs, mx);
-      } else {
-        const int64_t b1 = row / p.omap1.seg, l1 = row % p.omap1.seg;
-        v.x = gelu_f(v.x); v.y = gelu_f(v.y); v.z = gelu_f(v.z); v.w = gelu_f(v.w);
-        store4_dt(p.out1, b1 * p.omap1.bstride + l1 * p.omap1.ld + (col - p.n_split), p.out1_dt, v, qs, mx);
-      }
-      break;
-    }
-    default:
-      break;
+  }
+}
+
+// The same with the kind read at run time (the small-problem kernel).
+__device__ __forceinline__ void epi_apply4_any(const GemmProblem& p, int row, int col, float4 v, float dq, float qs,
+                                               uint32_t& mx) {
+  switch (p.epi) {
+    case kEpiStore: epi_apply4<kEpiStore>(p, row, col, v, dq, qs, mx); break;
+    case kEpiGelu: epi_apply4<kEpiGelu>(p, row, col, v, dq, qs, mx); break;
+    case kEpiResid: epi_apply4<kEpiResid>(p, row, col, v, dq, qs, mx); break;
+    case kEpiStoreF32: epi_apply4<kEpiStoreF32>(p, row, col, v, dq, qs, mx); break;
+    case kEpiSplitGelu: epi_apply4<kEpiSplitGelu>(p, row, col, v, dq, qs, mx); break;
+    default: break;
   }
 }
 
@@ -381,7 +384,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
       const int row = m0 + wm * WM + i * 32 + rr;
       if (row < p.M && col < p.N) {
         const float4 v = *reinterpret_cast<const float4*>(&cs[rr * CLD + c4]);
-        epi_apply4(p, row, col, v, dq, qs, mx);
+        epi_apply4_any(p, row, col, v, dq, qs, mx);
       }
     }
     __syncthreads();
@@ -409,12 +412,61 @@ __device__ __forceinline__ int dl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3;
 // s_waitcnt vmcnt(n) leaving expcnt / lgkmcnt unconstrained (gfx9 encoding)
 #define DL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
+// Epilogue of one 256 x 256 tile of the persistent kernels.  Each wave owns a
+// 128 x 128 block of 4 x 4 accumulator tiles; its 8 quarters (32 rows x 64
+// columns) pass one at a time through the wave's 8 KB of LDS staging
+// (accumulator element e of lane l in a 32x32 tile is row 8*(e/4) +
+// 4*(l/32) + e%4, column l%32), then 4 consecutive columns per lane go
+// through the fused epilogue.  The quarter loop is not unrolled: only the
+// staging (constant register indices) is replicated, so the kernel's code
+// stays small enough for the instruction cache.
+template <int Q>
+__device__ __forceinline__ void stage_quarter(const f32x16_t (&acc)[4][4], float* cs, int frow, int fhalf) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[Q >> 1][2 * (Q & 1) + jj][e];
+}
+
+template <int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x16_t (&acc)[4][4], float* cs,
+                                              int row0, int col0, int lane, float dq, float qs, uint32_t& mx) {
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int c4 = (lane & 15) * 4;
+#pragma unroll 1
+  for (int q = 0; q < 8; ++q) {
+    switch (q) {
+      case 0: stage_quarter<0>(acc, cs, frow, fhalf); break;
+      case 1: stage_quarter<1>(acc, cs, frow, fhalf); break;
+      case 2: stage_quarter<2>(acc, cs, frow, fhalf); break;
+      case 3: stage_quarter<3>(acc, cs, frow, fhalf); break;
+      case 4: stage_quarter<4>(acc, cs, frow, fhalf); break;
+      case 5: stage_quarter<5>(acc, cs, frow, fhalf); break;
+      case 6: stage_quarter<6>(acc, cs, frow, fhalf); break;
+      default: stage_quarter<7>(acc, cs, frow, fhalf); break;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
+    __builtin_amdgcn_sched_barrier(0);
+    const int col = col0 + (q & 1) * 64 + c4;
+#pragma unroll 1
+    for (int rr = lane >> 4; rr < 32; rr += 4) {
+      const int row = row0 + (q >> 1) * 32 + rr;
+      if (row < pc.M && col < pc.N) {
+        const float4 v = *reinterpret_cast<const float4*>(&cs[rr * 64 + c4]);
+        epi_apply4<EPI>(pc, row, col, v, dq, qs, mx);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next quarter overwrites the staging
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Persistent kernel: one block per CU walks the tiles t = blockIdx.x,
 // blockIdx.x + gridDim.x, ...  The first four stages of the next tile are
 // issued as soon as every wave has finished reading the current tile, so
 // their latency overlaps the epilogue, which stages the accumulators through
 // the fifth stage (left alone by that prefetch).
-template <int OP>
+template <int OP, int EPI>
 __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
   __shared__ __attribute__((aligned(1024))) char smem[kDlStages * kDlStageBytes];
@@ -568,40 +620,12 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
       prologue_issue();
     }
 
-    // Epilogue through stage 4, which the next tile's prologue leaves alone:
-    // each wave stages a 32 x 64 quarter of its 128 x 128 accumulator block
-    // (element e of lane l in a 32x32 MFMA tile is row 8*(e/4) + 4*(l/32) +
-    // e%4, column l%32), then applies the fused epilogue to 4 consecutive
-    // columns per lane.  Only the wave itself reads its region.
+    // epilogue through stage 4, which the next tile's prologue leaves alone
     GemmProblem pc = bt.p[0];
     if (cprob) pc = bt.p[1];
-    float* cs = reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64;
     uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[i][2 * h + jj][e];
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
-        __builtin_amdgcn_sched_barrier(0);
-        const int c4 = (lane & 15) * 4;
-        const int col = cn0 + wn * WN + h * 64 + c4;
-#pragma unroll 1
-        for (int rr = lane >> 4; rr < 32; rr += 4) {
-          const int row = cm0 + wm * WM + i * 32 + rr;
-          if (row < pc.M && col < pc.N) {
-            const float4 v = *reinterpret_cast<const float4*>(&cs[rr * 64 + c4]);
-            epi_apply4(pc, row, col, v, 1.0f, 1.0f, mx);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64,
+                       cm0 + wm * WM, cn0 + wn * WN, lane, 1.0f, 1.0f, mx);
   }
 }
 
@@ -617,6 +641,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 template <int S> using SetTag = std::integral_constant<int, S>;
 
+template <int EPI>
 __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
   constexpr int BK8 = 64;   // k values (bytes) per stage row
@@ -756,22 +781,18 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
     }
     __syncthreads();
     lfrag(0, SetTag<0>{});
-    // KT is even (the launcher sends K % 128 != 0 elsewhere).  Steady state:
-    // both steps of a pair refill; then 4 or 2 steps remain.
+    // KT is even and at least 4 (the launcher sends other K elsewhere).
+    // Steady state: both steps of a pair refill; exactly 4 steps remain after
+    // it, run straight-line so the accumulators never take two paths.
     int kt = 0;
     for (; kt + 5 < KT; kt += 2) {
       body(kt, SetTag<0>{}, V16{}, T_{}, T_{});
       body(kt + 1, SetTag<1>{}, V16{}, T_{}, T_{});
     }
-    if (KT - kt == 4) {
-      body(kt, SetTag<0>{}, V16{}, T_{}, F_{});
-      body(kt + 1, SetTag<1>{}, V8{}, T_{}, F_{});
-      body(kt + 2, SetTag<0>{}, V0{}, T_{}, F_{});
-      body(kt + 3, SetTag<1>{}, V0{}, F_{}, F_{});
-    } else {
-      body(kt, SetTag<0>{}, V0{}, T_{}, F_{});
-      body(kt + 1, SetTag<1>{}, V0{}, F_{}, F_{});
-    }
+    body(kt, SetTag<0>{}, V16{}, T_{}, F_{});
+    body(kt + 1, SetTag<1>{}, V8{}, T_{}, F_{});
+    body(kt + 2, SetTag<0>{}, V0{}, T_{}, F_{});
+    body(kt + 3, SetTag<1>{}, V0{}, F_{}, F_{});
 
     // tile done: every wave has read its last fragments once it passes this
     // barrier, so the stages may be refilled for the next tile
@@ -785,34 +806,9 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
     // epilogue through stage 4, as in gemm_pk_kernel
     GemmProblem pc = bt.p[0];
     if (cprob) pc = bt.p[1];
-    const float dq = epi_dequant(pc), qs = epi_out_scale(pc);
     uint32_t mx = 0;
-    float* cs = reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[i][2 * h + jj][e];
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
-        __builtin_amdgcn_sched_barrier(0);
-        const int c4 = (lane & 15) * 4;
-        const int col = cn0 + wn * WN + h * 64 + c4;
-#pragma unroll 1
-        for (int rr = lane >> 4; rr < 32; rr += 4) {
-          const int row = cm0 + wm * WM + i * 32 + rr;
-          if (row < pc.M && col < pc.N) {
-            const float4 v = *reinterpret_cast<const float4*>(&cs[rr * 64 + c4]);
-            epi_apply4(pc, row, col, v, dq, qs, mx);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64,
+                       cm0 + wm * WM, cn0 + wn * WN, lane, epi_dequant(pc), epi_out_scale(pc), mx);
     epi_amax_flush(pc, mx);
   }
 }
@@ -895,22 +891,31 @@ static double gemm_flops(const GemmBatch& bt) {
   return f;
 }
 
+template <int OP, int EPI>
+static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream) {
+  if constexpr (OP == kFP8)
+    hipLaunchKernelGGL((gemm_fp8_kernel<EPI>), dim3(grid), dim3(256), 0, stream, big);
+  else
+    hipLaunchKernelGGL((gemm_pk_kernel<OP, EPI>), dim3(grid), dim3(256), 0, stream, big);
+}
+
 template <int OP>
 static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   GemmBatch big = bt;
   const int tiles_big = assign_tiles(big, 256, 256);
   bool seg_ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
   for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].omap0.seg >= 32;
-  if constexpr (OP == kFP8)   // gemm_fp8_kernel walks k in pairs of 64-wide steps
-    for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K % 128 == 0;
+  if constexpr (OP == kFP8)   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
+    for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K % 128 == 0 && big.p[i].K >= 256;
   if (tiles_big >= 128 && seg_ok) {   // at least half the CUs get a 256 x 256 tile
     const int grid = tiles_big < 256 ? tiles_big : 256;
-    if constexpr (OP == kFP8) {
-      TimingScope ts(kKcGemmPkFp8, stream, flops);
-      hipLaunchKernelGGL(gemm_fp8_kernel, dim3(grid), dim3(256), 0, stream, big);
-    } else {
-      TimingScope ts(OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
-      hipLaunchKernelGGL((gemm_pk_kernel<OP>), dim3(grid), dim3(256), 0, stream, big);
+    TimingScope ts(OP == kFP8 ? kKcGemmPkFp8 : OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
+    switch (big.p[0].epi) {   // the problems of one launch share the epilogue kind
+      case kEpiStore: launch_persistent<OP, kEpiStore>(big, grid, stream); break;
+      case kEpiGelu: launch_persistent<OP, kEpiGelu>(big, grid, stream); break;
+      case kEpiResid: launch_persistent<OP, kEpiResid>(big, grid, stream); break;
+      case kEpiStoreF32: launch_persistent<OP, kEpiStoreF32>(big, grid, stream); break;
+      default: launch_persistent<OP, kEpiSplitGelu>(big, grid, stream); break;
     }
   } else {
     const int tiles = assign_tiles(bt, 128, 128);
