@@ -11,10 +11,11 @@
 // block) share one grid; the tile order keeps each XCD on a contiguous tile
 // range and walks tiles in groups of 8 tile rows so A and W panels are reused
 // from L2.
-//  * large problems: gemm_pk_kernel, persistent (one 256-thread block per CU),
-//    256 x 256 tiles, 5-stage LDS ring of 32-wide k steps filled by direct
-//    global->LDS loads three steps ahead, MFMA fragment reads interleaved with
-//    the MFMAs, next tile's loads overlapping the current epilogue;
+//  * large problems: gemm_rs_kernel, persistent (one 256-thread block per CU),
+//    256 x 256 tiles; operands staged global -> VGPR -> LDS in k = 64
+//    super-stages (two 64 KB LDS slots), MFMA fragment reads, LDS writes and
+//    global loads interleaved one-by-one with the MFMAs; the next tile's first
+//    loads overlap the current epilogue;
 //  * small problems: gemm_mfma_kernel, 128 x 128 tiles, register-staged
 //    double buffer.
 // fp32 path (fp32 workloads only): LDS-tiled FMA kernel with the same epilogues.
@@ -404,10 +405,16 @@ constexpr int kDlRows = 256;              // BM = BN
 constexpr int kDlStageBytes = 2 * kDlRows * kDlBK * 2;   // A + B, 32 KB
 
 // Stage layout: rows of 64 bytes (4 chunks of 16 B), A rows 0..255 then B rows
-// 0..255.  Logical chunk c of row r sits at physical chunk c ^ swz(r): a
-// 16-byte read of one chunk by 16 consecutive rows then touches 16 distinct
-// 4-bank groups with 64 banks, 8 consecutive rows with 32 banks.
-__device__ __forceinline__ int dl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 0..255.  Logical chunk c of row r sits at physical chunk c ^ ((r >> 2) & 3).
+// gfx950 serves a 16-byte-per-lane LDS read in four cycles of 16 lanes each
+// (64 banks of 4 bytes); measured on MI355X with the LDS bank-conflict
+// counter, the lanes of one cycle are those with equal lane bit 5 and equal
+// (bit 4 xor bit 2).  A fragment read (lane l -> row l % 32, chunk c or c+1)
+// then hits 16 distinct 4-bank groups in every cycle: rows r and r + 16 of one
+// cycle differ in (r >> 2) & 3 or in r % 4.  The global->LDS fill (lane l ->
+// row l / 4, a whole 64-byte row per 4 lanes) is conflict-free for any
+// in-row permutation.
+__device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
 
 // s_waitcnt vmcnt(n) leaving expcnt / lgkmcnt unconstrained (gfx9 encoding)
 #define DL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
@@ -428,52 +435,166 @@ __device__ __forceinline__ void stage_quarter(const f32x16_t (&acc)[4][4], float
     for (int e = 0; e < 16; ++e) cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[Q >> 1][2 * (Q & 1) + jj][e];
 }
 
+// The fused epilogue of one staged quarter (32 rows x 64 columns, read from
+// the wave's LDS staging cs) for the lane's 8 rows rbase + 4u and four
+// columns col..col+3, whose bias bq and gate gq come in as values.  All
+// residual rows are loaded before any is updated, so their latencies overlap.
+template <int EPI>
+__device__ __forceinline__ void apply_quarter(const GemmProblem& pc, const float* cs, int lrow, int c4, int rbase,
+                                              int col, float4 bq, float4 gq, bool uniform, float dq, float qs,
+                                              uint32_t& mx) {
+  const int seg = pc.omap0.seg;
+  const bool col_ok = col < pc.N;
+  float4 xr[8];
+  if constexpr (EPI == kEpiResid) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = rbase + 4 * u;
+      xr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row < pc.M && col_ok) {
+        const int64_t b = row / seg, l = row % seg;
+        xr[u] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(pc.out0) + b * pc.omap0.bstride +
+                                                 l * pc.omap0.ld + col);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = rbase + 4 * u;
+    if (row < pc.M && col_ok) {
+      const int64_t b = row / seg, l = row % seg;
+      const int64_t off0 = b * pc.omap0.bstride + l * pc.omap0.ld;
+      float4 w = *reinterpret_cast<const float4*>(&cs[(lrow + 4 * u) * 64 + c4]);
+      w.x = w.x * dq + bq.x; w.y = w.y * dq + bq.y;
+      w.z = w.z * dq + bq.z; w.w = w.w * dq + bq.w;
+      if constexpr (EPI == kEpiResid) {
+        float4 g = gq;   // assigned in a branch: a conditional lvalue would put gq in scratch memory
+        if (!uniform) g = *reinterpret_cast<const float4*>(pc.gate + b * pc.gate_bstride + col);
+        float4 r = xr[u];
+        r.x += g.x * w.x; r.y += g.y * w.y; r.z += g.z * w.z; r.w += g.w * w.w;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(pc.out0) + off0 + col) = r;
+      } else if constexpr (EPI == kEpiStore || EPI == kEpiGelu) {
+        if constexpr (EPI == kEpiGelu) {
+          w.x = gelu_f(w.x); w.y = gelu_f(w.y); w.z = gelu_f(w.z); w.w = gelu_f(w.w);
+        }
+        store4_dt(pc.out0, off0 + col, pc.out0_dt, w, qs, mx);
+      } else if constexpr (EPI == kEpiStoreF32) {
+        float* o = reinterpret_cast<float*>(pc.out0) + off0;
+        if (pc.col_stride0 == 1) {
+          *reinterpret_cast<float4*>(o + col) = w;
+        } else {
+          o[(int64_t)col * pc.col_stride0] = w.x;
+          o[(int64_t)(col + 1) * pc.col_stride0] = w.y;
+          o[(int64_t)(col + 2) * pc.col_stride0] = w.z;
+          o[(int64_t)(col + 3) * pc.col_stride0] = w.w;
+        }
+      } else if constexpr (EPI == kEpiSplitGelu) {
+        if (col < pc.n_split) {
+          store4_dt(pc.out0, off0 + col, pc.out0_dt, w, qs, mx);
+        } else {
+          const int64_t b1 = row / pc.omap1.seg, l1 = row % pc.omap1.seg;
+          w.x = gelu_f(w.x); w.y = gelu_f(w.y); w.z = gelu_f(w.z); w.w = gelu_f(w.w);
+          store4_dt(pc.out1, b1 * pc.omap1.bstride + l1 * pc.omap1.ld + (col - pc.n_split), pc.out1_dt, w, qs, mx);
+        }
+      }
+    }
+  }
+}
+
 template <int EPI>
 __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x16_t (&acc)[4][4], float* cs,
                                               int row0, int col0, int lane, float dq, float qs, uint32_t& mx) {
   const int frow = lane & 31, fhalf = lane >> 5;
-  const int c4 = (lane & 15) * 4;
+  const int c4 = (lane & 15) * 4, lrow = lane >> 4;
+  // bias and gate of the lane's four columns in each column half, read once
+  // per tile; the gate is that of the sample of the wave's rows (`uniform`
+  // is false when they span two samples, and the gate is then read per row)
+  const int rlast = min(row0 + 127, pc.M - 1);
+  const int64_t b0 = (row0 < pc.M ? row0 : rlast) / pc.omap0.seg;
+  const bool uniform = b0 == rlast / pc.omap0.seg;
+  float4 bias0 = make_float4(0.f, 0.f, 0.f, 0.f), bias1 = bias0, gate0 = bias0, gate1 = bias0;
+  {
+    const int cA = min(col0 + c4, pc.N - 4), cB = min(col0 + 64 + c4, pc.N - 4);
+    if (pc.bias) {
+      const uint2 ba = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(pc.bias) + cA);
+      const uint2 bb = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(pc.bias) + cB);
+      bias0 = make_float4(__uint_as_float(ba.x << 16), __uint_as_float(ba.x & 0xffff0000u),
+                          __uint_as_float(ba.y << 16), __uint_as_float(ba.y & 0xffff0000u));
+      bias1 = make_float4(__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
+                          __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u));
+    }
+    if constexpr (EPI == kEpiResid) {
+      gate0 = *reinterpret_cast<const float4*>(pc.gate + b0 * pc.gate_bstride + cA);
+      gate1 = *reinterpret_cast<const float4*>(pc.gate + b0 * pc.gate_bstride + cB);
+    }
+  }
+  // quarters 2qq (columns 0..63 of the wave) and 2qq + 1 (columns 64..127)
 #pragma unroll 1
-  for (int q = 0; q < 8; ++q) {
-    switch (q) {
+  for (int qq = 0; qq < 4; ++qq) {
+    switch (qq) {
       case 0: stage_quarter<0>(acc, cs, frow, fhalf); break;
-      case 1: stage_quarter<1>(acc, cs, frow, fhalf); break;
-      case 2: stage_quarter<2>(acc, cs, frow, fhalf); break;
-      case 3: stage_quarter<3>(acc, cs, frow, fhalf); break;
-      case 4: stage_quarter<4>(acc, cs, frow, fhalf); break;
-      case 5: stage_quarter<5>(acc, cs, frow, fhalf); break;
-      case 6: stage_quarter<6>(acc, cs, frow, fhalf); break;
-      default: stage_quarter<7>(acc, cs, frow, fhalf); break;
+      case 1: stage_quarter<2>(acc, cs, frow, fhalf); break;
+      case 2: stage_quarter<4>(acc, cs, frow, fhalf); break;
+      default: stage_quarter<6>(acc, cs, frow, fhalf); break;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
     __builtin_amdgcn_sched_barrier(0);
-    const int col = col0 + (q & 1) * 64 + c4;
-#pragma unroll 1
-    for (int rr = lane >> 4; rr < 32; rr += 4) {
-      const int row = row0 + (q >> 1) * 32 + rr;
-      if (row < pc.M && col < pc.N) {
-        const float4 v = *reinterpret_cast<const float4*>(&cs[rr * 64 + c4]);
-        epi_apply4<EPI>(pc, row, col, v, dq, qs, mx);
-      }
-    }
+    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + c4, bias0, gate0, uniform, dq, qs, mx);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next quarter overwrites the staging
+    __builtin_amdgcn_sched_barrier(0);
+    switch (qq) {
+      case 0: stage_quarter<1>(acc, cs, frow, fhalf); break;
+      case 1: stage_quarter<3>(acc, cs, frow, fhalf); break;
+      case 2: stage_quarter<5>(acc, cs, frow, fhalf); break;
+      default: stage_quarter<7>(acc, cs, frow, fhalf); break;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + 64 + c4, bias1, gate1, uniform, dq, qs, mx);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Persistent kernel: one block per CU walks the tiles t = blockIdx.x,
-// blockIdx.x + gridDim.x, ...  The first four stages of the next tile are
-// issued as soon as every wave has finished reading the current tile, so
-// their latency overlaps the epilogue, which stages the accumulators through
-// the fifth stage (left alone by that prefetch).
+// ---------------------------------------------------------------------------
+// Register-staged persistent kernel (16-bit operands): one 256-thread block
+// per CU walks the tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...; 256 x
+// 256 tiles, each wave owning 128 x 128 as 4 x 4 MFMA 32x32x16 tiles.  The
+// operands travel
+// global -> VGPR -> LDS in super-stages of k = 64, so every 8 lanes of a load
+// read one whole 128-byte line of a row.  Measured on MI355X, the block GEMMs
+// were bound by the number of L1->L2 requests: 64-byte row pieces (k = 32
+// per stage) capped them at about 6 TB/s of operand traffic.
+//  * LDS: two super-stage slots of 64 KB, each holding its two k = 32 halves
+//    in the 32 KB stage layout (so fragment reads are unchanged), plus 32 KB
+//    for the epilogue staging.
+//  * A super-stage is 4 slices of 16 MFMAs per wave (k = 16 each).  The
+//    fragments of slice n + 1 are read during slice n.  One barrier per
+//    super-stage, between slices 2 and 3: after it, slot sigma % 2 (whose last
+//    reads are in slice 2) is free, and slice 3 reads the first fragments of
+//    super-stage sigma + 1, written before the barrier.
+//  * One register set R holds one super-stage of this thread's operand
+//    words: during slices 0-2 of super-stage sigma each word of sigma + 1 is
+//    written to LDS and at once reloaded with its word of sigma + 2, so a
+//    load has a whole super-stage (64 MFMAs) to land.
+//  * Each MFMA is followed by at most two memory instructions in a fixed
+//    order (scheduling fences).
+//  * bf16 weights with fp16 activations (kF16) are widened to fp16 as they
+//    are written to LDS.
+//  * Operand rows are addressed as 32-bit byte offsets from the tile's A and
+//    W base pointers (the launcher keeps both spans under 4 GiB).
+// ---------------------------------------------------------------------------
+constexpr int kSsBytes = 2 * kDlStageBytes;   // one super-stage: 64 KB
+
 template <int OP, int EPI>
-__global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
+__global__ void __launch_bounds__(256, 1) gemm_rs_kernel(GemmBatch bt) {
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
-  __shared__ __attribute__((aligned(1024))) char smem[kDlStages * kDlStageBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kSsBytes + kDlStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int frow = lane & 31, fhalf = lane >> 5;
 
+  // fragment offsets within a 32 KB k-half
   int aoff[TM][2], boff[TN][2];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -487,11 +608,22 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) boff[j][kk] = (kDlRows + r) * 64 + (((2 * kk + fhalf) ^ dl_swz(r)) << 4);
   }
+  // Load u (0..15) of this wave covers super-stage rows (wave + 4u) * 8 .. + 7
+  // (A rows 0..255 for u < 8, then W rows), 8 lanes per 128-byte row; lane l
+  // takes row + l / 8 and k chunk cc = l % 8, which lands in k-half cc / 4 at
+  // chunk cc % 4 of the 64-byte stage row (swizzled).  LDS offset of that
+  // 16-byte piece within a super-stage slot, for load u:
+  //   (cc / 4) * 32K + row * 64 + ((cc % 4) ^ swz(row)) * 16,  row = (wave + 4u) * 8 + l / 8
+  // swz(row) = (row >> 2) & 3 does not depend on u (4u * 8 rows is a multiple
+  // of 16), so the offset is a per-lane constant plus u * 2048.
+  const int cc = lane & 7, lrow8 = lane >> 3;
+  const int wbase =
+      (cc >> 2) * kDlStageBytes + (wave * 8 + lrow8) * 64 + (((cc & 3) ^ dl_swz(wave * 8 + lrow8)) << 4);
 
-  // tile state (the problem descriptor itself is re-read from the kernel
-  // arguments where needed, so only these scalars stay live)
-  int prob = 0, m0 = 0, n0 = 0, KT = 0;
-  const char* src[8];
+  int prob = 0, m0 = 0, n0 = 0, NS = 0;
+  const char* abase = nullptr;
+  const char* wbase_g = nullptr;
+  uint32_t soff[16];   // byte offsets of this thread's 16 row pieces from abase / wbase_g
   auto setup = [&](int t) {
     const TileCoord tc = decode_tile_id(bt, t, BM, BN);
     GemmProblem p = bt.p[0];
@@ -499,98 +631,108 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
     prob = tc.prob;
     m0 = tc.tm * BM;
     n0 = tc.tn * BN;
-    KT = p.K / kDlBK;
-    const bf16_t* A = reinterpret_cast<const bf16_t*>(p.A);
-    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.W);
+    NS = p.K / 64;
+    abase = reinterpret_cast<const char*>(p.A);
+    wbase_g = reinterpret_cast<const char*>(p.W);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int ins = wave + 4 * u;
-      const int r = (ins & 15) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ dl_swz(r);
-      if (ins < 16) {
+    for (int u = 0; u < 16; ++u) {
+      const int r = ((wave + 4 * u) & 31) * 8 + lrow8;   // row within the A or W half
+      if (u < 8) {
         int gr = m0 + r;
         gr = gr < p.M ? gr : p.M - 1;
-        src[u] = reinterpret_cast<const char*>(A + (int64_t)(gr / p.amap.seg) * p.amap.bstride +
-                                               (int64_t)(gr % p.amap.seg) * p.amap.ld + c * 8);
+        soff[u] = (uint32_t)(((int64_t)(gr / p.amap.seg) * p.amap.bstride + (int64_t)(gr % p.amap.seg) * p.amap.ld +
+                              cc * 8) * 2);
       } else {
         int gr = n0 + r;
         gr = gr < p.N ? gr : p.N - 1;
-        src[u] = reinterpret_cast<const char*>(W + (int64_t)gr * p.ldw + c * 8);
+        soff[u] = (uint32_t)(((int64_t)gr * p.ldw + cc * 8) * 2);
       }
     }
   };
-  auto issue = [&](int kt) {
-    char* st = smem + (kt % kDlStages) * kDlStageBytes;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int ins = wave + 4 * u;
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[u] + (int64_t)kt * kDlBK * 2),
-                                       (lds_void_t*)(st + ins * 1024), 16, 0, 0);
-    }
+
+  u32x4_t R[16];
+  // load u of super-stage ss (past the tile's end: its last super-stage,
+  // whose slot is not read before the next tile rewrites it)
+  auto gload_one = [&](int ss, int u) {
+    const int k = ss < NS ? ss : NS - 1;
+    const char* base = (u < 8 ? abase : wbase_g) + (int64_t)k * 128;
+    R[u] = *reinterpret_cast<const u32x4_t*>(base + soff[u]);
   };
-  auto prologue_issue = [&]() {
-    const int pre = KT < 4 ? KT : 4;
-    for (int t = 0; t < pre; ++t) issue(t);
+  auto lwrite_one = [&](int ss, int u) {
+    u32x4_t v = R[u];
+    if constexpr (OP == kF16) {
+      if (u >= 8) v = bf16x8_to_f16x8(v);   // weights: bf16 -> fp16
+    }
+    *reinterpret_cast<u32x4_t*>(smem + (ss & 1) * kSsBytes + wbase + u * 2048) = v;
   };
 
   f32x16_t acc[TM][TN];
   u32x4_t af[2][TM], bfr[2][TN];
-  auto lfrag = [&](int kt, int s, int kk) {
-    const char* st = smem + (kt % kDlStages) * kDlStageBytes;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) af[s][i] = *reinterpret_cast<const u32x4_t*>(st + aoff[i][kk]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[s][j] = *reinterpret_cast<const u32x4_t*>(st + boff[j][kk]);
+  // fragment n (A tiles 0..3, then B tiles 0..3) of slice sl (0..3: k-half
+  // sl / 2, k16 step sl % 2) of super-stage ss, into register set s
+  auto frag_one = [&](int ss, int sl, int s, int n) {
+    const char* st = smem + (ss & 1) * kSsBytes + (sl >> 1) * kDlStageBytes;
+    if (n < TM)
+      af[s][n] = *reinterpret_cast<const u32x4_t*>(st + aoff[n][sl & 1]);
+    else
+      bfr[s][n - TM] = *reinterpret_cast<const u32x4_t*>(st + boff[n - TM][sl & 1]);
   };
-  auto mma = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      u32x4_t b = bfr[s][j];
-      if constexpr (OP == kF16) b = bf16x8_to_f16x8(b);   // kF16W: already fp16
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if constexpr (OP == kF16 || OP == kF16W)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s][i]),
-                                                            __builtin_bit_cast(f16x8_t, b), acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[s][i]),
-                                                             __builtin_bit_cast(bf16x8_t, b), acc[i][j], 0, 0, 0);
-      }
-    }
+  auto mfma_one = [&](int s, int idx) {
+    const int j = idx >> 2, i = idx & 3;
+    if constexpr (OP == kF16 || OP == kF16W)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s][i]),
+                                                        __builtin_bit_cast(f16x8_t, bfr[s][j]), acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[s][i]),
+                                                         __builtin_bit_cast(bf16x8_t, bfr[s][j]), acc[i][j], 0, 0, 0);
   };
-  auto body = [&](int kt, int vm_wait, bool next, bool refill) {
-    mma(0);
-    lfrag(kt, 1, 1);
+  // The write / reload pairs of super-stage ss: word u of ss + 1 goes to LDS,
+  // then the register takes word u of ss + 2.  Slices 0, 1, 2 carry words
+  // 0..5, 6..10, 11..15.
+  auto wl = [&](int ss, int u) {
+    lwrite_one(ss + 1, u);
+    gload_one(ss + 2, u);
+  };
+  auto super_stage = [&](int ss) {
+    // slice 0: MFMAs on set 0, fragments of slice 1 into set 1
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one(0, idx);
+      if (idx < 8) frag_one(ss, 1, 1, idx);
+      if (idx >= 2 && idx < 8) wl(ss, idx - 2);          // words 0..5
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (next) {
-      if (vm_wait == 16) DL_WAIT_VM(16); else if (vm_wait == 8) DL_WAIT_VM(8); else DL_WAIT_VM(0);
-      __syncthreads();
-      mma(1);
-      if (refill) issue(kt + 4);
-      lfrag(kt + 1, 0, 0);
+    // slice 1: set 1, fragments of slice 2 into set 0
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
-    } else {
-      mma(1);
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one(1, idx);
+      if (idx < 8) frag_one(ss, 2, 0, idx);
+      if (idx >= 2 && idx < 7) wl(ss, idx + 4);          // words 6..10
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // slice 2: set 0, fragments of slice 3 into set 1
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one(0, idx);
+      if (idx < 8) frag_one(ss, 3, 1, idx);
+      if (idx >= 2 && idx < 7) wl(ss, idx + 9);          // words 11..15
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // slice 3: set 1, fragments of slice 0 of super-stage ss + 1 into set 0
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one(1, idx);
+      if (idx < 8) frag_one(ss + 1, 0, 0, idx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   int t = blockIdx.x;
   if (t >= bt.total_tiles) return;
   setup(t);
-  prologue_issue();
+#pragma unroll
+  for (int u = 0; u < 16; ++u) gload_one(0, u);
   for (; t < bt.total_tiles; t += gridDim.x) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -598,33 +740,30 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    {
-      const int pre = KT < 4 ? KT : 4;   // stages of this tile already issued
-      if (pre == 4) DL_WAIT_VM(24); else if (pre == 3) DL_WAIT_VM(16); else if (pre == 2) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+    // super-stage 0 into slot 0; R takes super-stage 1
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      lwrite_one(0, u);
+      gload_one(1, u);
     }
     __syncthreads();
-    lfrag(0, 0, 0);
-    int kt = 0;
-    for (; kt + 4 < KT; ++kt) body(kt, 16, true, true);
-    if (kt + 3 < KT) { body(kt, 16, true, false); ++kt; }
-    if (kt + 2 < KT) { body(kt, 8, true, false); ++kt; }
-    if (kt + 1 < KT) { body(kt, 0, true, false); ++kt; }
-    body(kt, 0, false, false);
+#pragma unroll
+    for (int n = 0; n < TM + TN; ++n) frag_one(0, 0, 0, n);
+    for (int ss = 0; ss < NS; ++ss) super_stage(ss);
 
-    // tile done: every wave has read its last fragments once it passes this
-    // barrier, so the stages may be refilled for the next tile
+    // every wave has read its last fragments of this tile past this barrier;
+    // the next tile's first loads go out before the epilogue
     const int cprob = prob, cm0 = m0, cn0 = n0;
     __syncthreads();
     if (t + (int)gridDim.x < bt.total_tiles) {
       setup(t + gridDim.x);
-      prologue_issue();
+#pragma unroll
+      for (int u = 0; u < 16; ++u) gload_one(0, u);
     }
-
-    // epilogue through stage 4, which the next tile's prologue leaves alone
     GemmProblem pc = bt.p[0];
     if (cprob) pc = bt.p[1];
     uint32_t mx = 0;
-    tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64,
+    tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 2 * kSsBytes) + wave * 32 * 64,
                        cm0 + wm * WM, cn0 + wn * WN, lane, 1.0f, 1.0f, mx);
   }
 }
@@ -632,7 +771,8 @@ __global__ void __launch_bounds__(256, 1) gemm_pk_kernel(GemmBatch bt) {
 // ---------------------------------------------------------------------------
 // E4M3 operands ("FP8 training for Flux models", Configuration): persistent
 // 256 x 256 kernel on v_mfma_f32_32x32x64_f8f6f4 (no block scales).  Same LDS
-// ring, swizzle, prologue and epilogue as gemm_pk_kernel; a 64-byte stage row
+// ring layout and swizzle of 32 KB k32 stages, and the epilogue of the 16-bit
+// persistent kernel, with a 5-stage ring filled by direct global->LDS loads; a 64-byte stage row
 // now holds 64 k values, i.e. one MFMA k-step.  Lane half h of a fragment
 // takes row chunks h and 2 + h (32 bytes); A and B use the same split, so each
 // MFMA sums over all 64 k of the stage.  The 16 fragment reads of stage kt+1
@@ -803,7 +943,7 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
       prologue_issue();
     }
 
-    // epilogue through stage 4, as in gemm_pk_kernel
+    // epilogue through stage 4, which the next tile's prologue leaves alone
     GemmProblem pc = bt.p[0];
     if (cprob) pc = bt.p[1];
     uint32_t mx = 0;
@@ -896,7 +1036,7 @@ static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream
   if constexpr (OP == kFP8)
     hipLaunchKernelGGL((gemm_fp8_kernel<EPI>), dim3(grid), dim3(256), 0, stream, big);
   else
-    hipLaunchKernelGGL((gemm_pk_kernel<OP, EPI>), dim3(grid), dim3(256), 0, stream, big);
+    hipLaunchKernelGGL((gemm_rs_kernel<OP, EPI>), dim3(grid), dim3(256), 0, stream, big);
 }
 
 template <int OP>
@@ -905,8 +1045,17 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   const int tiles_big = assign_tiles(big, 256, 256);
   bool seg_ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
   for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].omap0.seg >= 32;
-  if constexpr (OP == kFP8)   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
+  if constexpr (OP == kFP8) {   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
     for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K % 128 == 0 && big.p[i].K >= 256;
+  } else {   // gemm_rs_kernel: k in super-stages of 64; operand rows as 32-bit byte offsets
+    for (int i = 0; i < big.count; ++i) {
+      const GemmProblem& q = big.p[i];
+      const int64_t last = q.M - 1;
+      const int64_t a_span = ((last / q.amap.seg) * q.amap.bstride + (last % q.amap.seg) * q.amap.ld + q.K) * 2;
+      const int64_t w_span = ((int64_t)(q.N - 1) * q.ldw + q.K) * 2;
+      seg_ok = seg_ok && q.K % 64 == 0 && a_span < (int64_t(1) << 32) && w_span < (int64_t(1) << 32);
+    }
+  }
   if (tiles_big >= 128 && seg_ok) {   // at least half the CUs get a 256 x 256 tile
     const int grid = tiles_big < 256 ? tiles_big : 256;
     TimingScope ts(OP == kFP8 ? kKcGemmPkFp8 : OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
