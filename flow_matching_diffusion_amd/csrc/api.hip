@@ -45,7 +45,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int esize(int prec) { return prec == FLUX_PREC_F32 ? 4 : 2; }
 // bytes of a block-linear activation operand: fp32, fp16 (bf16 workloads) or E4M3
 int act_esize(int prec) { return prec == FLUX_PREC_F32 ? 4 : prec == FLUX_PREC_FP8_E4M3 ? 1 : 2; }
-int64_t seq_pad_of(int64_t seq) { return round_up(seq, 128); }
+int64_t seq_pad_of(int64_t seq) { return round_up(seq, 256); }   // attention: 256 queries per block
 
 // Bump allocator over the caller's workspace (256-byte aligned regions).
 struct Carve {

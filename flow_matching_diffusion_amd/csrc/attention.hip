@@ -5,17 +5,28 @@
 // K / V tiles streamed through LDS, running max and sum in registers, no
 // L x L buffer.
 //
-// bf16 kernel (CDNA4, wave64, v_mfma_f32_32x32x16_bf16): a block owns 128
-// queries of one (batch, head); each of its 4 waves owns 32 queries.  Per
-// 64-key tile a wave computes S^T = K Q^T (keys on MFMA rows, its queries on
-// MFMA columns), so lane l holds 32 scores of query l % 32 and the row max /
-// sum need a single exchange with lane l ^ 32.  The probabilities then feed
+// bf16 kernel (CDNA4, wave64, v_mfma_f32_32x32x16_bf16): a block owns 256
+// queries of one (batch, head); each of its 8 waves (2 per SIMD, so one
+// wave's softmax overlaps the other's MFMAs) owns 32 queries.  256 queries
+// share each K / V^T tile, which halves the operand traffic per FLOP against
+// 128-query blocks; at 128 the tile stream needed about 32 bytes per clock
+// per CU from L2, beyond what MI355X sustains.  Blocks are placed so that the
+// query blocks of one (batch, head) run on one XCD and share its L2.
+// Per 64-key tile a wave computes S^T = K Q^T (keys on MFMA rows, its queries
+// on MFMA columns), so lane l holds 32 scores of query l % 32 and the row max
+// / sum need a single exchange with lane l ^ 32.  The probabilities then feed
 // O^T = V^T P^T directly from registers: K rows are stored in LDS in a
 // permuted order (bits 2 and 3 of the row index swapped within each 32-row
 // half) so that the accumulator registers of each lane hold 8 consecutive
 // keys per 16-key MFMA step, matching 8 consecutive keys of a V^T row.
+// The running max is raised lazily: O and the running sum are rescaled only
+// when a row's tile max exceeds its running max by more than 2^8 (log2
+// units), so probabilities stay below 256 (exact in bf16's range, same
+// relative rounding) and the 64 multiplies of O are skipped on almost every
+// tile.  The result is the same softmax; only the reference point of the
+// exponentials differs.
 // Inputs come from launch_prep: Q, K head-major [B, H, Lp, Dh] and V
-// transposed [B, H, Dh, Lp], Lp = seq rounded up to 128, zero padded.  The
+// transposed [B, H, Dh, Lp], Lp = seq rounded up to 256, zero padded.  The
 // output is written as bf16, fp16 or E4M3 (the operand type of the next
 // linear; E4M3 with the delayed scale of the row's stream).
 #include <math.h>
@@ -29,27 +40,40 @@ namespace flux {
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 template <int DH, int OUT>
-__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   constexpr int KT = 64;          // keys per tile
   constexpr int QW = 32;          // queries per wave
-  constexpr int QB = 4 * QW;      // queries per block
+  constexpr int NW = 8;           // waves per block
+  constexpr int QB = NW * QW;     // queries per block
+  constexpr int NT = NW * 64;     // threads
   constexpr int DCH = DH / 8;     // 16-byte chunks per K row
   constexpr int KS = DH / 16;     // MFMA k-steps of S^T
   constexpr int DT = DH / 32;     // 32-row tiles of O^T
-  constexpr int LK = KT * DCH / 256;
-  constexpr int LV = DH * 8 / 256;
-  // LDS rows padded by 16 bytes: a 16-byte read by 16 consecutive rows then
-  // hits 16 distinct 4-bank groups (conflict-free for 32 or 64 banks), and
-  // every read address is a per-lane base plus an immediate offset
+  constexpr int LK = KT * DCH / NT;
+  constexpr int LV = DH * 8 / NT;
+  constexpr float kLazy = 8.0f;   // rescale when a tile max exceeds the running max by this (log2)
+  // LDS rows padded by 16 bytes: a 16-byte read of 32 consecutive rows at one
+  // chunk then touches each 4-bank group once per 16-lane cycle (gfx950 serves
+  // a 16-byte-per-lane read in four such cycles), and every read address is a
+  // per-lane base plus an immediate offset
   constexpr int KLD = DH + 8;     // K tile row stride (elements)
   constexpr int VLD = KT + 8;     // V^T tile row stride (elements)
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][DH * VLD];
 
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // work item of this block: XCD x (blocks are dispatched round-robin over the
+  // 8 XCDs) takes the contiguous item range [x * per, (x + 1) * per), so the
+  // query blocks of a (batch, head) stay on one XCD
+  const int nq = a.seq_pad / QB;
+  const int total = a.batch * a.heads * nq;
+  const int per = (total + 7) / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= total) return;
+  const int qb = item % nq;
+  const int64_t bh = item / nq;
+  const int b = (int)(bh / a.heads), h = (int)(bh % a.heads);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int64_t bh = (int64_t)b * a.heads + h;
   const bf16_t* Qh = reinterpret_cast<const bf16_t*>(a.qh) + bh * a.seq_pad * DH;
   const bf16_t* Kh = reinterpret_cast<const bf16_t*>(a.kh) + bh * a.seq_pad * DH;
   const bf16_t* Vt = reinterpret_cast<const bf16_t*>(a.vt) + bh * DH * a.seq_pad;
@@ -63,25 +87,25 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int g = tid + 256 * i, kr = g / DCH, c = g % DCH;
+      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
       rk[i] = *reinterpret_cast<const u32x4_t*>(Kh + (int64_t)(k0 + kr) * DH + c * 8);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int g = tid + 256 * i, d = g >> 3, c = g & 7;
+      const int g = tid + NT * i, d = g >> 3, c = g & 7;
       rv[i] = *reinterpret_cast<const u32x4_t*>(Vt + (int64_t)d * a.seq_pad + k0 + c * 8);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int g = tid + 256 * i, kr = g / DCH, c = g % DCH;
+      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
       const int rho = (kr & 32) | swap23(kr & 31);
       *reinterpret_cast<u32x4_t*>(&Ks[buf][rho * KLD + c * 8]) = rk[i];
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int g = tid + 256 * i, d = g >> 3, c = g & 7;
+      const int g = tid + NT * i, d = g >> 3, c = g & 7;
       *reinterpret_cast<u32x4_t*>(&Vs[buf][d * VLD + c * 8]) = rv[i];
     }
   };
@@ -130,8 +154,19 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // lazy max: move the reference point only when the tile max exceeds it
+    // by more than kLazy (always on the first tile, where m_run = -inf)
+    const float m_tile = mx * sc;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
     bf16x8_t pf[4];
 #pragma unroll
@@ -141,8 +176,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2], sc, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2 + 1], sc, -m_new));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2], sc, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2 + 1], sc, -m_run));
           psum += p0 + p1;
           w[e2] = pack_bf16x2(p0, p1);
         }
@@ -150,12 +185,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
         pf[2 * u + hh] = __builtin_bit_cast(bf16x8_t, wv);
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DT; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+    l_run += psum;
     // O^T += V^T P^T over the 4 16-key steps of the tile
 #pragma unroll
     for (int i = 0; i < DT; ++i) {
@@ -263,21 +293,24 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, int dtype, int out_dtype, hipStream_t stream) {
   TimingScope ts(kKcAttn, stream, 4.0 * a.batch * a.heads * (double)a.seq * a.seq * a.head_dim);
   if (dtype == kBF16) {
-    const dim3 grid(a.seq_pad / 128, a.heads, a.batch);
+    // one block per 256 queries of a (batch, head), rounded up to whole XCD
+    // groups (blocks past the work exit at once)
+    const int items = a.batch * a.heads * (a.seq_pad / 256);
+    const dim3 grid(((items + 7) / 8) * 8);
     if (a.head_dim == 128) {
       if (out_dtype == kF16)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, kF16>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, kF16>), grid, dim3(512), 0, stream, a);
       else if (out_dtype == kFP8)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, kFP8>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, kFP8>), grid, dim3(512), 0, stream, a);
       else
-        hipLaunchKernelGGL((attn_bf16_kernel<128, kBF16>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, kBF16>), grid, dim3(512), 0, stream, a);
     } else {
       if (out_dtype == kF16)
-        hipLaunchKernelGGL((attn_bf16_kernel<64, kF16>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, kF16>), grid, dim3(512), 0, stream, a);
       else if (out_dtype == kFP8)
-        hipLaunchKernelGGL((attn_bf16_kernel<64, kFP8>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, kFP8>), grid, dim3(512), 0, stream, a);
       else
-        hipLaunchKernelGGL((attn_bf16_kernel<64, kBF16>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, kBF16>), grid, dim3(512), 0, stream, a);
     }
   } else {
     const dim3 grid(a.seq_pad / 64, a.heads, a.batch);
