@@ -75,14 +75,14 @@ def recorded_traffic(kernel_class):
 
 # kernel class of the timing hook -> (source file, kernel-name patterns of one launch of that class)
 KERNEL_CLASSES = {
-    "gemm_256_f16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_rs_kernel<[23],"]),
-    "gemm_256_bf16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_rs_kernel<1,"]),
+    "gemm_256_f16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_dl_kernel<[23],"]),
+    "gemm_256_bf16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_dl_kernel<1,"]),
     "gemm_256_fp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8_kernel<"]),
     "gemm_128x128": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_mfma_kernel<"]),
     "attention": ("flow_matching_diffusion_amd/csrc/attention.hip", [r"attn_(bf16|f32)_kernel"]),
     "ln_modulate": ("flow_matching_diffusion_amd/csrc/rowwise.hip", [r"ln_mod_kernel"]),
     "gemv": ("flow_matching_diffusion_amd/csrc/rowwise.hip", [r"gemv_kernel"]),
-    "qk_prep": ("flow_matching_diffusion_amd/csrc/rowwise.hip", [r"qk_prep_kernel", r"v_transpose_kernel"]),
+    "qk_prep": ("flow_matching_diffusion_amd/csrc/rowwise.hip", [r"prep_kernel<"]),
 }
 PROFILE_WORKLOAD = "flux12b_block_pair"
 PROFILE_COMMANDS = [

@@ -91,8 +91,24 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 // ---- activations -------------------------------------------------------------
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
-// GELU, erf form: x * Phi(x), with the device library's erff.
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// GELU, erf form: x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2.  erf by the
+// rational approximation 7.1.26 of Abramowitz and Stegun, "Handbook of
+// Mathematical Functions" (1964): for a >= 0, erf(a) = 1 - t (a1 + t (a2 +
+// t (a3 + t (a4 + t a5)))) exp(-a^2), t = 1 / (1 + p a), |error| <= 1.5e-7;
+// erf is odd.  About half the instructions of the library erff, which
+// matters in the GEMM epilogues that apply it to every MLP activation.
+__device__ __forceinline__ float erf_as(float x) {
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+  float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  poly = __builtin_fmaf(poly, t, 1.421413741f);
+  poly = __builtin_fmaf(poly, t, -0.284496736f);
+  poly = __builtin_fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
+  return copysignf(__builtin_fmaf(-poly, e, 1.0f), x);
+}
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
 
 // ---- OCP E4M3FN ("FP8 training for Flux models", Configuration: fp8 e4m3) ----
 // Byte of the nearest E4M3FN value to x, ties to the even code; |x| > 448

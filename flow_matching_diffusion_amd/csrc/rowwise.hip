@@ -228,9 +228,15 @@ hipError_t launch_patchify(const float* z, int batch, int channels, int hw, void
 // LayerNorm (no affine, biased variance) + adaLN modulate ("Flux architecture
 // deep dive", Implementation details / Adaptive layer normalization):
 // h = (x - mean) / sqrt(var + eps) * (1 + scale[b]) + shift[b].
-// One wave per token row; the row stays in registers (two-pass variance).
+// One wave per token row, the row in registers (two-pass variance).  A block
+// of 4 waves handles 4 * kLnRows consecutive rows; (1 + scale) and shift of
+// the sample of its first row are staged in LDS once, so L2 serves the
+// modulation vectors once per block instead of once per row (a row whose
+// sample differs reads them from global memory).  Registers are kept low
+// (no cross-row prefetch) so 4 blocks fit per CU and their rows overlap.
 // ===========================================================================
 constexpr int kLnMaxVec = 16;   // float4 per lane: D <= 64 * 4 * 16 = 4096
+constexpr int kLnRows = 2;      // rows per wave
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
@@ -253,93 +259,138 @@ __device__ __forceinline__ void store4<_Float16>(_Float16* p, float a, float b, 
   *reinterpret_cast<uint2*>(p) = v;
 }
 
-template <typename T>
+template <typename T, int NV>
 __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row_g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int si = 0;
-  int64_t r = row_g;
-  if (r >= a.s[0].rows) {
-    if (a.count < 2) return;
-    r -= a.s[0].rows;
-    si = 1;
-    if (r >= a.s[1].rows) return;
-  }
-  const LnSeg& s = a.s[si];
+  __shared__ float4 msc[NV * 64], msh[NV * 64];   // (1 + scale), shift of the block's first sample
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t blk_first = (int64_t)blockIdx.x * 4 * kLnRows;
   const int D = a.dim;
-  const int64_t b = r / s.xmap.seg, l = r % s.xmap.seg;
-  const float* x = s.x + b * s.xmap.bstride + l * s.xmap.ld;
-  T* out = reinterpret_cast<T*>(s.out) + b * s.omap.bstride + l * s.omap.ld;
-  const float* sh = s.shift + b * s.mod_bstride;
-  const float* sc = s.scale + b * s.mod_bstride;
-  const int nv = D / 256;
-  float4 v[kLnMaxVec];
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < kLnMaxVec; ++i) {
-    if (i < nv) {
-      v[i] = reinterpret_cast<const float4*>(x)[lane + 64 * i];
-      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  // global rows run over segment 0 then segment 1
+  auto locate = [&](int64_t g, int& si, int64_t& r) -> bool {
+    si = 0;
+    r = g;
+    if (r >= a.s[0].rows) {
+      if (a.count < 2) return false;
+      r -= a.s[0].rows;
+      si = 1;
+      if (r >= a.s[1].rows) return false;
+    }
+    return true;
+  };
+  int bsi;
+  int64_t brow;
+  if (!locate(blk_first, bsi, brow)) return;   // block-uniform
+  const int64_t bsam = brow / a.s[bsi].xmap.seg;
+  {
+    const float* scp = a.s[bsi].scale + bsam * a.s[bsi].mod_bstride;
+    const float* shp = a.s[bsi].shift + bsam * a.s[bsi].mod_bstride;
+    for (int i = threadIdx.x; i < NV * 64; i += 256) {
+      const float4 t = reinterpret_cast<const float4*>(scp)[i];
+      msc[i] = make_float4(1.f + t.x, 1.f + t.y, 1.f + t.z, 1.f + t.w);
+      msh[i] = reinterpret_cast<const float4*>(shp)[i];
     }
   }
-  const float mean = wave_sum(sum) / (float)D;
-  float sq = 0.f;
+  __syncthreads();
+
+  const int64_t first = blk_first + wave * kLnRows;
+  auto load_row = [&](int sidx, int64_t row, float4* dst) {
+    const LnSeg& sg = a.s[sidx];
+    const int64_t bb = row / sg.xmap.seg, ll = row % sg.xmap.seg;
+    const float* x = sg.x + bb * sg.xmap.bstride + ll * sg.xmap.ld;
 #pragma unroll
-  for (int i = 0; i < kLnMaxVec; ++i) {
-    if (i < nv) {
+    for (int i = 0; i < NV; ++i) dst[i] = reinterpret_cast<const float4*>(x)[lane + 64 * i];
+  };
+  int si;
+  int64_t r;
+  if (!locate(first, si, r)) return;   // wave-uniform; no barrier follows
+  float4 v[NV];
+#pragma unroll 1
+  for (int k = 0; k < kLnRows; ++k) {
+    load_row(si, r, v);
+    int si_n = 0;
+    int64_t r_n = 0;
+    const bool has_next = k + 1 < kLnRows && locate(first + k + 1, si_n, r_n);
+    const LnSeg& sg = a.s[si];
+    const int64_t bb = r / sg.xmap.seg, ll = r % sg.xmap.seg;
+    const bool staged = si == bsi && bb == bsam;   // wave-uniform
+    const float4* gsc = reinterpret_cast<const float4*>(sg.scale + bb * sg.mod_bstride);
+    const float4* gsh = reinterpret_cast<const float4*>(sg.shift + bb * sg.mod_bstride);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const float mean = wave_sum(sum) / (float)D;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
       const float dx = v[i].x - mean, dy = v[i].y - mean, dz = v[i].z - mean, dw = v[i].w - mean;
       sq += (dx * dx + dy * dy) + (dz * dz + dw * dw);
     }
-  }
-  const float var = wave_sum(sq) / (float)D;
-  const float rstd = 1.0f / sqrtf(var + a.eps);
-  if constexpr (sizeof(T) == 1) {
-    // E4M3 output with the record's delayed scale; the row's amax raises the record's
-    const float qs = fp8_scale(s.q);
+    const float var = wave_sum(sq) / (float)D;
+    const float rstd = 1.0f / sqrtf(var + a.eps);
+    T* out = reinterpret_cast<T*>(sg.out) + bb * sg.omap.bstride + ll * sg.omap.ld;
     uint32_t mx = 0;
+    const float qs = sizeof(T) == 1 ? fp8_scale(sg.q) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < kLnMaxVec; ++i) {
-      if (i < nv) {
-        const int c = (lane + 64 * i) * 4;
-        const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
-        const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
-        const float y0 = (v[i].x - mean) * rstd * (1.f + s4.x) + h4.x;
-        const float y1 = (v[i].y - mean) * rstd * (1.f + s4.y) + h4.y;
-        const float y2 = (v[i].z - mean) * rstd * (1.f + s4.z) + h4.z;
-        const float y3 = (v[i].w - mean) * rstd * (1.f + s4.w) + h4.w;
+    for (int i = 0; i < NV; ++i) {
+      const int c = (lane + 64 * i) * 4;
+      float4 s1, h4;
+      if (staged) {
+        s1 = msc[lane + 64 * i];
+        h4 = msh[lane + 64 * i];
+      } else {
+        const float4 t = gsc[lane + 64 * i];
+        s1 = make_float4(1.f + t.x, 1.f + t.y, 1.f + t.z, 1.f + t.w);
+        h4 = gsh[lane + 64 * i];
+      }
+      const float y0 = (v[i].x - mean) * rstd * s1.x + h4.x;
+      const float y1 = (v[i].y - mean) * rstd * s1.y + h4.y;
+      const float y2 = (v[i].z - mean) * rstd * s1.z + h4.z;
+      const float y3 = (v[i].w - mean) * rstd * s1.w + h4.w;
+      if constexpr (sizeof(T) == 1) {
+        // E4M3 output with the record's delayed scale; the row's amax raises the record's
         mx = max(mx, max(max(abs_bits(y0), abs_bits(y1)), max(abs_bits(y2), abs_bits(y3))));
         *reinterpret_cast<uint32_t*>(out + c) = f32_to_e4m3(y0 * qs) | (f32_to_e4m3(y1 * qs) << 8) |
                                                 (f32_to_e4m3(y2 * qs) << 16) | (f32_to_e4m3(y3 * qs) << 24);
+      } else {
+        store4<T>(out + c, y0, y1, y2, y3);
       }
     }
-    mx = wave_max_u32(mx);
-    if (lane == 0) fp8_amax_raise(s.q, __uint_as_float(mx));
-  } else {
-#pragma unroll
-    for (int i = 0; i < kLnMaxVec; ++i) {
-      if (i < nv) {
-        const int c = (lane + 64 * i) * 4;
-        const float4 s4 = *reinterpret_cast<const float4*>(sc + c);
-        const float4 h4 = *reinterpret_cast<const float4*>(sh + c);
-        store4<T>(out + c, (v[i].x - mean) * rstd * (1.f + s4.x) + h4.x, (v[i].y - mean) * rstd * (1.f + s4.y) + h4.y,
-                  (v[i].z - mean) * rstd * (1.f + s4.z) + h4.z, (v[i].w - mean) * rstd * (1.f + s4.w) + h4.w);
-      }
+    if constexpr (sizeof(T) == 1) {
+      mx = wave_max_u32(mx);
+      if (lane == 0) fp8_amax_raise(sg.q, __uint_as_float(mx));
     }
+    if (!has_next) break;
+    si = si_n;
+    r = r_n;
   }
 }
 
+template <typename T>
+static void launch_ln_mod_t(const LnArgs& a, dim3 grid, hipStream_t stream) {
+  // D is a multiple of 256, at most 4096 (checked by the API): NV float4 per lane
+#define FLUX_LN_CASE(nv) \
+  case nv: hipLaunchKernelGGL((ln_mod_kernel<T, nv>), grid, dim3(256), 0, stream, a); break;
+  switch (a.dim / 256) {
+    FLUX_LN_CASE(1) FLUX_LN_CASE(2) FLUX_LN_CASE(3) FLUX_LN_CASE(4) FLUX_LN_CASE(5) FLUX_LN_CASE(6)
+    FLUX_LN_CASE(7) FLUX_LN_CASE(8) FLUX_LN_CASE(9) FLUX_LN_CASE(10) FLUX_LN_CASE(11) FLUX_LN_CASE(12)
+    FLUX_LN_CASE(13) FLUX_LN_CASE(14) FLUX_LN_CASE(15) default: FLUX_LN_CASE(16)
+  }
+#undef FLUX_LN_CASE
+}
+
 hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {  // dtype: output element type
+  if (a.dim % 256 != 0 || a.dim < 256 || a.dim > 256 * kLnMaxVec) return hipErrorInvalidValue;
   int64_t rows = a.s[0].rows + (a.count > 1 ? a.s[1].rows : 0);
-  const dim3 grid((unsigned)ceil_div(rows, 4));
+  const dim3 grid((unsigned)ceil_div(rows, 4 * kLnRows));
   TimingScope ts(kKcLnMod, stream, (double)rows * a.dim * (4.0 + (dtype == kF32 ? 4.0 : dtype == kFP8 ? 1.0 : 2.0)));
   if (dtype == kFP8)
-    hipLaunchKernelGGL(ln_mod_kernel<uint8_t>, grid, dim3(256), 0, stream, a);
+    launch_ln_mod_t<uint8_t>(a, grid, stream);
   else if (dtype == kBF16)
-    hipLaunchKernelGGL(ln_mod_kernel<bf16_t>, grid, dim3(256), 0, stream, a);
+    launch_ln_mod_t<bf16_t>(a, grid, stream);
   else if (dtype == kF16)
-    hipLaunchKernelGGL(ln_mod_kernel<_Float16>, grid, dim3(256), 0, stream, a);
+    launch_ln_mod_t<_Float16>(a, grid, stream);
   else
-    hipLaunchKernelGGL(ln_mod_kernel<float>, grid, dim3(256), 0, stream, a);
+    launch_ln_mod_t<float>(a, grid, stream);
   return hipGetLastError();
 }
 
@@ -473,80 +524,127 @@ __device__ __forceinline__ void store_pair<bf16_t>(bf16_t* p, float u, float w) 
   *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(u, w);
 }
 
+// One block per (64 tokens, head, batch): q and k rows of the head get
+// RMSNorm + RoPE and go to their head-major rows; v goes through LDS and out
+// transposed.  Every global access is 16 bytes per lane: a chunk holds E =
+// 16 / sizeof(T) consecutive head dims, and the DH / E lanes of one
+// (token, head) row form an aligned group of the wave, so the RMSNorm sum is
+// a shuffle reduction within the group.  A lane's chunk position inside the
+// head is the same for every row it handles, so its RoPE pairs and norm
+// scales are loaded once per row from the per-token table and once per block.
 template <typename T, int DH>
-__global__ void __launch_bounds__(256) qk_prep_kernel(PrepArgs a) {
-  constexpr int PAIRS = DH / 2;               // one pair per lane
-  constexpr int PER_WAVE = 64 / PAIRS;        // (token, head) items per wave step
-  const int j = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane / PAIRS, m = lane % PAIRS;
+__global__ void __launch_bounds__(256) prep_kernel(PrepArgs a) {
+  constexpr int E = 16 / sizeof(T);          // elements per 16-byte chunk
+  constexpr int G = DH / E;                  // lanes per (token, head) row
+  constexpr int TOK = 64;                    // tokens per block
+  constexpr int PER = TOK * G / 256;         // chunks per thread per matrix
+  static_assert(PER >= 1 && (TOK * G) % 256 == 0, "tile shape");
+  typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));
+  __shared__ T tile[TOK][DH + E];            // v tile, rows padded by one chunk
+  const int j0 = blockIdx.x * TOK, h = blockIdx.y, b = blockIdx.z;
   const int H = a.heads;
-  const bool valid = j < a.seq;
-  const bool txt = j >= a.l_img;
-  const int64_t row_off = (int64_t)b * a.src_bstride + (int64_t)j * a.src_ld;
-  float c = 1.f, s = 0.f;
-  if (valid && a.rope) {
-    const float2 cs = reinterpret_cast<const float2*>(a.rope)[((int64_t)b * a.seq + j) * PAIRS + m];
-    c = cs.x;
-    s = cs.y;
-  }
-  // items: (which in {q, k}) x heads
-  for (int it = wave * PER_WAVE + sub; it < 2 * H; it += 4 * PER_WAVE) {
-    const int which = it / H, h = it % H;
-    float u = 0.f, w = 0.f;
-    if (valid) {
-      const T* src = reinterpret_cast<const T*>(which == 0 ? a.src_q : a.src_k) + row_off;
-      load_pair<T>(src + h * DH + 2 * m, u, w);
-      const float* g = which == 0 ? (txt ? a.gq_txt : a.gq_img) : (txt ? a.gk_txt : a.gk_img);
-      if (g) {
-        const float ms = wave_sum<PAIRS>(u * u + w * w) / (float)DH;
-        const float r = 1.0f / sqrtf(ms + a.eps);
-        u = u * r * g[2 * m];
-        w = w * r * g[2 * m + 1];
-      }
-      const float u2 = u * c - w * s;
-      const float w2 = u * s + w * c;
-      u = u2;
-      w = w2;
+  const int tid = threadIdx.x;
+  const int g = tid % G;                     // chunk position inside the head
+  const int d0 = g * E;
+  const int64_t head_row0 = ((int64_t)b * H + h) * a.seq_pad;
+  // q and k
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const T* src = reinterpret_cast<const T*>(which == 0 ? a.src_q : a.src_k) + (int64_t)b * a.src_bstride + h * DH;
+    T* dst = reinterpret_cast<T*>(which == 0 ? a.qh : a.kh);
+    chunk_t raw[PER];
+    int jj[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int r = (tid + 256 * i) / G;     // token within the tile
+      jj[i] = j0 + r;
+      if (jj[i] < a.seq) raw[i] = *reinterpret_cast<const chunk_t*>(src + (int64_t)jj[i] * a.src_ld + d0);
     }
-    T* dst = reinterpret_cast<T*>(which == 0 ? a.qh : a.kh) + (((int64_t)b * H + h) * a.seq_pad + j) * DH + 2 * m;
-    store_pair<T>(dst, u, w);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = jj[i];
+      float x[E];
+      if (j < a.seq) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < E / 2; ++e) {
+            x[2 * e] = __uint_as_float(raw[i][e] << 16);
+            x[2 * e + 1] = __uint_as_float(raw[i][e] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[e] = __uint_as_float(raw[i][e]);
+        }
+        const bool txt = j >= a.l_img;
+        const float* gm = which == 0 ? (txt ? a.gq_txt : a.gq_img) : (txt ? a.gk_txt : a.gk_img);
+        if (gm) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) ss += x[e] * x[e];
+          const float ms = wave_sum<G>(ss) / (float)DH;
+          const float rs = 1.0f / sqrtf(ms + a.eps);
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[e] = x[e] * rs * gm[d0 + e];
+        }
+        if (a.rope) {
+          const float2* cs = reinterpret_cast<const float2*>(a.rope) + ((int64_t)b * a.seq + j) * (DH / 2) + d0 / 2;
+#pragma unroll
+          for (int e = 0; e < E / 2; ++e) {
+            const float2 t = cs[e];
+            const float u = x[2 * e], w = x[2 * e + 1];
+            x[2 * e] = u * t.x - w * t.y;
+            x[2 * e + 1] = u * t.y + w * t.x;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = 0.f;
+      }
+      chunk_t o;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < E / 2; ++e) o[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = __float_as_uint(x[e]);
+      }
+      *reinterpret_cast<chunk_t*>(dst + (head_row0 + j) * DH + d0) = o;
+    }
   }
-}
-
-// v [rows j0..j0+63 of one head] -> vt[d][j0..j0+63] through LDS.
-template <typename T, int DH>
-__global__ void __launch_bounds__(256) v_transpose_kernel(PrepArgs a) {
-  __shared__ T tile[64][DH + 2];
-  const int j0 = blockIdx.x * 64, h = blockIdx.y % a.heads, b = blockIdx.y / a.heads;
-  const T* src = reinterpret_cast<const T*>(a.src_v) + (int64_t)b * a.src_bstride + h * DH;
-  for (int i = threadIdx.x; i < 64 * DH; i += 256) {
-    const int r = i / DH, d = i % DH;
-    const int j = j0 + r;
-    tile[r][d] = j < a.seq ? src[(int64_t)j * a.src_ld + d] : from_f32<T>(0.f);
+  // v: rows into LDS, columns out
+  {
+    const T* src = reinterpret_cast<const T*>(a.src_v) + (int64_t)b * a.src_bstride + h * DH;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int r = (tid + 256 * i) / G, j = j0 + r;
+      chunk_t c = {0u, 0u, 0u, 0u};
+      if (j < a.seq) c = *reinterpret_cast<const chunk_t*>(src + (int64_t)j * a.src_ld + d0);
+      *reinterpret_cast<chunk_t*>(&tile[r][d0]) = c;
+    }
   }
   __syncthreads();
-  T* dst = reinterpret_cast<T*>(a.vt) + ((int64_t)b * a.heads + h) * DH * a.seq_pad + j0;
-  for (int i = threadIdx.x; i < 64 * DH; i += 256) {
-    const int d = i / 64, r = i % 64;
-    dst[(int64_t)d * a.seq_pad + r] = tile[r][d];
+  {
+    // output row d of vt holds the tile's 64 tokens: TOK / E chunks per row
+    constexpr int CPR = TOK / E;
+    T* dst = reinterpret_cast<T*>(a.vt) + ((int64_t)b * H + h) * DH * a.seq_pad + j0;
+#pragma unroll
+    for (int i = 0; i < DH * CPR / 256; ++i) {
+      const int c = tid + 256 * i, d = c / CPR, r0 = (c % CPR) * E;
+      T vals[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vals[e] = tile[r0 + e][d];
+      *reinterpret_cast<chunk_t*>(dst + (int64_t)d * a.seq_pad + r0) = __builtin_bit_cast(chunk_t, vals);
+    }
   }
 }
 
 template <typename T>
 static hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
-  const dim3 g1(a.seq_pad, a.batch), g2(a.seq_pad / 64, a.batch * a.heads);
-  if (a.head_dim == 128) {
-    hipLaunchKernelGGL((qk_prep_kernel<T, 128>), g1, dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((v_transpose_kernel<T, 128>), g2, dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((qk_prep_kernel<T, 64>), g1, dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((v_transpose_kernel<T, 64>), g2, dim3(256), 0, stream, a);
-  }
+  const dim3 grid(a.seq_pad / 64, a.heads, a.batch);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((prep_kernel<T, 128>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prep_kernel<T, 64>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

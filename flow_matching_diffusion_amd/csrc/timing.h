@@ -5,8 +5,8 @@
 namespace flux {
 
 enum KernelClass : int {
-  kKcGemmPkF16 = 0,   // gemm_rs_kernel (256 x 256 persistent), fp16 activations
-  kKcGemmPkBf16,      // gemm_rs_kernel, bf16 activations
+  kKcGemmPkF16 = 0,   // gemm_dl_kernel (256 x 256 persistent), fp16 activations
+  kKcGemmPkBf16,      // gemm_dl_kernel, bf16 activations
   kKcGemm128,         // gemm_mfma_kernel (128 x 128 tiles)
   kKcGemmF32,
   kKcAttn,
