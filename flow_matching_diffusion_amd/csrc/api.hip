@@ -634,11 +634,16 @@ flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, i
 }
 
 // -------------------------------- output head --------------------------------
+// the output linear's split-K partial sums need up to kGemmMaxSplit fp32
+// copies of the [B*H*W, channels] output; channels is at most this many
+constexpr int kFinalMaxChannels = 256;
+
 size_t flux_final_workspace_bytes(int32_t precision, int32_t batch, int32_t height, int32_t width, int32_t hidden) {
   if (batch < 1 || height < 1 || width < 1 || hidden < 1) return 0;
   Carve c(nullptr);
   c.take((size_t)batch * 2 * hidden * 4);
   c.take((size_t)batch * height * width * hidden * esize(precision));
+  c.take((size_t)kGemmMaxSplit * batch * height * width * kFinalMaxChannels * 4);
   return (size_t)round_up((int64_t)c.off, 256);
 }
 
@@ -651,7 +656,8 @@ flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, i
   REQUIRE(batch >= 1 && channels >= 1 && height >= 1 && width >= 1, "sizes must be >= 1");
   if (hidden % 256 != 0 || hidden > 4096)
     return fail(FLUX_ERR_UNSUPPORTED, "hidden %d unsupported (a multiple of 256, at most 4096)", hidden);
-  if (channels % 4 != 0) return fail(FLUX_ERR_UNSUPPORTED, "channels must be a multiple of 4");
+  if (channels % 4 != 0 || channels > kFinalMaxChannels)
+    return fail(FLUX_ERR_UNSUPPORTED, "channels must be a multiple of 4, at most %d", kFinalMaxChannels);
   REQUIRE(eps > 0.f, "eps must be positive");
   REQUIRE(mod_w && mod_b && out_w && out_b && x_img && vec && v_pred, "a required pointer is NULL");
   REQUIRE(aligned16(x_img) && aligned16(vec) && aligned16(v_pred), "pointers must be 16-byte aligned");
@@ -665,6 +671,7 @@ flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, i
   Carve c(workspace);
   float* mod = static_cast<float*>(c.take((size_t)batch * 2 * hidden * 4));
   void* h = c.take((size_t)batch * HW * hidden * esize(precision));
+  float* partials = static_cast<float*>(c.take((size_t)kGemmMaxSplit * batch * HW * kFinalMaxChannels * 4));
   GemvBatch gv{};
   gv.count = 1;
   gv.p[0] = gemv_problem(mod_w, mod_b, 2 * hidden, hidden, vec, hidden, mod, 2 * hidden, 1, 0);
@@ -685,6 +692,7 @@ flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, i
   g.p[0] = gemm_problem(h, rmap(HW * hidden, hidden, HW), out_w, out_b, (int)(batch * HW), channels, hidden,
                         kEpiStoreF32, v_pred, rmap(channels * HW, 1, HW));
   g.p[0].col_stride0 = HW;
+  g.partials = partials;
   FLUX_HIP(launch_gemm(g, act, st), "output GEMM");
   return FLUX_OK;
 }

@@ -249,6 +249,10 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  // split-K: blockIdx.y takes k range [split * K / ksplit, ...) and writes an
+  // fp32 partial tile; gemm_splitk_reduce_kernel sums them in order
+  const int split = blockIdx.y;
+  const int kspan = p.K / bt.ksplit;
 
   // global row pointers of this thread's loads (rows clamped into range);
   // each thread moves 8 elements (one 16-byte LDS chunk) per row and stage
@@ -262,14 +266,15 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
     for (int i = 0; i < LA; ++i) {
       int r = m0 + i * 32 + lrow;
       r = r < p.M ? r : p.M - 1;
-      arow[i] = A + ((int64_t)(r / p.amap.seg) * p.amap.bstride + (int64_t)(r % p.amap.seg) * p.amap.ld + lchunk * 8) * ES;
+      arow[i] = A + ((int64_t)(r / p.amap.seg) * p.amap.bstride + (int64_t)(r % p.amap.seg) * p.amap.ld + lchunk * 8 +
+                     (int64_t)split * kspan) * ES;
     }
     const char* W = reinterpret_cast<const char*>(p.W);
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       int r = n0 + i * 32 + lrow;
       r = r < p.N ? r : p.N - 1;
-      brow[i] = W + ((int64_t)r * p.ldw + lchunk * 8) * ES;
+      brow[i] = W + ((int64_t)r * p.ldw + lchunk * 8 + (int64_t)split * kspan) * ES;
     }
   }
   u32x4_t ra[LA], rb[LB];
@@ -309,7 +314,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
   // buffer with their 16-wide k slices double-buffered in registers, so the
   // LDS reads of slice kk+1 overlap the MFMAs of slice kk.  One barrier per
   // iteration separates the buffer swap.
-  const int KT = p.K / kBK;
+  const int KT = kspan / kBK;
   const int frow = lane & 31, fhalf = lane >> 5;
   gload(0);
   lstore(0);
@@ -384,8 +389,13 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
     for (int rr = lane / LPR; rr < 32; rr += RPI) {
       const int row = m0 + wm * WM + i * 32 + rr;
       if (row < p.M && col < p.N) {
-        const float4 v = *reinterpret_cast<const float4*>(&cs[rr * CLD + c4]);
-        epi_apply4_any(p, row, col, v, dq, qs, mx);
+        float4 v = *reinterpret_cast<const float4*>(&cs[rr * CLD + c4]);
+        if (bt.ksplit > 1) {
+          v.x *= dq; v.y *= dq; v.z *= dq; v.w *= dq;
+          *reinterpret_cast<float4*>(bt.partials + ((int64_t)split * p.M + row) * p.N + col) = v;
+        } else {
+          epi_apply4_any(p, row, col, v, dq, qs, mx);
+        }
       }
     }
     __syncthreads();
@@ -930,6 +940,24 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   }
 }
 
+// Split-K reduction: out = epilogue(sum over splits s = 0..ksplit-1 in order
+// of partials[s]), four consecutive columns per thread; the accumulator
+// scale of E4M3 operands was applied when the partials were written.
+__global__ void __launch_bounds__(256) gemm_splitk_reduce_kernel(GemmProblem p, const float* __restrict__ partials,
+                                                                 int ksplit) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over M * N / 4
+  const int n4 = p.N / 4;
+  if (i >= (int64_t)p.M * n4) return;
+  const int row = (int)(i / n4), col = (int)(i % n4) * 4;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < ksplit; ++s) {
+    const float4 t = *reinterpret_cast<const float4*>(partials + ((int64_t)s * p.M + row) * p.N + col);
+    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+  }
+  uint32_t mx = 0;
+  epi_apply4_any(p, row, col, v, 1.0f, 1.0f, mx);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 kernel: 64 x 64 tile, 16 x 16 threads with 4 x 4 outputs each
 // ---------------------------------------------------------------------------
@@ -1018,6 +1046,7 @@ static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream
 
 template <int OP>
 static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
+  bt.ksplit = 1;
   GemmBatch big = bt;
   const int tiles_big = assign_tiles(big, 256, 256);
   bool seg_ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
@@ -1033,7 +1062,11 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
       seg_ok = seg_ok && q.K % 64 == 0 && a_span < (int64_t(1) << 32) && w_span < (int64_t(1) << 32);
     }
   }
-  if (tiles_big >= 128 && seg_ok) {   // at least half the CUs get a 256 x 256 tile
+  // the persistent kernel needs at least half the CUs busy with 256 x 256
+  // tiles; with K < 512 a tile is mostly epilogue, which smaller tiles spread
+  // over more CUs
+  for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K >= 512;
+  if (tiles_big >= 128 && seg_ok) {
     const int grid = tiles_big < 256 ? tiles_big : 256;
     TimingScope ts(OP == kFP8 ? kKcGemmPkFp8 : OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
     switch (big.p[0].epi) {   // the problems of one launch share the epilogue kind
@@ -1045,14 +1078,29 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
     }
   } else {
     const int tiles = assign_tiles(bt, 128, 128);
+    // split K when the tiles fill less than half the GPU, the caller gave
+    // scratch and the epilogue writes no E4M3 output (whose amax the
+    // reduction would have to raise)
+    int ks = 1;
+    const GemmProblem& q = bt.p[0];
+    if (bt.partials && bt.count == 1 && !q.qo && q.N % 4 == 0) {
+      while (ks < kGemmMaxSplit && tiles * ks * 2 <= 256 && q.K % (ks * 2 * kBK) == 0) ks *= 2;
+    }
+    bt.ksplit = ks;
     TimingScope ts(kKcGemm128, stream, flops);
-    hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, OP>), dim3(tiles), dim3(256), 0, stream, bt);
+    hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, OP>), dim3(tiles, ks), dim3(256), 0, stream, bt);
+    if (ks > 1) {
+      const int64_t n = (int64_t)q.M * (q.N / 4);
+      hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, q,
+                         bt.partials, ks);
+    }
   }
 }
 
 hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
   const double flops = gemm_flops(bt);
   if (op == kF32) {
+    bt.ksplit = 1;
     const int tiles = assign_tiles(bt, 64, 64);
     TimingScope ts(kKcGemmF32, stream, flops);
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, bt);

@@ -63,7 +63,12 @@ struct GemmBatch {
   GemmProblem p[kMaxGemmProblems];
   int32_t count;
   int32_t total_tiles;
+  // Optional split-K scratch for a single problem too small to fill the GPU
+  // with tiles: [kGemmMaxSplit, M, N] fp32 partial sums (null: no split).
+  float* partials;
+  int32_t ksplit;   // filled by the launcher
 };
+constexpr int kGemmMaxSplit = 8;
 
 hipError_t launch_gemm(GemmBatch batch, int op, hipStream_t stream);
 

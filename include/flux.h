@@ -277,6 +277,9 @@ flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, i
  * tok = Linear_out(LayerNorm(x_img)(1 + scale) + shift) [B, H*W, C];
  * v_pred[b, c, h, w] = tok[b, h*W + w, c].
  *  x_img [B, H*W, D] float, sample b at x_img + b*bstride;  v_pred [B, C, H, W] float out.
+ *  channels: a multiple of 4, at most 256 (FLUX_ERR_UNSUPPORTED otherwise).
+ *  The workspace also holds the output linear's split-K partial sums, which
+ *  are added in a fixed order (results do not depend on the split).
  */
 flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
                            int32_t hidden, float eps, const void* mod_w, const void* mod_b,
