@@ -84,32 +84,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(Qh + (int64_t)q * DH + ks * 16 + half * 8);
 
   u32x4_t rk[LK], rv[LV];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
-      rk[i] = *reinterpret_cast<const u32x4_t*>(Kh + (int64_t)(k0 + kr) * DH + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int g = tid + NT * i, d = g >> 3, c = g & 7;
-      rv[i] = *reinterpret_cast<const u32x4_t*>(Vt + (int64_t)d * a.seq_pad + k0 + c * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
-      const int rho = (kr & 32) | swap23(kr & 31);
-      *reinterpret_cast<u32x4_t*>(&Ks[buf][rho * KLD + c * 8]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int g = tid + NT * i, d = g >> 3, c = g & 7;
-      *reinterpret_cast<u32x4_t*>(&Vs[buf][d * VLD + c * 8]) = rv[i];
-    }
-  };
-
   f32x16_t o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
@@ -118,41 +92,40 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = a.scale_log2;
 
-  const int ntiles = (a.seq + KT - 1) / KT;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < ntiles) gload((t + 1) * KT);
-    // S^T for 64 keys x 32 queries: two 32 x 32 tiles
-    f32x16_t s[2];
+  // S^T of tile t (64 keys x 32 queries, two 32 x 32 tiles) from K buffer t % 2
+  auto s_tile = [&](int t, f32x16_t (&sv)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sv[u][e] = 0.f;
       const int rho = u * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[cur][rho * KLD + (ks * 2 + half) * 8]);
-        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[u], 0, 0, 0);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[t & 1][rho * KLD + (ks * 2 + half) * 8]);
+        sv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sv[u], 0, 0, 0);
       }
     }
-    // s[u][e] is the score of key t*64 + (2u + e/8)*16 + half*8 + e%8 for query l32
+  };
+  // softmax of tile t's scores (sv[u][e] is the score of key
+  // t*64 + (2u + e/8)*16 + half*8 + e%8 for query l32), in two parts: the
+  // row max and the (rare) rescale, which branch, then the exponentials and
+  // sums, straight-line code that the scheduler can interleave with MFMAs
+  bf16x8_t pf[4];
+  auto softmax_max = [&](int t, f32x16_t (&sv)[2]) {
     if ((t + 1) * KT > a.seq) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = t * KT + (2 * u + (e >> 3)) * 16 + half * 8 + (e & 7);
-          if (key >= a.seq) s[u][e] = -INFINITY;
+          if (key >= a.seq) sv[u][e] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[u][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // lazy max: move the reference point only when the tile max exceeds it
     // by more than kLazy (always on the first tile, where m_run = -inf)
@@ -167,36 +140,132 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       m_run = m_new;
     }
-    float psum = 0.f;
-    bf16x8_t pf[4];
+  };
+  // O^T += V^T P^T over the 4 16-key steps of tile t (V buffer t % 2), the
+  // V^T fragment reads three MFMAs ahead
+  auto pv_tile = [&](int t) {
+    constexpr int NP = DT * 4, AH = 3;
+    const bf16_t* vb = &Vs[t & 1][0];
+    // step m: output tile i = m % DT, key step kb = m / DT (chains alternate)
+    auto vfrag = [&](int m) {
+      return *reinterpret_cast<const bf16x8_t*>(vb + ((m % DT) * 32 + l32) * VLD + ((m / DT) * 2 + half) * 8);
+    };
+    bf16x8_t vq[NP];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int m = 0; m < AH; ++m) vq[m] = vfrag(m);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t w[4];
+    for (int m = 0; m < NP; ++m) {
+      if (m + AH < NP) vq[m + AH] = vfrag(m + AH);
+      o[m % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[m], pf[m / DT], o[m % DT], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Software pipeline, one barrier per tile: iteration t computes S(t + 1)
+  // while the softmax of S(t) runs (the MFMAs do not depend on it, so the
+  // SIMD executes both at once), then O += V(t) P(t).  LDS: K(t + 1) and
+  // V(t) are resident during iteration t; K(t + 2) goes to K(t)'s buffer and
+  // V(t + 1) to V(t - 1)'s, both read for the last time in iteration t - 1.
+  const int ntiles = (a.seq + KT - 1) / KT;
+  // prologue: K(0), V(0), K(1) in LDS; S(0); tiles K(2), V(1) in registers
+  auto gload_k = [&](int j) {
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2], sc, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][hh * 8 + 2 * e2 + 1], sc, -m_run));
+    for (int i = 0; i < LK; ++i) {
+      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
+      rk[i] = *reinterpret_cast<const u32x4_t*>(Kh + (int64_t)(j * KT + kr) * DH + c * 8);
+    }
+  };
+  auto gload_v = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int g = tid + NT * i, d = g >> 3, c = g & 7;
+      rv[i] = *reinterpret_cast<const u32x4_t*>(Vt + (int64_t)d * a.seq_pad + j * KT + c * 8);
+    }
+  };
+  auto lstore_k = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
+      const int rho = (kr & 32) | swap23(kr & 31);
+      *reinterpret_cast<u32x4_t*>(&Ks[j & 1][rho * KLD + c * 8]) = rk[i];
+    }
+  };
+  auto lstore_v = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int g = tid + NT * i, d = g >> 3, c = g & 7;
+      *reinterpret_cast<u32x4_t*>(&Vs[j & 1][d * VLD + c * 8]) = rv[i];
+    }
+  };
+  gload_k(0);
+  gload_v(0);
+  lstore_k(0);
+  lstore_v(0);
+  if (ntiles > 1) {
+    gload_k(1);
+    lstore_k(1);
+  }
+  if (ntiles > 2) gload_k(2);
+  if (ntiles > 1) gload_v(1);
+  __syncthreads();
+  f32x16_t sc_cur[2], sc_nxt[2];
+  s_tile(0, sc_cur);
+  for (int t = 0; t < ntiles; ++t) {
+    softmax_max(t, sc_cur);
+    // S(t + 1) with the exponentials of tile t in its MFMA shadow: step m
+    // (of 2 KS) issues one MFMA, the K fragment read of step m + 3 and
+    // 16 / (2 KS) probability pairs of tile t, fenced so
+    // the compiler keeps the interleave.  On the last tile the product is of
+    // a resident buffer and is discarded (no branch in the interleaved code).
+    {
+      constexpr int NM = 2 * KS, PP = 16 / NM;   // MFMA steps, probability pairs per step
+      constexpr int AH = 3;                      // fragment reads run this many steps ahead
+      const bf16_t* kb = &Ks[(t + 1) & 1][0];
+      // step m: score tile u = m % 2, k step ks = m / 2 (the two accumulation
+      // chains alternate, so consecutive MFMAs are independent)
+      auto kfrag = [&](int m) {
+        return *reinterpret_cast<const bf16x8_t*>(kb + ((m & 1) * 32 + l32) * KLD + ((m >> 1) * 2 + half) * 8);
+      };
+      bf16x8_t kq[NM];
+#pragma unroll
+      for (int m = 0; m < AH; ++m) kq[m] = kfrag(m);
+      float psum = 0.f;
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc_nxt[u][e] = 0.f;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int u = m & 1, ks = m >> 1;
+        if (m + AH < NM) kq[m + AH] = kfrag(m + AH);
+        sc_nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[m], qf[ks], sc_nxt[u], 0, 0, 0);
+#pragma unroll
+        for (int pp = 0; pp < PP; ++pp) {
+          // pair idx: scores (hh * 8 + 2 e2, + 1) of 32 x 32 tile uu
+          const int idx = m * PP + pp;
+          const int uu = idx >> 3, hh = (idx >> 2) & 1, e2 = idx & 3;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[uu][hh * 8 + 2 * e2], sc, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[uu][hh * 8 + 2 * e2 + 1], sc, -m_run));
           psum += p0 + p1;
           w[e2] = pack_bf16x2(p0, p1);
+          if (e2 == 3) {
+            u32x4_t wv = {w[0], w[1], w[2], w[3]};
+            pf[2 * uu + hh] = __builtin_bit_cast(bf16x8_t, wv);
+          }
         }
-        u32x4_t wv = {w[0], w[1], w[2], w[3]};
-        pf[2 * u + hh] = __builtin_bit_cast(bf16x8_t, wv);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      l_run += psum;
     }
-    l_run += psum;
-    // O^T += V^T P^T over the 4 16-key steps of the tile
+    pv_tile(t);
+    // next tiles: K(t + 2), V(t + 1) to LDS, K(t + 3), V(t + 2) loaded
+    if (t + 2 < ntiles) lstore_k(t + 2);
+    if (t + 1 < ntiles) lstore_v(t + 1);
+    if (t + 3 < ntiles) gload_k(t + 3);
+    if (t + 2 < ntiles) gload_v(t + 2);
 #pragma unroll
-    for (int i = 0; i < DT; ++i) {
-      const int d = i * 32 + l32;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vs[cur][d * VLD + (kb * 2 + half) * 8]);
-        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb], o[i], 0, 0, 0);
-      }
-    }
-    if (t + 1 < ntiles) lstore(cur ^ 1);
+    for (int u = 0; u < 2; ++u) sc_cur[u] = sc_nxt[u];
     __syncthreads();
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32);
