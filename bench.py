@@ -170,7 +170,15 @@ def summarize_counters(directory, out_dir):
         for cls, (_, pats) in KERNEL_CLASSES.items():
             if cls not in hook["kernels"]:
                 continue
-            avg = sum(float(r["AverageNs"]) for pat in pats for r in stats if re.search(pat, r["Name"])) / 1e3
+            rows = [r for r in stats if any(re.search(pat, r["Name"]) for pat in pats)]
+            # one launch of a class may be several kernels (prep: one; GEMM: one per epilogue kind):
+            # duration per launch = total time / calls, per kernel name, summed over the names that
+            # make up one launch when a class launches more than one kernel per call
+            per_name = [int(r["TotalDurationNs"]) / int(r["Calls"]) for r in rows]
+            if len(pats) > 1:
+                avg = sum(per_name) / 1e3
+            else:
+                avg = sum(int(r["TotalDurationNs"]) for r in rows) / max(1, sum(int(r["Calls"]) for r in rows)) / 1e3
             agree.append(f"| {cls} | {1e3 * hook['kernels'][cls]['ms_per_launch']:.1f} | {avg:.1f} |")
         out["dominant_kernel"] = hook["roofline"]["kernel"]
     os.makedirs(out_dir, exist_ok=True)
