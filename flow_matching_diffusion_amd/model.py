@@ -24,9 +24,13 @@ def device_array(a: np.ndarray, bf16: bool, device="cuda") -> torch.Tensor:
 
 
 def upload_weights(w: Dict[str, np.ndarray], bf16: bool, device="cuda") -> Dict[str, torch.Tensor]:
-    """Linear weights/biases in the operand type; RMSNorm scales stay float."""
+    """Linear weights/biases in the operand type; RMSNorm scales stay float.
+    Tensors already on the device (drawn there) are taken as they are."""
     out = {}
     for k, v in w.items():
+        if isinstance(v, torch.Tensor):
+            out[k] = v
+            continue
         is_norm = k.endswith("_norm") or k in ("q_norm", "k_norm")
         out[k] = device_array(v, bf16 and not is_norm, device)
     return out
@@ -96,6 +100,7 @@ class BlockStack:
         if weights_f16:
             self.double = [to_f16_weights(w) for w in self.double]
             self.single = [to_f16_weights(w) for w in self.single]
+            torch.cuda.synchronize()   # the bf16 sources of the conversions may be freed by the caller
         self.fp8_state = None
         if self.fp8:
             n = len(self.double) * 2 * len(F.FP8_STREAM_SLOTS) + len(self.single) * len(F.FP8_SINGLE_SLOTS)

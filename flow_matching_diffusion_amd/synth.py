@@ -280,3 +280,62 @@ def model_inputs(wl: Workload) -> Dict[str, np.ndarray]:
     if wl.vec_in_dim is not None:
         d["y"] = normal((wl.batch, wl.vec_in_dim), 1.0, wl.config_id, 0, "y", False)
     return d
+
+
+# --------------------------------------------------------------------------- #
+# device-drawn block weights for the full 12B-shaped stack
+# --------------------------------------------------------------------------- #
+def device_stream_seed(config_id: int, block_id: int, name: str) -> int:
+    """Seed of torch's device generator for one tensor (same key as the host
+    streams)."""
+    return int(np.random.SeedSequence([BASE_SEED, config_id, block_id, tensor_id(name)]).generate_state(1)[0])
+
+
+def _device_normal(shape, std: float, wl: Workload, blk: int, name: str, dtype, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(device_stream_seed(wl.config_id, blk, name))
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(dtype)
+
+
+def device_block_weights(wl: Workload, blk: int, kind: str, device="cuda", zero_mod: bool = False):
+    """Weights of double ("double") or single ("single") block blk drawn on the
+    device with torch's generator (Philox), for stacks too large to draw on the
+    host (the 12B-shaped forward holds 11.8 B parameters).  Same shapes, names
+    and distributions as double_block_weights / single_block_weights: linears
+    and biases N(0, 0.02) in the operand type, RMSNorm scales 1 + 0.1 N(0, 1)
+    in fp32.  zero_mod=True zeroes the modulation weights and biases (every
+    shift, scale and gate is 0, so the block is the identity on its inputs).
+    These arrays never reach the oracle."""
+    import torch
+    D, F = wl.hidden, wl.mlp_hidden
+    dt = torch.bfloat16 if operands_bf16(wl) else torch.float32
+    w = {}
+
+    def lin(name, n_out, n_in, zero=False):
+        if zero:
+            w[name + ".w"] = torch.zeros((n_out, n_in), dtype=dt, device=device)
+            w[name + ".b"] = torch.zeros((n_out,), dtype=dt, device=device)
+        else:
+            w[name + ".w"] = _device_normal((n_out, n_in), WEIGHT_STD, wl, blk, name + ".w", dt, device)
+            w[name + ".b"] = _device_normal((n_out,), WEIGHT_STD, wl, blk, name + ".b", dt, device)
+
+    def gamma(name):
+        w[name] = 1.0 + GAMMA_STD * _device_normal((wl.head_dim,), 1.0, wl, blk, name, torch.float32, device)
+
+    if kind == "double":
+        for s in ("img", "txt"):
+            lin(s + "_mod", 6 * D, D, zero_mod)
+            lin(s + "_qkv", 3 * D, D)
+            gamma(s + "_q_norm")
+            gamma(s + "_k_norm")
+            lin(s + "_proj", D, D)
+            lin(s + "_fc1", F, D)
+            lin(s + "_fc2", D, F)
+    else:
+        lin("mod", 3 * D, D, zero_mod)
+        lin("lin1", 3 * D + F, D)
+        gamma("q_norm")
+        gamma("k_norm")
+        lin("lin2", D, D + F)
+    return w
