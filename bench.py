@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "MMDiT block fwd tokens/s & joint-attn TFLOP/s (512 txt+4096 img, bf16)"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 (OCP e4m3) MFMA
 
 
 def algorithmic_work(wl):
@@ -247,10 +248,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="flux12b_blocks", choices=["flux12b_blocks", "flux12b_full"],
+    ap.add_argument("--workload", default="flux12b_blocks",
+                    choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8"],
                     help="flux12b_blocks (default): the block-pair step the headline metric is quoted on; "
                          "flux12b_full: the whole 19 + 38 block forward + loss at batch 2 (block weights "
-                         "drawn on the device; no CPU baseline)")
+                         "drawn on the device; no CPU baseline); flux12b_blocks_fp8: the block pair at batch 4 "
+                         "with E4M3 linears under delayed scaling (static weights cast during warm-up)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -313,10 +316,22 @@ def main() -> int:
     def step():
         m.forward_loss(z0, z1, t, txt, y, ids, out)
 
+    fp8 = wl.precision == "fp8"
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 2) if fp8 else args.warmup):
         step()
     torch.cuda.synchronize()
+    fp8_cast_ms = None
+    if fp8:
+        # static weights: cast once more with the settled scales (timed on its own), then the
+        # timed steps run blocks + scale update without the weight cast
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        m.fp8_cast_weights()
+        e1.record()
+        torch.cuda.synchronize()
+        fp8_cast_ms = e0.elapsed_time(e1)
+        m.cast_each_forward = False
     FX.flux_timing_read()                       # discard anything recorded so far
     FX.flux_timing_enable(True)
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -354,8 +369,10 @@ def main() -> int:
     dom = max(kt, key=lambda k: kt[k]["ms_per_step"])
     d = kt[dom]
     if "tflops" in d:
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(d["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(dom),
+        # a contraction is measured against the MFMA peak of its own operand type
+        peak = PEAK_FP8_TFLOPS if dom.endswith("fp8") else PEAK_BF16_TFLOPS
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(d["tflops"] / peak, 4), "traffic": recorded_traffic(dom),
                 "flops_per_launch": d["flops_per_launch"], "ms_per_launch": round(d["ms_per_launch"], 5)}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -396,7 +413,15 @@ def main() -> int:
     }
     if full:
         rec["metric"] = "Flux-12B-shaped forward + loss tokens/s (19 double + 38 single blocks, bf16)"
-    if not args.no_cpu_baseline and not full:
+    if fp8:
+        rec["metric"] = "MMDiT block fwd tokens/s, E4M3 linears with delayed scaling (512 txt+4096 img, batch 4)"
+        rec["dtype"] = "fp8_e4m3 linears, bf16 attention"
+        rec["config"]["workload"] = "flux12b_block_pair_fp8_rf_step"
+        rec["fp8_weight_cast_ms"] = round(fp8_cast_ms, 4)
+        fk = kt.get("gemm_256_fp8")
+        if fk:
+            rec["fp8_gemm_frac_of_fp8_peak"] = round(fk["tflops"] / PEAK_FP8_TFLOPS, 4)
+    if not args.no_cpu_baseline and not full and not fp8:
         print("[bench] cpu baseline (oracle double block)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, w2, inp, synth.joint_ids(wl), work)
     else:

@@ -177,10 +177,16 @@ class BlockStack:
         ws = self.ws.get(self.ws_bytes)
         F.flux_single_fwd(self.dims, self._sstructs[i], x, wl.seq * wl.hidden, vec, rope, ws, ws.numel())
 
+    # fp8: re-cast the weights with their current scales on every forward (a
+    # training step changes them); a caller with static weights may switch
+    # this off once the weight scales have settled (after the first update the
+    # scale of a static weight is 448 / amax and stays there)
+    cast_each_forward = True
+
     def blocks_fwd(self, x: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor) -> None:
         """All blocks in order; fp8 workloads cast the weights first and
         update the scales after."""
-        if self.fp8:
+        if self.fp8 and self.cast_each_forward:
             self.fp8_cast_weights()
         for i in range(len(self.double)):
             self.double_fwd(i, x, vec, rope)
