@@ -284,14 +284,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = i * 32 + 8 * g + 4 * half;
-          uint32_t w = 0;
+          float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float y = o[i][4 * g + e] * inv;
-            mx = max(mx, abs_bits(y));
-            w |= f32_to_e4m3(y * qs) << (8 * e);
+            y[e] = o[i][4 * g + e] * inv;
+            mx = max(mx, abs_bits(y[e]));
           }
-          *reinterpret_cast<uint32_t*>(out + d0) = w;
+          *reinterpret_cast<uint32_t*>(out + d0) = f32x4_to_e4m3(y[0] * qs, y[1] * qs, y[2] * qs, y[3] * qs);
         }
     }
     const uint32_t m_img = wave_max_u32(img_row ? mx : 0u);

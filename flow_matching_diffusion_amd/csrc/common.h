@@ -136,6 +136,24 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return code | sign;
 }
 
+// Four values as E4M3FN bytes (x0 in the low byte), the same bytes as
+// f32_to_e4m3 on each: v_med3 saturates finite and infinite values to
+// +-448, then the conversion instruction rounds to nearest even (subnormals
+// included).  A NaN comes out of med3 as a number, so a group holding one
+// takes the bit-level path.  Checked equal to f32_to_e4m3 over all 2^32 fp32
+// patterns in every byte position.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float x0, float x1, float x2, float x3) {
+  const float c0 = __builtin_amdgcn_fmed3f(x0, -448.0f, 448.0f);
+  const float c1 = __builtin_amdgcn_fmed3f(x1, -448.0f, 448.0f);
+  const float c2 = __builtin_amdgcn_fmed3f(x2, -448.0f, 448.0f);
+  const float c3 = __builtin_amdgcn_fmed3f(x3, -448.0f, 448.0f);
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, (int)w, true);
+  if (__builtin_isnan(x0) || __builtin_isnan(x1) || __builtin_isnan(x2) || __builtin_isnan(x3))
+    w = f32_to_e4m3(x0) | (f32_to_e4m3(x1) << 8) | (f32_to_e4m3(x2) << 16) | (f32_to_e4m3(x3) << 24);
+  return w;
+}
+
 __device__ __forceinline__ float fp8_scale(const flux_fp8_tensor* r) {
   return (r->flags & FLUX_FP8_SCALE_SET) ? r->scale : 1.0f;
 }

@@ -97,8 +97,7 @@ __device__ __forceinline__ uint2 pack4(float4 v, int dt) {
 // Four values as E4M3 bytes (scale qs), and their largest magnitude into mx.
 __device__ __forceinline__ uint32_t pack4_e4m3(float4 v, float qs, uint32_t& mx) {
   mx = max(mx, max(max(abs_bits(v.x), abs_bits(v.y)), max(abs_bits(v.z), abs_bits(v.w))));
-  return f32_to_e4m3(v.x * qs) | (f32_to_e4m3(v.y * qs) << 8) | (f32_to_e4m3(v.z * qs) << 16) |
-         (f32_to_e4m3(v.w * qs) << 24);
+  return f32x4_to_e4m3(v.x * qs, v.y * qs, v.z * qs, v.w * qs);
 }
 
 // Store four values of a 16-bit or E4M3 output whose element offset is off.
@@ -892,9 +891,13 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   using V0 = std::integral_constant<int, 0>;
 
   int t = blockIdx.x;
-  if (t >= bt.total_tiles) return;
+  if (t >= bt.total_tiles) return;   // block-uniform
   setup(t);
   prologue_issue();
+  // amax of each problem's E4M3 output over all tiles of this block, raised
+  // once per block at the end: atomics on one address serialize (about 11 ns
+  // each), so one per wave and tile would queue behind each other
+  uint32_t mxp[2] = {0u, 0u};
   for (; t < bt.total_tiles; t += gridDim.x) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -936,7 +939,22 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
     uint32_t mx = 0;
     tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 4 * kDlStageBytes) + wave * 32 * 64,
                        cm0 + wm * WM, cn0 + wn * WN, lane, epi_dequant(pc), epi_out_scale(pc), mx);
-    epi_amax_flush(pc, mx);
+    if (cprob) mxp[1] = max(mxp[1], mx);
+    else mxp[0] = max(mxp[0], mx);
+  }
+  if (bt.p[0].qo || (bt.count > 1 && bt.p[1].qo)) {   // block-uniform
+    // stage 0 is idle: the last tile's barrier has passed and no prologue followed it
+    uint32_t* red = reinterpret_cast<uint32_t*>(smem);   // [2][4]
+    const uint32_t m0w = wave_max_u32(mxp[0]), m1w = wave_max_u32(mxp[1]);
+    if (lane == 0) {
+      red[wave] = m0w;
+      red[4 + wave] = m1w;
+    }
+    __syncthreads();
+    if (tid < 2 && (tid == 0 || bt.count > 1)) {
+      const uint32_t m = max(max(red[4 * tid], red[4 * tid + 1]), max(red[4 * tid + 2], red[4 * tid + 3]));
+      if (bt.p[tid].qo && m) fp8_amax_raise(bt.p[tid].qo, __uint_as_float(m));
+    }
   }
 }
 

@@ -229,14 +229,18 @@ hipError_t launch_patchify(const float* z, int batch, int channels, int hw, void
 // deep dive", Implementation details / Adaptive layer normalization):
 // h = (x - mean) / sqrt(var + eps) * (1 + scale[b]) + shift[b].
 // One wave per token row, the row in registers (two-pass variance).  A block
-// of 4 waves handles 4 * kLnRows consecutive rows; (1 + scale) and shift of
-// the sample of its first row are staged in LDS once, so L2 serves the
-// modulation vectors once per block instead of once per row (a row whose
-// sample differs reads them from global memory).  Registers are kept low
-// (no cross-row prefetch) so 4 blocks fit per CU and their rows overlap.
+// of 4 waves owns a contiguous range of rows (at most kLnBlocks blocks, two
+// per CU); wave w takes rows w, w+4, ... of the range and loads its next row
+// while it normalizes the current one.  (1 + scale) and shift of the sample
+// of the block's first row are staged in LDS once (a row of another sample
+// reads them from global memory, where L2 serves them).
+// E4M3 output: the amax of each segment is reduced over the block and raises
+// the segment's record with one atomic per block.  Atomics on one address are
+// serialized by the memory system (about 11 ns each, measured), so one per
+// row would cost more than the whole kernel.
 // ===========================================================================
 constexpr int kLnMaxVec = 16;   // float4 per lane: D <= 64 * 4 * 16 = 4096
-constexpr int kLnRows = 2;      // rows per wave
+constexpr int kLnBlocks = 512;  // grid cap
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
@@ -260,26 +264,23 @@ __device__ __forceinline__ void store4<_Float16>(_Float16* p, float a, float b, 
 }
 
 template <typename T, int NV>
-__global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
+__global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a, int64_t rows_per_block) {
   __shared__ float4 msc[NV * 64], msh[NV * 64];   // (1 + scale), shift of the block's first sample
+  __shared__ uint32_t red[2][4];                  // per-wave amax of each segment (E4M3 output)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t blk_first = (int64_t)blockIdx.x * 4 * kLnRows;
+  const int64_t total = a.s[0].rows + (a.count > 1 ? (int64_t)a.s[1].rows : 0);
+  const int64_t b0 = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t b1 = b0 + rows_per_block < total ? b0 + rows_per_block : total;
+  if (b0 >= total) return;   // block-uniform
   const int D = a.dim;
-  // global rows run over segment 0 then segment 1
-  auto locate = [&](int64_t g, int& si, int64_t& r) -> bool {
-    si = 0;
-    r = g;
-    if (r >= a.s[0].rows) {
-      if (a.count < 2) return false;
-      r -= a.s[0].rows;
-      si = 1;
-      if (r >= a.s[1].rows) return false;
-    }
-    return true;
+  // global rows run over segment 0 then segment 1 (g < total)
+  auto locate = [&](int64_t g, int& si, int64_t& r) {
+    si = g >= a.s[0].rows ? 1 : 0;
+    r = si ? g - a.s[0].rows : g;
   };
   int bsi;
   int64_t brow;
-  if (!locate(blk_first, bsi, brow)) return;   // block-uniform
+  locate(b0, bsi, brow);
   const int64_t bsam = brow / a.s[bsi].xmap.seg;
   {
     const float* scp = a.s[bsi].scale + bsam * a.s[bsi].mod_bstride;
@@ -292,24 +293,32 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
   }
   __syncthreads();
 
-  const int64_t first = blk_first + wave * kLnRows;
-  auto load_row = [&](int sidx, int64_t row, float4* dst) {
+  auto load_row = [&](int64_t g, float4* dst) {
+    int sidx;
+    int64_t row;
+    locate(g, sidx, row);
     const LnSeg& sg = a.s[sidx];
     const int64_t bb = row / sg.xmap.seg, ll = row % sg.xmap.seg;
     const float* x = sg.x + bb * sg.xmap.bstride + ll * sg.xmap.ld;
 #pragma unroll
     for (int i = 0; i < NV; ++i) dst[i] = reinterpret_cast<const float4*>(x)[lane + 64 * i];
   };
-  int si;
-  int64_t r;
-  if (!locate(first, si, r)) return;   // wave-uniform; no barrier follows
-  float4 v[NV];
+  uint32_t mxs[2] = {0u, 0u};
+  float qsc[2] = {1.0f, 1.0f};   // E4M3 output: delayed scales, read once (stores may alias the records)
+  if constexpr (sizeof(T) == 1) {
+    qsc[0] = fp8_scale(a.s[0].q);
+    if (a.count > 1) qsc[1] = fp8_scale(a.s[1].q);
+  }
+  float4 v[NV], vn[NV];
+  int64_t g = b0 + wave;
+  if (g < b1) load_row(g, v);
 #pragma unroll 1
-  for (int k = 0; k < kLnRows; ++k) {
-    load_row(si, r, v);
-    int si_n = 0;
-    int64_t r_n = 0;
-    const bool has_next = k + 1 < kLnRows && locate(first + k + 1, si_n, r_n);
+  for (; g < b1; g += 4) {
+    const bool has_next = g + 4 < b1;   // wave-uniform
+    if (has_next) load_row(g + 4, vn);
+    int si;
+    int64_t r;
+    locate(g, si, r);
     const LnSeg& sg = a.s[si];
     const int64_t bb = r / sg.xmap.seg, ll = r % sg.xmap.seg;
     const bool staged = si == bsi && bb == bsam;   // wave-uniform
@@ -329,7 +338,7 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
     const float rstd = 1.0f / sqrtf(var + a.eps);
     T* out = reinterpret_cast<T*>(sg.out) + bb * sg.omap.bstride + ll * sg.omap.ld;
     uint32_t mx = 0;
-    const float qs = sizeof(T) == 1 ? fp8_scale(sg.q) : 1.0f;
+    const float qs = qsc[si];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = (lane + 64 * i) * 4;
@@ -347,29 +356,41 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a) {
       const float y2 = (v[i].z - mean) * rstd * s1.z + h4.z;
       const float y3 = (v[i].w - mean) * rstd * s1.w + h4.w;
       if constexpr (sizeof(T) == 1) {
-        // E4M3 output with the record's delayed scale; the row's amax raises the record's
+        // E4M3 output with the record's delayed scale; amax of the unscaled values
         mx = max(mx, max(max(abs_bits(y0), abs_bits(y1)), max(abs_bits(y2), abs_bits(y3))));
-        *reinterpret_cast<uint32_t*>(out + c) = f32_to_e4m3(y0 * qs) | (f32_to_e4m3(y1 * qs) << 8) |
-                                                (f32_to_e4m3(y2 * qs) << 16) | (f32_to_e4m3(y3 * qs) << 24);
+        *reinterpret_cast<uint32_t*>(out + c) = f32x4_to_e4m3(y0 * qs, y1 * qs, y2 * qs, y3 * qs);
       } else {
         store4<T>(out + c, y0, y1, y2, y3);
       }
     }
     if constexpr (sizeof(T) == 1) {
-      mx = wave_max_u32(mx);
-      if (lane == 0) fp8_amax_raise(sg.q, __uint_as_float(mx));
+      if (si) mxs[1] = max(mxs[1], mx);
+      else mxs[0] = max(mxs[0], mx);
     }
-    if (!has_next) break;
-    si = si_n;
-    r = r_n;
+    if (has_next) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = vn[i];
+    }
+  }
+  if constexpr (sizeof(T) == 1) {
+    const uint32_t m0 = wave_max_u32(mxs[0]), m1 = wave_max_u32(mxs[1]);
+    if (lane == 0) {
+      red[0][wave] = m0;
+      red[1][wave] = m1;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const uint32_t m = max(max(red[threadIdx.x][0], red[threadIdx.x][1]), max(red[threadIdx.x][2], red[threadIdx.x][3]));
+      if (m) fp8_amax_raise(a.s[threadIdx.x].q, __uint_as_float(m));
+    }
   }
 }
 
 template <typename T>
-static void launch_ln_mod_t(const LnArgs& a, dim3 grid, hipStream_t stream) {
+static void launch_ln_mod_t(const LnArgs& a, dim3 grid, int64_t rpb, hipStream_t stream) {
   // D is a multiple of 256, at most 4096 (checked by the API): NV float4 per lane
 #define FLUX_LN_CASE(nv) \
-  case nv: hipLaunchKernelGGL((ln_mod_kernel<T, nv>), grid, dim3(256), 0, stream, a); break;
+  case nv: hipLaunchKernelGGL((ln_mod_kernel<T, nv>), grid, dim3(256), 0, stream, a, rpb); break;
   switch (a.dim / 256) {
     FLUX_LN_CASE(1) FLUX_LN_CASE(2) FLUX_LN_CASE(3) FLUX_LN_CASE(4) FLUX_LN_CASE(5) FLUX_LN_CASE(6)
     FLUX_LN_CASE(7) FLUX_LN_CASE(8) FLUX_LN_CASE(9) FLUX_LN_CASE(10) FLUX_LN_CASE(11) FLUX_LN_CASE(12)
@@ -380,17 +401,21 @@ static void launch_ln_mod_t(const LnArgs& a, dim3 grid, hipStream_t stream) {
 
 hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {  // dtype: output element type
   if (a.dim % 256 != 0 || a.dim < 256 || a.dim > 256 * kLnMaxVec) return hipErrorInvalidValue;
-  int64_t rows = a.s[0].rows + (a.count > 1 ? a.s[1].rows : 0);
-  const dim3 grid((unsigned)ceil_div(rows, 4 * kLnRows));
+  const int64_t rows = a.s[0].rows + (a.count > 1 ? a.s[1].rows : 0);
+  if (rows <= 0) return hipSuccess;
+  int64_t blocks = ceil_div(rows, 4);
+  if (blocks > kLnBlocks) blocks = kLnBlocks;
+  const int64_t rpb = ceil_div(rows, blocks);
+  const dim3 grid((unsigned)ceil_div(rows, rpb));
   TimingScope ts(kKcLnMod, stream, (double)rows * a.dim * (4.0 + (dtype == kF32 ? 4.0 : dtype == kFP8 ? 1.0 : 2.0)));
   if (dtype == kFP8)
-    launch_ln_mod_t<uint8_t>(a, grid, stream);
+    launch_ln_mod_t<uint8_t>(a, grid, rpb, stream);
   else if (dtype == kBF16)
-    launch_ln_mod_t<bf16_t>(a, grid, stream);
+    launch_ln_mod_t<bf16_t>(a, grid, rpb, stream);
   else if (dtype == kF16)
-    launch_ln_mod_t<_Float16>(a, grid, stream);
+    launch_ln_mod_t<_Float16>(a, grid, rpb, stream);
   else
-    launch_ln_mod_t<float>(a, grid, stream);
+    launch_ln_mod_t<float>(a, grid, rpb, stream);
   return hipGetLastError();
 }
 
@@ -398,10 +423,13 @@ hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {  // d
 // Modulation GEMV (M = batch <= 4 per launch): y[b, n] (+)= sum_k W[n, k]
 // act(x[b, k]) + bias[n] ("Flux model API reference", AdaLN: Linear over
 // SiLU(vec); also the timestep / pooled-vector embedders).  Weight-bandwidth
-// bound: each wave streams whole W rows with 16-byte loads; act(x) is staged
-// in LDS once per block.
+// bound: each wave streams kGemvRows whole W rows at a time with 16-byte
+// loads, kGemvLoads per lane and row in flight; act(x) is staged in LDS once
+// per block and each LDS read of it serves all rows of the group.
 // ===========================================================================
 constexpr int kGemvMaxB = 4;
+constexpr int kGemvLoads = 4;   // 16-byte loads per lane and row in flight
+constexpr int kGemvRows = 4;    // W rows a wave reduces at once (act(x) read from LDS once for all)
 
 template <typename T>
 struct Vec16;  // 16 bytes of operand elements
@@ -431,40 +459,96 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvBatch a) {
   extern __shared__ float xs[];   // [batch][K]
   const GemvProblem& p = a.p[blockIdx.y];
   const int K = p.K, B = a.batch;
-  for (int i = threadIdx.x; i < B * K; i += blockDim.x) {
-    const int b = i / K, k = i % K;
-    const float v = p.x[(int64_t)b * p.x_bstride + k];
-    xs[i] = p.act_silu ? silu_f(v) : v;
+  if ((K & 3) == 0 && (p.x_bstride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0) {
+    // float4 staging, all of a thread's loads in flight before the first SiLU
+    constexpr int SU = 4;
+    const int K4 = K >> 2, n4 = B * K4;
+    for (int i0 = threadIdx.x; i0 < n4; i0 += 256 * SU) {
+      float4 v[SU];
+#pragma unroll
+      for (int j = 0; j < SU; ++j) {
+        const int i = i0 + 256 * j;
+        if (i < n4) v[j] = reinterpret_cast<const float4*>(p.x + (int64_t)(i / K4) * p.x_bstride)[i % K4];
+      }
+#pragma unroll
+      for (int j = 0; j < SU; ++j) {
+        const int i = i0 + 256 * j;
+        if (i < n4) {
+          if (p.act_silu) v[j] = make_float4(silu_f(v[j].x), silu_f(v[j].y), silu_f(v[j].z), silu_f(v[j].w));
+          reinterpret_cast<float4*>(xs)[i] = v[j];
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < B * K; i += blockDim.x) {
+      const int b = i / K, k = i % K;
+      const float v = p.x[(int64_t)b * p.x_bstride + k];
+      xs[i] = p.act_silu ? silu_f(v) : v;
+    }
   }
   __syncthreads();
   constexpr int E = Vec16<T>::n;
+  constexpr int U = kGemvLoads;
+  constexpr int R = kGemvRows;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const T* W = reinterpret_cast<const T*>(p.W);
   const T* bias = reinterpret_cast<const T*>(p.bias);
-  for (int n = blockIdx.x * 4 + wave; n < p.N; n += gridDim.x * 4) {
-    const T* wr = W + (int64_t)n * K;
-    float acc[kGemvMaxB] = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = lane * E; k0 < K; k0 += 64 * E) {
-      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(wr + k0);
-      float w[E];
-      unpack16<T>(raw, w);
+  for (int n0 = (blockIdx.x * 4 + wave) * R; n0 < p.N; n0 += gridDim.x * 4 * R) {
+    float acc[R][kGemvMaxB];
 #pragma unroll
-      for (int b = 0; b < kGemvMaxB; ++b) {
-        if (b < B) {
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[b] += w[e] * xs[b * K + k0 + e];
+      for (int b = 0; b < kGemvMaxB; ++b) acc[r][b] = 0.f;
+    for (int kc = 0; kc < K; kc += 64 * E * U) {
+      // R x U 16-byte loads issued before the first use
+      u32x4_t raw[R][U];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int k0 = kc + (u * 64 + lane) * E;
+          if (k0 < K && n0 + r < p.N) raw[r][u] = *reinterpret_cast<const u32x4_t*>(W + (int64_t)(n0 + r) * K + k0);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k0 = kc + (u * 64 + lane) * E;
+        if (k0 < K) {
+          // act(x) for these E columns, read from LDS once for all R rows
+          float xv[kGemvMaxB][E];
+#pragma unroll
+          for (int b = 0; b < kGemvMaxB; ++b)
+#pragma unroll
+            for (int e = 0; e < E; ++e) xv[b][e] = b < B ? xs[b * K + k0 + e] : 0.f;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (n0 + r < p.N) {
+              float w[E];
+              unpack16<T>(raw[r][u], w);
+#pragma unroll
+              for (int b = 0; b < kGemvMaxB; ++b) {
+                if (b < B) {
+#pragma unroll
+                  for (int e = 0; e < E; ++e) acc[r][b] += w[e] * xv[b][e];
+                }
+              }
+            }
+          }
         }
       }
     }
 #pragma unroll
-    for (int b = 0; b < kGemvMaxB; ++b) {
-      if (b < B) {
-        const float s = wave_sum(acc[b]);
-        if (lane == 0) {
-          float v = s + (bias ? load_f32<T>(bias + n) : 0.f);
-          float* y = p.y + (int64_t)b * p.y_bstride + n;
-          *y = p.accumulate ? *y + v : v;
+    for (int r = 0; r < R; ++r) {
+      const int n = n0 + r;
+#pragma unroll
+      for (int b = 0; b < kGemvMaxB; ++b) {
+        if (b < B && n < p.N) {
+          const float s = wave_sum(acc[r][b]);
+          if (lane == 0) {
+            float v = s + (bias ? load_f32<T>(bias + n) : 0.f);
+            float* y = p.y + (int64_t)b * p.y_bstride + n;
+            *y = p.accumulate ? *y + v : v;
+          }
         }
       }
     }
@@ -477,8 +561,11 @@ hipError_t launch_gemv(const GemvBatch& a, int dtype, hipStream_t stream) {
     maxn = a.p[i].N > maxn ? a.p[i].N : maxn;
     maxk = a.p[i].K > maxk ? a.p[i].K : maxk;
   }
-  int gx = (int)ceil_div(maxn, 4);
-  if (gx > 512) gx = 512;
+  // about three blocks per CU over all problems: each wave keeps kGemvLoads
+  // 16-byte loads per lane in flight
+  int gx = (int)ceil_div(maxn, 4 * kGemvRows);
+  const int cap = 768 / (a.count > 0 ? a.count : 1);
+  if (gx > cap) gx = cap;
   const size_t lds = (size_t)a.batch * maxk * sizeof(float);
   const dim3 grid(gx, a.count);
   double wbytes = 0.0;
@@ -723,12 +810,9 @@ __global__ void __launch_bounds__(256) fp8_quantize_kernel(const T* __restrict__
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      o[j] = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mx = max(mx, abs_bits(v[4 * j + e]));
-        o[j] |= f32_to_e4m3(v[4 * j + e] * qs) << (8 * e);
-      }
+      for (int e = 0; e < 4; ++e) mx = max(mx, abs_bits(v[4 * j + e]));
+      o[j] = f32x4_to_e4m3(v[4 * j] * qs, v[4 * j + 1] * qs, v[4 * j + 2] * qs, v[4 * j + 3] * qs);
     }
     reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
