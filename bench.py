@@ -34,16 +34,20 @@ PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 (OCP e4m3) MFMA
 
 
-def algorithmic_work(wl):
+def algorithmic_work(wl, single_seq=False):
     """FLOPs the method must do per step ("Flux architecture deep dive", MMDiT
     layer and Flux single block): every linear 2*M*N*K, attention 4*B*H*L^2*Dh,
     over the workload's double and single blocks plus the image embedding,
-    the text projection (when the workload has one) and the output linear."""
+    the text projection (when the workload has one) and the output linear.
+    single_seq: the single blocks in the sequential form (qkv, proj, fc1, fc2
+    over the joint sequence: the double block's linears)."""
     B, L, Li, Lt = wl.batch, wl.seq, wl.l_img, wl.l_txt
     D, F, H, dh, C = wl.hidden, wl.mlp_hidden, wl.heads, wl.head_dim, wl.latent_ch
     T = B * L
     gemm_double = 2 * T * D * (3 * D + D + F + F)         # qkv, proj, fc1, fc2 over both streams
     gemm_single = 2 * T * D * (3 * D + F) + 2 * T * (D + F) * D
+    if single_seq:
+        gemm_single = gemm_double
     attn = 4 * B * H * L * L * dh                         # QK^T and PV, no mask
     small_gemm = 2 * B * Li * C * D + 2 * B * Li * D * C  # image embedding, output linear
     if wl.context_dim:
@@ -249,11 +253,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="flux12b_blocks",
-                    choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8"],
+                    choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8", "flux12b_blocks_seq"],
                     help="flux12b_blocks (default): the block-pair step the headline metric is quoted on; "
                          "flux12b_full: the whole 19 + 38 block forward + loss at batch 2 (block weights "
                          "drawn on the device; no CPU baseline); flux12b_blocks_fp8: the block pair at batch 4 "
-                         "with E4M3 linears under delayed scaling (static weights cast during warm-up)")
+                         "with E4M3 linears under delayed scaling (static weights cast during warm-up); "
+                         "flux12b_blocks_seq: the block pair with the single block in its sequential form "
+                         "(flux_single_seq_fwd)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -292,7 +298,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     FX.lib()
     full = args.workload == "flux12b_full"
-    wl = synth.WORKLOADS[args.workload]
+    seq = args.workload == "flux12b_blocks_seq"
+    wl = synth.WORKLOADS["flux12b_blocks" if seq else args.workload]
     print(f"[bench] generating weights for {wl.name}", file=sys.stderr, flush=True)
     emb = synth.embed_weights(wl)
     mi = synth.model_inputs(wl)
@@ -302,7 +309,8 @@ def main() -> int:
         sws = [synth.device_block_weights(wl, wl.n_double + i, "single") for i in range(wl.n_single)]
     else:
         w2 = synth.double_block_weights(wl, 0)
-        dws, sws = [w2], [synth.single_block_weights(wl, 1)]
+        dws = [w2]
+        sws = [synth.single_seq_block_weights(wl, 1) if seq else synth.single_block_weights(wl, 1)]
         inp = synth.block_inputs(wl)
     # block linears held in fp16, converted once here (static weights; not timed)
     m = FluxModel(wl, emb, dws, sws, weights_f16=True)
@@ -352,7 +360,7 @@ def main() -> int:
     loss = float(out["loss"].item())
     assert np.isfinite(loss), "non-finite loss"
 
-    work = algorithmic_work(wl)
+    work = algorithmic_work(wl, single_seq=seq)
     kt = {}
     for k, (ms, n, w) in kernels.items():
         if not n:
@@ -421,7 +429,10 @@ def main() -> int:
         fk = kt.get("gemm_256_fp8")
         if fk:
             rec["fp8_gemm_frac_of_fp8_peak"] = round(fk["tflops"] / PEAK_FP8_TFLOPS, 4)
-    if not args.no_cpu_baseline and not full and not fp8:
+    if seq:
+        rec["metric"] = "MMDiT block fwd tokens/s, double + sequential single block (512 txt+4096 img)"
+        rec["config"]["workload"] = "flux12b_block_pair_sequential_single_rf_step"
+    if not args.no_cpu_baseline and not full and not fp8 and not seq:
         print("[bench] cpu baseline (oracle double block)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, w2, inp, synth.joint_ids(wl), work)
     else:

@@ -230,7 +230,7 @@ const char* flux_last_error(void) { return g_err; }
 
 size_t flux_workspace_bytes(const flux_dims* d, int32_t op) {
   if (check_dims(d) != FLUX_OK) return 0;
-  if (op == 0) return block_ws(d, nullptr).bytes;
+  if (op == 0 || op == 2) return block_ws(d, nullptr).bytes;   // the sequential block is a one-stream double block
   if (op == 1) return single_ws(d, nullptr).bytes;
   return 0;
 }
@@ -385,6 +385,21 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   }
   FLUX_HIP(launch_gemm(g, lin, st), "fc2 GEMM");
   return FLUX_OK;
+}
+
+// --------------------------- sequential single block ---------------------------
+flux_status flux_single_seq_fwd(const flux_dims* d, const flux_stream_weights* w, float* x, int64_t x_bstride,
+                                const float* vec, const float* rope, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  g_err[0] = 0;
+  flux_status s = check_dims(d);
+  if (s != FLUX_OK) return s;
+  // the whole joint sequence as the one (image) stream of a double block: same
+  // L, same workspace layout, rope rows in the same order
+  flux_dims one = *d;
+  one.l_img = d->l_img + d->l_txt;
+  one.l_txt = 0;
+  return flux_block_fwd(&one, w, nullptr, x, x_bstride, nullptr, 0, vec, rope, workspace, workspace_bytes, stream);
 }
 
 // --------------------------------- single block --------------------------------

@@ -34,7 +34,7 @@ FP8_SINGLE_SLOTS = ("lin1_x", "lin1_w", "lin2_x", "lin2_w")
 
 # every symbol include/flux.h declares
 EXPORTED = (
-    "flux_block_fwd", "flux_single_fwd", "rf_noise_loss", "flux_rope_table", "flux_embed_fwd",
+    "flux_block_fwd", "flux_single_fwd", "flux_single_seq_fwd", "rf_noise_loss", "flux_rope_table", "flux_embed_fwd",
     "flux_final_fwd", "flux_linear_fwd", "flux_attention_fwd", "flux_workspace_bytes",
     "flux_rf_workspace_bytes", "flux_embed_workspace_bytes", "flux_final_workspace_bytes",
     "flux_attention_workspace_bytes", "flux_status_string", "flux_last_error", "flux_timing_enable",
@@ -106,6 +106,7 @@ def lib() -> C.CDLL:
         "flux_block_fwd": [P(flux_dims), P(flux_stream_weights), P(flux_stream_weights), vp, i64, vp, i64, vp, vp,
                            vp, sz, vp],
         "flux_single_fwd": [P(flux_dims), P(flux_single_weights), vp, i64, vp, vp, vp, sz, vp],
+        "flux_single_seq_fwd": [P(flux_dims), P(flux_stream_weights), vp, i64, vp, vp, vp, sz, vp],
         "rf_noise_loss": [P(rf_args), vp],
         "flux_rope_table": [vp, i32, i32, P(C.c_int32), f32, vp, vp],
         "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
@@ -196,14 +197,17 @@ def dims_for(wl, batch: Optional[int] = None, weights_f16: bool = False) -> flux
                      wl.axes_dim, wl.theta, wl.eps, precision_code(wl.precision), weights_f16)
 
 
-def stream_weights(w: Dict[str, object], prefix: str, fp8=None) -> flux_stream_weights:
-    """fp8: device address of the stream's 8 flux_fp8_tensor records (fp8 dims only)."""
+def stream_weights(w: Dict[str, object], prefix: Optional[str], fp8=None) -> flux_stream_weights:
+    """Keys "<prefix>_mod.w" ...; prefix None: unprefixed keys ("mod.w", the
+    sequential single block).  fp8: device address of the stream's 8
+    flux_fp8_tensor records (fp8 dims only)."""
     s = flux_stream_weights()
+    pre = f"{prefix}_" if prefix else ""
     for f in ("mod", "qkv", "proj", "fc1", "fc2"):
-        setattr(s, f + "_w", ptr(w[f"{prefix}_{f}.w"]))
-        setattr(s, f + "_b", ptr(w[f"{prefix}_{f}.b"]))
-    s.q_norm = ptr(w[f"{prefix}_q_norm"])
-    s.k_norm = ptr(w[f"{prefix}_k_norm"])
+        setattr(s, f + "_w", ptr(w[f"{pre}{f}.w"]))
+        setattr(s, f + "_b", ptr(w[f"{pre}{f}.b"]))
+    s.q_norm = ptr(w[f"{pre}q_norm"])
+    s.k_norm = ptr(w[f"{pre}k_norm"])
     s.fp8 = ptr(fp8)
     return s
 
@@ -246,6 +250,12 @@ def flux_single_fwd(dims: flux_dims, w: flux_single_weights, x, x_bstride: int, 
                     workspace_bytes: int, stream=None) -> None:
     _check(lib().flux_single_fwd(C.byref(dims), C.byref(w), ptr(x), x_bstride, ptr(vec), ptr(rope), ptr(workspace),
                                  workspace_bytes, _stream(stream)), "flux_single_fwd")
+
+
+def flux_single_seq_fwd(dims: flux_dims, w: flux_stream_weights, x, x_bstride: int, vec, rope, workspace,
+                        workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_single_seq_fwd(C.byref(dims), C.byref(w), ptr(x), x_bstride, ptr(vec), ptr(rope),
+                                     ptr(workspace), workspace_bytes, _stream(stream)), "flux_single_seq_fwd")
 
 
 def flux_rf_workspace_bytes(batch: int, n_per_sample: int) -> int:

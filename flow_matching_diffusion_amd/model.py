@@ -56,7 +56,7 @@ class Workspace:
 
 # the block linears whose weights may be held in fp16 (not the modulation GEMVs)
 LINEARS = ("img_qkv.w", "img_proj.w", "img_fc1.w", "img_fc2.w", "txt_qkv.w", "txt_proj.w", "txt_fc1.w", "txt_fc2.w",
-           "lin1.w", "lin2.w")
+           "lin1.w", "lin2.w", "qkv.w", "proj.w", "fc1.w", "fc2.w")
 
 
 def to_f16_weights(w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
@@ -101,25 +101,34 @@ class BlockStack:
             self.double = [to_f16_weights(w) for w in self.double]
             self.single = [to_f16_weights(w) for w in self.single]
             torch.cuda.synchronize()   # the bf16 sources of the conversions may be freed by the caller
+        # a single block whose weights hold "qkv.w" is the sequential form
+        # (flux_single_seq_fwd: one stream of a double block over the joint
+        # sequence); otherwise the fused parallel form (flux_single_fwd)
+        self.single_seq = ["qkv.w" in w for w in single_ws]
         self.fp8_state = None
         if self.fp8:
-            n = len(self.double) * 2 * len(F.FP8_STREAM_SLOTS) + len(self.single) * len(F.FP8_SINGLE_SLOTS)
+            n_single = [len(F.FP8_STREAM_SLOTS) if q else len(F.FP8_SINGLE_SLOTS) for q in self.single_seq]
+            n = len(self.double) * 2 * len(F.FP8_STREAM_SLOTS) + sum(n_single)
             self.fp8_tensors = n
             self.fp8_state = torch.zeros(F.flux_fp8_state_bytes(n), dtype=torch.uint8, device=device)
             self._fp8_casts = []           # (master bf16, e4m3 copy, W record address)
             self._dq = [self._fp8_copies(w, ("img", "txt"), FP8_DOUBLE, 2 * 8 * i, 8)
                         for i, w in enumerate(self.double)]
-            base = len(self.double) * 16
-            self._sq = [self._fp8_copies(w, (None,), FP8_SINGLE, base + 4 * i, 4) for i, w in enumerate(self.single)]
+            first = [len(self.double) * 16 + sum(n_single[:i]) for i in range(len(self.single))]
+            self._sq = [self._fp8_copies(w, (None,), FP8_DOUBLE if q else FP8_SINGLE, f, 8 if q else 4)
+                        for w, q, f in zip(self.single, self.single_seq, first)]
             self._dstructs = [(F.stream_weights(q, "img", self.fp8_record(2 * 8 * i)),
                                F.stream_weights(q, "txt", self.fp8_record(2 * 8 * i + 8)))
                               for i, q in enumerate(self._dq)]
-            self._sstructs = [F.single_weights(q, self.fp8_record(base + 4 * i)) for i, q in enumerate(self._sq)]
+            self._sstructs = [F.stream_weights(w, None, self.fp8_record(f)) if q else
+                              F.single_weights(w, self.fp8_record(f))
+                              for w, q, f in zip(self._sq, self.single_seq, first)]
         else:
             self._dstructs = [(F.stream_weights(w, "img"), F.stream_weights(w, "txt")) for w in self.double]
-            self._sstructs = [F.single_weights(w) for w in self.single]
+            self._sstructs = [F.stream_weights(w, None) if q else F.single_weights(w)
+                              for w, q in zip(self.single, self.single_seq)]
         self.ws = Workspace(device)
-        self.ws_bytes = max(F.flux_workspace_bytes(self.dims, 0), F.flux_workspace_bytes(self.dims, 1))
+        self.ws_bytes = max(F.flux_workspace_bytes(self.dims, op) for op in (0, 1, 2))
         self.device = device
 
     # ------------------------------------------------------------------ fp8
@@ -175,7 +184,8 @@ class BlockStack:
     def single_fwd(self, i: int, x: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor) -> None:
         wl = self.wl
         ws = self.ws.get(self.ws_bytes)
-        F.flux_single_fwd(self.dims, self._sstructs[i], x, wl.seq * wl.hidden, vec, rope, ws, ws.numel())
+        fwd = F.flux_single_seq_fwd if self.single_seq[i] else F.flux_single_fwd
+        fwd(self.dims, self._sstructs[i], x, wl.seq * wl.hidden, vec, rope, ws, ws.numel())
 
     # fp8: re-cast the weights with their current scales on every forward (a
     # training step changes them); a caller with static weights may switch

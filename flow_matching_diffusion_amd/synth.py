@@ -197,6 +197,22 @@ def single_block_weights(wl: Workload, blk: int) -> Dict[str, np.ndarray]:
     return w
 
 
+def single_seq_block_weights(wl: Workload, blk: int) -> Dict[str, np.ndarray]:
+    """Sequential single block: mod [6D, D] (shift1, scale1, gate1, shift2,
+    scale2, gate2), qkv [3D, D], q_norm/k_norm [Dh], proj [D, D], fc1 [F, D],
+    fc2 [D, F] (one stream of a double block's shapes)."""
+    D, F, bf = wl.hidden, wl.mlp_hidden, operands_bf16(wl)
+    w: Dict[str, np.ndarray] = {}
+    w.update(_lin(wl, blk, "seq_mod", 6 * D, D, bf))
+    w.update(_lin(wl, blk, "seq_qkv", 3 * D, D, bf))
+    w["seq_q_norm"] = _gamma(wl, blk, "seq_q_norm")
+    w["seq_k_norm"] = _gamma(wl, blk, "seq_k_norm")
+    w.update(_lin(wl, blk, "seq_proj", D, D, bf))
+    w.update(_lin(wl, blk, "seq_fc1", F, D, bf))
+    w.update(_lin(wl, blk, "seq_fc2", D, F, bf))
+    return {k[len("seq_"):]: v for k, v in w.items()}
+
+
 def embed_weights(wl: Workload) -> Dict[str, np.ndarray]:
     """img_in [D, C]; txt_in [D, context] (if any); time_in 256->D->D;
     vector_in vec_in->D->D (if any); final mod [2D, D] (shift, scale); out [C, D]."""

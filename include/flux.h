@@ -201,6 +201,32 @@ flux_status flux_single_fwd(const flux_dims* dims, const flux_single_weights* w,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * flux_single_seq_fwd -- one single-stream block over the joint sequence in
+ * the sequential form the architecture page writes out step by step ("Flux
+ * architecture deep dive", Model components / Flux single block: adaLN,
+ * self-attention, gated residual, then adaLN, MLP, gated residual).
+ *
+ * (shift1, scale1, gate1, shift2, scale2, gate2) = Linear_mod(SiLU(vec));
+ * h = LayerNorm(x)(1 + scale1) + shift1; q|k|v = Linear_qkv(h); q, k <- RMSNorm
+ * over head_dim, RoPE; O = softmax attention over all L = l_img + l_txt rows;
+ * x += gate1 * Linear_proj(O); x += gate2 * fc2(GELU(fc1(LayerNorm(x)(1 +
+ * scale2) + shift2))).  This is the double block's per-stream computation
+ * with the whole joint sequence as its one stream, and it runs the same
+ * kernels.
+ *
+ *  w     one stream's weights (flux_stream_weights: mod [6D, D], qkv [3D, D],
+ *        q/k norms, proj, fc1, fc2; fp8: FLUX_FP8_STREAM_TENSORS records).
+ *  x     [B, L, D] float (image rows then text rows), sample b at
+ *        x + b*x_bstride; updated in place.
+ *  vec, rope as for flux_block_fwd; workspace of at least
+ *        flux_workspace_bytes(dims, 2) bytes.
+ * Errors as for flux_block_fwd.
+ */
+flux_status flux_single_seq_fwd(const flux_dims* dims, const flux_stream_weights* w, float* x,
+                                int64_t x_bstride, const float* vec, const float* rope,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * rf_noise_loss -- rectified-flow noising and velocity MSE ("Flux architecture
  * deep dive", Flow matching framework and Mathematical formulation / Flow
  * matching objective; "Flux model API reference", apply_flow_matching_noise
@@ -346,7 +372,8 @@ flux_status flux_fp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* 
                                 const flux_fp8_tensor* rw, const void* b, float* y, int64_t ldy,
                                 void* stream);
 
-/* Workspace sizes (bytes).  op: 0 double block, 1 single block. */
+/* Workspace sizes (bytes).  op: 0 double block, 1 single block, 2 sequential single block;
+ * 0 for invalid dims or op. */
 size_t flux_workspace_bytes(const flux_dims* dims, int32_t op);
 size_t flux_rf_workspace_bytes(int32_t batch, int64_t n_per_sample);
 size_t flux_embed_workspace_bytes(int32_t precision, int32_t batch, int32_t channels, int32_t height,

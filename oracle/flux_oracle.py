@@ -34,7 +34,7 @@ __all__ = [
     "f64", "rf_noise", "rf_noise_f32_order", "rf_loss",
     "timestep_embedding", "silu", "gelu", "linear", "layernorm", "modulate",
     "rmsnorm", "adaln", "rope_angles", "apply_rope", "attention_probs",
-    "attention", "double_block", "single_block", "final_layer",
+    "attention", "double_block", "single_block", "single_block_sequential", "final_layer",
     "conditioning_vector", "patchify", "unpatchify", "flux_forward",
     "param_count",
 ]
@@ -306,6 +306,44 @@ def single_block(x, vec, angles, w: Dict[str, np.ndarray], heads: int, eps: floa
         taps["attn"] = o
     cat = np.concatenate([o, gelu(y[:, sel, 3 * D:])], axis=-1)
     return x[:, sel] + gate[:, None, :] * lin("lin2", cat, w["lin2.w"], w["lin2.b"])
+
+
+def single_block_sequential(x, vec, angles, w: Dict[str, np.ndarray], heads: int, eps: float = 1e-6,
+                            rows: Optional[np.ndarray] = None, lin=None) -> np.ndarray:
+    """One single-stream block in the sequential form the architecture page
+    writes out step by step ("Flux architecture deep dive", Model components /
+    Flux single block): the whole joint sequence is one stream with two
+    adaLN-modulated sub-blocks, each closed by its own gated residual.
+
+    (shift1, scale1, gate1, shift2, scale2, gate2) = adaLN(vec) (six chunks);
+    h = LN(x)(1 + scale1) + shift1; q|k|v = Linear_qkv(h); q, k <- RMSNorm;
+    RoPE on q, k; O = softmax attention over every token;
+    x <- x + gate1 * Linear_proj(O);
+    h2 = LN(x)(1 + scale2) + shift2; x <- x + gate2 * fc2(GELU(fc1(h2))).
+    Weights: "mod" [6D, D], "qkv" [3D, D], "q_norm"/"k_norm" [Dh], "proj"
+    [D, D], "fc1" [F, D], "fc2" [D, F].  The text rows stay in the output
+    (reading S2 of the fused form applies here too: text leaves the sequence
+    only after the last block).
+    rows: optional token indices; only those output rows are evaluated.
+    lin: optional hook lin(name, x, W, b) for the token-path linears, named
+    "qkv", "proj", "fc1", "fc2".
+    """
+    lin = lin or _plain_linear
+    x = f64(x)
+    D = x.shape[-1]
+    sel = rows if rows is not None else np.arange(x.shape[1])
+    sh1, sc1, g1, sh2, sc2, g2 = adaln(vec, w["mod.w"], w["mod.b"], 6)
+    h = modulate(x, sh1, sc1, eps)
+    qkv = lin("qkv", h, w["qkv.w"], w["qkv.b"])
+    q = rmsnorm(_heads(qkv[:, sel, :D], heads), w["q_norm"], eps)
+    k = rmsnorm(_heads(qkv[..., D:2 * D], heads), w["k_norm"], eps)
+    v = _heads(qkv[..., 2 * D:], heads)
+    ang = f64(angles)
+    o = attention(apply_rope(q, ang[:, sel]), apply_rope(k, ang), v)
+    x1 = x[:, sel] + g1[:, None, :] * lin("proj", o, w["proj.w"], w["proj.b"])
+    h2 = modulate(x1, sh2, sc2, eps)
+    u = gelu(lin("fc1", h2, w["fc1.w"], w["fc1.b"]))
+    return x1 + g2[:, None, :] * lin("fc2", u, w["fc2.w"], w["fc2.b"])
 
 
 # --------------------------------------------------------------------------- #

@@ -148,3 +148,39 @@ def single_block(x, vec, ids, w, heads, axes_dim, theta, eps):
             rows.append([tok[c] + gate[c] * y2[c] for c in range(D)])
         out.append(rows)
     return out
+
+
+def single_block_sequential(x, vec, ids, w, heads, axes_dim, theta, eps):
+    """Sequential single block: six adaLN chunks; attention sub-block then MLP
+    sub-block over the whole sequence, each with its gated residual."""
+    x, vec, ids = map(_tolist, (x, vec, ids))
+    W = {k: _tolist(v) for k, v in w.items()}
+    B, D = len(vec), len(vec[0])
+    dh = D // heads
+    out = []
+    for b in range(B):
+        sv = [silu(a) for a in vec[b]]
+        m = vec_linear(sv, W["mod.w"], W["mod.b"])
+        ch = [m[i * D:(i + 1) * D] for i in range(6)]
+        Q, K, V = [], [], []
+        for n, tok in enumerate(x[b]):
+            y = vec_linear(ln_mod(tok, ch[0], ch[1], eps), W["qkv.w"], W["qkv.b"])
+            Q.append([rope_token(rms(y[hd * dh:(hd + 1) * dh], W["q_norm"], eps), ids[b][n], axes_dim, theta)
+                      for hd in range(heads)])
+            K.append([rope_token(rms(y[D + hd * dh:D + (hd + 1) * dh], W["k_norm"], eps), ids[b][n], axes_dim,
+                                 theta) for hd in range(heads)])
+            V.append([y[2 * D + hd * dh:2 * D + (hd + 1) * dh] for hd in range(heads)])
+        O = [[] for _ in x[b]]
+        for hd in range(heads):
+            oh = attend([q[hd] for q in Q], [k[hd] for k in K], [v[hd] for v in V])
+            for n in range(len(O)):
+                O[n].extend(oh[n])
+        rows = []
+        for n, tok in enumerate(x[b]):
+            p = vec_linear(O[n], W["proj.w"], W["proj.b"])
+            x1 = [tok[c] + ch[2][c] * p[c] for c in range(D)]
+            u = [gelu(a) for a in vec_linear(ln_mod(x1, ch[3], ch[4], eps), W["fc1.w"], W["fc1.b"])]
+            f = vec_linear(u, W["fc2.w"], W["fc2.b"])
+            rows.append([x1[c] + ch[5][c] * f[c] for c in range(D)])
+        out.append(rows)
+    return out

@@ -60,7 +60,8 @@ def test_bad_dims_rejected(kw, status):
     assert L.flux_block_fwd(C.byref(d), None, None, None, 0, None, 0, None, None, None, 0, None) == status
     assert L.flux_last_error()
     assert L.flux_single_fwd(C.byref(d), None, None, 0, None, None, None, 0, None) == status
-    assert F.flux_workspace_bytes(d, 0) == 0
+    assert L.flux_single_seq_fwd(C.byref(d), None, None, 0, None, None, None, 0, None) == status
+    assert F.flux_workspace_bytes(d, 0) == 0 and F.flux_workspace_bytes(d, 2) == 0
 
 
 def test_null_and_misaligned_pointers_rejected():
@@ -95,6 +96,15 @@ def test_null_and_misaligned_pointers_rejected():
     s = L.flux_block_fwd(C.byref(d), C.byref(w), C.byref(w), fake, 64 * 256, fake, 16 * 256, fake, fake, fake + 16,
                          ws_need, None)
     assert s == F.FLUX_ERR_INVALID_ARGUMENT
+    # sequential single block: the joint sequence as one stream (x stride covers l_img + l_txt rows)
+    ws_seq = F.flux_workspace_bytes(d, 2)
+    assert ws_seq > 0
+    s = L.flux_single_seq_fwd(C.byref(d), C.byref(w), fake, 64 * 256, fake, fake, fake, ws_seq, None)
+    assert s == F.FLUX_ERR_INVALID_ARGUMENT and b"bstride" in L.flux_last_error()
+    s = L.flux_single_seq_fwd(C.byref(d), C.byref(w2), fake, 80 * 256, fake, fake, fake, ws_seq, None)
+    assert s == F.FLUX_ERR_INVALID_ARGUMENT and b"NULL" in L.flux_last_error()
+    s = L.flux_single_seq_fwd(C.byref(d), C.byref(w), fake, 80 * 256, fake, fake, fake, ws_seq - 1, None)
+    assert s == F.FLUX_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_rf_argument_checks():
@@ -135,7 +145,8 @@ def test_workspace_sizes_grow_with_problem():
     big = F.flux_workspace_bytes(_dims(batch=4), 0)
     assert 0 < small < big
     assert F.flux_workspace_bytes(_dims(), 1) > 0
-    assert F.flux_workspace_bytes(_dims(), 2) == 0
+    assert F.flux_workspace_bytes(_dims(), 2) == F.flux_workspace_bytes(_dims(), 0)   # one-stream double block
+    assert F.flux_workspace_bytes(_dims(), 3) == 0
     assert F.flux_rf_workspace_bytes(2, 1 << 20) >= 2 * 8
 
 

@@ -317,6 +317,51 @@ def test_adaln_zero_blocks_are_identity():
     assert np.array_equal(O.single_block(x, inp["vec"], ang, w1, wl.heads), x)
 
 
+def _seq_case(wl):
+    w = synth.single_seq_block_weights(wl, 2)
+    w = {k: (v * 20 if k.endswith(".w") or k.endswith(".b") else v) for k, v in w.items()}
+    inp = synth.block_inputs(wl)
+    ids = synth.joint_ids(wl).astype(np.float64)
+    ids[..., 0] = RNG.integers(0, 3, size=ids.shape[:2])
+    x = np.concatenate([inp["x_img"], inp["x_txt"]], axis=1).astype(np.float64)
+    return w, x, inp["vec"].astype(np.float64), ids
+
+
+def test_single_block_sequential_bruteforce():
+    # the sequential single block ("Flux architecture deep dive", Flux single
+    # block, written step by step) against the pure-Python rerun
+    wl = _tiny_wl()
+    w, x, vec, ids = _seq_case(wl)
+    ang = O.rope_angles(ids, wl.axes_dim, wl.theta)
+    got = O.single_block_sequential(x, vec, ang, w, wl.heads, wl.eps)
+    ref = BF.single_block_sequential(x, vec, ids, w, wl.heads, wl.axes_dim, wl.theta, wl.eps)
+    np.testing.assert_allclose(got, ref, atol=1e-10, rtol=1e-11)
+    # both sub-blocks moved the stream: dropping either residual changes the result
+    assert np.abs(got - x).max() > 0.1
+    w_noattn = dict(w)
+    w_noattn["proj.w"] = np.zeros_like(w["proj.w"])
+    w_noattn["proj.b"] = np.zeros_like(w["proj.b"])
+    assert np.abs(O.single_block_sequential(x, vec, ang, w_noattn, wl.heads, wl.eps) - got).max() > 0.1
+
+
+def test_single_block_sequential_adaln_zero_rows_and_text_invariance():
+    wl = _tiny_wl(img_h=2, img_w=3, l_txt=3)
+    w, x, vec, ids = _seq_case(wl)
+    ang = O.rope_angles(ids, wl.axes_dim, wl.theta)
+    full = O.single_block_sequential(x, vec, ang, w, wl.heads)
+    sub = O.single_block_sequential(x, vec, ang, w, wl.heads, rows=np.array([1, 7]))
+    np.testing.assert_allclose(sub, full[:, [1, 7]], atol=1e-13)
+    wz = dict(w)
+    wz["mod.w"] = np.zeros_like(w["mod.w"])
+    wz["mod.b"] = np.zeros_like(w["mod.b"])
+    assert np.array_equal(O.single_block_sequential(x, vec, ang, wz, wl.heads), x)
+    # a token permutation (ids moved along) permutes the output rows
+    perm = RNG.permutation(x.shape[1])
+    angp = O.rope_angles(ids[:, perm], wl.axes_dim, wl.theta)
+    np.testing.assert_allclose(O.single_block_sequential(x[:, perm], vec, angp, w, wl.heads), full[:, perm],
+                               atol=1e-11)
+
+
 def test_double_block_attention_is_joint():
     # q = k = 0 makes attention uniform over the whole joint sequence, so with
     # v = h, proj = I, gate1 = 1 and the MLP gated off, every image AND text
