@@ -253,13 +253,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="flux12b_blocks",
-                    choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8", "flux12b_blocks_seq"],
+                    choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8", "flux12b_blocks_seq",
+                             "flux12b_sample_cfg"],
                     help="flux12b_blocks (default): the block-pair step the headline metric is quoted on; "
                          "flux12b_full: the whole 19 + 38 block forward + loss at batch 2 (block weights "
                          "drawn on the device; no CPU baseline); flux12b_blocks_fp8: the block pair at batch 4 "
                          "with E4M3 linears under delayed scaling (static weights cast during warm-up); "
                          "flux12b_blocks_seq: the block pair with the single block in its sequential form "
-                         "(flux_single_seq_fwd)")
+                         "(flux_single_seq_fwd); flux12b_sample_cfg: Euler sampling steps of one image with "
+                         "classifier-free guidance (conditional + null-prompt rows in one batch-2 forward, "
+                         "guidance embedding on) on the block-pair model")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -299,9 +302,13 @@ def main() -> int:
     FX.lib()
     full = args.workload == "flux12b_full"
     seq = args.workload == "flux12b_blocks_seq"
-    wl = synth.WORKLOADS["flux12b_blocks" if seq else args.workload]
+    sample = args.workload == "flux12b_sample_cfg"
+    if sample:
+        wl = synth.custom_workload("flux12b_sample_cfg", base="flux12b_blocks", batch=2)
+    else:
+        wl = synth.WORKLOADS["flux12b_blocks" if seq else args.workload]
     print(f"[bench] generating weights for {wl.name}", file=sys.stderr, flush=True)
-    emb = synth.embed_weights(wl)
+    emb = synth.embed_weights(wl, guidance=sample)
     mi = synth.model_inputs(wl)
     if full:
         w2 = None
@@ -323,6 +330,17 @@ def main() -> int:
 
     def step():
         m.forward_loss(z0, z1, t, txt, y, ids, out)
+
+    if sample:
+        si = synth.sampler_inputs(wl, 1)
+        s_z1, s_txt, s_ids, s_g = dev(si["z1"]), dev(si["txt"], True), dev(si["ids"]), dev(si["guidance"])
+        n_grid = args.warmup + args.steps
+        step_i = [0]
+
+        def step():   # noqa: F811 - one sampler step: batch-2 forward + guided Euler update
+            m.sample(s_z1, n_grid, s_txt, None, s_ids, cfg_w=3.5, guidance=s_g, out=out,
+                     steps=range(step_i[0], step_i[0] + 1))
+            step_i[0] += 1
 
     fp8 = wl.precision == "fp8"
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -357,8 +375,12 @@ def main() -> int:
     kernels = FX.flux_timing_read()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
-    loss = float(out["loss"].item())
-    assert np.isfinite(loss), "non-finite loss"
+    if sample:
+        loss = None
+        assert bool(torch.isfinite(out["z"]).all()), "non-finite sample"
+    else:
+        loss = float(out["loss"].item())
+        assert np.isfinite(loss), "non-finite loss"
 
     work = algorithmic_work(wl, single_seq=seq)
     kt = {}
@@ -429,10 +451,18 @@ def main() -> int:
         fk = kt.get("gemm_256_fp8")
         if fk:
             rec["fp8_gemm_frac_of_fp8_peak"] = round(fk["tflops"] / PEAK_FP8_TFLOPS, 4)
+    if sample:
+        rec["metric"] = ("CFG Euler sampling tokens/s (1 image: conditional + null-prompt rows in one batch-2 "
+                         "forward, 512 txt+4096 img, 1 double + 1 single block)")
+        rec["config"]["workload"] = "flux12b_block_pair_cfg_euler_sampling_step"
+        rec["config"]["step"] = ("embed (+ guidance embedding) + 1 double + 1 single block + head at batch 2, "
+                                 "then the fused CFG combination + Euler update")
+        rec["config"]["images"] = 1
+        rec["sampler_step_ms"] = round(ms_step, 4)
     if seq:
         rec["metric"] = "MMDiT block fwd tokens/s, double + sequential single block (512 txt+4096 img)"
         rec["config"]["workload"] = "flux12b_block_pair_sequential_single_rf_step"
-    if not args.no_cpu_baseline and not full and not fp8 and not seq:
+    if not args.no_cpu_baseline and not full and not fp8 and not seq and not sample:
         print("[bench] cpu baseline (oracle double block)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, w2, inp, synth.joint_ids(wl), work)
     else:

@@ -514,6 +514,12 @@ static bool overlap(const void* a, const void* b, int64_t bytes) {
   const char* y = static_cast<const char*>(b);
   return x < y + bytes && y < x + bytes;
 }
+// [a, a + la) and [b, b + lb) share a byte
+static bool ranges_overlap(const void* a, int64_t la, const void* b, int64_t lb) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + lb && y < x + la;
+}
 
 flux_status rf_noise_loss(const rf_args* a, void* stream) {
   g_err[0] = 0;
@@ -548,6 +554,42 @@ flux_status rf_noise_loss(const rf_args* a, void* stream) {
   return FLUX_OK;
 }
 
+// --------------------------------- sampling ---------------------------------
+flux_status flux_euler_step(const flux_euler_args* a, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(a, "args is NULL");
+  REQUIRE(a->batch >= 1, "batch must be >= 1 (got %d)", a->batch);
+  REQUIRE(a->n_per_sample >= 1, "n_per_sample must be >= 1");
+  REQUIRE((int64_t)a->batch * a->n_per_sample < ((int64_t)1 << 40), "problem too large");
+  REQUIRE(a->v && a->z, "v and z are required");
+  REQUIRE(aligned16(a->v) && aligned16(a->z) && (!a->z_model || aligned16(a->z_model)),
+          "v, z and z_model must be 16-byte aligned");
+  REQUIRE(isfinite(a->t_cur) && isfinite(a->t_next) && isfinite(a->guidance), "t_cur, t_next and guidance must be finite");
+  const int copies = a->z_model ? a->copies : 0;
+  REQUIRE(!a->z_model || copies == 1 || copies == 2, "copies must be 1 or 2 (got %d)", a->copies);
+  REQUIRE(!a->t_model || a->t_model_n >= 1, "t_model_n must be >= 1");
+  const int64_t zb = (int64_t)a->batch * a->n_per_sample * 4;
+  const int64_t vb = zb * (a->cfg ? 2 : 1);
+  REQUIRE(!ranges_overlap(a->z, zb, a->v, vb), "z must not overlap v");
+  if (a->z_model) {
+    const int64_t mb = zb * copies;
+    REQUIRE(!ranges_overlap(a->z_model, mb, a->v, vb), "z_model must not overlap v");
+    REQUIRE(!ranges_overlap(a->z_model, mb, a->z, zb), "z_model must not overlap z");
+  }
+  if (a->t_model) {
+    const int64_t tb = (int64_t)a->t_model_n * 4;
+    REQUIRE(!ranges_overlap(a->t_model, tb, a->v, vb) && !ranges_overlap(a->t_model, tb, a->z, zb),
+            "t_model must not overlap v or z");
+  }
+  // dt is the fp32 difference, as on the device side of the reading
+  const float dt = a->t_cur - a->t_next;
+  FLUX_HIP(launch_euler_step(a->batch, a->n_per_sample, a->v, a->cfg ? 1 : 0, a->guidance, dt, a->z, a->z_model,
+                             copies, a->t_next, a->t_model, a->t_model ? a->t_model_n : 0,
+                             static_cast<hipStream_t>(stream)),
+           "Euler step");
+  return FLUX_OK;
+}
+
 // -------------------------------- RoPE table --------------------------------
 flux_status flux_rope_table(const float* ids, int32_t batch, int32_t seq, const int32_t axes_dim[3], float theta,
                             float* table, void* stream) {
@@ -577,8 +619,9 @@ size_t flux_embed_workspace_bytes(int32_t precision, int32_t batch, int32_t chan
 flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
                            int32_t l_txt, int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
                            const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
-                           const float* y, float* x_img, int64_t img_bstride, float* x_txt, int64_t txt_bstride,
-                           float* vec, void* workspace, size_t workspace_bytes, void* stream) {
+                           const float* y, const float* guidance, float* x_img, int64_t img_bstride, float* x_txt,
+                           int64_t txt_bstride, float* vec, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   g_err[0] = 0;
   REQUIRE(precision == FLUX_PREC_F32 || precision == FLUX_PREC_BF16, "precision %d unknown", precision);
   REQUIRE(batch >= 1 && channels >= 1 && height >= 1 && width >= 1 && hidden >= 1, "sizes must be >= 1");
@@ -609,6 +652,8 @@ flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, i
     REQUIRE(w->vector_in1_b && w->vector_in2_w && w->vector_in2_b && y && y_dim >= 1 && y_dim % kq == 0,
             "vector_in needs both layers, y and y_dim (a multiple of %d)", kq);
   }
+  const bool has_g = w->guidance_in_w != nullptr;
+  if (has_g) REQUIRE(w->guidance_in_b && guidance, "guidance_in needs its bias and the guidance values");
   flux_status s = check_workspace(workspace, workspace_bytes,
                                   flux_embed_workspace_bytes(precision, batch, channels, height, width, hidden));
   if (s != FLUX_OK) return s;
@@ -645,6 +690,9 @@ flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, i
     g2.p[0] = gemv_problem(w->vector_in2_w, w->vector_in2_b, hidden, hidden, a2, hidden, vec, hidden, 1, 1);
     FLUX_HIP(run_gemv(g2, batch, dt, st), "vector embedder layer 2");
   }
+  if (has_g)
+    FLUX_HIP(launch_guidance_embed(batch, hidden, guidance, w->guidance_in_w, w->guidance_in_b, dt, vec, st),
+             "guidance embedding");
   return FLUX_OK;
 }
 

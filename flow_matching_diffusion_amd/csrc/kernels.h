@@ -144,6 +144,13 @@ hipError_t launch_rf_loss(int batch, int64_t n, const float* z0, const float* z1
                           float* loss, float* loss_ps, double* partials, int parts_per_sample,
                           hipStream_t stream);
 int rf_parts_per_sample(int64_t n);
+// z <- z - dt * (cfg ? v_u + w (v_c - v_u) : v); z also copied into `copies`
+// batch-halves of zm; tm[0..tm_n) = t_next
+hipError_t launch_euler_step(int batch, int64_t n, const float* v, int cfg, float w, float dt, float* z, float* zm,
+                             int copies, float t_next, float* tm, int tm_n, hipStream_t stream);
+// vec[b, :] += g[b] * W[:, 0] + bias  (W, bias in `dtype`, kBF16 or kF32)
+hipError_t launch_guidance_embed(int batch, int dim, const float* g, const void* w, const void* bias, int dtype,
+                                 float* vec, hipStream_t stream);
 hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStream_t stream);
 
 // ---------------------------------- fp8 ------------------------------------

@@ -64,6 +64,96 @@ hipError_t launch_rf_noise(int batch, int64_t n, const float* z0, const float* z
   return hipGetLastError();
 }
 
+// ===========================================================================
+// Sampling ("Flux architecture deep dive", Sampling (inference) / Euler
+// integration and Classifier-free guidance): one Euler step of dz/dt = v from
+// t_cur down to t_next, z <- z - dt * g, with g = v_u + w (v_c - v_u) under
+// guidance (model output rows 0..B-1 conditional, B..2B-1 unconditional) or
+// g = v.  Each operation is rounded in the order written (contraction off),
+// so the result is the same bits on every build.  The new z is also written
+// into each of `copies` halves of the next forward's input, and t_next into
+// its timestep vector.
+// ===========================================================================
+__global__ void __launch_bounds__(256) euler_step_kernel(int batch, int64_t n, const float* __restrict__ v, int cfg,
+                                                         float w, float dt, float* __restrict__ z,
+                                                         float* __restrict__ zm, int copies, float t_next,
+                                                         float* __restrict__ tm, int tm_n) {
+#pragma clang fp contract(off)
+  const int b = blockIdx.y;
+  const float* vc = v + (int64_t)b * n;
+  const float* vu = v + (int64_t)(batch + b) * n;
+  float* zb = z + (int64_t)b * n;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  auto step = [&](float zc, float c, float u) -> float {
+    float g = c;
+    if (cfg) {
+      const float d = c - u;
+      const float wd = w * d;
+      g = u + wd;
+    }
+    const float s = dt * g;
+    return zc - s;
+  };
+  if ((n & 3) == 0) {
+    const int64_t n4 = n >> 2;
+    for (int64_t i = i0; i < n4; i += stride) {
+      const float4 c = reinterpret_cast<const float4*>(vc)[i];
+      const float4 u = cfg ? reinterpret_cast<const float4*>(vu)[i] : c;
+      const float4 zc = reinterpret_cast<const float4*>(zb)[i];
+      const float4 r = make_float4(step(zc.x, c.x, u.x), step(zc.y, c.y, u.y), step(zc.z, c.z, u.z),
+                                   step(zc.w, c.w, u.w));
+      reinterpret_cast<float4*>(zb)[i] = r;
+      for (int k = 0; k < copies; ++k) reinterpret_cast<float4*>(zm + ((int64_t)k * batch + b) * n)[i] = r;
+    }
+  } else {
+    for (int64_t i = i0; i < n; i += stride) {
+      const float r = step(zb[i], vc[i], cfg ? vu[i] : vc[i]);
+      zb[i] = r;
+      for (int k = 0; k < copies; ++k) zm[((int64_t)k * batch + b) * n + i] = r;
+    }
+  }
+  if (tm && b == 0 && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < tm_n; i += blockDim.x) tm[i] = t_next;
+}
+
+hipError_t launch_euler_step(int batch, int64_t n, const float* v, int cfg, float w, float dt, float* z, float* zm,
+                             int copies, float t_next, float* tm, int tm_n, hipStream_t stream) {
+  const int64_t work = (n & 3) == 0 ? n / 4 : n;
+  int gx = (int)ceil_div(work, 256);
+  if (gx > 1024) gx = 1024;
+  TimingScope ts(kKcRf, stream, (double)batch * n * ((cfg ? 12.0 : 8.0) + 4.0 + 4.0 * copies));
+  hipLaunchKernelGGL(euler_step_kernel, dim3(gx, batch), dim3(256), 0, stream, batch, n, v, cfg, w, dt, z, zm,
+                     copies, t_next, tm, tm_n);
+  return hipGetLastError();
+}
+
+// Guidance embedding ("Flux architecture deep dive", Conditioning: the
+// optional guidance scale g enters the combined vector through a Linear):
+// vec[b, j] += g[b] * W[j] + bias[j], W the [D, 1] weight.
+template <typename T>
+__global__ void __launch_bounds__(256) guidance_embed_kernel(int batch, int dim, const float* __restrict__ g,
+                                                             const T* __restrict__ w, const T* __restrict__ bias,
+                                                             float* __restrict__ vec) {
+  const int b = blockIdx.y;
+  const float gb = g[b];
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < dim; j += gridDim.x * blockDim.x)
+    vec[(int64_t)b * dim + j] += gb * load_f32<T>(w + j) + load_f32<T>(bias + j);
+}
+
+hipError_t launch_guidance_embed(int batch, int dim, const float* g, const void* w, const void* bias, int dtype,
+                                 float* vec, hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(dim, 256), batch);
+  TimingScope ts(kKcMisc, stream);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(guidance_embed_kernel<bf16_t>, grid, dim3(256), 0, stream, batch, dim, g,
+                       static_cast<const bf16_t*>(w), static_cast<const bf16_t*>(bias), vec);
+  else
+    hipLaunchKernelGGL(guidance_embed_kernel<float>, grid, dim3(256), 0, stream, batch, dim, g,
+                       static_cast<const float*>(w), static_cast<const float*>(bias), vec);
+  return hipGetLastError();
+}
+
 // Velocity MSE, stage 1: block (g, b) sums (v_pred - (z1 - z0))^2 over its
 // slice of sample b in fp64.  Each thread walks a fixed strided set, then a
 // fixed butterfly/tree -> the same bits on every run.

@@ -39,7 +39,7 @@ EXPORTED = (
     "flux_rf_workspace_bytes", "flux_embed_workspace_bytes", "flux_final_workspace_bytes",
     "flux_attention_workspace_bytes", "flux_status_string", "flux_last_error", "flux_timing_enable",
     "flux_timing_classes", "flux_timing_class_name", "flux_timing_read", "flux_convert_bf16_to_f16",
-    "flux_fp8_state_bytes", "flux_fp8_quantize", "flux_fp8_update", "flux_fp8_linear_fwd",
+    "flux_fp8_state_bytes", "flux_fp8_quantize", "flux_fp8_update", "flux_fp8_linear_fwd", "flux_euler_step",
 )
 
 
@@ -83,7 +83,14 @@ class rf_args(C.Structure):
 class flux_embed_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("img_in_w", "img_in_b", "txt_in_w", "txt_in_b", "time_in1_w",
                                           "time_in1_b", "time_in2_w", "time_in2_b", "vector_in1_w",
-                                          "vector_in1_b", "vector_in2_w", "vector_in2_b")]
+                                          "vector_in1_b", "vector_in2_w", "vector_in2_b", "guidance_in_w",
+                                          "guidance_in_b")]
+
+
+class flux_euler_args(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("n_per_sample", C.c_int64), ("v", C.c_void_p), ("cfg", C.c_int32),
+                ("guidance", C.c_float), ("t_cur", C.c_float), ("t_next", C.c_float), ("z", C.c_void_p),
+                ("z_model", C.c_void_p), ("copies", C.c_int32), ("t_model", C.c_void_p), ("t_model_n", C.c_int32)]
 
 
 # --------------------------------------------------------------------------- #
@@ -110,7 +117,8 @@ def lib() -> C.CDLL:
         "rf_noise_loss": [P(rf_args), vp],
         "flux_rope_table": [vp, i32, i32, P(C.c_int32), f32, vp, vp],
         "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
-                           vp, i64, vp, i64, vp, vp, sz, vp],
+                           vp, vp, i64, vp, i64, vp, vp, sz, vp],
+        "flux_euler_step": [P(flux_euler_args), vp],
         "flux_final_fwd": [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
         "flux_attention_fwd": [i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, sz, vp],
@@ -226,7 +234,7 @@ def single_weights(w: Dict[str, object], fp8=None) -> flux_single_weights:
 
 def embed_weights(w: Dict[str, object]) -> flux_embed_weights:
     s = flux_embed_weights()
-    for f in ("img_in", "txt_in", "time_in1", "time_in2", "vector_in1", "vector_in2"):
+    for f in ("img_in", "txt_in", "time_in1", "time_in2", "vector_in1", "vector_in2", "guidance_in"):
         setattr(s, f + "_w", ptr(w.get(f + ".w")))
         setattr(s, f + "_b", ptr(w.get(f + ".b")))
     return s
@@ -283,11 +291,22 @@ def flux_embed_workspace_bytes(precision, batch, channels, height, width, hidden
 
 def flux_embed_fwd(precision, batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim,
                    w: flux_embed_weights, z_t, txt, t, y, x_img, img_bstride, x_txt, txt_bstride, vec, workspace,
-                   workspace_bytes, stream=None) -> None:
+                   workspace_bytes, stream=None, guidance=None) -> None:
     _check(lib().flux_embed_fwd(precision, batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim,
-                                C.byref(w), ptr(z_t), ptr(txt), ptr(t), ptr(y), ptr(x_img), img_bstride, ptr(x_txt),
-                                txt_bstride, ptr(vec), ptr(workspace), workspace_bytes, _stream(stream)),
+                                C.byref(w), ptr(z_t), ptr(txt), ptr(t), ptr(y), ptr(guidance), ptr(x_img),
+                                img_bstride, ptr(x_txt), txt_bstride, ptr(vec), ptr(workspace), workspace_bytes,
+                                _stream(stream)),
            "flux_embed_fwd")
+
+
+def flux_euler_step(batch: int, n_per_sample: int, v, z, t_cur: float, t_next: float, cfg: bool = False,
+                    guidance: float = 1.0, z_model=None, copies: int = 1, t_model=None, t_model_n: int = 0,
+                    stream=None) -> None:
+    a = flux_euler_args()
+    a.batch, a.n_per_sample, a.v, a.cfg, a.guidance = batch, n_per_sample, ptr(v), int(bool(cfg)), guidance
+    a.t_cur, a.t_next, a.z, a.z_model, a.copies = t_cur, t_next, ptr(z), ptr(z_model), copies
+    a.t_model, a.t_model_n = ptr(t_model), t_model_n
+    _check(lib().flux_euler_step(C.byref(a), _stream(stream)), "flux_euler_step")
 
 
 def flux_final_workspace_bytes(precision, batch, height, width, hidden) -> int:

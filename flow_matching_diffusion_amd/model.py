@@ -220,14 +220,9 @@ class FluxModel(BlockStack):
                             F.flux_final_workspace_bytes(p, wl.batch, wl.img_h, wl.img_w, wl.hidden),
                             F.flux_rf_workspace_bytes(wl.batch, wl.latent_ch * wl.l_img))
 
-    def forward_loss(self, z0, z1, t, txt, y, ids, out: Optional[Dict[str, torch.Tensor]] = None):
-        """Noise, forward, loss.  Returns a dict of device tensors: z_t, v_target,
-        x (joint residual after the blocks), vec, v_pred, loss, loss_per_sample."""
+    def _buffers(self, ids, o: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
         wl, dev = self.wl, self.device
         B, C, D = wl.batch, wl.latent_ch, wl.hidden
-        n = C * wl.l_img
-        p = precision_of(wl)
-        o = out if out is not None else {}
         if not o:
             f32 = dict(dtype=torch.float32, device=dev)
             o["z_t"] = torch.empty((B, C, wl.img_h, wl.img_w), **f32)
@@ -238,20 +233,80 @@ class FluxModel(BlockStack):
             o["loss"] = torch.empty((1,), **f32)
             o["loss_per_sample"] = torch.empty((B,), **f32)
             o["rope"] = self.rope_table(ids)
+        return o
+
+    def _forward(self, o, z_t, t, txt, y, guidance=None) -> None:
+        """Embeddings, blocks, output head: v_pred of z_t at times t into o."""
+        wl = self.wl
+        B, C, D = wl.batch, wl.latent_ch, wl.hidden
+        p = precision_of(wl)
         ws = self.ws.get(self.ws_bytes)
-        F.rf_noise_loss(B, n, z0, z1, t, z_t=o["z_t"], v_target=o["v_target"])
         x = o["x"]
         has_txt_in = "txt_in.w" in self.emb
         if not has_txt_in:
             x[:, wl.l_img:].copy_(txt)   # text enters at hidden width: a copy into the joint buffer
         F.flux_embed_fwd(p, B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
-                         wl.vec_in_dim or 0, self._estruct, o["z_t"], txt if has_txt_in else None, t,
+                         wl.vec_in_dim or 0, self._estruct, z_t, txt if has_txt_in else None, t,
                          y, x, wl.seq * D, x[:, wl.l_img:] if has_txt_in else None, wl.seq * D, o["vec"], ws,
-                         ws.numel())
+                         ws.numel(), guidance=guidance)
         self.blocks_fwd(x, o["vec"], o["rope"])
         F.flux_final_fwd(p, B, C, wl.img_h, wl.img_w, D, wl.eps, self.emb["final_mod.w"], self.emb["final_mod.b"],
                          self.emb["final_out.w"], self.emb["final_out.b"], x, wl.seq * D, o["vec"], o["v_pred"], ws,
                          ws.numel())
+
+    def forward_loss(self, z0, z1, t, txt, y, ids, out: Optional[Dict[str, torch.Tensor]] = None):
+        """Noise, forward, loss.  Returns a dict of device tensors: z_t, v_target,
+        x (joint residual after the blocks), vec, v_pred, loss, loss_per_sample."""
+        wl = self.wl
+        B, n = wl.batch, wl.latent_ch * wl.l_img
+        o = self._buffers(ids, out if out is not None else {})
+        ws = self.ws.get(self.ws_bytes)
+        F.rf_noise_loss(B, n, z0, z1, t, z_t=o["z_t"], v_target=o["v_target"])
+        self._forward(o, o["z_t"], t, txt, y)
         F.rf_noise_loss(B, n, z0, z1, t, v_pred=o["v_pred"], loss=o["loss"], loss_per_sample=o["loss_per_sample"],
                         workspace=ws, workspace_bytes=ws.numel())
+        return o
+
+    def forward(self, z_t, t, txt, y, ids, guidance=None, out: Optional[Dict[str, torch.Tensor]] = None):
+        """Velocity of z_t at times t (the model call of a sampler)."""
+        o = self._buffers(ids, out if out is not None else {})
+        self._forward(o, z_t, t, txt, y, guidance)
+        return o
+
+    def sample(self, z1, n_steps: int, txt, y, ids, cfg_w: Optional[float] = None, guidance=None,
+               out: Optional[Dict[str, torch.Tensor]] = None, steps=None):
+        """Euler sampling from noise z1 [B', C, H, W] at t = 1 down to t = 0 on
+        the uniform grid of n_steps steps ("Flux architecture deep dive",
+        Sampling (inference)).  With cfg_w the model batch is 2B' (this
+        model's workload batch): txt / y hold the conditional rows then the
+        unconditional (null prompt) rows, and each step combines the two
+        velocities by classifier-free guidance in the step kernel.  Without
+        cfg_w the model batch is B'.  guidance: optional [batch] device values
+        for the guidance embedding.  steps: optional range of step indices to
+        run (default all), for timing a subset.  Returns the state dict; "z"
+        holds the sample."""
+        wl = self.wl
+        cfg = cfg_w is not None
+        Bm = wl.batch
+        Bs = Bm // 2 if cfg else Bm
+        assert not cfg or Bm % 2 == 0, "classifier-free guidance needs an even model batch"
+        n = wl.latent_ch * wl.l_img
+        o = self._buffers(ids, out if out is not None else {})
+        if "z" not in o:
+            o["z"] = torch.empty((Bs,) + tuple(z1.shape[1:]), dtype=torch.float32, device=self.device)
+            o["t"] = torch.empty((Bm,), dtype=torch.float32, device=self.device)
+        ts = [1.0 - i / n_steps for i in range(n_steps + 1)]
+        run = range(n_steps) if steps is None else steps
+        for i in run:
+            if i == 0:
+                # the model input at t = 1 is the noise itself, in every batch half
+                o["z"].copy_(z1)
+                o["z_t"][:Bs].copy_(z1)
+                if cfg:
+                    o["z_t"][Bs:].copy_(z1)
+                o["t"].fill_(ts[0])
+            self._forward(o, o["z_t"], o["t"], txt, y, guidance)
+            F.flux_euler_step(Bs, n, o["v_pred"], o["z"], ts[i], ts[i + 1], cfg=cfg,
+                              guidance=cfg_w if cfg else 1.0, z_model=o["z_t"], copies=2 if cfg else 1,
+                              t_model=o["t"], t_model_n=Bm)
         return o

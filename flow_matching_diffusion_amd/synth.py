@@ -213,9 +213,10 @@ def single_seq_block_weights(wl: Workload, blk: int) -> Dict[str, np.ndarray]:
     return {k[len("seq_"):]: v for k, v in w.items()}
 
 
-def embed_weights(wl: Workload) -> Dict[str, np.ndarray]:
+def embed_weights(wl: Workload, guidance: bool = False) -> Dict[str, np.ndarray]:
     """img_in [D, C]; txt_in [D, context] (if any); time_in 256->D->D;
-    vector_in vec_in->D->D (if any); final mod [2D, D] (shift, scale); out [C, D]."""
+    vector_in vec_in->D->D (if any); guidance_in [D, 1] (guidance=True);
+    final mod [2D, D] (shift, scale); out [C, D]."""
     D, bf, blk = wl.hidden, operands_bf16(wl), 1000
     w: Dict[str, np.ndarray] = {}
     w.update(_lin(wl, blk, "img_in", D, wl.latent_ch, bf))
@@ -226,9 +227,35 @@ def embed_weights(wl: Workload) -> Dict[str, np.ndarray]:
     if wl.vec_in_dim is not None:
         w.update(_lin(wl, blk, "vector_in1", D, wl.vec_in_dim, bf))
         w.update(_lin(wl, blk, "vector_in2", D, D, bf))
+    if guidance:
+        w.update(_lin(wl, blk, "guidance_in", D, 1, bf))
     w.update(_lin(wl, blk, "final_mod", 2 * D, D, bf))
     w.update(_lin(wl, blk, "final_out", wl.latent_ch, D, bf))
     return w
+
+
+def sampler_inputs(wl: Workload, n_images: int) -> Dict[str, np.ndarray]:
+    """Inputs of classifier-free-guided sampling of n_images images with a
+    model of batch 2 * n_images: noise z1 [n, C, H, W] N(0,1); the
+    conditional text / pooled vector rows, then the null-prompt rows (the
+    embeddings an empty prompt would give, drawn as their own N(0,1) tensors;
+    no text encoder is part of the path); guidance values [2n] for the
+    guidance embedding; joint position ids [2n, L, 3]."""
+    C, bf = wl.latent_ch, operands_bf16(wl)
+    width = wl.context_dim if wl.context_dim is not None else wl.hidden
+    n = n_images
+    d = {"z1": normal((n, C, wl.img_h, wl.img_w), 1.0, wl.config_id, 0, "sample_z1", False)}
+    txt_c = normal((n, wl.l_txt, width), 1.0, wl.config_id, 0, "sample_txt", bf)
+    txt_u = normal((n, wl.l_txt, width), 1.0, wl.config_id, 0, "sample_txt_null", bf)
+    d["txt"] = np.concatenate([txt_c, txt_u], axis=0)
+    if wl.vec_in_dim is not None:
+        y_c = normal((n, wl.vec_in_dim), 1.0, wl.config_id, 0, "sample_y", False)
+        y_u = normal((n, wl.vec_in_dim), 1.0, wl.config_id, 0, "sample_y_null", False)
+        d["y"] = np.concatenate([y_c, y_u], axis=0)
+    d["guidance"] = np.full(2 * n, 3.5, dtype=np.float32)
+    ids = joint_ids(wl)
+    d["ids"] = np.repeat(ids[:1], 2 * n, axis=0)
+    return d
 
 
 # --------------------------------------------------------------------------- #

@@ -259,6 +259,43 @@ typedef struct {
 flux_status rf_noise_loss(const rf_args* args, void* stream);
 
 /*
+ * flux_euler_step -- one step of the Euler sampler with optional
+ * classifier-free guidance ("Flux architecture deep dive", Sampling
+ * (inference) / Euler integration and Classifier-free guidance).
+ *
+ *  g = v_uncond + guidance * (v_cond - v_uncond)   when cfg != 0,
+ *  g = v                                           otherwise;
+ *  z <- z - (t_cur - t_next) * g.
+ * Every operation is one rounded fp32 operation in the order written (d =
+ * v_c - v_u; w*d; v_u + w*d; dt = t_cur - t_next; dt*g; z - dt*g), so the
+ * result is bit-reproducible.
+ *
+ *  v        model velocity: [B, n] (cfg == 0) or [2B, n] (cfg != 0: rows
+ *           0..B-1 from the conditional, rows B..2B-1 from the unconditional
+ *           evaluation of one batched forward).
+ *  z        [B, n] current sample, updated in place.
+ *  z_model  nullable [copies*B, n]: the next forward's input, z written into
+ *           each of its `copies` batch-halves (copies 1 or 2).
+ *  t_model  nullable [t_model_n]: the next forward's timesteps, set to t_next.
+ * z and z_model must not overlap v or each other.
+ */
+typedef struct {
+  int32_t batch;              /* B >= 1 samples */
+  int64_t n_per_sample;       /* C*H*W >= 1 */
+  const float* v;
+  int32_t cfg;
+  float guidance;             /* w */
+  float t_cur, t_next;
+  float* z;
+  float* z_model;
+  int32_t copies;
+  float* t_model;
+  int32_t t_model_n;
+} flux_euler_args;
+
+flux_status flux_euler_step(const flux_euler_args* args, void* stream);
+
+/*
  * flux_rope_table -- 3D RoPE angles ("Flux architecture deep dive", 3D RoPE
  * mathematics; "Flux model API reference", EmbedND with rotary_interleaved).
  * For token position ids (p0, p1, p2) and axis a of width d_a (axes in order,
@@ -276,9 +313,12 @@ flux_status flux_rope_table(const float* ids, int32_t batch, int32_t seq, const 
  * details / Memory layout):
  *   x_img = Linear_img_in(patchify(z_t)), patchify [B,C,H,W] -> [B,H*W,C];
  *   x_txt = Linear_txt_in(txt) if txt_in_w is not NULL, else not written;
- *   vec   = Linear(SiLU(Linear(sinusoid(t)))) [+ Linear(SiLU(Linear(y)))],
+ *   vec   = Linear(SiLU(Linear(sinusoid(t)))) [+ Linear(SiLU(Linear(y)))]
+ *           [+ Linear_guidance(g)],
  *   sinusoid(t) = [cos(1000 t f_j) | sin(1000 t f_j)], f_j = 1e4^(-j/half),
- *   j < half = time_dim/2.
+ *   j < half = time_dim/2.  The guidance term (Conditioning: the optional
+ *   guidance scale g through a Linear 1 -> D) is added when guidance_in_w is
+ *   not NULL; `guidance` is then [B] float.
  * Element type of the weights and of txt follows `precision`.
  */
 typedef struct {
@@ -288,12 +328,13 @@ typedef struct {
   const void* time_in2_w; const void* time_in2_b;  /* [D, D], [D] */
   const void* vector_in1_w; const void* vector_in1_b;  /* [D, y_dim], [D] or NULL */
   const void* vector_in2_w; const void* vector_in2_b;  /* [D, D], [D] or NULL */
+  const void* guidance_in_w; const void* guidance_in_b; /* [D, 1], [D] or NULL */
 } flux_embed_weights;
 
 flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
                            int32_t l_txt, int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
                            const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
-                           const float* y, float* x_img, int64_t img_bstride, float* x_txt,
+                           const float* y, const float* guidance, float* x_img, int64_t img_bstride, float* x_txt,
                            int64_t txt_bstride, float* vec, void* workspace, size_t workspace_bytes,
                            void* stream);
 

@@ -35,7 +35,8 @@ __all__ = [
     "timestep_embedding", "silu", "gelu", "linear", "layernorm", "modulate",
     "rmsnorm", "adaln", "rope_angles", "apply_rope", "attention_probs",
     "attention", "double_block", "single_block", "single_block_sequential", "final_layer",
-    "conditioning_vector", "patchify", "unpatchify", "flux_forward",
+    "conditioning_vector", "patchify", "unpatchify", "flux_forward", "euler_timesteps",
+    "cfg_combine", "euler_step", "euler_cfg_step_f32_order", "euler_sample", "flux_sample_cfg",
     "param_count",
 ]
 
@@ -365,14 +366,20 @@ def unpatchify(tok, hh: int, ww: int) -> np.ndarray:
     return tok.transpose(0, 2, 1).reshape(b_, c, hh, ww)
 
 
-def conditioning_vector(t, y, w: Dict[str, np.ndarray], model_channels: int = 256) -> np.ndarray:
-    """vec = time_in(sinusoid(t)) [+ vector_in(y)], each embedder being
-    Linear -> SiLU -> Linear."""
+def conditioning_vector(t, y, w: Dict[str, np.ndarray], model_channels: int = 256,
+                        guidance=None) -> np.ndarray:
+    """vec = time_in(sinusoid(t)) [+ vector_in(y)] [+ guidance_in(g)], the
+    first two embedders being Linear -> SiLU -> Linear.  The guidance scale g
+    (one per sample) goes through one Linear 1 -> D ("Flux architecture deep
+    dive", Conditioning: the optional guidance scale enters the combined
+    vector through a Linear); W "guidance_in.w" [D, 1], b [D]."""
     e = timestep_embedding(t, model_channels)
     vec = linear(silu(linear(e, w["time_in1.w"], w["time_in1.b"])), w["time_in2.w"], w["time_in2.b"])
     if y is not None:
         vec = vec + linear(silu(linear(y, w["vector_in1.w"], w["vector_in1.b"])),
                            w["vector_in2.w"], w["vector_in2.b"])
+    if guidance is not None:
+        vec = vec + linear(f64(guidance).reshape(-1, 1), w["guidance_in.w"], w["guidance_in.b"])
     return vec
 
 
@@ -387,27 +394,108 @@ def final_layer(x_img, vec, w: Dict[str, np.ndarray], hh: int, ww: int, eps: flo
 def flux_forward(z_t, txt, y, t, ids, emb_w: Dict[str, np.ndarray],
                  double_ws: Sequence[Dict[str, np.ndarray]], single_ws: Sequence[Dict[str, np.ndarray]],
                  heads: int, axes_dim: Sequence[int], theta: float, eps: float = 1e-6,
-                 model_channels: int = 256, taps: Optional[dict] = None) -> np.ndarray:
+                 model_channels: int = 256, taps: Optional[dict] = None, guidance=None) -> np.ndarray:
     """Whole forward ("Flux architecture deep dive", Data flow / Complete
     forward pass): image tokens = Linear(patchify(z_t)); text tokens =
-    Linear(txt) when a txt_in projection exists, else txt as given; vec;
-    double blocks; concatenation image|text; single blocks; image rows ->
-    final layer -> velocity [B, C, H, W]."""
+    Linear(txt) when a txt_in projection exists, else txt as given; vec
+    (with the guidance embedding when guidance is given); double blocks;
+    concatenation image|text; single blocks (the sequential form when a
+    block's weights hold "qkv.w"); image rows -> final layer -> velocity
+    [B, C, H, W]."""
     z_t = f64(z_t)
     _, _, hh, ww = z_t.shape
     x_img = linear(patchify(z_t), emb_w["img_in.w"], emb_w["img_in.b"])
     x_txt = linear(txt, emb_w["txt_in.w"], emb_w["txt_in.b"]) if "txt_in.w" in emb_w else f64(txt)
-    vec = conditioning_vector(t, y, emb_w, model_channels)
+    vec = conditioning_vector(t, y, emb_w, model_channels, guidance)
     angles = rope_angles(ids, axes_dim, theta)
     for w in double_ws:
         x_img, x_txt = double_block(x_img, x_txt, vec, angles, w, heads, eps)
     x = np.concatenate([x_img, x_txt], axis=1)
     for w in single_ws:
-        x = single_block(x, vec, angles, w, heads, eps)
+        if "qkv.w" in w:
+            x = single_block_sequential(x, vec, angles, w, heads, eps)
+        else:
+            x = single_block(x, vec, angles, w, heads, eps)
     if taps is not None:
         taps["vec"] = vec
         taps["x_final"] = x
     return final_layer(x[:, :x_img.shape[1]], vec, emb_w, hh, ww, eps)
+
+
+# --------------------------------------------------------------------------- #
+# Sampling ("Flux architecture deep dive", Sampling (inference) / Euler
+# integration and Classifier-free guidance)
+# --------------------------------------------------------------------------- #
+def euler_timesteps(n_steps: int) -> np.ndarray:
+    """The uniform grid from t = 1 (noise) down to t = 0: n_steps + 1 points
+    1 - i / n_steps.  Step i evaluates the velocity at grid point i and moves
+    to grid point i + 1 (reading: the page's loop over 1.0, 0.9, ..., 0.0
+    names the grid, its last point being where integration ends)."""
+    return 1.0 - np.arange(n_steps + 1, dtype=np.float64) / n_steps
+
+
+def cfg_combine(v_cond, v_uncond, w: float) -> np.ndarray:
+    """Classifier-free guidance: v_uncond + w (v_cond - v_uncond)."""
+    vc, vu = f64(v_cond), f64(v_uncond)
+    return vu + w * (vc - vu)
+
+
+def euler_step(z, v, t_cur: float, t_next: float) -> np.ndarray:
+    """One Euler step of dz/dt = v from t_cur down to t_next:
+    z - (t_cur - t_next) v."""
+    return f64(z) - (t_cur - t_next) * f64(v)
+
+
+def euler_cfg_step_f32_order(z, v_cond, v_uncond, w, t_cur, t_next) -> np.ndarray:
+    """The CFG combination and the Euler step evaluated in float32 in one fixed
+    order, each operation rounded: d = v_c - v_u; g = v_u + w d (product then
+    sum); dt = t_cur - t_next; z - dt g (product then difference).  With
+    v_uncond None the combination is skipped (g = v_cond).  This order is the
+    reading used for the bit-exact comparison."""
+    f = np.float32
+    z = np.asarray(z, dtype=f)
+    vc = np.asarray(v_cond, dtype=f)
+    if v_uncond is None:
+        g = vc
+    else:
+        vu = np.asarray(v_uncond, dtype=f)
+        d = (vc - vu).astype(f)
+        g = (vu + (f(w) * d).astype(f)).astype(f)
+    dt = f(f(t_cur) - f(t_next))
+    return (z - (dt * g).astype(f)).astype(f)
+
+
+def euler_sample(z1, n_steps: int, velocity) -> np.ndarray:
+    """Integrate from noise z1 at t = 1 to t = 0 with n_steps Euler steps on
+    the uniform grid; velocity(z, t) returns the model's velocity at (z, t)."""
+    ts = euler_timesteps(n_steps)
+    z = f64(z1)
+    for i in range(n_steps):
+        z = euler_step(z, velocity(z, ts[i]), ts[i], ts[i + 1])
+    return z
+
+
+def flux_sample_cfg(z1, n_steps: int, guidance_w: float, cond: dict, uncond: Optional[dict], ids,
+                    emb_w: Dict[str, np.ndarray], double_ws, single_ws, heads: int, axes_dim, theta: float,
+                    eps: float = 1e-6, model_channels: int = 256, guidance=None) -> np.ndarray:
+    """Euler sampling of the Flux velocity model with classifier-free guidance:
+    at each step v = v_uncond + w (v_cond - v_uncond), v_cond from the
+    conditioning cond = {"txt", "y"} and v_uncond from the null conditioning
+    uncond (None: no guidance, v = v_cond).  guidance: optional [B] values
+    for the guidance embedding (passed to both evaluations)."""
+    B = f64(z1).shape[0]
+
+    def velocity(z, t):
+        tb = np.full(B, t)
+        vc = flux_forward(z, cond["txt"], cond.get("y"), tb, ids, emb_w, double_ws, single_ws, heads, axes_dim,
+                          theta, eps, model_channels, guidance=guidance)
+        if uncond is None:
+            return vc
+        vu = flux_forward(z, uncond["txt"], uncond.get("y"), tb, ids, emb_w, double_ws, single_ws, heads,
+                          axes_dim, theta, eps, model_channels, guidance=guidance)
+        return cfg_combine(vc, vu, guidance_w)
+
+    return euler_sample(z1, n_steps, velocity)
 
 
 # --------------------------------------------------------------------------- #

@@ -477,3 +477,92 @@ def test_flux_forward_composition():
     # unpatchify is the inverse of patchify with token index h*W + w
     np.testing.assert_array_equal(O.unpatchify(O.patchify(zt), wl.img_h, wl.img_w), zt)
     assert O.patchify(zt)[0, 1 * wl.img_w + 2, 3] == zt[0, 3, 1, 2]
+
+
+# --------------------------------------------------------------------------- #
+# Sampling ("Flux architecture deep dive", Sampling (inference) / Euler
+# integration and Classifier-free guidance; Conditioning: guidance scale)
+# --------------------------------------------------------------------------- #
+def test_cfg_combine_special_cases():
+    vc, vu = RNG.standard_normal((2, 3, 4)), RNG.standard_normal((2, 3, 4))
+    assert np.array_equal(O.cfg_combine(vc, vu, 0.0), vu)
+    np.testing.assert_allclose(O.cfg_combine(vc, vu, 1.0), vc, atol=1e-15)
+    np.testing.assert_allclose(O.cfg_combine(vc, vc, 3.5), vc, atol=1e-15)
+    # affine in w: g(w) = vu + w (vc - vu)
+    g2, g5 = O.cfg_combine(vc, vu, 2.0), O.cfg_combine(vc, vu, 5.0)
+    np.testing.assert_allclose((g5 - g2) / 3.0, vc - vu, atol=1e-14)
+
+
+def test_euler_grid():
+    ts = O.euler_timesteps(10)
+    assert ts[0] == 1.0 and ts[-1] == 0.0 and len(ts) == 11
+    np.testing.assert_allclose(np.diff(ts), -0.1, atol=1e-15)
+
+
+@pytest.mark.parametrize("n_steps", [1, 3, 7])
+def test_euler_integrates_the_straight_path_exactly(n_steps):
+    # rectified flow's path z_t = (1 - t) z0 + t z1 has the constant velocity
+    # z1 - z0, which Euler integrates exactly: from z1 at t = 1 it lands on z0
+    z0, z1 = RNG.standard_normal((2, 4, 3, 3)), RNG.standard_normal((2, 4, 3, 3))
+    out = O.euler_sample(z1, n_steps, lambda z, t: z1 - z0)
+    np.testing.assert_allclose(out, z0, atol=1e-12)
+    # and every intermediate state is on the path: check one step from t = 1
+    zt, _ = O.rf_noise(z0, z1, np.full(2, O.euler_timesteps(n_steps)[1]))
+    np.testing.assert_allclose(O.euler_step(z1, z1 - z0, 1.0, O.euler_timesteps(n_steps)[1]), zt, atol=1e-13)
+
+
+def test_euler_linear_ode_closed_form_and_first_order():
+    # dz/dt = lam z from t = 1 to 0: exact z1 e^(-lam); Euler multiplies by
+    # (1 - lam dt) per step, and its error halves when the steps double
+    lam, z1 = 0.8, RNG.standard_normal(5)
+    for n in (4, 8):
+        got = O.euler_sample(z1, n, lambda z, t: lam * z)
+        np.testing.assert_allclose(got, z1 * (1.0 - lam / n) ** n, rtol=1e-13)
+    e4 = np.abs(O.euler_sample(z1, 64, lambda z, t: lam * z) - z1 * np.exp(-lam)).max()
+    e8 = np.abs(O.euler_sample(z1, 128, lambda z, t: lam * z) - z1 * np.exp(-lam)).max()
+    assert 1.8 < e4 / e8 < 2.2
+
+
+def test_euler_cfg_f32_order():
+    z = RNG.standard_normal(1000).astype(np.float32)
+    vc = RNG.standard_normal(1000).astype(np.float32)
+    vu = RNG.standard_normal(1000).astype(np.float32)
+    got = O.euler_cfg_step_f32_order(z, vc, vu, 3.5, 0.75, 0.5)
+    ref = O.euler_step(z, O.cfg_combine(vc, vu, 3.5), 0.75, 0.5)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=4e-6 * np.abs(ref).max())
+    assert got.dtype == np.float32
+    # dt = 0 leaves z bit-identical; no guidance uses v_cond as is
+    assert np.array_equal(O.euler_cfg_step_f32_order(z, vc, vu, 3.5, 0.5, 0.5), z)
+    np.testing.assert_array_equal(O.euler_cfg_step_f32_order(z, vc, None, 7.0, 1.0, 0.0), (z - vc).astype(np.float32))
+    # v_uncond == v_cond: guidance changes nothing, bit for bit
+    assert np.array_equal(O.euler_cfg_step_f32_order(z, vc, vc, 3.5, 0.75, 0.5),
+                          O.euler_cfg_step_f32_order(z, vc, None, 1.0, 0.75, 0.5))
+
+
+def test_guidance_embedding_is_one_linear_of_g():
+    wl = _tiny_wl()
+    w = synth.embed_weights(wl, guidance=True)
+    t = np.array([0.3, 0.8])
+    g = np.array([3.5, 1.25])
+    base = O.conditioning_vector(t, None, w)
+    got = O.conditioning_vector(t, None, w, guidance=g) - base
+    for b in range(2):
+        ref = BF.vec_linear([float(g[b])], w["guidance_in.w"].astype(np.float64).tolist(),
+                            w["guidance_in.b"].astype(np.float64).tolist())
+        np.testing.assert_allclose(got[b], ref, atol=1e-12)
+
+
+def test_sampler_with_unit_guidance_equals_unguided_sampling():
+    wl = _tiny_wl(batch=1)
+    emb = synth.embed_weights(wl, guidance=True)
+    w2, w1 = synth.double_block_weights(wl, 0), synth.single_block_weights(wl, 1)
+    si = synth.sampler_inputs(wl, 1)
+    cond = {"txt": si["txt"][:1]}
+    uncond = {"txt": si["txt"][1:]}
+    ids = si["ids"][:1]
+    args = (emb, [w2], [w1], wl.heads, wl.axes_dim, wl.theta, wl.eps, wl.model_channels)
+    a = O.flux_sample_cfg(si["z1"], 3, 1.0, cond, uncond, ids, *args, guidance=si["guidance"][:1])
+    b = O.flux_sample_cfg(si["z1"], 3, 1.0, cond, None, ids, *args, guidance=si["guidance"][:1])
+    np.testing.assert_allclose(a, b, atol=1e-12)
+    c = O.flux_sample_cfg(si["z1"], 3, 4.0, cond, uncond, ids, *args, guidance=si["guidance"][:1])
+    assert np.abs(c - b).max() > 1e-4       # guidance moves the sample (small weights: a small move)
