@@ -444,29 +444,33 @@ __device__ __forceinline__ void stage_quarter(const f32x16_t (&acc)[4][4], float
     for (int e = 0; e < 16; ++e) cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[Q >> 1][2 * (Q & 1) + jj][e];
 }
 
+// The residual rows (kEpiResid) of the lane's 8 rows rbase + 4u and four
+// columns col..col+3 of a quarter, all loads issued together.
+__device__ __forceinline__ void load_resid(const GemmProblem& pc, int rbase, int col, float4 (&xr)[8]) {
+  const int seg = pc.omap0.seg;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = rbase + 4 * u;
+    xr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < pc.M && col < pc.N) {
+      const int64_t b = row / seg, l = row % seg;
+      xr[u] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(pc.out0) + b * pc.omap0.bstride +
+                                               l * pc.omap0.ld + col);
+    }
+  }
+}
+
 // The fused epilogue of one staged quarter (32 rows x 64 columns, read from
 // the wave's LDS staging cs) for the lane's 8 rows rbase + 4u and four
-// columns col..col+3, whose bias bq and gate gq come in as values.  All
-// residual rows are loaded before any is updated, so their latencies overlap.
+// columns col..col+3, whose bias bq and gate gq come in as values; xr holds
+// the residual rows for kEpiResid (loaded a quarter ahead by the caller, so
+// their latency overlaps the previous quarter).
 template <int EPI>
 __device__ __forceinline__ void apply_quarter(const GemmProblem& pc, const float* cs, int lrow, int c4, int rbase,
                                               int col, float4 bq, float4 gq, bool uniform, float dq, float qs,
-                                              uint32_t& mx) {
+                                              uint32_t& mx, const float4 (&xr)[8]) {
   const int seg = pc.omap0.seg;
   const bool col_ok = col < pc.N;
-  float4 xr[8];
-  if constexpr (EPI == kEpiResid) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int row = rbase + 4 * u;
-      xr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row < pc.M && col_ok) {
-        const int64_t b = row / seg, l = row % seg;
-        xr[u] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(pc.out0) + b * pc.omap0.bstride +
-                                                 l * pc.omap0.ld + col);
-      }
-    }
-  }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int row = rbase + 4 * u;
@@ -537,9 +541,14 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
       gate1 = *reinterpret_cast<const float4*>(pc.gate + b0 * pc.gate_bstride + cB);
     }
   }
-  // quarters 2qq (columns 0..63 of the wave) and 2qq + 1 (columns 64..127)
+  // quarters 2qq (columns 0..63 of the wave) and 2qq + 1 (columns 64..127);
+  // residual rows are loaded one quarter ahead (xa for the first column half,
+  // xb for the second)
+  float4 xa[8], xb[8];
+  if constexpr (EPI == kEpiResid) load_resid(pc, row0 + lrow, col0 + c4, xa);
 #pragma unroll 1
   for (int qq = 0; qq < 4; ++qq) {
+    if constexpr (EPI == kEpiResid) load_resid(pc, row0 + qq * 32 + lrow, col0 + 64 + c4, xb);
     switch (qq) {
       case 0: stage_quarter<0>(acc, cs, frow, fhalf); break;
       case 1: stage_quarter<2>(acc, cs, frow, fhalf); break;
@@ -548,9 +557,12 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
     __builtin_amdgcn_sched_barrier(0);
-    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + c4, bias0, gate0, uniform, dq, qs, mx);
+    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + c4, bias0, gate0, uniform, dq, qs, mx, xa);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next quarter overwrites the staging
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EPI == kEpiResid) {
+      if (qq < 3) load_resid(pc, row0 + (qq + 1) * 32 + lrow, col0 + c4, xa);
+    }
     switch (qq) {
       case 0: stage_quarter<1>(acc, cs, frow, fhalf); break;
       case 1: stage_quarter<3>(acc, cs, frow, fhalf); break;
@@ -559,7 +571,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
-    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + 64 + c4, bias1, gate1, uniform, dq, qs, mx);
+    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + 64 + c4, bias1, gate1, uniform, dq, qs, mx,
+                       xb);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
   }
