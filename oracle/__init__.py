@@ -13,7 +13,8 @@ an exp, an erf are library primitives), following the Flux pages:
   * "Flux model API reference" -- FluxConfig key parameters, AdaLN, RMSNorm,
     EmbedND, apply_flow_matching_noise, compute_flow_matching_loss.
   * "FP8 training for Flux models" -- Configuration (E4M3, delayed scaling),
-    in fp8_oracle.
+    in fp8_oracle; the "mxfp8" recipe (block-scaled E4M3 in the OCP MX
+    format) in mx_oracle.
 Where the pages leave a step open the oracle takes one stated reading; the
 readings are listed in the design notes and repeated next to the code.
 
@@ -23,3 +24,4 @@ a pure-Python brute force on tiny inputs).
 """
 from .flux_oracle import *  # noqa: F401,F403
 from . import fp8_oracle  # noqa: F401
+from . import mx_oracle  # noqa: F401
