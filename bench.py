@@ -89,7 +89,8 @@ def recorded_traffic(kernel_class):
 KERNEL_CLASSES = {
     "gemm_256_f16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_dl_kernel<[23],"]),
     "gemm_256_bf16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_dl_kernel<1,"]),
-    "gemm_256_fp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8_kernel<"]),
+    "gemm_256_fp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8_kernel<\d+, false>"]),
+    "gemm_256_mxfp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8_kernel<\d+, true>"]),
     "gemm_128x128": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_mfma_kernel<"]),
     "attention": ("flow_matching_diffusion_amd/csrc/attention.hip", [r"attn_(bf16|f32)_kernel"]),
     "ln_modulate": ("flow_matching_diffusion_amd/csrc/rowwise.hip", [r"ln_mod_kernel"]),
@@ -246,6 +247,84 @@ def cpu_baseline(wl, w2, inp, ids, work):
             "seconds": round(dt, 2)}
 
 
+def mx_linears_bench(args) -> int:
+    """The six token-path linears of the Flux-12B block pair at batch 4
+    (qkv, proj, fc1, fc2 over the joint 4608-token rows of 4 samples; lin1,
+    lin2 of the single block) as MXFP8 linears: per step, every input is
+    quantized to MXFP8 (flux_mx_quantize, bf16 source) and multiplied with its
+    MXFP8 weight (flux_mxfp8_linear_fwd).  Weights are quantized once, before
+    timing (static)."""
+    import numpy as np
+    import torch
+
+    from flow_matching_diffusion_amd import flux as FX
+
+    torch.cuda.set_device(0)
+    FX.lib()
+    B, L, D, F = 4, 4608, 3072, 12288
+    M = B * L
+    shapes = [("qkv", D, 3 * D), ("proj", D, D), ("fc1", D, F), ("fc2", F, D), ("lin1", D, 3 * D + F),
+              ("lin2", D + F, D)]
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    ops = []
+    for name, K, N in shapes:
+        x = (torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
+        w = (torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((FX.flux_mx_scale_bytes(M, K),), dtype=torch.uint8, device="cuda")
+        wq = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+        ws = torch.empty((FX.flux_mx_scale_bytes(N, K),), dtype=torch.uint8, device="cuda")
+        FX.flux_mx_quantize(FX.FLUX_PREC_BF16, w, N, K, wq, ws)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ops.append((name, K, N, x, xq, xs, wq, ws, y))
+        del w
+    torch.cuda.synchronize()
+
+    def step():
+        for name, K, N, x, xq, xs, wq, ws, y in ops:
+            FX.flux_mx_quantize(FX.FLUX_PREC_BF16, x, M, K, xq, xs)
+            FX.flux_mxfp8_linear_fwd(M, N, K, xq, xs, wq, ws, None, y, N)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    FX.flux_timing_read()
+    FX.flux_timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    FX.flux_timing_enable(False)
+    kernels = FX.flux_timing_read()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    flops = sum(2.0 * M * N * K for _, K, N, *_ in ops)
+    gms, gn, gw = kernels["gemm_256_mxfp8"]
+    qms, qn, qw = kernels["mx_quantize"]
+    assert abs(gw / args.steps - flops) <= 1e-6 * flops
+    tflops = gw / (gms * 1e-3) / 1e12
+    assert bool(torch.isfinite(ops[-1][-1]).all())
+    rec = {
+        "metric": "MXFP8 block-linear TFLOP/s (the six token-path linears of the Flux-12B block pair, batch 4, "
+                  "inputs quantized every step)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8_e4m3 (E8M0 scale per 32 values along K)", "data": "synthetic",
+        "config": {"workload": "flux12b_block_pair_mxfp8_linears", "rows": M, "hidden": D, "mlp_hidden": F,
+                   "linears": [n for n, *_ in shapes]},
+        "roofline": {"kernel": "gemm_256_mxfp8", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": gw / gn, "ms_per_launch": round(gms / gn, 5)},
+        "kernels": {"gemm_256_mxfp8": {"ms_per_launch": round(gms / gn, 5), "tflops": round(tflops, 2)},
+                    "mx_quantize": {"ms_per_launch": round(qms / qn, 5),
+                                    "gbs": round(qw / (qms * 1e-3) / 1e9, 1)}},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,7 +333,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="flux12b_blocks",
                     choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8", "flux12b_blocks_seq",
-                             "flux12b_sample_cfg"],
+                             "flux12b_sample_cfg", "flux12b_mxfp8_linears"],
                     help="flux12b_blocks (default): the block-pair step the headline metric is quoted on; "
                          "flux12b_full: the whole 19 + 38 block forward + loss at batch 2 (block weights "
                          "drawn on the device; no CPU baseline); flux12b_blocks_fp8: the block pair at batch 4 "
@@ -262,7 +341,8 @@ def main() -> int:
                          "flux12b_blocks_seq: the block pair with the single block in its sequential form "
                          "(flux_single_seq_fwd); flux12b_sample_cfg: Euler sampling steps of one image with "
                          "classifier-free guidance (conditional + null-prompt rows in one batch-2 forward, "
-                         "guidance embedding on) on the block-pair model")
+                         "guidance embedding on) on the block-pair model; flux12b_mxfp8_linears: the six "
+                         "token-path linears of the block pair at batch 4 as MXFP8 linears")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -283,6 +363,8 @@ def main() -> int:
     import numpy as np
     import torch
 
+    if args.workload == "flux12b_mxfp8_linears":
+        return mx_linears_bench(args)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

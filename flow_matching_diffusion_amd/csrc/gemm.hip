@@ -780,7 +780,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 template <int S> using SetTag = std::integral_constant<int, S>;
 
-template <int EPI>
+template <int EPI, bool MX>
 __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
   constexpr int BK8 = 64;   // k values (bytes) per stage row
@@ -804,7 +804,17 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   }
 
   int prob = 0, m0 = 0, n0 = 0, KT = 0;
-  const char* src[8];
+  // operand rows as 32-bit byte offsets from the (wave-uniform) A and W bases
+  const char* abase = nullptr;
+  const char* wbase = nullptr;
+  uint32_t src[8];
+  // MX: the lane's scale dwords of step kt at sca + kt * 256 (A rows of the
+  // wave) and scb + kt * 256 (W rows), loaded two steps ahead of use: cur
+  // holds step kt's, nxt step kt + 1's
+  const uint8_t* sca = nullptr;   // wave-uniform: lane offset sc_lane added at the load
+  const uint8_t* scb = nullptr;
+  const int sc_lane = fhalf * 128 + frow * 4;
+  uint32_t cur_a = 0u, cur_b = 0u, nxt_a = 0u, nxt_b = 0u;
   auto setup = [&](int t) {
     const TileCoord tc = decode_tile_id(bt, t, BM, BN);
     GemmProblem p = bt.p[0];
@@ -813,8 +823,12 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
     m0 = tc.tm * BM;
     n0 = tc.tn * BN;
     KT = p.K / BK8;
-    const char* A = reinterpret_cast<const char*>(p.A);
-    const char* W = reinterpret_cast<const char*>(p.W);
+    if constexpr (MX) {
+      sca = p.sa + (size_t)(m0 / 128 + wm) * KT * 256;
+      scb = p.sb + (size_t)(n0 / 128 + wn) * KT * 256;
+    }
+    abase = reinterpret_cast<const char*>(p.A);
+    wbase = reinterpret_cast<const char*>(p.W);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int ins = wave + 4 * u;
@@ -823,11 +837,12 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
       if (ins < 16) {
         int gr = m0 + r;
         gr = gr < p.M ? gr : p.M - 1;
-        src[u] = A + (int64_t)(gr / p.amap.seg) * p.amap.bstride + (int64_t)(gr % p.amap.seg) * p.amap.ld + c * 16;
+        src[u] = (uint32_t)((int64_t)(gr / p.amap.seg) * p.amap.bstride + (int64_t)(gr % p.amap.seg) * p.amap.ld +
+                            c * 16);
       } else {
         int gr = n0 + r;
         gr = gr < p.N ? gr : p.N - 1;
-        src[u] = W + (int64_t)gr * p.ldw + c * 16;
+        src[u] = (uint32_t)((int64_t)gr * p.ldw + c * 16);
       }
     }
   };
@@ -836,13 +851,22 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int ins = wave + 4 * u;
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[u] + (int64_t)kt * BK8),
-                                       (lds_void_t*)(st + ins * 1024), 16, 0, 0);
+      const char* g = (ins < 16 ? abase : wbase) + (int64_t)kt * BK8 + src[u];
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)(st + ins * 1024), 16, 0, 0);
     }
+  };
+  auto ld_scale = [&](int kk, uint32_t& a, uint32_t& b) {
+    const int kc = kk < KT ? kk : KT - 1;
+    a = *reinterpret_cast<const uint32_t*>(sca + (size_t)kc * 256 + sc_lane);
+    b = *reinterpret_cast<const uint32_t*>(scb + (size_t)kc * 256 + sc_lane);
   };
   auto prologue_issue = [&]() {
     const int pre = KT < 4 ? KT : 4;
     for (int t = 0; t < pre; ++t) issue(t);
+    if constexpr (MX) {
+      ld_scale(0, cur_a, cur_b);
+      ld_scale(1, nxt_a, nxt_b);
+    }
   };
 
   f32x16_t acc[TM][TN];
@@ -859,29 +883,53 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) fb[S][j][kk] = *reinterpret_cast<const u32x4_t*>(st + boff[j][kk]);
   };
+  // MFMA (i, j) of a step; MX: the scale of A fragment i is byte i of the
+  // lane's A dword, that of W fragment j byte j of its W dword (E8M0, one per
+  // lane's row and 32-value half of the step)
+  auto mma_ij = [&](auto set, auto ic, auto jc, uint32_t sa_w, uint32_t sb_w) {
+    constexpr int S = decltype(set)::value, i = decltype(ic)::value, j = decltype(jc)::value;
+    const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[S][j][0], fb[S][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[S][i][0], fa[S][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    if constexpr (MX)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, i, (int)sa_w, j, (int)sb_w);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
   auto mma = [&](auto set) {
-    constexpr int S = decltype(set)::value;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[S][j][0], fb[S][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[S][i][0], fa[S][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
-      }
-    }
+    const uint32_t sa_w = cur_a, sb_w = cur_b;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    mma_ij(set, I0{}, I0{}, sa_w, sb_w); mma_ij(set, I1{}, I0{}, sa_w, sb_w);
+    mma_ij(set, I2{}, I0{}, sa_w, sb_w); mma_ij(set, I3{}, I0{}, sa_w, sb_w);
+    mma_ij(set, I0{}, I1{}, sa_w, sb_w); mma_ij(set, I1{}, I1{}, sa_w, sb_w);
+    mma_ij(set, I2{}, I1{}, sa_w, sb_w); mma_ij(set, I3{}, I1{}, sa_w, sb_w);
+    mma_ij(set, I0{}, I2{}, sa_w, sb_w); mma_ij(set, I1{}, I2{}, sa_w, sb_w);
+    mma_ij(set, I2{}, I2{}, sa_w, sb_w); mma_ij(set, I3{}, I2{}, sa_w, sb_w);
+    mma_ij(set, I0{}, I3{}, sa_w, sb_w); mma_ij(set, I1{}, I3{}, sa_w, sb_w);
+    mma_ij(set, I2{}, I3{}, sa_w, sb_w); mma_ij(set, I3{}, I3{}, sa_w, sb_w);
   };
   // Stage kt's fragments are in set S.  Wait until stage kt+1 has landed for
   // every wave (VM: loads allowed to stay outstanding, i.e. those of the
   // stages issued beyond kt+1), refill the stage freed two steps ago with
   // kt+4, read stage kt+1 into the other set while the MFMAs of stage kt run.
   // All flags are compile-time so the k loop carries no branches.
+  // MX steps also load the scales of step kt + 2 right after the barrier, so
+  // two scale dwords join each step's loads: the VM allowances grow from 16 /
+  // 8 to 20 / 12 (loads issued after the stage being waited for).
   auto body = [&](int kt, auto set, auto vm, auto next, auto refill) {
     constexpr int S = decltype(set)::value;
+    uint32_t nn_a = 0u, nn_b = 0u;
     if constexpr (decltype(next)::value) {
       constexpr int VM = decltype(vm)::value;
-      if constexpr (VM == 16) DL_WAIT_VM(16); else if constexpr (VM == 8) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+      if constexpr (MX) {
+        if constexpr (VM == 16) DL_WAIT_VM(20); else if constexpr (VM == 8) DL_WAIT_VM(12); else DL_WAIT_VM(0);
+      } else {
+        if constexpr (VM == 16) DL_WAIT_VM(16); else if constexpr (VM == 8) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+      }
       __syncthreads();
+      if constexpr (MX) ld_scale(kt + 2, nn_a, nn_b);
       if constexpr (decltype(refill)::value) issue(kt + 4);
       lfrag(kt + 1, SetTag<1 - S>{});
       mma(SetTag<S>{});
@@ -894,6 +942,12 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     } else {
       mma(SetTag<S>{});
+    }
+    if constexpr (MX) {
+      cur_a = nxt_a;
+      cur_b = nxt_b;
+      nxt_a = nn_a;
+      nxt_b = nn_b;
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -920,7 +974,9 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     {
       const int pre = KT < 4 ? KT : 4;   // stages of this tile already issued
-      if (pre == 4) DL_WAIT_VM(24); else if (pre == 3) DL_WAIT_VM(16); else if (pre == 2) DL_WAIT_VM(8); else DL_WAIT_VM(0);
+      // (MX: the two scale loads of the prologue came after its stages)
+      if (MX && pre == 4) DL_WAIT_VM(28);
+      else if (pre == 4) DL_WAIT_VM(24); else if (pre == 3) DL_WAIT_VM(16); else if (pre == 2) DL_WAIT_VM(8); else DL_WAIT_VM(0);
     }
     __syncthreads();
     lfrag(0, SetTag<0>{});
@@ -1067,10 +1123,20 @@ static double gemm_flops(const GemmBatch& bt) {
   return f;
 }
 
+// Operand rows of gemm_fp8_kernel are 32-bit byte offsets from A and W.
+static bool fp8_span_ok(const GemmProblem& q) {
+  const int64_t last = q.M - 1;
+  const int64_t a_span = (last / q.amap.seg) * q.amap.bstride + (last % q.amap.seg) * q.amap.ld + q.K;
+  const int64_t w_span = (int64_t)(q.N - 1) * q.ldw + q.K;
+  return a_span < (int64_t(1) << 32) && w_span < (int64_t(1) << 32);
+}
+
 template <int OP, int EPI>
 static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream) {
   if constexpr (OP == kFP8)
-    hipLaunchKernelGGL((gemm_fp8_kernel<EPI>), dim3(grid), dim3(256), 0, stream, big);
+    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, false>), dim3(grid), dim3(256), 0, stream, big);
+  else if constexpr (OP == kMXFP8)
+    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, true>), dim3(grid), dim3(256), 0, stream, big);
   else
     hipLaunchKernelGGL((gemm_dl_kernel<OP, EPI>), dim3(grid), dim3(256), 0, stream, big);
 }
@@ -1084,6 +1150,7 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].omap0.seg >= 32;
   if constexpr (OP == kFP8) {   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
     for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K % 128 == 0 && big.p[i].K >= 256;
+    for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && fp8_span_ok(big.p[i]);
   } else {   // gemm_dl_kernel: k in super-stages of 64; operand rows as 32-bit byte offsets
     for (int i = 0; i < big.count; ++i) {
       const GemmProblem& q = big.p[i];
@@ -1128,8 +1195,28 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   }
 }
 
+// MXFP8: always the persistent kernel (its K loop needs K % 128 == 0, K >= 256, checked
+// by the API), one or two problems sharing the epilogue kind.
+static void launch_mx(GemmBatch bt, hipStream_t stream, double flops) {
+  bt.ksplit = 1;
+  const int tiles = assign_tiles(bt, 256, 256);
+  const int grid = tiles < 256 ? tiles : 256;
+  TimingScope ts(kKcGemmPkMx, stream, flops);
+  switch (bt.p[0].epi) {
+    case kEpiStore: launch_persistent<kMXFP8, kEpiStore>(bt, grid, stream); break;
+    case kEpiGelu: launch_persistent<kMXFP8, kEpiGelu>(bt, grid, stream); break;
+    case kEpiResid: launch_persistent<kMXFP8, kEpiResid>(bt, grid, stream); break;
+    case kEpiStoreF32: launch_persistent<kMXFP8, kEpiStoreF32>(bt, grid, stream); break;
+    default: launch_persistent<kMXFP8, kEpiSplitGelu>(bt, grid, stream); break;
+  }
+}
+
 hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
   const double flops = gemm_flops(bt);
+  if (op == kMXFP8) {
+    launch_mx(bt, stream, flops);
+    return hipGetLastError();
+  }
   if (op == kF32) {
     bt.ksplit = 1;
     const int tiles = assign_tiles(bt, 64, 64);

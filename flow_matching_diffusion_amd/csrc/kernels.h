@@ -18,6 +18,9 @@ constexpr int kF16W = 3;
 // weights on the fp8 MFMA; as an output type, values quantized with the
 // scale of an flux_fp8_tensor record whose amax they raise.
 constexpr int kFP8 = 4;
+// MXFP8 (OCP MX, E4M3 elements): as a GEMM operand type, E4M3 bytes of A and W
+// with one E8M0 scale per 32 values along K, applied by the scaled MFMA.
+constexpr int kMXFP8 = 5;
 
 // ---------------------------------------------------------------------------
 // Row addressing shared by the token-wise kernels.  A logical row r of a
@@ -54,6 +57,8 @@ struct GemmProblem {
   const flux_fp8_tensor* qa;            // kFP8 operands: records A and W were quantized with;
   const flux_fp8_tensor* qw;            //   the accumulator is multiplied by both scale_inv
   flux_fp8_tensor* qo;                  // kFP8 output (out0 of kEpiGelu, out1 of kEpiSplitGelu)
+  const uint8_t* sa;                    // kMXFP8 operands: E8M0 block scales of A and W in the
+  const uint8_t* sb;                    //   GEMM layout of launch_mx_quantize (null otherwise)
   int32_t tile_begin;                   // filled by the launcher
   int32_t tiles_n;                      // filled by the launcher
 };
@@ -152,6 +157,17 @@ hipError_t launch_euler_step(int batch, int64_t n, const float* v, int cfg, floa
 hipError_t launch_guidance_embed(int batch, int dim, const float* g, const void* w, const void* bias, int dtype,
                                  float* vec, hipStream_t stream);
 hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStream_t stream);
+
+// --------------------------------- MXFP8 -----------------------------------
+// Block-scaled E4M3 of rows x k values (k % 64 == 0): codes [rows, k] row-major
+// and one E8M0 byte per 32 values along k, stored for the persistent GEMM:
+// the byte of (row, block kb) sits at
+//   (((row / 128) * (k / 64) + kb / 2) * 2 + kb % 2) * 128 + (row % 32) * 4 + (row / 32) % 4,
+// so one dword per lane holds the scales of its four 32-row fragments for one
+// 64-wide k step.  Rows are padded to a multiple of 256 (pad rows: zeros).
+inline size_t mx_scale_bytes(int64_t rows, int64_t k) { return (size_t)(((rows + 255) / 256) * 256 * (k / 32)); }
+hipError_t launch_mx_quantize(const void* src, int src_dtype, int rows, int k, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
 
 // ---------------------------------- fp8 ------------------------------------
 // dst = e4m3(src * scale(rec)); rec->amax_bits raised to max |src|.  src_dtype kF32 or kBF16.

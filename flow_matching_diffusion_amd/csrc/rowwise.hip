@@ -865,6 +865,94 @@ hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStr
 // ===========================================================================
 // FP8 (E4M3) delayed scaling ("FP8 training for Flux models", Configuration).
 // ===========================================================================
+// MXFP8 quantization (the "mxfp8" recipe of "FP8 training for Flux models",
+// Configuration; block-scaled E4M3 in the OCP MX format): every 32 values of
+// a row share the scale 2^X, X = floor(log2 max|v|) - 8 clamped to [-127, 127]
+// (-127 for an all-zero block, NaN byte 0xFF and unscaled elements for a
+// block holding a non-finite value); the elements are E4M3 of v * 2^-X, a
+// product that is exact.  Four lanes own a block, 8 values each; the block
+// maximum is two lane exchanges.  Scale bytes go to the GEMM layout of
+// mx_scale_bytes; rows past `rows` up to the 256-row padding get zero codes
+// and the all-zero scale.
+// ===========================================================================
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+  const u32x4_t r = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(r[i] << 16);
+    v[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) mx_quantize_kernel(const T* __restrict__ src, int rows, int k, int rows_pad,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int per_row = k / 8;   // a multiple of 8: groups of 4 lanes never straddle rows
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= (int64_t)rows_pad * per_row) return;   // whole groups of 4 lanes leave together
+  const int row = (int)(g / per_row), c8 = (int)(g % per_row);
+  float v[8];
+  if (row < rows) {
+    load8<T>(src + (int64_t)row * k + c8 * 8, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i]));   // NaN patterns sort above infinity
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  uint32_t sbyte;
+  float inv = 1.0f;
+  if (m >= 0x7f800000u) {
+    sbyte = 0xFFu;   // non-finite block: NaN scale, elements unscaled
+  } else {
+    // floor(log2 m) for a normal m; any subnormal m gives X = -127 anyway
+    const int e = m >= 0x00800000u ? (int)(m >> 23) - 127 : -127;
+    int X = m == 0u ? -127 : e - 8;
+    X = X < -127 ? -127 : X;
+    sbyte = (uint32_t)(X + 127);
+    inv = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X, a normal float for X in [-127, 119]
+  }
+  if (row < rows) {
+    uint2 o;
+    o.x = f32x4_to_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    o.y = f32x4_to_e4m3(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    *reinterpret_cast<uint2*>(codes + (int64_t)row * k + c8 * 8) = o;
+  }
+  if ((c8 & 3) == 0) {
+    const int kb = c8 >> 2, kt = kb >> 1, h = kb & 1;
+    const int64_t idx = (((int64_t)(row >> 7) * (k >> 6) + kt) * 2 + h) * 128 + (row & 31) * 4 + ((row >> 5) & 3);
+    scales[idx] = (uint8_t)sbyte;
+  }
+}
+
+hipError_t launch_mx_quantize(const void* src, int src_dtype, int rows, int k, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream) {
+  const int rows_pad = ((rows + 255) / 256) * 256;
+  const int64_t threads = (int64_t)rows_pad * (k / 8);
+  const dim3 grid((unsigned)ceil_div(threads, 256));
+  TimingScope ts(kKcMxQuant, stream, (double)rows * k * ((src_dtype == kBF16 ? 2.0 : 4.0) + 1.0 + 1.0 / 32));
+  if (src_dtype == kBF16)
+    hipLaunchKernelGGL(mx_quantize_kernel<bf16_t>, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(src), rows,
+                       k, rows_pad, codes, scales);
+  else
+    hipLaunchKernelGGL(mx_quantize_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(src), rows,
+                       k, rows_pad, codes, scales);
+  return hipGetLastError();
+}
+
+// ===========================================================================
 // dst = e4m3(src * scale(rec)) over a whole tensor (the weight cast of a
 // forward); each thread converts 16 consecutive elements per step, and one
 // atomic per wave raises the record's amax.

@@ -17,6 +17,8 @@ enum KernelClass : int {
   kKcMisc,
   kKcGemmPkFp8,       // gemm_fp8_kernel (E4M3 operands)
   kKcFp8Cast,         // fp8 quantization of a whole tensor (weight cast)
+  kKcGemmPkMx,        // gemm_fp8_kernel with MXFP8 block scales
+  kKcMxQuant,         // MXFP8 quantization
   kKcCount
 };
 

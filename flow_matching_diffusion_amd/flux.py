@@ -40,6 +40,7 @@ EXPORTED = (
     "flux_attention_workspace_bytes", "flux_status_string", "flux_last_error", "flux_timing_enable",
     "flux_timing_classes", "flux_timing_class_name", "flux_timing_read", "flux_convert_bf16_to_f16",
     "flux_fp8_state_bytes", "flux_fp8_quantize", "flux_fp8_update", "flux_fp8_linear_fwd", "flux_euler_step",
+    "flux_mx_scale_bytes", "flux_mx_quantize", "flux_mxfp8_linear_fwd",
 )
 
 
@@ -119,6 +120,8 @@ def lib() -> C.CDLL:
         "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
                            vp, vp, i64, vp, i64, vp, vp, sz, vp],
         "flux_euler_step": [P(flux_euler_args), vp],
+        "flux_mx_quantize": [i32, vp, i32, i32, vp, vp, vp],
+        "flux_mxfp8_linear_fwd": [i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
         "flux_final_fwd": [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
         "flux_attention_fwd": [i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, sz, vp],
@@ -137,6 +140,8 @@ def lib() -> C.CDLL:
     L.flux_workspace_bytes.restype = sz
     L.flux_rf_workspace_bytes.argtypes = [i32, i64]
     L.flux_rf_workspace_bytes.restype = sz
+    L.flux_mx_scale_bytes.argtypes = [i32, i32]
+    L.flux_mx_scale_bytes.restype = sz
     L.flux_embed_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.flux_embed_workspace_bytes.restype = sz
     L.flux_final_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -297,6 +302,32 @@ def flux_embed_fwd(precision, batch, channels, height, width, l_txt, ctx_dim, hi
                                 img_bstride, ptr(x_txt), txt_bstride, ptr(vec), ptr(workspace), workspace_bytes,
                                 _stream(stream)),
            "flux_embed_fwd")
+
+
+def flux_mx_scale_bytes(rows: int, k: int) -> int:
+    return lib().flux_mx_scale_bytes(rows, k)
+
+
+def flux_mx_quantize(src_precision: int, src, rows: int, k: int, codes, scales, stream=None) -> None:
+    _check(lib().flux_mx_quantize(src_precision, ptr(src), rows, k, ptr(codes), ptr(scales), _stream(stream)),
+           "flux_mx_quantize")
+
+
+def flux_mxfp8_linear_fwd(m: int, n: int, k: int, x, x_scales, w, w_scales, b, y, ldy: int, stream=None) -> None:
+    _check(lib().flux_mxfp8_linear_fwd(m, n, k, ptr(x), ptr(x_scales), ptr(w), ptr(w_scales), ptr(b), ptr(y), ldy,
+                                       _stream(stream)), "flux_mxfp8_linear_fwd")
+
+
+def mx_scales_unswizzle(sc, rows: int, k: int):
+    """[rows, k/32] scale bytes from the GEMM layout of flux_mx_quantize
+    (numpy uint8 array in, numpy out; pad rows dropped)."""
+    import numpy as np
+    s = np.asarray(sc, dtype=np.uint8)
+    rp = ((rows + 255) // 256) * 256
+    # byte (((row/128)*(k/64) + kb/2)*2 + kb%2)*128 + (row%32)*4 + (row/32)%4
+    t = s[: rp * (k // 32)].reshape(rp // 128, k // 64, 2, 32, 4)      # [rb, kt, h, l32, i]
+    t = t.transpose(0, 4, 3, 1, 2).reshape(rp, k // 32)                 # rows rb*128 + i*32 + l32
+    return t[:rows]
 
 
 def flux_euler_step(batch: int, n_per_sample: int, v, z, t_cur: float, t_next: float, cfg: bool = False,

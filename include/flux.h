@@ -413,6 +413,38 @@ flux_status flux_fp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* 
                                 const flux_fp8_tensor* rw, const void* b, float* y, int64_t ldy,
                                 void* stream);
 
+/*
+ * MXFP8 linears (the "mxfp8" recipe named in "FP8 training for Flux models",
+ * Configuration; block-scaled E4M3 in the OCP MX v1.0 format): each 32
+ * consecutive values along K share one power-of-two scale stored as an E8M0
+ * byte, applied inside gfx950's scaled fp8 MFMA.
+ *
+ * flux_mx_scale_bytes -- bytes of the scale array of a [rows, k] operand:
+ *   rows rounded up to a multiple of 256, times k / 32.
+ *
+ * flux_mx_quantize -- codes [rows, k] (row-major E4M3 bytes) and scales of
+ *   src [rows, k] (FLUX_PREC_F32 float or FLUX_PREC_BF16, row-major): block
+ *   exponent X = floor(log2 max|v|) - 8 clamped to [-127, 127] (-127 for an
+ *   all-zero block), scale byte X + 127 (0xFF, the E8M0 NaN, for a block
+ *   holding a non-finite value, whose elements are then encoded unscaled),
+ *   code = e4m3(v * 2^-X) rounded to nearest even with saturation to +-448.
+ *   The scale array has the layout the GEMM reads: the byte of (row, block
+ *   kb) is at (((row/128)*(k/64) + kb/2)*2 + kb%2)*128 + (row%32)*4 + (row/32)%4,
+ *   pad rows get the all-zero block's byte.  k a multiple of 64; pointers
+ *   16-byte aligned; codes and scales must not overlap src.
+ *
+ * flux_mxfp8_linear_fwd -- y = sum over K blocks of 2^(X_x + X_w) (x_q w_q^T)
+ *   + b: x [M, K] and w [N, K] as written by flux_mx_quantize (row stride K),
+ *   b [N] bf16 or NULL, y [M, N] float (row stride ldy).  K a multiple of 128
+ *   and at least 256, N a multiple of 4.
+ */
+size_t flux_mx_scale_bytes(int32_t rows, int32_t k);
+flux_status flux_mx_quantize(int32_t src_precision, const void* src, int32_t rows, int32_t k, uint8_t* codes,
+                             uint8_t* scales, void* stream);
+flux_status flux_mxfp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* x, const uint8_t* x_scales,
+                                  const uint8_t* w, const uint8_t* w_scales, const void* b, float* y, int64_t ldy,
+                                  void* stream);
+
 /* Workspace sizes (bytes).  op: 0 double block, 1 single block, 2 sequential single block;
  * 0 for invalid dims or op. */
 size_t flux_workspace_bytes(const flux_dims* dims, int32_t op);

@@ -159,3 +159,19 @@ def test_convert_and_weights_f16_checks():
     d = _dims(precision=F.FLUX_PREC_F32, weights_f16=1)
     assert F.flux_workspace_bytes(d, 0) == 0      # fp16-held weights need FLUX_PREC_BF16
     assert F.flux_workspace_bytes(_dims(weights_f16=1), 0) > 0
+
+
+def test_mx_scale_layout_helper():
+    # the binding's unswizzle inverts the byte layout flux.h documents
+    import numpy as np
+    rows, k = 300, 192
+    rp = 512
+    buf = np.zeros(F.flux_mx_scale_bytes(rows, k), dtype=np.uint8)
+    assert buf.size == rp * (k // 32)
+    ref = np.zeros((rp, k // 32), dtype=np.uint8)
+    for row in range(rp):
+        for kb in range(k // 32):
+            v = (row * 7 + kb * 13) % 251
+            ref[row, kb] = v
+            buf[(((row // 128) * (k // 64) + kb // 2) * 2 + kb % 2) * 128 + (row % 32) * 4 + (row // 32) % 4] = v
+    assert np.array_equal(F.mx_scales_unswizzle(buf, rows, k), ref[:rows])
