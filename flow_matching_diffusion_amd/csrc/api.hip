@@ -850,6 +850,23 @@ flux_status flux_mxfp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t
   return FLUX_OK;
 }
 
+flux_status flux_fp8_quantize_current(int32_t src_precision, const void* src, int64_t n, flux_fp8_tensor* rec,
+                                      uint8_t* dst, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(src_precision == FLUX_PREC_F32 || src_precision == FLUX_PREC_BF16,
+          "src_precision must be FLUX_PREC_F32 or FLUX_PREC_BF16 (got %d)", src_precision);
+  REQUIRE(n >= 1 && n < ((int64_t)1 << 40), "n must be in [1, 2^40)");
+  REQUIRE(src && dst && rec, "src, rec and dst are required");
+  REQUIRE(aligned16(src) && aligned16(dst) && aligned16(rec), "pointers must be 16-byte aligned");
+  const int64_t sbytes = n * (src_precision == FLUX_PREC_F32 ? 4 : 2);
+  REQUIRE(!ranges_overlap(dst, n, src, sbytes), "src and dst must not overlap");
+  const int sdt = src_precision == FLUX_PREC_F32 ? kF32 : kBF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FLUX_HIP(launch_fp8_current_scale(src, sdt, n, rec, st), "fp8 current scale");
+  FLUX_HIP(launch_fp8_quantize(src, sdt, n, rec, dst, st), "fp8 quantize");
+  return FLUX_OK;
+}
+
 flux_status flux_fp8_quantize(int32_t src_precision, const void* src, int64_t n, flux_fp8_tensor* rec, uint8_t* dst,
                               void* stream) {
   g_err[0] = 0;

@@ -173,6 +173,9 @@ hipError_t launch_mx_quantize(const void* src, int src_dtype, int rows, int k, u
 // dst = e4m3(src * scale(rec)); rec->amax_bits raised to max |src|.  src_dtype kF32 or kBF16.
 hipError_t launch_fp8_quantize(const void* src, int src_dtype, int64_t n, flux_fp8_tensor* rec, uint8_t* dst,
                                hipStream_t stream);
+// current scaling: rec->amax = max |src|, then scale = fp32(448 / amax), scale_inv = 1 / scale
+hipError_t launch_fp8_current_scale(const void* src, int src_dtype, int64_t n, flux_fp8_tensor* rec,
+                                    hipStream_t stream);
 // delayed-scaling update of n records (algo 0 most_recent, 1 max)
 hipError_t launch_fp8_update(flux_fp8_tensor* rec, int n, int algo, int margin, hipStream_t stream);
 

@@ -1018,6 +1018,65 @@ hipError_t launch_fp8_quantize(const void* src, int src_dtype, int64_t n, flux_f
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Current ("tensorwise") scaling, the alternative recipe the FP8 page names:
+// the scale comes from the amax of the tensor being quantized, not from
+// earlier forwards.  Three launches ahead of the quantization: clear the
+// record's amax, reduce max |src| into it (one atomic per block), set
+// scale = fp32(448 / amax) and scale_inv = 1 / scale when the amax is finite
+// and positive (else keep the scale; a non-finite amax sets the sticky flag).
+// ---------------------------------------------------------------------------
+__global__ void fp8_amax_clear_kernel(flux_fp8_tensor* rec) {
+  if (threadIdx.x == 0) rec->amax_bits = 0u;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) fp8_amax_kernel(const T* __restrict__ src, int64_t n, flux_fp8_tensor* rec) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    m = max(m, abs_bits(load_f32<T>(src + i)));   // NaN patterns sort above every finite one
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t b = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (b) fp8_amax_raise(rec, __uint_as_float(b));
+  }
+}
+
+__global__ void fp8_current_scale_kernel(flux_fp8_tensor* rec) {
+  if (threadIdx.x != 0) return;
+  const float a = __uint_as_float(rec->amax_bits);
+  uint32_t flags = rec->flags;
+  if (!__builtin_isfinite(a)) flags |= FLUX_FP8_NONFINITE;
+  if (__builtin_isfinite(a) && a > 0.f) {
+    const float sc = 448.0f / a;
+    rec->scale = sc;
+    rec->scale_inv = 1.0f / sc;
+    flags |= FLUX_FP8_SCALE_SET;
+  }
+  rec->flags = flags;
+}
+
+hipError_t launch_fp8_current_scale(const void* src, int src_dtype, int64_t n, flux_fp8_tensor* rec,
+                                    hipStream_t stream) {
+  TimingScope ts(kKcFp8Cast, stream, (double)n * (src_dtype == kF32 ? 4.0 : 2.0));
+  hipLaunchKernelGGL(fp8_amax_clear_kernel, dim3(1), dim3(64), 0, stream, rec);
+  int64_t blocks = ceil_div(n, 256 * 8);
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  if (src_dtype == kF32)
+    hipLaunchKernelGGL(fp8_amax_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const float*>(src), n, rec);
+  else
+    hipLaunchKernelGGL(fp8_amax_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const bf16_t*>(src), n, rec);
+  hipLaunchKernelGGL(fp8_current_scale_kernel, dim3(1), dim3(64), 0, stream, rec);
+  return hipGetLastError();
+}
+
+
 // One thread per record: the amax recorded since the last update enters the
 // history ring, the selected amax (newest entry, or the history maximum with
 // NaN propagating) gives scale = (448 / amax) * 2^-margin when it is finite

@@ -40,7 +40,7 @@ EXPORTED = (
     "flux_attention_workspace_bytes", "flux_status_string", "flux_last_error", "flux_timing_enable",
     "flux_timing_classes", "flux_timing_class_name", "flux_timing_read", "flux_convert_bf16_to_f16",
     "flux_fp8_state_bytes", "flux_fp8_quantize", "flux_fp8_update", "flux_fp8_linear_fwd", "flux_euler_step",
-    "flux_mx_scale_bytes", "flux_mx_quantize", "flux_mxfp8_linear_fwd",
+    "flux_mx_scale_bytes", "flux_mx_quantize", "flux_mxfp8_linear_fwd", "flux_fp8_quantize_current",
 )
 
 
@@ -127,6 +127,7 @@ def lib() -> C.CDLL:
         "flux_attention_fwd": [i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, sz, vp],
         "flux_convert_bf16_to_f16": [vp, vp, i64, vp],
         "flux_fp8_quantize": [i32, vp, i64, vp, vp, vp],
+        "flux_fp8_quantize_current": [i32, vp, i64, vp, vp, vp],
         "flux_fp8_update": [vp, i32, i32, i32, vp],
         "flux_fp8_linear_fwd": [i32, i32, i32, vp, i64, vp, i64, vp, vp, vp, vp, i64, vp],
     }
@@ -396,6 +397,11 @@ def flux_fp8_state_bytes(n_tensors: int) -> int:
 def flux_fp8_quantize(src_precision: int, src, n: int, rec, dst, stream=None) -> None:
     _check(lib().flux_fp8_quantize(src_precision, ptr(src), n, ptr(rec), ptr(dst), _stream(stream)),
            "flux_fp8_quantize")
+
+
+def flux_fp8_quantize_current(src_precision: int, src, n: int, rec, dst, stream=None) -> None:
+    _check(lib().flux_fp8_quantize_current(src_precision, ptr(src), n, ptr(rec), ptr(dst), _stream(stream)),
+           "flux_fp8_quantize_current")
 
 
 def flux_fp8_update(recs, n_tensors: int, algo: int = 0, margin: int = 0, stream=None) -> None:

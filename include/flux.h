@@ -398,6 +398,13 @@ flux_status flux_convert_bf16_to_f16(const void* src, void* dst, int64_t n, void
  *   consecutive records; algo 0 = most_recent, 1 = max; 0 <= margin <= 32.
  *   Run it after a forward, on the same stream.
  *
+ * flux_fp8_quantize_current -- the current ("tensorwise") scaling recipe the
+ *   page lists beside delayed scaling: rec->amax_bits = max |src| of this
+ *   tensor, then, when that amax is finite and positive, rec->scale =
+ *   fp32(448 / amax), rec->scale_inv = 1 / scale and FLUX_FP8_SCALE_SET (a
+ *   non-finite amax keeps the scale and sets FLUX_FP8_NONFINITE); then dst as
+ *   flux_fp8_quantize with that scale.  The history is not touched.
+ *
  * flux_fp8_linear_fwd -- y = (x_q w_q^T) * scale_inv(rx) * scale_inv(rw) + b:
  *   x_q [M, K] E4M3 bytes (row stride ldx), w_q [N, K] E4M3 bytes (row stride
  *   ldw), quantized with the records rx and rw; b [N] bf16 or NULL; y [M, N]
@@ -406,6 +413,8 @@ flux_status flux_convert_bf16_to_f16(const void* src, void* dst, int64_t n, void
 size_t flux_fp8_state_bytes(int32_t n_tensors);
 flux_status flux_fp8_quantize(int32_t src_precision, const void* src, int64_t n, flux_fp8_tensor* rec,
                               uint8_t* dst, void* stream);
+flux_status flux_fp8_quantize_current(int32_t src_precision, const void* src, int64_t n, flux_fp8_tensor* rec,
+                                      uint8_t* dst, void* stream);
 flux_status flux_fp8_update(flux_fp8_tensor* recs, int32_t n_tensors, int32_t algo, int32_t margin,
                             void* stream);
 flux_status flux_fp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* x, int64_t ldx,

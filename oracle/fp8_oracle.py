@@ -26,6 +26,9 @@ Readings taken where that page is silent (each repeated at its function):
      each double-block stream; lin1 and lin2 of the single block); the
      modulation linears, the embeddings, the output head and attention keep
      their bf16 operands.
+  F6 the "tensorwise" alternative recipe the page lists scales each tensor
+     with its own current amax: s = fp32(448 / amax) of the tensor being
+     quantized, no history.
 """
 from __future__ import annotations
 
@@ -36,7 +39,7 @@ import numpy as np
 from .flux_oracle import f64, linear
 
 __all__ = ["E4M3_MAX", "HISTORY_LEN", "e4m3_decode", "e4m3_encode", "quantize", "amax", "fp8_linear",
-           "scale_update", "fp8_linears", "TOKEN_LINEARS_DOUBLE", "TOKEN_LINEARS_SINGLE"]
+           "scale_update", "current_scale", "fp8_linears", "TOKEN_LINEARS_DOUBLE", "TOKEN_LINEARS_SINGLE"]
 
 E4M3_MAX = 448.0
 HISTORY_LEN = 1024
@@ -123,6 +126,16 @@ def scale_update(history: np.ndarray, amax_now: float, scale: float, algo: str =
     else:
         new = np.float32(scale)
     return hist, float(new), nonfinite
+
+
+def current_scale(x, scale_before: float = 1.0) -> float:
+    """Current ("tensorwise") scaling, the recipe the page lists beside delayed
+    scaling (F6): the scale of a tensor comes from its own amax,
+    fp32(448 / fp32(amax)); a zero or non-finite amax keeps scale_before."""
+    a = np.float32(amax(x))
+    if np.isfinite(a) and a > 0:
+        return float(np.float32(np.float32(E4M3_MAX) / a))
+    return float(np.float32(scale_before))
 
 
 def fp8_linears(scales: Dict[str, Tuple[float, float]],

@@ -231,3 +231,20 @@ def test_amax_closed_forms():
     assert Q.amax(np.zeros((0,))) == 0.0
     assert np.isnan(Q.amax(np.array([1.0, np.nan, -7.0])))
     assert Q.amax(np.array([-np.inf, 1.0])) == np.inf
+
+
+def test_current_scale_definition():
+    # F6: fp32(448 / amax) of the tensor itself; its largest element then maps to
+    # 448 (code 0x7E) up to one fp32 rounding of the product, and a zero or
+    # non-finite tensor keeps the previous scale
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        x = (rng.standard_normal(1000) * np.exp2(rng.integers(-30, 30))).astype(np.float32)
+        s = Q.current_scale(x)
+        a = np.float32(np.abs(x).max())
+        assert s == float(np.float32(np.float32(448.0) / a))
+        q = Q.quantize(x, s)
+        assert (q[np.argmax(np.abs(x))] & 0x7F) == 0x7E
+        assert np.all((q & 0x7F) <= 0x7E)
+    assert Q.current_scale(np.zeros(8), 3.0) == 3.0
+    assert Q.current_scale(np.array([1.0, np.inf]), 2.5) == 2.5

@@ -117,6 +117,34 @@ def test_quantize_fp32_source_ragged_and_amax():
     assert _read_records(rec, 1)[0]["amax"] == float(np.abs(v).max())
 
 
+@pytest.mark.parametrize("bf16", [True, False])
+def test_quantize_current_scaling(bf16):
+    # the "tensorwise" recipe: the scale comes from this tensor's own amax
+    _say(f"fp8 current scaling bf16={bf16}")
+    rng = np.random.default_rng(5 if bf16 else 6)
+    v = (rng.standard_normal(300_007) * 7.3).astype(np.float32)
+    v[17] = -91.0
+    if bf16:
+        v = synth.round_to_bf16(v).astype(np.float32)
+        src = torch.from_numpy(synth.bf16_bits(v).view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        src = dev(v)
+    rec = _records(1, [5.0])                     # a stale delayed scale that must be replaced
+    dst = torch.empty(v.size, dtype=torch.uint8, device="cuda")
+    F().flux_fp8_quantize_current(F().FLUX_PREC_BF16 if bf16 else F().FLUX_PREC_F32, src, v.size, rec, dst)
+    torch.cuda.synchronize()
+    s = Q.current_scale(v)
+    r = _read_records(rec, 1)[0]
+    assert r["scale"] == s and r["scale_inv"] == float(np.float32(1.0) / np.float32(s))
+    assert r["amax"] == float(np.abs(v).max())
+    assert np.array_equal(dst.cpu().numpy(), Q.quantize(v, s))
+    # a zero tensor keeps the previous scale
+    z = torch.zeros(1000, dtype=torch.float32, device="cuda")
+    F().flux_fp8_quantize_current(F().FLUX_PREC_F32, z, 1000, rec, dst)
+    torch.cuda.synchronize()
+    assert _read_records(rec, 1)[0]["scale"] == s
+
+
 # --------------------------------------------------------------------------- #
 # delayed-scaling update
 # --------------------------------------------------------------------------- #
