@@ -331,6 +331,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager steps only (the default also captures the step in a HIP graph and "
+                         "reports the replay time as ms_per_step)")
     ap.add_argument("--workload", default="flux12b_blocks",
                     choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8", "flux12b_blocks_seq",
                              "flux12b_sample_cfg", "flux12b_mxfp8_linears"],
@@ -440,11 +443,12 @@ def main() -> int:
         torch.cuda.synchronize()
         fp8_cast_ms = e0.elapsed_time(e1)
         m.cast_each_forward = False
+    # per-kernel durations: eager steps with the HIP-event hook around every launch
     FX.flux_timing_read()                       # discard anything recorded so far
     FX.flux_timing_enable(True)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timing {args.steps} steps (per-kernel hook)", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record()
@@ -455,8 +459,54 @@ def main() -> int:
     wall = time.perf_counter() - w0
     FX.flux_timing_enable(False)
     kernels = FX.flux_timing_read()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step_eager = ev0.elapsed_time(ev1) / args.steps
+    ms_step = ms_step_eager
+    graph_ok = None
+    # the step time: the same step captured once in a HIP graph and replayed
+    # (no hook events, no launch gaps).  Every replay is checked against an
+    # eager step on the same inputs before timing (a deterministic forward:
+    # bit-identical outputs); the sampler's steps differ in their scalar
+    # arguments and stay eager.
+    if not args.no_graph and not sample:
+        print("[bench] capturing the step in a HIP graph", file=sys.stderr, flush=True)
+        step()
+        torch.cuda.synchronize()
+        ref_v = out["v_pred"].clone()
+        ref_l = out["loss"].clone()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()                                  # eager on the capture stream once (allocations settle)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph_ok = True
+        for r in range(3):
+            out["v_pred"].zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            same = bool(torch.equal(out["v_pred"], ref_v)) and bool(torch.equal(out["loss"], ref_l))
+            if not same and not fp8:
+                graph_ok = False
+            step()                                  # eager work between replays
+            torch.cuda.synchronize()
+        if not fp8:
+            assert graph_ok, "graph replay differs from the eager step"
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_step = g0.elapsed_time(g1) / args.steps
     if sample:
         loss = None
         assert bool(torch.isfinite(out["z"]).all()), "non-finite sample"
@@ -520,6 +570,8 @@ def main() -> int:
         "gemm_tflops": round(gemm_tflops, 2) if gemm_tflops else None,
         "step_tflops": round(work["total_flops"] / (ms_step * 1e-3) / 1e12, 2),
         "kernels": {k: {kk: (round(vv, 5) if vv < 1e6 else vv) for kk, vv in v.items()} for k, v in kt.items()},
+        "ms_per_step_eager_with_hook": round(ms_step_eager, 4),
+        "graph": None if graph_ok is None else ("replays bit-identical to eager" if graph_ok else "replayed"),
         "wall_s": round(wall, 3),
         "loss": loss,
     }
