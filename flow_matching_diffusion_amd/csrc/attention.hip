@@ -210,6 +210,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
   f32x16_t sc_cur[2], sc_nxt[2];
   s_tile(0, sc_cur);
+  // iteration 0 overwrites K(0)'s buffer with K(2): every wave must have read
+  // K(0) first
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     softmax_max(t, sc_cur);
     // S(t + 1) with the exponentials of tile t in its MFMA shadow: step m
