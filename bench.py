@@ -204,7 +204,7 @@ def summarize_counters(directory, out_dir):
                  "| class | fetch MiB/launch | write MiB/launch | total MiB/launch |\n|---|---|---|---|\n"
                  + "\n".join(lines) + "\n")
     with open(os.path.join(out_dir, f"kernel_stats_{PROFILE_WORKLOAD}.md"), "w") as fh:
-        fh.write(f"# rocprofv3 --kernel-trace --stats, {PROFILE_WORKLOAD} (20 timed + 5 warmup steps)\n\n"
+        fh.write(f"# rocprofv3 --kernel-trace --stats, {PROFILE_WORKLOAD} (5 warmup, 20 timed eager steps, the graph capture and its replay check, 20 timed graph replays)\n\n"
                  f"Made by:\n\n    {PROFILE_COMMANDS[0]}\n\n"
                  "| kernel | calls | total ms | avg us | % |\n|---|---|---|---|---|\n")
         for r in stats:
