@@ -273,6 +273,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
+  // training: P = exp2(s * sc - m_run) / l_tot = exp2(s * sc - lse)
+  if (a.lse && half == 0) a.lse[bh * a.seq_pad + q] = q < a.seq ? m_run + __log2f(l_tot) : INFINITY;
   if constexpr (OUT == kFP8) {
     // E4M3 output with the delayed scale of the row's stream (image rows
     // oq[0], text rows oq[1]); each stream's amax is raised once per wave

@@ -131,10 +131,115 @@ struct AttnArgs {
   float scale_log2;                                       // log2(e) / sqrt(head_dim)
   flux_fp8_tensor* oq[2];                                 // kFP8 output: rows < l_img use oq[0], others oq[1]
   int32_t l_img;
+  float* lse;   // optional [B, H, seq_pad]: log2-domain log-sum-exp of the scaled scores per query
+                //   (+inf for queries >= seq), so that P = exp2(s * scale_log2 - lse); bf16 kernel only
 };
 // in_dtype kBF16 (bf16 MFMA) or kF32; out_dtype kBF16 / kF16 / kFP8 with bf16
 // inputs, kF32 with fp32 inputs
 hipError_t launch_attention(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
+
+// ------------------------------- backward --------------------------------
+// dst[z][c][r] = bf16(src[z][r][c]) for r < R, c < C; zero for R <= r < R_fill.
+// C, R_fill, the source row stride and dst_ld multiples of 4.
+struct TransposeArgs {
+  const void* src; int64_t src_zstride; RowMap smap;     // row r of slice z at src + z * src_zstride + smap(r)
+  void* dst; int64_t dst_zstride; int64_t dst_ld;
+  int32_t R, C, R_fill, Z;
+};
+hipError_t launch_transpose(const TransposeArgs& a, int src_dtype, hipStream_t stream);
+
+// out[z * out_zstride + c] (mode 0 =, 1 +=) sum over the R rows of sample z
+// (global row z * R + r addressed through amap / bmap) of A (* Bm); fixed order.
+// part: scratch of Z * nrb * C floats; C % 4 == 0.
+struct ColsumArgs {
+  const void* A; RowMap amap;
+  const float* Bm; RowMap bmap;          // optional elementwise factor (fp32)
+  int32_t R, C, Z;
+  int32_t rpb, nrb;                      // rows per partial, partial count (rpb * nrb >= R)
+  float* part;
+};
+hipError_t launch_colsum(ColsumArgs a, int a_dtype, float* out, int64_t out_zstride, int mode, hipStream_t stream);
+
+struct ReduceArgs {
+  const float* part; int32_t np; int32_t C; int32_t Z;
+  int64_t pstride;                       // floats from one partial to the next (0: C)
+  float* out; int64_t out_zstride;
+  int32_t mode;                          // 0 store, 1 add, 2 add times SiLU'(aux)
+  const float* aux; int64_t aux_zstride;
+};
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
+enum EwOp : int { kEwGateBwd = 0, kEwGeluBwd = 1, kEwGelu = 2, kEwGateAdd = 3 };
+struct EwArgs {
+  int32_t op;
+  const void* x; RowMap xmap;
+  const void* y; RowMap ymap;
+  void* out; RowMap omap;
+  const float* gate; int64_t gate_bstride;   // gate[(r / xmap.seg) * gate_bstride + c]
+  int64_t rows; int32_t C;                   // C % 4 == 0
+};
+hipError_t launch_elementwise(const EwArgs& a, hipStream_t stream);
+
+// LayerNorm-modulate backward over `batch` samples of `seg` rows each:
+// dx (fp32, +=), dshift / dscale (fp32, written at [b * mod_bstride + c]).
+// part_sh / part_sc: scratch of batch * ln_bwd_blocks(seg, batch) * 4 * dim floats each.
+struct LnBwdArgs {
+  const float* x; RowMap xmap;
+  const float* dh; RowMap dhmap;
+  float* dx; RowMap dxmap;
+  const float* scale; int64_t mod_bstride;
+  float* dshift; float* dscale;
+  float* part_sh; float* part_sc;
+  int32_t seg, batch, rpb;
+  float eps;
+};
+int ln_bwd_blocks(int seg, int batch);
+hipError_t launch_ln_mod_bwd(LnBwdArgs a, int dim, hipStream_t stream);
+
+// q / k RMSNorm + RoPE backward (head_dim 128).  dq, dk, dv fp32 head-major
+// [B, H, seq_pad, 128]; src: the forward's q|k|v token rows (bf16, q at column
+// 0, k at D, v at 2D); dst: bf16 token rows of the same layout.  part:
+// prep_bwd_parts(...) * 512 floats, [block][stream][q / k][d].
+struct PrepBwdArgs {
+  const float* dq; const float* dk; const float* dv;
+  const void* src; int64_t src_bstride; int64_t src_ld;
+  void* dst; int64_t dst_bstride; int64_t dst_ld;
+  const float* gq_img; const float* gk_img; const float* gq_txt; const float* gk_txt;
+  const float* rope;
+  int32_t batch, seq, seq_pad, heads, l_img;
+  float eps;
+  float* part;
+};
+int prep_bwd_parts(int batch, int seq, int heads);
+hipError_t launch_prep_bwd(const PrepBwdArgs& a, hipStream_t stream);
+
+// Attention backward (bf16, head_dim 128).  Inputs head-major bf16: qh, kh, vh
+// [B, H, seq_pad, 128], qt, kt [B, H, 128, seq_pad]; lse [B, H, seq_pad] from
+// the forward; dout / o bf16 token rows (head h at column h * 128).  Scratch:
+// doh [B, H, seq_pad, 128], dot [B, H, 128, seq_pad] bf16, dd [B, H, seq_pad]
+// fp32.  Outputs fp32 head-major dq, dk, dv [B, H, seq_pad, 128] (rows < seq).
+struct AttnBwdArgs {
+  const void* qh; const void* kh; const void* vh; const void* qt; const void* kt;
+  const float* lse;
+  const void* dout; int64_t dout_bstride; int64_t dout_ld;
+  const void* o; int64_t o_bstride; int64_t o_ld;
+  void* doh; void* dot; float* dd;
+  float* dq; float* dk; float* dv;
+  int32_t batch, seq, seq_pad, heads;
+  float scale_log2, scale;
+};
+hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t stream);
+
+// adaLN modulation backward: m = W SiLU(vec) + b, W [N, K] (weight dtype),
+// dm [B, N] (row stride dm_bstride).  dw [N, K], db [N] written; dvec [B, K]
+// += SiLU'(vec) * W^T dm.  part: scratch of batch * nrc * K floats.
+struct ModBwdArgs {
+  const void* w; const float* vec; const float* dm; int64_t dm_bstride;
+  float* dw; float* db; float* dvec;
+  int32_t N, K, batch, nrc, rpc;
+  float* part;
+};
+hipError_t launch_mod_bwd(ModBwdArgs a, int w_dtype, hipStream_t stream);
 
 // ------------------------------ small kernels ------------------------------
 hipError_t launch_rope_table(const float* ids, int batch, int seq, const int32_t axes[3], float theta,

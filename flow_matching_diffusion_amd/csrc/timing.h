@@ -19,6 +19,8 @@ enum KernelClass : int {
   kKcFp8Cast,         // fp8 quantization of a whole tensor (weight cast)
   kKcGemmPkMx,        // gemm_fp8_kernel with MXFP8 block scales
   kKcMxQuant,         // MXFP8 quantization
+  kKcAttnBwd,         // attention backward (dK / dV and dQ kernels)
+  kKcBwdElem,         // backward row-wise, element-wise, transpose and reduction kernels
   kKcCount
 };
 

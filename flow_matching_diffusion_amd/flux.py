@@ -41,6 +41,9 @@ EXPORTED = (
     "flux_timing_classes", "flux_timing_class_name", "flux_timing_read", "flux_convert_bf16_to_f16",
     "flux_fp8_state_bytes", "flux_fp8_quantize", "flux_fp8_update", "flux_fp8_linear_fwd", "flux_euler_step",
     "flux_mx_scale_bytes", "flux_mx_quantize", "flux_mxfp8_linear_fwd", "flux_fp8_quantize_current",
+    "flux_train_saved_bytes", "flux_bwd_workspace_bytes", "flux_block_fwd_train", "flux_block_bwd",
+    "flux_single_fwd_train", "flux_single_bwd", "flux_attention_train_workspace_bytes", "flux_attention_fwd_train",
+    "flux_attention_bwd",
 )
 
 
@@ -72,6 +75,16 @@ class flux_stream_weights(C.Structure):
 class flux_single_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "lin1_w", "lin1_b", "q_norm", "k_norm", "lin2_w",
                                           "lin2_b", "fp8")]
+
+
+class flux_stream_grads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "qkv_w", "qkv_b", "q_norm", "k_norm", "proj_w",
+                                          "proj_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+
+
+class flux_single_grads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "lin1_w", "lin1_b", "q_norm", "k_norm", "lin2_w",
+                                          "lin2_b")]
 
 
 class rf_args(C.Structure):
@@ -130,6 +143,15 @@ def lib() -> C.CDLL:
         "flux_fp8_quantize_current": [i32, vp, i64, vp, vp, vp],
         "flux_fp8_update": [vp, i32, i32, i32, vp],
         "flux_fp8_linear_fwd": [i32, i32, i32, vp, i64, vp, i64, vp, vp, vp, vp, i64, vp],
+        "flux_block_fwd_train": [P(flux_dims), P(flux_stream_weights), P(flux_stream_weights), vp, i64, vp, i64, vp,
+                                 vp, vp, sz, vp],
+        "flux_block_bwd": [P(flux_dims), P(flux_stream_weights), P(flux_stream_weights), vp, i64, vp, i64, vp, vp, vp,
+                           sz, P(flux_stream_grads), P(flux_stream_grads), vp, vp, sz, vp],
+        "flux_single_fwd_train": [P(flux_dims), P(flux_single_weights), vp, i64, vp, vp, vp, sz, vp],
+        "flux_single_bwd": [P(flux_dims), P(flux_single_weights), vp, i64, vp, vp, vp, sz, P(flux_single_grads), vp,
+                            vp, sz, vp],
+        "flux_attention_fwd_train": [i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp],
+        "flux_attention_bwd": [i32, i32, i32, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -149,6 +171,12 @@ def lib() -> C.CDLL:
     L.flux_final_workspace_bytes.restype = sz
     L.flux_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.flux_attention_workspace_bytes.restype = sz
+    L.flux_train_saved_bytes.argtypes = [P(flux_dims), i32]
+    L.flux_train_saved_bytes.restype = sz
+    L.flux_bwd_workspace_bytes.argtypes = [P(flux_dims), i32]
+    L.flux_bwd_workspace_bytes.restype = sz
+    L.flux_attention_train_workspace_bytes.argtypes = [i32, i32, i32]
+    L.flux_attention_train_workspace_bytes.restype = sz
     L.flux_status_string.argtypes = [C.c_int]
     L.flux_status_string.restype = C.c_char_p
     L.flux_last_error.argtypes = []
@@ -235,6 +263,28 @@ def single_weights(w: Dict[str, object], fp8=None) -> flux_single_weights:
     s.q_norm = ptr(w["q_norm"])
     s.k_norm = ptr(w["k_norm"])
     s.fp8 = ptr(fp8)
+    return s
+
+
+def stream_grads(g: Dict[str, object], prefix: Optional[str]) -> flux_stream_grads:
+    """fp32 gradient buffers keyed like the weights ("<prefix>_qkv.w", ...)."""
+    s = flux_stream_grads()
+    pre = f"{prefix}_" if prefix else ""
+    for f in ("mod", "qkv", "proj", "fc1", "fc2"):
+        setattr(s, f + "_w", ptr(g[f"{pre}{f}.w"]))
+        setattr(s, f + "_b", ptr(g[f"{pre}{f}.b"]))
+    s.q_norm = ptr(g[f"{pre}q_norm"])
+    s.k_norm = ptr(g[f"{pre}k_norm"])
+    return s
+
+
+def single_grads(g: Dict[str, object]) -> flux_single_grads:
+    s = flux_single_grads()
+    for f in ("mod", "lin1", "lin2"):
+        setattr(s, f + "_w", ptr(g[f + ".w"]))
+        setattr(s, f + "_b", ptr(g[f + ".b"]))
+    s.q_norm = ptr(g["q_norm"])
+    s.k_norm = ptr(g["k_norm"])
     return s
 
 
@@ -421,3 +471,60 @@ def fp8_record_fields(raw: bytes) -> dict:
     hist = struct.unpack_from(f"<{FLUX_FP8_HISTORY}f", raw, 32)
     return {"scale": scale, "scale_inv": scale_inv, "amax": struct.unpack("<f", struct.pack("<I", amax_bits))[0],
             "flags": flags, "hist_len": hist_len, "hist_pos": hist_pos, "history": hist}
+
+
+# --------------------------------------------------------------------------- #
+# training (backward)
+# --------------------------------------------------------------------------- #
+def flux_train_saved_bytes(dims: flux_dims, op: int) -> int:
+    return lib().flux_train_saved_bytes(C.byref(dims), op)
+
+
+def flux_bwd_workspace_bytes(dims: flux_dims, op: int) -> int:
+    return lib().flux_bwd_workspace_bytes(C.byref(dims), op)
+
+
+def flux_block_fwd_train(dims: flux_dims, img_w: flux_stream_weights, txt_w: flux_stream_weights, img,
+                         img_bstride: int, txt, txt_bstride: int, vec, rope, saved, saved_bytes: int,
+                         stream=None) -> None:
+    _check(lib().flux_block_fwd_train(C.byref(dims), C.byref(img_w), C.byref(txt_w), ptr(img), img_bstride, ptr(txt),
+                                      txt_bstride, ptr(vec), ptr(rope), ptr(saved), saved_bytes, _stream(stream)),
+           "flux_block_fwd_train")
+
+
+def flux_block_bwd(dims: flux_dims, img_w: flux_stream_weights, txt_w: flux_stream_weights, d_img, img_bstride: int,
+                   d_txt, txt_bstride: int, vec, rope, saved, saved_bytes: int, img_grads: flux_stream_grads,
+                   txt_grads: flux_stream_grads, dvec, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_block_bwd(C.byref(dims), C.byref(img_w), C.byref(txt_w), ptr(d_img), img_bstride, ptr(d_txt),
+                                txt_bstride, ptr(vec), ptr(rope), ptr(saved), saved_bytes, C.byref(img_grads),
+                                C.byref(txt_grads), ptr(dvec), ptr(workspace), workspace_bytes, _stream(stream)),
+           "flux_block_bwd")
+
+
+def flux_single_fwd_train(dims: flux_dims, w: flux_single_weights, x, x_bstride: int, vec, rope, saved,
+                          saved_bytes: int, stream=None) -> None:
+    _check(lib().flux_single_fwd_train(C.byref(dims), C.byref(w), ptr(x), x_bstride, ptr(vec), ptr(rope), ptr(saved),
+                                       saved_bytes, _stream(stream)), "flux_single_fwd_train")
+
+
+def flux_single_bwd(dims: flux_dims, w: flux_single_weights, dx, x_bstride: int, vec, rope, saved, saved_bytes: int,
+                    grads: flux_single_grads, dvec, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_single_bwd(C.byref(dims), C.byref(w), ptr(dx), x_bstride, ptr(vec), ptr(rope), ptr(saved),
+                                 saved_bytes, C.byref(grads), ptr(dvec), ptr(workspace), workspace_bytes,
+                                 _stream(stream)), "flux_single_bwd")
+
+
+def flux_attention_train_workspace_bytes(batch: int, seq: int, heads: int) -> int:
+    return lib().flux_attention_train_workspace_bytes(batch, seq, heads)
+
+
+def flux_attention_fwd_train(batch: int, seq: int, heads: int, q, k, v, ld: int, o, ldo: int, lse, workspace,
+                             workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_attention_fwd_train(batch, seq, heads, ptr(q), ptr(k), ptr(v), ld, ptr(o), ldo, ptr(lse),
+                                          ptr(workspace), workspace_bytes, _stream(stream)), "flux_attention_fwd_train")
+
+
+def flux_attention_bwd(batch: int, seq: int, heads: int, q, k, v, ld: int, o, dout, ldo: int, lse, dqkv, workspace,
+                       workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_attention_bwd(batch, seq, heads, ptr(q), ptr(k), ptr(v), ld, ptr(o), ptr(dout), ldo, ptr(lse),
+                                    ptr(dqkv), ptr(workspace), workspace_bytes, _stream(stream)), "flux_attention_bwd")

@@ -466,6 +466,82 @@ size_t flux_attention_workspace_bytes(int32_t precision, int32_t batch, int32_t 
                                       int32_t head_dim);
 
 /*
+ * Training: the backward pass of the blocks under the rectified-flow
+ * objective ("Flux architecture deep dive", Flow matching framework: the
+ * velocity MSE is backpropagated through the network; the gradients follow
+ * from the forward definitions of the double and single blocks by the chain
+ * rule).  Training runs with precision FLUX_PREC_BF16, weights_f16 = 0 and
+ * head_dim 128 (anything else: FLUX_ERR_UNSUPPORTED): bf16 activations and
+ * weights on the bf16 MFMA, fp32 accumulation, fp32 residual stream and fp32
+ * gradients.
+ *
+ * A training forward computes the same block output as flux_block_fwd /
+ * flux_single_fwd (up to the rounding of its bf16 activations) and keeps in
+ * `saved` (caller-allocated, 256-byte aligned, flux_train_saved_bytes(dims,
+ * op) bytes; op 0 double block, 1 single block) everything its backward
+ * reads: the residual before each half, the modulation vectors, the
+ * LayerNorm-modulate outputs, the linear outputs before GELU and before each
+ * gate, the attention operands, output and per-query log-sum-exp.
+ *
+ * A backward takes the gradient of the objective with respect to the
+ * block's output, in the residual buffers (d_img / d_txt, or dx; same layout
+ * and strides as the forward's residual), and overwrites it in place with
+ * the gradient with respect to the block's input.  It writes (=) every
+ * parameter gradient into the caller's fp32 buffers (same shapes as the
+ * weights: W [out, in], b [out], norm scales [head_dim]) and ADDS (+=) the
+ * gradient with respect to vec into dvec [B, hidden] (several blocks share
+ * one vec).  `saved` must hold the training forward of the same block on the
+ * same inputs and weights; workspace: flux_bwd_workspace_bytes(dims, op)
+ * bytes, 256-byte aligned.  Sums over tokens run in a fixed order, so the
+ * results are bitwise repeatable.  Errors as elsewhere: checked on the host
+ * before anything is enqueued.
+ */
+typedef struct {
+  float *mod_w, *mod_b, *qkv_w, *qkv_b, *q_norm, *k_norm, *proj_w, *proj_b, *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+} flux_stream_grads;
+typedef struct {
+  float *mod_w, *mod_b, *lin1_w, *lin1_b, *q_norm, *k_norm, *lin2_w, *lin2_b;
+} flux_single_grads;
+
+size_t flux_train_saved_bytes(const flux_dims* dims, int32_t op);
+size_t flux_bwd_workspace_bytes(const flux_dims* dims, int32_t op);
+flux_status flux_block_fwd_train(const flux_dims* dims, const flux_stream_weights* img_w,
+                                 const flux_stream_weights* txt_w, float* img, int64_t img_batch_stride, float* txt,
+                                 int64_t txt_batch_stride, const float* vec, const float* rope, void* saved,
+                                 size_t saved_bytes, void* stream);
+flux_status flux_block_bwd(const flux_dims* dims, const flux_stream_weights* img_w, const flux_stream_weights* txt_w,
+                           float* d_img, int64_t img_batch_stride, float* d_txt, int64_t txt_batch_stride,
+                           const float* vec, const float* rope, const void* saved, size_t saved_bytes,
+                           const flux_stream_grads* img_grads, const flux_stream_grads* txt_grads, float* dvec,
+                           void* workspace, size_t workspace_bytes, void* stream);
+flux_status flux_single_fwd_train(const flux_dims* dims, const flux_single_weights* w, float* x,
+                                  int64_t x_batch_stride, const float* vec, const float* rope, void* saved,
+                                  size_t saved_bytes, void* stream);
+flux_status flux_single_bwd(const flux_dims* dims, const flux_single_weights* w, float* dx, int64_t x_batch_stride,
+                            const float* vec, const float* rope, const void* saved, size_t saved_bytes,
+                            const flux_single_grads* grads, float* dvec, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Softmax attention alone, training form (bf16, head_dim 128, no mask):
+ * q, k, v, o, dout bf16 [B, seq, heads*128] token rows (q, k, v with row
+ * stride ld; o and dout with row stride ldo).  flux_attention_fwd_train
+ * writes o and lse [B, heads, round_up(seq, 256)] fp32 (log2-domain
+ * log-sum-exp of the scaled scores per query).  flux_attention_bwd
+ * recomputes the probabilities from q, k and lse and writes dq | dk | dv as
+ * bf16 [B, seq, 3*heads*128] (dq at column 0, dk at heads*128, dv at
+ * 2*heads*128).  Workspace: flux_attention_train_workspace_bytes bytes,
+ * 256-byte aligned, for either call.
+ */
+size_t flux_attention_train_workspace_bytes(int32_t batch, int32_t seq, int32_t heads);
+flux_status flux_attention_fwd_train(int32_t batch, int32_t seq, int32_t heads, const void* q, const void* k,
+                                     const void* v, int64_t ld, void* o, int64_t ldo, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+flux_status flux_attention_bwd(int32_t batch, int32_t seq, int32_t heads, const void* q, const void* k, const void* v,
+                               int64_t ld, const void* o, const void* dout, int64_t ldo, const float* lse, void* dqkv,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing (diagnostics, off by default).  While enabled, each kernel
  * launch made by the library is bracketed by two hipEvents recorded on that
  * launch's stream.  flux_timing_read waits for the recorded events, writes
