@@ -775,7 +775,7 @@ attn_bwd_dq_kernel(AttnBwdArgs a) {
 }
 
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t stream) {
-  const double L = a.seq, work = 4.0 * a.batch * a.heads * L * L * 128.0;   // per product of L x L x Dh
+  const double L = a.seq, work = 4.0 * a.batch * a.heads * L * L * 128.0;   // two products of L x L x Dh
   {
     TimingScope ts(kKcBwdElem, stream, (double)a.batch * a.seq * a.heads * 128.0 * 8.0);
     hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)(a.seq_pad / 64), (unsigned)a.heads, (unsigned)a.batch),
@@ -784,15 +784,15 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(a.seq_pad / 128), (unsigned)a.heads, (unsigned)a.batch);
+  // algorithmic work: five L x L x Dh products (S recomputed, dP, dV, dK, dQ),
+  // 2.5 times the forward's two; the dQ kernel's second S and dP are overhead
   {
-    // S, dP, dV, dK: four L x L x Dh products
     TimingScope ts(kKcAttnBwd, stream, 2.0 * work);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // S, dP, dQ: three more
-  TimingScope ts(kKcAttnBwd, stream, 1.5 * work);
+  TimingScope ts(kKcAttnBwd, stream, 0.5 * work);
   hipLaunchKernelGGL(attn_bwd_dq_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

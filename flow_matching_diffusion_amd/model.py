@@ -310,3 +310,46 @@ class FluxModel(BlockStack):
                               guidance=cfg_w if cfg else 1.0, z_model=o["z_t"], copies=2 if cfg else 1,
                               t_model=o["t"], t_model_n=Bm)
         return o
+
+
+class BlockPairTrainer:
+    """Training forward and backward of one double block followed by one
+    single block over the joint [B, L_img + L_txt, D] residual (bf16, head_dim
+    128): the training forwards keep their activations in `saved` buffers,
+    the backwards turn the output gradient into the input gradient in place
+    and write every parameter gradient (fp32, keyed like the weights) and the
+    vec gradient (accumulated into dvec)."""
+
+    def __init__(self, wl: synth.Workload, w2: Dict[str, object], w1: Dict[str, object], device="cuda"):
+        self.wl = wl
+        self.dims = F.dims_for(wl)
+        self.w2 = upload_weights(w2, True, device)
+        self.w1 = upload_weights(w1, True, device)
+        self.iw, self.tw = F.stream_weights(self.w2, "img"), F.stream_weights(self.w2, "txt")
+        self.sw = F.single_weights(self.w1)
+        nb = [F.flux_train_saved_bytes(self.dims, op) for op in (0, 1)]
+        if min(nb) == 0:
+            raise F.FluxError(F.FLUX_ERR_UNSUPPORTED, "BlockPairTrainer", F.lib().flux_last_error().decode())
+        self.saved = [torch.empty(n, dtype=torch.uint8, device=device) for n in nb]
+        self.ws_bytes = max(F.flux_bwd_workspace_bytes(self.dims, op) for op in (0, 1))
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.g2 = {k: torch.empty(tuple(v.shape), dtype=torch.float32, device=device) for k, v in self.w2.items()}
+        self.g1 = {k: torch.empty(tuple(v.shape), dtype=torch.float32, device=device) for k, v in self.w1.items()}
+        self.gi, self.gt = F.stream_grads(self.g2, "img"), F.stream_grads(self.g2, "txt")
+        self.gs = F.single_grads(self.g1)
+
+    def forward(self, x: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor) -> None:
+        wl = self.wl
+        L, D = wl.seq, wl.hidden
+        txt = x.data_ptr() + wl.l_img * D * 4
+        F.flux_block_fwd_train(self.dims, self.iw, self.tw, x, L * D, txt, L * D, vec, rope, self.saved[0],
+                               self.saved[0].numel())
+        F.flux_single_fwd_train(self.dims, self.sw, x, L * D, vec, rope, self.saved[1], self.saved[1].numel())
+
+    def backward(self, d: torch.Tensor, vec: torch.Tensor, rope: torch.Tensor, dvec: torch.Tensor) -> None:
+        wl = self.wl
+        L, D = wl.seq, wl.hidden
+        F.flux_single_bwd(self.dims, self.sw, d, L * D, vec, rope, self.saved[1], self.saved[1].numel(), self.gs,
+                          dvec, self.ws, self.ws_bytes)
+        F.flux_block_bwd(self.dims, self.iw, self.tw, d, L * D, d.data_ptr() + wl.l_img * D * 4, L * D, vec, rope,
+                         self.saved[0], self.saved[0].numel(), self.gi, self.gt, dvec, self.ws, self.ws_bytes)

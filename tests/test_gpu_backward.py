@@ -239,3 +239,64 @@ def test_train_rejects_unsupported():
     d = f.dims_for(synth.custom_workload("bwd_f32", base="tiny_fp32", hidden=256, heads=2, head_dim=128,
                                          mlp_hidden=512, axes_dim=(16, 56, 56)))
     assert f.flux_bwd_workspace_bytes(d, 1) == 0
+
+
+# ------------------------- full Flux-12B block shapes ------------------------- #
+def _pair_at_full_size(zero_mod):
+    from flow_matching_diffusion_amd.model import BlockPairTrainer
+    wl = synth.WORKLOADS["flux12b_blocks"]
+    B, L, D = wl.batch, wl.seq, wl.hidden
+    tr = BlockPairTrainer(wl, synth.device_block_weights(wl, 0, "double", zero_mod=zero_mod),
+                          synth.device_block_weights(wl, 1, "single", zero_mod=zero_mod))
+    g = torch.Generator(device="cuda").manual_seed(99)
+    x_in = torch.randn((B, L, D), generator=g, device="cuda")
+    d_out = torch.randn((B, L, D), generator=g, device="cuda")
+    vec = torch.randn((B, D), generator=g, device="cuda")
+    rope = torch.empty((B, L, 64, 2), dtype=torch.float32, device="cuda")
+    F().flux_rope_table(torch.from_numpy(synth.joint_ids(wl)).cuda(), B, L, wl.axes_dim, wl.theta, rope)
+
+    def run():
+        x, d, dvec = x_in.clone(), d_out.clone(), torch.zeros_like(vec)
+        tr.forward(x, vec, rope)
+        tr.backward(d, vec, rope, dvec)
+        torch.cuda.synchronize()
+        return x, d, dvec, {k: v.clone() for k, v in {**tr.g2, **{"s_" + k: v for k, v in tr.g1.items()}}.items()}
+
+    return tr, x_in, d_out, run
+
+
+def test_pair_backward_flux12b_adaln_zero_identity():
+    # every shift, scale and gate is zero: both blocks are the identity, so the
+    # input gradient equals the output gradient bit for bit, every gradient
+    # below the gates is exactly zero, and so is the vec gradient (zero
+    # modulation weights); the gate rows of the modulation bias gradient are
+    # the column sums of y * dout and do not vanish
+    _say("block pair training forward + backward, Flux-12B shapes (L=4608), adaLN-zero")
+    tr, x_in, d_out, run = _pair_at_full_size(True)
+    x, d, dvec, g = run()
+    assert torch.equal(x, x_in)
+    assert torch.equal(d, d_out)
+    assert bool((dvec == 0).all())
+    D = tr.wl.hidden
+    for k, v in g.items():
+        if k.endswith("mod.w") or k.endswith("mod.b"):
+            continue
+        assert bool((v == 0).all()), k
+    for k in ("img_mod.b", "txt_mod.b"):
+        gate_rows = torch.cat([g[k][2 * D:3 * D], g[k][5 * D:]])
+        assert bool(torch.isfinite(g[k]).all()) and float(gate_rows.abs().max()) > 0, k
+        assert bool((g[k][:2 * D] == 0).all()), k
+    assert float(g["s_mod.b"][2 * D:].abs().max()) > 0 and bool((g["s_mod.b"][:2 * D] == 0).all())
+
+
+def test_pair_backward_flux12b_repeatable_and_finite():
+    _say("block pair training forward + backward, Flux-12B shapes (L=4608): two runs bit-identical, finite")
+    tr, x_in, d_out, run = _pair_at_full_size(False)
+    a = run()
+    b = run()
+    for u, v in zip(a[:3], b[:3]):
+        assert torch.equal(u, v)
+        assert bool(torch.isfinite(u).all())
+    for k in a[3]:
+        assert torch.equal(a[3][k], b[3][k]), k
+        assert bool(torch.isfinite(a[3][k]).all()) and float(a[3][k].abs().max()) > 0, k
