@@ -124,23 +124,50 @@ __global__ void __launch_bounds__(256) colsum_partial_kernel(ColsumArgs a) {
   *reinterpret_cast<float4*>(a.part + ((int64_t)z * a.nrb + rb) * a.C + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
-// out[z * out_zstride + c] (=, += or += silu'(aux[z][c]) *) sum_p part[(z * np + p) * pstride + c]
-__global__ void __launch_bounds__(256) reduce_parts_kernel(ReduceArgs a) {
+// Partials of sample z sit at part + z * zs + i * ps (i < np).  The sum runs
+// as a fixed tree: chunks of kRedChunk partials are summed in place (into the
+// chunk's first slot) until at most kRedChunk remain, then the last pass
+// writes out[z * out_zstride + c] (=, += or += silu'(aux[z][c]) *) the sum.
+constexpr int kRedChunk = 16;
+
+__global__ void __launch_bounds__(256) reduce_chunks_kernel(float* part, int np, int64_t ps, int64_t zs, int C) {
+  const int c = blockIdx.x * 256 + threadIdx.x, k = blockIdx.y, z = blockIdx.z;
+  if (c >= C) return;
+  float* base = part + (int64_t)z * zs + c;
+  const int i0 = k * kRedChunk, i1 = min(np, i0 + kRedChunk);
+  float s = 0.f;
+  for (int i = i0; i < i1; ++i) s += base[(int64_t)i * ps];
+  base[(int64_t)i0 * ps] = s;
+}
+
+__global__ void __launch_bounds__(256) reduce_parts_kernel(ReduceArgs a, int np, int64_t ps, int64_t zs) {
   const int c = blockIdx.x * 256 + threadIdx.x, z = blockIdx.y;
   if (c >= a.C) return;
   float s = 0.f;
-  const int64_t ps = a.pstride ? a.pstride : a.C;
-  const float* p = a.part + (int64_t)z * a.np * ps + c;
-  for (int i = 0; i < a.np; ++i) s += p[(int64_t)i * ps];
+  const float* p = a.part + (int64_t)z * zs + c;
+  for (int i = 0; i < np; ++i) s += p[(int64_t)i * ps];
   float* o = a.out + (int64_t)z * a.out_zstride + c;
   if (a.mode == 0) *o = s;
   else if (a.mode == 1) *o += s;
   else *o += s * silu_grad_f(a.aux[(int64_t)z * a.aux_zstride + c]);
 }
 
+// note: overwrites the partials (scratch)
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   TimingScope ts(kKcBwdElem, stream, 4.0 * a.Z * (double)a.C * (a.np + 1));
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)ceil_div(a.C, 256), (unsigned)a.Z), dim3(256), 0, stream, a);
+  int np = a.np;
+  int64_t ps = a.pstride ? a.pstride : a.C;
+  const int64_t zs = (int64_t)a.np * ps;
+  float* part = const_cast<float*>(a.part);
+  while (np > kRedChunk) {
+    const int nch = (int)ceil_div(np, kRedChunk);
+    hipLaunchKernelGGL(reduce_chunks_kernel, dim3((unsigned)ceil_div(a.C, 256), (unsigned)nch, (unsigned)a.Z),
+                       dim3(256), 0, stream, part, np, ps, zs, a.C);
+    np = nch;
+    ps *= kRedChunk;
+  }
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)ceil_div(a.C, 256), (unsigned)a.Z), dim3(256), 0, stream, a,
+                     np, ps, zs);
   return hipGetLastError();
 }
 
@@ -822,15 +849,25 @@ __global__ void __launch_bounds__(256) mod_dw_kernel(ModBwdArgs a) {
 
 template <typename TW>
 __global__ void __launch_bounds__(256) mod_dvec_partial_kernel(ModBwdArgs a) {
-  const int c = blockIdx.x * 256 + threadIdx.x, rc = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4, rc = blockIdx.y;
   if (c >= a.K) return;
   const int r0 = rc * a.rpc, r1 = min(a.N, r0 + a.rpc);
   const TW* W = reinterpret_cast<const TW*>(a.w);
   for (int b = 0; b < a.batch; ++b) {
-    float s = 0.f;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
     const float* g = a.dm + (int64_t)b * a.dm_bstride;
-    for (int r = r0; r < r1; ++r) s += load_f32(W + (int64_t)r * a.K + c) * g[r];
-    a.part[((int64_t)b * gridDim.y + rc) * a.K + c] = s;
+    for (int r = r0; r < r1; ++r) {
+      const float gr = g[r];
+      if constexpr (sizeof(TW) == 4) {
+        const float4 w = *reinterpret_cast<const float4*>(W + (int64_t)r * a.K + c);
+        s[0] += w.x * gr; s[1] += w.y * gr; s[2] += w.z * gr; s[3] += w.w * gr;
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(W + (int64_t)r * a.K + c);
+        s[0] += __uint_as_float(w.x << 16) * gr; s[1] += __uint_as_float(w.x & 0xffff0000u) * gr;
+        s[2] += __uint_as_float(w.y << 16) * gr; s[3] += __uint_as_float(w.y & 0xffff0000u) * gr;
+      }
+    }
+    *reinterpret_cast<float4*>(a.part + ((int64_t)b * gridDim.y + rc) * a.K + c) = make_float4(s[0], s[1], s[2], s[3]);
   }
 }
 
@@ -849,7 +886,7 @@ hipError_t launch_mod_bwd(ModBwdArgs a, int w_dtype, hipStream_t stream) {
   a.rpc = (int)ceil_div(a.N, nrc);
   {
     TimingScope ts(kKcBwdElem, stream, (double)a.batch * a.N * a.K * (w_dtype == kF32 ? 4.0 : 2.0));
-    const dim3 grid((unsigned)ceil_div(a.K, 256), (unsigned)nrc);
+    const dim3 grid((unsigned)ceil_div(a.K, 1024), (unsigned)nrc);
     if (w_dtype == kF32) hipLaunchKernelGGL(mod_dvec_partial_kernel<float>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(mod_dvec_partial_kernel<bf16_t>, grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();

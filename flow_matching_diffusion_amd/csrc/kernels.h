@@ -167,6 +167,7 @@ struct ReduceArgs {
   int32_t mode;                          // 0 store, 1 add, 2 add times SiLU'(aux)
   const float* aux; int64_t aux_zstride;
 };
+// the partials are scratch: the fixed-order tree sums them in place
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 
 enum EwOp : int { kEwGateBwd = 0, kEwGeluBwd = 1, kEwGelu = 2, kEwGateAdd = 3 };
@@ -232,7 +233,7 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t stream);
 
 // adaLN modulation backward: m = W SiLU(vec) + b, W [N, K] (weight dtype),
 // dm [B, N] (row stride dm_bstride).  dw [N, K], db [N] written; dvec [B, K]
-// += SiLU'(vec) * W^T dm.  part: scratch of batch * nrc * K floats.
+// += SiLU'(vec) * W^T dm.  part: scratch of batch * nrc * K floats; K % 4 == 0.
 struct ModBwdArgs {
   const void* w; const float* vec; const float* dm; int64_t dm_bstride;
   float* dw; float* db; float* dvec;

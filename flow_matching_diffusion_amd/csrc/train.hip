@@ -111,7 +111,7 @@ AttnWs attn_ws(Carve& c, int64_t B, int64_t H, int64_t Lp) {
 }
 
 constexpr int kColParts = 64;    // row partials of a column sum
-constexpr int kModParts = 64;    // row chunks of the modulation GEMV transpose
+constexpr int kModParts = 256;   // row chunks of the modulation GEMV transpose
 
 struct Parts {
   float* col; float* ln_sh; float* ln_sc; float* prep; float* mod;
