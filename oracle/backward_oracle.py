@@ -30,12 +30,14 @@ from typing import Dict, Tuple
 import numpy as np
 from scipy.special import erf as _erf
 
-from .flux_oracle import (_heads, adaln, apply_rope, attention_probs, f64, gelu, layernorm, linear, modulate,
-                          rmsnorm, silu)
+from .flux_oracle import (_heads, adaln, apply_rope, attention_probs, double_block, f64, final_layer, gelu, layernorm,
+                          linear, modulate, patchify, rf_loss, rf_noise, rmsnorm, rope_angles, silu, single_block,
+                          timestep_embedding)
 
 __all__ = [
     "rf_loss_grad", "linear_vjp", "silu_grad", "gelu_grad", "modulate_vjp", "rmsnorm_vjp", "rope_vjp",
-    "attention_vjp", "adaln_vjp", "single_block_vjp", "double_block_vjp",
+    "attention_vjp", "adaln_vjp", "single_block_vjp", "double_block_vjp", "final_layer_vjp", "conditioning_vjp",
+    "flux_train_vjp",
 ]
 
 
@@ -223,3 +225,85 @@ def double_block_vjp(x_img, x_txt, vec, angles, w: Dict[str, np.ndarray], heads:
         dv_s, g[s + "_mod.w"], g[s + "_mod.b"] = adaln_vjp(vec, w[s + "_mod.w"], _cat(dm[s]))
         dvec = dvec + dv_s
     return dx["img"], dx["txt"], dvec, g
+
+
+def final_layer_vjp(x_img, vec, w: Dict[str, np.ndarray], eps: float, dv):
+    """Gradients of flux_oracle.final_layer (AdaLNContinuous, Linear D -> C,
+    unpatchify) for the velocity gradient dv [B, C, H, W].  unpatchify is a
+    permutation, so its transpose is patchify.  Returns (dx_img, dvec, grads)."""
+    x_img = f64(x_img)
+    shift, scale = adaln(vec, w["final_mod.w"], w["final_mod.b"], 2)
+    h = modulate(x_img, shift, scale, eps)
+    g: Dict[str, np.ndarray] = {}
+    dh, g["final_out.w"], g["final_out.b"] = linear_vjp(h, w["final_out.w"], patchify(dv))
+    dx, dsh, dsc = modulate_vjp(x_img, shift, scale, dh, eps)
+    dvec, g["final_mod.w"], g["final_mod.b"] = adaln_vjp(vec, w["final_mod.w"], _cat([dsh, dsc]))
+    return dx, dvec, g
+
+
+def conditioning_vjp(t, y, w: Dict[str, np.ndarray], dvec, model_channels: int = 256) -> Dict[str, np.ndarray]:
+    """Gradients of the two Linear -> SiLU -> Linear embedders of
+    flux_oracle.conditioning_vector (time, and the pooled vector when y is
+    given) for the vec gradient dvec [B, D]."""
+    g: Dict[str, np.ndarray] = {}
+    pairs = [("time_in", timestep_embedding(t, model_channels))]
+    if y is not None:
+        pairs.append(("vector_in", f64(y)))
+    for name, e in pairs:
+        a1 = linear(e, w[name + "1.w"], w[name + "1.b"])
+        ds1, g[name + "2.w"], g[name + "2.b"] = linear_vjp(silu(a1), w[name + "2.w"], dvec)
+        _, g[name + "1.w"], g[name + "1.b"] = linear_vjp(e, w[name + "1.w"], ds1 * silu_grad(a1))
+    return g
+
+
+def flux_train_vjp(z0, z1, t, txt, y, ids, emb_w: Dict[str, np.ndarray], double_ws, single_ws, heads: int,
+                   axes_dim, theta: float, eps: float = 1e-6, model_channels: int = 256):
+    """One rectified-flow training step of the model of flux_oracle.flux_forward
+    (fused single blocks, no guidance embedding): z_t = (1 - t) z0 + t z1, the
+    velocity prediction, J = mean((v_pred - (z1 - z0))^2), then the gradient of
+    J with respect to every weight.  Returns (J, emb_grads, [double grads],
+    [single grads])."""
+    z_t, _ = rf_noise(z0, z1, t)
+    _, _, hh, ww = z_t.shape
+    patches = patchify(z_t)
+    x_img = linear(patches, emb_w["img_in.w"], emb_w["img_in.b"])
+    has_txt_in = "txt_in.w" in emb_w
+    x_txt = linear(txt, emb_w["txt_in.w"], emb_w["txt_in.b"]) if has_txt_in else f64(txt)
+    e = timestep_embedding(t, model_channels)
+    vec = linear(silu(linear(e, emb_w["time_in1.w"], emb_w["time_in1.b"])), emb_w["time_in2.w"], emb_w["time_in2.b"])
+    if y is not None:
+        vec = vec + linear(silu(linear(y, emb_w["vector_in1.w"], emb_w["vector_in1.b"])),
+                           emb_w["vector_in2.w"], emb_w["vector_in2.b"])
+    angles = rope_angles(ids, axes_dim, theta)
+    l_img = x_img.shape[1]
+    d_in = []
+    for w in double_ws:
+        d_in.append((x_img, x_txt))
+        x_img, x_txt = double_block(x_img, x_txt, vec, angles, w, heads, eps)
+    x = np.concatenate([x_img, x_txt], axis=1)
+    s_in = []
+    for w in single_ws:
+        s_in.append(x)
+        x = single_block(x, vec, angles, w, heads, eps)
+    v_pred = final_layer(x[:, :l_img], vec, emb_w, hh, ww, eps)
+    loss, _ = rf_loss(v_pred, z0, z1)
+
+    dv = rf_loss_grad(v_pred, z0, z1)
+    dx_img, dvec, g_emb = final_layer_vjp(x[:, :l_img], vec, emb_w, eps, dv)
+    dx = np.zeros_like(x)
+    dx[:, :l_img] = dx_img
+    g_single = [None] * len(single_ws)
+    for i in reversed(range(len(single_ws))):
+        dx, dv_b, g_single[i] = single_block_vjp(s_in[i], vec, angles, single_ws[i], heads, eps, dx)
+        dvec = dvec + dv_b
+    d_img, d_txt = dx[:, :l_img], dx[:, l_img:]
+    g_double = [None] * len(double_ws)
+    for i in reversed(range(len(double_ws))):
+        xi, xt = d_in[i]
+        d_img, d_txt, dv_b, g_double[i] = double_block_vjp(xi, xt, vec, angles, double_ws[i], heads, eps, d_img, d_txt)
+        dvec = dvec + dv_b
+    _, g_emb["img_in.w"], g_emb["img_in.b"] = linear_vjp(patches, emb_w["img_in.w"], d_img)
+    if has_txt_in:
+        _, g_emb["txt_in.w"], g_emb["txt_in.b"] = linear_vjp(txt, emb_w["txt_in.w"], d_txt)
+    g_emb.update(conditioning_vjp(t, y, emb_w, dvec, model_channels))
+    return loss, g_emb, g_double, g_single

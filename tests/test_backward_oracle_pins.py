@@ -184,3 +184,73 @@ def test_block_vjp_adaln_zero():
     for n in ("lin1.w", "lin1.b", "lin2.w", "lin2.b", "q_norm", "k_norm"):
         assert np.all(g[n] == 0.0), n
     assert np.abs(g["mod.b"][2 * D:]).max() > 0 and np.all(g["mod.b"][:2 * D] == 0.0)
+
+
+# --------------------------- head, embeddings, step --------------------------- #
+C_LAT, HH, WW, CTX, YD, MC = 4, 2, 3, 12, 10, 16
+
+
+def _emb_w(rng, with_y=True, with_txt=True):
+    s, w = 0.3, {}
+    shapes = {"img_in": (D, C_LAT), "time_in1": (D, MC), "time_in2": (D, D), "final_mod": (2 * D, D),
+              "final_out": (C_LAT, D)}
+    if with_y:
+        shapes.update({"vector_in1": (D, YD), "vector_in2": (D, D)})
+    if with_txt:
+        shapes["txt_in"] = (D, CTX)
+    for n, shp in shapes.items():
+        w[n + ".w"] = rng.standard_normal(shp) * s
+        w[n + ".b"] = rng.standard_normal(shp[0]) * s
+    return w
+
+
+def test_final_layer_vjp():
+    rng = np.random.default_rng(10)
+    w = _emb_w(rng)
+    x, vec = rng.standard_normal((B, HH * WW, D)), rng.standard_normal((B, D))
+    dv = rng.standard_normal((B, C_LAT, HH, WW))
+    dx, dvec, g = G.final_layer_vjp(x, vec, w, 1e-6, dv)
+    fwd = lambda xx=x, vv=vec, ww=w: O.final_layer(xx, vv, ww, HH, WW, 1e-6)
+    _dir_check(lambda t: fwd(xx=t), x, dx, dv, rng)
+    _dir_check(lambda t: fwd(vv=t), vec, dvec, dv, rng)
+    for n in ("final_mod.w", "final_mod.b", "final_out.w", "final_out.b"):
+        _dir_check(lambda t: fwd(ww=dict(w, **{n: t})), w[n], g[n], dv, rng)
+
+
+def test_conditioning_vjp():
+    rng = np.random.default_rng(11)
+    w = _emb_w(rng)
+    t, y = rng.uniform(size=B), rng.standard_normal((B, YD))
+    dvec = rng.standard_normal((B, D))
+    g = G.conditioning_vjp(t, y, w, dvec, MC)
+    assert set(g) == {"time_in1.w", "time_in1.b", "time_in2.w", "time_in2.b", "vector_in1.w", "vector_in1.b",
+                      "vector_in2.w", "vector_in2.b"}
+    for n in g:
+        _dir_check(lambda u: O.conditioning_vector(t, y, dict(w, **{n: u}), MC), w[n], g[n], dvec, rng)
+
+
+def test_flux_train_vjp():
+    # the gradient of the whole step's loss with respect to every weight group,
+    # along random directions, against central differences of the forward loss
+    rng = np.random.default_rng(12)
+    w_emb = _emb_w(rng)
+    w2, w1 = _double_w(rng), _single_w(rng)
+    z0, z1 = rng.standard_normal((B, C_LAT, HH, WW)), rng.standard_normal((B, C_LAT, HH, WW))
+    t = rng.uniform(0.05, 0.95, size=B)
+    txt, y = rng.standard_normal((B, LT, CTX)), rng.standard_normal((B, YD))
+    ids = np.concatenate([np.stack([np.zeros((B, HH * WW)), np.repeat(np.arange(HH), WW)[None].repeat(B, 0),
+                                    np.tile(np.arange(WW), HH)[None].repeat(B, 0)], -1), np.zeros((B, LT, 3))], 1)
+    loss, g_emb, g2, g1 = G.flux_train_vjp(z0, z1, t, txt, y, ids, w_emb, [w2], [w1], H, AXES, 1e4, 1e-6, MC)
+
+    def J(we=w_emb, a=w2, b=w1):
+        v = O.flux_forward(O.rf_noise(z0, z1, t)[0], txt, y, t, ids, we, [a], [b], H, AXES, 1e4, 1e-6, MC)
+        return np.array(O.rf_loss(v, z0, z1)[0])
+
+    assert abs(loss - float(J())) <= 1e-12 * max(1.0, abs(loss))
+    assert set(g_emb) == set(w_emb)
+    for n in w_emb:
+        _dir_check(lambda u: J(we=dict(w_emb, **{n: u})), w_emb[n], g_emb[n], 1.0, rng)
+    for n in ("img_qkv.w", "txt_fc2.b", "img_q_norm", "txt_mod.w"):
+        _dir_check(lambda u: J(a=dict(w2, **{n: u})), w2[n], g2[0][n], 1.0, rng)
+    for n in ("lin1.w", "k_norm", "mod.b"):
+        _dir_check(lambda u: J(b=dict(w1, **{n: u})), w1[n], g1[0][n], 1.0, rng)
