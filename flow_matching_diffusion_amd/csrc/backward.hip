@@ -149,7 +149,8 @@ __global__ void __launch_bounds__(256) reduce_parts_kernel(ReduceArgs a, int np,
   float* o = a.out + (int64_t)z * a.out_zstride + c;
   if (a.mode == 0) *o = s;
   else if (a.mode == 1) *o += s;
-  else *o += s * silu_grad_f(a.aux[(int64_t)z * a.aux_zstride + c]);
+  else if (a.mode == 2) *o += s * silu_grad_f(a.aux[(int64_t)z * a.aux_zstride + c]);
+  else *o = s * silu_grad_f(a.aux[(int64_t)z * a.aux_zstride + c]);
 }
 
 // note: overwrites the partials (scratch)
@@ -839,7 +840,11 @@ __global__ void __launch_bounds__(256) mod_dw_kernel(ModBwdArgs a) {
     for (int b = 0; b < a.batch; ++b) {
       const float g = a.dm[(int64_t)b * a.dm_bstride + r];
       const float4 v = *reinterpret_cast<const float4*>(a.vec + (int64_t)b * a.K + c);
-      s[0] += g * silu_f(v.x); s[1] += g * silu_f(v.y); s[2] += g * silu_f(v.z); s[3] += g * silu_f(v.w);
+      if (a.silu_in) {
+        s[0] += g * silu_f(v.x); s[1] += g * silu_f(v.y); s[2] += g * silu_f(v.z); s[3] += g * silu_f(v.w);
+      } else {
+        s[0] += g * v.x; s[1] += g * v.y; s[2] += g * v.z; s[3] += g * v.w;
+      }
       sb += g;
     }
     *reinterpret_cast<float4*>(a.dw + (int64_t)r * a.K + c) = make_float4(s[0], s[1], s[2], s[3]);
@@ -882,6 +887,7 @@ hipError_t launch_mod_bwd(ModBwdArgs a, int w_dtype, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!a.dvec) return hipSuccess;   // no input gradient wanted
   const int nrc = a.nrc;
   a.rpc = (int)ceil_div(a.N, nrc);
   {
@@ -894,8 +900,31 @@ hipError_t launch_mod_bwd(ModBwdArgs a, int w_dtype, hipStream_t stream) {
   }
   ReduceArgs r{};
   r.part = a.part; r.np = nrc; r.C = a.K; r.Z = a.batch;
-  r.out = a.dvec; r.out_zstride = a.K; r.mode = 2; r.aux = a.vec; r.aux_zstride = a.K;
+  r.out = a.dvec; r.out_zstride = a.K; r.mode = a.dvec_store ? 3 : 2; r.aux = a.vec; r.aux_zstride = a.K;
   return launch_reduce(r, stream);
+}
+
+// ===========================================================================
+// Gradient of the velocity MSE J = mean((v_pred - (z1 - z0))^2) over all
+// n elements: dv = (2 / n) (v_pred - v*), v* = z1 - z0 rounded to fp32 as
+// the forward's target.
+// ===========================================================================
+__global__ void __launch_bounds__(256) rf_loss_grad_kernel(const float* v, const float* z0, const float* z1, float* dv,
+                                                           int64_t n, float c) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float tgt = z1[i] - z0[i];
+    dv[i] = c * (v[i] - tgt);
+  }
+}
+
+hipError_t launch_rf_loss_grad(const float* v, const float* z0, const float* z1, float* dv, int64_t n,
+                               hipStream_t stream) {
+  int64_t blocks = ceil_div(n > 0 ? n : 1, 256);
+  if (blocks > 4096) blocks = 4096;
+  TimingScope ts(kKcRf, stream, 16.0 * (double)n);
+  hipLaunchKernelGGL(rf_loss_grad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, v, z0, z1, dv, n,
+                     (float)(2.0 / (double)n));
+  return hipGetLastError();
 }
 
 }  // namespace flux

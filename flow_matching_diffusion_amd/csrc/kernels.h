@@ -164,7 +164,7 @@ struct ReduceArgs {
   const float* part; int32_t np; int32_t C; int32_t Z;
   int64_t pstride;                       // floats from one partial to the next (0: C)
   float* out; int64_t out_zstride;
-  int32_t mode;                          // 0 store, 1 add, 2 add times SiLU'(aux)
+  int32_t mode;                          // 0 store, 1 add, 2 add times SiLU'(aux), 3 store times SiLU'(aux)
   const float* aux; int64_t aux_zstride;
 };
 // the partials are scratch: the fixed-order tree sums them in place
@@ -236,11 +236,17 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t stream);
 // += SiLU'(vec) * W^T dm.  part: scratch of batch * nrc * K floats; K % 4 == 0.
 struct ModBwdArgs {
   const void* w; const float* vec; const float* dm; int64_t dm_bstride;
-  float* dw; float* db; float* dvec;
+  float* dw; float* db; float* dvec;     // dvec may be NULL (no input gradient)
   int32_t N, K, batch, nrc, rpc;
+  int32_t silu_in;                       // 1: m = W SiLU(vec) + b; 0: m = W vec + b (dW only, dvec must be NULL)
+  int32_t dvec_store;                    // 1: dvec = instead of +=
   float* part;
 };
 hipError_t launch_mod_bwd(ModBwdArgs a, int w_dtype, hipStream_t stream);
+
+// dv = (2 / n) (v - (z1 - z0)) over n fp32 elements (velocity MSE gradient)
+hipError_t launch_rf_loss_grad(const float* v, const float* z0, const float* z1, float* dv, int64_t n,
+                               hipStream_t stream);
 
 // ------------------------------ small kernels ------------------------------
 hipError_t launch_rope_table(const float* ids, int batch, int seq, const int32_t axes[3], float theta,

@@ -255,6 +255,7 @@ hipError_t mod_bwd(const void* w, const float* vec, const float* dm, int64_t N, 
   a.w = w; a.vec = vec; a.dm = dm; a.dm_bstride = N;
   a.dw = dw; a.db = db; a.dvec = dvec;
   a.N = (int32_t)N; a.K = (int32_t)D; a.batch = (int32_t)B; a.nrc = kModParts;
+  a.silu_in = 1;
   a.part = p.mod;
   return launch_mod_bwd(a, kBF16, st);
 }
@@ -764,6 +765,213 @@ flux_status flux_attention_bwd(int32_t batch, int32_t seq, int32_t heads, const 
   pb.batch = batch; pb.seq = seq; pb.seq_pad = (int)Lp; pb.heads = heads; pb.l_img = seq;
   pb.part = part;
   FLUX_HIP(launch_prep_bwd(pb, st), "token-major gradients");
+  return FLUX_OK;
+}
+
+
+// ------------------- loss, output head and embeddings -------------------
+flux_status flux_rf_loss_grad(int32_t batch, int64_t n_per_sample, const float* v_pred, const float* z0,
+                              const float* z1, float* dv, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(batch >= 1 && n_per_sample >= 1, "batch and n_per_sample must be >= 1");
+  REQUIRE(v_pred && z0 && z1 && dv, "v_pred, z0, z1 and dv are required");
+  FLUX_HIP(launch_rf_loss_grad(v_pred, z0, z1, dv, (int64_t)batch * n_per_sample, static_cast<hipStream_t>(stream)),
+           "loss gradient");
+  return FLUX_OK;
+}
+
+namespace {
+struct FinalBwdWs {
+  float* mod; void* h; void* dtok; void* dtokT; void* hT; void* woT; float* dh; float* dm; Parts pt;
+  size_t bytes;
+};
+FinalBwdWs final_bwd_ws(int64_t B, int64_t C, int64_t HW, int64_t D, void* base) {
+  Carve c(base);
+  FinalBwdWs w{};
+  const int64_t T = B * HW, Tp = tok_pad(T);
+  w.mod = static_cast<float*>(c.take(B * 2 * D * 4));
+  w.h = c.take(T * D * 2);
+  w.dtok = c.take(T * C * 2);
+  w.dtokT = c.take(C * Tp * 2);
+  w.hT = c.take(D * Tp * 2);
+  w.woT = c.take(D * C * 2);
+  w.dh = static_cast<float*>(c.take(T * D * 4));
+  w.dm = static_cast<float*>(c.take(B * 2 * D * 4));
+  w.pt.col = static_cast<float*>(c.take(kColParts * (C > D ? C : D) * 4));
+  const int64_t ln_parts = B * ln_bwd_blocks((int)HW, (int)B) * 4 * D;
+  w.pt.ln_sh = static_cast<float*>(c.take(ln_parts * 4));
+  w.pt.ln_sc = static_cast<float*>(c.take(ln_parts * 4));
+  w.pt.mod = static_cast<float*>(c.take(B * kModParts * D * 4));
+  w.bytes = (size_t)round_up((int64_t)c.off, 256);
+  return w;
+}
+
+struct EmbedBwdWs {
+  void* tok; void* tokT; void* dT; void* txtT; float* emb; float* a1; float* da1; Parts pt;
+  size_t bytes;
+};
+EmbedBwdWs embed_bwd_ws(int64_t B, int64_t C, int64_t HW, int64_t Lt, int64_t ctx, int64_t D, void* base) {
+  Carve c(base);
+  EmbedBwdWs w{};
+  const int64_t Ti = tok_pad(B * HW), Tt = tok_pad(B * (Lt > 0 ? Lt : 1));
+  const int64_t Tm = Ti > Tt ? Ti : Tt;
+  w.tok = c.take(B * HW * C * 2);
+  w.tokT = c.take(C * Ti * 2);
+  w.dT = c.take(D * Tm * 2);
+  w.txtT = c.take((ctx > 0 ? ctx : 1) * Tt * 2);
+  w.emb = static_cast<float*>(c.take(B * 256 * 4));
+  w.a1 = static_cast<float*>(c.take(B * D * 4));
+  w.da1 = static_cast<float*>(c.take(B * D * 4));
+  w.pt.col = static_cast<float*>(c.take(kColParts * D * 4));
+  w.pt.mod = static_cast<float*>(c.take(B * kModParts * D * 4));
+  w.bytes = (size_t)round_up((int64_t)c.off, 256);
+  return w;
+}
+}  // namespace
+
+size_t flux_final_bwd_workspace_bytes(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t hidden) {
+  if (batch < 1 || channels < 1 || height < 1 || width < 1 || hidden < 1) return 0;
+  return final_bwd_ws(batch, channels, (int64_t)height * width, hidden, nullptr).bytes;
+}
+
+flux_status flux_final_bwd(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t hidden, float eps,
+                           const void* mod_w, const void* mod_b, const void* out_w, const float* x_img,
+                           int64_t bstride, const float* vec, const float* dv, float* dx_img, float* dvec,
+                           float* g_mod_w, float* g_mod_b, float* g_out_w, float* g_out_b, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(batch >= 1 && channels >= 1 && height >= 1 && width >= 1, "sizes must be >= 1");
+  if (hidden % 256 != 0 || hidden > 4096)
+    return fail(FLUX_ERR_UNSUPPORTED, "hidden %d unsupported (a multiple of 256, at most 4096)", hidden);
+  if (channels % 64 != 0) return fail(FLUX_ERR_UNSUPPORTED, "channels must be a multiple of 64 (got %d)", channels);
+  REQUIRE(eps > 0.f, "eps must be positive");
+  const void* req[] = {mod_w, mod_b, out_w, x_img, vec, dv, dx_img, dvec, g_mod_w, g_mod_b, g_out_w, g_out_b};
+  for (const void* p : req) REQUIRE(p && aligned16(p), "every pointer is required, 16-byte aligned");
+  const int64_t B = batch, C = channels, HW = (int64_t)height * width, D = hidden, T = B * HW, Tp = tok_pad(T);
+  REQUIRE(bstride >= HW * D && bstride % 4 == 0, "bstride too small or not a multiple of 4");
+  flux_status s = check_workspace(workspace, workspace_bytes, final_bwd_ws(B, C, HW, D, nullptr).bytes);
+  if (s != FLUX_OK) return s;
+  const FinalBwdWs w = final_bwd_ws(B, C, HW, D, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const RowMap xm = rmap(bstride, D, HW), rowsD = rmap(T * D, D, T), rowsC = rmap(T * C, C, T), none = rmap(0, 1, 1);
+  GemvBatch gv{};
+  gv.count = 1;
+  gv.p[0] = gemv_problem(mod_w, mod_b, (int)(2 * D), (int)D, vec, D, w.mod, 2 * D, 1, 0);
+  FLUX_HIP(run_gemv(gv, (int)B, kBF16, st), "final modulation GEMV");
+  LnArgs la{};
+  la.count = 1; la.dim = (int)D; la.eps = eps;
+  la.s[0].x = x_img; la.s[0].xmap = xm;
+  la.s[0].out = w.h; la.s[0].omap = rmap(HW * D, D, HW);
+  la.s[0].shift = w.mod; la.s[0].scale = w.mod + D; la.s[0].mod_bstride = 2 * D;
+  la.s[0].rows = (int32_t)T;
+  FLUX_HIP(launch_ln_mod(la, kBF16, st), "final LayerNorm-modulate");
+  FLUX_HIP(launch_patchify(dv, (int)B, (int)C, (int)HW, w.dtok, kBF16, st), "velocity gradient tokens");
+  FLUX_HIP(colsum(w.dtok, kBF16, rowsC, nullptr, none, T, C, 1, g_out_b, 0, w.pt.col, st), "output bias gradient");
+  FLUX_HIP(transpose_rows(out_w, kBF16, rmap(C * D, D, C), C, D, w.woT, C, st), "W_out^T");
+  FLUX_HIP(transpose_rows(w.dtok, kBF16, rowsC, T, C, w.dtokT, Tp, st), "dtok^T");
+  FLUX_HIP(transpose_rows(w.h, kBF16, rowsD, T, D, w.hT, Tp, st), "h^T");
+  GemmBatch g{};
+  g.count = 1;
+  g.p[0] = bf16_problem(w.dtok, rowsC, w.woT, nullptr, T, D, C, w.dh, rowsD, true);
+  FLUX_HIP(launch_gemm(g, kBF16, st), "output data gradient");
+  g.p[0] = bf16_problem(w.dtokT, rmap(C * Tp, Tp, C), w.hT, nullptr, C, D, Tp, g_out_w, rmap(C * D, D, C), true);
+  FLUX_HIP(launch_gemm(g, kBF16, st), "output weight gradient");
+  FLUX_HIP(ln_bwd(x_img, xm, w.dh, rowsD, dx_img, xm, w.mod + D, 2 * D, w.dm, w.dm + D, HW, B, D, eps, w.pt, st),
+           "final LayerNorm-modulate backward");
+  FLUX_HIP(mod_bwd(mod_w, vec, w.dm, 2 * D, D, B, g_mod_w, g_mod_b, dvec, w.pt, st), "final modulation backward");
+  return FLUX_OK;
+}
+
+size_t flux_embed_bwd_workspace_bytes(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t l_txt,
+                                      int32_t ctx_dim, int32_t hidden) {
+  if (batch < 1 || channels < 1 || height < 1 || width < 1 || hidden < 1 || l_txt < 0 || ctx_dim < 0) return 0;
+  return embed_bwd_ws(batch, channels, (int64_t)height * width, l_txt, ctx_dim, hidden, nullptr).bytes;
+}
+
+flux_status flux_embed_bwd(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t l_txt,
+                           int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
+                           const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
+                           const float* y, const float* d_img, int64_t img_bstride, const float* d_txt,
+                           int64_t txt_bstride, const float* dvec, const flux_embed_grads* g, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(batch >= 1 && channels >= 1 && height >= 1 && width >= 1 && hidden >= 1, "sizes must be >= 1");
+  REQUIRE(w && g && w->img_in_w && w->time_in1_w && w->time_in1_b && w->time_in2_w && w->time_in2_b,
+          "image and time embedder weights and the gradient struct are required");
+  REQUIRE(z_t && t && d_img && dvec && aligned16(z_t) && aligned16(d_img) && aligned16(dvec),
+          "z_t, t, d_img and dvec are required (16-byte aligned)");
+  REQUIRE(time_dim >= 8 && time_dim % 8 == 0 && time_dim <= 256, "time_dim must be a multiple of 8 in [8, 256]");
+  if (channels % 64 != 0) return fail(FLUX_ERR_UNSUPPORTED, "channels must be a multiple of 64 (got %d)", channels);
+  REQUIRE(hidden % 8 == 0 && hidden <= 4096, "hidden must be a multiple of 8, at most 4096");
+  const int64_t B = batch, C = channels, HW = (int64_t)height * width, D = hidden;
+  REQUIRE(img_bstride >= HW * D && img_bstride % 4 == 0, "img_bstride too small or not a multiple of 4");
+  const bool has_txt = w->txt_in_w != nullptr, has_y = w->vector_in1_w != nullptr;
+  float* const gp[] = {g->img_in_w, g->img_in_b, g->time_in1_w, g->time_in1_b, g->time_in2_w, g->time_in2_b};
+  for (float* p : gp) REQUIRE(p && aligned16(p), "gradient pointers must be non-NULL and 16-byte aligned");
+  if (has_txt) {
+    REQUIRE(txt && d_txt && l_txt >= 1 && ctx_dim >= 1 && g->txt_in_w && g->txt_in_b, "txt_in needs txt, d_txt and its gradients");
+    if (ctx_dim % 64 != 0) return fail(FLUX_ERR_UNSUPPORTED, "ctx_dim must be a multiple of 64");
+    REQUIRE(txt_bstride >= (int64_t)l_txt * D && txt_bstride % 4 == 0, "txt_bstride too small");
+    REQUIRE(aligned16(txt) && aligned16(d_txt) && aligned16(g->txt_in_w) && aligned16(g->txt_in_b),
+            "pointers must be 16-byte aligned");
+  }
+  if (has_y)
+    REQUIRE(y && y_dim >= 8 && y_dim % 8 == 0 && w->vector_in2_w && g->vector_in1_w && g->vector_in1_b &&
+                g->vector_in2_w && g->vector_in2_b,
+            "vector_in needs y (y_dim a multiple of 8) and its gradients");
+  const int64_t Lt = has_txt ? l_txt : 0, ctx = has_txt ? ctx_dim : 0;
+  flux_status s = check_workspace(workspace, workspace_bytes, embed_bwd_ws(B, C, HW, Lt, ctx, D, nullptr).bytes);
+  if (s != FLUX_OK) return s;
+  const EmbedBwdWs ws = embed_bwd_ws(B, C, HW, Lt, ctx, D, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const RowMap none = rmap(0, 1, 1);
+  const int64_t Ti = tok_pad(B * HW);
+  // image input linear: dW = d_img^T patchify(z_t), db = sum d_img
+  FLUX_HIP(launch_patchify(z_t, (int)B, (int)C, (int)HW, ws.tok, kBF16, st), "patchify");
+  FLUX_HIP(transpose_rows(ws.tok, kBF16, rmap(B * HW * C, C, B * HW), B * HW, C, ws.tokT, Ti, st), "tokens^T");
+  FLUX_HIP(transpose_rows(d_img, kF32, rmap(img_bstride, D, HW), B * HW, D, ws.dT, Ti, st), "d_img^T");
+  GemmBatch gb{};
+  gb.count = 1;
+  gb.p[0] = bf16_problem(ws.dT, rmap(D * Ti, Ti, D), ws.tokT, nullptr, D, C, Ti, g->img_in_w, rmap(D * C, C, D), true);
+  FLUX_HIP(launch_gemm(gb, kBF16, st), "image input weight gradient");
+  FLUX_HIP(colsum(d_img, kF32, rmap(img_bstride, D, HW), nullptr, none, B * HW, D, 1, g->img_in_b, 0, ws.pt.col, st),
+           "image input bias gradient");
+  if (has_txt) {
+    const int64_t Tt = tok_pad(B * Lt);
+    FLUX_HIP(transpose_rows(txt, kBF16, rmap(Lt * ctx, ctx, Lt), B * Lt, ctx, ws.txtT, Tt, st), "txt^T");
+    FLUX_HIP(transpose_rows(d_txt, kF32, rmap(txt_bstride, D, Lt), B * Lt, D, ws.dT, Tt, st), "d_txt^T");
+    gb.p[0] = bf16_problem(ws.dT, rmap(D * Tt, Tt, D), ws.txtT, nullptr, D, ctx, Tt, g->txt_in_w,
+                           rmap(D * ctx, ctx, D), true);
+    FLUX_HIP(launch_gemm(gb, kBF16, st), "text input weight gradient");
+    FLUX_HIP(colsum(d_txt, kF32, rmap(txt_bstride, D, Lt), nullptr, none, B * Lt, D, 1, g->txt_in_b, 0, ws.pt.col,
+                    st), "text input bias gradient");
+  }
+  // embedders: vec += W2 SiLU(W1 e + b1) + b2, e the timestep sinusoid or y
+  FLUX_HIP(launch_timestep_embed(t, (int)B, time_dim, 1000.f, 10000.f, ws.emb, st), "timestep sinusoid");
+  auto mlp_bwd = [&](const void* w1, const void* b1, const void* w2, const float* e, int64_t K, float* g1w, float* g1b,
+                     float* g2w, float* g2b) -> flux_status {
+    GemvBatch gv{};
+    gv.count = 1;
+    gv.p[0] = gemv_problem(w1, b1, (int)D, (int)K, e, K, ws.a1, D, 0, 0);
+    FLUX_HIP(run_gemv(gv, (int)B, kBF16, st), "embedder layer 1");
+    ModBwdArgs a{};
+    a.w = w2; a.vec = ws.a1; a.dm = dvec; a.dm_bstride = D; a.dw = g2w; a.db = g2b; a.dvec = ws.da1;
+    a.N = (int32_t)D; a.K = (int32_t)D; a.batch = (int32_t)B; a.nrc = kModParts; a.silu_in = 1; a.dvec_store = 1;
+    a.part = ws.pt.mod;
+    FLUX_HIP(launch_mod_bwd(a, kBF16, st), "embedder layer 2 backward");
+    ModBwdArgs b{};
+    b.w = w1; b.vec = e; b.dm = ws.da1; b.dm_bstride = D; b.dw = g1w; b.db = g1b; b.dvec = nullptr;
+    b.N = (int32_t)D; b.K = (int32_t)K; b.batch = (int32_t)B; b.nrc = kModParts; b.silu_in = 0;
+    b.part = ws.pt.mod;
+    FLUX_HIP(launch_mod_bwd(b, kBF16, st), "embedder layer 1 backward");
+    return FLUX_OK;
+  };
+  if ((s = mlp_bwd(w->time_in1_w, w->time_in1_b, w->time_in2_w, ws.emb, time_dim, g->time_in1_w, g->time_in1_b,
+                   g->time_in2_w, g->time_in2_b)) != FLUX_OK)
+    return s;
+  if (has_y && (s = mlp_bwd(w->vector_in1_w, w->vector_in1_b, w->vector_in2_w, y, y_dim, g->vector_in1_w,
+                            g->vector_in1_b, g->vector_in2_w, g->vector_in2_b)) != FLUX_OK)
+    return s;
   return FLUX_OK;
 }
 

@@ -43,7 +43,8 @@ EXPORTED = (
     "flux_mx_scale_bytes", "flux_mx_quantize", "flux_mxfp8_linear_fwd", "flux_fp8_quantize_current",
     "flux_train_saved_bytes", "flux_bwd_workspace_bytes", "flux_block_fwd_train", "flux_block_bwd",
     "flux_single_fwd_train", "flux_single_bwd", "flux_attention_train_workspace_bytes", "flux_attention_fwd_train",
-    "flux_attention_bwd",
+    "flux_attention_bwd", "flux_rf_loss_grad", "flux_final_bwd_workspace_bytes", "flux_final_bwd",
+    "flux_embed_bwd_workspace_bytes", "flux_embed_bwd",
 )
 
 
@@ -85,6 +86,12 @@ class flux_stream_grads(C.Structure):
 class flux_single_grads(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("mod_w", "mod_b", "lin1_w", "lin1_b", "q_norm", "k_norm", "lin2_w",
                                           "lin2_b")]
+
+
+class flux_embed_grads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("img_in_w", "img_in_b", "txt_in_w", "txt_in_b", "time_in1_w",
+                                          "time_in1_b", "time_in2_w", "time_in2_b", "vector_in1_w",
+                                          "vector_in1_b", "vector_in2_w", "vector_in2_b")]
 
 
 class rf_args(C.Structure):
@@ -152,6 +159,11 @@ def lib() -> C.CDLL:
                             vp, sz, vp],
         "flux_attention_fwd_train": [i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp],
         "flux_attention_bwd": [i32, i32, i32, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, sz, vp],
+        "flux_rf_loss_grad": [i32, i64, vp, vp, vp, vp, vp],
+        "flux_final_bwd": [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                           vp],
+        "flux_embed_bwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp, vp,
+                           i64, vp, i64, vp, P(flux_embed_grads), vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -177,6 +189,10 @@ def lib() -> C.CDLL:
     L.flux_bwd_workspace_bytes.restype = sz
     L.flux_attention_train_workspace_bytes.argtypes = [i32, i32, i32]
     L.flux_attention_train_workspace_bytes.restype = sz
+    L.flux_final_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.flux_final_bwd_workspace_bytes.restype = sz
+    L.flux_embed_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.flux_embed_bwd_workspace_bytes.restype = sz
     L.flux_status_string.argtypes = [C.c_int]
     L.flux_status_string.restype = C.c_char_p
     L.flux_last_error.argtypes = []
@@ -285,6 +301,14 @@ def single_grads(g: Dict[str, object]) -> flux_single_grads:
         setattr(s, f + "_b", ptr(g[f + ".b"]))
     s.q_norm = ptr(g["q_norm"])
     s.k_norm = ptr(g["k_norm"])
+    return s
+
+
+def embed_grads(g: Dict[str, object]) -> flux_embed_grads:
+    s = flux_embed_grads()
+    for f in ("img_in", "txt_in", "time_in1", "time_in2", "vector_in1", "vector_in2"):
+        setattr(s, f + "_w", ptr(g.get(f + ".w")))
+        setattr(s, f + "_b", ptr(g.get(f + ".b")))
     return s
 
 
@@ -528,3 +552,33 @@ def flux_attention_bwd(batch: int, seq: int, heads: int, q, k, v, ld: int, o, do
                        workspace_bytes: int, stream=None) -> None:
     _check(lib().flux_attention_bwd(batch, seq, heads, ptr(q), ptr(k), ptr(v), ld, ptr(o), ptr(dout), ldo, ptr(lse),
                                     ptr(dqkv), ptr(workspace), workspace_bytes, _stream(stream)), "flux_attention_bwd")
+
+
+def flux_rf_loss_grad(batch: int, n_per_sample: int, v_pred, z0, z1, dv, stream=None) -> None:
+    _check(lib().flux_rf_loss_grad(batch, n_per_sample, ptr(v_pred), ptr(z0), ptr(z1), ptr(dv), _stream(stream)),
+           "flux_rf_loss_grad")
+
+
+def flux_final_bwd_workspace_bytes(batch, channels, height, width, hidden) -> int:
+    return lib().flux_final_bwd_workspace_bytes(batch, channels, height, width, hidden)
+
+
+def flux_final_bwd(batch, channels, height, width, hidden, eps, mod_w, mod_b, out_w, x_img, bstride, vec, dv, dx_img,
+                   dvec, g_mod_w, g_mod_b, g_out_w, g_out_b, workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().flux_final_bwd(batch, channels, height, width, hidden, eps, ptr(mod_w), ptr(mod_b), ptr(out_w),
+                                ptr(x_img), bstride, ptr(vec), ptr(dv), ptr(dx_img), ptr(dvec), ptr(g_mod_w),
+                                ptr(g_mod_b), ptr(g_out_w), ptr(g_out_b), ptr(workspace), workspace_bytes,
+                                _stream(stream)), "flux_final_bwd")
+
+
+def flux_embed_bwd_workspace_bytes(batch, channels, height, width, l_txt, ctx_dim, hidden) -> int:
+    return lib().flux_embed_bwd_workspace_bytes(batch, channels, height, width, l_txt, ctx_dim, hidden)
+
+
+def flux_embed_bwd(batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim, w: flux_embed_weights,
+                   z_t, txt, t, y, d_img, img_bstride, d_txt, txt_bstride, dvec, grads: flux_embed_grads, workspace,
+                   workspace_bytes, stream=None) -> None:
+    _check(lib().flux_embed_bwd(batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim, C.byref(w),
+                                ptr(z_t), ptr(txt), ptr(t), ptr(y), ptr(d_img), img_bstride, ptr(d_txt), txt_bstride,
+                                ptr(dvec), C.byref(grads), ptr(workspace), workspace_bytes, _stream(stream)),
+           "flux_embed_bwd")

@@ -353,3 +353,97 @@ class BlockPairTrainer:
                           dvec, self.ws, self.ws_bytes)
         F.flux_block_bwd(self.dims, self.iw, self.tw, d, L * D, d.data_ptr() + wl.l_img * D * 4, L * D, vec, rope,
                          self.saved[0], self.saved[0].numel(), self.gi, self.gt, dvec, self.ws, self.ws_bytes)
+
+
+class FluxTrainer:
+    """One rectified-flow training step of a whole (bf16, head_dim 128) model:
+    noising, input embeddings, double blocks, single blocks (fused form) and
+    the output head with their training forwards, the velocity MSE, then the
+    backward in reverse order -- the loss gradient, the head, every block and
+    the embeddings -- leaving the fp32 gradient of every weight in `grads`
+    (embeddings and head), `g_double[i]` and `g_single[i]`.  The guidance
+    embedding is not part of the step."""
+
+    def __init__(self, wl: synth.Workload, emb_w: Dict[str, object], double_ws, single_ws, device="cuda"):
+        self.wl, self.device = wl, device
+        B, C, D = wl.batch, wl.latent_ch, wl.hidden
+        self.dims = F.dims_for(wl)
+        self.emb = upload_weights(emb_w, True, device)
+        self.estruct = F.embed_weights(self.emb)
+        self.dw = [upload_weights(w, True, device) for w in double_ws]
+        self.sw = [upload_weights(w, True, device) for w in single_ws]
+        self.dstructs = [(F.stream_weights(w, "img"), F.stream_weights(w, "txt")) for w in self.dw]
+        self.sstructs = [F.single_weights(w) for w in self.sw]
+        f32 = dict(dtype=torch.float32, device=device)
+        grad = lambda w: {k: torch.empty(tuple(v.shape), **f32) for k, v in w.items()}
+        self.grads = grad({k: v for k, v in self.emb.items() if not k.startswith("guidance_in")})
+        self.g_double = [grad(w) for w in self.dw]
+        self.g_single = [grad(w) for w in self.sw]
+        self.gstructs = ([(F.stream_grads(g, "img"), F.stream_grads(g, "txt")) for g in self.g_double],
+                         [F.single_grads(g) for g in self.g_single])
+        self.egrads = F.embed_grads(self.grads)
+        saved = lambda op: torch.empty(F.flux_train_saved_bytes(self.dims, op), dtype=torch.uint8, device=device)
+        self.saved_d = [saved(0) for _ in self.dw]
+        self.saved_s = [saved(1) for _ in self.sw]
+        ctx = wl.context_dim or 0
+        self.ws_bytes = max(F.flux_bwd_workspace_bytes(self.dims, 0), F.flux_bwd_workspace_bytes(self.dims, 1),
+                            F.flux_embed_workspace_bytes(F.FLUX_PREC_BF16, B, C, wl.img_h, wl.img_w, D),
+                            F.flux_final_workspace_bytes(F.FLUX_PREC_BF16, B, wl.img_h, wl.img_w, D),
+                            F.flux_rf_workspace_bytes(B, C * wl.l_img),
+                            F.flux_final_bwd_workspace_bytes(B, C, wl.img_h, wl.img_w, D),
+                            F.flux_embed_bwd_workspace_bytes(B, C, wl.img_h, wl.img_w, wl.l_txt, ctx, D))
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        shp = (B, C, wl.img_h, wl.img_w)
+        self.o = {"z_t": torch.empty(shp, **f32), "v_target": torch.empty(shp, **f32),
+                  "v_pred": torch.empty(shp, **f32), "dv": torch.empty(shp, **f32),
+                  "x": torch.empty((B, wl.seq, D), **f32), "d": torch.empty((B, wl.seq, D), **f32),
+                  "vec": torch.empty((B, D), **f32), "dvec": torch.empty((B, D), **f32),
+                  "loss": torch.empty((1,), **f32), "loss_per_sample": torch.empty((B,), **f32)}
+        self.rope = None
+
+    def step(self, z0, z1, t, txt, y, ids) -> torch.Tensor:
+        """Returns the loss (a device tensor); gradients land in the grad dicts."""
+        wl, o, ws = self.wl, self.o, self.ws
+        B, C, D, L, Li = wl.batch, wl.latent_ch, wl.hidden, wl.seq, wl.l_img
+        n = C * Li
+        bf = F.FLUX_PREC_BF16
+        if self.rope is None:
+            self.rope = torch.empty((B, L, wl.head_dim // 2, 2), dtype=torch.float32, device=self.device)
+            F.flux_rope_table(ids, B, L, wl.axes_dim, wl.theta, self.rope)
+        x, d, vec, dvec = o["x"], o["d"], o["vec"], o["dvec"]
+        txt_ptr = x.data_ptr() + Li * D * 4
+        d_txt_ptr = d.data_ptr() + Li * D * 4
+        has_txt_in = "txt_in.w" in self.emb
+        F.rf_noise_loss(B, n, z0, z1, t, z_t=o["z_t"], v_target=o["v_target"])
+        if not has_txt_in:
+            x[:, Li:].copy_(txt)
+        F.flux_embed_fwd(bf, B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
+                         wl.vec_in_dim or 0, self.estruct, o["z_t"], txt if has_txt_in else None, t, y, x, L * D,
+                         txt_ptr if has_txt_in else None, L * D, vec, ws, self.ws_bytes)
+        for (iw, tw), sv in zip(self.dstructs, self.saved_d):
+            F.flux_block_fwd_train(self.dims, iw, tw, x, L * D, txt_ptr, L * D, vec, self.rope, sv, sv.numel())
+        for sw, sv in zip(self.sstructs, self.saved_s):
+            F.flux_single_fwd_train(self.dims, sw, x, L * D, vec, self.rope, sv, sv.numel())
+        e = self.emb
+        F.flux_final_fwd(bf, B, C, wl.img_h, wl.img_w, D, wl.eps, e["final_mod.w"], e["final_mod.b"], e["final_out.w"],
+                         e["final_out.b"], x, L * D, vec, o["v_pred"], ws, self.ws_bytes)
+        F.rf_noise_loss(B, n, z0, z1, t, v_pred=o["v_pred"], loss=o["loss"], loss_per_sample=o["loss_per_sample"],
+                        workspace=ws, workspace_bytes=self.ws_bytes)
+        # backward
+        F.flux_rf_loss_grad(B, n, o["v_pred"], z0, z1, o["dv"])
+        d.zero_()
+        dvec.zero_()
+        g = self.grads
+        F.flux_final_bwd(B, C, wl.img_h, wl.img_w, D, wl.eps, e["final_mod.w"], e["final_mod.b"], e["final_out.w"], x,
+                         L * D, vec, o["dv"], d, dvec, g["final_mod.w"], g["final_mod.b"], g["final_out.w"],
+                         g["final_out.b"], ws, self.ws_bytes)
+        dstr, sstr = self.gstructs
+        for sw, sv, gs in reversed(list(zip(self.sstructs, self.saved_s, sstr))):
+            F.flux_single_bwd(self.dims, sw, d, L * D, vec, self.rope, sv, sv.numel(), gs, dvec, ws, self.ws_bytes)
+        for (iw, tw), sv, (gi, gt) in reversed(list(zip(self.dstructs, self.saved_d, dstr))):
+            F.flux_block_bwd(self.dims, iw, tw, d, L * D, d_txt_ptr, L * D, vec, self.rope, sv, sv.numel(), gi, gt,
+                             dvec, ws, self.ws_bytes)
+        F.flux_embed_bwd(B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
+                         wl.vec_in_dim or 0, self.estruct, o["z_t"], txt if has_txt_in else None, t, y, d, L * D,
+                         d_txt_ptr if has_txt_in else None, L * D, dvec, self.egrads, ws, self.ws_bytes)
+        return o["loss"]

@@ -523,6 +523,44 @@ flux_status flux_single_bwd(const flux_dims* dims, const flux_single_weights* w,
                             void* stream);
 
 /*
+ * The rest of a rectified-flow training step (bf16 weights):
+ * flux_rf_loss_grad writes dv = 2 (v_pred - (z1 - z0)) / N, the gradient of
+ * the velocity MSE over all N = batch * n_per_sample elements, fp32.
+ * flux_final_bwd differentiates the output head of flux_final_fwd (its
+ * AdaLN modulation and LayerNorm-modulate are recomputed from x_img and vec):
+ * it ADDS the image-row input gradient into dx_img (rows like x_img) and the
+ * vec gradient into dvec, and writes the fp32 gradients of the head's
+ * weights.  flux_embed_bwd writes (=) the fp32 gradients of the image and
+ * text input linears and of the time and pooled-vector embedders, given the
+ * gradients d_img, d_txt of the embedded token rows and dvec of the
+ * conditioning vector; the guidance embedding is not differentiated.
+ * channels and ctx_dim multiples of 64; workspaces from the *_bytes calls,
+ * 256-byte aligned.
+ */
+typedef struct {
+  float *img_in_w, *img_in_b, *txt_in_w, *txt_in_b, *time_in1_w, *time_in1_b, *time_in2_w, *time_in2_b;
+  float *vector_in1_w, *vector_in1_b, *vector_in2_w, *vector_in2_b;
+} flux_embed_grads;
+
+flux_status flux_rf_loss_grad(int32_t batch, int64_t n_per_sample, const float* v_pred, const float* z0,
+                              const float* z1, float* dv, void* stream);
+size_t flux_final_bwd_workspace_bytes(int32_t batch, int32_t channels, int32_t height, int32_t width,
+                                      int32_t hidden);
+flux_status flux_final_bwd(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t hidden, float eps,
+                           const void* mod_w, const void* mod_b, const void* out_w, const float* x_img,
+                           int64_t bstride, const float* vec, const float* dv, float* dx_img, float* dvec,
+                           float* g_mod_w, float* g_mod_b, float* g_out_w, float* g_out_b, void* workspace,
+                           size_t workspace_bytes, void* stream);
+size_t flux_embed_bwd_workspace_bytes(int32_t batch, int32_t channels, int32_t height, int32_t width,
+                                      int32_t l_txt, int32_t ctx_dim, int32_t hidden);
+flux_status flux_embed_bwd(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t l_txt,
+                           int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
+                           const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
+                           const float* y, const float* d_img, int64_t img_batch_stride, const float* d_txt,
+                           int64_t txt_batch_stride, const float* dvec, const flux_embed_grads* grads,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Softmax attention alone, training form (bf16, head_dim 128, no mask):
  * q, k, v, o, dout bf16 [B, seq, heads*128] token rows (q, k, v with row
  * stride ld; o and dout with row stride ldo).  flux_attention_fwd_train

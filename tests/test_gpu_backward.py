@@ -300,3 +300,41 @@ def test_pair_backward_flux12b_repeatable_and_finite():
     for k in a[3]:
         assert torch.equal(a[3][k], b[3][k]), k
         assert bool(torch.isfinite(a[3][k]).all()) and float(a[3][k].abs().max()) > 0, k
+
+
+# ------------------------------ whole training step ------------------------------ #
+STEP_WL = {
+    # text and pooled-vector embedders present, ragged text, B = 2
+    "embedders": synth.custom_workload("step_embedders", base="flux535m", batch=2, hidden=256, heads=2, head_dim=128,
+                                       mlp_hidden=512, img_h=6, img_w=8, l_txt=11, context_dim=128, vec_in_dim=64),
+    # text at hidden width, no pooled vector (the block-pair bench's model)
+    "plain": synth.custom_workload("step_plain", base="flux535m", batch=1, hidden=256, heads=2, head_dim=128,
+                                   mlp_hidden=512, img_h=8, img_w=8, l_txt=16, context_dim=None, vec_in_dim=None),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_WL))
+def test_flux_train_step(name):
+    from flow_matching_diffusion_amd.model import FluxTrainer
+    wl = STEP_WL[name]
+    _say(f"whole training step {name}: noise, embeddings, double + single block, head, MSE, backward")
+    emb = synth.embed_weights(wl)
+    w2, w1 = synth.double_block_weights(wl, 0), synth.single_block_weights(wl, 1)
+    mi = synth.model_inputs(wl)
+    tr = FluxTrainer(wl, emb, [w2], [w1])
+    y = _dev(mi["y"]) if "y" in mi else None
+    loss = tr.step(_dev(mi["z0"]), _dev(mi["z1"]), _dev(mi["t"]), _dev(mi["txt"], wl.context_dim is not None), y,
+                   _dev(mi["ids"]))
+    torch.cuda.synchronize()
+    ref_loss, g_emb, g2, g1 = G.flux_train_vjp(mi["z0"], mi["z1"], mi["t"], mi["txt"], mi.get("y"), mi["ids"], emb, [w2],
+                                               [w1], wl.heads, wl.axes_dim, wl.theta, wl.eps, wl.model_channels)
+    got = float(loss.item())
+    print(f"    loss: gpu {got:.6f} oracle {ref_loss:.6f}", flush=True)
+    assert abs(got - ref_loss) <= 1e-2 * ref_loss
+    assert set(tr.grads) == set(g_emb)
+    for n in sorted(g_emb):
+        _close(tr.grads[n].cpu().numpy(), g_emb[n], "d " + n)
+    for n in sorted(w2):
+        _close(tr.g_double[0][n].cpu().numpy(), g2[0][n], "d double " + n)
+    for n in sorted(w1):
+        _close(tr.g_single[0][n].cpu().numpy(), g1[0][n], "d single " + n)
