@@ -326,41 +326,33 @@ def mx_linears_bench(args) -> int:
 
 
 def train_bench(args) -> int:
-    """Training step of the Flux-12B block pair at batch 1 (4096 image + 512
-    text tokens): the training forward of one double block and one single
-    block (activations kept), then their backward from a fixed synthetic
-    output gradient -- input, vec and every parameter gradient.  Weights are
-    drawn on the device; the residual input and output gradient are copied
-    into the working buffers inside every step."""
+    """One rectified-flow training step of the Flux-12B-shaped block-pair model
+    at batch 1 (4096 image + 512 text tokens): noising, image embedding and
+    conditioning vector, the training forward of one double and one single
+    block, the output head and the velocity MSE, then the backward of all of
+    it in reverse (loss gradient, head, single block, double block,
+    embeddings) -- every weight gradient.  Block weights are drawn on the
+    device; the other weights and the inputs come from the host streams."""
     import torch
 
     from flow_matching_diffusion_amd import flux as FX
     from flow_matching_diffusion_amd import synth
-    from flow_matching_diffusion_amd.model import BlockPairTrainer
+    from flow_matching_diffusion_amd.model import FluxTrainer, device_array
 
     torch.cuda.set_device(0)
     FX.lib()
     wl = synth.WORKLOADS["flux12b_blocks"]
-    B, L, D = wl.batch, wl.seq, wl.hidden
-    print(f"[bench] drawing weights for {wl.name} on the device", file=sys.stderr, flush=True)
-    tr = BlockPairTrainer(wl, synth.device_block_weights(wl, 0, "double"), synth.device_block_weights(wl, 1, "single"))
-    g = torch.Generator(device="cuda").manual_seed(4321)
-    x_in = torch.randn((B, L, D), generator=g, device="cuda", dtype=torch.float32)
-    d_out = torch.randn((B, L, D), generator=g, device="cuda", dtype=torch.float32)
-    vec = torch.randn((B, D), generator=g, device="cuda", dtype=torch.float32)
-    ids = torch.from_numpy(synth.joint_ids(wl)).cuda()
-    rope = torch.empty((B, L, wl.head_dim // 2, 2), dtype=torch.float32, device="cuda")
-    FX.flux_rope_table(ids, B, L, wl.axes_dim, wl.theta, rope)
-    x = torch.empty_like(x_in)
-    d = torch.empty_like(d_out)
-    dvec = torch.zeros_like(vec)
+    B, L, D, Li, C = wl.batch, wl.seq, wl.hidden, wl.l_img, wl.latent_ch
+    print(f"[bench] drawing weights for {wl.name}", file=sys.stderr, flush=True)
+    tr = FluxTrainer(wl, synth.embed_weights(wl), [synth.device_block_weights(wl, 0, "double")],
+                     [synth.device_block_weights(wl, 1, "single")])
+    mi = synth.model_inputs(wl)
+    dev = lambda a, bf=False: device_array(a, bf)
+    z0, z1, t, ids = dev(mi["z0"]), dev(mi["z1"]), dev(mi["t"]), dev(mi["ids"])
+    txt = dev(mi["txt"])
 
     def step():
-        x.copy_(x_in)
-        tr.forward(x, vec, rope)
-        d.copy_(d_out)
-        dvec.zero_()
-        tr.backward(d, vec, rope, dvec)
+        return tr.step(z0, z1, t, txt, None, ids)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -378,11 +370,11 @@ def train_bench(args) -> int:
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        step()
+        loss = step()
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
-    assert bool(torch.isfinite(d).all()) and bool(torch.isfinite(tr.g2["img_qkv.w"]).all())
+    assert bool(torch.isfinite(loss).all()) and bool(torch.isfinite(tr.g_double[0]["img_qkv.w"]).all())
     table = {}
     for name, (ms, n, work) in kernels.items():
         if n == 0:
@@ -395,29 +387,33 @@ def train_bench(args) -> int:
         else:
             ent["gbs"] = round(work / (ms * 1e-3) / 1e9, 1)
         table[name] = ent
-    # algorithmic FLOPs of the step: forward GEMMs, twice that for their data and weight gradients,
+    # algorithmic FLOPs: block GEMMs forward plus their data and weight gradients; the image input
+    # linear forward plus its weight gradient; the head linear forward, data and weight gradients;
     # attention forward (two L x L x Dh products per head) and backward (five)
-    fwd_gemm = 2.0 * B * L * D * D * (3 + 1 + 4 + 4 + 7 + 5)
+    blk = 2.0 * B * L * D * D * (3 + 1 + 4 + 4 + 7 + 5)
+    small = 2.0 * B * Li * C * D
     att = 4.0 * B * wl.heads * L * L * wl.head_dim
-    flops = 3.0 * fwd_gemm + 2 * att + 2 * 2.5 * att
+    flops = 3.0 * blk + 2.0 * small + 3.0 * small + 2 * att + 2 * 2.5 * att
     recorded = sum(w for nm, (ms, n, w) in kernels.items() if nm.startswith("gemm") or nm.startswith("attention"))
     assert abs(recorded / args.steps - flops) <= 1e-6 * flops, (recorded / args.steps, flops)
     dom = max((k for k in table if "tflops" in table[k]), key=lambda k: table[k]["ms_per_step"])
     peak = PEAK_BF16_TFLOPS
     rec = {
-        "metric": "MMDiT block pair training step tokens/s (training forward + backward, 512 txt + 4096 img, bf16)",
+        "metric": "MMDiT block pair rectified-flow training step tokens/s (forward + backward, 512 txt + 4096 img, "
+                  "bf16)",
         "value": round(B * L / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (device-drawn weights, N(0,1) input and output "
-                                                      "gradient)",
-        "config": {"workload": "flux12b_block_pair_train_step", "batch": B, "l_txt": wl.l_txt, "l_img": wl.l_img,
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (device-drawn block weights)",
+        "config": {"workload": "flux12b_block_pair_train_step", "batch": B, "l_txt": wl.l_txt, "l_img": Li,
                    "hidden": D, "heads": wl.heads, "head_dim": wl.head_dim, "mlp_hidden": wl.mlp_hidden,
                    "double_blocks": 1, "single_blocks": 1,
-                   "step": "double + single block training forward, then single + double block backward"},
+                   "step": "rf noise + embed + vec + double + single block training forwards + head + velocity "
+                           "MSE, then the backward of all of it (every weight gradient)"},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": table[dom]["tflops"], "peak": peak,
                      "unit": "TFLOP/s", "frac": round(table[dom]["tflops"] / peak, 4), "traffic": None,
                      "flops_per_launch": table[dom]["flops_per_launch"], "ms_per_launch": table[dom]["ms_per_launch"]},
         "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "loss": float(loss.item()),
         "kernels": table,
         "cpu_baseline": None,
     }
@@ -446,7 +442,8 @@ def main() -> int:
                          "classifier-free guidance (conditional + null-prompt rows in one batch-2 forward, "
                          "guidance embedding on) on the block-pair model; flux12b_mxfp8_linears: the six "
                          "token-path linears of the block pair at batch 4 as MXFP8 linears; "
-                         "flux12b_blocks_train: the block pair's training forward and backward at batch 1")
+                         "flux12b_blocks_train: a whole rectified-flow training step (forward and backward) of the "
+                         "block-pair model at batch 1")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
