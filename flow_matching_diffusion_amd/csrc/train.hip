@@ -320,9 +320,21 @@ flux_status check_grad_ptrs(float* const* ps, int n, const char* what) {
 
 extern "C" {
 
+// the sequential single block is a one-stream double block over all L tokens
+static flux_dims one_stream(const flux_dims* d) {
+  flux_dims one = *d;
+  one.l_img = d->l_img + d->l_txt;
+  one.l_txt = 0;
+  return one;
+}
+
 size_t flux_train_saved_bytes(const flux_dims* d, int32_t op) {
   if (check_train_dims(d) != FLUX_OK) return 0;
   if (op == 0) return block_saved(d, nullptr).bytes;
+  if (op == 2) {
+    const flux_dims one = one_stream(d);
+    return block_saved(&one, nullptr).bytes;
+  }
   if (op == 1) return single_saved(d, nullptr).bytes;
   return 0;
 }
@@ -330,6 +342,10 @@ size_t flux_train_saved_bytes(const flux_dims* d, int32_t op) {
 size_t flux_bwd_workspace_bytes(const flux_dims* d, int32_t op) {
   if (check_train_dims(d) != FLUX_OK) return 0;
   if (op == 0) return block_bwd_ws(d, nullptr).bytes;
+  if (op == 2) {
+    const flux_dims one = one_stream(d);
+    return block_bwd_ws(&one, nullptr).bytes;
+  }
   if (op == 1) return single_bwd_ws(d, nullptr).bytes;
   return 0;
 }
@@ -692,6 +708,27 @@ flux_status flux_block_bwd(const flux_dims* d, const flux_stream_weights* iw, co
              "modulation backward");
   }
   return FLUX_OK;
+}
+
+// ------------------------ sequential single block ------------------------
+flux_status flux_single_seq_fwd_train(const flux_dims* d, const flux_stream_weights* w, float* x, int64_t x_bstride,
+                                      const float* vec, const float* rope, void* saved, size_t saved_bytes,
+                                      void* stream) {
+  g_err[0] = 0;
+  REQUIRE(d, "dims is NULL");
+  const flux_dims one = one_stream(d);
+  return flux_block_fwd_train(&one, w, nullptr, x, x_bstride, nullptr, 0, vec, rope, saved, saved_bytes, stream);
+}
+
+flux_status flux_single_seq_bwd(const flux_dims* d, const flux_stream_weights* w, float* dx, int64_t x_bstride,
+                                const float* vec, const float* rope, const void* saved, size_t saved_bytes,
+                                const flux_stream_grads* grads, float* dvec, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  g_err[0] = 0;
+  REQUIRE(d, "dims is NULL");
+  const flux_dims one = one_stream(d);
+  return flux_block_bwd(&one, w, nullptr, dx, x_bstride, nullptr, 0, vec, rope, saved, saved_bytes, grads, nullptr,
+                        dvec, workspace, workspace_bytes, stream);
 }
 
 // ------------------------- attention alone (bf16) -------------------------

@@ -44,7 +44,7 @@ EXPORTED = (
     "flux_train_saved_bytes", "flux_bwd_workspace_bytes", "flux_block_fwd_train", "flux_block_bwd",
     "flux_single_fwd_train", "flux_single_bwd", "flux_attention_train_workspace_bytes", "flux_attention_fwd_train",
     "flux_attention_bwd", "flux_rf_loss_grad", "flux_final_bwd_workspace_bytes", "flux_final_bwd",
-    "flux_embed_bwd_workspace_bytes", "flux_embed_bwd",
+    "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
 )
 
 
@@ -160,6 +160,9 @@ def lib() -> C.CDLL:
         "flux_attention_fwd_train": [i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp],
         "flux_attention_bwd": [i32, i32, i32, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_rf_loss_grad": [i32, i64, vp, vp, vp, vp, vp],
+        "flux_single_seq_fwd_train": [P(flux_dims), P(flux_stream_weights), vp, i64, vp, vp, vp, sz, vp],
+        "flux_single_seq_bwd": [P(flux_dims), P(flux_stream_weights), vp, i64, vp, vp, vp, sz, P(flux_stream_grads),
+                                vp, vp, sz, vp],
         "flux_final_bwd": [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                            vp],
         "flux_embed_bwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp, vp,
@@ -582,3 +585,17 @@ def flux_embed_bwd(batch, channels, height, width, l_txt, ctx_dim, hidden, time_
                                 ptr(z_t), ptr(txt), ptr(t), ptr(y), ptr(d_img), img_bstride, ptr(d_txt), txt_bstride,
                                 ptr(dvec), C.byref(grads), ptr(workspace), workspace_bytes, _stream(stream)),
            "flux_embed_bwd")
+
+
+def flux_single_seq_fwd_train(dims: flux_dims, w: flux_stream_weights, x, x_bstride: int, vec, rope, saved,
+                              saved_bytes: int, stream=None) -> None:
+    _check(lib().flux_single_seq_fwd_train(C.byref(dims), C.byref(w), ptr(x), x_bstride, ptr(vec), ptr(rope),
+                                           ptr(saved), saved_bytes, _stream(stream)), "flux_single_seq_fwd_train")
+
+
+def flux_single_seq_bwd(dims: flux_dims, w: flux_stream_weights, dx, x_bstride: int, vec, rope, saved,
+                        saved_bytes: int, grads: flux_stream_grads, dvec, workspace, workspace_bytes: int,
+                        stream=None) -> None:
+    _check(lib().flux_single_seq_bwd(C.byref(dims), C.byref(w), ptr(dx), x_bstride, ptr(vec), ptr(rope), ptr(saved),
+                                     saved_bytes, C.byref(grads), ptr(dvec), ptr(workspace), workspace_bytes,
+                                     _stream(stream)), "flux_single_seq_bwd")

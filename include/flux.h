@@ -503,6 +503,8 @@ typedef struct {
   float *mod_w, *mod_b, *lin1_w, *lin1_b, *q_norm, *k_norm, *lin2_w, *lin2_b;
 } flux_single_grads;
 
+/* op 2: the sequential single block (flux_single_seq_fwd's one-stream form:
+ * weights in a flux_stream_weights, gradients in a flux_stream_grads). */
 size_t flux_train_saved_bytes(const flux_dims* dims, int32_t op);
 size_t flux_bwd_workspace_bytes(const flux_dims* dims, int32_t op);
 flux_status flux_block_fwd_train(const flux_dims* dims, const flux_stream_weights* img_w,
@@ -521,6 +523,14 @@ flux_status flux_single_bwd(const flux_dims* dims, const flux_single_weights* w,
                             const float* vec, const float* rope, const void* saved, size_t saved_bytes,
                             const flux_single_grads* grads, float* dvec, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+flux_status flux_single_seq_fwd_train(const flux_dims* dims, const flux_stream_weights* w, float* x,
+                                      int64_t x_batch_stride, const float* vec, const float* rope, void* saved,
+                                      size_t saved_bytes, void* stream);
+flux_status flux_single_seq_bwd(const flux_dims* dims, const flux_stream_weights* w, float* dx,
+                                int64_t x_batch_stride, const float* vec, const float* rope, const void* saved,
+                                size_t saved_bytes, const flux_stream_grads* grads, float* dvec, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * The rest of a rectified-flow training step (bf16 weights):

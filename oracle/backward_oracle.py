@@ -37,7 +37,7 @@ from .flux_oracle import (_heads, adaln, apply_rope, attention_probs, double_blo
 __all__ = [
     "rf_loss_grad", "linear_vjp", "silu_grad", "gelu_grad", "modulate_vjp", "rmsnorm_vjp", "rope_vjp",
     "attention_vjp", "adaln_vjp", "single_block_vjp", "double_block_vjp", "final_layer_vjp", "conditioning_vjp",
-    "flux_train_vjp",
+    "flux_train_vjp", "single_block_sequential_vjp",
 ]
 
 
@@ -307,3 +307,43 @@ def flux_train_vjp(z0, z1, t, txt, y, ids, emb_w: Dict[str, np.ndarray], double_
         _, g_emb["txt_in.w"], g_emb["txt_in.b"] = linear_vjp(txt, emb_w["txt_in.w"], d_txt)
     g_emb.update(conditioning_vjp(t, y, emb_w, dvec, model_channels))
     return loss, g_emb, g_double, g_single
+
+
+def single_block_sequential_vjp(x, vec, angles, w: Dict[str, np.ndarray], heads: int, eps: float, dout):
+    """Gradients of flux_oracle.single_block_sequential (one stream: two
+    adaLN halves with qkv / proj / fc1 / fc2, attention over every token) for
+    the output gradient dout [B, L, D].  Returns (dx, dvec, grads) keyed like w."""
+    x, ang = f64(x), f64(angles)
+    D = x.shape[-1]
+    m = adaln(vec, w["mod.w"], w["mod.b"], 6)
+    h1 = modulate(x, m[0], m[1], eps)
+    qkv = linear(h1, w["qkv.w"], w["qkv.b"])
+    qr, kr, v = _heads(qkv[..., :D], heads), _heads(qkv[..., D:2 * D], heads), _heads(qkv[..., 2 * D:], heads)
+    q = apply_rope(rmsnorm(qr, w["q_norm"], eps), ang)
+    k = apply_rope(rmsnorm(kr, w["k_norm"], eps), ang)
+    p = attention_probs(q, k)
+    o = np.matmul(p, v.transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3).reshape(x.shape[0], x.shape[1], D)
+    y1 = linear(o, w["proj.w"], w["proj.b"])
+    x1 = x + m[2][:, None, :] * y1
+    h2 = modulate(x1, m[3], m[4], eps)
+    a = linear(h2, w["fc1.w"], w["fc1.b"])
+    u = gelu(a)
+    y2 = linear(u, w["fc2.w"], w["fc2.b"])
+
+    g: Dict[str, np.ndarray] = {}
+    d = f64(dout)
+    dm5 = (y2 * d).sum(axis=1)
+    du, g["fc2.w"], g["fc2.b"] = linear_vjp(u, w["fc2.w"], m[5][:, None, :] * d)
+    dh2, g["fc1.w"], g["fc1.b"] = linear_vjp(h2, w["fc1.w"], du * gelu_grad(a))
+    dx1_ln, dm3, dm4 = modulate_vjp(x1, m[3], m[4], dh2, eps)
+    dx1 = d + dx1_ln
+    dm2 = (y1 * dx1).sum(axis=1)
+    do, g["proj.w"], g["proj.b"] = linear_vjp(o, w["proj.w"], m[2][:, None, :] * dx1)
+    dq, dk, dv = attention_vjp(q, k, v, do)
+    dqr, g["q_norm"] = rmsnorm_vjp(qr, w["q_norm"], rope_vjp(dq, ang), eps)
+    dkr, g["k_norm"] = rmsnorm_vjp(kr, w["k_norm"], rope_vjp(dk, ang), eps)
+    flat = lambda t: t.reshape(t.shape[0], t.shape[1], -1)
+    dh1, g["qkv.w"], g["qkv.b"] = linear_vjp(h1, w["qkv.w"], _cat([flat(dqr), flat(dkr), flat(dv)]))
+    dx_ln, dm0, dm1 = modulate_vjp(x, m[0], m[1], dh1, eps)
+    dvec, g["mod.w"], g["mod.b"] = adaln_vjp(vec, w["mod.w"], _cat([dm0, dm1, dm2, dm3, dm4, dm5]))
+    return dx1 + dx_ln, dvec, g

@@ -254,3 +254,18 @@ def test_flux_train_vjp():
         _dir_check(lambda u: J(a=dict(w2, **{n: u})), w2[n], g2[0][n], 1.0, rng)
     for n in ("lin1.w", "k_norm", "mod.b"):
         _dir_check(lambda u: J(b=dict(w1, **{n: u})), w1[n], g1[0][n], 1.0, rng)
+
+
+def test_single_block_sequential_vjp():
+    rng = np.random.default_rng(13)
+    L = LI + LT
+    w = {k[len("img_"):]: v for k, v in _double_w(rng).items() if k.startswith("img_")}
+    x, vec, ang = rng.standard_normal((B, L, D)), rng.standard_normal((B, D)), _angles(rng, L)
+    dout = rng.standard_normal((B, L, D))
+    dx, dvec, g = G.single_block_sequential_vjp(x, vec, ang, w, H, 1e-6, dout)
+    fwd = lambda xx=x, vv=vec, ww=w: O.single_block_sequential(xx, vv, ang, ww, H, 1e-6)
+    _dir_check(lambda t: fwd(xx=t), x, dx, dout, rng)
+    _dir_check(lambda t: fwd(vv=t), vec, dvec, dout, rng)
+    assert set(g) == set(w)
+    for n in w:
+        _dir_check(lambda t: fwd(ww=dict(w, **{n: t})), w[n], g[n], dout, rng)

@@ -338,3 +338,34 @@ def test_flux_train_step(name):
         _close(tr.g_double[0][n].cpu().numpy(), g2[0][n], "d double " + n)
     for n in sorted(w1):
         _close(tr.g_single[0][n].cpu().numpy(), g1[0][n], "d single " + n)
+
+
+@pytest.mark.parametrize("name", ["ragged", "wide"])
+def test_single_seq_block_backward(name):
+    wl = WL[name]
+    _say(f"sequential single block forward-train + backward {name} (B={wl.batch}, L={wl.seq}, D={wl.hidden})")
+    from flow_matching_diffusion_amd.model import upload_weights
+    f = F()
+    w = synth.single_seq_block_weights(wl, 2)
+    inp, dout, rope, ang, _ = _setup(wl, 8)
+    x0 = np.concatenate([inp["x_img"], inp["x_txt"]], axis=1)
+    dims = f.dims_for(wl)
+    wd = upload_weights(w, True)
+    sw = f.stream_weights(wd, None)
+    L, D = wl.seq, wl.hidden
+    x, vec = _dev(x0), _dev(inp["vec"])
+    sb = f.flux_train_saved_bytes(dims, 2)
+    saved = _ws(sb)
+    f.flux_single_seq_fwd_train(dims, sw, x, L * D, vec, rope, saved, sb)
+    d, dvec = _dev(dout), torch.zeros_like(vec)
+    grads = _grad_buffers(w)
+    wsb = f.flux_bwd_workspace_bytes(dims, 2)
+    ws = _ws(wsb)
+    f.flux_single_seq_bwd(dims, sw, d, L * D, vec, rope, saved, sb, f.stream_grads(grads, None), dvec, ws, wsb)
+    torch.cuda.synchronize()
+    _close(x.cpu().numpy(), O.single_block_sequential(x0, inp["vec"], ang, w, wl.heads, wl.eps), "forward output")
+    rdx, rdvec, rg = G.single_block_sequential_vjp(x0, inp["vec"], ang, w, wl.heads, wl.eps, dout)
+    _close(d.cpu().numpy(), rdx, "dx")
+    _close(dvec.cpu().numpy(), rdvec, "dvec")
+    for n in sorted(w):
+        _close(grads[n].cpu().numpy(), rg[n], "d " + n)
