@@ -29,6 +29,12 @@ Readings taken where that page is silent (each repeated at its function):
   F6 the "tensorwise" alternative recipe the page lists scales each tensor
      with its own current amax: s = fp32(448 / amax) of the tensor being
      quantized, no history.
+  F7 fp8 attention (listed on the page, off by default, without a recipe):
+     Q, K and V are each quantized with their own current scale (F6); the
+     scores and the output are formed from the dequantized values
+     dec(code) * fp32(1 / s).  The GPU also packs the probabilities to E4M3
+     (relative error <= 2^-4 each); the oracle keeps them exact and the test
+     bounds that step.
 """
 from __future__ import annotations
 
@@ -36,9 +42,10 @@ from typing import Callable, Dict, Optional, Tuple
 
 import numpy as np
 
-from .flux_oracle import f64, linear
+from .flux_oracle import attention, f64, linear
 
 __all__ = ["E4M3_MAX", "HISTORY_LEN", "e4m3_decode", "e4m3_encode", "quantize", "amax", "fp8_linear",
+           "attention_fp8",
            "scale_update", "current_scale", "fp8_linears", "TOKEN_LINEARS_DOUBLE", "TOKEN_LINEARS_SINGLE"]
 
 E4M3_MAX = 448.0
@@ -152,3 +159,12 @@ def fp8_linears(scales: Dict[str, Tuple[float, float]],
         s_x, s_w = scales[name]
         return fp8_linear(x, w, b, s_x, s_w)
     return lin
+
+
+def attention_fp8(q, k, v):
+    """Softmax attention on E4M3 operands (F7): q, k, v [B, L, H, Dh] are
+    quantized with their current scales and dequantized with fp32(1 / s);
+    returns (o [B, Lq, H * Dh], (s_q, s_k, s_v))."""
+    scales = tuple(current_scale(x) for x in (q, k, v))
+    deq = [e4m3_decode(quantize(x, sx)) * float(np.float32(1.0) / np.float32(sx)) for x, sx in zip((q, k, v), scales)]
+    return attention(*deq), scales

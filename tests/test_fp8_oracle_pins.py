@@ -248,3 +248,34 @@ def test_current_scale_definition():
         assert np.all((q & 0x7F) <= 0x7E)
     assert Q.current_scale(np.zeros(8), 3.0) == 3.0
     assert Q.current_scale(np.array([1.0, np.inf]), 2.5) == 2.5
+
+
+def test_attention_fp8_exact_on_representable_inputs():
+    # values in {0, +-1, +-2, +-4} with amax 4: the current scale is 112 and
+    # 112, 224 and 448 are E4M3 values, so quantization is exact and fp8
+    # attention is the plain attention of the inputs
+    rng = np.random.default_rng(21)
+    vals = np.array([0.0, 1.0, -1.0, 2.0, -2.0, 4.0, -4.0])
+    q, k, v = (vals[rng.integers(0, len(vals), size=(2, 9, 3, 16))] for _ in range(3))
+    for x in (q, k, v):
+        x[0, 0, 0, 0] = 4.0
+    o, scales = Q.attention_fp8(q, k, v)
+    assert scales == (112.0, 112.0, 112.0)
+    for x in (q, k, v):   # the codes are exact
+        assert np.array_equal(Q.e4m3_decode(Q.quantize(x, 112.0)), x * 112.0)
+    # dequantization multiplies by fp32(1/112), which is 1/112 to 2^-24: the
+    # attention agrees to that rounding, amplified a little by the softmax
+    np.testing.assert_allclose(o, O.attention(q, k, v), rtol=2e-5, atol=1e-9)
+
+
+def test_attention_fp8_error_bound():
+    # every operand carries a relative error <= 2^-4 (E4M3 keeps 3 fraction
+    # bits) unless it is below the subnormal range; the output of random
+    # attention moves by a few per cent at most
+    rng = np.random.default_rng(22)
+    q, k, v = (rng.standard_normal((1, 40, 2, 32)) for _ in range(3))
+    q *= 0.3
+    o, _ = Q.attention_fp8(q, k, v)
+    ref = O.attention(q, k, v)
+    rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
+    assert 1e-3 < rel < 5e-2, rel
