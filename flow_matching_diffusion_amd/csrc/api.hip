@@ -769,4 +769,55 @@ flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, in
   return FLUX_OK;
 }
 
+// ---------------------------------- fp8 attention ----------------------------------
+size_t flux_attention_fp8_workspace_bytes(int32_t batch, int32_t seq, int32_t heads) {
+  if (batch < 1 || seq < 1 || heads < 1) return 0;
+  Carve c(nullptr);
+  const int64_t n = (int64_t)batch * heads * seq_pad_of(seq) * 128;
+  for (int i = 0; i < 3; ++i) c.take(n * 2);
+  for (int i = 0; i < 3; ++i) c.take(n);
+  return (size_t)round_up((int64_t)c.off, 256);
+}
+
+flux_status flux_attention_fp8_fwd(int32_t batch, int32_t seq, int32_t heads, const void* q, const void* k,
+                                   const void* v, int64_t ld_in, void* o, int64_t ld_out, flux_fp8_tensor* recs,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(batch >= 1 && seq >= 1 && heads >= 1, "batch, seq and heads must be >= 1");
+  REQUIRE(q && k && v && o && recs, "q, k, v, o and recs are required");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(recs),
+          "pointers must be 16-byte aligned");
+  const int64_t D = (int64_t)heads * 128;
+  REQUIRE(ld_in >= D && ld_out >= D && ld_in % 8 == 0 && ld_out % 8 == 0,
+          "row strides must be >= heads*128 and multiples of 8");
+  flux_status s = check_workspace(workspace, workspace_bytes, flux_attention_fp8_workspace_bytes(batch, seq, heads));
+  if (s != FLUX_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t Lp = seq_pad_of(seq), n = (int64_t)batch * heads * Lp * 128;
+  Carve c(workspace);
+  PrepArgs pa{};
+  pa.src_q = q; pa.src_k = k; pa.src_v = v;
+  pa.src_bstride = (int64_t)seq * ld_in; pa.src_ld = ld_in;
+  pa.batch = batch; pa.seq = seq; pa.seq_pad = (int)Lp; pa.heads = heads; pa.head_dim = 128; pa.l_img = seq;
+  pa.eps = 1e-6f;
+  pa.qh = c.take(n * 2); pa.kh = c.take(n * 2); pa.vt = c.take(n * 2);
+  FLUX_HIP(launch_prep(pa, kBF16, st), "attention layout");
+  // per-tensor current scaling of Q, K and V (padding rows are zero)
+  void* src[3] = {pa.qh, pa.kh, pa.vt};
+  uint8_t* codes[3];
+  for (int i = 0; i < 3; ++i) {
+    codes[i] = static_cast<uint8_t*>(c.take(n));
+    FLUX_HIP(launch_fp8_current_scale(src[i], kBF16, n, recs + i, st), "fp8 current scale");
+    FLUX_HIP(launch_fp8_quantize(src[i], kBF16, n, recs + i, codes[i], st), "fp8 quantize");
+  }
+  AttnArgs aa{};
+  aa.qh = codes[0]; aa.kh = codes[1]; aa.vt = codes[2];
+  aa.sq = recs; aa.sk = recs + 1; aa.sv = recs + 2;
+  aa.out = o; aa.out_bstride = (int64_t)seq * ld_out; aa.out_ld = ld_out;
+  aa.batch = batch; aa.seq = seq; aa.seq_pad = (int)Lp; aa.heads = heads; aa.head_dim = 128;
+  aa.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
+  FLUX_HIP(launch_attention(aa, kFP8, kBF16, st), "fp8 attention");
+  return FLUX_OK;
+}
+
 }  // extern "C"

@@ -363,8 +363,202 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// E4M3 kernel ("FP8 training for Flux models": fp8 attention, off by default):
+// Q, K and V^T are E4M3 codes with one scale per tensor; S^T = K Q^T and
+// O^T = V^T P^T run on v_mfma_f32_32x32x64_f8f6f4, the probabilities are
+// packed to E4M3 (below 2^8 with the lazy max, inside E4M3's range).  Same
+// block shape, placement, lazy max and software pipeline as the bf16 kernel.
+// The MFMA sums its 64 products in an order of its own; A and B only have to
+// give each lane half and register byte the same k.  For S^T lane half h holds
+// head-dim bytes [64 s + 32 h, + 32) of k step s in both operands.  For O^T
+// the B operand is the lane's 32 probabilities in accumulator order, i.e. keys
+// 32 u + 8 (e / 4) + 4 h + e % 4 for byte 16 u + e; V^T tiles are stored with
+// their columns permuted in groups of 4 keys so that these 32 keys are the
+// 32 contiguous bytes [32 h, 32 h + 32) of the lane's V^T row.
+typedef int i32x8a_t __attribute__((ext_vector_type(8)));
+
+__global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
+  constexpr int DH = 128, KT = 64, QW = 32, NW = 8, QB = NW * QW, NT = NW * 64, DT = DH / 32;
+  constexpr int KLD = DH + 16;    // K tile row stride (bytes): 16 lanes of a read hit distinct bank groups
+  constexpr int VLD = KT + 16;    // V^T tile row stride (bytes)
+  constexpr float kLazy = 8.0f;
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][KT * KLD];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][DH * VLD];
+  const int nq = a.seq_pad / QB;
+  const int total = a.batch * a.heads * nq;
+  const int per = (total + 7) / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= total) return;
+  const int qb = item % nq;
+  const int64_t bh = item / nq;
+  const int b = (int)(bh / a.heads), h = (int)(bh % a.heads);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const uint8_t* Qh = reinterpret_cast<const uint8_t*>(a.qh) + bh * a.seq_pad * DH;
+  const uint8_t* Kh = reinterpret_cast<const uint8_t*>(a.kh) + bh * a.seq_pad * DH;
+  const uint8_t* Vt = reinterpret_cast<const uint8_t*>(a.vt) + bh * DH * a.seq_pad;
+
+  const int q = qb * QB + wave * QW + l32;
+  i32x8a_t qf[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) qf[st] = *reinterpret_cast<const i32x8a_t*>(Qh + (int64_t)q * DH + 64 * st + 32 * half);
+  f32x16_t o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = a.scale_log2 * fp8_scale_inv(a.sq) * fp8_scale_inv(a.sk);
+
+  auto mma = [](i32x8a_t x, i32x8a_t y, f32x16_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+  };
+  auto kfrag = [&](int t, int u, int st) {
+    return *reinterpret_cast<const i32x8a_t*>(&Ks[t & 1][(u * 32 + l32) * KLD + 64 * st + 32 * half]);
+  };
+  // S^T of tile t: sv[u][e] is the score of key t*64 + 32u + 8(e/4) + 4 half + e%4
+  auto s_tile = [&](int t, f32x16_t (&sv)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[u][e] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) sv[u] = mma(kfrag(t, u, st), qf[st], sv[u]);
+    }
+  };
+  auto softmax_max = [&](int t, f32x16_t (&sv)[2]) {
+    if ((t + 1) * KT > a.seq) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = t * KT + 32 * u + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (key >= a.seq) sv[u][e] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[u][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_tile = mx * sc;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      m_run = m_new;
+    }
+  };
+  uint32_t pw[8];   // E4M3 probabilities of the current tile: dword 4u + g holds elements 4g..4g+3 of tile u
+  auto pv_tile = [&](int t) {
+    const i32x8a_t pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      const i32x8a_t vf = *reinterpret_cast<const i32x8a_t*>(&Vs[t & 1][(i * 32 + l32) * VLD + 32 * half]);
+      o[i] = mma(vf, pb, o[i]);
+    }
+  };
+  u32x4_t rk, rv;
+  const int kr = tid >> 3, kc = (tid & 7) * 16;    // K tile: 64 rows x 8 chunks
+  const int vd = tid >> 2, va = tid & 3;           // V^T tile: 128 rows x 4 chunks of 16 keys
+  auto gload_k = [&](int j) { rk = *reinterpret_cast<const u32x4_t*>(Kh + (int64_t)(j * KT + kr) * DH + kc); };
+  auto gload_v = [&](int j) { rv = *reinterpret_cast<const u32x4_t*>(Vt + (int64_t)vd * a.seq_pad + j * KT + va * 16); };
+  auto lstore_k = [&](int j) { *reinterpret_cast<u32x4_t*>(&Ks[j & 1][kr * KLD + kc]) = rk; };
+  auto lstore_v = [&](int j) {
+    // keys 16 va + 4 g2 .. + 4 go to column 32 (g2 & 1) + 16 (va >> 1) + 4 ((2 va + (g2 >> 1)) & 3)
+#pragma unroll
+    for (int g2 = 0; g2 < 4; ++g2) {
+      const int col = 32 * (g2 & 1) + 16 * (va >> 1) + 4 * ((2 * va + (g2 >> 1)) & 3);
+      *reinterpret_cast<uint32_t*>(&Vs[j & 1][vd * VLD + col]) = rv[g2];
+    }
+  };
+  const int ntiles = (a.seq + KT - 1) / KT;
+  gload_k(0);
+  gload_v(0);
+  lstore_k(0);
+  lstore_v(0);
+  if (ntiles > 1) {
+    gload_k(1);
+    lstore_k(1);
+  }
+  if (ntiles > 2) gload_k(2);
+  if (ntiles > 1) gload_v(1);
+  __syncthreads();
+  f32x16_t sc_cur[2], sc_nxt[2];
+  s_tile(0, sc_cur);
+  // iteration 0 overwrites K(0)'s buffer with K(2): every wave must have read K(0) first
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    softmax_max(t, sc_cur);
+    // S(t + 1) (from a resident buffer, discarded, on the last tile) with the
+    // exponentials of tile t in its MFMA shadow: step m issues one MFMA and
+    // the 8 probabilities of elements 8 (m & 1) .. + 8 of tile m >> 1
+    {
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc_nxt[u][e] = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int u = m & 1, st = m >> 1;
+        sc_nxt[u] = mma(kfrag(t + 1, u, st), qf[st], sc_nxt[u]);
+        const int uu = m >> 1;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * (m & 1) + gg;
+          float p[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            p[c] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc_cur[uu][4 * g + c], sc, -m_run));
+            psum += p[c];
+          }
+          pw[4 * uu + g] = f32x4_to_e4m3(p[0], p[1], p[2], p[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run += psum;
+    }
+    pv_tile(t);
+    if (t + 2 < ntiles) lstore_k(t + 2);
+    if (t + 1 < ntiles) lstore_v(t + 1);
+    if (t + 3 < ntiles) gload_k(t + 3);
+    if (t + 2 < ntiles) gload_v(t + 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sc_cur[u] = sc_nxt[u];
+    __syncthreads();
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = fp8_scale_inv(a.sv) / l_tot;
+  if (q < a.seq) {
+    bf16_t* out = reinterpret_cast<bf16_t*>(a.out) + (int64_t)b * a.out_bstride + (int64_t)q * a.out_ld + h * DH;
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = i * 32 + 8 * g + 4 * half;
+        uint2 v;
+        v.x = pack_bf16x2(o[i][4 * g] * inv, o[i][4 * g + 1] * inv);
+        v.y = pack_bf16x2(o[i][4 * g + 2] * inv, o[i][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(out + d0) = v;
+      }
+  }
+}
+
 hipError_t launch_attention(const AttnArgs& a, int dtype, int out_dtype, hipStream_t stream) {
   TimingScope ts(kKcAttn, stream, 4.0 * a.batch * a.heads * (double)a.seq * a.seq * a.head_dim);
+  if (dtype == kFP8) {
+    if (a.head_dim != 128 || out_dtype != kBF16 || !a.sq || !a.sk || !a.sv) return hipErrorInvalidValue;
+    const int items = a.batch * a.heads * (a.seq_pad / 256);
+    const dim3 grid(((items + 7) / 8) * 8);
+    hipLaunchKernelGGL(attn_fp8_kernel, grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
   if (dtype == kBF16) {
     // one block per 256 queries of a (batch, head), rounded up to whole XCD
     // groups (blocks past the work exit at once)

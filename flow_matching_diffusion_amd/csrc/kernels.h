@@ -133,9 +133,12 @@ struct AttnArgs {
   int32_t l_img;
   float* lse;   // optional [B, H, seq_pad]: log2-domain log-sum-exp of the scaled scores per query
                 //   (+inf for queries >= seq), so that P = exp2(s * scale_log2 - lse); bf16 kernel only
+  // kFP8 inputs (head_dim 128, bf16 output): qh, kh, vt hold E4M3 codes quantized
+  // with the scales of these records; scores and output are rescaled by scale_inv
+  const flux_fp8_tensor* sq; const flux_fp8_tensor* sk; const flux_fp8_tensor* sv;
 };
-// in_dtype kBF16 (bf16 MFMA) or kF32; out_dtype kBF16 / kF16 / kFP8 with bf16
-// inputs, kF32 with fp32 inputs
+// in_dtype kBF16 (bf16 MFMA), kFP8 (E4M3 codes on the fp8 MFMA, bf16 output) or
+// kF32; out_dtype kBF16 / kF16 / kFP8 with bf16 inputs, kF32 with fp32 inputs
 hipError_t launch_attention(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
 
 // ------------------------------- backward --------------------------------

@@ -45,6 +45,7 @@ EXPORTED = (
     "flux_single_fwd_train", "flux_single_bwd", "flux_attention_train_workspace_bytes", "flux_attention_fwd_train",
     "flux_attention_bwd", "flux_rf_loss_grad", "flux_final_bwd_workspace_bytes", "flux_final_bwd",
     "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
+    "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd",
 )
 
 
@@ -160,6 +161,7 @@ def lib() -> C.CDLL:
         "flux_attention_fwd_train": [i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp],
         "flux_attention_bwd": [i32, i32, i32, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_rf_loss_grad": [i32, i64, vp, vp, vp, vp, vp],
+        "flux_attention_fp8_fwd": [i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp],
         "flux_single_seq_fwd_train": [P(flux_dims), P(flux_stream_weights), vp, i64, vp, vp, vp, sz, vp],
         "flux_single_seq_bwd": [P(flux_dims), P(flux_stream_weights), vp, i64, vp, vp, vp, sz, P(flux_stream_grads),
                                 vp, vp, sz, vp],
@@ -196,6 +198,8 @@ def lib() -> C.CDLL:
     L.flux_final_bwd_workspace_bytes.restype = sz
     L.flux_embed_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.flux_embed_bwd_workspace_bytes.restype = sz
+    L.flux_attention_fp8_workspace_bytes.argtypes = [i32, i32, i32]
+    L.flux_attention_fp8_workspace_bytes.restype = sz
     L.flux_status_string.argtypes = [C.c_int]
     L.flux_status_string.restype = C.c_char_p
     L.flux_last_error.argtypes = []
@@ -599,3 +603,13 @@ def flux_single_seq_bwd(dims: flux_dims, w: flux_stream_weights, dx, x_bstride: 
     _check(lib().flux_single_seq_bwd(C.byref(dims), C.byref(w), ptr(dx), x_bstride, ptr(vec), ptr(rope), ptr(saved),
                                      saved_bytes, C.byref(grads), ptr(dvec), ptr(workspace), workspace_bytes,
                                      _stream(stream)), "flux_single_seq_bwd")
+
+
+def flux_attention_fp8_workspace_bytes(batch: int, seq: int, heads: int) -> int:
+    return lib().flux_attention_fp8_workspace_bytes(batch, seq, heads)
+
+
+def flux_attention_fp8_fwd(batch: int, seq: int, heads: int, q, k, v, ld_in: int, o, ld_out: int, recs, workspace,
+                           workspace_bytes: int, stream=None) -> None:
+    _check(lib().flux_attention_fp8_fwd(batch, seq, heads, ptr(q), ptr(k), ptr(v), ld_in, ptr(o), ld_out, ptr(recs),
+                                        ptr(workspace), workspace_bytes, _stream(stream)), "flux_attention_fp8_fwd")

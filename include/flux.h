@@ -590,6 +590,21 @@ flux_status flux_attention_bwd(int32_t batch, int32_t seq, int32_t heads, const 
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Softmax attention with E4M3 operands ("FP8 training for Flux models": fp8
+ * attention, off by default), head_dim 128: q, k, v bf16 [B, seq, heads*128]
+ * token rows (row stride ld_in) are quantized to E4M3 with per-tensor
+ * current scaling -- recs[0..2] (Q, K, V; flux_fp8_tensor records) receive
+ * amax, scale = fp32(448 / amax) and scale_inv as flux_fp8_quantize_current
+ * sets them -- then S = q k^T / sqrt(128) and O = P v run on the fp8 MFMA,
+ * with the probabilities P packed to E4M3; o bf16 (row stride ld_out).
+ * Workspace: flux_attention_fp8_workspace_bytes bytes, 256-byte aligned.
+ */
+size_t flux_attention_fp8_workspace_bytes(int32_t batch, int32_t seq, int32_t heads);
+flux_status flux_attention_fp8_fwd(int32_t batch, int32_t seq, int32_t heads, const void* q, const void* k,
+                                   const void* v, int64_t ld_in, void* o, int64_t ld_out, flux_fp8_tensor* recs,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing (diagnostics, off by default).  While enabled, each kernel
  * launch made by the library is bracketed by two hipEvents recorded on that
  * launch's stream.  flux_timing_read waits for the recorded events, writes

@@ -393,3 +393,36 @@ def test_fp8_single_block_c5_sampled(c5_case):
     o = O.single_block(x, inp["vec"], ang, w1, wl.heads, wl.eps, rows=sel, lin=Q.fp8_linears(sc, seen))
     _check_act_scales(sc, seen, ["lin1"])
     _close(g[:, sel], o, "fp8 single")
+
+
+# --------------------------- fp8 attention (F7) --------------------------- #
+@pytest.mark.parametrize("B,L,H", [(1, 80, 2), (2, 333, 2), (1, 4608, 24)])
+def test_attention_fp8(B, L, H):
+    _say(f"fp8 attention B={B} L={L} H={H} Dh=128")
+    rng = np.random.default_rng(L + 7 * H)
+    D = H * 128
+    q = synth.round_to_bf16(0.25 * rng.standard_normal((B, L, D)).astype(np.float32))
+    k = synth.round_to_bf16(rng.standard_normal((B, L, D)).astype(np.float32))
+    v = synth.round_to_bf16(rng.standard_normal((B, L, D)).astype(np.float32))
+    f = F()
+    rec = _records(3)
+    o = torch.empty((B, L, D), dtype=torch.bfloat16, device="cuda")
+    wsb = f.flux_attention_fp8_workspace_bytes(B, L, H)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    bf = lambda a: torch.from_numpy(synth.bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16)
+    f.flux_attention_fp8_fwd(B, L, H, bf(q), bf(k), bf(v), D, o, D, rec, ws, wsb)
+    torch.cuda.synchronize()
+    # the recorded scales are the current scales of Q, K and V, bit for bit
+    scales = tuple(Q.current_scale(x) for x in (q, k, v))
+    assert tuple(r["scale"] for r in _read_records(rec, 3)) == scales
+    # reference on the sampled query rows (all of them up to 512 tokens)
+    rows = np.arange(L) if L <= 512 else np.unique(np.r_[rng.choice(L, 48, replace=False), 0, L - 1])
+    hd = lambda a: a.reshape(a.shape[0], a.shape[1], H, 128)
+    deq = lambda x, s: Q.e4m3_decode(Q.quantize(x, s)) * float(np.float32(1.0) / np.float32(s))
+    ref8 = O.attention(hd(deq(q[:, rows], scales[0])), hd(deq(k, scales[1])), hd(deq(v, scales[2])))
+    ref = O.attention(hd(q[:, rows]), hd(k), hd(v))
+    got = o.float().cpu().numpy()[:, rows]
+    rel8 = float(np.linalg.norm(got - ref8) / np.linalg.norm(ref8))
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    print(f"    fp8 attention: rel_l2 vs the fp8 oracle {rel8:.2e}, vs exact attention {rel:.2e}", flush=True)
+    assert np.isfinite(got).all() and rel8 <= 5e-2 and rel <= 5e-2
