@@ -421,6 +421,71 @@ def train_bench(args) -> int:
     return 0
 
 
+def attention_fp8_bench(args) -> int:
+    """Joint attention of the Flux-12B block shapes (B=1, 4608 tokens, 24
+    heads of 128) with E4M3 operands: per step, Q, K and V (bf16 token rows)
+    are laid out head-major, quantized with their current scales and attended
+    on the fp8 MFMA (flux_attention_fp8_fwd)."""
+    import torch
+
+    from flow_matching_diffusion_amd import flux as FX
+
+    torch.cuda.set_device(0)
+    FX.lib()
+    B, L, H = 1, 4608, 24
+    D = H * 128
+    g = torch.Generator(device="cuda").manual_seed(77)
+    q, k, v = ((torch.randn((B, L, D), generator=g, device="cuda") * s).to(torch.bfloat16) for s in (0.25, 1.0, 1.0))
+    o = torch.empty((B, L, D), dtype=torch.bfloat16, device="cuda")
+    rec = torch.zeros(3 * FX.FP8_TENSOR_BYTES, dtype=torch.uint8, device="cuda")
+    wsb = FX.flux_attention_fp8_workspace_bytes(B, L, H)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def step():
+        FX.flux_attention_fp8_fwd(B, L, H, q, k, v, D, o, D, rec, ws, wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    FX.flux_timing_read()
+    FX.flux_timing_enable(True)              # per-kernel durations (HIP events around each launch)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    FX.flux_timing_enable(False)
+    kernels = FX.flux_timing_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()                              # the step time, without the hook
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    flops = 4.0 * B * H * L * L * 128
+    ams, an, aw = kernels["attention"]
+    assert abs(aw / args.steps - flops) <= 1e-6 * flops
+    tf = aw / (ams * 1e-3) / 1e12
+    assert bool(torch.isfinite(o.float()).all())
+    table = {n: {"ms_per_launch": round(ms / c, 5), "launches_per_step": c / args.steps} for n, (ms, c, w) in
+             kernels.items() if c}
+    rec_out = {
+        "metric": "joint attention TFLOP/s with E4M3 operands (Flux-12B block shape, 4096 img + 512 txt tokens, "
+                  "24 heads)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3 Q, K, V and P (per-tensor current scales), fp32 accumulation",
+        "data": "synthetic", "config": {"workload": "flux12b_joint_attention_fp8", "batch": B, "seq": L, "heads": H,
+                                        "head_dim": 128},
+        "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": aw / an, "ms_per_launch": round(ams / an, 5)},
+        "kernels": table,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec_out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -432,7 +497,8 @@ def main() -> int:
                          "reports the replay time as ms_per_step)")
     ap.add_argument("--workload", default="flux12b_blocks",
                     choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8", "flux12b_blocks_seq",
-                             "flux12b_sample_cfg", "flux12b_mxfp8_linears", "flux12b_blocks_train"],
+                             "flux12b_sample_cfg", "flux12b_mxfp8_linears", "flux12b_blocks_train",
+                             "flux12b_attention_fp8"],
                     help="flux12b_blocks (default): the block-pair step the headline metric is quoted on; "
                          "flux12b_full: the whole 19 + 38 block forward + loss at batch 2 (block weights "
                          "drawn on the device; no CPU baseline); flux12b_blocks_fp8: the block pair at batch 4 "
@@ -443,7 +509,8 @@ def main() -> int:
                          "guidance embedding on) on the block-pair model; flux12b_mxfp8_linears: the six "
                          "token-path linears of the block pair at batch 4 as MXFP8 linears; "
                          "flux12b_blocks_train: a whole rectified-flow training step (forward and backward) of the "
-                         "block-pair model at batch 1")
+                         "block-pair model at batch 1; flux12b_attention_fp8: the joint attention of the block "
+                         "shape with E4M3 operands")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -468,6 +535,8 @@ def main() -> int:
         return mx_linears_bench(args)
     if args.workload == "flux12b_blocks_train":
         return train_bench(args)
+    if args.workload == "flux12b_attention_fp8":
+        return attention_fp8_bench(args)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

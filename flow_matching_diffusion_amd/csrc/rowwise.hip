@@ -955,10 +955,12 @@ hipError_t launch_mx_quantize(const void* src, int src_dtype, int rows, int k, u
 // ===========================================================================
 // dst = e4m3(src * scale(rec)) over a whole tensor (the weight cast of a
 // forward); each thread converts 16 consecutive elements per step, and one
-// atomic per wave raises the record's amax.
+// atomic per block raises the record's amax (atomics on one address
+// serialize, so the grid is kept to at most 1024 blocks).
 template <typename T>
 __global__ void __launch_bounds__(256) fp8_quantize_kernel(const T* __restrict__ src, int64_t n,
                                                            flux_fp8_tensor* rec, uint8_t* __restrict__ dst) {
+  __shared__ uint32_t red[4];
   const float qs = fp8_scale(rec);
   const int64_t n16 = n / 16;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -1001,13 +1003,18 @@ __global__ void __launch_bounds__(256) fp8_quantize_kernel(const T* __restrict__
     dst[k] = (uint8_t)f32_to_e4m3(x * qs);
   }
   mx = wave_max_u32(mx);
-  if ((threadIdx.x & 63) == 0) fp8_amax_raise(rec, __uint_as_float(mx));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t b = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (b) fp8_amax_raise(rec, __uint_as_float(b));
+  }
 }
 
 hipError_t launch_fp8_quantize(const void* src, int src_dtype, int64_t n, flux_fp8_tensor* rec, uint8_t* dst,
                                hipStream_t stream) {
   int64_t blocks = ceil_div(n / 16 > 0 ? n / 16 : 1, 256);
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 1024) blocks = 1024;
   TimingScope ts(kKcFp8Cast, stream, (double)n * ((src_dtype == kF32 ? 4.0 : 2.0) + 1.0));
   if (src_dtype == kF32)
     hipLaunchKernelGGL(fp8_quantize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
@@ -1034,8 +1041,24 @@ template <typename T>
 __global__ void __launch_bounds__(256) fp8_amax_kernel(const T* __restrict__ src, int64_t n, flux_fp8_tensor* rec) {
   __shared__ uint32_t red[4];
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    m = max(m, abs_bits(load_f32<T>(src + i)));   // NaN patterns sort above every finite one
+  // 16-byte loads over the whole vectors, then the tail element by element
+  constexpr int V = 16 / sizeof(T);
+  const int64_t nv = n / V, stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv; i += stride) {
+    const uint4 w = reinterpret_cast<const uint4*>(src)[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (sizeof(T) == 4) {
+        m = max(m, ws[e] & 0x7fffffffu);   // NaN patterns sort above every finite one
+      } else {
+        m = max(m, abs_bits(__uint_as_float(ws[e] << 16)));
+        m = max(m, abs_bits(__uint_as_float(ws[e] & 0xffff0000u)));
+      }
+    }
+  }
+  for (int64_t i = nv * V + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    m = max(m, abs_bits(load_f32<T>(src + i)));
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -1063,8 +1086,8 @@ hipError_t launch_fp8_current_scale(const void* src, int src_dtype, int64_t n, f
                                     hipStream_t stream) {
   TimingScope ts(kKcFp8Cast, stream, (double)n * (src_dtype == kF32 ? 4.0 : 2.0));
   hipLaunchKernelGGL(fp8_amax_clear_kernel, dim3(1), dim3(64), 0, stream, rec);
-  int64_t blocks = ceil_div(n, 256 * 8);
-  if (blocks > 2048) blocks = 2048;
+  int64_t blocks = ceil_div(n, 256 * 64);
+  if (blocks > 512) blocks = 512;
   if (blocks < 1) blocks = 1;
   if (src_dtype == kF32)
     hipLaunchKernelGGL(fp8_amax_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
