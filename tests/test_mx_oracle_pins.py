@@ -103,3 +103,61 @@ def test_mx_linear_against_block_sums():
     # and the quantized product stays close to the exact one (E4M3 precision)
     ref = x @ w.T + b
     assert np.abs(got - ref).max() <= 0.1 * np.abs(x @ w.T).max() + 1e-12
+
+
+# --------------------------------- MXFP4 --------------------------------- #
+def test_e2m1_grid_and_rounding():
+    # the grid the format defines, every code round-trips, ties go to the even code
+    assert [float(MX.e2m1_decode(c)) for c in range(8)] == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert [float(MX.e2m1_decode(c)) for c in range(8, 16)] == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    for c in range(16):
+        if c != 8:
+            assert int(MX.e2m1_encode(MX.e2m1_decode(c))) == c
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for v, want in ties.items():
+        assert float(MX.e2m1_decode(MX.e2m1_encode(v))) == want, v
+        assert float(MX.e2m1_decode(MX.e2m1_encode(-v))) == -want, v
+    assert float(MX.e2m1_decode(MX.e2m1_encode(100.0))) == 6.0
+    assert float(MX.e2m1_decode(MX.e2m1_encode(0.26))) == 0.5 and float(MX.e2m1_decode(MX.e2m1_encode(0.24))) == 0.0
+    # brute force: the encoder picks a nearest grid value for every input of a fine sweep
+    xs = np.linspace(-7, 7, 2801)
+    got = MX.e2m1_decode(MX.e2m1_encode(xs))
+    grid = np.r_[-MX._E2M1[::-1], MX._E2M1]
+    best = np.abs(np.clip(xs, -6, 6)[:, None] - grid[None, :]).min(axis=1)
+    assert np.allclose(np.abs(np.clip(xs, -6, 6) - got), best, atol=0)
+
+
+def test_mxfp4_exponent_and_roundtrip():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 96)) * np.exp2(rng.integers(-20, 20, size=(5, 1)))
+    packed, s = MX.mxfp4_quantize(x)
+    X = s.astype(np.int64) - 127
+    a = np.abs(x.reshape(5, 3, 32)).max(axis=-1)
+    # the block max lands in [4, 8) after the shift: E2M1's top binade, rounded at most to 6
+    assert np.all((a / np.exp2(X) >= 4) & (a / np.exp2(X) < 8))
+    # values already on the scaled grid round-trip exactly
+    grid = MX._E2M1[rng.integers(0, 8, size=(2, 64))] * np.where(rng.uniform(size=(2, 64)) < 0.5, -1, 1)
+    grid[:, ::32] = 6.0
+    y = grid * 2.0 ** 5
+    assert np.array_equal(MX.mxfp4_dequantize(*MX.mxfp4_quantize(y)), y)
+    # the even-indexed element sits in the low nibble
+    p, _ = MX.mxfp4_quantize(np.r_[np.full(31, 6.0), 0.5].reshape(1, 32) * 1.0)
+    assert p[0, 0] == (7 | (7 << 4)) and p[0, 15] == (7 | (1 << 4))
+
+
+def test_mxfp4_linear_block_sum():
+    rng = np.random.default_rng(32)
+    x, w = rng.standard_normal((3, 64)), rng.standard_normal((4, 64))
+    y = MX.mxfp4_linear(x, w)
+    xq, xs = MX.mxfp4_quantize(x)
+    wq, ws = MX.mxfp4_quantize(w)
+    xd, wd = MX.mxfp4_dequantize(xq, xs), MX.mxfp4_dequantize(wq, ws)
+    for i in range(3):
+        for j in range(4):
+            s = 0.0
+            for kb in range(2):
+                part = sum(xd[i, 32 * kb + t] * wd[j, 32 * kb + t] for t in range(32))
+                s += part
+            assert abs(y[i, j] - s) <= 1e-12 * max(1.0, abs(s))
+    # and within E2M1 precision of the exact product
+    assert np.linalg.norm(y - x @ w.T) / np.linalg.norm(x @ w.T) < 0.3
