@@ -32,6 +32,7 @@ METRIC = "MMDiT block fwd tokens/s & joint-attn TFLOP/s (512 txt+4096 img, bf16)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 (OCP e4m3) MFMA
+PEAK_FP4_TFLOPS = 10066.3      # MI355X dense fp4 (OCP e2m1) MFMA, twice the fp8 rate (published as 10.1 PFLOP/s)
 
 
 def algorithmic_work(wl, single_seq=False):
@@ -247,13 +248,13 @@ def cpu_baseline(wl, w2, inp, ids, work):
             "seconds": round(dt, 2)}
 
 
-def mx_linears_bench(args) -> int:
+def mx_linears_bench(args, fp4=False) -> int:
     """The six token-path linears of the Flux-12B block pair at batch 4
     (qkv, proj, fc1, fc2 over the joint 4608-token rows of 4 samples; lin1,
-    lin2 of the single block) as MXFP8 linears: per step, every input is
-    quantized to MXFP8 (flux_mx_quantize, bf16 source) and multiplied with its
-    MXFP8 weight (flux_mxfp8_linear_fwd).  Weights are quantized once, before
-    timing (static)."""
+    lin2 of the single block) as MXFP8 (E4M3 elements) or, with fp4, MXFP4
+    (E2M1 elements) linears: per step, every input is quantized (bf16 source)
+    and multiplied with its quantized weight.  Weights are quantized once,
+    before timing (static)."""
     import numpy as np
     import torch
 
@@ -265,16 +266,23 @@ def mx_linears_bench(args) -> int:
     M = B * L
     shapes = [("qkv", D, 3 * D), ("proj", D, D), ("fc1", D, F), ("fc2", F, D), ("lin1", D, 3 * D + F),
               ("lin2", D + F, D)]
+    if fp4:
+        scale_bytes, quantize, linear = FX.flux_mxfp4_scale_bytes, FX.flux_mxfp4_quantize, FX.flux_mxfp4_linear_fwd
+        gemm_cls, quant_cls, peak, tag = "gemm_256_mxfp4", "mxfp4_quantize", PEAK_FP4_TFLOPS, "mxfp4"
+    else:
+        scale_bytes, quantize, linear = FX.flux_mx_scale_bytes, FX.flux_mx_quantize, FX.flux_mxfp8_linear_fwd
+        gemm_cls, quant_cls, peak, tag = "gemm_256_mxfp8", "mx_quantize", PEAK_FP8_TFLOPS, "mxfp8"
+    cb = 2 if fp4 else 1   # values per code byte
     g = torch.Generator(device="cuda").manual_seed(1234)
     ops = []
     for name, K, N in shapes:
         x = (torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
         w = (torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
-        xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
-        xs = torch.empty((FX.flux_mx_scale_bytes(M, K),), dtype=torch.uint8, device="cuda")
-        wq = torch.empty((N, K), dtype=torch.uint8, device="cuda")
-        ws = torch.empty((FX.flux_mx_scale_bytes(N, K),), dtype=torch.uint8, device="cuda")
-        FX.flux_mx_quantize(FX.FLUX_PREC_BF16, w, N, K, wq, ws)
+        xq = torch.empty((M, K // cb), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((scale_bytes(M, K),), dtype=torch.uint8, device="cuda")
+        wq = torch.empty((N, K // cb), dtype=torch.uint8, device="cuda")
+        ws = torch.empty((scale_bytes(N, K),), dtype=torch.uint8, device="cuda")
+        quantize(FX.FLUX_PREC_BF16, w, N, K, wq, ws)
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         ops.append((name, K, N, x, xq, xs, wq, ws, y))
         del w
@@ -282,8 +290,8 @@ def mx_linears_bench(args) -> int:
 
     def step():
         for name, K, N, x, xq, xs, wq, ws, y in ops:
-            FX.flux_mx_quantize(FX.FLUX_PREC_BF16, x, M, K, xq, xs)
-            FX.flux_mxfp8_linear_fwd(M, N, K, xq, xs, wq, ws, None, y, N)
+            quantize(FX.FLUX_PREC_BF16, x, M, K, xq, xs)
+            linear(M, N, K, xq, xs, wq, ws, None, y, N)
 
     for _ in range(args.warmup):
         step()
@@ -300,25 +308,27 @@ def mx_linears_bench(args) -> int:
     kernels = FX.flux_timing_read()
     ms_step = e0.elapsed_time(e1) / args.steps
     flops = sum(2.0 * M * N * K for _, K, N, *_ in ops)
-    gms, gn, gw = kernels["gemm_256_mxfp8"]
-    qms, qn, qw = kernels["mx_quantize"]
+    gms, gn, gw = kernels[gemm_cls]
+    qms, qn, qw = kernels[quant_cls]
     assert abs(gw / args.steps - flops) <= 1e-6 * flops
     tflops = gw / (gms * 1e-3) / 1e12
     assert bool(torch.isfinite(ops[-1][-1]).all())
+    elem = "E2M1" if fp4 else "E4M3"
     rec = {
-        "metric": "MXFP8 block-linear TFLOP/s (the six token-path linears of the Flux-12B block pair, batch 4, "
-                  "inputs quantized every step)",
+        "metric": f"{tag.upper()} block-linear TFLOP/s (the six token-path linears of the Flux-12B block pair, "
+                  "batch 4, inputs quantized every step)",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp8_e4m3 (E8M0 scale per 32 values along K)", "data": "synthetic",
-        "config": {"workload": "flux12b_block_pair_mxfp8_linears", "rows": M, "hidden": D, "mlp_hidden": F,
+        "vs_baseline": None, "dtype": f"{tag}_{elem.lower()} (E8M0 scale per 32 values along K)",
+        "data": "synthetic",
+        "config": {"workload": f"flux12b_block_pair_{tag}_linears", "rows": M, "hidden": D, "mlp_hidden": F,
                    "linears": [n for n, *_ in shapes]},
-        "roofline": {"kernel": "gemm_256_mxfp8", "bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "roofline": {"kernel": gemm_cls, "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": None, "flops_per_launch": gw / gn, "ms_per_launch": round(gms / gn, 5)},
-        "kernels": {"gemm_256_mxfp8": {"ms_per_launch": round(gms / gn, 5), "tflops": round(tflops, 2)},
-                    "mx_quantize": {"ms_per_launch": round(qms / qn, 5),
-                                    "gbs": round(qw / (qms * 1e-3) / 1e9, 1)}},
+        "kernels": {gemm_cls: {"ms_per_launch": round(gms / gn, 5), "tflops": round(tflops, 2)},
+                    quant_cls: {"ms_per_launch": round(qms / qn, 5),
+                                "gbs": round(qw / (qms * 1e-3) / 1e9, 1)}},
         "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
@@ -498,7 +508,7 @@ def main() -> int:
     ap.add_argument("--workload", default="flux12b_blocks",
                     choices=["flux12b_blocks", "flux12b_full", "flux12b_blocks_fp8", "flux12b_blocks_seq",
                              "flux12b_sample_cfg", "flux12b_mxfp8_linears", "flux12b_blocks_train",
-                             "flux12b_attention_fp8"],
+                             "flux12b_attention_fp8", "flux12b_mxfp4_linears"],
                     help="flux12b_blocks (default): the block-pair step the headline metric is quoted on; "
                          "flux12b_full: the whole 19 + 38 block forward + loss at batch 2 (block weights "
                          "drawn on the device; no CPU baseline); flux12b_blocks_fp8: the block pair at batch 4 "
@@ -510,7 +520,7 @@ def main() -> int:
                          "token-path linears of the block pair at batch 4 as MXFP8 linears; "
                          "flux12b_blocks_train: a whole rectified-flow training step (forward and backward) of the "
                          "block-pair model at batch 1; flux12b_attention_fp8: the joint attention of the block "
-                         "shape with E4M3 operands")
+                         "shape with E4M3 operands; flux12b_mxfp4_linears: the six linears as MXFP4 linears")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -533,6 +543,8 @@ def main() -> int:
 
     if args.workload == "flux12b_mxfp8_linears":
         return mx_linears_bench(args)
+    if args.workload == "flux12b_mxfp4_linears":
+        return mx_linears_bench(args, fp4=True)
     if args.workload == "flux12b_blocks_train":
         return train_bench(args)
     if args.workload == "flux12b_attention_fp8":

@@ -653,6 +653,58 @@ flux_status flux_mxfp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t
   return FLUX_OK;
 }
 
+// ---------------------------------- MXFP4 ----------------------------------
+size_t flux_mxfp4_scale_bytes(int32_t rows, int32_t k) {
+  if (rows < 1 || k < 128 || k % 128 != 0) return 0;
+  return mx_scale_bytes(rows, k);
+}
+
+flux_status flux_mxfp4_quantize(int32_t src_precision, const void* src, int32_t rows, int32_t k, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(src_precision == FLUX_PREC_F32 || src_precision == FLUX_PREC_BF16,
+          "src_precision must be FLUX_PREC_F32 or FLUX_PREC_BF16 (got %d)", src_precision);
+  REQUIRE(rows >= 1 && k >= 128 && k % 128 == 0, "rows must be >= 1 and k a positive multiple of 128");
+  REQUIRE((int64_t)rows * k < ((int64_t)1 << 36), "problem too large");
+  REQUIRE(src && codes && scales, "src, codes and scales are required");
+  REQUIRE(aligned16(src) && aligned16(codes) && aligned16(scales), "pointers must be 16-byte aligned");
+  const int64_t sbytes = (int64_t)rows * k * (src_precision == FLUX_PREC_F32 ? 4 : 2);
+  const int64_t cbytes = (int64_t)rows * (k / 2), scb = (int64_t)mx_scale_bytes(rows, k);
+  REQUIRE(!ranges_overlap(codes, cbytes, src, sbytes) && !ranges_overlap(scales, scb, src, sbytes) &&
+              !ranges_overlap(scales, scb, codes, cbytes),
+          "codes, scales and src must not overlap");
+  FLUX_HIP(launch_mxfp4_quantize(src, src_precision == FLUX_PREC_F32 ? kF32 : kBF16, rows, k, codes, scales,
+                                 static_cast<hipStream_t>(stream)),
+           "MXFP4 quantize");
+  return FLUX_OK;
+}
+
+flux_status flux_mxfp4_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* x, const uint8_t* x_scales,
+                                  const uint8_t* w, const uint8_t* w_scales, const void* b, float* y, int64_t ldy,
+                                  void* stream) {
+  g_err[0] = 0;
+  REQUIRE(m >= 1 && n >= 1 && k >= 1, "m, n, k must be >= 1");
+  REQUIRE(x && x_scales && w && w_scales && y, "x, x_scales, w, w_scales and y are required");
+  REQUIRE(aligned16(x) && aligned16(w) && aligned16(x_scales) && aligned16(w_scales) && aligned16(y) &&
+              (!b || aligned16(b)),
+          "pointers must be 16-byte aligned");
+  if (k % 256 != 0 || k < 512)
+    return fail(FLUX_ERR_UNSUPPORTED, "MXFP4 linear needs k %% 256 == 0 and k >= 512 (got %d)", k);
+  if (n % 4 != 0) return fail(FLUX_ERR_UNSUPPORTED, "n must be a multiple of 4 (got %d)", n);
+  REQUIRE(ldy >= n && ldy % 4 == 0, "ldy must be >= n and a multiple of 4");
+  REQUIRE((int64_t)m * (k / 2) < ((int64_t)1 << 32) && (int64_t)n * (k / 2) < ((int64_t)1 << 32),
+          "x and w must each span less than 4 GiB");
+  GemmBatch g{};
+  g.count = 1;
+  g.p[0] = gemm_problem(x, rmap((int64_t)m * (k / 2), k / 2, m), w, b, m, n, k, kEpiStoreF32, y,
+                        rmap((int64_t)m * ldy, ldy, m));
+  g.p[0].ldw = k / 2;
+  g.p[0].sa = x_scales;
+  g.p[0].sb = w_scales;
+  FLUX_HIP(launch_gemm(g, kMXFP4, static_cast<hipStream_t>(stream)), "MXFP4 linear GEMM");
+  return FLUX_OK;
+}
+
 flux_status flux_fp8_quantize_current(int32_t src_precision, const void* src, int64_t n, flux_fp8_tensor* rec,
                                       uint8_t* dst, void* stream) {
   g_err[0] = 0;

@@ -780,10 +780,24 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 template <int S> using SetTag = std::integral_constant<int, S>;
 
-template <int EPI, bool MX>
+// Operand formats of gemm_fp8_kernel.  MXFP4 ("FP8 training for Flux models",
+// Configuration, the microscaling recipes; OCP MX v1.0): a 64-byte stage row
+// holds 128 E2M1 values, four 32-value MX blocks, one per 16-byte chunk.  The
+// lane-half split is the one of E4M3: chunk h feeds the first fp4 MFMA of the
+// stage and chunk 2 + h the second, each taking its low 16 bytes as the
+// operand (the fp4 form of the instruction reads four registers).  A and W
+// are packed alike, so whatever order the hardware gives the values inside a
+// lane half, both operands agree on it.  The E8M0 scale a lane half passes
+// covers exactly the 32 values it supplies; a lane's scales of both MFMAs are
+// adjacent dwords (launch_mxfp4_quantize), loaded as one 8-byte word.
+constexpr int kFmtE4M3 = 0, kFmtMx8 = 1, kFmtMx4 = 2;
+
+template <int EPI, int FMT>
 __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
+  constexpr bool MX = FMT != kFmtE4M3, FP4 = FMT == kFmtMx4;
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
-  constexpr int BK8 = 64;   // k values (bytes) per stage row
+  constexpr int BK8 = 64;   // bytes per stage row: 64 E4M3 or 128 E2M1 values
+  constexpr int SCS = FP4 ? 512 : 256;   // scale bytes of one stage for a wave's 128 rows
   __shared__ __attribute__((aligned(1024))) char smem[kDlStages * kDlStageBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -808,13 +822,13 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   const char* abase = nullptr;
   const char* wbase = nullptr;
   uint32_t src[8];
-  // MX: the lane's scale dwords of step kt at sca + kt * 256 (A rows of the
-  // wave) and scb + kt * 256 (W rows), loaded two steps ahead of use: cur
-  // holds step kt's, nxt step kt + 1's
+  // MX: the lane's scale word of step kt at sca + kt * SCS (A rows of the
+  // wave) and scb + kt * SCS (W rows), loaded two steps ahead of use: cur
+  // holds step kt's, nxt step kt + 1's (MXFP8 uses .x only)
   const uint8_t* sca = nullptr;   // wave-uniform: lane offset sc_lane added at the load
   const uint8_t* scb = nullptr;
-  const int sc_lane = fhalf * 128 + frow * 4;
-  uint32_t cur_a = 0u, cur_b = 0u, nxt_a = 0u, nxt_b = 0u;
+  const int sc_lane = FP4 ? fhalf * 256 + frow * 8 : fhalf * 128 + frow * 4;
+  uint2 cur_a = {0u, 0u}, cur_b = {0u, 0u}, nxt_a = {0u, 0u}, nxt_b = {0u, 0u};
   auto setup = [&](int t) {
     const TileCoord tc = decode_tile_id(bt, t, BM, BN);
     GemmProblem p = bt.p[0];
@@ -822,10 +836,10 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
     prob = tc.prob;
     m0 = tc.tm * BM;
     n0 = tc.tn * BN;
-    KT = p.K / BK8;
+    KT = FP4 ? p.K / (2 * BK8) : p.K / BK8;
     if constexpr (MX) {
-      sca = p.sa + (size_t)(m0 / 128 + wm) * KT * 256;
-      scb = p.sb + (size_t)(n0 / 128 + wn) * KT * 256;
+      sca = p.sa + (size_t)(m0 / 128 + wm) * KT * SCS;
+      scb = p.sb + (size_t)(n0 / 128 + wn) * KT * SCS;
     }
     abase = reinterpret_cast<const char*>(p.A);
     wbase = reinterpret_cast<const char*>(p.W);
@@ -855,10 +869,15 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
       __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)(st + ins * 1024), 16, 0, 0);
     }
   };
-  auto ld_scale = [&](int kk, uint32_t& a, uint32_t& b) {
+  auto ld_scale = [&](int kk, uint2& a, uint2& b) {
     const int kc = kk < KT ? kk : KT - 1;
-    a = *reinterpret_cast<const uint32_t*>(sca + (size_t)kc * 256 + sc_lane);
-    b = *reinterpret_cast<const uint32_t*>(scb + (size_t)kc * 256 + sc_lane);
+    if constexpr (FP4) {
+      a = *reinterpret_cast<const uint2*>(sca + (size_t)kc * SCS + sc_lane);
+      b = *reinterpret_cast<const uint2*>(scb + (size_t)kc * SCS + sc_lane);
+    } else {
+      a.x = *reinterpret_cast<const uint32_t*>(sca + (size_t)kc * SCS + sc_lane);
+      b.x = *reinterpret_cast<const uint32_t*>(scb + (size_t)kc * SCS + sc_lane);
+    }
   };
   auto prologue_issue = [&]() {
     const int pre = KT < 4 ? KT : 4;
@@ -895,20 +914,44 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
     else
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
   };
+  // MXFP4: fp4 MFMA (i, j) on chunk C (0: chunk h, 1: chunk 2 + h) of the
+  // stage; the upper half of the 8-register operand is left undefined
+  auto mma4_ij = [&](auto set, auto ic, auto jc, auto cc, uint32_t sa_w, uint32_t sb_w) {
+    constexpr int S = decltype(set)::value, i = decltype(ic)::value, j = decltype(jc)::value;
+    constexpr int C = decltype(cc)::value;
+    const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[S][j][C], fb[S][j][C], 0, 1, 2, 3, -1, -1, -1, -1));
+    const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[S][i][C], fa[S][i][C], 0, 1, 2, 3, -1, -1, -1, -1));
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, i, (int)sa_w, j, (int)sb_w);
+  };
   auto mma = [&](auto set) {
-    const uint32_t sa_w = cur_a, sb_w = cur_b;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    mma_ij(set, I0{}, I0{}, sa_w, sb_w); mma_ij(set, I1{}, I0{}, sa_w, sb_w);
-    mma_ij(set, I2{}, I0{}, sa_w, sb_w); mma_ij(set, I3{}, I0{}, sa_w, sb_w);
-    mma_ij(set, I0{}, I1{}, sa_w, sb_w); mma_ij(set, I1{}, I1{}, sa_w, sb_w);
-    mma_ij(set, I2{}, I1{}, sa_w, sb_w); mma_ij(set, I3{}, I1{}, sa_w, sb_w);
-    mma_ij(set, I0{}, I2{}, sa_w, sb_w); mma_ij(set, I1{}, I2{}, sa_w, sb_w);
-    mma_ij(set, I2{}, I2{}, sa_w, sb_w); mma_ij(set, I3{}, I2{}, sa_w, sb_w);
-    mma_ij(set, I0{}, I3{}, sa_w, sb_w); mma_ij(set, I1{}, I3{}, sa_w, sb_w);
-    mma_ij(set, I2{}, I3{}, sa_w, sb_w); mma_ij(set, I3{}, I3{}, sa_w, sb_w);
+    if constexpr (FP4) {
+      auto half = [&](auto cc, uint32_t sa_w, uint32_t sb_w) {
+        mma4_ij(set, I0{}, I0{}, cc, sa_w, sb_w); mma4_ij(set, I1{}, I0{}, cc, sa_w, sb_w);
+        mma4_ij(set, I2{}, I0{}, cc, sa_w, sb_w); mma4_ij(set, I3{}, I0{}, cc, sa_w, sb_w);
+        mma4_ij(set, I0{}, I1{}, cc, sa_w, sb_w); mma4_ij(set, I1{}, I1{}, cc, sa_w, sb_w);
+        mma4_ij(set, I2{}, I1{}, cc, sa_w, sb_w); mma4_ij(set, I3{}, I1{}, cc, sa_w, sb_w);
+        mma4_ij(set, I0{}, I2{}, cc, sa_w, sb_w); mma4_ij(set, I1{}, I2{}, cc, sa_w, sb_w);
+        mma4_ij(set, I2{}, I2{}, cc, sa_w, sb_w); mma4_ij(set, I3{}, I2{}, cc, sa_w, sb_w);
+        mma4_ij(set, I0{}, I3{}, cc, sa_w, sb_w); mma4_ij(set, I1{}, I3{}, cc, sa_w, sb_w);
+        mma4_ij(set, I2{}, I3{}, cc, sa_w, sb_w); mma4_ij(set, I3{}, I3{}, cc, sa_w, sb_w);
+      };
+      half(I0{}, cur_a.x, cur_b.x);
+      half(I1{}, cur_a.y, cur_b.y);
+    } else {
+      const uint32_t sa_w = cur_a.x, sb_w = cur_b.x;
+      mma_ij(set, I0{}, I0{}, sa_w, sb_w); mma_ij(set, I1{}, I0{}, sa_w, sb_w);
+      mma_ij(set, I2{}, I0{}, sa_w, sb_w); mma_ij(set, I3{}, I0{}, sa_w, sb_w);
+      mma_ij(set, I0{}, I1{}, sa_w, sb_w); mma_ij(set, I1{}, I1{}, sa_w, sb_w);
+      mma_ij(set, I2{}, I1{}, sa_w, sb_w); mma_ij(set, I3{}, I1{}, sa_w, sb_w);
+      mma_ij(set, I0{}, I2{}, sa_w, sb_w); mma_ij(set, I1{}, I2{}, sa_w, sb_w);
+      mma_ij(set, I2{}, I2{}, sa_w, sb_w); mma_ij(set, I3{}, I2{}, sa_w, sb_w);
+      mma_ij(set, I0{}, I3{}, sa_w, sb_w); mma_ij(set, I1{}, I3{}, sa_w, sb_w);
+      mma_ij(set, I2{}, I3{}, sa_w, sb_w); mma_ij(set, I3{}, I3{}, sa_w, sb_w);
+    }
   };
   // Stage kt's fragments are in set S.  Wait until stage kt+1 has landed for
   // every wave (VM: loads allowed to stay outstanding, i.e. those of the
@@ -920,7 +963,7 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   // 8 to 20 / 12 (loads issued after the stage being waited for).
   auto body = [&](int kt, auto set, auto vm, auto next, auto refill) {
     constexpr int S = decltype(set)::value;
-    uint32_t nn_a = 0u, nn_b = 0u;
+    uint2 nn_a = {0u, 0u}, nn_b = {0u, 0u};
     if constexpr (decltype(next)::value) {
       constexpr int VM = decltype(vm)::value;
       if constexpr (MX) {
@@ -933,13 +976,14 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
       if constexpr (decltype(refill)::value) issue(kt + 4);
       lfrag(kt + 1, SetTag<1 - S>{});
       mma(SetTag<S>{});
+      constexpr int MF = FP4 ? 2 : 1;   // MFMAs per interleave slot
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 * MF, 0);
     } else {
       mma(SetTag<S>{});
     }
@@ -1134,9 +1178,11 @@ static bool fp8_span_ok(const GemmProblem& q) {
 template <int OP, int EPI>
 static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream) {
   if constexpr (OP == kFP8)
-    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, false>), dim3(grid), dim3(256), 0, stream, big);
+    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtE4M3>), dim3(grid), dim3(256), 0, stream, big);
   else if constexpr (OP == kMXFP8)
-    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, true>), dim3(grid), dim3(256), 0, stream, big);
+    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtMx8>), dim3(grid), dim3(256), 0, stream, big);
+  else if constexpr (OP == kMXFP4)
+    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtMx4>), dim3(grid), dim3(256), 0, stream, big);
   else
     hipLaunchKernelGGL((gemm_dl_kernel<OP, EPI>), dim3(grid), dim3(256), 0, stream, big);
 }
@@ -1195,26 +1241,30 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   }
 }
 
-// MXFP8: always the persistent kernel (its K loop needs K % 128 == 0, K >= 256, checked
-// by the API), one or two problems sharing the epilogue kind.
+// MX operands: always the persistent kernel (its K loop needs an even number
+// of at least 4 stages: MXFP8 K % 128 == 0 and K >= 256, MXFP4 K % 256 == 0
+// and K >= 512, checked by the API), one or two problems sharing the epilogue
+// kind.
+template <int OP>
 static void launch_mx(GemmBatch bt, hipStream_t stream, double flops) {
   bt.ksplit = 1;
   const int tiles = assign_tiles(bt, 256, 256);
   const int grid = tiles < 256 ? tiles : 256;
-  TimingScope ts(kKcGemmPkMx, stream, flops);
+  TimingScope ts(OP == kMXFP4 ? kKcGemmPkMx4 : kKcGemmPkMx, stream, flops);
   switch (bt.p[0].epi) {
-    case kEpiStore: launch_persistent<kMXFP8, kEpiStore>(bt, grid, stream); break;
-    case kEpiGelu: launch_persistent<kMXFP8, kEpiGelu>(bt, grid, stream); break;
-    case kEpiResid: launch_persistent<kMXFP8, kEpiResid>(bt, grid, stream); break;
-    case kEpiStoreF32: launch_persistent<kMXFP8, kEpiStoreF32>(bt, grid, stream); break;
-    default: launch_persistent<kMXFP8, kEpiSplitGelu>(bt, grid, stream); break;
+    case kEpiStore: launch_persistent<OP, kEpiStore>(bt, grid, stream); break;
+    case kEpiGelu: launch_persistent<OP, kEpiGelu>(bt, grid, stream); break;
+    case kEpiResid: launch_persistent<OP, kEpiResid>(bt, grid, stream); break;
+    case kEpiStoreF32: launch_persistent<OP, kEpiStoreF32>(bt, grid, stream); break;
+    default: launch_persistent<OP, kEpiSplitGelu>(bt, grid, stream); break;
   }
 }
 
 hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
   const double flops = gemm_flops(bt);
-  if (op == kMXFP8) {
-    launch_mx(bt, stream, flops);
+  if (op == kMXFP8 || op == kMXFP4) {
+    if (op == kMXFP8) launch_mx<kMXFP8>(bt, stream, flops);
+    else launch_mx<kMXFP4>(bt, stream, flops);
     return hipGetLastError();
   }
   if (op == kF32) {

@@ -21,6 +21,11 @@ constexpr int kFP8 = 4;
 // MXFP8 (OCP MX, E4M3 elements): as a GEMM operand type, E4M3 bytes of A and W
 // with one E8M0 scale per 32 values along K, applied by the scaled MFMA.
 constexpr int kMXFP8 = 5;
+// MXFP4 (OCP MX, E2M1 elements): as a GEMM operand type, A and W rows of
+// packed E2M1 codes (two per byte, the even element in the low nibble; K counts
+// values, the row strides amap.ld and ldw count bytes) with one E8M0 scale per
+// 32 values along K in the layout of launch_mxfp4_quantize.
+constexpr int kMXFP4 = 6;
 
 // ---------------------------------------------------------------------------
 // Row addressing shared by the token-wise kernels.  A logical row r of a
@@ -57,8 +62,8 @@ struct GemmProblem {
   const flux_fp8_tensor* qa;            // kFP8 operands: records A and W were quantized with;
   const flux_fp8_tensor* qw;            //   the accumulator is multiplied by both scale_inv
   flux_fp8_tensor* qo;                  // kFP8 output (out0 of kEpiGelu, out1 of kEpiSplitGelu)
-  const uint8_t* sa;                    // kMXFP8 operands: E8M0 block scales of A and W in the
-  const uint8_t* sb;                    //   GEMM layout of launch_mx_quantize (null otherwise)
+  const uint8_t* sa;                    // kMXFP8 / kMXFP4 operands: E8M0 block scales of A and W in
+  const uint8_t* sb;                    //   the GEMM layout of their quantizer (null otherwise)
   int32_t tile_begin;                   // filled by the launcher
   int32_t tiles_n;                      // filled by the launcher
 };
@@ -283,6 +288,15 @@ hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStr
 inline size_t mx_scale_bytes(int64_t rows, int64_t k) { return (size_t)(((rows + 255) / 256) * 256 * (k / 32)); }
 hipError_t launch_mx_quantize(const void* src, int src_dtype, int rows, int k, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream);
+// MXFP4: codes [rows, k / 2] (two E2M1 codes a byte, the even element in the
+// low nibble) and one E8M0 byte per 32 values, k a multiple of 128.  The scale
+// layout serves the two fp4 MFMAs of one 128-value stage of the persistent
+// GEMM with a single 8-byte load per lane: the byte of (row, block kb) sits at
+//   ((row / 128) * (k / 128) + kb / 4) * 512 + (kb % 2) * 256 + (row % 32) * 8
+//     + ((kb % 4) / 2) * 4 + (row / 32) % 4.
+// The byte count is that of mx_scale_bytes (rows padded to 256).
+hipError_t launch_mxfp4_quantize(const void* src, int src_dtype, int rows, int k, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
 
 // ---------------------------------- fp8 ------------------------------------
 // dst = e4m3(src * scale(rec)); rec->amax_bits raised to max |src|.  src_dtype kF32 or kBF16.

@@ -952,6 +952,85 @@ hipError_t launch_mx_quantize(const void* src, int src_dtype, int rows, int k, u
   return hipGetLastError();
 }
 
+// MXFP4 quantization (OCP MX v1.0 with E2M1 elements, the fp4 sibling of
+// the recipe above): the block exponent is X = floor(log2 max|v|) - 2, 2 being
+// the exponent of E2M1's largest value 6 = 1.5 * 2^2, clamped to [-127, 127]
+// (-127 for an all-zero block; NaN byte 0xFF and unscaled elements for a block
+// holding a non-finite value).  v * 2^-X is exact and lies below 8; it rounds
+// to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code (the
+// one whose mantissa bit is 0), and saturates at 6.
+// ===========================================================================
+// E2M1 code of a finite float: the magnitude code counts the grid midpoints
+// below |v|.  A midpoint between code 2c and 2c + 1 goes down (to the even
+// code), one between 2c + 1 and 2c + 2 goes up; bit 3 is the sign.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                     (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) mxfp4_quantize_kernel(const T* __restrict__ src, int rows, int k, int rows_pad,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  const int per_row = k / 8;   // k is a multiple of 128: groups of 4 lanes never straddle rows
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= (int64_t)rows_pad * per_row) return;   // whole groups of 4 lanes leave together
+  const int row = (int)(g / per_row), c8 = (int)(g % per_row);
+  float v[8];
+  if (row < rows) {
+    load8<T>(src + (int64_t)row * k + c8 * 8, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i]));   // NaN patterns sort above infinity
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  uint32_t sbyte;
+  float inv = 1.0f;
+  if (m >= 0x7f800000u) {
+    sbyte = 0xFFu;   // non-finite block: NaN scale, elements unscaled
+  } else {
+    // floor(log2 m) for a normal m; any subnormal m gives X = -127 anyway
+    const int e = m >= 0x00800000u ? (int)(m >> 23) - 127 : -127;
+    int X = m == 0u ? -127 : e - 2;
+    X = X < -127 ? -127 : X;
+    sbyte = (uint32_t)(X + 127);
+    inv = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X, a normal float for X in [-127, 125]
+  }
+  if (row < rows) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o |= e2m1_code(v[i] * inv) << (4 * i);
+    *reinterpret_cast<uint32_t*>(codes + (int64_t)row * (k / 2) + c8 * 4) = o;
+  }
+  if ((c8 & 3) == 0) {
+    const int kb = c8 >> 2, q = kb & 3;
+    const int64_t idx = ((int64_t)(row >> 7) * (k >> 7) + (kb >> 2)) * 512 + (q & 1) * 256 + (row & 31) * 8 +
+                        (q >> 1) * 4 + ((row >> 5) & 3);
+    scales[idx] = (uint8_t)sbyte;
+  }
+}
+
+hipError_t launch_mxfp4_quantize(const void* src, int src_dtype, int rows, int k, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  const int rows_pad = ((rows + 255) / 256) * 256;
+  const int64_t threads = (int64_t)rows_pad * (k / 8);
+  const dim3 grid((unsigned)ceil_div(threads, 256));
+  TimingScope ts(kKcMx4Quant, stream, (double)rows * k * ((src_dtype == kBF16 ? 2.0 : 4.0) + 0.5 + 1.0 / 32));
+  if (src_dtype == kBF16)
+    hipLaunchKernelGGL(mxfp4_quantize_kernel<bf16_t>, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(src),
+                       rows, k, rows_pad, codes, scales);
+  else
+    hipLaunchKernelGGL(mxfp4_quantize_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(src), rows,
+                       k, rows_pad, codes, scales);
+  return hipGetLastError();
+}
+
 // ===========================================================================
 // dst = e4m3(src * scale(rec)) over a whole tensor (the weight cast of a
 // forward); each thread converts 16 consecutive elements per step, and one

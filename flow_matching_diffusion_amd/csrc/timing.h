@@ -21,6 +21,8 @@ enum KernelClass : int {
   kKcMxQuant,         // MXFP8 quantization
   kKcAttnBwd,         // attention backward (dK / dV and dQ kernels)
   kKcBwdElem,         // backward row-wise, element-wise, transpose and reduction kernels
+  kKcGemmPkMx4,       // gemm_fp8_kernel on MXFP4 operands
+  kKcMx4Quant,        // MXFP4 quantization
   kKcCount
 };
 

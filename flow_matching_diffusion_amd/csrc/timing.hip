@@ -37,7 +37,8 @@ hipEvent_t take_event() {
 const char* kNames[kKcCount] = {"gemm_256_f16", "gemm_256_bf16", "gemm_128x128", "gemm_f32", "attention",
                                 "ln_modulate",       "gemv",              "qk_prep",  "rf_noise_loss",
                                 "misc",        "gemm_256_fp8",       "fp8_quantize",
-                                "gemm_256_mxfp8", "mx_quantize", "attention_bwd", "bwd_elementwise"};
+                                "gemm_256_mxfp8", "mx_quantize", "attention_bwd", "bwd_elementwise",
+                                "gemm_256_mxfp4", "mxfp4_quantize"};
 }  // namespace
 
 TimingScope::TimingScope(int cls, hipStream_t s, double work) : cls_(cls), work_(work), stream_(s), start_(nullptr) {

@@ -45,7 +45,8 @@ EXPORTED = (
     "flux_single_fwd_train", "flux_single_bwd", "flux_attention_train_workspace_bytes", "flux_attention_fwd_train",
     "flux_attention_bwd", "flux_rf_loss_grad", "flux_final_bwd_workspace_bytes", "flux_final_bwd",
     "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
-    "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd",
+    "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd", "flux_mxfp4_scale_bytes", "flux_mxfp4_quantize",
+    "flux_mxfp4_linear_fwd",
 )
 
 
@@ -143,6 +144,8 @@ def lib() -> C.CDLL:
         "flux_euler_step": [P(flux_euler_args), vp],
         "flux_mx_quantize": [i32, vp, i32, i32, vp, vp, vp],
         "flux_mxfp8_linear_fwd": [i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
+        "flux_mxfp4_quantize": [i32, vp, i32, i32, vp, vp, vp],
+        "flux_mxfp4_linear_fwd": [i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
         "flux_final_fwd": [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
         "flux_attention_fwd": [i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, i64, vp, sz, vp],
@@ -182,6 +185,8 @@ def lib() -> C.CDLL:
     L.flux_rf_workspace_bytes.restype = sz
     L.flux_mx_scale_bytes.argtypes = [i32, i32]
     L.flux_mx_scale_bytes.restype = sz
+    L.flux_mxfp4_scale_bytes.argtypes = [i32, i32]
+    L.flux_mxfp4_scale_bytes.restype = sz
     L.flux_embed_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.flux_embed_workspace_bytes.restype = sz
     L.flux_final_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -409,6 +414,32 @@ def mx_scales_unswizzle(sc, rows: int, k: int):
     # byte (((row/128)*(k/64) + kb/2)*2 + kb%2)*128 + (row%32)*4 + (row/32)%4
     t = s[: rp * (k // 32)].reshape(rp // 128, k // 64, 2, 32, 4)      # [rb, kt, h, l32, i]
     t = t.transpose(0, 4, 3, 1, 2).reshape(rp, k // 32)                 # rows rb*128 + i*32 + l32
+    return t[:rows]
+
+
+def flux_mxfp4_scale_bytes(rows: int, k: int) -> int:
+    return lib().flux_mxfp4_scale_bytes(rows, k)
+
+
+def flux_mxfp4_quantize(src_precision: int, src, rows: int, k: int, codes, scales, stream=None) -> None:
+    _check(lib().flux_mxfp4_quantize(src_precision, ptr(src), rows, k, ptr(codes), ptr(scales), _stream(stream)),
+           "flux_mxfp4_quantize")
+
+
+def flux_mxfp4_linear_fwd(m: int, n: int, k: int, x, x_scales, w, w_scales, b, y, ldy: int, stream=None) -> None:
+    _check(lib().flux_mxfp4_linear_fwd(m, n, k, ptr(x), ptr(x_scales), ptr(w), ptr(w_scales), ptr(b), ptr(y), ldy,
+                                       _stream(stream)), "flux_mxfp4_linear_fwd")
+
+
+def mxfp4_scales_unswizzle(sc, rows: int, k: int):
+    """[rows, k/32] scale bytes from the GEMM layout of flux_mxfp4_quantize
+    (numpy uint8 array in, numpy out; pad rows dropped)."""
+    import numpy as np
+    s = np.asarray(sc, dtype=np.uint8)
+    rp = ((rows + 255) // 256) * 256
+    # byte ((row/128)*(k/128) + kb/4)*512 + (kb%2)*256 + (row%32)*8 + ((kb%4)/2)*4 + (row/32)%4
+    t = s[: rp * (k // 32)].reshape(rp // 128, k // 128, 2, 32, 2, 4)   # [rb, kt, kb%2, l32, (kb%4)/2, i]
+    t = t.transpose(0, 5, 3, 1, 4, 2).reshape(rp, k // 32)              # rows rb*128 + i*32 + l32; kb = 4kt+2m+h
     return t[:rows]
 
 

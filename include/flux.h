@@ -454,6 +454,43 @@ flux_status flux_mxfp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t
                                   const uint8_t* w, const uint8_t* w_scales, const void* b, float* y, int64_t ldy,
                                   void* stream);
 
+/*
+ * MXFP4 linears (OCP MX v1.0 with E2M1 elements: the fp4 member of the
+ * microscaling family whose fp8 member is the "mxfp8" recipe of "FP8 training
+ * for Flux models", Configuration): each 32 consecutive values along K share
+ * one E8M0 power-of-two scale, applied inside gfx950's scaled MFMA in its fp4
+ * form.
+ *
+ * flux_mxfp4_scale_bytes -- bytes of the scale array of a [rows, k] operand
+ *   (rows rounded up to a multiple of 256, times k / 32); 0 unless rows >= 1
+ *   and k is a positive multiple of 128.
+ *
+ * flux_mxfp4_quantize -- codes [rows, k / 2] (row-major bytes, two E2M1 codes
+ *   each, the even-indexed element in the low nibble; code bit 3 is the sign,
+ *   bits 2-1 the exponent with bias 1, bit 0 the mantissa) and scales of src
+ *   [rows, k] (FLUX_PREC_F32 float or FLUX_PREC_BF16, row-major): block
+ *   exponent X = floor(log2 max|v|) - 2 clamped to [-127, 127] (-127 for an
+ *   all-zero block), scale byte X + 127 (0xFF for a block holding a
+ *   non-finite value, whose elements are then encoded unscaled), code =
+ *   e2m1(v * 2^-X) rounded to nearest with ties to the even code and
+ *   saturation to +-6.  The scale byte of (row, block kb) is at
+ *   ((row/128)*(k/128) + kb/4)*512 + (kb%2)*256 + (row%32)*8 + ((kb%4)/2)*4
+ *   + (row/32)%4; pad rows get the all-zero block's byte.  k a multiple of
+ *   128; pointers 16-byte aligned; codes and scales must not overlap src.
+ *
+ * flux_mxfp4_linear_fwd -- y = sum over K blocks of 2^(X_x + X_w) (x_q w_q^T)
+ *   + b: x [M, K / 2 bytes] and w [N, K / 2 bytes] as written by
+ *   flux_mxfp4_quantize, b [N] bf16 or NULL, y [M, N] float (row stride ldy).
+ *   K counts values: a multiple of 256 and at least 512 (else
+ *   FLUX_ERR_UNSUPPORTED); N a multiple of 4.
+ */
+size_t flux_mxfp4_scale_bytes(int32_t rows, int32_t k);
+flux_status flux_mxfp4_quantize(int32_t src_precision, const void* src, int32_t rows, int32_t k, uint8_t* codes,
+                                uint8_t* scales, void* stream);
+flux_status flux_mxfp4_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t* x, const uint8_t* x_scales,
+                                  const uint8_t* w, const uint8_t* w_scales, const void* b, float* y, int64_t ldy,
+                                  void* stream);
+
 /* Workspace sizes (bytes).  op: 0 double block, 1 single block, 2 sequential single block;
  * 0 for invalid dims or op. */
 size_t flux_workspace_bytes(const flux_dims* dims, int32_t op);

@@ -175,3 +175,25 @@ def test_mx_scale_layout_helper():
             ref[row, kb] = v
             buf[(((row // 128) * (k // 64) + kb // 2) * 2 + kb % 2) * 128 + (row % 32) * 4 + (row // 32) % 4] = v
     assert np.array_equal(F.mx_scales_unswizzle(buf, rows, k), ref[:rows])
+
+
+def test_mxfp4_scale_layout_helper():
+    # the binding's unswizzle inverts the MXFP4 byte layout flux.h documents
+    import numpy as np
+    rows, k = 300, 384
+    rp = 512
+    assert F.flux_mxfp4_scale_bytes(rows, 320) == 0          # k must be a multiple of 128
+    buf = np.zeros(F.flux_mxfp4_scale_bytes(rows, k), dtype=np.uint8)
+    assert buf.size == rp * (k // 32)
+    ref = np.zeros((rp, k // 32), dtype=np.uint8)
+    seen = set()
+    for row in range(rp):
+        for kb in range(k // 32):
+            v = (row * 7 + kb * 13) % 251
+            ref[row, kb] = v
+            off = (((row // 128) * (k // 128) + kb // 4) * 512 + (kb % 2) * 256 + (row % 32) * 8
+                   + ((kb % 4) // 2) * 4 + (row // 32) % 4)
+            seen.add(off)
+            buf[off] = v
+    assert len(seen) == buf.size                               # the layout is a bijection
+    assert np.array_equal(F.mxfp4_scales_unswizzle(buf, rows, k), ref[:rows])
