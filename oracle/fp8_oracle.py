@@ -35,6 +35,14 @@ Readings taken where that page is silent (each repeated at its function):
      dec(code) * fp32(1 / s).  The GPU also packs the probabilities to E4M3
      (relative error <= 2^-4 each); the oracle keeps them exact and the test
      bounds that step.
+  F8 the "blockwise" alternative recipe the page lists: E4M3 elements with
+     one scale per tile along K, tiles of 1 x 128 values for activations (one
+     row) and 128 x 128 for weights (128 rows, the last tile of a ragged row
+     count holding the rows that exist); a tile's scale 2^e is the largest
+     power of two with amax * 2^e <= 448, e clamped to [-127, 127] (e = 0 for
+     an all-zero tile); elements are e4m3(v * 2^e), an exact product; the
+     linear is y = sum over 128-wide k blocks of 2^-(e_x + e_w) sum q_x q_w
+     + b.  A tile holding a non-finite value is not defined here.
 """
 from __future__ import annotations
 
@@ -45,7 +53,7 @@ import numpy as np
 from .flux_oracle import attention, f64, linear
 
 __all__ = ["E4M3_MAX", "HISTORY_LEN", "e4m3_decode", "e4m3_encode", "quantize", "amax", "fp8_linear",
-           "attention_fp8",
+           "attention_fp8", "BLOCK_K", "block_exponents", "block_quantize", "block_dequantize", "block_linear",
            "scale_update", "current_scale", "fp8_linears", "TOKEN_LINEARS_DOUBLE", "TOKEN_LINEARS_SINGLE"]
 
 E4M3_MAX = 448.0
@@ -168,3 +176,50 @@ def attention_fp8(q, k, v):
     scales = tuple(current_scale(x) for x in (q, k, v))
     deq = [e4m3_decode(quantize(x, sx)) * float(np.float32(1.0) / np.float32(sx)) for x, sx in zip((q, k, v), scales)]
     return attention(*deq), scales
+
+
+# ------------------------------- blockwise (F8) -------------------------------
+BLOCK_K = 128
+
+
+def block_exponents(x, tile_rows: int) -> np.ndarray:
+    """Exponent e of every tile_rows x 128 tile of x [R, K] (F8), int64
+    [ceil(R / tile_rows), K / 128]: the largest integer with amax * 2^e <= 448."""
+    x = f64(x)
+    R, K = x.shape
+    assert K % BLOCK_K == 0 and tile_rows >= 1
+    assert np.isfinite(x).all(), "blockwise tiles must be finite"
+    nt = -(-R // tile_rows)
+    a = np.zeros((nt, K // BLOCK_K))
+    for t in range(nt):
+        blk = np.abs(x[t * tile_rows:(t + 1) * tile_rows])
+        a[t] = blk.reshape(blk.shape[0], K // BLOCK_K, BLOCK_K).max(axis=(0, 2))
+    # a = m 2^E with m in [0.5, 1): a 2^e <= 448 = 0.875 2^9  <=>  m 2^(E + e) <= 0.875 2^9
+    m, E = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.where(m <= 0.875, 9 - E, 8 - E).astype(np.int64)
+    e = np.where(a > 0, e, 0)
+    return np.clip(e, -127, 127)
+
+
+def block_quantize(x, tile_rows: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(E4M3 codes [R, K], tile exponents) of x under F8."""
+    x = f64(x)
+    e = block_exponents(x, tile_rows)
+    per_row = np.repeat(e, tile_rows, axis=0)[: x.shape[0]]
+    return e4m3_encode(x * np.repeat(np.exp2(per_row.astype(np.float64)), BLOCK_K, axis=1)), e
+
+
+def block_dequantize(codes, e, tile_rows: int) -> np.ndarray:
+    codes = np.asarray(codes)
+    per_row = np.repeat(np.asarray(e, dtype=np.int64), tile_rows, axis=0)[: codes.shape[0]]
+    return e4m3_decode(codes) * np.repeat(np.exp2(-per_row.astype(np.float64)), BLOCK_K, axis=1)
+
+
+def block_linear(x, w, b=None) -> np.ndarray:
+    """x [M, K] in 1 x 128 tiles and w [N, K] in 128 x 128 tiles (F8),
+    y = deq(x) deq(w)^T (+ b) in fp64: every product of two E4M3 values and
+    two powers of two is exact, so this is F8's block sum up to fp64 rounding."""
+    xq, ex = block_quantize(x, 1)
+    wq, ew = block_quantize(w, 128)
+    y = block_dequantize(xq, ex, 1) @ block_dequantize(wq, ew, 128).T
+    return y + f64(b) if b is not None else y

@@ -279,3 +279,72 @@ def test_attention_fp8_error_bound():
     ref = O.attention(q, k, v)
     rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
     assert 1e-3 < rel < 5e-2, rel
+
+
+# ------------------------------ blockwise (F8) ------------------------------ #
+def test_block_exponent_is_the_largest_fitting_power_of_two():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((7, 384)) * np.exp2(rng.integers(-60, 60, size=(7, 3)).repeat(128, axis=1))
+    e = Q.block_exponents(x, 1)
+    a = np.abs(x).reshape(7, 3, 128).max(axis=-1)
+    # multiplying by a power of two is exact in fp64, so the defining bounds can be checked directly
+    assert np.all(a * np.exp2(e) <= 448.0) and np.all(a * np.exp2(e + 1) > 448.0)
+    # the boundary cases: 448 fits at e = 0, a hair above does not, 224 fits at e = 1
+    t = np.zeros((5, 128))
+    t[0, 5], t[1, 5], t[2, 5], t[3, 5] = 448.0, np.nextafter(448.0, 1e9), 224.0, 2.0 ** -140
+    assert Q.block_exponents(t, 1).ravel().tolist() == [0, -1, 1, 127, 0]   # clamp at 127; zero tile: 0
+
+
+def test_block_weight_tiles_share_one_scale():
+    rng = np.random.default_rng(42)
+    w = rng.standard_normal((300, 256)) * 0.02              # 3 row tiles, the last one ragged (44 rows)
+    e0 = Q.block_exponents(w, 128)
+    assert e0.shape == (3, 2)
+    w2 = w.copy()
+    w2[130, 200] = 100.0                                     # row tile 1, k block 1
+    e1 = Q.block_exponents(w2, 128)
+    changed = e1 != e0
+    assert changed[1, 1] and changed.sum() == 1
+    q0, _ = Q.block_quantize(w, 128)
+    q1, _ = Q.block_quantize(w2, 128)
+    diff_rows = np.unique(np.nonzero(q0 != q1)[0])
+    assert diff_rows.min() >= 128 and diff_rows.max() < 256   # only rows of that tile re-encode
+    assert np.all(np.nonzero(q0 != q1)[1] >= 128)             # and only in that k block
+    assert Q.block_exponents(w[256:], 128).tolist() == e0[2:].tolist()   # the ragged tile is its own rows
+
+
+def test_block_roundtrip_and_error_bound():
+    rng = np.random.default_rng(43)
+    # E4M3 values with each row's tile anchored at 448 and scaled by 2^-e: exact round trip
+    codes = rng.integers(0, 0x7F, size=(4, 256))
+    codes[:, ::128] = 0x7E                                   # 448
+    e = rng.integers(-20, 20, size=(4, 2))
+    x = Q.e4m3_decode(codes) * np.repeat(np.exp2(-e.astype(float)), 128, axis=1)
+    qx, ex = Q.block_quantize(x, 1)
+    assert np.array_equal(ex, e) and np.array_equal(Q.block_dequantize(qx, ex, 1), x)
+    # random data: every element within half an E4M3 step (2^-4 relative) or the subnormal step
+    y = rng.standard_normal((6, 256))
+    qy, ey = Q.block_quantize(y, 1)
+    d = Q.block_dequantize(qy, ey, 1)
+    step = np.repeat(np.exp2(-ey.astype(float) - 9), 128, axis=1)
+    assert np.all(np.abs(d - y) <= np.maximum(np.abs(y) * 2.0 ** -4, step / 2) * (1 + 1e-12))
+
+
+def test_block_linear_brute_force():
+    rng = np.random.default_rng(44)
+    x, w = rng.standard_normal((2, 256)), rng.standard_normal((3, 256)) * 0.1
+    b = rng.standard_normal(3)
+    y = Q.block_linear(x, w, b)
+    qx, ex = Q.block_quantize(x, 1)
+    qw, ew = Q.block_quantize(w, 128)
+    for i in range(2):
+        for j in range(3):
+            s = float(b[j])
+            for kb in range(2):
+                part = 0.0
+                for t in range(128 * kb, 128 * kb + 128):
+                    part += float(Q.e4m3_decode(qx[i, t])) * float(Q.e4m3_decode(qw[j, t]))
+                s += part * 2.0 ** -(int(ex[i, kb]) + int(ew[0, kb]))
+            assert abs(y[i, j] - s) <= 1e-12 * max(1.0, abs(s))
+    exact = x @ w.T + b
+    assert np.linalg.norm(y - exact) / np.linalg.norm(exact) < 0.05
