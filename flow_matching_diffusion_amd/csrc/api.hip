@@ -653,6 +653,28 @@ flux_status flux_mxfp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t
   return FLUX_OK;
 }
 
+flux_status flux_fp8_block_quantize(int32_t src_precision, const void* src, int32_t rows, int32_t k,
+                                    int32_t tile_rows, uint8_t* codes, uint8_t* scales, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(src_precision == FLUX_PREC_F32 || src_precision == FLUX_PREC_BF16,
+          "src_precision must be FLUX_PREC_F32 or FLUX_PREC_BF16 (got %d)", src_precision);
+  REQUIRE(tile_rows == 1 || tile_rows == 128, "tile_rows must be 1 (activations) or 128 (weights), got %d",
+          tile_rows);
+  REQUIRE(rows >= 1 && k >= 128 && k % 128 == 0, "rows must be >= 1 and k a positive multiple of 128");
+  REQUIRE((int64_t)rows * k < ((int64_t)1 << 36), "problem too large");
+  REQUIRE(src && codes && scales, "src, codes and scales are required");
+  REQUIRE(aligned16(src) && aligned16(codes) && aligned16(scales), "pointers must be 16-byte aligned");
+  const int64_t sbytes = (int64_t)rows * k * (src_precision == FLUX_PREC_F32 ? 4 : 2);
+  const int64_t scb = (int64_t)mx_scale_bytes(rows, k);
+  REQUIRE(!ranges_overlap(codes, (int64_t)rows * k, src, sbytes) && !ranges_overlap(scales, scb, src, sbytes) &&
+              !ranges_overlap(scales, scb, codes, (int64_t)rows * k),
+          "codes, scales and src must not overlap");
+  FLUX_HIP(launch_fp8_block_quantize(src, src_precision == FLUX_PREC_F32 ? kF32 : kBF16, rows, k, tile_rows, codes,
+                                     scales, static_cast<hipStream_t>(stream)),
+           "blockwise fp8 quantize");
+  return FLUX_OK;
+}
+
 // ---------------------------------- MXFP4 ----------------------------------
 size_t flux_mxfp4_scale_bytes(int32_t rows, int32_t k) {
   if (rows < 1 || k < 128 || k % 128 != 0) return 0;

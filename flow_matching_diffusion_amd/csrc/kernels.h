@@ -295,6 +295,11 @@ hipError_t launch_mx_quantize(const void* src, int src_dtype, int rows, int k, u
 //   ((row / 128) * (k / 128) + kb / 4) * 512 + (kb % 2) * 256 + (row % 32) * 8
 //     + ((kb % 4) / 2) * 4 + (row / 32) % 4.
 // The byte count is that of mx_scale_bytes (rows padded to 256).
+// Blockwise E4M3 (tiles of tile_rows x 128 along k, tile_rows 1 or 128, one
+// power-of-two scale each): codes [rows, k] and E8M0 bytes 127 - e in the
+// mx_quantize layout, so the MXFP8 GEMM takes the operands as they are.
+hipError_t launch_fp8_block_quantize(const void* src, int src_dtype, int rows, int k, int tile_rows, uint8_t* codes,
+                                     uint8_t* scales, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const void* src, int src_dtype, int rows, int k, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);
 

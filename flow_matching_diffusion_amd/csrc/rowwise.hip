@@ -1032,6 +1032,116 @@ hipError_t launch_mxfp4_quantize(const void* src, int src_dtype, int rows, int k
 }
 
 // ===========================================================================
+// Blockwise E4M3 quantization (the "blockwise" recipe of "FP8 training for
+// Flux models", Configuration): one power-of-two scale 2^e per tile along K,
+// tiles of 1 x 128 values (activations) or 128 x 128 (weights), e the largest
+// integer with amax * 2^e <= 448, clamped to [-127, 127] (0 for an all-zero
+// tile; a tile holding a non-finite value gets the NaN byte 0xFF and its
+// elements are encoded unscaled).  With a power-of-two scale the dequantized
+// product of a 128-wide k block is 2^-(e_x + e_w) times the code product, so
+// the scales are written as E8M0 bytes 127 - e, replicated over the four
+// 32-value blocks of the tile, into the layout of mx_quantize_kernel: the
+// MXFP8 GEMM consumes the operands unchanged.
+//
+// One 256-thread block per 128 x 128 tile: thread t covers columns
+// 8 (t % 16) .. + 7 of tile rows t / 16 + 16 j, j < 8, so sixteen lanes read
+// one row's 256 contiguous bytes (bf16) per load.
+// ===========================================================================
+__device__ __forceinline__ int block_scale_exp(uint32_t m) {
+  if (m == 0u) return 0;
+  if (m < 0x00800000u) return 127;   // subnormal amax: e >= 135 before the clamp
+  const int ex = (int)(m >> 23) - 127;   // amax = 1.f * 2^ex
+  // amax * 2^e <= 448 = 1.75 * 2^8: e = 8 - ex when 1.f <= 1.75, else 7 - ex
+  const int e = (m & 0x7fffffu) <= 0x600000u ? 8 - ex : 7 - ex;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) fp8_block_quantize_kernel(const T* __restrict__ src, int rows, int k,
+                                                                 int tile_rows, uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales) {
+  __shared__ uint32_t red[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int col = blockIdx.x * 128 + (t & 15) * 8;
+  const int row0 = blockIdx.y * 128 + (t >> 4);
+  float v[8][8];
+  uint32_t rm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = row0 + 16 * j;
+    if (row < rows) {
+      load8<T>(src + (int64_t)row * k + col, v[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[j][i]));   // NaN patterns sort above infinity
+    rm[j] = m;
+  }
+  if (tile_rows == 1) {   // block-uniform: the row's amax over its sixteen lanes
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t m = rm[j];
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+      rm[j] = m;
+    }
+  } else {                // the whole tile's amax
+    uint32_t m = rm[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) m = max(m, rm[j]);
+    m = wave_max_u32(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rm[j] = m;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = row0 + 16 * j;
+    uint32_t sbyte;
+    float mul = 1.0f;
+    if (rm[j] >= 0x7f800000u) {
+      sbyte = 0xFFu;
+    } else {
+      const int e = block_scale_exp(rm[j]);
+      sbyte = (uint32_t)(127 - e);
+      mul = __uint_as_float((uint32_t)(127 + e) << 23);   // 2^e, normal: a finite amax gives e >= -120
+    }
+    if (row < rows) {
+      uint2 o;
+      o.x = f32x4_to_e4m3(v[j][0] * mul, v[j][1] * mul, v[j][2] * mul, v[j][3] * mul);
+      o.y = f32x4_to_e4m3(v[j][4] * mul, v[j][5] * mul, v[j][6] * mul, v[j][7] * mul);
+      *reinterpret_cast<uint2*>(codes + (int64_t)row * k + col) = o;
+    }
+    if ((t & 3) == 0) {   // the first lane of each 32-value block writes its byte (pad rows too)
+      const int kb = col >> 5, kt = kb >> 1, h = kb & 1;
+      const int64_t idx = (((int64_t)(row >> 7) * (k >> 6) + kt) * 2 + h) * 128 + (row & 31) * 4 + ((row >> 5) & 3);
+      scales[idx] = (uint8_t)sbyte;
+    }
+  }
+}
+
+hipError_t launch_fp8_block_quantize(const void* src, int src_dtype, int rows, int k, int tile_rows, uint8_t* codes,
+                                     uint8_t* scales, hipStream_t stream) {
+  const int rows_pad = ((rows + 255) / 256) * 256;
+  const dim3 grid((unsigned)(k / 128), (unsigned)(rows_pad / 128));
+  TimingScope ts(kKcMxQuant, stream, (double)rows * k * ((src_dtype == kBF16 ? 2.0 : 4.0) + 1.0 + 1.0 / 32));
+  if (src_dtype == kBF16)
+    hipLaunchKernelGGL(fp8_block_quantize_kernel<bf16_t>, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(src),
+                       rows, k, tile_rows, codes, scales);
+  else
+    hipLaunchKernelGGL(fp8_block_quantize_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(src),
+                       rows, k, tile_rows, codes, scales);
+  return hipGetLastError();
+}
+
+// ===========================================================================
 // dst = e4m3(src * scale(rec)) over a whole tensor (the weight cast of a
 // forward); each thread converts 16 consecutive elements per step, and one
 // atomic per block raises the record's amax (atomics on one address

@@ -46,7 +46,7 @@ EXPORTED = (
     "flux_attention_bwd", "flux_rf_loss_grad", "flux_final_bwd_workspace_bytes", "flux_final_bwd",
     "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
     "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd", "flux_mxfp4_scale_bytes", "flux_mxfp4_quantize",
-    "flux_mxfp4_linear_fwd",
+    "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize",
 )
 
 
@@ -145,6 +145,7 @@ def lib() -> C.CDLL:
         "flux_mx_quantize": [i32, vp, i32, i32, vp, vp, vp],
         "flux_mxfp8_linear_fwd": [i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
         "flux_mxfp4_quantize": [i32, vp, i32, i32, vp, vp, vp],
+        "flux_fp8_block_quantize": [i32, vp, i32, i32, i32, vp, vp, vp],
         "flux_mxfp4_linear_fwd": [i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
         "flux_final_fwd": [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
@@ -415,6 +416,12 @@ def mx_scales_unswizzle(sc, rows: int, k: int):
     t = s[: rp * (k // 32)].reshape(rp // 128, k // 64, 2, 32, 4)      # [rb, kt, h, l32, i]
     t = t.transpose(0, 4, 3, 1, 2).reshape(rp, k // 32)                 # rows rb*128 + i*32 + l32
     return t[:rows]
+
+
+def flux_fp8_block_quantize(src_precision: int, src, rows: int, k: int, tile_rows: int, codes, scales,
+                            stream=None) -> None:
+    _check(lib().flux_fp8_block_quantize(src_precision, ptr(src), rows, k, tile_rows, ptr(codes), ptr(scales),
+                                         _stream(stream)), "flux_fp8_block_quantize")
 
 
 def flux_mxfp4_scale_bytes(rows: int, k: int) -> int:

@@ -455,6 +455,30 @@ flux_status flux_mxfp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t
                                   void* stream);
 
 /*
+ * Blockwise E4M3 (the "blockwise" recipe listed in "FP8 training for Flux
+ * models", Configuration, which the page does not define; read here as one
+ * power-of-two scale per tile along K).
+ *
+ * flux_fp8_block_quantize -- codes [rows, k] (row-major E4M3 bytes) and scales
+ *   of src [rows, k] (FLUX_PREC_F32 float or FLUX_PREC_BF16, row-major) in
+ *   tiles of tile_rows x 128 values (tile_rows 1 for activations, 128 for
+ *   weights; the last row tile of a ragged row count holds the rows that
+ *   exist).  A tile's exponent e is the largest integer with
+ *   amax * 2^e <= 448, clamped to [-127, 127] (0 for an all-zero tile);
+ *   code = e4m3(v * 2^e) rounded to nearest even.  The scale array
+ *   (flux_mx_scale_bytes(rows, k) bytes) holds the E8M0 byte 127 - e of each
+ *   tile, repeated for its four 32-value blocks, in the layout of
+ *   flux_mx_quantize (0xFF for a tile holding a non-finite value, whose
+ *   elements are then encoded unscaled), so flux_mxfp8_linear_fwd computes
+ *   y = sum over 128-wide k blocks of 2^-(e_x + e_w) (x_q w_q^T) + b from an
+ *   activation quantized with tile_rows 1 and a weight quantized with
+ *   tile_rows 128.  k a multiple of 128; pointers 16-byte aligned; codes and
+ *   scales must not overlap src.
+ */
+flux_status flux_fp8_block_quantize(int32_t src_precision, const void* src, int32_t rows, int32_t k,
+                                    int32_t tile_rows, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
  * MXFP4 linears (OCP MX v1.0 with E2M1 elements: the fp4 member of the
  * microscaling family whose fp8 member is the "mxfp8" recipe of "FP8 training
  * for Flux models", Configuration): each 32 consecutive values along K share
