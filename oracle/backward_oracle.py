@@ -241,11 +241,15 @@ def final_layer_vjp(x_img, vec, w: Dict[str, np.ndarray], eps: float, dv):
     return dx, dvec, g
 
 
-def conditioning_vjp(t, y, w: Dict[str, np.ndarray], dvec, model_channels: int = 256) -> Dict[str, np.ndarray]:
+def conditioning_vjp(t, y, w: Dict[str, np.ndarray], dvec, model_channels: int = 256,
+                     guidance=None) -> Dict[str, np.ndarray]:
     """Gradients of the two Linear -> SiLU -> Linear embedders of
     flux_oracle.conditioning_vector (time, and the pooled vector when y is
-    given) for the vec gradient dvec [B, D]."""
+    given) and, when guidance [B] is given, of its Linear 1 -> D, for the vec
+    gradient dvec [B, D]."""
     g: Dict[str, np.ndarray] = {}
+    if guidance is not None:
+        _, g["guidance_in.w"], g["guidance_in.b"] = linear_vjp(f64(guidance).reshape(-1, 1), w["guidance_in.w"], dvec)
     pairs = [("time_in", timestep_embedding(t, model_channels))]
     if y is not None:
         pairs.append(("vector_in", f64(y)))
@@ -257,9 +261,10 @@ def conditioning_vjp(t, y, w: Dict[str, np.ndarray], dvec, model_channels: int =
 
 
 def flux_train_vjp(z0, z1, t, txt, y, ids, emb_w: Dict[str, np.ndarray], double_ws, single_ws, heads: int,
-                   axes_dim, theta: float, eps: float = 1e-6, model_channels: int = 256):
+                   axes_dim, theta: float, eps: float = 1e-6, model_channels: int = 256, guidance=None):
     """One rectified-flow training step of the model of flux_oracle.flux_forward
-    (fused single blocks, no guidance embedding): z_t = (1 - t) z0 + t z1, the
+    (fused single blocks; the guidance embedding when guidance [B] is given,
+    the guidance values themselves being inputs): z_t = (1 - t) z0 + t z1, the
     velocity prediction, J = mean((v_pred - (z1 - z0))^2), then the gradient of
     J with respect to every weight.  Returns (J, emb_grads, [double grads],
     [single grads])."""
@@ -274,6 +279,8 @@ def flux_train_vjp(z0, z1, t, txt, y, ids, emb_w: Dict[str, np.ndarray], double_
     if y is not None:
         vec = vec + linear(silu(linear(y, emb_w["vector_in1.w"], emb_w["vector_in1.b"])),
                            emb_w["vector_in2.w"], emb_w["vector_in2.b"])
+    if guidance is not None:
+        vec = vec + linear(f64(guidance).reshape(-1, 1), emb_w["guidance_in.w"], emb_w["guidance_in.b"])
     angles = rope_angles(ids, axes_dim, theta)
     l_img = x_img.shape[1]
     d_in = []
@@ -305,7 +312,7 @@ def flux_train_vjp(z0, z1, t, txt, y, ids, emb_w: Dict[str, np.ndarray], double_
     _, g_emb["img_in.w"], g_emb["img_in.b"] = linear_vjp(patches, emb_w["img_in.w"], d_img)
     if has_txt_in:
         _, g_emb["txt_in.w"], g_emb["txt_in.b"] = linear_vjp(txt, emb_w["txt_in.w"], d_txt)
-    g_emb.update(conditioning_vjp(t, y, emb_w, dvec, model_channels))
+    g_emb.update(conditioning_vjp(t, y, emb_w, dvec, model_channels, guidance))
     return loss, g_emb, g_double, g_single
 
 

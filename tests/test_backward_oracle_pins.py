@@ -229,6 +229,20 @@ def test_conditioning_vjp():
         _dir_check(lambda u: O.conditioning_vector(t, y, dict(w, **{n: u}), MC), w[n], g[n], dvec, rng)
 
 
+def test_conditioning_vjp_with_guidance():
+    rng = np.random.default_rng(13)
+    w = _emb_w(rng)
+    w["guidance_in.w"], w["guidance_in.b"] = rng.standard_normal((D, 1)), rng.standard_normal(D)
+    t, y, gs = rng.uniform(size=B), rng.standard_normal((B, YD)), rng.uniform(1.0, 5.0, size=B)
+    dvec = rng.standard_normal((B, D))
+    g = G.conditioning_vjp(t, y, w, dvec, MC, guidance=gs)
+    assert {"guidance_in.w", "guidance_in.b"} <= set(g)
+    for n in ("guidance_in.w", "guidance_in.b", "time_in2.w"):
+        _dir_check(lambda u: O.conditioning_vector(t, y, dict(w, **{n: u}), MC, gs), w[n], g[n], dvec, rng)
+    # the embedding is affine in its weights: dW = sum_b g_b dvec_b exactly
+    assert np.allclose(g["guidance_in.w"][:, 0], gs @ dvec, rtol=1e-14, atol=0)
+
+
 def test_flux_train_vjp():
     # the gradient of the whole step's loss with respect to every weight group,
     # along random directions, against central differences of the forward loss
