@@ -927,4 +927,31 @@ hipError_t launch_rf_loss_grad(const float* v, const float* z0, const float* z1,
   return hipGetLastError();
 }
 
+// Gradient of the guidance embedding, a Linear 1 -> D of the guidance value
+// g_b added to vec ("Flux architecture deep dive", Conditioning):
+// dW[d] = sum_b g_b dvec[b, d], db[d] = sum_b dvec[b, d], summed over b in
+// order (one thread per d).
+__global__ void __launch_bounds__(256) guidance_bwd_kernel(const float* __restrict__ dvec,
+                                                           const float* __restrict__ g, int batch, int D,
+                                                           float* __restrict__ dw, float* __restrict__ db) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= D) return;
+  float sw = 0.f, sb = 0.f;
+  for (int b = 0; b < batch; ++b) {
+    const float v = dvec[(int64_t)b * D + d];
+    sw = fmaf(g[b], v, sw);
+    sb += v;
+  }
+  dw[d] = sw;
+  db[d] = sb;
+}
+
+hipError_t launch_guidance_bwd(const float* dvec, const float* g, int batch, int D, float* dw, float* db,
+                               hipStream_t stream) {
+  TimingScope ts(kKcBwdElem, stream, (double)batch * D * 4.0 + D * 8.0);
+  hipLaunchKernelGGL(guidance_bwd_kernel, dim3((unsigned)ceil_div(D, 256)), dim3(256), 0, stream, dvec, g, batch, D,
+                     dw, db);
+  return hipGetLastError();
+}
+
 }  // namespace flux

@@ -253,6 +253,9 @@ struct ModBwdArgs {
 hipError_t launch_mod_bwd(ModBwdArgs a, int w_dtype, hipStream_t stream);
 
 // dv = (2 / n) (v - (z1 - z0)) over n fp32 elements (velocity MSE gradient)
+// dW = sum_b g_b dvec_b and db = sum_b dvec_b of the guidance embedding (fp32)
+hipError_t launch_guidance_bwd(const float* dvec, const float* g, int batch, int D, float* dw, float* db,
+                               hipStream_t stream);
 hipError_t launch_rf_loss_grad(const float* v, const float* z0, const float* z1, float* dv, int64_t n,
                                hipStream_t stream);
 

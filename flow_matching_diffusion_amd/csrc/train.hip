@@ -928,9 +928,9 @@ size_t flux_embed_bwd_workspace_bytes(int32_t batch, int32_t channels, int32_t h
 flux_status flux_embed_bwd(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t l_txt,
                            int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
                            const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
-                           const float* y, const float* d_img, int64_t img_bstride, const float* d_txt,
-                           int64_t txt_bstride, const float* dvec, const flux_embed_grads* g, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           const float* y, const float* guidance, const float* d_img, int64_t img_bstride,
+                           const float* d_txt, int64_t txt_bstride, const float* dvec, const flux_embed_grads* g,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   REQUIRE(batch >= 1 && channels >= 1 && height >= 1 && width >= 1 && hidden >= 1, "sizes must be >= 1");
   REQUIRE(w && g && w->img_in_w && w->time_in1_w && w->time_in1_b && w->time_in2_w && w->time_in2_b,
@@ -956,6 +956,10 @@ flux_status flux_embed_bwd(int32_t batch, int32_t channels, int32_t height, int3
     REQUIRE(y && y_dim >= 8 && y_dim % 8 == 0 && w->vector_in2_w && g->vector_in1_w && g->vector_in1_b &&
                 g->vector_in2_w && g->vector_in2_b,
             "vector_in needs y (y_dim a multiple of 8) and its gradients");
+  if (guidance)
+    REQUIRE(w->guidance_in_w && g->guidance_in_w && g->guidance_in_b && aligned16(g->guidance_in_w) &&
+                aligned16(g->guidance_in_b),
+            "guidance needs the guidance embedding's weight and 16-byte aligned gradients");
   const int64_t Lt = has_txt ? l_txt : 0, ctx = has_txt ? ctx_dim : 0;
   flux_status s = check_workspace(workspace, workspace_bytes, embed_bwd_ws(B, C, HW, Lt, ctx, D, nullptr).bytes);
   if (s != FLUX_OK) return s;
@@ -1009,6 +1013,9 @@ flux_status flux_embed_bwd(int32_t batch, int32_t channels, int32_t height, int3
   if (has_y && (s = mlp_bwd(w->vector_in1_w, w->vector_in1_b, w->vector_in2_w, y, y_dim, g->vector_in1_w,
                             g->vector_in1_b, g->vector_in2_w, g->vector_in2_b)) != FLUX_OK)
     return s;
+  if (guidance)
+    FLUX_HIP(launch_guidance_bwd(dvec, guidance, (int)B, (int)D, g->guidance_in_w, g->guidance_in_b, st),
+             "guidance embedding backward");
   return FLUX_OK;
 }
 

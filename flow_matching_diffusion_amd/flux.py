@@ -93,7 +93,8 @@ class flux_single_grads(C.Structure):
 class flux_embed_grads(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("img_in_w", "img_in_b", "txt_in_w", "txt_in_b", "time_in1_w",
                                           "time_in1_b", "time_in2_w", "time_in2_b", "vector_in1_w",
-                                          "vector_in1_b", "vector_in2_w", "vector_in2_b")]
+                                          "vector_in1_b", "vector_in2_w", "vector_in2_b", "guidance_in_w",
+                                          "guidance_in_b")]
 
 
 class rf_args(C.Structure):
@@ -172,7 +173,7 @@ def lib() -> C.CDLL:
         "flux_final_bwd": [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                            vp],
         "flux_embed_bwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp, vp,
-                           i64, vp, i64, vp, P(flux_embed_grads), vp, sz, vp],
+                           vp, i64, vp, i64, vp, P(flux_embed_grads), vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -319,7 +320,7 @@ def single_grads(g: Dict[str, object]) -> flux_single_grads:
 
 def embed_grads(g: Dict[str, object]) -> flux_embed_grads:
     s = flux_embed_grads()
-    for f in ("img_in", "txt_in", "time_in1", "time_in2", "vector_in1", "vector_in2"):
+    for f in ("img_in", "txt_in", "time_in1", "time_in2", "vector_in1", "vector_in2", "guidance_in"):
         setattr(s, f + "_w", ptr(g.get(f + ".w")))
         setattr(s, f + "_b", ptr(g.get(f + ".b")))
     return s
@@ -622,9 +623,10 @@ def flux_embed_bwd_workspace_bytes(batch, channels, height, width, l_txt, ctx_di
 
 def flux_embed_bwd(batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim, w: flux_embed_weights,
                    z_t, txt, t, y, d_img, img_bstride, d_txt, txt_bstride, dvec, grads: flux_embed_grads, workspace,
-                   workspace_bytes, stream=None) -> None:
+                   workspace_bytes, stream=None, guidance=None) -> None:
     _check(lib().flux_embed_bwd(batch, channels, height, width, l_txt, ctx_dim, hidden, time_dim, y_dim, C.byref(w),
-                                ptr(z_t), ptr(txt), ptr(t), ptr(y), ptr(d_img), img_bstride, ptr(d_txt), txt_bstride,
+                                ptr(z_t), ptr(txt), ptr(t), ptr(y), ptr(guidance), ptr(d_img), img_bstride, ptr(d_txt),
+                                txt_bstride,
                                 ptr(dvec), C.byref(grads), ptr(workspace), workspace_bytes, _stream(stream)),
            "flux_embed_bwd")
 

@@ -361,8 +361,9 @@ class FluxTrainer:
     the output head with their training forwards, the velocity MSE, then the
     backward in reverse order -- the loss gradient, the head, every block and
     the embeddings -- leaving the fp32 gradient of every weight in `grads`
-    (embeddings and head), `g_double[i]` and `g_single[i]`.  The guidance
-    embedding is not part of the step."""
+    (embeddings and head), `g_double[i]` and `g_single[i]`.  When the
+    embedding weights hold the guidance embedding, step() takes the guidance
+    values and its gradients join `grads`."""
 
     def __init__(self, wl: synth.Workload, emb_w: Dict[str, object], double_ws, single_ws, device="cuda"):
         self.wl, self.device = wl, device
@@ -376,7 +377,7 @@ class FluxTrainer:
         self.sstructs = [F.single_weights(w) for w in self.sw]
         f32 = dict(dtype=torch.float32, device=device)
         grad = lambda w: {k: torch.empty(tuple(v.shape), **f32) for k, v in w.items()}
-        self.grads = grad({k: v for k, v in self.emb.items() if not k.startswith("guidance_in")})
+        self.grads = grad(self.emb)
         self.g_double = [grad(w) for w in self.dw]
         self.g_single = [grad(w) for w in self.sw]
         self.gstructs = ([(F.stream_grads(g, "img"), F.stream_grads(g, "txt")) for g in self.g_double],
@@ -401,8 +402,12 @@ class FluxTrainer:
                   "loss": torch.empty((1,), **f32), "loss_per_sample": torch.empty((B,), **f32)}
         self.rope = None
 
-    def step(self, z0, z1, t, txt, y, ids) -> torch.Tensor:
-        """Returns the loss (a device tensor); gradients land in the grad dicts."""
+    def step(self, z0, z1, t, txt, y, ids, guidance=None) -> torch.Tensor:
+        """Returns the loss (a device tensor); gradients land in the grad dicts.
+        guidance: [batch] float device values, required exactly when the model
+        has the guidance embedding."""
+        if (guidance is None) == ("guidance_in.w" in self.emb):
+            raise ValueError("guidance values are needed exactly when the model has a guidance embedding")
         wl, o, ws = self.wl, self.o, self.ws
         B, C, D, L, Li = wl.batch, wl.latent_ch, wl.hidden, wl.seq, wl.l_img
         n = C * Li
@@ -419,7 +424,7 @@ class FluxTrainer:
             x[:, Li:].copy_(txt)
         F.flux_embed_fwd(bf, B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
                          wl.vec_in_dim or 0, self.estruct, o["z_t"], txt if has_txt_in else None, t, y, x, L * D,
-                         txt_ptr if has_txt_in else None, L * D, vec, ws, self.ws_bytes)
+                         txt_ptr if has_txt_in else None, L * D, vec, ws, self.ws_bytes, guidance=guidance)
         for (iw, tw), sv in zip(self.dstructs, self.saved_d):
             F.flux_block_fwd_train(self.dims, iw, tw, x, L * D, txt_ptr, L * D, vec, self.rope, sv, sv.numel())
         for sw, sv in zip(self.sstructs, self.saved_s):
@@ -445,5 +450,6 @@ class FluxTrainer:
                              dvec, ws, self.ws_bytes)
         F.flux_embed_bwd(B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
                          wl.vec_in_dim or 0, self.estruct, o["z_t"], txt if has_txt_in else None, t, y, d, L * D,
-                         d_txt_ptr if has_txt_in else None, L * D, dvec, self.egrads, ws, self.ws_bytes)
+                         d_txt_ptr if has_txt_in else None, L * D, dvec, self.egrads, ws, self.ws_bytes,
+                         guidance=guidance)
         return o["loss"]

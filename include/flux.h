@@ -604,13 +604,18 @@ flux_status flux_single_seq_bwd(const flux_dims* dims, const flux_stream_weights
  * weights.  flux_embed_bwd writes (=) the fp32 gradients of the image and
  * text input linears and of the time and pooled-vector embedders, given the
  * gradients d_img, d_txt of the embedded token rows and dvec of the
- * conditioning vector; the guidance embedding is not differentiated.
+ * conditioning vector; with guidance [B] float (the values the forward's
+ * guidance embedding took, or NULL when it had none) it also writes the
+ * gradients of that Linear 1 -> D: guidance_in_w[d] = sum_b g_b dvec[b, d],
+ * guidance_in_b[d] = sum_b dvec[b, d] (the guidance values themselves are
+ * inputs and get no gradient).
  * channels and ctx_dim multiples of 64; workspaces from the *_bytes calls,
  * 256-byte aligned.
  */
 typedef struct {
   float *img_in_w, *img_in_b, *txt_in_w, *txt_in_b, *time_in1_w, *time_in1_b, *time_in2_w, *time_in2_b;
   float *vector_in1_w, *vector_in1_b, *vector_in2_w, *vector_in2_b;
+  float *guidance_in_w, *guidance_in_b; /* [D] each; used when guidance is given */
 } flux_embed_grads;
 
 flux_status flux_rf_loss_grad(int32_t batch, int64_t n_per_sample, const float* v_pred, const float* z0,
@@ -627,8 +632,9 @@ size_t flux_embed_bwd_workspace_bytes(int32_t batch, int32_t channels, int32_t h
 flux_status flux_embed_bwd(int32_t batch, int32_t channels, int32_t height, int32_t width, int32_t l_txt,
                            int32_t ctx_dim, int32_t hidden, int32_t time_dim, int32_t y_dim,
                            const flux_embed_weights* w, const float* z_t, const void* txt, const float* t,
-                           const float* y, const float* d_img, int64_t img_batch_stride, const float* d_txt,
-                           int64_t txt_batch_stride, const float* dvec, const flux_embed_grads* grads,
+                           const float* y, const float* guidance, const float* d_img, int64_t img_batch_stride,
+                           const float* d_txt, int64_t txt_batch_stride, const float* dvec,
+                           const flux_embed_grads* grads,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*

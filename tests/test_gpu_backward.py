@@ -310,6 +310,9 @@ STEP_WL = {
     # text at hidden width, no pooled vector (the block-pair bench's model)
     "plain": synth.custom_workload("step_plain", base="flux535m", batch=1, hidden=256, heads=2, head_dim=128,
                                    mlp_hidden=512, img_h=8, img_w=8, l_txt=16, context_dim=None, vec_in_dim=None),
+    # all embedders and the guidance embedding (Linear 1 -> D of per-sample guidance values)
+    "guidance": synth.custom_workload("step_guidance", base="flux535m", batch=3, hidden=256, heads=2, head_dim=128,
+                                      mlp_hidden=512, img_h=4, img_w=8, l_txt=7, context_dim=128, vec_in_dim=64),
 }
 
 
@@ -318,16 +321,19 @@ def test_flux_train_step(name):
     from flow_matching_diffusion_amd.model import FluxTrainer
     wl = STEP_WL[name]
     _say(f"whole training step {name}: noise, embeddings, double + single block, head, MSE, backward")
-    emb = synth.embed_weights(wl)
+    with_g = name == "guidance"
+    emb = synth.embed_weights(wl, guidance=with_g)
     w2, w1 = synth.double_block_weights(wl, 0), synth.single_block_weights(wl, 1)
     mi = synth.model_inputs(wl)
+    gv = np.linspace(1.0, 5.0, wl.batch).astype(np.float32) if with_g else None
     tr = FluxTrainer(wl, emb, [w2], [w1])
     y = _dev(mi["y"]) if "y" in mi else None
     loss = tr.step(_dev(mi["z0"]), _dev(mi["z1"]), _dev(mi["t"]), _dev(mi["txt"], wl.context_dim is not None), y,
-                   _dev(mi["ids"]))
+                   _dev(mi["ids"]), guidance=_dev(gv) if with_g else None)
     torch.cuda.synchronize()
     ref_loss, g_emb, g2, g1 = G.flux_train_vjp(mi["z0"], mi["z1"], mi["t"], mi["txt"], mi.get("y"), mi["ids"], emb, [w2],
-                                               [w1], wl.heads, wl.axes_dim, wl.theta, wl.eps, wl.model_channels)
+                                               [w1], wl.heads, wl.axes_dim, wl.theta, wl.eps, wl.model_channels,
+                                               guidance=gv)
     got = float(loss.item())
     print(f"    loss: gpu {got:.6f} oracle {ref_loss:.6f}", flush=True)
     assert abs(got - ref_loss) <= 1e-2 * ref_loss
