@@ -662,6 +662,8 @@ flux_status flux_fp8_block_quantize(int32_t src_precision, const void* src, int3
           tile_rows);
   REQUIRE(rows >= 1 && k >= 128 && k % 128 == 0, "rows must be >= 1 and k a positive multiple of 128");
   REQUIRE((int64_t)rows * k < ((int64_t)1 << 36), "problem too large");
+  // one block per 128-row tile along the grid's y dimension (at most 65535)
+  REQUIRE((int64_t)(rows + 255) / 256 * 2 <= 65535, "rows must be at most 8388480");
   REQUIRE(src && codes && scales, "src, codes and scales are required");
   REQUIRE(aligned16(src) && aligned16(codes) && aligned16(scales), "pointers must be 16-byte aligned");
   const int64_t sbytes = (int64_t)rows * k * (src_precision == FLUX_PREC_F32 ? 4 : 2);

@@ -472,7 +472,7 @@ flux_status flux_mxfp8_linear_fwd(int32_t m, int32_t n, int32_t k, const uint8_t
  *   elements are then encoded unscaled), so flux_mxfp8_linear_fwd computes
  *   y = sum over 128-wide k blocks of 2^-(e_x + e_w) (x_q w_q^T) + b from an
  *   activation quantized with tile_rows 1 and a weight quantized with
- *   tile_rows 128.  k a multiple of 128; pointers 16-byte aligned; codes and
+ *   tile_rows 128.  k a multiple of 128, rows at most 8388480; pointers 16-byte aligned; codes and
  *   scales must not overlap src.
  */
 flux_status flux_fp8_block_quantize(int32_t src_precision, const void* src, int32_t rows, int32_t k,

@@ -197,3 +197,20 @@ def test_mxfp4_scale_layout_helper():
             buf[off] = v
     assert len(seen) == buf.size                               # the layout is a bijection
     assert np.array_equal(F.mxfp4_scales_unswizzle(buf, rows, k), ref[:rows])
+
+
+def test_mx_and_blockwise_argument_checks():
+    # rejected before any device work: bad tile shape, k, row count, MXFP4 linear k
+    L = F.lib()
+    fake = 1 << 40
+    bf = F.FLUX_PREC_BF16
+    assert L.flux_fp8_block_quantize(bf, fake, 256, 256, 2, fake, fake, None) == F.FLUX_ERR_INVALID_ARGUMENT
+    assert L.flux_fp8_block_quantize(bf, fake, 256, 192, 1, fake, fake, None) == F.FLUX_ERR_INVALID_ARGUMENT
+    assert L.flux_fp8_block_quantize(bf, fake, 8388480 + 1, 128, 128, fake, fake, None) == \
+        F.FLUX_ERR_INVALID_ARGUMENT
+    assert L.flux_mxfp4_quantize(bf, fake, 256, 192, fake, fake, None) == F.FLUX_ERR_INVALID_ARGUMENT
+    assert L.flux_mxfp4_linear_fwd(256, 256, 384, fake, fake, fake, fake, None, fake, 256, None) == \
+        F.FLUX_ERR_UNSUPPORTED
+    assert L.flux_mxfp4_linear_fwd(256, 258, 512, fake, fake, fake, fake, None, fake, 260, None) == \
+        F.FLUX_ERR_UNSUPPORTED                                                  # N % 4
+    assert F.flux_mxfp4_scale_bytes(300, 512) == 512 * 16
