@@ -408,6 +408,18 @@ flux_status flux_rope_table(const float* ids, int32_t batch, int32_t seq, const 
   return FLUX_OK;
 }
 
+flux_status flux_timestep_embed(const float* t, int32_t batch, int32_t dim, float time_factor, float* out,
+                                void* stream) {
+  g_err[0] = 0;
+  REQUIRE(t && out, "t and out are required");
+  REQUIRE(batch >= 1 && batch <= (1 << 20), "batch must be in [1, 2^20]");
+  REQUIRE(dim >= 2 && dim % 2 == 0 && dim <= 4096, "dim must be even, in [2, 4096]");
+  REQUIRE(isfinite(time_factor), "time_factor must be finite");
+  FLUX_HIP(launch_timestep_embed(t, batch, dim, time_factor, 10000.f, out, static_cast<hipStream_t>(stream)),
+           "timestep sinusoid");
+  return FLUX_OK;
+}
+
 // -------------------------------- embeddings --------------------------------
 size_t flux_embed_workspace_bytes(int32_t precision, int32_t batch, int32_t channels, int32_t height, int32_t width,
                                   int32_t hidden) {

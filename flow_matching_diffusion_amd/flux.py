@@ -46,7 +46,7 @@ EXPORTED = (
     "flux_attention_bwd", "flux_rf_loss_grad", "flux_final_bwd_workspace_bytes", "flux_final_bwd",
     "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
     "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd", "flux_mxfp4_scale_bytes", "flux_mxfp4_quantize",
-    "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize",
+    "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize", "flux_timestep_embed",
 )
 
 
@@ -147,6 +147,7 @@ def lib() -> C.CDLL:
         "flux_mxfp8_linear_fwd": [i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
         "flux_mxfp4_quantize": [i32, vp, i32, i32, vp, vp, vp],
         "flux_fp8_block_quantize": [i32, vp, i32, i32, i32, vp, vp, vp],
+        "flux_timestep_embed": [vp, i32, i32, f32, vp, vp],
         "flux_mxfp4_linear_fwd": [i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp],
         "flux_final_fwd": [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp],
         "flux_linear_fwd": [i32, i32, i32, i32, vp, i64, vp, vp, vp, i64, vp],
@@ -417,6 +418,11 @@ def mx_scales_unswizzle(sc, rows: int, k: int):
     t = s[: rp * (k // 32)].reshape(rp // 128, k // 64, 2, 32, 4)      # [rb, kt, h, l32, i]
     t = t.transpose(0, 4, 3, 1, 2).reshape(rp, k // 32)                 # rows rb*128 + i*32 + l32
     return t[:rows]
+
+
+def flux_timestep_embed(t, batch: int, dim: int, time_factor: float, out, stream=None) -> None:
+    _check(lib().flux_timestep_embed(ptr(t), batch, dim, time_factor, ptr(out), _stream(stream)),
+           "flux_timestep_embed")
 
 
 def flux_fp8_block_quantize(src_precision: int, src, rows: int, k: int, tile_rows: int, codes, scales,

@@ -308,6 +308,18 @@ flux_status flux_rope_table(const float* ids, int32_t batch, int32_t seq, const 
                             float theta, float* table, void* stream);
 
 /*
+ * flux_timestep_embed -- sinusoidal encoding of the flow time ("Flux
+ * architecture deep dive", Conditioning / Timestep embedding; "Flux model API
+ * reference", TimeStepEmbedder): tau = time_factor * t_b (1000 in the model),
+ * f_j = 10000^(-j / (dim/2)) for j < dim/2, out[b] = [cos(tau f_j) | sin(tau f_j)],
+ * evaluated in fp64 and stored as float.  flux_embed_fwd applies it itself;
+ * this call exposes the step alone.
+ *  t [batch] float; out [batch, dim] float (dim even, at most 4096).
+ */
+flux_status flux_timestep_embed(const float* t, int32_t batch, int32_t dim, float time_factor, float* out,
+                                void* stream);
+
+/*
  * flux_embed_fwd -- inputs of the transformer ("Flux architecture deep dive",
  * Model components / Input embeddings and Conditioning; Implementation
  * details / Memory layout):

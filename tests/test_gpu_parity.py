@@ -121,6 +121,23 @@ def test_rope_table(name, cg):
     np.testing.assert_allclose(g[..., 1], np.sin(ang), atol=1e-7, rtol=0)
 
 
+@pytest.mark.parametrize("batch,dim", [(1, 256), (5, 256), (3, 18)])
+def test_timestep_embed(batch, dim):
+    # both sides evaluate the sinusoid in fp64 from the same float32 t; the
+    # float store is the only rounding
+    _say(f"timestep sinusoid batch={batch} dim={dim}")
+    rng = np.random.default_rng(batch * 31 + dim)
+    t = rng.uniform(0.0, 1.0, size=batch).astype(np.float32)
+    t[0] = 1.0
+    if batch > 1:
+        t[1] = 0.0
+    out = torch.full((batch, dim), float("nan"), device="cuda")
+    F().flux_timestep_embed(dev(t), batch, dim, 1000.0, out)
+    torch.cuda.synchronize()
+    ref = O.timestep_embedding(t.astype(np.float64), dim, 1000.0)
+    np.testing.assert_allclose(out.cpu().numpy().astype(np.float64), ref, atol=1e-7, rtol=0)
+
+
 # --------------------------------------------------------------------------- #
 # linear (GEMM)
 # --------------------------------------------------------------------------- #
