@@ -214,3 +214,22 @@ def test_mx_and_blockwise_argument_checks():
     assert L.flux_mxfp4_linear_fwd(256, 258, 512, fake, fake, fake, fake, None, fake, 260, None) == \
         F.FLUX_ERR_UNSUPPORTED                                                  # N % 4
     assert F.flux_mxfp4_scale_bytes(300, 512) == 512 * 16
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # with the shared library absent the binding raises instead of falling back
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from flow_matching_diffusion_amd import flux as F\n"
+            "F.LIB_PATH = %r\n"
+            "try:\n"
+            "    F.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "    sys.exit(0)\n"
+            "sys.exit(3)\n") % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                str(tmp_path / "absent" / "libflux.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "missing" in r.stdout
