@@ -184,3 +184,66 @@ def single_block_sequential(x, vec, ids, w, heads, axes_dim, theta, eps):
             rows.append([x1[c] + ch[5][c] * f[c] for c in range(D)])
         out.append(rows)
     return out
+
+
+# --------------------------------------------------------------------------- #
+# Conditioning vector and output head ("Flux architecture deep dive",
+# Conditioning and Model components / Output processing; "Flux model API
+# reference", Embeddings and AdaLNContinuous).  Written per sample and per
+# element; the frequencies are powers of max_period, not exponentials of logs.
+# --------------------------------------------------------------------------- #
+def sinusoid(t, dim, time_factor=1000.0, max_period=10000.0):
+    """[cos(tau f_0) .. cos(tau f_{n-1}) | sin(tau f_0) .. sin(tau f_{n-1})],
+    tau = time_factor * t, f_j = max_period ** (-j / n), n = dim / 2."""
+    n = dim // 2
+    tau = time_factor * t
+    freqs = [max_period ** (-float(j) / n) for j in range(n)]
+    return [math.cos(tau * f) for f in freqs] + [math.sin(tau * f) for f in freqs]
+
+
+def mlp_embed(x, w1, b1, w2, b2):
+    """Linear -> SiLU -> Linear on one vector."""
+    return vec_linear([silu(a) for a in vec_linear(x, w1, b1)], w2, b2)
+
+
+def conditioning_vector(t, y, w, model_channels, guidance=None):
+    """vec[b] = time MLP(sinusoid(t[b])) (+ pooled MLP(y[b])) (+ guidance
+    Linear(g[b])): t [B], y [B][in] or None -> [B][D]."""
+    t, y, guidance = map(_tolist, (t, y, guidance))
+    W = {k: _tolist(v) for k, v in w.items()}
+    out = []
+    for b in range(len(t)):
+        v = mlp_embed(sinusoid(t[b], model_channels), W["time_in1.w"], W["time_in1.b"], W["time_in2.w"],
+                      W["time_in2.b"])
+        if y is not None:
+            p = mlp_embed(y[b], W["vector_in1.w"], W["vector_in1.b"], W["vector_in2.w"], W["vector_in2.b"])
+            v = [v[i] + p[i] for i in range(len(v))]
+        if guidance is not None:
+            g = vec_linear([guidance[b]], W["guidance_in.w"], W["guidance_in.b"])
+            v = [v[i] + g[i] for i in range(len(v))]
+        out.append(v)
+    return out
+
+
+def patch_tokens(z):
+    """[B][C][H][W] -> [B][H*W][C], token h*W + w."""
+    z = _tolist(z)
+    return [[[z[b][c][h][x] for c in range(len(z[b]))] for h in range(len(z[b][0])) for x in range(len(z[b][0][0]))]
+            for b in range(len(z))]
+
+
+def final_layer(x_img, vec, w, hh, ww, eps):
+    """(shift, scale) = Linear(SiLU(vec)) split in two; each image token
+    goes through LN(x)(1 + scale) + shift and the output Linear D -> C; the
+    token h*W + w lands at [c][h][w].  x_img [B][H*W][D] -> [B][C][H][W]."""
+    x_img, vec = map(_tolist, (x_img, vec))
+    W = {k: _tolist(v) for k, v in w.items()}
+    out = []
+    for b in range(len(vec)):
+        D = len(vec[b])
+        m = vec_linear([silu(a) for a in vec[b]], W["final_mod.w"], W["final_mod.b"])
+        shift, scale = m[:D], m[D:2 * D]
+        toks = [vec_linear(ln_mod(x, shift, scale, eps), W["final_out.w"], W["final_out.b"]) for x in x_img[b]]
+        C = len(toks[0])
+        out.append([[[toks[h * ww + x][c] for x in range(ww)] for h in range(hh)] for c in range(C)])
+    return out

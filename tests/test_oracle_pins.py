@@ -456,24 +456,90 @@ def test_config_constants_match_page():
 # --------------------------------------------------------------------------- #
 # Whole forward (composition of the pinned parts)
 # --------------------------------------------------------------------------- #
+def _emb_case(wl, guidance=False):
+    emb = synth.embed_weights(wl, guidance=guidance)
+    # weights well above N(0,0.02) so SiLU and the LayerNorm act non-linearly
+    return {k: v.astype(np.float64) * 20.0 for k, v in emb.items()}
+
+
+def test_conditioning_vector_bruteforce():
+    # "Flux architecture deep dive", Conditioning: vec = time MLP(sinusoid) +
+    # pooled-vector MLP (+ guidance Linear), each MLP Linear -> SiLU -> Linear
+    wl = _tiny_wl(vec_in_dim=6, model_channels=8)
+    emb = _emb_case(wl, guidance=True)
+    t = np.array([0.13, 0.92])
+    y = RNG.standard_normal((2, 6))
+    g = np.array([3.5, 1.25])
+    for yy, gg in ((None, None), (y, None), (y, g)):
+        got = O.conditioning_vector(t, yy, emb, wl.model_channels, guidance=gg)
+        ref = np.array(BF.conditioning_vector(t, yy, emb, wl.model_channels, guidance=gg))
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_conditioning_vector_t0_closed_form():
+    # at t = 0 the sinusoid is [1]*n | [0]*n, so the time MLP's first layer
+    # sees the row sums of its first n weight columns plus the bias
+    wl = _tiny_wl(vec_in_dim=None, model_channels=8)
+    emb = _emb_case(wl)
+    n = wl.model_channels // 2
+    pre = emb["time_in1.w"][:, :n].sum(axis=1) + emb["time_in1.b"]
+    act = pre / (1.0 + np.exp(-pre))
+    ref = emb["time_in2.w"] @ act + emb["time_in2.b"]
+    got = O.conditioning_vector(np.zeros(1), None, emb, wl.model_channels)
+    np.testing.assert_allclose(got[0], ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_final_layer_bruteforce():
+    # "Flux architecture deep dive", Model components / Output processing:
+    # AdaLNContinuous (shift, scale), Linear D -> C, tokens back to [B, C, H, W]
+    wl = _tiny_wl(img_h=2, img_w=3, latent_ch=4)
+    emb = _emb_case(wl)
+    x_img = RNG.standard_normal((2, 6, wl.hidden)) * 3.0 + 1.0
+    vec = RNG.standard_normal((2, wl.hidden))
+    got = O.final_layer(x_img, vec, emb, 2, 3, wl.eps)
+    ref = np.array(BF.final_layer(x_img, vec, emb, 2, 3, wl.eps))
+    assert got.shape == (2, 4, 2, 3)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_final_layer_zero_modulation_closed_form():
+    # zero modulation weights: shift = scale = 0 and the head is
+    # unpatchify(Linear(LN(x))) with a plain LayerNorm (no affine part)
+    wl = _tiny_wl(img_h=2, img_w=3, latent_ch=4)
+    emb = _emb_case(wl)
+    emb["final_mod.w"][:] = 0.0
+    emb["final_mod.b"][:] = 0.0
+    x_img = RNG.standard_normal((2, 6, wl.hidden)) * 3.0 + 1.0
+    vec = RNG.standard_normal((2, wl.hidden))
+    ln = (x_img - x_img.mean(axis=-1, keepdims=True)) / np.sqrt(x_img.var(axis=-1, keepdims=True) + wl.eps)
+    tok = np.einsum("bld,cd->blc", ln, emb["final_out.w"]) + emb["final_out.b"]
+    got = O.final_layer(x_img, vec, emb, 2, 3, wl.eps)
+    for h in range(2):
+        for w in range(3):
+            np.testing.assert_allclose(got[:, :, h, w], tok[:, h * 3 + w, :], rtol=0, atol=1e-12)
+
+
 def test_flux_forward_composition():
+    # the whole forward against a reference assembled only from the
+    # pure-Python pieces (embedding, conditioning, both blocks, head)
     wl = _tiny_wl(img_h=2, img_w=3, latent_ch=4, context_dim=None, vec_in_dim=6, model_channels=8)
-    emb = synth.embed_weights(wl)
+    emb = _emb_case(wl)
     w2, w1, _, ids = _block_case(wl)
     mi = synth.model_inputs(wl)
     zt, _ = O.rf_noise(mi["z0"], mi["z1"], mi["t"])
     v = O.flux_forward(zt, mi["txt"], mi["y"], mi["t"], ids, emb, [w2], [w1], wl.heads, wl.axes_dim, wl.theta,
                        wl.eps, wl.model_channels)
     assert v.shape == mi["z0"].shape
-    # the same forward assembled by hand from pinned pieces
-    x_img = O.linear(O.patchify(zt), emb["img_in.w"], emb["img_in.b"])
-    vec = O.conditioning_vector(mi["t"], mi["y"], emb, wl.model_channels)
-    ang = O.rope_angles(ids, wl.axes_dim, wl.theta)
+    toks = BF.patch_tokens(zt)
+    W_in, b_in = emb["img_in.w"].tolist(), emb["img_in.b"].tolist()
+    x_img = [[BF.vec_linear(tk, W_in, b_in) for tk in row] for row in toks]
+    vec = BF.conditioning_vector(mi["t"].astype(np.float64), mi["y"].astype(np.float64), emb, wl.model_channels)
     bi, bt = BF.double_block(x_img, mi["txt"].astype(np.float64), vec, ids, w2, wl.heads, wl.axes_dim, wl.theta,
                              wl.eps)
-    x = BF.single_block(np.concatenate([bi, bt], axis=1), vec, ids, w1, wl.heads, wl.axes_dim, wl.theta, wl.eps)
-    ref = O.final_layer(np.asarray(x)[:, :wl.l_img], vec, emb, wl.img_h, wl.img_w, wl.eps)
-    np.testing.assert_allclose(v, ref, atol=1e-10)
+    x = BF.single_block([bi[b] + bt[b] for b in range(len(bi))], vec, ids, w1, wl.heads, wl.axes_dim, wl.theta,
+                        wl.eps)
+    ref = np.array(BF.final_layer([row[:wl.l_img] for row in x], vec, emb, wl.img_h, wl.img_w, wl.eps))
+    np.testing.assert_allclose(v, ref, rtol=0, atol=1e-10 * max(1.0, np.abs(ref).max()))
     # unpatchify is the inverse of patchify with token index h*W + w
     np.testing.assert_array_equal(O.unpatchify(O.patchify(zt), wl.img_h, wl.img_w), zt)
     assert O.patchify(zt)[0, 1 * wl.img_w + 2, 3] == zt[0, 3, 1, 2]
