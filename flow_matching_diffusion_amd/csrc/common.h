@@ -32,15 +32,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// fp32 -> fp16 (round to nearest even), two values packed low | high
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+// fp32 -> fp16 with saturation: magnitudes above fp16's largest finite value
+// (65504, infinities included) become +-65504 instead of infinity, so an
+// out-of-range activation cannot turn into inf and then NaN downstream.
+// NaN stays NaN (the comparison is false for it).
+__device__ __forceinline__ _Float16 f32_to_f16_sat(float x) {
+  const float c = fabsf(x) > 65504.0f ? copysignf(65504.0f, x) : x;
+  return (_Float16)c;
 }
 
-// Eight bf16 (a 16-byte word) to eight fp16.  Exact for magnitudes in fp16's
-// normal range [2^-14, 65504]; smaller magnitudes lose at most 2^-24 (round
-// toward zero on the few bits fp16 subnormals cannot hold).
+// fp32 -> fp16 (round to nearest even, saturating), two values packed low | high
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, f32_to_f16_sat(lo)) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_f16_sat(hi)) << 16);
+}
+
+// Eight bf16 (a 16-byte word) to eight fp16, rounding toward zero.  Exact for
+// magnitudes in fp16's normal range [2^-14, 65504]; smaller magnitudes lose
+// at most 2^-24 (the few bits fp16 subnormals cannot hold); finite magnitudes
+// above 65504 become +-65504 (toward zero never rounds up to infinity).
 __device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t w) {
   u32x4_t r;
 #pragma unroll
@@ -60,7 +70,7 @@ template <> __device__ __forceinline__ float load_f32<_Float16>(const _Float16* 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
-template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return f32_to_f16_sat(v); }
 
 // ---- wave reductions (fixed butterfly order -> deterministic) ---------------
 template <int WIDTH = kWave>

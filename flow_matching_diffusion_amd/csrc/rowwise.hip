@@ -832,7 +832,10 @@ hipError_t launch_prep(const PrepArgs& a, int dtype, hipStream_t stream) {
 }
 
 // ===========================================================================
-// One-time bf16 -> fp16 conversion of static weights (round to nearest even)
+// One-time bf16 -> fp16 conversion of static weights.  Rounds toward zero,
+// the same rule as the conversion inside the GEMM (bf16x8_to_f16x8): exact in
+// fp16's normal range, at most 2^-24 lost below 2^-14, magnitudes above 65504
+// saturate to +-65504.
 // ===========================================================================
 __global__ void __launch_bounds__(256) convert_bf16_f16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                                int64_t n8, const bf16_t* __restrict__ src_tail,
@@ -840,14 +843,11 @@ __global__ void __launch_bounds__(256) convert_bf16_f16_kernel(const uint4* __re
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
     const uint4 v = src[i];
-    uint4 o;
-    o.x = pack_f16x2(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u));
-    o.y = pack_f16x2(__uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-    o.z = pack_f16x2(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u));
-    o.w = pack_f16x2(__uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
-    dst[i] = o;
+    const u32x4_t o = bf16x8_to_f16x8(u32x4_t{v.x, v.y, v.z, v.w});
+    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  if (blockIdx.x == 0 && (int)threadIdx.x < tail) dst_tail[threadIdx.x] = (_Float16)bf16_to_f32(src_tail[threadIdx.x]);
+  if (blockIdx.x == 0 && (int)threadIdx.x < tail)
+    dst_tail[threadIdx.x] = __builtin_amdgcn_cvt_pkrtz(bf16_to_f32(src_tail[threadIdx.x]), 0.0f)[0];
 }
 
 hipError_t launch_convert_bf16_f16(const void* src, void* dst, int64_t n, hipStream_t stream) {
@@ -1264,9 +1264,13 @@ __global__ void fp8_current_scale_kernel(flux_fp8_tensor* rec) {
   if (!__builtin_isfinite(a)) flags |= FLUX_FP8_NONFINITE;
   if (__builtin_isfinite(a) && a > 0.f) {
     const float sc = 448.0f / a;
-    rec->scale = sc;
-    rec->scale_inv = 1.0f / sc;
-    flags |= FLUX_FP8_SCALE_SET;
+    const float inv = 1.0f / sc;
+    // an amax so small that 448 / amax overflows keeps the old scale
+    if (__builtin_isfinite(sc) && __builtin_isfinite(inv) && inv > 0.f) {
+      rec->scale = sc;
+      rec->scale_inv = inv;
+      flags |= FLUX_FP8_SCALE_SET;
+    }
   }
   rec->flags = flags;
 }
@@ -1291,8 +1295,9 @@ hipError_t launch_fp8_current_scale(const void* src, int src_dtype, int64_t n, f
 
 // One thread per record: the amax recorded since the last update enters the
 // history ring, the selected amax (newest entry, or the history maximum with
-// NaN propagating) gives scale = (448 / amax) * 2^-margin when it is finite
-// and positive; the amax is then cleared for the next forward.
+// NaN propagating) gives scale = (448 / amax) * 2^-margin when the amax is
+// finite and positive and the scale and its reciprocal are finite and
+// non-zero; the amax is then cleared for the next forward.
 __global__ void fp8_update_kernel(flux_fp8_tensor* recs, int n, int algo, int margin) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -1318,9 +1323,13 @@ __global__ void fp8_update_kernel(flux_fp8_tensor* recs, int n, int algo, int ma
   if (!(__builtin_isfinite(a))) flags |= FLUX_FP8_NONFINITE;
   if (__builtin_isfinite(sel) && sel > 0.f) {
     const float s = ldexpf(448.0f / sel, -margin);
-    t->scale = s;
-    t->scale_inv = 1.0f / s;
-    flags |= FLUX_FP8_SCALE_SET;
+    const float inv = 1.0f / s;
+    // a scale that overflows (or underflows) fp32 is not taken: the old one stays
+    if (__builtin_isfinite(s) && s > 0.f && __builtin_isfinite(inv)) {
+      t->scale = s;
+      t->scale_inv = inv;
+      flags |= FLUX_FP8_SCALE_SET;
+    }
   }
   t->flags = flags;
   t->amax_bits = 0u;

@@ -26,9 +26,13 @@
  *    float.  With FLUX_PREC_BF16 weights and biases are bf16 (raw 16-bit
  *    patterns); attention runs on bf16 q, k, v with fp32 softmax and
  *    accumulation; the block linears multiply fp16 activations by the bf16
- *    weights, converted to fp16 inside the kernel (exact for magnitudes in
- *    fp16's normal range, error below 2^-24 under it), with fp32
- *    accumulation.  fp16 activations keep 3 more mantissa bits than bf16 at
+ *    weights, converted to fp16 (round toward zero) inside the kernel or once
+ *    beforehand (exact for magnitudes in fp16's normal range, error below
+ *    2^-24 under it), with fp32 accumulation.  The fp16 activation stores
+ *    (LayerNorm-modulate output, attention output, GELU output) round to
+ *    nearest even and saturate at +-65504, so a value beyond fp16's range is
+ *    clipped rather than turned into infinity; NaN stays NaN.  fp16
+ *    activations keep 3 more mantissa bits than bf16 at
  *    the same matrix-core rate, which the max-abs error bound of the block
  *    outputs needs at Flux-12B widths.  With FLUX_PREC_FP8_E4M3 the token-path
  *    linears of the blocks (qkv, proj, fc1, fc2; lin1, lin2) take OCP E4M3FN
@@ -389,8 +393,10 @@ flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, in
 
 /*
  * flux_convert_bf16_to_f16 -- dst[i] = fp16(src[i]) for n elements, rounded
- * to nearest even (exact for magnitudes in [2^-14, 65504]; a weight under
- * 2^-14 keeps an error below 2^-25).  For the one-time conversion of static
+ * toward zero, the rule the GEMM applies when it converts bf16 weights itself
+ * (exact for magnitudes in [2^-14, 65504]; a weight under 2^-14 keeps an
+ * error below 2^-24; finite magnitudes above 65504 saturate to +-65504;
+ * infinities and NaN pass through).  For the one-time conversion of static
  * linear weights used with flux_dims.weights_f16 = 1.  src and dst are device
  * pointers, 16-byte aligned, not overlapping.
  */

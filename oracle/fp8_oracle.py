@@ -43,6 +43,11 @@ Readings taken where that page is silent (each repeated at its function):
      an all-zero tile); elements are e4m3(v * 2^e), an exact product; the
      linear is y = sum over 128-wide k blocks of 2^-(e_x + e_w) sum q_x q_w
      + b.  A tile holding a non-finite value is not defined here.
+  F9 a new scale (delayed update or current scaling) is taken only when it
+     and its reciprocal are finite and non-zero in fp32; a selected amax
+     below about 448 / FLT_MAX, whose 448 / amax overflows, keeps the previous
+     scale exactly as a zero or non-finite amax does (the page's recipe
+     assumes a usable scale; an infinite one would turn zeros into NaN).
 """
 from __future__ import annotations
 
@@ -136,20 +141,37 @@ def scale_update(history: np.ndarray, amax_now: float, scale: float, algo: str =
     else:
         raise ValueError(algo)
     nonfinite = not np.isfinite(np.float32(amax_now))
+    new = np.float32(scale)
     if np.isfinite(sel) and sel > 0:
-        new = np.float32(np.float32(E4M3_MAX) / sel) * np.float32(2.0 ** -margin)
-    else:
-        new = np.float32(scale)
+        with np.errstate(over="ignore", divide="ignore"):
+            cand = np.float32(np.float32(E4M3_MAX) / sel) * np.float32(2.0 ** -margin)
+        if _usable_scale(cand):
+            new = cand
     return hist, float(new), nonfinite
+
+
+def _usable_scale(s) -> bool:
+    """A new scale replaces the old one only when it and its reciprocal are
+    finite, non-zero fp32 values (reading F9: a selected amax so small that
+    448 / amax overflows fp32 keeps the previous scale, as a non-finite amax
+    does; otherwise the cast would multiply zeros by infinity)."""
+    s = np.float32(s)
+    with np.errstate(over="ignore", divide="ignore"):
+        inv = np.float32(1.0) / s
+    return bool(np.isfinite(s) and s > 0 and np.isfinite(inv))
 
 
 def current_scale(x, scale_before: float = 1.0) -> float:
     """Current ("tensorwise") scaling, the recipe the page lists beside delayed
     scaling (F6): the scale of a tensor comes from its own amax,
-    fp32(448 / fp32(amax)); a zero or non-finite amax keeps scale_before."""
+    fp32(448 / fp32(amax)); a zero or non-finite amax, or one whose scale
+    overflows fp32 (F9), keeps scale_before."""
     a = np.float32(amax(x))
     if np.isfinite(a) and a > 0:
-        return float(np.float32(np.float32(E4M3_MAX) / a))
+        with np.errstate(over="ignore", divide="ignore"):
+            cand = np.float32(np.float32(E4M3_MAX) / a)
+        if _usable_scale(cand):
+            return float(cand)
     return float(np.float32(scale_before))
 
 

@@ -158,6 +158,25 @@ def test_scale_update_keeps_scale_on_zero_or_nonfinite_amax():
         assert s == 5.5 and nf == flag and len(h) == 3
 
 
+def test_scale_update_keeps_scale_when_the_new_one_overflows():
+    # F9: 448 / amax above FLT_MAX (amax below ~1.3e-36, subnormals included)
+    # keeps the old scale; no RuntimeWarning, no infinite scale
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        for a in (5e-39, 1e-37, 1e-45):
+            h, s, nf = Q.scale_update([], a, 3.0)
+            assert s == 3.0 and not nf and len(h) == 1
+            assert Q.current_scale(np.array([0.0, a, -a]), 2.5) == 2.5
+        # the smallest amax whose scale is still finite is taken, and so is its reciprocal
+        a = np.float32(448.0) / np.float32(3.0e38)
+        _, s, _ = Q.scale_update([], float(a), 3.0)
+        assert s == float(np.float32(448.0) / a) and np.isfinite(s) and np.isfinite(np.float32(1.0) / np.float32(s))
+        # the max algorithm selects the largest entry, whose scale is finite
+        _, s, _ = Q.scale_update([5e-39, 2.0], 5e-39, 3.0, algo="max")
+        assert s == 224.0
+
+
 def test_scale_update_max_algorithm_and_history_window():
     h = np.array([], np.float32)
     for a in [10.0] + [1.0] * (Q.HISTORY_LEN - 1):

@@ -153,7 +153,8 @@ def test_update_matches_oracle():
     cases = [  # (scale before or None, amax, history, algo, margin)
         (None, 3.5, [], 0, 0), (None, 0.07312, [], 0, 2), (7.0, 0.0, [1.0], 0, 0), (7.0, np.inf, [], 0, 0),
         (7.0, np.nan, [], 1, 0), (None, 1.0, [10.0] + [1.0] * 1022, 1, 0), (None, 2.0, [10.0] + [1.0] * 1023, 1, 0),
-        (3.0, 5e-39, [], 0, 0), (None, 448.0, [0.5, 900.0], 1, 1),
+        (3.0, 5e-39, [], 0, 0), (None, 448.0, [0.5, 900.0], 1, 1), (3.0, 1e-37, [], 0, 0),
+        (None, 5e-39, [], 0, 0),
     ]
     n = len(cases)
     rec = _records(n, [c[0] for c in cases], [c[1] for c in cases], [c[2] for c in cases])
@@ -175,6 +176,15 @@ def test_update_matches_oracle():
         assert same.all()
         if g["flags"] & 1:
             assert g["scale_inv"] == float(np.float32(1.0) / np.float32(g["scale"]))
+        assert np.isfinite(g["scale"]) and np.isfinite(g["scale_inv"]) and g["scale_inv"] > 0
+    # after an update whose 448 / amax overflowed, a cast of zeros gives zero codes (no 0 * inf = NaN)
+    i = cases.index((3.0, 5e-39, [], 0, 0))
+    r = rec[i * F().FP8_TENSOR_BYTES:(i + 1) * F().FP8_TENSOR_BYTES]
+    z = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    dst = torch.full((4096,), 0x55, dtype=torch.uint8, device="cuda")
+    F().flux_fp8_quantize(F().FLUX_PREC_F32, z, 4096, r, dst)
+    torch.cuda.synchronize()
+    assert int(dst.max().item()) == 0
 
 
 # --------------------------------------------------------------------------- #

@@ -293,22 +293,39 @@ def test_single_block_small(name, wf16):
     _check_single(wl, w1, inp, ids, g)
 
 
-def test_convert_bf16_to_f16_matches_rne():
+def _f16_toward_zero(a):
+    """fp16 of float32 values rounded toward zero, saturating finite values
+    at +-65504 (numpy rounds to nearest; step back one ulp where it rounded
+    away from zero)."""
+    with np.errstate(over="ignore"):
+        r = a.astype(np.float16)
+    big = np.isfinite(a) & (np.abs(a) > 65504.0)
+    r[big] = np.copysign(np.float16(65504.0), a[big]).astype(np.float16)
+    up = np.isfinite(r) & (np.abs(r.astype(np.float32)) > np.abs(a))
+    r[up] = np.nextafter(r[up], np.float16(0.0))
+    return r
+
+
+def test_convert_bf16_to_f16_toward_zero():
     _say("bf16 -> fp16 weight conversion")
     rng = np.random.default_rng(5)
     a = (0.02 * rng.standard_normal(100003)).astype(np.float32)
     a[:40] = np.float32(2.0) ** -np.arange(10, 50, dtype=np.float32)      # down through fp16 subnormals
     a[40:60] = rng.standard_normal(20).astype(np.float32) * 1000.0         # large magnitudes
+    a[60:64] = [7.0e4, -1.0e6, 65504.0, -3.0e38]                            # beyond fp16's range: saturate
+    a[100002] = -(2.0 ** -20) * 1.5                                        # odd tail element, subnormal
     a = synth.round_to_bf16(a)
     src = dev(a, True)
     dst = torch.empty(a.shape, dtype=torch.float16, device="cuda")
     F().flux_convert_bf16_to_f16(src, dst, a.size)
     torch.cuda.synchronize()
-    ref = a.astype(np.float16)                                             # numpy: round to nearest even
+    ref = _f16_toward_zero(a)
     assert np.array_equal(dst.cpu().numpy().view(np.uint16), ref.view(np.uint16))
     # exact wherever the magnitude is in fp16's normal range
-    normal = np.abs(a) >= 2.0 ** -14
+    normal = (np.abs(a) >= 2.0 ** -14) & (np.abs(a) <= 65504.0)
     assert np.array_equal(ref[normal].astype(np.float32), a[normal])
+    inr = np.abs(a) <= 65504.0
+    assert np.abs(ref[inr].astype(np.float64) - a[inr]).max() <= 2.0 ** -24
 
 
 def test_block_no_text_tokens():
