@@ -224,28 +224,49 @@ def summarize_counters(directory, out_dir):
     return 0
 
 
-def cpu_baseline(wl, w2, inp, ids, work):
-    """The fp64 oracle's double block on the full bench input (all 4608
-    tokens), timed on this host and scaled by algorithmic FLOPs to one step."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, emb, dws, sws, mi, work):
+    """The fp64 oracle running the whole bench step once on this host: rf
+    noising, image embedding, conditioning vector, the double and the single
+    block over all 4608 tokens, the output head and the velocity MSE, on the
+    same seeded inputs and weights as the GPU step.  BLAS threads are the
+    host cores this process may use."""
     import numpy as np
 
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    threads = cores
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [cores])
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
-    ang = O.rope_angles(ids, wl.axes_dim, wl.theta)
+        limiter = None
     t0 = time.perf_counter()
-    oi, ot = O.double_block(inp["x_img"], inp["x_txt"], inp["vec"], ang, w2, wl.heads, wl.eps)
+    zt, _ = O.rf_noise(mi["z0"], mi["z1"], mi["t"])
+    v = O.flux_forward(zt, mi["txt"], None, mi["t"], mi["ids"], emb, dws, sws, wl.heads, wl.axes_dim, wl.theta,
+                       wl.eps, wl.model_channels)
+    loss, _ = O.rf_loss(v, mi["z0"], mi["z1"])
     dt = time.perf_counter() - t0
-    assert np.isfinite(oi).all() and np.isfinite(ot).all()
-    flops_s = work["double_block_flops"] / dt
-    value = wl.tokens * flops_s / work["total_flops"]
-    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, one double block over the full {wl.l_txt}+{wl.l_img}-token input "
-                       f"({dt:.1f} s, {flops_s / 1e9:.1f} GFLOP/s), scaled by algorithmic FLOPs to one step"),
-            "seconds": round(dt, 2)}
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    assert np.isfinite(loss)
+    return {"value": round(wl.tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, one whole step (rf noise, embed, 1 double + 1 single block over "
+                       f"{wl.l_txt}+{wl.l_img} tokens, head, velocity MSE; {work['total_flops'] / 1e12:.2f} TFLOP) "
+                       f"in {dt:.1f} s = {work['total_flops'] / dt / 1e9:.1f} GFLOP/s on {threads} BLAS threads "
+                       f"({cores} usable cores, {_cpu_model()})"),
+            "seconds": round(dt, 2), "loss": loss}
 
 
 def mx_linears_bench(args, fp4=False) -> int:
@@ -582,9 +603,9 @@ def main() -> int:
         sws = [synth.device_block_weights(wl, wl.n_double + i, "single") for i in range(wl.n_single)]
     else:
         w2 = synth.double_block_weights(wl, 0)
+        w1 = synth.single_seq_block_weights(wl, 1) if seq else synth.single_block_weights(wl, 1)
         dws = [w2]
-        sws = [synth.single_seq_block_weights(wl, 1) if seq else synth.single_block_weights(wl, 1)]
-        inp = synth.block_inputs(wl)
+        sws = [w1]
     # block linears held in fp16, converted once here (static weights; not timed)
     m = FluxModel(wl, emb, dws, sws, weights_f16=True)
     del dws, sws
@@ -737,7 +758,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 weights and attention q/k/v; fp16 GEMM activation operands x fp16 copies of the weights, "
+                 "fp32 accumulation; fp32 residual stream",
         "data": "synthetic",
         "config": {"workload": "flux12b_full_forward_rf_step" if full else "flux12b_block_pair_rf_step",
                    "batch": wl.batch, "l_txt": wl.l_txt,
@@ -779,7 +801,7 @@ def main() -> int:
         rec["config"]["workload"] = "flux12b_block_pair_sequential_single_rf_step"
     if not args.no_cpu_baseline and not full and not fp8 and not seq and not sample:
         print("[bench] cpu baseline (oracle double block)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(wl, w2, inp, synth.joint_ids(wl), work)
+        rec["cpu_baseline"] = cpu_baseline(wl, emb, [w2], [w1], mi, work)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

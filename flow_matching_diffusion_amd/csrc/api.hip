@@ -324,8 +324,9 @@ static bool ranges_overlap(const void* a, int64_t la, const void* b, int64_t lb)
   return x < y + lb && y < x + la;
 }
 
-flux_status rf_noise_loss(const rf_args* a, void* stream) {
-  g_err[0] = 0;
+// Host-side checks shared by rf_noise_loss and rf_noise_loss_noalloc (the
+// workspace is checked by the caller).
+static flux_status rf_check(const rf_args* a) {
   REQUIRE(a, "args is NULL");
   REQUIRE(a->batch >= 1, "batch must be >= 1 (got %d)", a->batch);
   REQUIRE(a->n_per_sample >= 1, "n_per_sample must be >= 1");
@@ -340,21 +341,31 @@ flux_status rf_noise_loss(const rf_args* a, void* stream) {
     REQUIRE(!overlap(o, a->z0, bytes) && !overlap(o, a->z1, bytes), "z_t / v_target must not alias z0 or z1");
   }
   if (a->z_t && a->v_target) REQUIRE(!overlap(a->z_t, a->v_target, bytes), "z_t and v_target must not alias");
-  const bool want_loss = a->loss || a->loss_per_sample;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (want_loss) {
-    REQUIRE(a->v_pred, "a loss output needs v_pred");
-    flux_status s = check_workspace(a->workspace, a->workspace_bytes,
-                                    flux_rf_workspace_bytes(a->batch, a->n_per_sample));
-    if (s != FLUX_OK) return s;
-  }
+  if (a->loss || a->loss_per_sample) REQUIRE(a->v_pred, "a loss output needs v_pred");
+  return FLUX_OK;
+}
+
+// Enqueue noising and loss; `partials` holds batch * rf_parts_per_sample(n)
+// doubles when a loss is asked for.
+static flux_status rf_launch(const rf_args* a, double* partials, hipStream_t st) {
   if (a->z_t || a->v_target)
     FLUX_HIP(launch_rf_noise(a->batch, a->n_per_sample, a->z0, a->z1, a->t, a->z_t, a->v_target, st), "rf noise");
-  if (want_loss)
+  if (a->loss || a->loss_per_sample)
     FLUX_HIP(launch_rf_loss(a->batch, a->n_per_sample, a->z0, a->z1, a->v_pred, a->loss, a->loss_per_sample,
-                            static_cast<double*>(a->workspace), rf_parts_per_sample(a->n_per_sample), st),
+                            partials, rf_parts_per_sample(a->n_per_sample), st),
              "rf loss");
   return FLUX_OK;
+}
+
+flux_status rf_noise_loss(const rf_args* a, void* stream) {
+  g_err[0] = 0;
+  flux_status s = rf_check(a);
+  if (s != FLUX_OK) return s;
+  if (a->loss || a->loss_per_sample) {
+    s = check_workspace(a->workspace, a->workspace_bytes, flux_rf_workspace_bytes(a->batch, a->n_per_sample));
+    if (s != FLUX_OK) return s;
+  }
+  return rf_launch(a, static_cast<double*>(a->workspace), static_cast<hipStream_t>(stream));
 }
 
 // --------------------------------- sampling ---------------------------------
