@@ -800,7 +800,7 @@ def main() -> int:
         rec["metric"] = "MMDiT block fwd tokens/s, double + sequential single block (512 txt+4096 img)"
         rec["config"]["workload"] = "flux12b_block_pair_sequential_single_rf_step"
     if not args.no_cpu_baseline and not full and not fp8 and not seq and not sample:
-        print("[bench] cpu baseline (oracle double block)", file=sys.stderr, flush=True)
+        print("[bench] cpu baseline (oracle, whole step)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, emb, [w2], [w1], mi, work)
     else:
         rec["cpu_baseline"] = None

@@ -176,7 +176,7 @@ def test_update_matches_oracle():
         assert same.all()
         if g["flags"] & 1:
             assert g["scale_inv"] == float(np.float32(1.0) / np.float32(g["scale"]))
-        assert np.isfinite(g["scale"]) and np.isfinite(g["scale_inv"]) and g["scale_inv"] > 0
+            assert np.isfinite(g["scale"]) and np.isfinite(g["scale_inv"]) and g["scale_inv"] > 0
     # after an update whose 448 / amax overflowed, a cast of zeros gives zero codes (no 0 * inf = NaN)
     i = cases.index((3.0, 5e-39, [], 0, 0))
     r = rec[i * F().FP8_TENSOR_BYTES:(i + 1) * F().FP8_TENSOR_BYTES]
