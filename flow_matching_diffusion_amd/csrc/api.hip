@@ -15,6 +15,17 @@
 using namespace flux;
 using namespace flux::api;
 
+// Destination of the fused q|k|v epilogue: the attention operand layouts
+// (head-major q, k; transposed v) with RMSNorm scales gq / gk and the RoPE
+// table; tok0 is the joint position of the problem's first row of a sample.
+static QkvOut qkv_out(const flux_dims* d, void* qh, void* kh, void* vt, const float* gq, const float* gk,
+                      const float* rope, int64_t L, int64_t Lp, int64_t tok0) {
+  QkvOut q{};
+  q.qh = qh; q.kh = kh; q.vt = vt; q.gq = gq; q.gk = gk; q.rope = rope;
+  q.heads = d->heads; q.seq = (int32_t)L; q.seq_pad = (int32_t)Lp; q.tok0 = (int32_t)tok0; q.eps = d->eps;
+  return q;
+}
+
 // ================================ public API ================================
 extern "C" {
 
@@ -120,10 +131,20 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i].qa = rec(i, FLUX_FP8_QKV_X);
     g.p[i].qw = rec(i, FLUX_FP8_QKV_W);
   }
+  const int64_t Lp = seq_pad_of(L);
+  // 3-4 fused: on the persistent GEMM the epilogue applies RMSNorm(q),
+  // RMSNorm(k) and RoPE and writes the attention layouts itself
+  if (!f32 && d->head_dim == 128 && gemm_is_persistent(g, lin)) {
+    for (int i = 0; i < ns; ++i) {
+      g.p[i].epi = kEpiQkv;
+      g.p[i].qkv = qkv_out(d, w.qh, w.kh, w.vt, sw[i]->q_norm, sw[i]->k_norm, rope, L, Lp, off[i]);
+    }
+    FLUX_HIP(launch_attn_pad_zero(w.qh, w.kh, w.vt, (int)B, d->heads, (int)L, (int)Lp, st), "attention padding");
+    FLUX_HIP(launch_gemm(g, lin, st), "qkv GEMM + q/k norm + RoPE");
+  } else {
   FLUX_HIP(launch_gemm(g, lin, st), "qkv GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE, head-major layout
-  const int64_t Lp = seq_pad_of(L);
   PrepArgs pa{};
   pa.src_q = w.big;
   pa.src_k = elem_ptr(w.big, D, es);
@@ -138,6 +159,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
   pa.rope = rope; pa.eps = d->eps;
   pa.qh = w.qh; pa.kh = w.kh; pa.vt = w.vt;
   FLUX_HIP(launch_prep(pa, qkv_t, st), "q/k norm + RoPE");
+  }
 
   // 5. joint attention over image|text rows
   AttnArgs aa{};
@@ -267,10 +289,18 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   g.p[0].qa = rec(FLUX_FP8_LIN1_X);
   g.p[0].qw = rec(FLUX_FP8_LIN1_W);
   g.p[0].qo = rec(FLUX_FP8_LIN2_X);
+  const int64_t Lp = seq_pad_of(L);
+  // 3-4 fused on the persistent GEMM: q|k|v columns go to the attention
+  // layouts with RMSNorm and RoPE applied, the rest through GELU
+  if (!f32 && d->head_dim == 128 && gemm_is_persistent(g, lin)) {
+    g.p[0].epi = kEpiQkvSplitGelu;
+    g.p[0].qkv = qkv_out(d, w.qh, w.kh, w.vt, sw->q_norm, sw->k_norm, rope, L, Lp, 0);
+    FLUX_HIP(launch_attn_pad_zero(w.qh, w.kh, w.vt, (int)B, d->heads, (int)L, (int)Lp, st), "attention padding");
+    FLUX_HIP(launch_gemm(g, lin, st), "linear1 GEMM + q/k norm + RoPE");
+  } else {
   FLUX_HIP(launch_gemm(g, lin, st), "linear1 GEMM");
 
   // 4. RMSNorm(q), RMSNorm(k), RoPE
-  const int64_t Lp = seq_pad_of(L);
   PrepArgs pa{};
   pa.src_q = w.qkv;
   pa.src_k = elem_ptr(w.qkv, D, es);
@@ -284,6 +314,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   pa.rope = rope; pa.eps = d->eps;
   pa.qh = w.qh; pa.kh = w.kh; pa.vt = w.vt;
   FLUX_HIP(launch_prep(pa, qkv_t, st), "q/k norm + RoPE");
+  }
 
   // 5. attention -> columns 0..D of the linear2 input
   AttnArgs aa{};

@@ -514,9 +514,184 @@ __device__ __forceinline__ void apply_quarter(const GemmProblem& pc, const float
   }
 }
 
+// The q|k|v projection straight into the attention layouts ("Flux model API
+// reference", RMSNorm and EmbedND; "Flux architecture deep dive", 3D RoPE
+// mathematics).  A wave's 128 columns are exactly one head of q, k or v.  Each
+// 32-row strip is staged as its two 64-column halves; a lane then holds
+// columns c4..c4+3 of both halves for 8 rows, so the RMSNorm sum over the
+// head's 128 values is a 16-lane butterfly (fixed order), and the
+// interleaved RoPE pairs (2m, 2m+1) are lane-local.  q and k rows are written
+// head-major, v transposed, all in bf16.
+__device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16_t (&acc)[4][4], float* cs,
+                                             int row0, int col0, int lane, float dq) {
+  if (col0 >= pc.N) return;                       // wave-uniform: no columns here
+  const QkvOut& q = pc.qkv;
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int c4 = (lane & 15) * 4, lrow = lane >> 4;
+  const int D = q.heads * 128;
+  const int region = col0 / D;                    // 0 q, 1 k, 2 v (wave-uniform)
+  const int h = (col0 - region * D) >> 7;
+  float4 bA = make_float4(0.f, 0.f, 0.f, 0.f), bB = bA;
+  if (pc.bias) {
+    const uint2 ba = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(pc.bias) + col0 + c4);
+    const uint2 bb = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(pc.bias) + col0 + 64 + c4);
+    bA = make_float4(__uint_as_float(ba.x << 16), __uint_as_float(ba.x & 0xffff0000u), __uint_as_float(ba.y << 16),
+                     __uint_as_float(ba.y & 0xffff0000u));
+    bB = make_float4(__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u), __uint_as_float(bb.y << 16),
+                     __uint_as_float(bb.y & 0xffff0000u));
+  }
+  float4 gA = make_float4(1.f, 1.f, 1.f, 1.f), gB = gA;
+  const float* gm = region == 0 ? q.gq : q.gk;
+  if (region < 2 && gm) {
+    gA = *reinterpret_cast<const float4*>(gm + c4);
+    gB = *reinterpret_cast<const float4*>(gm + 64 + c4);
+  }
+  bf16_t* dst = reinterpret_cast<bf16_t*>(region == 0 ? q.qh : q.kh);
+  bf16_t* vt = reinterpret_cast<bf16_t*>(q.vt);
+  const int seg = pc.omap0.seg;
+  if (region == 2) {
+    // v: each staged 32 x 64 quarter is read by columns (lane = head dim, a
+    // conflict-free LDS row per step) and written transposed, 8 tokens per
+    // 16-byte store, when the strip's 32 rows are 32 consecutive tokens of one
+    // sample starting at a multiple of 8; otherwise element by element
+    float bl0 = 0.f, bl1 = 0.f;   // bias of the lane's column in each half
+    if (pc.bias) {
+      const bf16_t* bp = reinterpret_cast<const bf16_t*>(pc.bias);
+      bl0 = bf16_to_f32(bp[col0 + lane]);
+      bl1 = bf16_to_f32(bp[col0 + 64 + lane]);
+    }
+#pragma unroll 1
+    for (int Q = 0; Q < 8; ++Q) {
+      switch (Q) {
+        case 0: stage_quarter<0>(acc, cs, frow, fhalf); break;
+        case 1: stage_quarter<1>(acc, cs, frow, fhalf); break;
+        case 2: stage_quarter<2>(acc, cs, frow, fhalf); break;
+        case 3: stage_quarter<3>(acc, cs, frow, fhalf); break;
+        case 4: stage_quarter<4>(acc, cs, frow, fhalf); break;
+        case 5: stage_quarter<5>(acc, cs, frow, fhalf); break;
+        case 6: stage_quarter<6>(acc, cs, frow, fhalf); break;
+        default: stage_quarter<7>(acc, cs, frow, fhalf); break;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+      const int half = Q & 1, r0 = row0 + (Q >> 1) * 32;
+      const float bv = half ? bl1 : bl0;
+      const int b0 = r0 < pc.M ? r0 / seg : 0;
+      const int l0 = q.tok0 + (r0 < pc.M ? r0 % seg : 0);
+      const bool fast = r0 + 31 < pc.M && (r0 % seg) + 31 < seg && (l0 & 7) == 0;   // wave-uniform
+      bf16_t* col = vt + (((int64_t)b0 * q.heads + h) * 128 + half * 64 + lane) * q.seq_pad;
+      if (fast) {
+#pragma unroll
+        for (int g8 = 0; g8 < 4; ++g8) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pk[e] = pack_bf16x2(cs[(8 * g8 + 2 * e) * 64 + lane] * dq + bv, cs[(8 * g8 + 2 * e + 1) * 64 + lane] * dq + bv);
+          *reinterpret_cast<uint4*>(col + l0 + 8 * g8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+      } else {
+        for (int r = 0; r < 32; ++r) {
+          const int row = r0 + r;
+          if (row >= pc.M) break;
+          const int b = row / seg, l = q.tok0 + row % seg;
+          vt[(((int64_t)b * q.heads + h) * 128 + half * 64 + lane) * q.seq_pad + l] =
+              f32_to_bf16(cs[r * 64 + lane] * dq + bv);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
+#pragma unroll 1
+  for (int qq = 0; qq < 4; ++qq) {
+    float4 wA[8], wB[8], tA[8], tB[8];
+    // the RoPE pairs of the strip's rows, loaded before the staging so their
+    // latency overlaps it (rows past M read row 0's entry and store nothing)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = row0 + qq * 32 + lrow + 4 * u;
+      const int rr = row < pc.M ? row : 0;
+      const float* tab = q.rope + ((int64_t)(rr / seg) * q.seq + q.tok0 + rr % seg) * 128;   // 64 (cos, sin)
+      if (q.rope) {
+        tA[u] = *reinterpret_cast<const float4*>(tab + c4);
+        tB[u] = *reinterpret_cast<const float4*>(tab + 64 + c4);
+      }
+    }
+    switch (qq) {
+      case 0: stage_quarter<0>(acc, cs, frow, fhalf); break;
+      case 1: stage_quarter<2>(acc, cs, frow, fhalf); break;
+      case 2: stage_quarter<4>(acc, cs, frow, fhalf); break;
+      default: stage_quarter<6>(acc, cs, frow, fhalf); break;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 t = *reinterpret_cast<const float4*>(&cs[(lrow + 4 * u) * 64 + c4]);
+      wA[u] = make_float4(t.x * dq + bA.x, t.y * dq + bA.y, t.z * dq + bA.z, t.w * dq + bA.w);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+    switch (qq) {
+      case 0: stage_quarter<1>(acc, cs, frow, fhalf); break;
+      case 1: stage_quarter<3>(acc, cs, frow, fhalf); break;
+      case 2: stage_quarter<5>(acc, cs, frow, fhalf); break;
+      default: stage_quarter<7>(acc, cs, frow, fhalf); break;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 t = *reinterpret_cast<const float4*>(&cs[(lrow + 4 * u) * 64 + c4]);
+      wB[u] = make_float4(t.x * dq + bB.x, t.y * dq + bB.y, t.z * dq + bB.z, t.w * dq + bB.w);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = row0 + qq * 32 + lrow + 4 * u;
+      const bool ok = row < pc.M;
+      const int rr = ok ? row : 0;
+      const int b = rr / seg, l = q.tok0 + rr % seg;
+      const int64_t hrow = (int64_t)b * q.heads + h;
+      float4 a = wA[u], c = wB[u];
+      {
+        float ss = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + c.x * c.x + c.y * c.y + c.z * c.z + c.w * c.w;
+        ss = wave_sum<16>(ss);
+        const float rs = 1.0f / sqrtf(ss / 128.0f + q.eps);
+        a = make_float4(a.x * rs * gA.x, a.y * rs * gA.y, a.z * rs * gA.z, a.w * rs * gA.w);
+        c = make_float4(c.x * rs * gB.x, c.y * rs * gB.y, c.z * rs * gB.z, c.w * rs * gB.w);
+        if (q.rope) {
+          const float4 ta = tA[u], tb = tB[u];
+          a = make_float4(a.x * ta.x - a.y * ta.y, a.x * ta.y + a.y * ta.x, a.z * ta.z - a.w * ta.w,
+                          a.z * ta.w + a.w * ta.z);
+          c = make_float4(c.x * tb.x - c.y * tb.y, c.x * tb.y + c.y * tb.x, c.z * tb.z - c.w * tb.w,
+                          c.z * tb.w + c.w * tb.z);
+        }
+        if (ok) {
+          bf16_t* o = dst + (hrow * q.seq_pad + l) * 128;
+          *reinterpret_cast<uint2*>(o + c4) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+          *reinterpret_cast<uint2*>(o + 64 + c4) = make_uint2(pack_bf16x2(c.x, c.y), pack_bf16x2(c.z, c.w));
+        }
+      }
+    }
+  }
+}
+
 template <int EPI>
 __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x16_t (&acc)[4][4], float* cs,
                                               int row0, int col0, int lane, float dq, float qs, uint32_t& mx) {
+  if constexpr (EPI == kEpiQkv) {
+    qkv_epilogue(pc, acc, cs, row0, col0, lane, dq);
+    return;
+  } else if constexpr (EPI == kEpiQkvSplitGelu) {
+    if (col0 < pc.n_split) {
+      qkv_epilogue(pc, acc, cs, row0, col0, lane, dq);
+      return;
+    }
+  }
+  constexpr int E = EPI == kEpiQkvSplitGelu ? (int)kEpiSplitGelu : EPI;   // columns past n_split: GELU to out1
   const int frow = lane & 31, fhalf = lane >> 5;
   const int c4 = (lane & 15) * 4, lrow = lane >> 4;
   // bias and gate of the lane's four columns in each column half, read once
@@ -536,7 +711,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
       bias1 = make_float4(__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
                           __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u));
     }
-    if constexpr (EPI == kEpiResid) {
+    if constexpr (E == kEpiResid) {
       gate0 = *reinterpret_cast<const float4*>(pc.gate + b0 * pc.gate_bstride + cA);
       gate1 = *reinterpret_cast<const float4*>(pc.gate + b0 * pc.gate_bstride + cB);
     }
@@ -545,10 +720,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
   // residual rows are loaded one quarter ahead (xa for the first column half,
   // xb for the second)
   float4 xa[8], xb[8];
-  if constexpr (EPI == kEpiResid) load_resid(pc, row0 + lrow, col0 + c4, xa);
+  if constexpr (E == kEpiResid) load_resid(pc, row0 + lrow, col0 + c4, xa);
 #pragma unroll 1
   for (int qq = 0; qq < 4; ++qq) {
-    if constexpr (EPI == kEpiResid) load_resid(pc, row0 + qq * 32 + lrow, col0 + 64 + c4, xb);
+    if constexpr (E == kEpiResid) load_resid(pc, row0 + qq * 32 + lrow, col0 + 64 + c4, xb);
     switch (qq) {
       case 0: stage_quarter<0>(acc, cs, frow, fhalf); break;
       case 1: stage_quarter<2>(acc, cs, frow, fhalf); break;
@@ -557,10 +732,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
     __builtin_amdgcn_sched_barrier(0);
-    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + c4, bias0, gate0, uniform, dq, qs, mx, xa);
+    apply_quarter<E>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + c4, bias0, gate0, uniform, dq, qs, mx, xa);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next quarter overwrites the staging
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (EPI == kEpiResid) {
+    if constexpr (E == kEpiResid) {
       if (qq < 3) load_resid(pc, row0 + (qq + 1) * 32 + lrow, col0 + c4, xa);
     }
     switch (qq) {
@@ -571,7 +746,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
-    apply_quarter<EPI>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + 64 + c4, bias1, gate1, uniform, dq, qs, mx,
+    apply_quarter<E>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + 64 + c4, bias1, gate1, uniform, dq, qs, mx,
                        xb);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
@@ -1187,40 +1362,59 @@ static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream
     hipLaunchKernelGGL((gemm_dl_kernel<OP, EPI>), dim3(grid), dim3(256), 0, stream, big);
 }
 
-template <int OP>
-static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
-  bt.ksplit = 1;
-  GemmBatch big = bt;
+// Conditions of the persistent 256 x 256 kernels for 16-bit or E4M3 operands.
+static bool persistent_ok(GemmBatch big, int op) {
   const int tiles_big = assign_tiles(big, 256, 256);
-  bool seg_ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
-  for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].omap0.seg >= 32;
-  if constexpr (OP == kFP8) {   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
-    for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K % 128 == 0 && big.p[i].K >= 256;
-    for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && fp8_span_ok(big.p[i]);
+  bool ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
+  for (int i = 0; i < big.count; ++i) ok = ok && big.p[i].omap0.seg >= 32;
+  if (op == kFP8) {   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
+    for (int i = 0; i < big.count; ++i) ok = ok && big.p[i].K % 128 == 0 && big.p[i].K >= 256;
+    for (int i = 0; i < big.count; ++i) ok = ok && fp8_span_ok(big.p[i]);
   } else {   // gemm_dl_kernel: k in super-stages of 64; operand rows as 32-bit byte offsets
     for (int i = 0; i < big.count; ++i) {
       const GemmProblem& q = big.p[i];
       const int64_t last = q.M - 1;
       const int64_t a_span = ((last / q.amap.seg) * q.amap.bstride + (last % q.amap.seg) * q.amap.ld + q.K) * 2;
       const int64_t w_span = ((int64_t)(q.N - 1) * q.ldw + q.K) * 2;
-      seg_ok = seg_ok && q.K % 64 == 0 && a_span < (int64_t(1) << 32) && w_span < (int64_t(1) << 32);
+      ok = ok && q.K % 64 == 0 && a_span < (int64_t(1) << 32) && w_span < (int64_t(1) << 32);
     }
   }
   // the persistent kernel needs at least half the CUs busy with 256 x 256
   // tiles; with K < 512 a tile is mostly epilogue, which smaller tiles spread
   // over more CUs
-  for (int i = 0; i < big.count; ++i) seg_ok = seg_ok && big.p[i].K >= 512;
-  if (tiles_big >= 128 && seg_ok) {
+  for (int i = 0; i < big.count; ++i) ok = ok && big.p[i].K >= 512;
+  return tiles_big >= 128 && ok;
+}
+
+bool gemm_is_persistent(const GemmBatch& bt, int op) {
+  if (op == kMXFP8 || op == kMXFP4 || op == kF32) return false;   // no attention-layout epilogue there
+  return persistent_ok(bt, op);
+}
+
+template <int OP>
+static hipError_t launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
+  bt.ksplit = 1;
+  GemmBatch big = bt;
+  const int tiles_big = assign_tiles(big, 256, 256);
+  const int epi = big.p[0].epi;   // the problems of one launch share the epilogue kind
+  if (persistent_ok(big, OP)) {
     const int grid = tiles_big < 256 ? tiles_big : 256;
     TimingScope ts(OP == kFP8 ? kKcGemmPkFp8 : OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
-    switch (big.p[0].epi) {   // the problems of one launch share the epilogue kind
+    switch (epi) {
       case kEpiStore: launch_persistent<OP, kEpiStore>(big, grid, stream); break;
       case kEpiGelu: launch_persistent<OP, kEpiGelu>(big, grid, stream); break;
       case kEpiResid: launch_persistent<OP, kEpiResid>(big, grid, stream); break;
       case kEpiStoreF32: launch_persistent<OP, kEpiStoreF32>(big, grid, stream); break;
+      case kEpiQkv: launch_persistent<OP, kEpiQkv>(big, grid, stream); break;
+      case kEpiQkvSplitGelu: launch_persistent<OP, kEpiQkvSplitGelu>(big, grid, stream); break;
       default: launch_persistent<OP, kEpiSplitGelu>(big, grid, stream); break;
     }
-  } else {
+    return hipSuccess;
+  }
+  // the attention-layout epilogues exist in the persistent kernels only; the
+  // caller checks gemm_is_persistent first
+  if (epi == kEpiQkv || epi == kEpiQkvSplitGelu) return hipErrorInvalidValue;
+  {
     const int tiles = assign_tiles(bt, 128, 128);
     // split K when the tiles fill less than half the GPU, the caller gave
     // scratch and the epilogue writes no E4M3 output (whose amax the
@@ -1239,6 +1433,7 @@ static void launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
                          bt.partials, ks);
     }
   }
+  return hipSuccess;
 }
 
 // MX operands: always the persistent kernel (its K loop needs an even number
@@ -1260,6 +1455,31 @@ static void launch_mx(GemmBatch bt, hipStream_t stream, double flops) {
   }
 }
 
+// Zero the rows [seq, seq_pad) of every (batch, head) of qh and kh and the
+// columns [seq, seq_pad) of every row of vt.
+__global__ void attn_pad_zero_kernel(bf16_t* qh, bf16_t* kh, bf16_t* vt, int batch, int heads, int seq,
+                                     int seq_pad) {
+  const int pad = seq_pad - seq;
+  const int64_t bh = blockIdx.y;              // (batch, head)
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < pad * 128; i += gridDim.x * blockDim.x) {
+    const int r = seq + i / 128, d = i % 128;
+    qh[(bh * seq_pad + r) * 128 + d] = 0;
+    kh[(bh * seq_pad + r) * 128 + d] = 0;
+    vt[(bh * 128 + d) * seq_pad + r] = 0;
+  }
+}
+
+hipError_t launch_attn_pad_zero(void* qh, void* kh, void* vt, int batch, int heads, int seq, int seq_pad,
+                                hipStream_t stream) {
+  if (seq_pad <= seq) return hipSuccess;
+  TimingScope ts(kKcMisc, stream);
+  const int n = (seq_pad - seq) * 128;
+  hipLaunchKernelGGL(attn_pad_zero_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)(batch * heads)), dim3(256), 0,
+                     stream, static_cast<bf16_t*>(qh), static_cast<bf16_t*>(kh), static_cast<bf16_t*>(vt), batch,
+                     heads, seq, seq_pad);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
   const double flops = gemm_flops(bt);
   if (op == kMXFP8 || op == kMXFP4) {
@@ -1274,14 +1494,16 @@ hipError_t launch_gemm(GemmBatch bt, int op, hipStream_t stream) {
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(tiles), dim3(256), 0, stream, bt);
     return hipGetLastError();
   }
+  hipError_t e;
   if (op == kFP8)
-    launch_mfma<kFP8>(bt, stream, flops);
+    e = launch_mfma<kFP8>(bt, stream, flops);
   else if (op == kF16W)
-    launch_mfma<kF16W>(bt, stream, flops);
+    e = launch_mfma<kF16W>(bt, stream, flops);
   else if (op == kF16)
-    launch_mfma<kF16>(bt, stream, flops);
+    e = launch_mfma<kF16>(bt, stream, flops);
   else
-    launch_mfma<kBF16>(bt, stream, flops);
+    e = launch_mfma<kBF16>(bt, stream, flops);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

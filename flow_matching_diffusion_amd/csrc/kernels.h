@@ -47,6 +47,24 @@ enum EpiKind : int {
   kEpiResid = 2,      // out0 (float) += gate[b, col] * (acc + bias)
   kEpiStoreF32 = 3,   // out0 (float) = acc + bias            (column stride col_stride)
   kEpiSplitGelu = 4,  // col < n_split: out0 = T0(acc + bias); else out1[col - n_split] = T1(GELU(acc + bias))
+  // The attention operands straight from the q|k|v projection (persistent
+  // kernel, head_dim 128): columns [0, D) are q, [D, 2D) k, [2D, 3D) v of
+  // `QkvOut`; q and k rows get RMSNorm (per head, scale gq / gk) and RoPE,
+  // then go to the head-major layouts qh / kh; v goes to vt transposed.
+  kEpiQkv = 5,
+  // kEpiQkv on columns < n_split (= 3D), GELU to out1 on the rest (single block)
+  kEpiQkvSplitGelu = 6,
+};
+
+// Destination of the kEpiQkv epilogues: the layouts launch_prep writes.
+struct QkvOut {
+  void* qh; void* kh;                   // [B, heads, seq_pad, 128] bf16
+  void* vt;                             // [B, heads, 128, seq_pad] bf16
+  const float* gq; const float* gk;     // RMSNorm scales [128]
+  const float* rope;                    // [B, seq, 64, 2] (cos, sin) per pair
+  int32_t heads, seq, seq_pad;          // joint sequence
+  int32_t tok0;                         // joint position of this problem's row l = 0 of a sample
+  float eps;
 };
 
 struct GemmProblem {
@@ -64,6 +82,7 @@ struct GemmProblem {
   flux_fp8_tensor* qo;                  // kFP8 output (out0 of kEpiGelu, out1 of kEpiSplitGelu)
   const uint8_t* sa;                    // kMXFP8 / kMXFP4 operands: E8M0 block scales of A and W in
   const uint8_t* sb;                    //   the GEMM layout of their quantizer (null otherwise)
+  QkvOut qkv;                           // kEpiQkv / kEpiQkvSplitGelu (rows map to samples by omap0.seg)
   int32_t tile_begin;                   // filled by the launcher
   int32_t tiles_n;                      // filled by the launcher
 };
@@ -81,6 +100,13 @@ struct GemmBatch {
 constexpr int kGemmMaxSplit = 8;
 
 hipError_t launch_gemm(GemmBatch batch, int op, hipStream_t stream);
+// True when launch_gemm runs this batch (16-bit or E4M3 operands) on the
+// persistent 256 x 256 kernel, the only one with the kEpiQkv epilogues.
+bool gemm_is_persistent(const GemmBatch& batch, int op);
+// Zero the padded rows [seq, seq_pad) of qh / kh and the padded columns of vt
+// (the attention kernels read them; kEpiQkv writes real rows only).
+hipError_t launch_attn_pad_zero(void* qh, void* kh, void* vt, int batch, int heads, int seq, int seq_pad,
+                                hipStream_t stream);
 
 // ------------------------------ LN + modulate ------------------------------
 struct LnSeg {

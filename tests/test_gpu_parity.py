@@ -428,3 +428,34 @@ def test_forward_tiny_bf16_with_pooled_vector():
 def test_forward_flux535m():
     _say("whole forward + loss flux535m (L=1536), fp16-held linear weights")
     _forward_case(synth.WORKLOADS["flux535m"], weights_f16=True)
+
+
+@pytest.fixture(scope="module")
+def padded_case():
+    # batch 2, 50x60 image + 77 text tokens: L = 3077 is padded to 3328 for
+    # attention, the text stream starts at a row that is not a multiple of 32,
+    # and the q|k|v projection still runs on the persistent GEMM, whose
+    # epilogue writes the attention layouts (RMSNorm and RoPE fused)
+    wl = synth.custom_workload("padded_12b_width", base="flux12b_blocks", batch=2, img_h=50, img_w=60, l_txt=77)
+    _say("generating padded 12B-width weights")
+    w2, w1, inp, ids = _block_fixture(wl)
+    ids = synth.joint_ids(wl, channel_group=True)        # axis-0 ids nonzero: every RoPE axis turns
+    return wl, w2, w1, inp, ids
+
+
+@pytest.mark.slow
+def test_fused_qkv_epilogue_double_block_padded(padded_case):
+    wl, w2, w1, inp, ids = padded_case
+    _say("double block, B=2, L=3000+77 (padded to 3328), fused q/k norm + RoPE epilogue, sampled rows")
+    g = _run_pair(wl, w2, w1, inp, ids, "double", True)
+    ri, rt = _sample_rows(wl, 3)
+    _check_double(wl, w2, inp, ids, g, rows=(ri, rt))
+
+
+@pytest.mark.slow
+def test_fused_qkv_epilogue_single_block_padded(padded_case):
+    wl, w2, w1, inp, ids = padded_case
+    _say("single block, B=2, L=3077 (padded to 3328), fused q/k norm + RoPE epilogue, sampled rows")
+    g = _run_pair(wl, w2, w1, inp, ids, "single", True)
+    ri, rt = _sample_rows(wl, 4)
+    _check_single(wl, w1, inp, ids, g, rows=np.r_[ri, wl.l_img + rt])
