@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/flux.h"
 #include "api_common.h"
 #include "common.h"
@@ -397,6 +399,51 @@ flux_status rf_noise_loss(const rf_args* a, void* stream) {
     if (s != FLUX_OK) return s;
   }
   return rf_launch(a, static_cast<double*>(a->workspace), static_cast<hipStream_t>(stream));
+}
+
+// ------------------------- rf_noise_loss without a workspace -------------------------
+// The loss partials live in a file-scope device array instead of a caller
+// workspace.  In host code `scratch` names a host-side stand-in, so its device
+// address is looked up once per device (hipGetSymbolAddress with that device
+// current) and only that address is ever passed to kernels.
+constexpr int kRfScratchDoubles = 8192;   // 64 KiB: batch * parts <= 8192
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) double scratch[kRfScratchDoubles];
+
+static std::mutex g_scratch_mu;
+static double* g_scratch_ptr[kMaxDevices];
+
+static flux_status scratch_for_current_device(double** out) {
+  int dev = -1;
+  FLUX_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FLUX_ERR_UNSUPPORTED, "device ordinal %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    FLUX_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(FLUX_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = static_cast<double*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FLUX_OK;
+}
+
+int64_t flux_rf_noalloc_max_partials(void) { return kRfScratchDoubles; }
+
+flux_status rf_noise_loss_noalloc(const rf_args* a, void* stream) {
+  g_err[0] = 0;
+  flux_status s = rf_check(a);
+  if (s != FLUX_OK) return s;
+  double* partials = nullptr;
+  if (a->loss || a->loss_per_sample) {
+    const int64_t need = (int64_t)a->batch * rf_parts_per_sample(a->n_per_sample);
+    if (need > kRfScratchDoubles)
+      return fail(FLUX_ERR_WORKSPACE_TOO_SMALL,
+                  "batch %d needs %lld loss partials, above the static scratch of %d; use rf_noise_loss",
+                  a->batch, (long long)need, kRfScratchDoubles);
+    if ((s = scratch_for_current_device(&partials)) != FLUX_OK) return s;
+  }
+  return rf_launch(a, partials, static_cast<hipStream_t>(stream));
 }
 
 // --------------------------------- sampling ---------------------------------

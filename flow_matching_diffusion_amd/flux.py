@@ -46,7 +46,8 @@ EXPORTED = (
     "flux_attention_bwd", "flux_rf_loss_grad", "flux_final_bwd_workspace_bytes", "flux_final_bwd",
     "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
     "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd", "flux_mxfp4_scale_bytes", "flux_mxfp4_quantize",
-    "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize", "flux_timestep_embed",
+    "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize", "flux_timestep_embed", "rf_noise_loss_noalloc",
+    "flux_rf_noalloc_max_partials",
 )
 
 
@@ -139,6 +140,7 @@ def lib() -> C.CDLL:
         "flux_single_fwd": [P(flux_dims), P(flux_single_weights), vp, i64, vp, vp, vp, sz, vp],
         "flux_single_seq_fwd": [P(flux_dims), P(flux_stream_weights), vp, i64, vp, vp, vp, sz, vp],
         "rf_noise_loss": [P(rf_args), vp],
+        "rf_noise_loss_noalloc": [P(rf_args), vp],
         "flux_rope_table": [vp, i32, i32, P(C.c_int32), f32, vp, vp],
         "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
                            vp, vp, i64, vp, i64, vp, vp, sz, vp],
@@ -181,6 +183,8 @@ def lib() -> C.CDLL:
         fn.argtypes = args
         fn.restype = C.c_int
     L.flux_workspace_bytes.argtypes = [P(flux_dims), i32]
+    L.flux_rf_noalloc_max_partials.argtypes = []
+    L.flux_rf_noalloc_max_partials.restype = i64
     L.flux_fp8_state_bytes.argtypes = [i32]
     L.flux_fp8_state_bytes.restype = sz
     L.flux_workspace_bytes.restype = sz
@@ -373,6 +377,19 @@ def rf_noise_loss(batch: int, n_per_sample: int, z0, z1, t, z_t=None, v_target=N
     a.loss, a.loss_per_sample, a.workspace = map(ptr, (loss, loss_per_sample, workspace))
     a.workspace_bytes = workspace_bytes
     _check(lib().rf_noise_loss(C.byref(a), _stream(stream)), "rf_noise_loss")
+
+
+def rf_noise_loss_noalloc(batch: int, n_per_sample: int, z0, z1, t, z_t=None, v_target=None, v_pred=None,
+                          loss=None, loss_per_sample=None, stream=None) -> None:
+    a = rf_args()
+    a.batch, a.n_per_sample = batch, n_per_sample
+    a.z0, a.z1, a.t, a.z_t, a.v_target, a.v_pred = map(ptr, (z0, z1, t, z_t, v_target, v_pred))
+    a.loss, a.loss_per_sample = map(ptr, (loss, loss_per_sample))
+    _check(lib().rf_noise_loss_noalloc(C.byref(a), _stream(stream)), "rf_noise_loss_noalloc")
+
+
+def flux_rf_noalloc_max_partials() -> int:
+    return lib().flux_rf_noalloc_max_partials()
 
 
 def flux_rope_table(ids, batch: int, seq: int, axes_dim, theta: float, table, stream=None) -> None:

@@ -263,6 +263,25 @@ typedef struct {
 flux_status rf_noise_loss(const rf_args* args, void* stream);
 
 /*
+ * rf_noise_loss_noalloc -- rf_noise_loss for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and errors as rf_noise_loss; args->workspace and workspace_bytes are
+ * ignored.  The loss partials go to a static 64 KiB device array (8192
+ * doubles) that each GPU holds until the process ends; a loss over more than
+ * flux_rf_noalloc_max_partials() partials (batch * min(256, ceil(n / 4096)))
+ * returns FLUX_ERR_WORKSPACE_TOO_SMALL with nothing enqueued.  The array's
+ * device address is looked up on the first call on each device (the device
+ * current on the calling thread).  Every call on one GPU shares that array
+ * and no clearing is needed (each call writes every partial it reads), so
+ * calls that overlap in time on one GPU (different streams, or threads
+ * without ordering) race and must be serialised by the caller.  Never calls
+ * hipMalloc or hipFree.
+ */
+flux_status rf_noise_loss_noalloc(const rf_args* args, void* stream);
+int64_t flux_rf_noalloc_max_partials(void);
+
+/*
  * flux_euler_step -- one step of the Euler sampler with optional
  * classifier-free guidance ("Flux architecture deep dive", Sampling
  * (inference) / Euler integration and Classifier-free guidance).
@@ -705,6 +724,7 @@ flux_status flux_timing_enable(int32_t on);
 int32_t flux_timing_classes(void);
 const char* flux_timing_class_name(int32_t cls);
 flux_status flux_timing_read(double* ms, int64_t* launches, double* work, int32_t n);
+
 
 /* Static text for a status code; thread-local detail of the last failure on
  * this thread ("" when none). */

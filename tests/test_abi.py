@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(F.LIB_PATH), reason="libflux.
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:flux_status|size_t|int32_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:flux_status|size_t|int32_t|int64_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_symbol():
