@@ -224,6 +224,108 @@ def summarize_counters(directory, out_dir):
     return 0
 
 
+HBM_CLASSES = ("ln_modulate", "gemv", "rf_noise_loss", "qk_prep")
+
+
+def hbm_checks(FX, step, steps):
+    """HBM-class kernels measured two ways, and the streaming ceiling.
+
+    warm: the hooked eager steps as the step runs them (inputs may sit in L2
+    or the 256 MB Infinity Cache, e.g. the residual a GEMM epilogue has just
+    written); cold: the same steps with 512 MB overwritten before every timed
+    launch (flux_timing_flush), so each kernel reads from HBM.  copy: the
+    library's streaming copy of 1 GiB (read + write), the practical ceiling."""
+    import torch
+    out = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for mode in ("warm", "cold"):
+        FX.flux_timing_read()
+        FX.flux_timing_flush(flush if mode == "cold" else None, flush.numel())
+        FX.flux_timing_enable(True)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        FX.flux_timing_enable(False)
+        FX.flux_timing_flush(None)
+        k = FX.flux_timing_read()
+        out[mode] = {c: {"us_per_launch": round(1e3 * ms / n, 2), "gbs": round(w / (ms * 1e-3) / 1e9, 1)}
+                     for c, (ms, n, w) in k.items() if n and c in HBM_CLASSES}
+    del flush
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        FX.flux_stream_copy(src, dst, n)
+    FX.flux_timing_read()
+    FX.flux_timing_enable(True)
+    for _ in range(10):
+        FX.flux_stream_copy(src, dst, n)
+    torch.cuda.synchronize()
+    FX.flux_timing_enable(False)
+    ms, cnt, w = FX.flux_timing_read()["hbm_copy"]
+    out["copy_1gib_gbs"] = round(w / (ms * 1e-3) / 1e9, 1)
+    out["note"] = ("gbs = algorithmic bytes / launch time; cold = 512 MB overwritten before each timed launch; "
+                   "copy = flux_stream_copy of 1 GiB, read + write counted")
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def hbm_sweep() -> int:
+    """rf noising + loss (rf_noise_loss) and the streaming copy from 2^20 to
+    2^28 elements (fp32), cold: each size's buffers are touched once, then a
+    512 MB flush runs before each timed launch.  One JSON line per size."""
+    import torch
+    from flow_matching_diffusion_amd import flux as FX
+    torch.cuda.set_device(0)
+    FX.lib()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for lg in range(20, 29, 2):
+        n = 1 << lg
+        z0 = torch.randn(n, device="cuda")
+        z1 = torch.randn(n, device="cuda")
+        t = torch.full((1,), 0.3, device="cuda")
+        zt, vt, vp = torch.empty_like(z0), torch.empty_like(z0), torch.randn(n, device="cuda")
+        loss = torch.empty(1, device="cuda")
+        wsb = FX.lib().flux_rf_workspace_bytes(1, n)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+        rec = {"elements": n}
+        for mode in ("warm", "cold"):
+            FX.rf_noise_loss(1, n, z0, z1, t, z_t=zt, v_target=vt)
+            FX.rf_noise_loss(1, n, z0, z1, t, v_pred=vp, loss=loss, workspace=ws, workspace_bytes=wsb)
+            torch.cuda.synchronize()
+            FX.flux_timing_read()
+            FX.flux_timing_flush(flush if mode == "cold" else None, flush.numel())
+            FX.flux_timing_enable(True)
+            for _ in range(5):
+                FX.rf_noise_loss(1, n, z0, z1, t, z_t=zt, v_target=vt)          # 16 B per element
+            torch.cuda.synchronize()
+            FX.flux_timing_enable(False)
+            ms, cnt, w = FX.flux_timing_read()["rf_noise_loss"]
+            rec[mode + "_noise_gbs"] = round(w / (ms * 1e-3) / 1e9, 1)
+            rec[mode + "_noise_us"] = round(1e3 * ms / cnt, 2)
+            FX.flux_timing_enable(True)
+            for _ in range(5):
+                FX.rf_noise_loss(1, n, z0, z1, t, v_pred=vp, loss=loss, workspace=ws, workspace_bytes=wsb)
+            torch.cuda.synchronize()
+            FX.flux_timing_enable(False)
+            ms, cnt, w = FX.flux_timing_read()["rf_noise_loss"]
+            rec[mode + "_loss_gbs"] = round(w / (ms * 1e-3) / 1e9, 1)
+            rec[mode + "_loss_us"] = round(1e3 * ms / cnt, 2)
+            FX.flux_timing_enable(True)
+            for _ in range(5):
+                FX.flux_stream_copy(z0, zt, 4 * n)
+            torch.cuda.synchronize()
+            FX.flux_timing_enable(False)
+            FX.flux_timing_flush(None)
+            ms, cnt, w = FX.flux_timing_read()["hbm_copy"]
+            rec[mode + "_copy_gbs"] = round(w / (ms * 1e-3) / 1e9, 1)
+        print(json.dumps(rec), flush=True)
+        del z0, z1, zt, vt, vp, ws
+        torch.cuda.empty_cache()
+    return 0
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -545,6 +647,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a device copy of this many MiB, 5 times (the known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--hbm-sweep", action="store_true",
+                    help="only run the HBM sweep: rf noising / loss and the streaming copy from 2^20 to 2^28 "
+                         "fp32 elements, warm and with the caches flushed before each timed launch")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
                     help="no GPU: write profiles/traffic.json and the profile summaries from the rocprofv3 "
                          "CSV folders under DIR (see PROFILE_COMMANDS)")
@@ -562,6 +667,8 @@ def main() -> int:
     import numpy as np
     import torch
 
+    if args.hbm_sweep:
+        return hbm_sweep()
     if args.workload == "flux12b_mxfp8_linears":
         return mx_linears_bench(args)
     if args.workload == "flux12b_mxfp4_linears":
@@ -662,6 +769,7 @@ def main() -> int:
     FX.flux_timing_enable(False)
     kernels = FX.flux_timing_read()
     ms_step_eager = ev0.elapsed_time(ev1) / args.steps
+    hbm = hbm_checks(FX, step, args.steps) if not sample else None
     ms_step = ms_step_eager
     graph_ok = None
     # the step time: the same step captured once in a HIP graph and replayed
@@ -774,6 +882,7 @@ def main() -> int:
         "step_tflops": round(work["total_flops"] / (ms_step * 1e-3) / 1e12, 2),
         "kernels": {k: {kk: (round(vv, 5) if vv < 1e6 else vv) for kk, vv in v.items()} for k, v in kt.items()},
         "ms_per_step_eager_with_hook": round(ms_step_eager, 4),
+        "hbm": hbm,
         "graph": None if graph_ok is None else ("replays bit-identical to eager" if graph_ok else "replayed"),
         "wall_s": round(wall, 3),
         "loss": loss,

@@ -23,11 +23,15 @@ enum KernelClass : int {
   kKcBwdElem,         // backward row-wise, element-wise, transpose and reduction kernels
   kKcGemmPkMx4,       // gemm_fp8_kernel on MXFP4 operands
   kKcMx4Quant,        // MXFP4 quantization
+  kKcCopy,            // flux_stream_copy (the HBM streaming reference)
   kKcCount
 };
 
 // Records a start event on `s` at construction and a stop event at
-// destruction when timing is enabled; does nothing otherwise.  `work` is the
+// destruction when timing is enabled; does nothing otherwise.  With a flush
+// buffer set (flux_timing_flush), the construction first enqueues a kernel
+// that overwrites that buffer, so the timed launch starts with its data
+// evicted from L2 and the Infinity Cache.  `work` is the
 // launch's algorithmic work: FLOPs for the GEMM and attention classes, bytes
 // that must cross HBM for the others.
 class TimingScope {

@@ -47,7 +47,7 @@ EXPORTED = (
     "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
     "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd", "flux_mxfp4_scale_bytes", "flux_mxfp4_quantize",
     "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize", "flux_timestep_embed", "rf_noise_loss_noalloc",
-    "flux_rf_noalloc_max_partials",
+    "flux_rf_noalloc_max_partials", "flux_timing_flush", "flux_stream_copy",
 )
 
 
@@ -141,6 +141,8 @@ def lib() -> C.CDLL:
         "flux_single_seq_fwd": [P(flux_dims), P(flux_stream_weights), vp, i64, vp, vp, vp, sz, vp],
         "rf_noise_loss": [P(rf_args), vp],
         "rf_noise_loss_noalloc": [P(rf_args), vp],
+        "flux_timing_flush": [vp, i64],
+        "flux_stream_copy": [vp, vp, i64, vp],
         "flux_rope_table": [vp, i32, i32, P(C.c_int32), f32, vp, vp],
         "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
                            vp, vp, i64, vp, i64, vp, vp, sz, vp],
@@ -512,6 +514,16 @@ def flux_attention_fwd(precision, batch, seq, heads, head_dim, q, k, v, ld_in, o
 
 def flux_timing_enable(on: bool) -> None:
     _check(lib().flux_timing_enable(1 if on else 0), "flux_timing_enable")
+
+
+def flux_timing_flush(buffer=None, nbytes: int = 0) -> None:
+    """Overwrite `buffer` (device, nbytes) before every timed launch, so timed
+    kernels start with cold caches; None turns it off."""
+    _check(lib().flux_timing_flush(ptr(buffer), nbytes if buffer is not None else 0), "flux_timing_flush")
+
+
+def flux_stream_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check(lib().flux_stream_copy(ptr(src), ptr(dst), nbytes, _stream(stream)), "flux_stream_copy")
 
 
 def flux_timing_read() -> Dict[str, tuple]:

@@ -725,6 +725,25 @@ int32_t flux_timing_classes(void);
 const char* flux_timing_class_name(int32_t cls);
 flux_status flux_timing_read(double* ms, int64_t* launches, double* work, int32_t n);
 
+/*
+ * Measurement helpers (diagnostics).
+ *
+ * flux_timing_flush -- while timing is enabled and `buffer` is not NULL,
+ *   every timed launch is preceded, on its stream and outside its events, by
+ *   a kernel that overwrites `bytes` of `buffer` (device memory the caller
+ *   owns; 16-byte aligned, bytes >= 16; 512 MB evicts the 4 MB L2 of every
+ *   XCD and the 256 MB Infinity Cache), so the timed kernel reads its inputs
+ *   from HBM.  NULL turns the flush off.  The library keeps the pointer, not
+ *   a copy: it must stay valid while set.
+ *
+ * flux_stream_copy -- dst[0, bytes) = src[0, bytes), device pointers,
+ *   16-byte aligned, not overlapping: a streaming copy (16 bytes per lane,
+ *   four loads in flight per lane) whose bandwidth is the practical HBM
+ *   ceiling the row-wise kernels are compared with.  Timed as the class
+ *   "hbm_copy" with 2 * bytes of traffic.
+ */
+flux_status flux_timing_flush(void* buffer, int64_t bytes);
+flux_status flux_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Static text for a status code; thread-local detail of the last failure on
  * this thread ("" when none). */
