@@ -359,6 +359,114 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a, int64_t rows_per_
   __shared__ uint32_t red[2][4];                  // per-wave amax of each segment (E4M3 output)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t total = a.s[0].rows + (a.count > 1 ? (int64_t)a.s[1].rows : 0);
+  const int64_t b0 = (int64_t)blockIdx.x * 4;     // one row per wave
+  if (b0 >= total) return;   // block-uniform
+  const int D = a.dim;
+  // global rows run over segment 0 then segment 1 (g < total)
+  auto locate = [&](int64_t g, int& si, int64_t& r) {
+    si = g >= a.s[0].rows ? 1 : 0;
+    r = si ? g - a.s[0].rows : g;
+  };
+  // 1. the wave's row, all NV loads in flight before anything else
+  const int64_t g = b0 + wave;
+  const bool has_row = g < total;   // wave-uniform
+  int si = 0;
+  int64_t r = 0;
+  float4 v[NV];
+  if (has_row) {
+    locate(g, si, r);
+    const LnSeg& sg = a.s[si];
+    const int64_t bb = r / sg.xmap.seg, ll = r % sg.xmap.seg;
+    const float* x = sg.x + bb * sg.xmap.bstride + ll * sg.xmap.ld;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = reinterpret_cast<const float4*>(x)[lane + 64 * i];
+  }
+  // 2. (1 + scale) and shift of the block's first row's sample, staged while
+  // the rows are in flight
+  int bsi;
+  int64_t brow;
+  locate(b0, bsi, brow);
+  const int64_t bsam = brow / a.s[bsi].xmap.seg;
+  {
+    const float* scp = a.s[bsi].scale + bsam * a.s[bsi].mod_bstride;
+    const float* shp = a.s[bsi].shift + bsam * a.s[bsi].mod_bstride;
+    for (int i = threadIdx.x; i < NV * 64; i += 256) {
+      const float4 t = reinterpret_cast<const float4*>(scp)[i];
+      msc[i] = make_float4(1.f + t.x, 1.f + t.y, 1.f + t.z, 1.f + t.w);
+      msh[i] = reinterpret_cast<const float4*>(shp)[i];
+    }
+  }
+  __syncthreads();
+  uint32_t mx = 0;
+  if (has_row) {
+    const LnSeg& sg = a.s[si];
+    const int64_t bb = r / sg.xmap.seg, ll = r % sg.xmap.seg;
+    const bool staged = si == bsi && bb == bsam;   // wave-uniform
+    const float4* gsc = reinterpret_cast<const float4*>(sg.scale + bb * sg.mod_bstride);
+    const float4* gsh = reinterpret_cast<const float4*>(sg.shift + bb * sg.mod_bstride);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const float mean = wave_sum(sum) / (float)D;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float dx = v[i].x - mean, dy = v[i].y - mean, dz = v[i].z - mean, dw = v[i].w - mean;
+      sq += (dx * dx + dy * dy) + (dz * dz + dw * dw);
+    }
+    const float var = wave_sum(sq) / (float)D;
+    const float rstd = 1.0f / sqrtf(var + a.eps);
+    T* out = reinterpret_cast<T*>(sg.out) + bb * sg.omap.bstride + ll * sg.omap.ld;
+    float qs = 1.0f;   // E4M3 output: the record's delayed scale
+    if constexpr (sizeof(T) == 1) qs = fp8_scale(sg.q);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = (lane + 64 * i) * 4;
+      float4 s1, h4;
+      if (staged) {
+        s1 = msc[lane + 64 * i];
+        h4 = msh[lane + 64 * i];
+      } else {
+        const float4 t = gsc[lane + 64 * i];
+        s1 = make_float4(1.f + t.x, 1.f + t.y, 1.f + t.z, 1.f + t.w);
+        h4 = gsh[lane + 64 * i];
+      }
+      const float y0 = (v[i].x - mean) * rstd * s1.x + h4.x;
+      const float y1 = (v[i].y - mean) * rstd * s1.y + h4.y;
+      const float y2 = (v[i].z - mean) * rstd * s1.z + h4.z;
+      const float y3 = (v[i].w - mean) * rstd * s1.w + h4.w;
+      if constexpr (sizeof(T) == 1) {
+        // E4M3 output with the record's delayed scale; amax of the unscaled values
+        mx = max(mx, max(max(abs_bits(y0), abs_bits(y1)), max(abs_bits(y2), abs_bits(y3))));
+        *reinterpret_cast<uint32_t*>(out + c) = f32x4_to_e4m3(y0 * qs, y1 * qs, y2 * qs, y3 * qs);
+      } else {
+        store4<T>(out + c, y0, y1, y2, y3);
+      }
+    }
+  }
+  if constexpr (sizeof(T) == 1) {
+    const uint32_t m = wave_max_u32(mx);
+    if (lane == 0) {
+      red[0][wave] = has_row && si == 0 ? m : 0u;
+      red[1][wave] = has_row && si == 1 ? m : 0u;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2 && threadIdx.x < a.count) {
+      const uint32_t mm = max(max(red[threadIdx.x][0], red[threadIdx.x][1]), max(red[threadIdx.x][2], red[threadIdx.x][3]));
+      if (mm) fp8_amax_raise(a.s[threadIdx.x].q, __uint_as_float(mm));
+    }
+  }
+}
+
+// E4M3 output: the kernel above keeps one amax atomic per block of 4 rows;
+// this one walks a contiguous row range per block (at most kLnBlocks blocks),
+// so the amax atomics stay few.
+template <typename T, int NV>
+__global__ void __launch_bounds__(256) ln_mod_rows_kernel(LnArgs a, int64_t rows_per_block) {
+  __shared__ float4 msc[NV * 64], msh[NV * 64];   // (1 + scale), shift of the block's first sample
+  __shared__ uint32_t red[2][4];                  // per-wave amax of each segment (E4M3 output)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t total = a.s[0].rows + (a.count > 1 ? (int64_t)a.s[1].rows : 0);
   const int64_t b0 = (int64_t)blockIdx.x * rows_per_block;
   const int64_t b1 = b0 + rows_per_block < total ? b0 + rows_per_block : total;
   if (b0 >= total) return;   // block-uniform
@@ -479,8 +587,13 @@ __global__ void __launch_bounds__(256) ln_mod_kernel(LnArgs a, int64_t rows_per_
 template <typename T>
 static void launch_ln_mod_t(const LnArgs& a, dim3 grid, int64_t rpb, hipStream_t stream) {
   // D is a multiple of 256, at most 4096 (checked by the API): NV float4 per lane
-#define FLUX_LN_CASE(nv) \
-  case nv: hipLaunchKernelGGL((ln_mod_kernel<T, nv>), grid, dim3(256), 0, stream, a, rpb); break;
+#define FLUX_LN_CASE(nv)                                                                             \
+  case nv:                                                                                           \
+    if constexpr (sizeof(T) == 1)                                                                    \
+      hipLaunchKernelGGL((ln_mod_rows_kernel<T, nv>), grid, dim3(256), 0, stream, a, rpb);           \
+    else                                                                                             \
+      hipLaunchKernelGGL((ln_mod_kernel<T, nv>), grid, dim3(256), 0, stream, a, rpb);                \
+    break;
   switch (a.dim / 256) {
     FLUX_LN_CASE(1) FLUX_LN_CASE(2) FLUX_LN_CASE(3) FLUX_LN_CASE(4) FLUX_LN_CASE(5) FLUX_LN_CASE(6)
     FLUX_LN_CASE(7) FLUX_LN_CASE(8) FLUX_LN_CASE(9) FLUX_LN_CASE(10) FLUX_LN_CASE(11) FLUX_LN_CASE(12)
@@ -493,8 +606,10 @@ hipError_t launch_ln_mod(const LnArgs& a, int dtype, hipStream_t stream) {  // d
   if (a.dim % 256 != 0 || a.dim < 256 || a.dim > 256 * kLnMaxVec) return hipErrorInvalidValue;
   const int64_t rows = a.s[0].rows + (a.count > 1 ? a.s[1].rows : 0);
   if (rows <= 0) return hipSuccess;
+  // 16/32-bit output: one row per wave, every row's loads in flight at once;
+  // E4M3 output: contiguous row ranges, at most kLnBlocks blocks
   int64_t blocks = ceil_div(rows, 4);
-  if (blocks > kLnBlocks) blocks = kLnBlocks;
+  if (dtype == kFP8 && blocks > kLnBlocks) blocks = kLnBlocks;
   const int64_t rpb = ceil_div(rows, blocks);
   const dim3 grid((unsigned)ceil_div(rows, rpb));
   TimingScope ts(kKcLnMod, stream, (double)rows * a.dim * (4.0 + (dtype == kF32 ? 4.0 : dtype == kFP8 ? 1.0 : 2.0)));
