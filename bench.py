@@ -110,8 +110,14 @@ PROFILE_COMMANDS = [
     "python -u bench.py --copy-calibration-mib 1024",
     "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_write -o copy -- "
     "python -u bench.py --copy-calibration-mib 1024",
+    "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv -d gpurun_out/pmc_mfma -o bench -- "
+    "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+    "-f csv -d gpurun_out/pmc_lds -o bench -- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline",
     "python bench.py --summarize-counters gpurun_out --profiles-out gpurun_out/profiles",
 ]
+SIMDS = 256 * 4   # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 
 
 def _csv(directory, suffix):
@@ -146,7 +152,7 @@ def summarize_counters(directory, out_dir):
     factors = {}
     for counter, sub in (("FETCH_SIZE", "pmc_copy_fetch"), ("WRITE_SIZE", "pmc_copy_write")):
         per = _counter_per_dispatch(_csv(os.path.join(directory, sub), "counter_collection.csv"), counter)
-        vals = [v for k, vs in per.items() if "copyBuffer" in k for v in vs]
+        vals = [v for k, vs in per.items() if "stream_copy_kernel" in k for v in vs]
         factors[counter] = copy_bytes / (1024.0 * sum(vals) / len(vals))
     fetch = _counter_per_dispatch(_csv(os.path.join(directory, "pmc_fetch"), "counter_collection.csv"), "FETCH_SIZE")
     write = _counter_per_dispatch(_csv(os.path.join(directory, "pmc_write"), "counter_collection.csv"), "WRITE_SIZE")
@@ -220,8 +226,65 @@ def summarize_counters(directory, out_dir):
                      "| class | hook us | rocprofv3 us |\n|---|---|---|\n" + "\n".join(agree) + "\n")
             fh.write("\nbench.py line of this run:\n\n    " + json.dumps({k: hook[k] for k in (
                 "value", "unit", "ms_per_step", "roofline", "attention_tflops", "gemm_tflops")}) + "\n")
+    summarize_mfma_lds(directory, out_dir)
     print(json.dumps(out, indent=1))
     return 0
+
+
+def summarize_mfma_lds(directory, out_dir):
+    """MFMA utilisation and LDS bank conflicts per kernel from the two extra
+    --pmc passes of PROFILE_COMMANDS: busy = sum over SIMDs of
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); the
+    engine clock of a dispatch = (GRBM_GUI_ACTIVE / 8) / its duration; counted
+    MFMA FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_{F16,BF16}; conflict rate =
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    import re
+    try:
+        mf = _csv(os.path.join(directory, "pmc_mfma"), "counter_collection.csv")
+        ld = _csv(os.path.join(directory, "pmc_lds"), "counter_collection.csv")
+    except SystemExit:
+        return
+    def per(rows, counter):
+        return _counter_per_dispatch(rows, counter)
+    dur = {}   # kernel -> [dispatch duration ns] in the MFMA pass
+    for r in mf:
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    busy, gui, sqb = (per(mf, c) for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES"))
+    conf, act, m16, mb16 = (per(ld, c) for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                                                  "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+    # _counter_per_dispatch scales nothing: raw counter values (KiB only for FETCH/WRITE_SIZE)
+    lines = []
+    for name in sorted(set(busy) | set(conf)):
+        short = re.sub(r"\(.*$", "", name.replace("void ", ""))[:60]
+        b, g = busy.get(name, []), gui.get(name, [])
+        util = (sum(b) / (sum(g) / XCDS * SIMDS)) if b and g and sum(g) > 0 else None
+        d = dur.get(name, [])
+        # GHz; only for dispatches long enough (>= 50 us) that counting overhead does not matter
+        clock = (sum(g) / XCDS / sum(d)) if g and d and min(d) >= 50000 else None
+        c, a = conf.get(name, []), act.get(name, [])
+        crate = (sum(c) / sum(a)) if c and a and sum(a) > 0 else None
+        mops = sum(m16.get(name, [])) + sum(mb16.get(name, []))
+        n = max(len(b), len(c), 1)
+        nd = max(len(m16.get(name, [])), len(mb16.get(name, [])), 1)
+        flops = 512.0 * mops / nd
+        if util is None and crate is None:
+            continue
+        if (util or 0) < 1e-4 and (crate or 0) < 1e-4 and flops == 0:
+            continue
+        lines.append(f"| {short} | {n} | {'' if util is None else f'{100 * util:.1f}'} | "
+                     f"{'' if clock is None else f'{clock:.2f}'} | "
+                     f"{'' if crate is None else f'{100 * crate:.2f}'} | {flops / 1e9:.1f} |")
+    cmds = "\n".join("    " + c for c in PROFILE_COMMANDS if "pmc SQ_" in c)
+    with open(os.path.join(out_dir, f"mfma_lds_counters_{PROFILE_WORKLOAD}.md"), "w") as fh:
+        fh.write(f"# MFMA utilisation and LDS bank conflicts per kernel, {PROFILE_WORKLOAD}\n\nMade by:\n\n{cmds}\n\n"
+                 "MFMA busy = sum of SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 "
+                 "SIMDs), the fraction of engine cycles the matrix units were busy; engine clock = "
+                 "(GRBM_GUI_ACTIVE / 8) / dispatch duration (in the counters' own run); "
+                 "LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; counted GFLOP per dispatch = "
+                 "512 x (SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16) / 1e9.\n\n"
+                 "| kernel | dispatches | MFMA busy % | engine clock GHz | LDS bank-conflict % | "
+                 "counted GFLOP / dispatch |\n|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n")
 
 
 HBM_CLASSES = ("ln_modulate", "gemv", "rf_noise_loss", "qk_prep")
@@ -678,11 +741,12 @@ def main() -> int:
     if args.workload == "flux12b_attention_fp8":
         return attention_fp8_bench(args)
     if args.copy_calibration_mib:
+        from flow_matching_diffusion_amd import flux as FX
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            FX.flux_stream_copy(src, dst, n)   # stream_copy_kernel: n bytes read, n written
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
         return 0
