@@ -325,6 +325,33 @@ def model_inputs(wl: Workload) -> Dict[str, np.ndarray]:
     return d
 
 
+def iter_block_weights(wl: Workload, workers: int = 8, window: int = 8):
+    """Yield ("double", i, weights) for i < n_double, then ("single", i,
+    weights) for i < n_single, in order, with block ids i (double) and
+    n_double + i (single), the same host streams as double_block_weights /
+    single_block_weights.  Up to `window` blocks are drawn ahead on `workers`
+    threads (numpy's generators release the GIL while they fill arrays), so a
+    caller can upload one block while the next ones are drawn; memory stays
+    bounded by the window."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [("double", i) for i in range(wl.n_double)] + [("single", i) for i in range(wl.n_single)]
+
+    def draw(job):
+        kind, i = job
+        if kind == "double":
+            return double_block_weights(wl, i)
+        return single_block_weights(wl, wl.n_double + i)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        pending = [ex.submit(draw, j) for j in jobs[:window]]
+        for n, job in enumerate(jobs):
+            w = pending[n].result()
+            pending[n] = None
+            if n + window < len(jobs):
+                pending.append(ex.submit(draw, jobs[n + window]))
+            yield job[0], job[1], w
+
+
 # --------------------------------------------------------------------------- #
 # device-drawn block weights for the full 12B-shaped stack
 # --------------------------------------------------------------------------- #
