@@ -170,15 +170,53 @@ __global__ void __launch_bounds__(kRfLossThreads) rf_loss_partial_kernel(int64_t
                                                                          const float* __restrict__ vp,
                                                                          double* __restrict__ partials) {
   const int b = blockIdx.y, g = blockIdx.x, parts = gridDim.x;
-  const int64_t per = ceil_div(n, parts);
+  const int64_t per = round_up(ceil_div(n, parts), 4);   // a multiple of 4: whole float4 words per part
   const int64_t lo = (int64_t)g * per;
   const int64_t hi = lo + per < n ? lo + per : n;
   const int64_t base = (int64_t)b * n;
   double acc = 0.0;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += kRfLossThreads) {
-    const float v = __fsub_rn(z1[base + i], z0[base + i]);
-    const float d = __fsub_rn(vp[base + i], v);
+  auto sq = [&](float z0v, float z1v, float pv) {
+    const float d = __fsub_rn(pv, __fsub_rn(z1v, z0v));
     acc += (double)d * (double)d;
+  };
+  // 16-byte path: the part's float4 words, four strides of the block at a
+  // time so 12 loads per thread are in flight; each thread adds its values in
+  // one fixed order, so the sum has the same bits on every run
+  const bool vec4 = (n & 3) == 0 && (per & 3) == 0 &&
+                    ((reinterpret_cast<uintptr_t>(z0) | reinterpret_cast<uintptr_t>(z1) |
+                      reinterpret_cast<uintptr_t>(vp)) & 15) == 0;
+  if (vec4) {
+    const float4* a4 = reinterpret_cast<const float4*>(z0 + base);
+    const float4* c4 = reinterpret_cast<const float4*>(z1 + base);
+    const float4* p4 = reinterpret_cast<const float4*>(vp + base);
+    const int64_t lo4 = lo >> 2, hi4 = hi >> 2;
+    constexpr int S = kRfLossThreads;
+    int64_t i = lo4 + threadIdx.x;
+    for (; i + 3 * S < hi4; i += 4 * S) {
+      float4 a[4], c[4], q[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a[j] = a4[i + j * S];
+        c[j] = c4[i + j * S];
+        q[j] = p4[i + j * S];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sq(a[j].x, c[j].x, q[j].x);
+        sq(a[j].y, c[j].y, q[j].y);
+        sq(a[j].z, c[j].z, q[j].z);
+        sq(a[j].w, c[j].w, q[j].w);
+      }
+    }
+    for (; i < hi4; i += S) {
+      const float4 a = a4[i], c = c4[i], q = p4[i];
+      sq(a.x, c.x, q.x);
+      sq(a.y, c.y, q.y);
+      sq(a.z, c.z, q.z);
+      sq(a.w, c.w, q.w);
+    }
+  } else {
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kRfLossThreads) sq(z0[base + i], z1[base + i], vp[base + i]);
   }
   acc = wave_sum_f64(acc);
   __shared__ double red[kRfLossThreads / kWave];
