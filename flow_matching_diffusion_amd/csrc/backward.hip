@@ -38,10 +38,14 @@ __device__ __forceinline__ float silu_grad_f(float x) {
 }
 
 // ===========================================================================
-// Batched transpose to bf16: dst[z][c][r] = src[z][r][c] (r < R, c < C);
+// Batched transpose to bf16: dst[z][c][r] = src[z][r][c] (r < R, c < C) from
+// fp32, bf16 or fp16 sources;
 // columns r in [R, R_fill) of dst are zero (padding of a GEMM's K).
 // 64 x 64 tiles through LDS; 4 consecutive elements per thread on both sides.
 // ===========================================================================
+template <typename TS> constexpr bool kBf16Src = false;
+template <> constexpr bool kBf16Src<bf16_t> = true;
+
 template <typename TS>
 __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
   __shared__ float tile[64][65];
@@ -57,9 +61,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
         const float4 f = *reinterpret_cast<const float4*>(src + row_off(a.smap, r) + c);
         v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
       } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(src + row_off(a.smap, r) + c);
-        v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-        v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+        unpack4_16(*reinterpret_cast<const uint2*>(src + row_off(a.smap, r) + c), sizeof(TS) == 2 && !kBf16Src<TS>, v);
       }
     }
 #pragma unroll
@@ -85,6 +87,8 @@ hipError_t launch_transpose(const TransposeArgs& a, int src_dtype, hipStream_t s
                                                     (double)a.R_fill * a.C * 2));
   if (src_dtype == kF32)
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, stream, a);
+  else if (src_dtype == kF16)
+    hipLaunchKernelGGL(transpose_kernel<_Float16>, grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -193,8 +197,9 @@ hipError_t launch_colsum(ColsumArgs a, int a_dtype, float* out, int64_t out_zstr
 // Elementwise steps, 4 columns per thread, rows through RowMaps
 // ===========================================================================
 // kEwGateBwd:  out (bf16) = gate[b][c] * x (float)        dy of x += gate * y
-// kEwGeluBwd:  out (bf16) = x (bf16) * GELU'(y (bf16))    d(pre-activation) of u = GELU(a)
-// kEwGelu:     out (bf16) = GELU(x (bf16))
+// kEwGeluBwd:  out (16-bit) = x (16-bit) * GELU'(y (16-bit))   d(pre-activation) of u = GELU(a)
+// kEwGelu:     out (16-bit) = GELU(x (16-bit))
+// (16-bit: bf16, or fp16 where the f16 mask bit of that operand is set)
 // kEwGateAdd:  out (float) += gate[b][c] * x (float)      the forward's gated residual
 __global__ void __launch_bounds__(256) elementwise_kernel(EwArgs a) {
   const int64_t n4 = (int64_t)a.rows * (a.C / 4);
@@ -208,14 +213,11 @@ __global__ void __launch_bounds__(256) elementwise_kernel(EwArgs a) {
       const float4 g = *reinterpret_cast<const float4*>(a.gate + (r / a.xmap.seg) * a.gate_bstride + c);
       y[0] = g.x; y[1] = g.y; y[2] = g.z; y[3] = g.w;
     } else {
-      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(a.x) + row_off(a.xmap, r) + c);
-      x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
-      x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
-      if (a.op == kEwGeluBwd) {
-        const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(a.y) + row_off(a.ymap, r) + c);
-        y[0] = __uint_as_float(w.x << 16); y[1] = __uint_as_float(w.x & 0xffff0000u);
-        y[2] = __uint_as_float(w.y << 16); y[3] = __uint_as_float(w.y & 0xffff0000u);
-      }
+      unpack4_16(*reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(a.x) + row_off(a.xmap, r) + c),
+                 a.f16 & 1, x);
+      if (a.op == kEwGeluBwd)
+        unpack4_16(*reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(a.y) + row_off(a.ymap, r) + c),
+                   a.f16 & 2, y);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -229,10 +231,7 @@ __global__ void __launch_bounds__(256) elementwise_kernel(EwArgs a) {
       v.x += o[0]; v.y += o[1]; v.z += o[2]; v.w += o[3];
       *p = v;
     } else {
-      uint2 w;
-      w.x = pack_bf16x2(o[0], o[1]);
-      w.y = pack_bf16x2(o[2], o[3]);
-      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + row_off(a.omap, r) + c) = w;
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + row_off(a.omap, r) + c) = pack4_16(o, a.f16 & 4);
     }
   }
 }
@@ -484,7 +483,7 @@ int prep_bwd_parts(int batch, int seq, int heads) { return (int)ceil_div(seq, 64
 
 // ===========================================================================
 // Attention backward, step 0: from the output gradient dO and the output O
-// (bf16 token rows, head h at column h * 128): dOh [B, H, Lp, 128], its
+// (token rows, head h at column h * 128; dO bf16, O bf16 or fp16): dOh [B, H, Lp, 128], its
 // transpose dOt [B, H, 128, Lp] (zero beyond seq) and Dv[q] = dO[q] . O[q]
 // per head (0 beyond seq).  One block per (64 tokens, head, sample).
 // ===========================================================================
@@ -503,12 +502,11 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(AttnBwdArgs a) {
                                              (int64_t)j * a.dout_ld + h * DH + d0);
       const uint4 ov = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.o) + (int64_t)b * a.o_bstride +
                                                         (int64_t)j * a.o_ld + h * DH + d0);
-      const uint32_t* pd = reinterpret_cast<const uint32_t*>(&dov);
-      const uint32_t* po = reinterpret_cast<const uint32_t*>(&ov);
+      float fd[8], fo[8];
+      unpack4_16(make_uint2(dov.x, dov.y), false, fd); unpack4_16(make_uint2(dov.z, dov.w), false, fd + 4);
+      unpack4_16(make_uint2(ov.x, ov.y), a.o_f16, fo); unpack4_16(make_uint2(ov.z, ov.w), a.o_f16, fo + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dot += __uint_as_float(pd[e] << 16) * __uint_as_float(po[e] << 16) +
-               __uint_as_float(pd[e] & 0xffff0000u) * __uint_as_float(po[e] & 0xffff0000u);
+      for (int e = 0; e < 4; ++e) dot += fd[2 * e] * fo[2 * e] + fd[2 * e + 1] * fo[2 * e + 1];
     }
     dot = wave_sum<16>(dot);
     *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(a.doh) + (bh * a.seq_pad + j) * DH + d0) = dov;

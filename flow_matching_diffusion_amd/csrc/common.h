@@ -47,6 +47,29 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_f16_sat(hi)) << 16);
 }
 
+// Four 16-bit values (an 8-byte word, low half first) to fp32 and back:
+// fp16 when f16, else bf16; the stores round to nearest even (fp16 saturating).
+__device__ __forceinline__ void unpack4_16(uint2 u, bool f16, float* v) {
+  const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (f16) {
+      v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+      v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    } else {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ uint2 pack4_16(const float* v, bool f16) {
+  uint2 u;
+  u.x = f16 ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+  u.y = f16 ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
+  return u;
+}
+
 // Eight bf16 (a 16-byte word) to eight fp16, rounding toward zero.  Exact for
 // magnitudes in fp16's normal range [2^-14, 65504]; smaller magnitudes lose
 // at most 2^-24 (the few bits fp16 subnormals cannot hold); finite magnitudes

@@ -174,7 +174,8 @@ hipError_t launch_attention(const AttnArgs& a, int in_dtype, int out_dtype, hipS
 
 // ------------------------------- backward --------------------------------
 // dst[z][c][r] = bf16(src[z][r][c]) for r < R, c < C; zero for R <= r < R_fill.
-// C, R_fill, the source row stride and dst_ld multiples of 4.
+// src_dtype kF32, kBF16 or kF16.  C, R_fill, the source row stride and dst_ld
+// multiples of 4.
 struct TransposeArgs {
   const void* src; int64_t src_zstride; RowMap smap;     // row r of slice z at src + z * src_zstride + smap(r)
   void* dst; int64_t dst_zstride; int64_t dst_ld;
@@ -212,6 +213,7 @@ struct EwArgs {
   void* out; RowMap omap;
   const float* gate; int64_t gate_bstride;   // gate[(r / xmap.seg) * gate_bstride + c]
   int64_t rows; int32_t C;                   // C % 4 == 0
+  int32_t f16;                               // 16-bit operands that are fp16 (else bf16): 1 x, 2 y, 4 out
 };
 hipError_t launch_elementwise(const EwArgs& a, hipStream_t stream);
 
@@ -250,7 +252,8 @@ hipError_t launch_prep_bwd(const PrepBwdArgs& a, hipStream_t stream);
 
 // Attention backward (bf16, head_dim 128).  Inputs head-major bf16: qh, kh, vh
 // [B, H, seq_pad, 128], qt, kt [B, H, 128, seq_pad]; lse [B, H, seq_pad] from
-// the forward; dout / o bf16 token rows (head h at column h * 128).  Scratch:
+// the forward; dout bf16 and o bf16 or fp16 (o_f16) token rows (head h at
+// column h * 128).  Scratch:
 // doh [B, H, seq_pad, 128], dot [B, H, 128, seq_pad] bf16, dd [B, H, seq_pad]
 // fp32.  Outputs fp32 head-major dq, dk, dv [B, H, seq_pad, 128] (rows < seq).
 struct AttnBwdArgs {
@@ -262,6 +265,7 @@ struct AttnBwdArgs {
   float* dq; float* dk; float* dv;
   int32_t batch, seq, seq_pad, heads;
   float scale_log2, scale;
+  int32_t o_f16;                         // o is fp16 (else bf16)
 };
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t stream);
 

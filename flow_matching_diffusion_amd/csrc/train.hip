@@ -4,11 +4,15 @@
 // mean squared error, backpropagate; Model components: the double and single
 // blocks differentiated step by step).
 //
-// Training runs in bf16 (bf16 activations and weights on the bf16 MFMA, fp32
-// accumulation, fp32 residual stream and gradients), head_dim 128.  Data
-// gradients of a linear y = x W^T are dy W (the forward GEMM with the
-// transposed weight), weight gradients dy^T x (the forward GEMM on the
-// transposed activations, the token axis zero-padded to a multiple of 64).
+// Weights are bf16; head_dim 128.  The forward's block linears take fp16
+// activation operands (LayerNorm-modulate, attention and GELU outputs) times
+// the bf16 weights converted to fp16 per tile, on the fp16 MFMA with fp32
+// accumulation, as the inference forward does; the q|k|v projection is kept
+// in bf16 for the q / k norm, and the residual stream and every gradient are
+// fp32 or bf16.  Data gradients of a linear y = x W^T are dy W (bf16 MFMA,
+// the forward GEMM with the transposed weight), weight gradients dy^T x (the
+// same GEMM on the transposed activations, rounded to bf16, the token axis
+// zero-padded to a multiple of 64).
 #include "api_common.h"
 
 using namespace flux;
@@ -33,9 +37,10 @@ flux_status check_train_dims(const flux_dims* d) {
 struct SingleSaved {
   float* mod;      // [B, 3D]
   float* x0;       // [B, L, D] block input
-  void* h;         // [B, L, D]      bf16 LN-modulate output
-  void* lin1;      // [B, L, 3D + F] bf16 q|k|v|mlp pre-activation
-  void* cat;       // [B, L, D + F]  bf16 attention output | GELU(mlp)
+  void* h;         // [B, L, D]      fp16 LN-modulate output
+  void* qkv;       // [B, L, 3D]     bf16 q|k|v columns of linear1
+  void* a;         // [B, L, F]      fp16 MLP pre-activation columns of linear1
+  void* cat;       // [B, L, D + F]  fp16 attention output | GELU(a)
   void* qh; void* kh; void* vt;   // attention operands
   float* lse;      // [B, H, Lp]
   float* y;        // [B, L, D] linear2 output before the gate
@@ -49,7 +54,8 @@ SingleSaved single_saved(const flux_dims* d, void* base) {
   s.mod = static_cast<float*>(c.take(B * 3 * D * 4));
   s.x0 = static_cast<float*>(c.take(B * L * D * 4));
   s.h = c.take(B * L * D * 2);
-  s.lin1 = c.take(B * L * (3 * D + F) * 2);
+  s.qkv = c.take(B * L * 3 * D * 2);
+  s.a = c.take(B * L * F * 2);
   s.cat = c.take(B * L * (D + F) * 2);
   s.qh = c.take(B * d->heads * Lp * 128 * 2);
   s.kh = c.take(B * d->heads * Lp * 128 * 2);
@@ -63,7 +69,7 @@ SingleSaved single_saved(const flux_dims* d, void* base) {
 struct BlockSaved {   // joint [B, L, .] rows, image rows first
   float* mod[2];      // [B, 6D] per stream
   float* x0; float* x1;   // residual before the block and after the attention half
-  void* h1; void* qkv; void* o; void* h2; void* a1; void* u;   // bf16
+  void* h1; void* qkv; void* o; void* h2; void* a1; void* u;   // fp16 but qkv (bf16)
   float* y1; float* y2;   // projection and fc2 outputs before their gates
   void* qh; void* kh; void* vt; float* lse;
   size_t bytes;
@@ -231,10 +237,10 @@ hipError_t colsum(const void* A, int a_dt, RowMap am, const float* Bm, RowMap bm
 }
 
 hipError_t elementwise(int op, const void* x, RowMap xm, const void* y, RowMap ym, void* out, RowMap om,
-                       const float* gate, int64_t gate_bs, int64_t rows, int64_t C, hipStream_t st) {
+                       const float* gate, int64_t gate_bs, int64_t rows, int64_t C, hipStream_t st, int f16 = 0) {
   EwArgs a{};
   a.op = op; a.x = x; a.xmap = xm; a.y = y; a.ymap = ym; a.out = out; a.omap = om;
-  a.gate = gate; a.gate_bstride = gate_bs; a.rows = rows; a.C = (int32_t)C;
+  a.gate = gate; a.gate_bstride = gate_bs; a.rows = rows; a.C = (int32_t)C; a.f16 = f16;
   return launch_elementwise(a, st);
 }
 
@@ -260,10 +266,11 @@ hipError_t mod_bwd(const void* w, const float* vec, const float* dm, int64_t N, 
   return launch_mod_bwd(a, kBF16, st);
 }
 
-// attention backward from saved head-major operands; dO and O bf16 token rows
+// attention backward from saved head-major operands; dO bf16 and O (bf16, or
+// fp16 when o_f16) token rows
 hipError_t attention_bwd(int64_t B, int64_t L, int64_t H, const void* qh, const void* kh, const void* vt,
                          const float* lse, const void* dO, int64_t do_bs, int64_t do_ld, const void* o, int64_t o_bs,
-                         int64_t o_ld, const AttnWs& w, hipStream_t st) {
+                         int64_t o_ld, bool o_f16, const AttnWs& w, hipStream_t st) {
   const int64_t Lp = seq_pad_of(L);
   hipError_t e = transpose_heads(qh, w.qt, B * H, Lp, 128, st);
   if (e == hipSuccess) e = transpose_heads(kh, w.kt, B * H, Lp, 128, st);
@@ -272,7 +279,7 @@ hipError_t attention_bwd(int64_t B, int64_t L, int64_t H, const void* qh, const 
   AttnBwdArgs a{};
   a.qh = qh; a.kh = kh; a.vh = w.vh; a.qt = w.qt; a.kt = w.kt; a.lse = lse;
   a.dout = dO; a.dout_bstride = do_bs; a.dout_ld = do_ld;
-  a.o = o; a.o_bstride = o_bs; a.o_ld = o_ld;
+  a.o = o; a.o_bstride = o_bs; a.o_ld = o_ld; a.o_f16 = o_f16 ? 1 : 0;
   a.doh = w.doh; a.dot = w.dot; a.dd = w.dd;
   a.dq = w.dq; a.dk = w.dk; a.dv = w.dv;
   a.batch = (int32_t)B; a.seq = (int32_t)L; a.seq_pad = (int32_t)Lp; a.heads = (int32_t)H;
@@ -295,12 +302,24 @@ hipError_t gamma_grads(const float* part, int nblk, float* out[2][2], hipStream_
   return hipSuccess;
 }
 
-GemmProblem bf16_problem(const void* A, RowMap am, const void* W, const void* bias, int64_t M, int64_t N, int64_t K,
-                         void* out, RowMap om, bool out_f32) {
-  GemmProblem p = gemm_problem(A, am, W, bias, (int)M, (int)N, (int)K, out_f32 ? kEpiStoreF32 : kEpiStore, out, om);
-  p.out0_dt = out_f32 ? kF32 : kBF16;
+// y = A W^T (+ bias) stored as out_dt (kF32, kBF16 or kF16); A is bf16 for
+// launch_gemm(.., kBF16) and fp16 for launch_gemm(.., kF16), W bf16 for both
+GemmProblem lin_problem(const void* A, RowMap am, const void* W, const void* bias, int64_t M, int64_t N, int64_t K,
+                        void* out, RowMap om, int out_dt) {
+  GemmProblem p = gemm_problem(A, am, W, bias, (int)M, (int)N, (int)K, out_dt == kF32 ? kEpiStoreF32 : kEpiStore, out,
+                               om);
+  p.out0_dt = out_dt;
   return p;
 }
+
+GemmProblem bf16_problem(const void* A, RowMap am, const void* W, const void* bias, int64_t M, int64_t N, int64_t K,
+                         void* out, RowMap om, bool out_f32) {
+  return lin_problem(A, am, W, bias, M, N, K, out, om, out_f32 ? kF32 : kBF16);
+}
+
+// GELU elementwise masks: fp16 pre-activation in, fp16 activation out (forward);
+// fp16 pre-activation beside the bf16 gradients (backward)
+constexpr int kGeluF16 = 1 | 4, kGeluBwdF16 = 2;
 
 flux_status check_single_weights(const flux_single_weights* sw) {
   REQUIRE(sw, "weights are NULL");
@@ -376,18 +395,21 @@ flux_status flux_single_fwd_train(const flux_dims* d, const flux_single_weights*
   la.s[0].out = sv.h; la.s[0].omap = rmap(L * D, D, L);
   la.s[0].shift = sv.mod; la.s[0].scale = sv.mod + D; la.s[0].mod_bstride = 3 * D;
   la.s[0].rows = (int32_t)(B * L);
-  FLUX_HIP(launch_ln_mod(la, kBF16, st), "LayerNorm-modulate");
+  FLUX_HIP(launch_ln_mod(la, kF16, st), "LayerNorm-modulate");
+  // linear1 as two problems of one launch: the q|k|v rows of W1 into bf16, the MLP rows into fp16
   GemmBatch g{};
-  g.count = 1;
-  g.p[0] = bf16_problem(sv.h, rmap(L * D, D, L), sw->lin1_w, sw->lin1_b, B * L, 3 * D + F, D, sv.lin1,
-                        rmap(L * (3 * D + F), 3 * D + F, L), false);
-  FLUX_HIP(launch_gemm(g, kBF16, st), "linear1 GEMM");
-  FLUX_HIP(elementwise(kEwGelu, elem_ptr(sv.lin1, 3 * D, 2), rmap(L * (3 * D + F), 3 * D + F, L), nullptr, rmap(0, 1, 1),
-                       elem_ptr(sv.cat, D, 2), rmap(L * (D + F), D + F, L), nullptr, 0, B * L, F, st),
+  g.count = 2;
+  g.p[0] = lin_problem(sv.h, rmap(L * D, D, L), sw->lin1_w, sw->lin1_b, B * L, 3 * D, D, sv.qkv, rmap(L * 3 * D, 3 * D, L),
+                       kBF16);
+  g.p[1] = lin_problem(sv.h, rmap(L * D, D, L), elem_ptr(sw->lin1_w, 3 * D * D, 2), elem_ptr(sw->lin1_b, 3 * D, 2), B * L,
+                       F, D, sv.a, rmap(L * F, F, L), kF16);
+  FLUX_HIP(launch_gemm(g, kF16, st), "linear1 GEMM");
+  FLUX_HIP(elementwise(kEwGelu, sv.a, rmap(L * F, F, L), nullptr, rmap(0, 1, 1), elem_ptr(sv.cat, D, 2),
+                       rmap(L * (D + F), D + F, L), nullptr, 0, B * L, F, st, kGeluF16),
            "GELU");
   PrepArgs pa{};
-  pa.src_q = sv.lin1; pa.src_k = elem_ptr(sv.lin1, D, 2); pa.src_v = elem_ptr(sv.lin1, 2 * D, 2);
-  pa.src_bstride = L * (3 * D + F); pa.src_ld = 3 * D + F;
+  pa.src_q = sv.qkv; pa.src_k = elem_ptr(sv.qkv, D, 2); pa.src_v = elem_ptr(sv.qkv, 2 * D, 2);
+  pa.src_bstride = L * 3 * D; pa.src_ld = 3 * D;
   pa.batch = (int)B; pa.seq = (int)L; pa.seq_pad = (int)Lp; pa.heads = d->heads; pa.head_dim = 128;
   pa.l_img = (int)L;
   pa.gq_img = pa.gq_txt = sw->q_norm;
@@ -402,10 +424,11 @@ flux_status flux_single_fwd_train(const flux_dims* d, const flux_single_weights*
   aa.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
   aa.l_img = (int)L;
   aa.lse = sv.lse;
-  FLUX_HIP(launch_attention(aa, kBF16, kBF16, st), "attention");
-  g.p[0] = bf16_problem(sv.cat, rmap(L * (D + F), D + F, L), sw->lin2_w, sw->lin2_b, B * L, D, D + F, sv.y,
-                        rmap(L * D, D, L), true);
-  FLUX_HIP(launch_gemm(g, kBF16, st), "linear2 GEMM");
+  FLUX_HIP(launch_attention(aa, kBF16, kF16, st), "attention");
+  g.count = 1;
+  g.p[0] = lin_problem(sv.cat, rmap(L * (D + F), D + F, L), sw->lin2_w, sw->lin2_b, B * L, D, D + F, sv.y,
+                       rmap(L * D, D, L), kF32);
+  FLUX_HIP(launch_gemm(g, kF16, st), "linear2 GEMM");
   FLUX_HIP(elementwise(kEwGateAdd, sv.y, rmap(L * D, D, L), nullptr, rmap(0, 1, 1), x, rmap(x_bstride, D, L),
                        sv.mod + 2 * D, 3 * D, B * L, D, st),
            "gated residual");
@@ -445,7 +468,7 @@ flux_status flux_single_bwd(const flux_dims* d, const flux_single_weights* sw, f
   // linear2: d[O | u] = dy W2, dW2 = dy^T [O | u]
   FLUX_HIP(transpose_rows(sw->lin2_w, kBF16, rmap(D * (D + F), D + F, D), D, D + F, w.w2T, D, st), "W2^T");
   FLUX_HIP(transpose_rows(w.dy, kBF16, rowsD, T, D, w.dyT, Tp, st), "dy^T");
-  FLUX_HIP(transpose_rows(sv.cat, kBF16, rowsCat, T, D + F, w.catT, Tp, st), "[O|u]^T");
+  FLUX_HIP(transpose_rows(sv.cat, kF16, rowsCat, T, D + F, w.catT, Tp, st), "[O|u]^T");
   GemmBatch g{};
   g.count = 1;
   g.p[0] = bf16_problem(w.dy, rowsD, w.w2T, nullptr, T, D + F, D, w.dcat, rmap(T * (D + F), D + F, T), false);
@@ -454,16 +477,17 @@ flux_status flux_single_bwd(const flux_dims* d, const flux_single_weights* sw, f
                         rmap(D * (D + F), D + F, D), true);
   FLUX_HIP(launch_gemm(g, kBF16, st), "linear2 weight gradient");
   // u = GELU(a): da = du GELU'(a) -> columns 3D.. of d(linear1 output)
-  FLUX_HIP(elementwise(kEwGeluBwd, elem_ptr(w.dcat, D, 2), rmap(T * (D + F), D + F, T), elem_ptr(sv.lin1, 3 * D, 2),
-                       rowsLin1, elem_ptr(w.dlin1, 3 * D, 2), rmap(T * (3 * D + F), 3 * D + F, T), nullptr, 0, T, F, st),
+  FLUX_HIP(elementwise(kEwGeluBwd, elem_ptr(w.dcat, D, 2), rmap(T * (D + F), D + F, T), sv.a, rmap(L * F, F, L),
+                       elem_ptr(w.dlin1, 3 * D, 2), rmap(T * (3 * D + F), 3 * D + F, T), nullptr, 0, T, F, st,
+                       kGeluBwdF16),
            "GELU backward");
   // attention, then q / k RMSNorm + RoPE backward -> columns 0..3D
   FLUX_HIP(attention_bwd(B, L, d->heads, sv.qh, sv.kh, sv.vt, sv.lse, w.dcat, L * (D + F), D + F, sv.cat, L * (D + F),
-                         D + F, w.at, st),
+                         D + F, true, w.at, st),
            "attention backward");
   PrepBwdArgs pb{};
   pb.dq = w.at.dq; pb.dk = w.at.dk; pb.dv = w.at.dv;
-  pb.src = sv.lin1; pb.src_bstride = L * (3 * D + F); pb.src_ld = 3 * D + F;
+  pb.src = sv.qkv; pb.src_bstride = L * 3 * D; pb.src_ld = 3 * D;
   pb.dst = w.dlin1; pb.dst_bstride = L * (3 * D + F); pb.dst_ld = 3 * D + F;
   pb.gq_img = pb.gq_txt = sw->q_norm;
   pb.gk_img = pb.gk_txt = sw->k_norm;
@@ -479,7 +503,7 @@ flux_status flux_single_bwd(const flux_dims* d, const flux_single_weights* sw, f
   FLUX_HIP(transpose_rows(sw->lin1_w, kBF16, rmap((3 * D + F) * D, D, 3 * D + F), 3 * D + F, D, w.w1T, 3 * D + F, st),
            "W1^T");
   FLUX_HIP(transpose_rows(w.dlin1, kBF16, rowsLin1, T, 3 * D + F, w.dlin1T, Tp, st), "d(lin1)^T");
-  FLUX_HIP(transpose_rows(sv.h, kBF16, rowsD, T, D, w.hT, Tp, st), "h^T");
+  FLUX_HIP(transpose_rows(sv.h, kF16, rowsD, T, D, w.hT, Tp, st), "h^T");
   g.p[0] = bf16_problem(w.dlin1, rowsLin1, w.w1T, nullptr, T, D, 3 * D + F, w.dh, rmap(T * D, D, T), true);
   FLUX_HIP(launch_gemm(g, kBF16, st), "linear1 data gradient");
   g.p[0] = bf16_problem(w.dlin1T, rmap((3 * D + F) * Tp, Tp, 3 * D + F), w.hT, nullptr, 3 * D + F, D, Tp, gr->lin1_w,
@@ -538,16 +562,16 @@ flux_status flux_block_fwd_train(const flux_dims* d, const flux_stream_weights* 
       a.s[i].shift = sv.mod[i] + chunk * D; a.s[i].scale = sv.mod[i] + (chunk + 1) * D; a.s[i].mod_bstride = 6 * D;
       a.s[i].rows = (int32_t)(B * seg[i]);
     }
-    return launch_ln_mod(a, kBF16, st);
+    return launch_ln_mod(a, kF16, st);
   };
   FLUX_HIP(snapshot(sv.x0), "residual snapshot");
   FLUX_HIP(ln_mod(0, sv.h1), "LayerNorm-modulate (attention)");
   GemmBatch g{};
   g.count = ns;
   for (int i = 0; i < ns; ++i)
-    g.p[i] = bf16_problem(elem_ptr(sv.h1, off[i] * D, 2), jrow(i, D), sw[i]->qkv_w, sw[i]->qkv_b, B * seg[i], 3 * D, D,
-                          elem_ptr(sv.qkv, off[i] * 3 * D, 2), jrow(i, 3 * D), false);
-  FLUX_HIP(launch_gemm(g, kBF16, st), "qkv GEMM");
+    g.p[i] = lin_problem(elem_ptr(sv.h1, off[i] * D, 2), jrow(i, D), sw[i]->qkv_w, sw[i]->qkv_b, B * seg[i], 3 * D, D,
+                         elem_ptr(sv.qkv, off[i] * 3 * D, 2), jrow(i, 3 * D), kBF16);
+  FLUX_HIP(launch_gemm(g, kF16, st), "qkv GEMM");
   PrepArgs pa{};
   pa.src_q = sv.qkv; pa.src_k = elem_ptr(sv.qkv, D, 2); pa.src_v = elem_ptr(sv.qkv, 2 * D, 2);
   pa.src_bstride = L * 3 * D; pa.src_ld = 3 * D;
@@ -566,11 +590,11 @@ flux_status flux_block_fwd_train(const flux_dims* d, const flux_stream_weights* 
   aa.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
   aa.l_img = (int)Li;
   aa.lse = sv.lse;
-  FLUX_HIP(launch_attention(aa, kBF16, kBF16, st), "joint attention");
+  FLUX_HIP(launch_attention(aa, kBF16, kF16, st), "joint attention");
   for (int i = 0; i < ns; ++i)
-    g.p[i] = bf16_problem(elem_ptr(sv.o, off[i] * D, 2), jrow(i, D), sw[i]->proj_w, sw[i]->proj_b, B * seg[i], D, D,
-                          sv.y1 + off[i] * D, jrow(i, D), true);
-  FLUX_HIP(launch_gemm(g, kBF16, st), "output projection GEMM");
+    g.p[i] = lin_problem(elem_ptr(sv.o, off[i] * D, 2), jrow(i, D), sw[i]->proj_w, sw[i]->proj_b, B * seg[i], D, D,
+                         sv.y1 + off[i] * D, jrow(i, D), kF32);
+  FLUX_HIP(launch_gemm(g, kF16, st), "output projection GEMM");
   for (int i = 0; i < ns; ++i)
     FLUX_HIP(elementwise(kEwGateAdd, sv.y1 + off[i] * D, jrow(i, D), nullptr, rmap(0, 1, 1), xs[i],
                          rmap(xbs[i], D, seg[i]), sv.mod[i] + 2 * D, 6 * D, B * seg[i], D, st),
@@ -578,16 +602,16 @@ flux_status flux_block_fwd_train(const flux_dims* d, const flux_stream_weights* 
   FLUX_HIP(snapshot(sv.x1), "residual snapshot");
   FLUX_HIP(ln_mod(3, sv.h2), "LayerNorm-modulate (MLP)");
   for (int i = 0; i < ns; ++i)
-    g.p[i] = bf16_problem(elem_ptr(sv.h2, off[i] * D, 2), jrow(i, D), sw[i]->fc1_w, sw[i]->fc1_b, B * seg[i], F, D,
-                          elem_ptr(sv.a1, off[i] * F, 2), jrow(i, F), false);
-  FLUX_HIP(launch_gemm(g, kBF16, st), "fc1 GEMM");
+    g.p[i] = lin_problem(elem_ptr(sv.h2, off[i] * D, 2), jrow(i, D), sw[i]->fc1_w, sw[i]->fc1_b, B * seg[i], F, D,
+                         elem_ptr(sv.a1, off[i] * F, 2), jrow(i, F), kF16);
+  FLUX_HIP(launch_gemm(g, kF16, st), "fc1 GEMM");
   FLUX_HIP(elementwise(kEwGelu, sv.a1, rmap(L * F, F, L), nullptr, rmap(0, 1, 1), sv.u, rmap(L * F, F, L), nullptr, 0,
-                       B * L, F, st),
+                       B * L, F, st, kGeluF16),
            "GELU");
   for (int i = 0; i < ns; ++i)
-    g.p[i] = bf16_problem(elem_ptr(sv.u, off[i] * F, 2), jrow(i, F), sw[i]->fc2_w, sw[i]->fc2_b, B * seg[i], D, F,
-                          sv.y2 + off[i] * D, jrow(i, D), true);
-  FLUX_HIP(launch_gemm(g, kBF16, st), "fc2 GEMM");
+    g.p[i] = lin_problem(elem_ptr(sv.u, off[i] * F, 2), jrow(i, F), sw[i]->fc2_w, sw[i]->fc2_b, B * seg[i], D, F,
+                         sv.y2 + off[i] * D, jrow(i, D), kF32);
+  FLUX_HIP(launch_gemm(g, kF16, st), "fc2 GEMM");
   for (int i = 0; i < ns; ++i)
     FLUX_HIP(elementwise(kEwGateAdd, sv.y2 + off[i] * D, jrow(i, D), nullptr, rmap(0, 1, 1), xs[i],
                          rmap(xbs[i], D, seg[i]), sv.mod[i] + 5 * D, 6 * D, B * seg[i], D, st),
@@ -634,7 +658,7 @@ flux_status flux_block_bwd(const flux_dims* d, const flux_stream_weights* iw, co
   GemmBatch g{};
   g.count = ns;
   // one linear of both streams: y = x W^T + b with output gradient dyv (bf16 joint rows, width N) and
-  // input x (bf16 joint rows, width K); writes dx (joint rows, width K; fp32 or bf16), dW and db
+  // input x (the forward's fp16 joint rows, width K); writes dx (joint rows, width K; fp32 or bf16), dW and db
   auto linear_bwd = [&](const void* dyv, int64_t N, const void* x, int64_t K, const void* const* W, int wsel,
                         void* dxv, bool dx_f32) -> flux_status {
     for (int i = 0; i < ns; ++i) {
@@ -644,7 +668,7 @@ flux_status flux_block_bwd(const flux_dims* d, const flux_stream_weights* iw, co
       FLUX_HIP(colsum(dyi, kBF16, jrow(i, N), nullptr, none, B * seg[i], N, 1, gb, 0, w.pt.col, st), "bias gradient");
       FLUX_HIP(transpose_rows(W[i], kBF16, rmap(N * K, K, N), N, K, w.wT[i], N, st), "W^T");
       FLUX_HIP(transpose_rows(dyi, kBF16, jrow(i, N), B * seg[i], N, w.yT[i], Tp[i], st), "dy^T");
-      FLUX_HIP(transpose_rows(elem_ptr(x, off[i] * K, 2), kBF16, jrow(i, K), B * seg[i], K, w.xT[i], Tp[i], st), "x^T");
+      FLUX_HIP(transpose_rows(elem_ptr(x, off[i] * K, 2), kF16, jrow(i, K), B * seg[i], K, w.xT[i], Tp[i], st), "x^T");
       g.p[i] = bf16_problem(dyi, jrow(i, N), w.wT[i], nullptr, B * seg[i], K, N,
                             elem_ptr(dxv, off[i] * K, dx_f32 ? 4 : 2), jrow(i, K), dx_f32);
     }
@@ -670,7 +694,7 @@ flux_status flux_block_bwd(const flux_dims* d, const flux_stream_weights* iw, co
   }
   if ((s = linear_bwd(w.dy, D, sv.u, F, Wfc2, 3, w.du, false)) != FLUX_OK) return s;
   FLUX_HIP(elementwise(kEwGeluBwd, w.du, rmap(L * F, F, L), sv.a1, rmap(L * F, F, L), w.du, rmap(L * F, F, L), nullptr,
-                       0, B * L, F, st), "GELU backward");
+                       0, B * L, F, st, kGeluBwdF16), "GELU backward");
   if ((s = linear_bwd(w.du, F, sv.h2, D, Wfc1, 2, w.dh, true)) != FLUX_OK) return s;
   for (int i = 0; i < ns; ++i)
     FLUX_HIP(ln_bwd(sv.x1 + off[i] * D, jrow(i, D), w.dh + off[i] * D, jrow(i, D), ds[i], drow(i), sv.mod[i] + 4 * D,
@@ -684,7 +708,7 @@ flux_status flux_block_bwd(const flux_dims* d, const flux_stream_weights* iw, co
                          sv.mod[i] + 2 * D, 6 * D, B * seg[i], D, st), "dy (attention)");
   }
   if ((s = linear_bwd(w.dy, D, sv.o, D, Wproj, 1, w.dO, false)) != FLUX_OK) return s;
-  FLUX_HIP(attention_bwd(B, L, d->heads, sv.qh, sv.kh, sv.vt, sv.lse, w.dO, L * D, D, sv.o, L * D, D, w.at, st),
+  FLUX_HIP(attention_bwd(B, L, d->heads, sv.qh, sv.kh, sv.vt, sv.lse, w.dO, L * D, D, sv.o, L * D, D, true, w.at, st),
            "attention backward");
   PrepBwdArgs pb{};
   pb.dq = w.at.dq; pb.dk = w.at.dk; pb.dv = w.at.dv;
@@ -794,7 +818,7 @@ flux_status flux_attention_bwd(int32_t batch, int32_t seq, int32_t heads, const 
   pa.batch = batch; pa.seq = seq; pa.seq_pad = (int)Lp; pa.heads = heads; pa.head_dim = 128; pa.l_img = seq;
   pa.qh = qh; pa.kh = kh; pa.vt = vt;
   FLUX_HIP(launch_prep(pa, kBF16, st), "head-major layout");
-  FLUX_HIP(attention_bwd(batch, seq, heads, qh, kh, vt, lse, dout, seq * ldo, ldo, o, seq * ldo, ldo, w, st),
+  FLUX_HIP(attention_bwd(batch, seq, heads, qh, kh, vt, lse, dout, seq * ldo, ldo, o, seq * ldo, ldo, false, w, st),
            "attention backward");
   PrepBwdArgs pb{};
   pb.dq = w.dq; pb.dk = w.dk; pb.dv = w.dv;

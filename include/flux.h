@@ -569,12 +569,17 @@ size_t flux_attention_workspace_bytes(int32_t precision, int32_t batch, int32_t 
  * velocity MSE is backpropagated through the network; the gradients follow
  * from the forward definitions of the double and single blocks by the chain
  * rule).  Training runs with precision FLUX_PREC_BF16, weights_f16 = 0 and
- * head_dim 128 (anything else: FLUX_ERR_UNSUPPORTED): bf16 activations and
- * weights on the bf16 MFMA, fp32 accumulation, fp32 residual stream and fp32
- * gradients.
+ * head_dim 128 (anything else: FLUX_ERR_UNSUPPORTED).  The forward's block
+ * linears multiply fp16 activations (LayerNorm-modulate, attention and GELU
+ * outputs, saturating at +-65504) by the bf16 weights converted to fp16 per
+ * tile, accumulating in fp32, as flux_block_fwd does; the q|k|v projection is
+ * rounded to bf16 before the q / k norm.  The backward runs on the bf16 MFMA
+ * with bf16 gradient operands (the saved fp16 activations rounded to bf16 for
+ * the weight gradients), fp32 accumulation, fp32 residual stream and fp32
+ * parameter gradients.
  *
  * A training forward computes the same block output as flux_block_fwd /
- * flux_single_fwd (up to the rounding of its bf16 activations) and keeps in
+ * flux_single_fwd (up to the rounding of its activations) and keeps in
  * `saved` (caller-allocated, 256-byte aligned, flux_train_saved_bytes(dims,
  * op) bytes; op 0 double block, 1 single block) everything its backward
  * reads: the residual before each half, the modulation vectors, the
