@@ -211,6 +211,10 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
     g.p[i].qw = rec(i, FLUX_FP8_FC2_W);
   }
   FLUX_HIP(launch_gemm(g, lin, st), "fc2 GEMM");
+  if (debug_checks_on())
+    for (int i = 0; i < ns; ++i)
+      FLUX_HIP(debug_check(xs[i], kF32, B, seg[i] * D, xbs[i], -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_RESIDUAL, st),
+               "debug check of the residual");
   return FLUX_OK;
 }
 
@@ -336,6 +340,9 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
   g.p[0].qa = rec(FLUX_FP8_LIN2_X);
   g.p[0].qw = rec(FLUX_FP8_LIN2_W);
   FLUX_HIP(launch_gemm(g, lin, st), "linear2 GEMM");
+  if (debug_checks_on())
+    FLUX_HIP(debug_check(x, kF32, B, L * D, x_bstride, -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_RESIDUAL, st),
+             "debug check of the residual");
   return FLUX_OK;
 }
 
@@ -381,12 +388,21 @@ static flux_status rf_check(const rf_args* a) {
 // Enqueue noising and loss; `partials` holds batch * rf_parts_per_sample(n)
 // doubles when a loss is asked for.
 static flux_status rf_launch(const rf_args* a, double* partials, hipStream_t st) {
+  const bool dbg = debug_checks_on();
+  if (dbg) FLUX_HIP(debug_check(a->t, kF32, 1, a->batch, a->batch, 0.f, 1.f, FLUX_DBG_T_RANGE, st), "debug check of t");
   if (a->z_t || a->v_target)
     FLUX_HIP(launch_rf_noise(a->batch, a->n_per_sample, a->z0, a->z1, a->t, a->z_t, a->v_target, st), "rf noise");
   if (a->loss || a->loss_per_sample)
     FLUX_HIP(launch_rf_loss(a->batch, a->n_per_sample, a->z0, a->z1, a->v_pred, a->loss, a->loss_per_sample,
                             partials, rf_parts_per_sample(a->n_per_sample), st),
              "rf loss");
+  if (dbg && (a->loss || a->loss_per_sample)) {
+    const int64_t n = (int64_t)a->batch * a->n_per_sample;
+    FLUX_HIP(debug_check(a->v_pred, kF32, 1, n, n, -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_LOSS, st), "debug check of v_pred");
+    FLUX_HIP(debug_check(a->loss, kF32, 1, 1, 1, -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_LOSS, st), "debug check of the loss");
+    FLUX_HIP(debug_check(a->loss_per_sample, kF32, 1, a->batch, a->batch, -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_LOSS, st),
+             "debug check of the per-sample loss");
+  }
   return FLUX_OK;
 }
 
@@ -661,6 +677,10 @@ flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, i
   g.p[0].col_stride0 = HW;
   g.partials = partials;
   FLUX_HIP(launch_gemm(g, act, st), "output GEMM");
+  if (debug_checks_on()) {
+    const int64_t n = (int64_t)batch * channels * HW;
+    FLUX_HIP(debug_check(v_pred, kF32, 1, n, n, -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_OUTPUT, st), "debug check of v_pred");
+  }
   return FLUX_OK;
 }
 

@@ -38,6 +38,15 @@ inline flux_status hip_fail(hipError_t e, const char* what) {
     if (!(cond)) return fail(FLUX_ERR_INVALID_ARGUMENT, __VA_ARGS__);       \
   } while (0)
 
+// Device checks (FLUX_DEBUG_CHECKS): whether they are on, and a read-only pass
+// that ORs `bit` into the device's status word if any value of `rows` rows of
+// `cols` elements (dtype kF32 / kBF16 / kF16, rows `row_stride` elements
+// apart) is outside [lo, hi] or NaN.
+bool debug_checks_on();
+hipError_t debug_check(const void* p, int dt, int64_t rows, int64_t cols, int64_t row_stride, float lo, float hi,
+                       uint32_t bit, hipStream_t st);
+constexpr float kDbgBig = 3.402823466e38f;   // [-kDbgBig, kDbgBig]: finite
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // bytes of a q/k/v or attention element (bf16 unless fp32)
 inline int esize(int prec) { return prec == FLUX_PREC_F32 ? 4 : 2; }

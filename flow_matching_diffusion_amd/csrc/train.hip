@@ -432,6 +432,9 @@ flux_status flux_single_fwd_train(const flux_dims* d, const flux_single_weights*
   FLUX_HIP(elementwise(kEwGateAdd, sv.y, rmap(L * D, D, L), nullptr, rmap(0, 1, 1), x, rmap(x_bstride, D, L),
                        sv.mod + 2 * D, 3 * D, B * L, D, st),
            "gated residual");
+  if (debug_checks_on())
+    FLUX_HIP(debug_check(x, kF32, B, L * D, x_bstride, -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_RESIDUAL, st),
+             "debug check of the residual");
   return FLUX_OK;
 }
 
@@ -514,6 +517,9 @@ flux_status flux_single_bwd(const flux_dims* d, const flux_single_weights* sw, f
            "LayerNorm-modulate backward");
   // modulation: dW, db, dvec += SiLU'(vec) W^T dm
   FLUX_HIP(mod_bwd(sw->mod_w, vec, w.dm, 3 * D, D, B, gr->mod_w, gr->mod_b, dvec, w.pt, st), "modulation backward");
+  if (debug_checks_on())
+    FLUX_HIP(debug_check(dx, kF32, B, L * D, dx_bstride, -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_GRAD, st),
+             "debug check of the input gradient");
   return FLUX_OK;
 }
 
@@ -616,6 +622,10 @@ flux_status flux_block_fwd_train(const flux_dims* d, const flux_stream_weights* 
     FLUX_HIP(elementwise(kEwGateAdd, sv.y2 + off[i] * D, jrow(i, D), nullptr, rmap(0, 1, 1), xs[i],
                          rmap(xbs[i], D, seg[i]), sv.mod[i] + 5 * D, 6 * D, B * seg[i], D, st),
              "gated residual (MLP)");
+  if (debug_checks_on())
+    for (int i = 0; i < ns; ++i)
+      FLUX_HIP(debug_check(xs[i], kF32, B, seg[i] * D, xbs[i], -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_RESIDUAL, st),
+               "debug check of the residual");
   return FLUX_OK;
 }
 
@@ -731,6 +741,10 @@ flux_status flux_block_bwd(const flux_dims* d, const flux_stream_weights* iw, co
     FLUX_HIP(mod_bwd(sw[i]->mod_w, vec, w.dm[i], 6 * D, D, B, gs[i]->mod_w, gs[i]->mod_b, dvec, w.pt, st),
              "modulation backward");
   }
+  if (debug_checks_on())
+    for (int i = 0; i < ns; ++i)
+      FLUX_HIP(debug_check(ds[i], kF32, B, seg[i] * D, dbs[i], -kDbgBig, kDbgBig, FLUX_DBG_NONFINITE_GRAD, st),
+               "debug check of the input gradient");
   return FLUX_OK;
 }
 

@@ -47,7 +47,8 @@ EXPORTED = (
     "flux_embed_bwd_workspace_bytes", "flux_embed_bwd", "flux_single_seq_fwd_train", "flux_single_seq_bwd",
     "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd", "flux_mxfp4_scale_bytes", "flux_mxfp4_quantize",
     "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize", "flux_timestep_embed", "rf_noise_loss_noalloc",
-    "flux_rf_noalloc_max_partials", "flux_timing_flush", "flux_stream_copy",
+    "flux_rf_noalloc_max_partials", "flux_timing_flush", "flux_stream_copy", "flux_debug_checks",
+    "flux_debug_status",
 )
 
 
@@ -143,6 +144,8 @@ def lib() -> C.CDLL:
         "rf_noise_loss_noalloc": [P(rf_args), vp],
         "flux_timing_flush": [vp, i64],
         "flux_stream_copy": [vp, vp, i64, vp],
+        "flux_debug_checks": [i32],
+        "flux_debug_status": [P(C.c_uint32), i32],
         "flux_rope_table": [vp, i32, i32, P(C.c_int32), f32, vp, vp],
         "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
                            vp, vp, i64, vp, i64, vp, vp, sz, vp],
@@ -524,6 +527,26 @@ def flux_timing_flush(buffer=None, nbytes: int = 0) -> None:
 
 def flux_stream_copy(src, dst, nbytes: int, stream=None) -> None:
     _check(lib().flux_stream_copy(ptr(src), ptr(dst), nbytes, _stream(stream)), "flux_stream_copy")
+
+
+# device checks (status word bits)
+FLUX_DBG_T_RANGE = 1
+FLUX_DBG_NONFINITE_RESIDUAL = 2
+FLUX_DBG_NONFINITE_LOSS = 4
+FLUX_DBG_NONFINITE_OUTPUT = 8
+FLUX_DBG_NONFINITE_GRAD = 16
+
+
+def flux_debug_checks(on: Optional[bool] = None) -> bool:
+    """Turn the device checks on / off (None: leave); returns the previous setting."""
+    return bool(lib().flux_debug_checks(-1 if on is None else (1 if on else 0)))
+
+
+def flux_debug_status(clear: bool = False) -> int:
+    """The current device's status word (synchronizes the device)."""
+    v = C.c_uint32(0)
+    _check(lib().flux_debug_status(C.byref(v), 1 if clear else 0), "flux_debug_status")
+    return int(v.value)
 
 
 def flux_timing_read() -> Dict[str, tuple]:

@@ -750,6 +750,39 @@ flux_status flux_timing_read(double* ms, int64_t* launches, double* work, int32_
 flux_status flux_timing_flush(void* buffer, int64_t bytes);
 flux_status flux_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/*
+ * Device checks, off by default.  Two preconditions are not checked on the
+ * device in normal runs: timesteps lie in [0, 1] ("Flux model API
+ * reference", Common issues: the timestep range) and the values the model
+ * computes are finite.  With checks on -- the environment variable
+ * FLUX_DEBUG_CHECKS set to anything but "" or "0" when the library is first
+ * used, or flux_debug_checks(1) -- the entry points below enqueue, on the
+ * caller's stream after their own work, read-only passes over the named
+ * tensors that OR a bit into a status word of the current device:
+ *   FLUX_DBG_T_RANGE             rf_noise_loss(_noalloc): a t outside [0, 1] or NaN
+ *   FLUX_DBG_NONFINITE_RESIDUAL  flux_block_fwd, flux_single_fwd, flux_single_seq_fwd
+ *                                and the training forwards: a non-finite residual
+ *                                value after the block
+ *   FLUX_DBG_NONFINITE_LOSS      rf_noise_loss(_noalloc): a non-finite v_pred, loss or
+ *                                per-sample loss
+ *   FLUX_DBG_NONFINITE_OUTPUT    flux_final_fwd: a non-finite velocity
+ *   FLUX_DBG_NONFINITE_GRAD      the block backwards: a non-finite input gradient
+ * The word persists until cleared; the checks never change a result.  Each
+ * check is one extra read of the tensor (about as long as a copy of it).
+ *
+ * flux_debug_checks -- on = 1 turns the checks on, 0 off, a negative value
+ *   leaves the setting; returns the setting before the call (1 on, 0 off).
+ * flux_debug_status -- synchronizes the current device, writes its status
+ *   word to *status and, when clear != 0, resets it to 0.
+ */
+#define FLUX_DBG_T_RANGE 1u
+#define FLUX_DBG_NONFINITE_RESIDUAL 2u
+#define FLUX_DBG_NONFINITE_LOSS 4u
+#define FLUX_DBG_NONFINITE_OUTPUT 8u
+#define FLUX_DBG_NONFINITE_GRAD 16u
+int32_t flux_debug_checks(int32_t on);
+flux_status flux_debug_status(uint32_t* status, int32_t clear);
+
 /* Static text for a status code; thread-local detail of the last failure on
  * this thread ("" when none). */
 const char* flux_status_string(flux_status s);

@@ -233,3 +233,17 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "missing" in r.stdout
+
+
+def test_debug_checks_setting_and_null_status():
+    # the setting is host state; the status read rejects NULL before touching the device
+    prev = F.flux_debug_checks(None)
+    try:
+        F.flux_debug_checks(True)
+        assert F.flux_debug_checks(None) is True
+        assert F.flux_debug_checks(False) is True
+        assert F.flux_debug_checks(None) is False
+    finally:
+        F.flux_debug_checks(prev)
+    assert F.lib().flux_debug_status(None, 0) == 1
+    assert b"status" in F.lib().flux_last_error()
