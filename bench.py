@@ -434,6 +434,124 @@ def cpu_baseline(wl, emb, dws, sws, mi, work):
             "seconds": round(dt, 2), "loss": loss}
 
 
+def _blas_name() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info() if p.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return "unknown"
+
+
+ORACLE_CONFIGS = ("C1", "C2", "C3", "C4", "C5")
+
+
+def oracle_timing(which) -> int:
+    """The fp64 numpy oracle timed on this host's usable cores, one JSON line
+    per configuration (a reported baseline beside the GPU numbers, never the
+    target):
+      C1  tiny fp32 model, whole forward + loss (repeated for >= 2 s);
+      C2  the Flux-535M-shaped model (1536 tokens), whole forward + loss;
+      C3  the Flux-12B block-pair step (4608 tokens), whole;
+      C4  the 19 + 38-block Flux-12B forward at batch 2, extrapolated: one
+          double and one single block of one sample timed, times 19 / 38 and
+          the batch, plus the embeddings and head timed at batch 2;
+      C5  the block pair with E4M3 linears (the fp8 simulation: every token-path
+          operand quantized and decoded, current scaling), one sample of the
+          batch of 4 timed, times 4.
+    No GPU is used."""
+    import numpy as np
+
+    import oracle as O
+    from oracle import fp8_oracle as Q
+    from flow_matching_diffusion_amd import synth
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        pass
+    cpu, blas = _cpu_model(), _blas_name()
+
+    def emit(cfg, wl, seconds, flops, tokens, sample):
+        print(json.dumps({"config": cfg, "workload": wl.name, "kind": "oracle", "seconds": round(seconds, 3),
+                          "tokens_per_s": round(tokens / seconds, 3), "fp64_gflops": round(flops / seconds / 1e9, 1),
+                          "cores": cores, "cpu": cpu, "blas": blas, "sample": sample}), flush=True)
+
+    def whole(cfg, wl):
+        emb = synth.embed_weights(wl)
+        dws = [synth.double_block_weights(wl, i) for i in range(wl.n_double)]
+        sws = [synth.single_block_weights(wl, wl.n_double + i) for i in range(wl.n_single)]
+        mi = synth.model_inputs(wl)
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 2.0:
+            zt, _ = O.rf_noise(mi["z0"], mi["z1"], mi["t"])
+            v = O.flux_forward(zt, mi["txt"], mi.get("y"), mi["t"], mi["ids"], emb, dws, sws, wl.heads, wl.axes_dim,
+                               wl.theta, wl.eps, wl.model_channels)
+            loss, _ = O.rf_loss(v, mi["z0"], mi["z1"])
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        assert np.isfinite(loss)
+        emit(cfg, wl, dt, algorithmic_work(wl)["total_flops"], wl.tokens,
+             f"whole forward + loss, mean of {reps} run(s)")
+
+    def pair_one_sample(wl, lin=None):
+        one = synth.custom_workload(wl.name + "_one_sample", base=wl.name, batch=1)
+        inp = synth.block_inputs(one)
+        ang = O.rope_angles(synth.joint_ids(one), wl.axes_dim, wl.theta)
+        w2, w1 = synth.double_block_weights(one, 0), synth.single_block_weights(one, 1)
+        t0 = time.perf_counter()
+        xi, xt = O.double_block(inp["x_img"], inp["x_txt"], inp["vec"], ang, w2, wl.heads, wl.eps, lin=lin)
+        td = time.perf_counter() - t0
+        print(f"[oracle] {wl.name}: double block of one sample {td:.1f} s", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        y = O.single_block(np.concatenate([xi, xt], axis=1), inp["vec"], ang, w1, wl.heads, wl.eps, lin=lin)
+        ts = time.perf_counter() - t0
+        print(f"[oracle] {wl.name}: single block of one sample {ts:.1f} s", file=sys.stderr, flush=True)
+        assert np.isfinite(y).all()
+        return td, ts
+
+    for cfg in which:
+        if cfg == "C1":
+            whole(cfg, synth.WORKLOADS["tiny_fp32"])
+        elif cfg == "C2":
+            whole(cfg, synth.WORKLOADS["flux535m"])
+        elif cfg == "C3":
+            whole(cfg, synth.WORKLOADS["flux12b_blocks"])
+        elif cfg == "C4":
+            wl = synth.WORKLOADS["flux12b_full"]
+            td, ts = pair_one_sample(wl)
+            emb, mi = synth.embed_weights(wl), synth.model_inputs(wl)
+            t0 = time.perf_counter()
+            zt, _ = O.rf_noise(mi["z0"], mi["z1"], mi["t"])
+            v = O.flux_forward(zt, mi["txt"], mi.get("y"), mi["t"], mi["ids"], emb, [], [], wl.heads, wl.axes_dim,
+                               wl.theta, wl.eps, wl.model_channels)
+            O.rf_loss(v, mi["z0"], mi["z1"])
+            te = time.perf_counter() - t0
+            total = wl.batch * (wl.n_double * td + wl.n_single * ts) + te
+            emit(cfg, wl, total, algorithmic_work(wl)["total_flops"], wl.tokens,
+                 f"extrapolated: one double ({td:.1f} s) and one single block ({ts:.1f} s) of one sample timed, "
+                 f"x{wl.n_double} / x{wl.n_single} blocks x{wl.batch} samples, plus noising, embeddings, head "
+                 f"and loss at batch {wl.batch} ({te:.1f} s)")
+        elif cfg == "C5":
+            wl = synth.WORKLOADS["flux12b_blocks_fp8"]
+
+            def fp8_lin(name, x, w, b):
+                return Q.fp8_linear(x, w, b, Q.current_scale(x), Q.current_scale(w))
+
+            td, ts = pair_one_sample(wl, lin=fp8_lin)
+            work = algorithmic_work(synth.custom_workload("c5_one", base=wl.name, batch=1))
+            blocks = work["total_flops"] - 2 * 2 * wl.l_img * wl.latent_ch * wl.hidden   # no embedding / head
+            emit(cfg, wl, wl.batch * (td + ts), wl.batch * blocks, wl.tokens,
+                 f"block pair with E4M3 linears (fp8 simulation, current scaling), one sample timed "
+                 f"({td + ts:.1f} s), x{wl.batch} samples")
+        else:
+            print(f"unknown configuration {cfg}", file=sys.stderr)
+            return 2
+    return 0
+
+
 def mx_linears_bench(args, fp4=False) -> int:
     """The six token-path linears of the Flux-12B block pair at batch 4
     (qkv, proj, fc1, fc2 over the joint 4608-token rows of 4 samples; lin1,
@@ -713,12 +831,18 @@ def main() -> int:
     ap.add_argument("--hbm-sweep", action="store_true",
                     help="only run the HBM sweep: rf noising / loss and the streaming copy from 2^20 to 2^28 "
                          "fp32 elements, warm and with the caches flushed before each timed launch")
+    ap.add_argument("--oracle-timing", metavar="CONFIGS", default=None,
+                    help="no GPU: time the fp64 oracle on this host for a comma-separated subset of "
+                         + ",".join(ORACLE_CONFIGS) + " (one JSON line each; C4 and C5 extrapolated from one "
+                         "sample, as each line says)")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
                     help="no GPU: write profiles/traffic.json and the profile summaries from the rocprofv3 "
                          "CSV folders under DIR (see PROFILE_COMMANDS)")
     ap.add_argument("--profiles-out", default=os.path.join(ROOT, "profiles"),
                     help="where --summarize-counters writes")
     args = ap.parse_args()
+    if args.oracle_timing:
+        return oracle_timing([c.strip() for c in args.oracle_timing.split(",") if c.strip()])
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.profiles_out)
     world = int(os.environ.get("WORLD_SIZE", "1"))
