@@ -391,7 +391,10 @@ flux_status flux_final_fwd(int32_t precision, int32_t batch, int32_t channels, i
 
 /*
  * flux_linear_fwd -- y = x W^T + b, the linear layer used throughout the
- * blocks, exposed on its own.  x [M, K] (row stride lda), W [N, K], b [N] or
+ * blocks, exposed on its own ("Flux architecture deep dive", Model components:
+ * the q|k|v, projection and MLP linears of the MMDiT layer and the linear1 /
+ * linear2 of the single block; weights in the [out, in] layout of a torch
+ * Linear).  x [M, K] (row stride lda), W [N, K], b [N] or
  * NULL, all of element type `precision`; y [M, N] float (row stride ldy).
  * K must be a multiple of 64 for bf16.
  */
