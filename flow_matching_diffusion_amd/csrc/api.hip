@@ -44,6 +44,8 @@ const char* flux_status_string(flux_status s) {
 
 const char* flux_last_error(void) { return g_err; }
 
+int32_t flux_gemm_stream_k(int32_t mode, int32_t spin) { return gemm_stream_k(mode, spin); }
+
 size_t flux_workspace_bytes(const flux_dims* d, int32_t op) {
   if (check_dims(d) != FLUX_OK) return 0;
   if (op == 0 || op == 2) return block_ws(d, nullptr).bytes;   // the sequential block is a one-stream double block
@@ -123,6 +125,7 @@ flux_status flux_block_fwd(const flux_dims* d, const flux_stream_weights* iw, co
 
   // 3. q|k|v = Linear_qkv(h) per stream, one grouped launch
   GemmBatch g{};
+  attach_sk(g, w.sk);
   g.count = ns;
   for (int i = 0; i < ns; ++i)
     g.p[i] = gemm_problem(elem_ptr(w.h, off[i] * D, aes), rmap(L * D, D, seg[i]), sw[i]->qkv_w, sw[i]->qkv_b,
@@ -284,6 +287,7 @@ flux_status flux_single_fwd(const flux_dims* d, const flux_single_weights* sw, f
 
   // 3. q|k|v -> qkv buffer; GELU(mlp_in) -> columns D.. of the linear2 input
   GemmBatch g{};
+  attach_sk(g, w.sk);
   g.count = 1;
   g.p[0] = gemm_problem(w.h, rmap(L * D, D, L), sw->lin1_w, sw->lin1_b, (int)(B * L), (int)(3 * D + F), (int)D,
                         kEpiSplitGelu, w.qkv, rmap(L * 3 * D, 3 * D, L));

@@ -109,8 +109,16 @@ struct BlockWs {
   void* qh;
   void* kh;
   void* vt;
+  void* sk;   // stream-K partial sums and flags of the persistent GEMM (16-bit workloads)
   size_t bytes;
 };
+
+// The stream-K area of a block workspace (kGemmSkBytes) attached to a GEMM batch.
+inline void attach_sk(GemmBatch& g, void* sk) {
+  g.sk_part = static_cast<float*>(sk);
+  g.sk_flag = sk ? reinterpret_cast<int32_t*>(static_cast<char*>(sk) + kGemmSkMaxGrid * kGemmSkSlotFloats * 4)
+                 : nullptr;
+}
 
 inline BlockWs block_ws(const flux_dims* d, void* base) {
   Carve c(base);
@@ -125,6 +133,7 @@ inline BlockWs block_ws(const flux_dims* d, void* base) {
   w.qh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.kh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.vt = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.sk = d->precision == FLUX_PREC_BF16 ? c.take(kGemmSkBytes) : nullptr;
   w.bytes = (size_t)round_up((int64_t)c.off, 256);
   return w;
 }
@@ -137,6 +146,7 @@ struct SingleWs {
   void* qh;
   void* kh;
   void* vt;
+  void* sk;   // stream-K partial sums and flags of the persistent GEMM (16-bit workloads)
   size_t bytes;
 };
 
@@ -152,6 +162,7 @@ inline SingleWs single_ws(const flux_dims* d, void* base) {
   w.qh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.kh = c.take(B * d->heads * Lp * d->head_dim * es);
   w.vt = c.take(B * d->heads * Lp * d->head_dim * es);
+  w.sk = d->precision == FLUX_PREC_BF16 ? c.take(kGemmSkBytes) : nullptr;
   w.bytes = (size_t)round_up((int64_t)c.off, 256);
   return w;
 }

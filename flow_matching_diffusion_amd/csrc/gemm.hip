@@ -21,6 +21,8 @@
 // fp32 path (fp32 workloads only): LDS-tiled FMA kernel with the same epilogues.
 #include <type_traits>
 
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -180,13 +182,9 @@ struct TileCoord {
   int prob, tm, tn;
 };
 
-__device__ __forceinline__ TileCoord decode_tile_id(const GemmBatch& bt, int bid, int BM, int BN) {
-  // Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8);
-  // give XCD x the contiguous tile range [x*q + min(x, r), ...).
-  const int total = bt.total_tiles;
-  const int q = total / 8, rem = total % 8;
-  const int x = bid % 8, i = bid / 8;
-  const int id = x * q + (x < rem ? x : rem) + i;
+// Tile coordinates of tile id (problem, then groups of kGroupM tile rows
+// walked column by column, so consecutive ids share operand panels).
+__device__ __forceinline__ TileCoord tile_coord(const GemmBatch& bt, int id, int BM, int BN) {
   TileCoord c;
   c.prob = (bt.count > 1 && id >= bt.p[1].tile_begin) ? 1 : 0;
   const int local = id - (c.prob ? bt.p[1].tile_begin : bt.p[0].tile_begin);
@@ -201,6 +199,19 @@ __device__ __forceinline__ TileCoord decode_tile_id(const GemmBatch& bt, int bid
   c.tm = first_m + in % gm;
   c.tn = in / gm;
   return c;
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8);
+// XCD x gets the contiguous tile-id range [x*q + min(x, r), ...) of
+// xcd_tiles(x) ids, walked by its blocks i = bid / 8 in order.
+__device__ __forceinline__ int xcd_first(int total, int x) {
+  const int q = total / 8, rem = total % 8;
+  return x * q + (x < rem ? x : rem);
+}
+__device__ __forceinline__ int xcd_tiles(int total, int x) { return total / 8 + (x < total % 8 ? 1 : 0); }
+
+__device__ __forceinline__ TileCoord decode_tile_id(const GemmBatch& bt, int bid, int BM, int BN) {
+  return tile_coord(bt, xcd_first(bt.total_tiles, bid % 8) + bid / 8, BM, BN);
 }
 
 __device__ __forceinline__ TileCoord decode_tile(const GemmBatch& bt, int BM, int BN) {
@@ -444,6 +455,58 @@ __device__ __forceinline__ void stage_quarter(const f32x16_t (&acc)[4][4], float
     for (int e = 0; e < 16; ++e) cs[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * 64 + jj * 32 + frow] = acc[Q >> 1][2 * (Q & 1) + jj][e];
 }
 
+// Stream-K hand-over at the staged-quarter level (the wave's quarters Q =
+// 0..7 as stage_quarter lays them out, 2048 floats each, at wave region + Q *
+// 2048 of a block's slot).  A contributor (out set) copies each staged quarter
+// to its slot and writes no output; an owner (nin > 0) adds, in block order,
+// the staged quarters of the contributors whose bit is set in mask, before
+// the epilogue reads them.  Returns true when the quarter's outputs are to be
+// skipped.
+struct SkIo {
+  float* out;          // contributor: this wave's region of the block's slot
+  const float* in;     // owner: this wave's region of the first contributor's slot
+  int nin;             // owner: contributors (consecutive blocks, kGemmSkSlotFloats apart)
+  uint32_t mask;       // owner: contributors whose sums arrived (the others were recomputed here)
+};
+
+// Partial sums cross compute units (and XCDs) through device-coherent
+// accesses: 16-byte buffer stores and loads with the sc1 cache policy (coherent
+// at device scope, so no L2 write-back or invalidate is needed); a
+// contributor's stores have completed (vmcnt) before its flag is raised.
+constexpr int kCpolDevice = 16;   // sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const float* region) {
+  // a wave's 16384-float region of a slot
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(region), 0, 16384 * 4, 0x00020000);
+}
+
+__device__ __forceinline__ bool sk_quarter(float* cs, const SkIo& sk, int Q, int lane) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  float4* c4p = reinterpret_cast<float4*>(cs);
+  if (sk.out) {
+    const __amdgpu_buffer_rsrc_t r = sk_rsrc(sk.out);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, c4p[k * 64 + lane]), r,
+                                             (Q * 512 + k * 64 + lane) * 16, 0, kCpolDevice);
+    return true;
+  }
+  for (int c = 0; c < sk.nin; ++c) {
+    if (!((sk.mask >> c) & 1u)) continue;
+    const __amdgpu_buffer_rsrc_t r = sk_rsrc(sk.in + (int64_t)c * kGemmSkSlotFloats);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(r, (Q * 512 + k * 64 + lane) * 16, 0, kCpolDevice));
+      float4 w = c4p[k * 64 + lane];
+      w.x += v.x; w.y += v.y; w.z += v.z; w.w += v.w;
+      c4p[k * 64 + lane] = w;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the staged quarter is final
+  return false;
+}
+
 // The residual rows (kEpiResid) of the lane's 8 rows rbase + 4u and four
 // columns col..col+3 of a quarter, all loads issued together.
 __device__ __forceinline__ void load_resid(const GemmProblem& pc, int rbase, int col, float4 (&xr)[8]) {
@@ -523,7 +586,7 @@ __device__ __forceinline__ void apply_quarter(const GemmProblem& pc, const float
 // interleaved RoPE pairs (2m, 2m+1) are lane-local.  q and k rows are written
 // head-major, v transposed, all in bf16.
 __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16_t (&acc)[4][4], float* cs,
-                                             int row0, int col0, int lane, float dq) {
+                                             int row0, int col0, int lane, float dq, const SkIo& sk) {
   if (col0 >= pc.N) return;                       // wave-uniform: no columns here
   const QkvOut& q = pc.qkv;
   const int frow = lane & 31, fhalf = lane >> 5;
@@ -574,6 +637,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_sched_barrier(0);
+      if (sk_quarter(cs, sk, Q, lane)) continue;
       const int half = Q & 1, r0 = row0 + (Q >> 1) * 32;
       const float bv = half ? bl1 : bl0;
       const int b0 = r0 < pc.M ? r0 / seg : 0;
@@ -626,6 +690,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
+    const bool skip = sk_quarter(cs, sk, 2 * qq, lane);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float4 t = *reinterpret_cast<const float4*>(&cs[(lrow + 4 * u) * 64 + c4]);
@@ -641,6 +706,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
+    sk_quarter(cs, sk, 2 * qq + 1, lane);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float4 t = *reinterpret_cast<const float4*>(&cs[(lrow + 4 * u) * 64 + c4]);
@@ -648,6 +714,7 @@ __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
+    if (skip) continue;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int row = row0 + qq * 32 + lrow + 4 * u;
@@ -681,13 +748,14 @@ __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16
 
 template <int EPI>
 __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x16_t (&acc)[4][4], float* cs,
-                                              int row0, int col0, int lane, float dq, float qs, uint32_t& mx) {
+                                              int row0, int col0, int lane, float dq, float qs, uint32_t& mx,
+                                              const SkIo& sk = SkIo{}) {
   if constexpr (EPI == kEpiQkv) {
-    qkv_epilogue(pc, acc, cs, row0, col0, lane, dq);
+    qkv_epilogue(pc, acc, cs, row0, col0, lane, dq, sk);
     return;
   } else if constexpr (EPI == kEpiQkvSplitGelu) {
     if (col0 < pc.n_split) {
-      qkv_epilogue(pc, acc, cs, row0, col0, lane, dq);
+      qkv_epilogue(pc, acc, cs, row0, col0, lane, dq, sk);
       return;
     }
   }
@@ -732,7 +800,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes have landed
     __builtin_amdgcn_sched_barrier(0);
-    apply_quarter<E>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + c4, bias0, gate0, uniform, dq, qs, mx, xa);
+    if (!sk_quarter(cs, sk, 2 * qq, lane))
+      apply_quarter<E>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + c4, bias0, gate0, uniform, dq, qs, mx, xa);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next quarter overwrites the staging
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (E == kEpiResid) {
@@ -746,7 +815,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
-    apply_quarter<E>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + 64 + c4, bias1, gate1, uniform, dq, qs, mx,
+    if (!sk_quarter(cs, sk, 2 * qq + 1, lane))
+      apply_quarter<E>(pc, cs, lrow, c4, row0 + qq * 32 + lrow, col0 + 64 + c4, bias1, gate1, uniform, dq, qs, mx,
                        xb);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
@@ -809,8 +879,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
   const char* abase = nullptr;
   const char* wbase_g = nullptr;
   uint32_t soff[16];
-  auto setup = [&](int t) {
-    const TileCoord tc = decode_tile_id(bt, t, BM, BN);
+  auto setup = [&](int id) {   // tile id (see tile_coord)
+    const TileCoord tc = tile_coord(bt, id, BM, BN);
     GemmProblem p = bt.p[0];
     if (tc.prob) p = bt.p[1];
     prob = tc.prob;
@@ -899,47 +969,170 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
     }
   };
 
-  // super-stage 0 whole and loads 0..7 of super-stage 1 of the current tile
-  auto prologue = [&]() {
+  // super-stage s0 whole and loads 0..7 of super-stage s0 + 1 of the current tile
+  auto prologue = [&](int s0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) dma_one(0, u);
+    for (int u = 0; u < 16; ++u) dma_one(s0, u);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dma_one(1, u);
+    for (int u = 0; u < 8; ++u) dma_one(s0 + 1, u);
   };
-
-  int t = blockIdx.x;
-  if (t >= bt.total_tiles) return;
-  setup(t);
-  prologue();
-  for (; t < bt.total_tiles; t += gridDim.x) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // super-stages [s0, s1) of the current tile into acc, the prologue of s0
+  // already issued; on return every load has landed and every wave has read
+  // its last fragments (the LDS slots are free)
+  auto run_stages = [&](int s0, int s1) __attribute__((always_inline)) {
     DL_WAIT_VM(8);
     __syncthreads();
 #pragma unroll
-    for (int n = 0; n < TM + TN; ++n) frag_one(0, 0, 0, n);
-    for (int ss = 0; ss < NS; ++ss) super_stage(ss);
-
-    // all loads of this tile (the clamped ones past its end included) have
-    // landed and every wave has read its last fragments past this barrier;
-    // the next tile's first loads then overlap the epilogue
-    const int cprob = prob, cm0 = m0, cn0 = n0;
+    for (int n = 0; n < TM + TN; ++n) frag_one(s0, 0, 0, n);
+    for (int ss = s0; ss < s1; ++ss) super_stage(ss);
     DL_WAIT_VM(0);
     __syncthreads();
-    if (t + (int)gridDim.x < bt.total_tiles) {
-      setup(t + gridDim.x);
-      prologue();
+  };
+
+  // Work items of this block (block i = blockIdx.x / 8 of XCD x = blockIdx.x %
+  // 8, which owns the tile ids [xcd_first(x), + xcd_tiles(x))): the XCD's
+  // tiles i, i + 32, ... of its data-parallel part, then (stream-K tail,
+  // XCD-local) the block's share [u0, u1) of the units (tile x super-stage) of
+  // the XCD's remaining tiles, split evenly over its 32 blocks: first the
+  // share of a tile it does not finish (contributor: its partial sums go to
+  // its slot), then the end of a tile others began (owner: adds theirs before
+  // the epilogue), then whole tiles.  Every block publishes before it waits,
+  // so an owner only waits for shares that were computed first.  Slots and
+  // flags are indexed x * 32 + i, so an owner's contributors are consecutive.
+  enum { kFull = 0, kContrib = 1, kOwner = 2 };
+  // GX: blocks of this XCD (blocks b with b % 8 == x; all XCDs have 32 in stream-K launches)
+  const int G = gridDim.x, xcd = blockIdx.x % 8, bi = blockIdx.x / 8, GX = (G - xcd + 7) / 8;
+  const int slot = xcd * GX + bi;
+  const bool sk = bt.sk_part != nullptr && bt.sk_units > 0;
+  const int first = xcd_first(bt.total_tiles, xcd), ntx = xcd_tiles(bt.total_tiles, xcd);
+  const int ndx = sk ? min(ntx, (bt.sk_tail / G) * GX) : ntx;   // data-parallel tiles of the XCD
+  const int n_dp = ndx > bi ? (ndx - bi + GX - 1) / GX : 0;
+  int tns = 1;                                    // super-stages per tail tile (one K per split launch)
+  int64_t UX = 0;                                 // tail units of the XCD
+  int jc = -1, sac = 0, sbc = 0, jo = -1, sao = 0, jf0 = 0, jf1 = -1;
+  if (sk) {
+    tns = bt.p[0].K / 64;
+    UX = (int64_t)(ntx - ndx) * tns;
+    const int64_t u0 = (int64_t)bi * UX / GX, u1 = (int64_t)(bi + 1) * UX / GX;
+    if (u1 > u0) {
+      const int j0 = (int)(u0 / tns), j1 = (int)((u1 - 1) / tns);
+      if (u1 < (int64_t)(j1 + 1) * tns) {   // the share ends inside tile j1
+        jc = j1;
+        sac = (int)((u0 > (int64_t)j1 * tns ? u0 : (int64_t)j1 * tns) - (int64_t)j1 * tns);
+        sbc = (int)(u1 - (int64_t)j1 * tns);
+      }
+      if (u0 > (int64_t)j0 * tns && jc != j0) {   // the share begins inside tile j0 and finishes it
+        jo = j0;
+        sao = (int)(u0 - (int64_t)j0 * tns);
+      }
+      jf0 = u0 > (int64_t)j0 * tns ? j0 + 1 : j0;
+      jf1 = jc == j1 ? j1 - 1 : j1;
+    }
+  }
+  const int tail0 = first + ndx;                  // tile id of tail tile 0 of the XCD
+  const int n_c = jc >= 0 ? 1 : 0, n_o = jo >= 0 ? 1 : 0, n_f = jf1 >= jf0 ? jf1 - jf0 + 1 : 0;
+  const int n_items = n_dp + n_c + n_o + n_f;
+  struct Item { int tile, s0, s1, kind; };
+  auto item = [&](int i) __attribute__((always_inline)) {
+    Item it;
+    if (i < n_dp) {
+      it.tile = first + bi + i * GX; it.s0 = 0; it.s1 = -1; it.kind = kFull;   // s1 = -1: all super-stages
+      return it;
+    }
+    i -= n_dp;
+    if (i < n_c) { it.tile = tail0 + jc; it.s0 = sac; it.s1 = sbc; it.kind = kContrib; return it; }
+    i -= n_c;
+    if (i < n_o) { it.tile = tail0 + jo; it.s0 = sao; it.s1 = -1; it.kind = kOwner; return it; }
+    i -= n_o;
+    it.tile = tail0 + jf0 + i; it.s0 = 0; it.s1 = -1; it.kind = kFull;
+    return it;
+  };
+  // The owner of tail tile jo takes the shares of blocks b' < b that cover its
+  // super-stages [0, sao): consecutive blocks bf..bl (every block holds at
+  // least one unit).  It waits for their flags; a share that has not arrived
+  // after sk_spin polls is computed here into acc instead, so the wait always
+  // ends.  The arrived shares are added in block order at the staged-quarter
+  // level of the epilogue (SkIo).
+  // (the block-wide word lives in the epilogue staging area, free while an
+  // owner waits: every wave has finished the previous epilogue)
+  int* arrived = reinterpret_cast<int*>(smem + 2 * kSsBytes);
+  auto owner_wait = [&](SkIo& io) __attribute__((always_inline)) {
+    const int64_t U = UX;
+    const int64_t t0 = (int64_t)jo * tns;
+    // XCD-local block holding unit u: the largest i' with floor(i' U / GX) <= u
+    auto block_of = [&](int64_t u) { return (int)(((u + 1) * GX + U - 1) / U - 1); };
+    const int bf = block_of(t0), bl = block_of(t0 + sao - 1);
+    const int spin = bt.sk_spin > 0 ? bt.sk_spin : (1 << 20);
+    uint32_t mask = 0;
+    for (int c = bf; c <= bl; ++c) {
+      const int64_t cu0 = (int64_t)c * U / GX, cu1 = (int64_t)(c + 1) * U / GX;
+      const int c0 = (int)((cu0 > t0 ? cu0 : t0) - t0), c1 = (int)((cu1 < t0 + sao ? cu1 : t0 + sao) - t0);
+      if (c1 <= c0) continue;   // block c holds none of these super-stages
+      if (tid == 0) {
+        int n = 0;
+        while (__hip_atomic_load(bt.sk_flag + xcd * GX + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+               n < spin) {
+          __builtin_amdgcn_s_sleep(2);
+          ++n;
+        }
+        *arrived = __hip_atomic_load(bt.sk_flag + xcd * GX + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      const bool got = *arrived != 0;
+      __syncthreads();
+      if (got) {
+        mask |= 1u << (c - bf);
+      } else {
+        prologue(c0);
+        run_stages(c0, c1);
+      }
+    }
+    io.in = bt.sk_part + (int64_t)(xcd * GX + bf) * kGemmSkSlotFloats + (int64_t)wave * 16384;
+    io.nin = bl - bf + 1;
+    io.mask = mask;
+  };
+
+  if (n_items == 0) return;
+  Item cur = item(0);
+  setup(cur.tile);
+  prologue(cur.s0);
+  for (int i = 0; i < n_items; ++i) {
+#pragma unroll
+    for (int ii = 0; ii < TM; ++ii)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[ii][j][e] = 0.f;
+    run_stages(cur.s0, cur.s1 < 0 ? NS : cur.s1);
+    SkIo io{};
+    if (cur.kind == kOwner) owner_wait(io);
+    if (cur.kind == kContrib) io.out = bt.sk_part + (int64_t)slot * kGemmSkSlotFloats + (int64_t)wave * 16384;
+    // all loads of this item have landed and every wave has read its last
+    // fragments; the next item's first loads then overlap the epilogue
+    const int cprob = prob, cm0 = m0, cn0 = n0;
+    const int ckind = cur.kind;
+    if (i + 1 < n_items) {
+      cur = item(i + 1);
+      setup(cur.tile);
+      prologue(cur.s0);
     }
     GemmProblem pc = bt.p[0];
     if (cprob) pc = bt.p[1];
     uint32_t mx = 0;
     tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 2 * kSsBytes) + wave * 32 * 64,
-                       cm0 + wm * WM, cn0 + wn * WN, lane, 1.0f, 1.0f, mx);
+                       cm0 + wm * WM, cn0 + wn * WN, lane, 1.0f, 1.0f, mx, io);
+    if (ckind == kContrib) {
+      // every wave's device-coherent stores have completed before the flag is raised
+      DL_WAIT_VM(0);
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(bt.sk_flag + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+}
+
+// Zero the stream-K flags of one launch (a kernel, so the launch can be captured).
+__global__ void sk_clear_kernel(int32_t* flag, int n) {
+  if ((int)threadIdx.x < n) flag[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1391,6 +1584,20 @@ bool gemm_is_persistent(const GemmBatch& bt, int op) {
   return persistent_ok(bt, op);
 }
 
+// Stream-K setting of the persistent 16-bit GEMM (flux_gemm_stream_k): off by
+// default, since at the 12B block shapes the owners' waits for the partial
+// sums cost more than the balanced tail gains; the spin limit of an owner's
+// wait (0: the kernel's default).
+static std::atomic<int> g_sk_mode{0};
+static std::atomic<int> g_sk_spin{0};
+
+int gemm_stream_k(int mode, int spin) {
+  const int prev = g_sk_mode.load();
+  if (mode >= 0) g_sk_mode.store(mode ? 1 : 0);
+  g_sk_spin.store(spin > 0 ? spin : 0);
+  return prev;
+}
+
 template <int OP>
 static hipError_t launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   bt.ksplit = 1;
@@ -1398,7 +1605,27 @@ static hipError_t launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
   const int tiles_big = assign_tiles(big, 256, 256);
   const int epi = big.p[0].epi;   // the problems of one launch share the epilogue kind
   if (persistent_ok(big, OP)) {
-    const int grid = tiles_big < 256 ? tiles_big : 256;
+    int grid = tiles_big < 256 ? tiles_big : 256;
+    // stream-K tail (16-bit operands, problems of one K, a workspace given):
+    // the tiles past the last full round of 256 are shared out along K over
+    // all 256 blocks when there are at least 64 of them (so a tile has at most
+    // five shares and every block at least one super-stage)
+    big.sk_tail = tiles_big;
+    big.sk_units = 0;
+    if constexpr (OP == kBF16 || OP == kF16 || OP == kF16W) {
+      bool same_k = true;
+      for (int i = 1; i < big.count; ++i) same_k = same_k && big.p[i].K == big.p[0].K;
+      const int full = (tiles_big / kGemmSkMaxGrid) * kGemmSkMaxGrid, rest = tiles_big - full;
+      const int64_t units = (int64_t)rest * (big.p[0].K / 64);
+      if (g_sk_mode.load() && big.sk_part && big.sk_flag && same_k && rest >= 64 && units >= kGemmSkMaxGrid &&
+          units < (int64_t(1) << 30)) {
+        grid = kGemmSkMaxGrid;
+        big.sk_tail = full;
+        big.sk_units = (int32_t)units;
+        big.sk_spin = g_sk_spin.load();
+        hipLaunchKernelGGL(sk_clear_kernel, dim3(1), dim3(kGemmSkMaxGrid), 0, stream, big.sk_flag, kGemmSkMaxGrid);
+      }
+    }
     TimingScope ts(OP == kFP8 ? kKcGemmPkFp8 : OP == kBF16 ? kKcGemmPkBf16 : kKcGemmPkF16, stream, flops);
     switch (epi) {
       case kEpiStore: launch_persistent<OP, kEpiStore>(big, grid, stream); break;

@@ -96,10 +96,27 @@ struct GemmBatch {
   // with tiles: [kGemmMaxSplit, M, N] fp32 partial sums (null: no split).
   float* partials;
   int32_t ksplit;   // filled by the launcher
+  // Stream-K tail of the persistent 16-bit kernel (sk_part null: off).  The
+  // tiles past the grid's last full round are cut along K into equal shares
+  // of super-stages, one contiguous share per block; a block hands the part
+  // of a tile it does not finish to the block that does, through sk_part
+  // (kGemmSkSlotFloats fp32 per block) and sk_flag (one int per block, zeroed
+  // by the launcher before each launch).  Needs kGemmSkMaxGrid slots.
+  float* sk_part;
+  int32_t* sk_flag;
+  int32_t sk_tail;    // filled by the launcher: first tile of the tail
+  int32_t sk_units;   // filled by the launcher: tail tiles x super-stages (0: no tail split)
+  int32_t sk_spin;    // polls an owner waits for a share before computing it itself (0: default)
 };
 constexpr int kGemmMaxSplit = 8;
+constexpr int kGemmSkMaxGrid = 256;
+constexpr int64_t kGemmSkSlotFloats = 256 * 256;
+constexpr int64_t kGemmSkBytes = kGemmSkMaxGrid * kGemmSkSlotFloats * 4 + 1024;   // partials + flags
 
 hipError_t launch_gemm(GemmBatch batch, int op, hipStream_t stream);
+// Stream-K tail of the persistent 16-bit GEMM: mode 1 on, 0 off, < 0 leave;
+// spin > 0 sets the owner's poll limit (0: default).  Returns the previous mode.
+int gemm_stream_k(int mode, int spin);
 // True when launch_gemm runs this batch (16-bit or E4M3 operands) on the
 // persistent 256 x 256 kernel, the only one with the kEpiQkv epilogues.
 bool gemm_is_persistent(const GemmBatch& batch, int op);

@@ -48,7 +48,7 @@ EXPORTED = (
     "flux_attention_fp8_workspace_bytes", "flux_attention_fp8_fwd", "flux_mxfp4_scale_bytes", "flux_mxfp4_quantize",
     "flux_mxfp4_linear_fwd", "flux_fp8_block_quantize", "flux_timestep_embed", "rf_noise_loss_noalloc",
     "flux_rf_noalloc_max_partials", "flux_timing_flush", "flux_stream_copy", "flux_debug_checks",
-    "flux_debug_status",
+    "flux_debug_status", "flux_gemm_stream_k",
 )
 
 
@@ -145,6 +145,7 @@ def lib() -> C.CDLL:
         "flux_timing_flush": [vp, i64],
         "flux_stream_copy": [vp, vp, i64, vp],
         "flux_debug_checks": [i32],
+        "flux_gemm_stream_k": [i32, i32],
         "flux_debug_status": [P(C.c_uint32), i32],
         "flux_rope_table": [vp, i32, i32, P(C.c_int32), f32, vp, vp],
         "flux_embed_fwd": [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P(flux_embed_weights), vp, vp, vp, vp,
@@ -527,6 +528,12 @@ def flux_timing_flush(buffer=None, nbytes: int = 0) -> None:
 
 def flux_stream_copy(src, dst, nbytes: int, stream=None) -> None:
     _check(lib().flux_stream_copy(ptr(src), ptr(dst), nbytes, _stream(stream)), "flux_stream_copy")
+
+
+def flux_gemm_stream_k(on: Optional[bool] = None, spin: int = 0) -> bool:
+    """Stream-K tail of the block linears on / off (None: leave) and the owner's
+    poll limit (0: default); returns the previous setting."""
+    return bool(lib().flux_gemm_stream_k(-1 if on is None else (1 if on else 0), spin))
 
 
 # device checks (status word bits)

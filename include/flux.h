@@ -179,7 +179,10 @@ typedef struct {
  *  rope  [B, L, head_dim/2, 2] float (cos, sin) per token and pair, image
  *        rows first, as written by flux_rope_table.
  *  workspace  device scratch of at least flux_workspace_bytes(dims, 0) bytes,
- *        256-byte aligned; its content on entry is ignored.
+ *        256-byte aligned; its content on entry is ignored.  With
+ *        FLUX_PREC_BF16 it includes a 64 MB stream-K area (see
+ *        flux_gemm_stream_k); calls that run at the same time need workspaces
+ *        of their own.
  */
 flux_status flux_block_fwd(const flux_dims* dims, const flux_stream_weights* img_w,
                            const flux_stream_weights* txt_w, float* img, int64_t img_bstride,
@@ -785,6 +788,28 @@ flux_status flux_stream_copy(const void* src, void* dst, int64_t bytes, void* st
 #define FLUX_DBG_NONFINITE_GRAD 16u
 int32_t flux_debug_checks(int32_t on);
 flux_status flux_debug_status(uint32_t* status, int32_t clear);
+
+/*
+ * Stream-K tail of the block linears (16-bit workloads, off by default).  A
+ * persistent GEMM launch covers its 256 x 256 output tiles in rounds of 256
+ * (one block per compute unit); when the last round is partial (64 tiles or
+ * more), the K range of its tiles is shared out evenly over all 256 blocks
+ * instead.  A block that computes only part of a tile's K range writes its
+ * fp32 partial sums to the stream-K area of the block workspace and raises a
+ * flag; the block that finishes the tile adds them, in a fixed order, before
+ * the epilogue, so results are bitwise repeatable (they differ from the
+ * whole-tile order only by rounding).  If a partial has not arrived after
+ * `spin` polls, the finishing block computes that K range itself, so a launch
+ * always completes.
+ *
+ * flux_gemm_stream_k -- mode 1 on, 0 off, a negative value leaves the
+ *   setting; spin > 0 sets the poll limit, 0 restores the default.  Returns
+ *   the mode before the call.  Process-wide; meant for tuning and tests.
+ *   Off by default: on the 12B block linears the tail split alone would save
+ *   at most about 3% of the block time, and the finishing blocks' waits for
+ *   the partial sums cost more than that.
+ */
+int32_t flux_gemm_stream_k(int32_t mode, int32_t spin);
 
 /* Static text for a status code; thread-local detail of the last failure on
  * this thread ("" when none). */

@@ -459,3 +459,69 @@ def test_fused_qkv_epilogue_single_block_padded(padded_case):
     g = _run_pair(wl, w2, w1, inp, ids, "single", True)
     ri, rt = _sample_rows(wl, 4)
     _check_single(wl, w1, inp, ids, g, rows=np.r_[ri, wl.l_img + rt])
+
+
+def test_fp16_activation_store_saturates():
+    """fp16 activation stores saturate at +-65504 instead of overflowing to
+    infinity: the output head's LayerNorm-modulate output (an fp16 operand of
+    the output linear) with scale = 999424 reaches |h| ~ 1e6.  The reference
+    clips h at 65504, rounds it to fp16 and applies the linear in float64."""
+    _say("output head with |LayerNorm-modulate output| far beyond fp16's range (saturating fp16 store)")
+    rng = np.random.default_rng(65504)
+    B, C, H, W, D, eps = 1, 64, 4, 4, 256, 1e-6
+    HW = H * W
+    x = rng.standard_normal((B, HW, D)).astype(np.float32)
+    vec = rng.standard_normal((B, D)).astype(np.float32)
+    mod_w = np.zeros((2 * D, D), np.float32)
+    mod_b = np.concatenate([np.zeros(D), np.full(D, 999424.0)]).astype(np.float32)   # shift 0, scale 999424 (bf16-exact)
+    out_w = synth.round_to_bf16((0.02 * rng.standard_normal((C, D))).astype(np.float32))
+    out_b = np.zeros(C, np.float32)
+    f = F()
+    v = torch.empty((B, C, H, W), device="cuda")
+    wsb = f.flux_final_workspace_bytes(f.FLUX_PREC_BF16, B, H, W, D)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    f.flux_final_fwd(f.FLUX_PREC_BF16, B, C, H, W, D, eps, dev(mod_w, True), dev(mod_b, True), dev(out_w, True),
+                     dev(out_b, True), dev(x), HW * D, dev(vec), v, ws, wsb)
+    torch.cuda.synchronize()
+    got = v.cpu().numpy()
+    xd = x.astype(np.float64)
+    mu = xd.mean(-1, keepdims=True)
+    var = ((xd - mu) ** 2).mean(-1, keepdims=True)
+    h = (xd - mu) / np.sqrt(var + eps) * (1.0 + 999424.0)
+    assert np.abs(h).max() > 1e5          # far beyond fp16's largest finite value
+    h16 = np.clip(h, -65504.0, 65504.0).astype(np.float16).astype(np.float64)
+    tok = h16 @ out_w.astype(np.float64).T
+    ref = tok.reshape(B, H, W, C).transpose(0, 3, 1, 2)
+    assert np.isfinite(got).all(), "an fp16 activation overflowed"
+    assert_close(got, ref, "v_pred with saturated activations", max_abs=1e-3 * np.abs(ref).max(), rel=1e-3)
+
+
+@pytest.mark.slow
+def test_stream_k_tail_matches_whole_tiles_and_repeats(big_case):
+    """Stream-K tail of the block linears (qkv 648 tiles, fc1 864, proj / fc2
+    216 per launch at L=4608): two runs are bitwise equal; the outputs agree
+    with the whole-tile path (stream-K off) to rounding; with a poll limit of
+    one the finishing blocks compute late shares themselves and the result
+    still agrees.  The oracle check of the same block is
+    test_double_block_flux12b_shapes_sampled."""
+    wl, w2, w1, inp, ids = big_case
+    f = F()
+    _say("stream-K tail: double + single block at L=4608, repeatability, whole-tile and fallback agreement")
+    prev = f.flux_gemm_stream_k(True)
+    try:
+        for which in ("double", "single"):
+            a = _run_pair(wl, w2, w1, inp, ids, which, True)
+            b = _run_pair(wl, w2, w1, inp, ids, which, True)
+            assert np.array_equal(a, b), f"{which}: stream-K run is not bitwise repeatable"
+            f.flux_gemm_stream_k(False)
+            c = _run_pair(wl, w2, w1, inp, ids, which, True)
+            f.flux_gemm_stream_k(True, spin=1)
+            d = _run_pair(wl, w2, w1, inp, ids, which, True)
+            f.flux_gemm_stream_k(True, spin=0)
+            x0 = np.concatenate([inp["x_img"], inp["x_txt"]], axis=1)
+            for name, o in (("whole tiles", c), ("poll limit 1", d)):
+                # compare the block's update (output - input): every element of it
+                # went through the linears
+                assert_close(a - x0, o - x0, f"{which}: stream-K vs {name}", max_abs=1e-2, rel=1e-3)
+    finally:
+        f.flux_gemm_stream_k(prev, spin=0)
