@@ -13,9 +13,9 @@
 // from L2.
 //  * large problems: gemm_dl_kernel, persistent (one 256-thread block per CU),
 //    256 x 256 tiles; operands loaded global -> LDS directly in k = 64
-//    super-stages (two 64 KB LDS slots), MFMA fragment reads and loads
-//    interleaved one-by-one with the MFMAs; the next tile's first loads
-//    overlap the current epilogue;
+//    super-stages (a ring of five 32 KB operand halves), MFMA fragment reads
+//    and loads interleaved one-by-one with the MFMAs; the next tile's first
+//    loads overlap the current epilogue;
 //  * small problems: gemm_mfma_kernel, 128 x 128 tiles, register-staged
 //    double buffer.
 // fp32 path (fp32 workloads only): LDS-tiled FMA kernel with the same epilogues.
@@ -831,26 +831,45 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
 // one whole 128-byte line of a row (64-byte row pieces left the kernel bound
 // by L1 -> L2 requests; staging through VGPRs with ds_write cost more waits
 // and LDS instructions than the direct path, measured on MI355X).
-//  * LDS: two super-stage slots of 64 KB (A rows 0..255 then W rows, 128
-//    bytes each, chunk c of row r at physical chunk c ^ ((r >> 1) & 7)) plus
-//    32 KB for the epilogue staging.  gfx950 serves a 16-byte-per-lane LDS
-//    read in four cycles of 16 lanes, the lanes of a cycle having equal lane
-//    bit 5 and equal (bit 4 xor bit 2) (measured with the bank-conflict
-//    counter); under that grouping the fragment reads of this layout hit each
-//    4-bank group once per cycle.
+//  * LDS: a ring of five 32 KB slots, each holding one operand half of a
+//    super-stage (A rows 0..255 or W rows 0..255, 128 bytes each, chunk c of
+//    row r at physical chunk c ^ ((r >> 1) & 7)); slot 4 doubles as the
+//    epilogue staging, which runs while no load targets it.  gfx950 serves
+//    a 16-byte-per-lane LDS read in four cycles of 16 lanes, the lanes of a
+//    cycle having equal lane bit 5 and equal (bit 4 xor bit 2) (measured
+//    with the bank-conflict counter); under that grouping the fragment reads
+//    of this layout hit each 4-bank group once per cycle.
 //  * A super-stage is 4 slices of 16 MFMAs per wave (k = 16 each); the
 //    fragments of slice n + 1 are read during slice n.  One barrier per
-//    super-stage, between slices 2 and 3: after it the slot of super-stage
-//    sigma (last read in slice 2) takes super-stage sigma + 2, and slice 3
-//    reads the first fragments of sigma + 1, whose loads the barrier waited
-//    for.  Loads of sigma + 1 are spread over slice 3 of sigma - 1 and slices
-//    0-1 of sigma, one per MFMA or every other MFMA (scheduling fences).
-//  * The next tile's first 1.5 super-stages are loaded while the epilogue of
-//    the current tile runs (its staging area is a separate slot).
+//    super-stage, between slices 2 and 3, before slice 3 reads the first
+//    fragments of the next super-stage.  With five halves in the ring the A
+//    half of super-stage j + 2 loads during slices 0-1 of j and its W half
+//    during slice 3 of j, so each load has three to seven slices (0.8 to
+//    1.8 us) to land before the barrier that waits for it; with two whole
+//    64 KB slots, the W half had one to two slices and the waits for it cost
+//    about 15 % of the kernel (measured on MI355X).  The barrier waits only
+//    for the loads it needs (s_waitcnt vmcnt(8): the A half of j + 2 stays
+//    in flight); __syncthreads() would wait for all of them.
+//  * The next tile's first two super-stages are loaded while the epilogue
+//    of the current tile runs (in slots 0-3).
 //  * Operand rows are addressed as 32-bit byte offsets from the tile's A and
 //    W base pointers (the launcher keeps both spans under 4 GiB).
 // ---------------------------------------------------------------------------
-constexpr int kSsBytes = 2 * kDlStageBytes;   // one super-stage: 64 KB
+// Block barrier of an LDS ring fed by direct global->LDS loads: the wave's
+// own LDS accesses are complete before it arrives, global loads stay in
+// flight.  __syncthreads() would also wait for every outstanding global load
+// (its workgroup fences imply s_waitcnt vmcnt(0)), i.e. for the operands
+// still being prefetched; the caller bounds those with a counted vmcnt wait
+// first.  The asm statements keep the compiler from moving memory accesses
+// across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kHalf = 32768;   // one operand (A or W) of a super-stage: 256 rows x 128 bytes
+constexpr int kHalfSlots = 5;  // LDS ring of operand halves; slot 4 doubles as the epilogue staging
 
 // 128-byte rows (k = 64), chunk c of row r at physical chunk c ^ ((r >> 1) & 7)
 __device__ __forceinline__ int ss_swz(int r) { return (r >> 1) & 7; }
@@ -858,27 +877,28 @@ __device__ __forceinline__ int ss_swz(int r) { return (r >> 1) & 7; }
 template <int OP, int EPI>
 __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kSsBytes + kDlStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kHalfSlots * kHalf];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int frow = lane & 31, fhalf = lane >> 5;
   const int fs = ss_swz(frow);   // swizzle of every fragment row of this lane
-  // fragment offsets (slice sl: k16 step, chunks 2 sl + fhalf)
+  // fragment offsets in an operand half (slice sl: k16 step, chunks 2 sl + fhalf)
   int aoff[4], boff[4];
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl) {
     aoff[sl] = (wm * WM + frow) * 128 + (((2 * sl + fhalf) ^ fs) << 4);
-    boff[sl] = (kDlRows + wn * WN + frow) * 128 + (((2 * sl + fhalf) ^ fs) << 4);
+    boff[sl] = (wn * WN + frow) * 128 + (((2 * sl + fhalf) ^ fs) << 4);
   }
-  // direct load u (0..15) of this wave: LDS rows (wave + 4u) * 8 .. + 7, lane
-  // l at row + l / 8, physical chunk l % 8 = logical chunk (l % 8) ^ swz
+  // direct load u (0..7) of an operand half by this wave: LDS rows (wave +
+  // 4u) * 8 .. + 7, lane l at row + l / 8, physical chunk l % 8 = logical
+  // chunk (l % 8) ^ swz
   const int lrow8 = lane >> 3;
   const int lchunk = (lane & 7) ^ ss_swz(wave * 8 + lrow8);   // swz(row) does not depend on u
 
-  int prob = 0, m0 = 0, n0 = 0, NS = 0;
+  int prob = 0, m0 = 0, n0 = 0, NS = 0;   // NS: k128 units of the tile (two super-stages each)
   const char* abase = nullptr;
   const char* wbase_g = nullptr;
-  uint32_t soff[16];
+  uint32_t soff[16];   // 0..7 A rows, 8..15 W rows
   auto setup = [&](int id) {   // tile id (see tile_coord)
     const TileCoord tc = tile_coord(bt, id, BM, BN);
     GemmProblem p = bt.p[0];
@@ -886,7 +906,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
     prob = tc.prob;
     m0 = tc.tm * BM;
     n0 = tc.tn * BN;
-    NS = p.K / 64;
+    NS = p.K / 128;
     abase = reinterpret_cast<const char*>(p.A);
     wbase_g = reinterpret_cast<const char*>(p.W);
 #pragma unroll
@@ -904,21 +924,24 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
       }
     }
   };
-  auto dma_one = [&](int ss, int u) {
-    const int k = ss < NS ? ss : NS - 1;
-    const char* g = (u < 8 ? abase : wbase_g) + (int64_t)k * 128 + soff[u];
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)(smem + (ss & 1) * kSsBytes + (wave + 4 * u) * 1024),
-                                     16, 0, 0);
+  // Operand halves in the ring: half h = 2 ss (A of super-stage ss) or 2 ss +
+  // 1 (W of ss), counted from the first super-stage of the current range,
+  // lives in slot h % 5.
+  auto slot_of = [&](int h) { return smem + (h % kHalfSlots) * kHalf; };
+  // load u (0..7) of half h (super-stage ss of the tile, W when w)
+  auto dma_one = [&](int h, int ss, bool w, int u) {
+    const char* g = (w ? wbase_g : abase) + (int64_t)ss * 128 + soff[(w ? 8 : 0) + u];
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)(slot_of(h) + ((wave + 4 * u) & 31) * 1024), 16, 0, 0);
   };
 
   f32x16_t acc[TM][TN];
   u32x4_t af[2][TM], bfr[2][TN], bcv[TN];
-  auto frag_one = [&](int ss, int sl, int s, int n) {
-    const char* st = smem + (ss & 1) * kSsBytes;
+  // fragment n (0..3 A, 4..7 W) of slice sl of local super-stage j into set s
+  auto frag_one = [&](int j, int sl, int s, int n) {
     if (n < TM)
-      af[s][n] = *reinterpret_cast<const u32x4_t*>(st + aoff[sl] + n * 32 * 128);
+      af[s][n] = *reinterpret_cast<const u32x4_t*>(slot_of(2 * j) + aoff[sl] + n * 32 * 128);
     else
-      bfr[s][n - TM] = *reinterpret_cast<const u32x4_t*>(st + boff[sl] + (n - TM) * 32 * 128);
+      bfr[s][n - TM] = *reinterpret_cast<const u32x4_t*>(slot_of(2 * j + 1) + boff[sl] + (n - TM) * 32 * 128);
   };
   auto mfma_one = [&](int s, int idx) {
     const int j = idx >> 2, i = idx & 3;
@@ -934,65 +957,90 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[s][i]),
                                                          __builtin_bit_cast(bf16x8_t, bcv[j]), acc[i][j], 0, 0, 0);
   };
-  // super-stage ss: slices 0..3; loads of ss + 2 go into slot ss % 2 after
-  // the barrier (its last reads are in slice 2); the barrier waits for all
-  // loads of ss + 1 (issued during the previous super-stage)
-  auto super_stage = [&](int ss) {
+  // Super-stage j of the range (tile super-stage ss0 + j): slices 0..3 of 16
+  // MFMAs, the fragments of slice n + 1 read during slice n.  ISSUE: the A
+  // half of j + 2 loads during slices 0-1, at every other MFMA (into the slot
+  // of W of j - 1, free since the previous barrier), and its W half during
+  // slice 3, one load per MFMA (into the slot of A of j, free after this
+  // super-stage's barrier); denser load issue stalls the wave's MFMAs.  NEXT: the barrier
+  // between slices 2 and 3 waits until j + 1 has landed for every wave (VM:
+  // loads left in flight, those of A of j + 2), and slice 3 reads the first
+  // fragments of j + 1.  Flags are compile-time, so the k loop has no branches.
+  auto super_stage = [&](int j, int ss0, auto issue, auto vm, auto next) __attribute__((always_inline)) {
+    constexpr bool ISSUE = decltype(issue)::value, NEXT = decltype(next)::value;
+    constexpr int VM = decltype(vm)::value;
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       mfma_one(0, idx);
-      if (idx < 8) frag_one(ss, 1, 1, idx);
-      else if ((idx & 1) == 0) dma_one(ss + 1, 8 + ((idx - 8) >> 1));   // loads 8..11 of ss + 1
+      if (idx < 8) frag_one(j, 1, 1, idx);
+      else if (ISSUE && (idx & 1) == 0) dma_one(2 * j + 4, ss0 + j + 2, false, (idx - 8) >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       mfma_one(1, idx);
-      if (idx < 8) frag_one(ss, 2, 0, idx);
-      else if ((idx & 1) == 0) dma_one(ss + 1, 12 + ((idx - 8) >> 1));  // loads 12..15 of ss + 1
+      if (idx < 8) frag_one(j, 2, 0, idx);
+      else if (ISSUE && (idx & 1) == 0) dma_one(2 * j + 4, ss0 + j + 2, false, 4 + ((idx - 8) >> 1));
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       mfma_one(0, idx);
-      if (idx < 8) frag_one(ss, 3, 1, idx);
+      if (idx < 8) frag_one(j, 3, 1, idx);
       __builtin_amdgcn_sched_barrier(0);
     }
-    DL_WAIT_VM(0);
-    __syncthreads();
+    if constexpr (NEXT) {
+      if constexpr (VM == 8) DL_WAIT_VM(8);
+      else DL_WAIT_VM(0);
+      lds_barrier();
+    }
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       mfma_one(1, idx);
-      if (idx < 8) frag_one(ss + 1, 0, 0, idx);
-      else dma_one(ss + 2, idx - 8);                                        // loads 0..7 of ss + 2
+      if (NEXT && idx < 8) frag_one(j + 1, 0, 0, idx);
+      else if (ISSUE && idx >= 8) dma_one(2 * j + 5, ss0 + j + 2, true, idx - 8);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using V8 = std::integral_constant<int, 8>;
+  using V0 = std::integral_constant<int, 0>;
 
-  // super-stage s0 whole and loads 0..7 of super-stage s0 + 1 of the current tile
-  auto prologue = [&](int s0) __attribute__((always_inline)) {
+  // The first two super-stages (A, W, A, W halves 0..3) of the range of k128
+  // units starting at u0 of the current tile.
+  auto prologue = [&](int u0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) dma_one(s0, u);
+    for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dma_one(s0 + 1, u);
+      for (int u = 0; u < 8; ++u) dma_one(h, 2 * u0 + (h >> 1), (h & 1) != 0, u);
   };
-  // super-stages [s0, s1) of the current tile into acc, the prologue of s0
-  // already issued; on return every load has landed and every wave has read
-  // its last fragments (the LDS slots are free)
-  auto run_stages = [&](int s0, int s1) __attribute__((always_inline)) {
-    DL_WAIT_VM(8);
-    __syncthreads();
+  // k128 units [u0, u1) of the current tile into acc, the prologue of u0
+  // already issued (settled: no other global memory operation was issued
+  // after it, so the wait for super-stage 0 may leave super-stage 1 in
+  // flight); on return every load has landed and every wave has read its
+  // last fragments (the ring and the staging slot are free).  A range has at
+  // least two super-stages, so it always ends in the same straight-line
+  // drain (a branch between drains of different length makes the register
+  // allocator spill the accumulators).
+  auto run_stages = [&](int u0, int u1, bool settled) __attribute__((always_inline)) {
+    const int ss0 = 2 * u0, n = 2 * (u1 - u0);
+    if (settled) DL_WAIT_VM(16);
+    else DL_WAIT_VM(0);
+    lds_barrier();
 #pragma unroll
-    for (int n = 0; n < TM + TN; ++n) frag_one(s0, 0, 0, n);
-    for (int ss = s0; ss < s1; ++ss) super_stage(ss);
-    DL_WAIT_VM(0);
+    for (int m = 0; m < TM + TN; ++m) frag_one(0, 0, 0, m);
+    int j = 0;
+    for (; j + 2 < n; ++j) super_stage(j, ss0, T_{}, V8{}, T_{});
+    super_stage(j, ss0, F_{}, V0{}, T_{});
+    super_stage(j + 1, ss0, F_{}, V0{}, F_{});
     __syncthreads();
   };
 
   // Work items of this block (block i = blockIdx.x / 8 of XCD x = blockIdx.x %
   // 8, which owns the tile ids [xcd_first(x), + xcd_tiles(x))): the XCD's
   // tiles i, i + 32, ... of its data-parallel part, then (stream-K tail,
-  // XCD-local) the block's share [u0, u1) of the units (tile x super-stage) of
+  // XCD-local) the block's share [u0, u1) of the units (tile x k128 unit) of
   // the XCD's remaining tiles, split evenly over its 32 blocks: first the
   // share of a tile it does not finish (contributor: its partial sums go to
   // its slot), then the end of a tile others began (owner: adds theirs before
@@ -1007,11 +1055,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
   const int first = xcd_first(bt.total_tiles, xcd), ntx = xcd_tiles(bt.total_tiles, xcd);
   const int ndx = sk ? min(ntx, (bt.sk_tail / G) * GX) : ntx;   // data-parallel tiles of the XCD
   const int n_dp = ndx > bi ? (ndx - bi + GX - 1) / GX : 0;
-  int tns = 1;                                    // super-stages per tail tile (one K per split launch)
+  int tns = 1;                                    // k128 units per tail tile (one K per split launch)
   int64_t UX = 0;                                 // tail units of the XCD
   int jc = -1, sac = 0, sbc = 0, jo = -1, sao = 0, jf0 = 0, jf1 = -1;
   if (sk) {
-    tns = bt.p[0].K / 64;
+    tns = bt.p[0].K / 128;
     UX = (int64_t)(ntx - ndx) * tns;
     const int64_t u0 = (int64_t)bi * UX / GX, u1 = (int64_t)(bi + 1) * UX / GX;
     if (u1 > u0) {
@@ -1036,7 +1084,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
   auto item = [&](int i) __attribute__((always_inline)) {
     Item it;
     if (i < n_dp) {
-      it.tile = first + bi + i * GX; it.s0 = 0; it.s1 = -1; it.kind = kFull;   // s1 = -1: all super-stages
+      it.tile = first + bi + i * GX; it.s0 = 0; it.s1 = -1; it.kind = kFull;   // s1 = -1: all k units
       return it;
     }
     i -= n_dp;
@@ -1048,14 +1096,14 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
     return it;
   };
   // The owner of tail tile jo takes the shares of blocks b' < b that cover its
-  // super-stages [0, sao): consecutive blocks bf..bl (every block holds at
+  // k units [0, sao): consecutive blocks bf..bl (every block holds at
   // least one unit).  It waits for their flags; a share that has not arrived
   // after sk_spin polls is computed here into acc instead, so the wait always
   // ends.  The arrived shares are added in block order at the staged-quarter
   // level of the epilogue (SkIo).
   // (the block-wide word lives in the epilogue staging area, free while an
   // owner waits: every wave has finished the previous epilogue)
-  int* arrived = reinterpret_cast<int*>(smem + 2 * kSsBytes);
+  int* arrived = reinterpret_cast<int*>(smem + 4 * kHalf);
   auto owner_wait = [&](SkIo& io) __attribute__((always_inline)) {
     const int64_t U = UX;
     const int64_t t0 = (int64_t)jo * tns;
@@ -1067,7 +1115,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
     for (int c = bf; c <= bl; ++c) {
       const int64_t cu0 = (int64_t)c * U / GX, cu1 = (int64_t)(c + 1) * U / GX;
       const int c0 = (int)((cu0 > t0 ? cu0 : t0) - t0), c1 = (int)((cu1 < t0 + sao ? cu1 : t0 + sao) - t0);
-      if (c1 <= c0) continue;   // block c holds none of these super-stages
+      if (c1 <= c0) continue;   // block c holds none of these units
       if (tid == 0) {
         int n = 0;
         while (__hip_atomic_load(bt.sk_flag + xcd * GX + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
@@ -1084,7 +1132,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
         mask |= 1u << (c - bf);
       } else {
         prologue(c0);
-        run_stages(c0, c1);
+        run_stages(c0, c1, false);
       }
     }
     io.in = bt.sk_part + (int64_t)(xcd * GX + bf) * kGemmSkSlotFloats + (int64_t)wave * 16384;
@@ -1103,7 +1151,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[ii][j][e] = 0.f;
-    run_stages(cur.s0, cur.s1 < 0 ? NS : cur.s1);
+    run_stages(cur.s0, cur.s1 < 0 ? NS : cur.s1, i == 0);
     SkIo io{};
     if (cur.kind == kOwner) owner_wait(io);
     if (cur.kind == kContrib) io.out = bt.sk_part + (int64_t)slot * kGemmSkSlotFloats + (int64_t)wave * 16384;
@@ -1119,7 +1167,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
     GemmProblem pc = bt.p[0];
     if (cprob) pc = bt.p[1];
     uint32_t mx = 0;
-    tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 2 * kSsBytes) + wave * 32 * 64,
+    tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 4 * kHalf) + wave * 32 * 64,
                        cm0 + wm * WM, cn0 + wn * WN, lane, 1.0f, 1.0f, mx, io);
     if (ckind == kContrib) {
       // every wave's device-coherent stores have completed before the flag is raised
@@ -1563,13 +1611,13 @@ static bool persistent_ok(GemmBatch big, int op) {
   if (op == kFP8) {   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
     for (int i = 0; i < big.count; ++i) ok = ok && big.p[i].K % 128 == 0 && big.p[i].K >= 256;
     for (int i = 0; i < big.count; ++i) ok = ok && fp8_span_ok(big.p[i]);
-  } else {   // gemm_dl_kernel: k in super-stages of 64; operand rows as 32-bit byte offsets
+  } else {   // gemm_dl_kernel: k in units of 128; operand rows as 32-bit byte offsets
     for (int i = 0; i < big.count; ++i) {
       const GemmProblem& q = big.p[i];
       const int64_t last = q.M - 1;
       const int64_t a_span = ((last / q.amap.seg) * q.amap.bstride + (last % q.amap.seg) * q.amap.ld + q.K) * 2;
       const int64_t w_span = ((int64_t)(q.N - 1) * q.ldw + q.K) * 2;
-      ok = ok && q.K % 64 == 0 && a_span < (int64_t(1) << 32) && w_span < (int64_t(1) << 32);
+      ok = ok && q.K % 128 == 0 && a_span < (int64_t(1) << 32) && w_span < (int64_t(1) << 32);
     }
   }
   // the persistent kernel needs at least half the CUs busy with 256 x 256
@@ -1609,14 +1657,14 @@ static hipError_t launch_mfma(GemmBatch bt, hipStream_t stream, double flops) {
     // stream-K tail (16-bit operands, problems of one K, a workspace given):
     // the tiles past the last full round of 256 are shared out along K over
     // all 256 blocks when there are at least 64 of them (so a tile has at most
-    // five shares and every block at least one super-stage)
+    // five shares and every block at least one k unit)
     big.sk_tail = tiles_big;
     big.sk_units = 0;
     if constexpr (OP == kBF16 || OP == kF16 || OP == kF16W) {
       bool same_k = true;
       for (int i = 1; i < big.count; ++i) same_k = same_k && big.p[i].K == big.p[0].K;
       const int full = (tiles_big / kGemmSkMaxGrid) * kGemmSkMaxGrid, rest = tiles_big - full;
-      const int64_t units = (int64_t)rest * (big.p[0].K / 64);
+      const int64_t units = (int64_t)rest * (big.p[0].K / 128);
       if (g_sk_mode.load() && big.sk_part && big.sk_flag && same_k && rest >= 64 && units >= kGemmSkMaxGrid &&
           units < (int64_t(1) << 30)) {
         grid = kGemmSkMaxGrid;
