@@ -509,17 +509,33 @@ __device__ __forceinline__ bool sk_quarter(float* cs, const SkIo& sk, int Q, int
 
 // The residual rows (kEpiResid) of the lane's 8 rows rbase + 4u and four
 // columns col..col+3 of a quarter, all loads issued together.
+// Sample b and position l (row = b seg + l) of the rows rbase + 4u, u = 0..7,
+// for segments of seg >= 32 rows: one division, then at most one wrap, since
+// the eight rows span 29 consecutive rows.
+__device__ __forceinline__ void seg_rows(int rbase, int seg, int (&b)[8], int (&l)[8]) {
+  int bb = rbase / seg, ll = rbase - bb * seg;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    b[u] = bb;
+    l[u] = ll;
+    ll += 4;
+    if (ll >= seg) {
+      ll -= seg;
+      ++bb;
+    }
+  }
+}
+
 __device__ __forceinline__ void load_resid(const GemmProblem& pc, int rbase, int col, float4 (&xr)[8]) {
-  const int seg = pc.omap0.seg;
+  int sb[8], sl[8];
+  seg_rows(rbase, pc.omap0.seg, sb, sl);
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int row = rbase + 4 * u;
     xr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < pc.M && col < pc.N) {
-      const int64_t b = row / seg, l = row % seg;
-      xr[u] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(pc.out0) + b * pc.omap0.bstride +
-                                               l * pc.omap0.ld + col);
-    }
+    if (row < pc.M && col < pc.N)
+      xr[u] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(pc.out0) +
+                                               (int64_t)sb[u] * pc.omap0.bstride + (int64_t)sl[u] * pc.omap0.ld + col);
   }
 }
 
@@ -532,14 +548,16 @@ template <int EPI>
 __device__ __forceinline__ void apply_quarter(const GemmProblem& pc, const float* cs, int lrow, int c4, int rbase,
                                               int col, float4 bq, float4 gq, bool uniform, float dq, float qs,
                                               uint32_t& mx, const float4 (&xr)[8]) {
-  const int seg = pc.omap0.seg;
   const bool col_ok = col < pc.N;
+  int sb[8], sl[8], sb1[8], sl1[8];
+  seg_rows(rbase, pc.omap0.seg, sb, sl);
+  if constexpr (EPI == kEpiSplitGelu) seg_rows(rbase, pc.omap1.seg, sb1, sl1);
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int row = rbase + 4 * u;
     if (row < pc.M && col_ok) {
-      const int64_t b = row / seg, l = row % seg;
-      const int64_t off0 = b * pc.omap0.bstride + l * pc.omap0.ld;
+      const int64_t b = sb[u];
+      const int64_t off0 = b * pc.omap0.bstride + (int64_t)sl[u] * pc.omap0.ld;
       float4 w = *reinterpret_cast<const float4*>(&cs[(lrow + 4 * u) * 64 + c4]);
       w.x = w.x * dq + bq.x; w.y = w.y * dq + bq.y;
       w.z = w.z * dq + bq.z; w.w = w.w * dq + bq.w;
@@ -568,9 +586,9 @@ __device__ __forceinline__ void apply_quarter(const GemmProblem& pc, const float
         if (col < pc.n_split) {
           store4_dt(pc.out0, off0 + col, pc.out0_dt, w, qs, mx);
         } else {
-          const int64_t b1 = row / pc.omap1.seg, l1 = row % pc.omap1.seg;
           w.x = gelu_f(w.x); w.y = gelu_f(w.y); w.z = gelu_f(w.z); w.w = gelu_f(w.w);
-          store4_dt(pc.out1, b1 * pc.omap1.bstride + l1 * pc.omap1.ld + (col - pc.n_split), pc.out1_dt, w, qs, mx);
+          store4_dt(pc.out1, (int64_t)sb1[u] * pc.omap1.bstride + (int64_t)sl1[u] * pc.omap1.ld + (col - pc.n_split),
+                    pc.out1_dt, w, qs, mx);
         }
       }
     }
@@ -670,13 +688,20 @@ __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16
 #pragma unroll 1
   for (int qq = 0; qq < 4; ++qq) {
     float4 wA[8], wB[8], tA[8], tB[8];
+    int sb[8], sl[8];   // sample and position of the strip's rows (rows past M: sample 0, position 0)
+    seg_rows(row0 + qq * 32 + lrow, seg, sb, sl);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (row0 + qq * 32 + lrow + 4 * u >= pc.M) {
+        sb[u] = 0;
+        sl[u] = 0;
+      }
+    }
     // the RoPE pairs of the strip's rows, loaded before the staging so their
     // latency overlaps it (rows past M read row 0's entry and store nothing)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int row = row0 + qq * 32 + lrow + 4 * u;
-      const int rr = row < pc.M ? row : 0;
-      const float* tab = q.rope + ((int64_t)(rr / seg) * q.seq + q.tok0 + rr % seg) * 128;   // 64 (cos, sin)
+      const float* tab = q.rope + ((int64_t)sb[u] * q.seq + q.tok0 + sl[u]) * 128;   // 64 (cos, sin)
       if (q.rope) {
         tA[u] = *reinterpret_cast<const float4*>(tab + c4);
         tB[u] = *reinterpret_cast<const float4*>(tab + 64 + c4);
@@ -719,9 +744,8 @@ __device__ __forceinline__ void qkv_epilogue(const GemmProblem& pc, const f32x16
     for (int u = 0; u < 8; ++u) {
       const int row = row0 + qq * 32 + lrow + 4 * u;
       const bool ok = row < pc.M;
-      const int rr = ok ? row : 0;
-      const int b = rr / seg, l = q.tok0 + rr % seg;
-      const int64_t hrow = (int64_t)b * q.heads + h;
+      const int l = q.tok0 + sl[u];
+      const int64_t hrow = (int64_t)sb[u] * q.heads + h;
       float4 a = wA[u], c = wB[u];
       {
         float ss = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + c.x * c.x + c.y * c.y + c.z * c.z + c.w * c.w;
@@ -1606,8 +1630,9 @@ static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream
 // Conditions of the persistent 256 x 256 kernels for 16-bit or E4M3 operands.
 static bool persistent_ok(GemmBatch big, int op) {
   const int tiles_big = assign_tiles(big, 256, 256);
-  bool ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample
-  for (int i = 0; i < big.count; ++i) ok = ok && big.p[i].omap0.seg >= 32;
+  bool ok = true;   // the persistent kernel's epilogue needs >= 32 rows per sample (seg_rows)
+  for (int i = 0; i < big.count; ++i)
+    ok = ok && big.p[i].omap0.seg >= 32 && (big.p[i].out1 == nullptr || big.p[i].omap1.seg >= 32);
   if (op == kFP8) {   // gemm_fp8_kernel walks k in pairs of 64-wide steps, at least 4 of them
     for (int i = 0; i < big.count; ++i) ok = ok && big.p[i].K % 128 == 0 && big.p[i].K >= 256;
     for (int i = 0; i < big.count; ++i) ok = ok && fp8_span_ok(big.p[i]);
