@@ -1411,7 +1411,7 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
       } else {
         if constexpr (VM == 16) DL_WAIT_VM(16); else if constexpr (VM == 8) DL_WAIT_VM(8); else DL_WAIT_VM(0);
       }
-      __syncthreads();
+      lds_barrier();
       if constexpr (MX) ld_scale(kt + 2, nn_a, nn_b);
       if constexpr (decltype(refill)::value) issue(kt + 4);
       lfrag(kt + 1, SetTag<1 - S>{});
