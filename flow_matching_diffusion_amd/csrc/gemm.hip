@@ -920,8 +920,11 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
   const int lchunk = (lane & 7) ^ ss_swz(wave * 8 + lrow8);   // swz(row) does not depend on u
 
   int prob = 0, m0 = 0, n0 = 0, NS = 0;   // NS: k128 units of the tile (two super-stages each)
-  const char* abase = nullptr;
-  const char* wbase_g = nullptr;
+  // A and W as raw buffers (the launcher keeps both spans under 4 GiB): a
+  // load's address is the row offset soff (a VGPR, fixed per tile) plus the
+  // super-stage's k offset (an SGPR), so issuing it takes no vector
+  // arithmetic
+  __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000), rsrc_w = rsrc_a;
   uint32_t soff[16];   // 0..7 A rows, 8..15 W rows
   auto setup = [&](int id) {   // tile id (see tile_coord)
     const TileCoord tc = tile_coord(bt, id, BM, BN);
@@ -931,8 +934,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
     m0 = tc.tm * BM;
     n0 = tc.tn * BN;
     NS = p.K / 128;
-    abase = reinterpret_cast<const char*>(p.A);
-    wbase_g = reinterpret_cast<const char*>(p.W);
+    rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), 0, -1, 0x00020000);
+    rsrc_w = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.W), 0, -1, 0x00020000);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int r = ((wave + 4 * u) & 31) * 8 + lrow8;
@@ -954,8 +957,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
   auto slot_of = [&](int h) { return smem + (h % kHalfSlots) * kHalf; };
   // load u (0..7) of half h (super-stage ss of the tile, W when w)
   auto dma_one = [&](int h, int ss, bool w, int u) {
-    const char* g = (w ? wbase_g : abase) + (int64_t)ss * 128 + soff[(w ? 8 : 0) + u];
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)(slot_of(h) + ((wave + 4 * u) & 31) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(w ? rsrc_w : rsrc_a,
+                                             (lds_void_t*)(slot_of(h) + ((wave + 4 * u) & 31) * 1024), 16,
+                                             (int)soff[(w ? 8 : 0) + u], ss * 128, 0, 0);
   };
 
   f32x16_t acc[TM][TN];
