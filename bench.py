@@ -663,7 +663,7 @@ def train_bench(args) -> int:
     mi = synth.model_inputs(wl)
     dev = lambda a, bf=False: device_array(a, bf)
     z0, z1, t, ids = dev(mi["z0"]), dev(mi["z1"]), dev(mi["t"]), dev(mi["ids"])
-    txt = dev(mi["txt"])
+    txt = dev(mi["txt"], True)
 
     def step():
         return tr.step(z0, z1, t, txt, None, ids)

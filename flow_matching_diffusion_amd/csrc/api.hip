@@ -565,9 +565,14 @@ flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, i
   REQUIRE(img_bstride >= HW * hidden && img_bstride % 4 == 0, "img_bstride too small or not a multiple of 4");
   REQUIRE(aligned16(x_img) && aligned16(vec) && aligned16(z_t), "pointers must be 16-byte aligned");
   const bool has_txt = w->txt_in_w != nullptr;
+  const bool copy_txt = !has_txt && txt && x_txt;   // text already at the hidden width
   if (has_txt) {
     REQUIRE(w->txt_in_b && txt && x_txt && l_txt >= 1 && ctx_dim >= 1, "txt_in needs txt, x_txt, l_txt and ctx_dim");
     if (bf && ctx_dim % 64 != 0) return fail(FLUX_ERR_UNSUPPORTED, "bf16 txt_in needs ctx_dim %% 64 == 0");
+  }
+  if (copy_txt)
+    REQUIRE(l_txt >= 1 && (ctx_dim == 0 || ctx_dim == hidden), "text without txt_in must be [B, l_txt, hidden]");
+  if (has_txt || copy_txt) {
     REQUIRE(txt_bstride >= (int64_t)l_txt * hidden && txt_bstride % 4 == 0, "txt_bstride too small");
     REQUIRE(aligned16(x_txt) && aligned16(txt), "pointers must be 16-byte aligned");
   }
@@ -598,6 +603,7 @@ flux_status flux_embed_fwd(int32_t precision, int32_t batch, int32_t channels, i
     g.p[1] = gemm_problem(txt, rmap((int64_t)l_txt * ctx_dim, ctx_dim, l_txt), w->txt_in_w, w->txt_in_b,
                           batch * l_txt, hidden, ctx_dim, kEpiStoreF32, x_txt, rmap(txt_bstride, hidden, l_txt));
   FLUX_HIP(launch_gemm(g, dt, st), "input projection GEMM");
+  if (copy_txt) FLUX_HIP(launch_rows_to_f32(txt, batch, l_txt, hidden, dt, x_txt, txt_bstride, st), "text rows");
 
   // conditioning vector
   FLUX_HIP(launch_timestep_embed(t, batch, time_dim, 1000.f, 10000.f, emb, st), "timestep sinusoid");

@@ -313,6 +313,9 @@ hipError_t launch_timestep_embed(const float* t, int batch, int dim, float time_
                                  float* out, hipStream_t stream);
 hipError_t launch_patchify(const float* z, int batch, int channels, int hw, void* out, int dtype,
                            hipStream_t stream);
+// src [batch, rows, width] (kBF16 or kF32, width % 4 == 0) -> fp32 rows at dst + b * dst_bstride
+hipError_t launch_rows_to_f32(const void* src, int batch, int rows, int width, int dtype, float* dst,
+                              int64_t dst_bstride, hipStream_t stream);
 hipError_t launch_rf_noise(int batch, int64_t n, const float* z0, const float* z1, const float* t,
                            float* zt, float* vt, hipStream_t stream);
 hipError_t launch_rf_loss(int batch, int64_t n, const float* z0, const float* z1, const float* vpred,

@@ -352,6 +352,41 @@ hipError_t launch_patchify(const float* z, int batch, int channels, int hw, void
   return hipGetLastError();
 }
 
+// Text tokens that enter the joint sequence at the hidden width (no context
+// projection): sample b of src ([batch, rows, width] contiguous, element T)
+// into fp32 rows at dst + b * dst_bstride.  Four elements per thread (width
+// is a multiple of 4).
+template <typename T>
+__global__ void __launch_bounds__(256) rows_to_f32_kernel(const T* __restrict__ src, int64_t n, float* __restrict__ dst,
+                                                          int64_t dst_bstride) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element of the sample
+  if (i >= n) return;
+  const T* s = src + blockIdx.y * n + i;
+  float4 v;
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(s);
+    v = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                    __uint_as_float(u.y & 0xffff0000u));
+  } else {
+    v = *reinterpret_cast<const float4*>(s);
+  }
+  *reinterpret_cast<float4*>(dst + blockIdx.y * dst_bstride + i) = v;
+}
+
+hipError_t launch_rows_to_f32(const void* src, int batch, int rows, int width, int dtype, float* dst,
+                              int64_t dst_bstride, hipStream_t stream) {
+  const int64_t n = (int64_t)rows * width;
+  const dim3 grid((unsigned)ceil_div(n / 4, 256), batch);
+  TimingScope ts(kKcMisc, stream);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(rows_to_f32_kernel<bf16_t>, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(src), n,
+                       dst, dst_bstride);
+  else
+    hipLaunchKernelGGL(rows_to_f32_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(src), n, dst,
+                       dst_bstride);
+  return hipGetLastError();
+}
+
 // ===========================================================================
 // LayerNorm (no affine, biased variance) + adaLN modulate ("Flux architecture
 // deep dive", Implementation details / Adaptive layer normalization):

@@ -17,6 +17,13 @@ from . import flux as F
 from . import synth
 
 
+def _check_text(txt, dtype) -> None:
+    """The text tokens' element type follows the precision (flux_embed_fwd);
+    the library reads them as that type, so a mismatch is refused here."""
+    if txt.dtype != dtype:
+        raise ValueError(f"text tokens must be {dtype}, got {txt.dtype}")
+
+
 def device_array(a: np.ndarray, bf16: bool, device="cuda") -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     t = t.to(device)
@@ -242,13 +249,11 @@ class FluxModel(BlockStack):
         p = precision_of(wl)
         ws = self.ws.get(self.ws_bytes)
         x = o["x"]
-        has_txt_in = "txt_in.w" in self.emb
-        if not has_txt_in:
-            x[:, wl.l_img:].copy_(txt)   # text enters at hidden width: a copy into the joint buffer
+        # text enters through txt_in, or at the hidden width (the library then copies it into the joint buffer)
+        _check_text(txt, torch.bfloat16 if p == F.FLUX_PREC_BF16 else torch.float32)
         F.flux_embed_fwd(p, B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
-                         wl.vec_in_dim or 0, self._estruct, z_t, txt if has_txt_in else None, t,
-                         y, x, wl.seq * D, x[:, wl.l_img:] if has_txt_in else None, wl.seq * D, o["vec"], ws,
-                         ws.numel(), guidance=guidance)
+                         wl.vec_in_dim or 0, self._estruct, z_t, txt, t, y, x, wl.seq * D, x[:, wl.l_img:],
+                         wl.seq * D, o["vec"], ws, ws.numel(), guidance=guidance)
         self.blocks_fwd(x, o["vec"], o["rope"])
         F.flux_final_fwd(p, B, C, wl.img_h, wl.img_w, D, wl.eps, self.emb["final_mod.w"], self.emb["final_mod.b"],
                          self.emb["final_out.w"], self.emb["final_out.b"], x, wl.seq * D, o["vec"], o["v_pred"], ws,
@@ -418,13 +423,11 @@ class FluxTrainer:
         x, d, vec, dvec = o["x"], o["d"], o["vec"], o["dvec"]
         txt_ptr = x.data_ptr() + Li * D * 4
         d_txt_ptr = d.data_ptr() + Li * D * 4
-        has_txt_in = "txt_in.w" in self.emb
+        _check_text(txt, torch.bfloat16)
         F.rf_noise_loss(B, n, z0, z1, t, z_t=o["z_t"], v_target=o["v_target"])
-        if not has_txt_in:
-            x[:, Li:].copy_(txt)
         F.flux_embed_fwd(bf, B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
-                         wl.vec_in_dim or 0, self.estruct, o["z_t"], txt if has_txt_in else None, t, y, x, L * D,
-                         txt_ptr if has_txt_in else None, L * D, vec, ws, self.ws_bytes, guidance=guidance)
+                         wl.vec_in_dim or 0, self.estruct, o["z_t"], txt, t, y, x, L * D, txt_ptr, L * D, vec, ws,
+                         self.ws_bytes, guidance=guidance)
         for (iw, tw), sv in zip(self.dstructs, self.saved_d):
             F.flux_block_fwd_train(self.dims, iw, tw, x, L * D, txt_ptr, L * D, vec, self.rope, sv, sv.numel())
         for sw, sv in zip(self.sstructs, self.saved_s):
@@ -448,6 +451,7 @@ class FluxTrainer:
         for (iw, tw), sv, (gi, gt) in reversed(list(zip(self.dstructs, self.saved_d, dstr))):
             F.flux_block_bwd(self.dims, iw, tw, d, L * D, d_txt_ptr, L * D, vec, self.rope, sv, sv.numel(), gi, gt,
                              dvec, ws, self.ws_bytes)
+        has_txt_in = "txt_in.w" in self.emb
         F.flux_embed_bwd(B, C, wl.img_h, wl.img_w, wl.l_txt, wl.context_dim or 0, D, wl.model_channels,
                          wl.vec_in_dim or 0, self.estruct, o["z_t"], txt if has_txt_in else None, t, y, d, L * D,
                          d_txt_ptr if has_txt_in else None, L * D, dvec, self.egrads, ws, self.ws_bytes,

@@ -350,7 +350,10 @@ flux_status flux_timestep_embed(const float* t, int32_t batch, int32_t dim, floa
  * Model components / Input embeddings and Conditioning; Implementation
  * details / Memory layout):
  *   x_img = Linear_img_in(patchify(z_t)), patchify [B,C,H,W] -> [B,H*W,C];
- *   x_txt = Linear_txt_in(txt) if txt_in_w is not NULL, else not written;
+ *   x_txt = Linear_txt_in(txt) if txt_in_w is not NULL; else, when txt and
+ *           x_txt are both given, the text is already at the hidden width
+ *           (txt [B, l_txt, hidden], ctx_dim 0 or hidden) and x_txt = txt as
+ *           float; else x_txt is not written;
  *   vec   = Linear(SiLU(Linear(sinusoid(t)))) [+ Linear(SiLU(Linear(y)))]
  *           [+ Linear_guidance(g)],
  *   sinusoid(t) = [cos(1000 t f_j) | sin(1000 t f_j)], f_j = 1e4^(-j/half),

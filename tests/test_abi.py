@@ -126,6 +126,27 @@ def test_rf_argument_checks():
     assert L.rf_noise_loss(C.byref(a), None) == F.FLUX_ERR_INVALID_ARGUMENT
 
 
+def test_embed_text_at_hidden_width_checks():
+    """flux_embed_fwd without txt_in copies txt into x_txt only when the text
+    is already [B, l_txt, hidden]: another width, a short batch stride or a
+    misaligned pointer is rejected before anything is enqueued."""
+    L = F.lib()
+    fake = 1 << 40
+    w = F.flux_embed_weights()
+    w.img_in_w, w.img_in_b, w.time_in1_w, w.time_in1_b, w.time_in2_w, w.time_in2_b = (fake + i * 4096 for i in range(6))
+    B, Cc, H, W, Lt, D = 1, 64, 2, 2, 4, 256
+    z, t, x_img, vec, txt, x_txt, ws = (fake + (1 << 30) + i * (1 << 24) for i in range(7))
+
+    def call(ctx_dim, txt_bstride, txt_ptr=txt):
+        return L.flux_embed_fwd(F.FLUX_PREC_BF16, B, Cc, H, W, Lt, ctx_dim, D, 256, 0, C.byref(w), z, txt_ptr, t,
+                                None, None, x_img, H * W * D, x_txt, txt_bstride, vec, ws, 8, None)
+    assert call(100, Lt * D) == F.FLUX_ERR_INVALID_ARGUMENT                 # text width is not the hidden width
+    assert b"l_txt, hidden" in L.flux_last_error()
+    assert call(0, Lt * D - 4) == F.FLUX_ERR_INVALID_ARGUMENT               # batch stride shorter than a sample
+    assert call(D, Lt * D, txt + 8) == F.FLUX_ERR_INVALID_ARGUMENT           # misaligned text
+    assert call(0, Lt * D) == F.FLUX_ERR_WORKSPACE_TOO_SMALL                 # arguments fine, workspace too small
+
+
 def test_linear_and_attention_argument_checks():
     L = F.lib()
     fake = 1 << 40

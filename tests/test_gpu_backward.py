@@ -334,10 +334,13 @@ def test_flux_train_step(name):
     gv = np.linspace(1.0, 5.0, wl.batch).astype(np.float32) if with_g else None
     tr = FluxTrainer(wl, emb, [w2], [w1])
     y = _dev(mi["y"]) if "y" in mi else None
-    loss = tr.step(_dev(mi["z0"]), _dev(mi["z1"]), _dev(mi["t"]), _dev(mi["txt"], wl.context_dim is not None), y,
+    # the text is bf16 on the device (the element type of the bf16 path, with or
+    # without txt_in); the oracle takes the same bf16 values
+    txt = synth.round_to_bf16(mi["txt"])
+    loss = tr.step(_dev(mi["z0"]), _dev(mi["z1"]), _dev(mi["t"]), _dev(txt, True), y,
                    _dev(mi["ids"]), guidance=_dev(gv) if with_g else None)
     torch.cuda.synchronize()
-    ref_loss, g_emb, g2, g1 = G.flux_train_vjp(mi["z0"], mi["z1"], mi["t"], mi["txt"], mi.get("y"), mi["ids"], emb, [w2],
+    ref_loss, g_emb, g2, g1 = G.flux_train_vjp(mi["z0"], mi["z1"], mi["t"], txt, mi.get("y"), mi["ids"], emb, [w2],
                                                [w1], wl.heads, wl.axes_dim, wl.theta, wl.eps, wl.model_channels,
                                                guidance=gv)
     got = float(loss.item())

@@ -119,12 +119,12 @@ def test_train_step_gradient_check(f):
     mi = synth.model_inputs(wl)
     tr = FluxTrainer(wl, emb, [w2], [w1])
     f.flux_debug_status(clear=True)
-    tr.step(_dev(mi["z0"]), _dev(mi["z1"]), _dev(mi["t"]), _dev(mi["txt"]), None, _dev(mi["ids"]))
+    tr.step(_dev(mi["z0"]), _dev(mi["z1"]), _dev(mi["t"]), _dev(mi["txt"], True), None, _dev(mi["ids"]))
     torch.cuda.synchronize()
     assert f.flux_debug_status(clear=True) == 0
     z0 = mi["z0"].copy()
     z0.reshape(-1)[5] = np.inf
-    tr.step(_dev(z0), _dev(mi["z1"]), _dev(mi["t"]), _dev(mi["txt"]), None, _dev(mi["ids"]))
+    tr.step(_dev(z0), _dev(mi["z1"]), _dev(mi["t"]), _dev(mi["txt"], True), None, _dev(mi["ids"]))
     torch.cuda.synchronize()
     st = f.flux_debug_status(clear=True)
     assert st & f.FLUX_DBG_NONFINITE_GRAD and st & f.FLUX_DBG_NONFINITE_RESIDUAL, hex(st)
