@@ -207,12 +207,13 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   }
   if (ntiles > 2) gload_k(2);
   if (ntiles > 1) gload_v(1);
-  __syncthreads();
+  // the barriers publish LDS stores; K(2) and V(1) stay in flight in registers
+  lds_barrier();
   f32x16_t sc_cur[2], sc_nxt[2];
   s_tile(0, sc_cur);
   // iteration 0 overwrites K(0)'s buffer with K(2): every wave must have read
   // K(0) first
-  __syncthreads();
+  lds_barrier();
   for (int t = 0; t < ntiles; ++t) {
     softmax_max(t, sc_cur);
     // S(t + 1) with the exponentials of tile t in its MFMA shadow: step m
@@ -269,7 +270,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
     if (t + 2 < ntiles) gload_v(t + 2);
 #pragma unroll
     for (int u = 0; u < 2; ++u) sc_cur[u] = sc_nxt[u];
-    __syncthreads();
+    // K(t + 3) and V(t + 2) are only stored to LDS in the next iteration:
+    // the barrier waits for the LDS stores, not for these loads
+    lds_barrier();
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
@@ -531,7 +534,9 @@ __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
     if (t + 2 < ntiles) gload_v(t + 2);
 #pragma unroll
     for (int u = 0; u < 2; ++u) sc_cur[u] = sc_nxt[u];
-    __syncthreads();
+    // K(t + 3) and V(t + 2) are only stored to LDS in the next iteration:
+    // the barrier waits for the LDS stores, not for these loads
+    lds_barrier();
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = fp8_scale_inv(a.sv) / l_tot;

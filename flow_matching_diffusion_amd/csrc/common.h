@@ -95,6 +95,20 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return f32_to_f16_sat(v); }
 
+// Block barrier for LDS hand-offs that leaves global loads in flight: the
+// wave's own LDS accesses are complete before it arrives (lgkmcnt(0)), but
+// outstanding global loads are not waited for.  __syncthreads() would also
+// wait for every one of them (its workgroup fences imply s_waitcnt
+// vmcnt(0)): for loads into registers the compiler waits where the registers
+// are used, and for direct-to-LDS loads the caller bounds them with a
+// counted vmcnt wait first.  The asm statements keep the compiler from
+// moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- wave reductions (fixed butterfly order -> deterministic) ---------------
 template <int WIDTH = kWave>
 __device__ __forceinline__ float wave_sum(float v) {

@@ -879,19 +879,6 @@ __device__ __forceinline__ void tile_epilogue(const GemmProblem& pc, const f32x1
 //  * Operand rows are addressed as 32-bit byte offsets from the tile's A and
 //    W base pointers (the launcher keeps both spans under 4 GiB).
 // ---------------------------------------------------------------------------
-// Block barrier of an LDS ring fed by direct global->LDS loads: the wave's
-// own LDS accesses are complete before it arrives, global loads stay in
-// flight.  __syncthreads() would also wait for every outstanding global load
-// (its workgroup fences imply s_waitcnt vmcnt(0)), i.e. for the operands
-// still being prefetched; the caller bounds those with a counted vmcnt wait
-// first.  The asm statements keep the compiler from moving memory accesses
-// across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 constexpr int kHalf = 32768;   // one operand (A or W) of a super-stage: 256 rows x 128 bytes
 constexpr int kHalfSlots = 5;  // LDS ring of operand halves; slot 4 doubles as the epilogue staging
 
