@@ -90,8 +90,8 @@ def recorded_traffic(kernel_class):
 KERNEL_CLASSES = {
     "gemm_256_f16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_dl_kernel<[23],"]),
     "gemm_256_bf16": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_dl_kernel<1,"]),
-    "gemm_256_fp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8_kernel<\d+, false>"]),
-    "gemm_256_mxfp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8_kernel<\d+, true>"]),
+    "gemm_256_fp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8r_kernel<\d+>"]),
+    "gemm_256_mxfp8": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_fp8_kernel<\d+, 1>"]),
     "gemm_128x128": ("flow_matching_diffusion_amd/csrc/gemm.hip", [r"gemm_mfma_kernel<"]),
     "attention": ("flow_matching_diffusion_amd/csrc/attention.hip", [r"attn_(bf16|f32)_kernel"]),
     "ln_modulate": ("flow_matching_diffusion_amd/csrc/rowwise.hip", [r"ln_mod_kernel"]),

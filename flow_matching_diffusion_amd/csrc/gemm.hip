@@ -5,8 +5,8 @@
 // 16-bit operand paths, fp32 accumulation on 32x32x16 MFMA; operands bf16 x
 // bf16, fp16 activations x bf16 weights converted to fp16 in the kernel (exact
 // in fp16's normal range), or fp16 x fp16.  E4M3 x E4M3 operands run on the
-// 32x32x64 fp8 MFMA (gemm_fp8_kernel), small E4M3 problems on the 128 x 128
-// kernel after an exact widening to fp16.  A and W are both K-contiguous (torch
+// 32x32x64 fp8 MFMA (gemm_fp8r_kernel; the MX formats on gemm_fp8_kernel),
+// small E4M3 problems on the 128 x 128 kernel after an exact widening to fp16.  A and W are both K-contiguous (torch
 // Linear layout).  Several problems (the image and text streams of a double
 // block) share one grid; the tile order keeps each XCD on a contiguous tile
 // range and walks tiles in groups of 8 tile rows so A and W panels are reused
@@ -1502,6 +1502,191 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// E4M3 operands on the ring of the 16-bit persistent kernel: a super-stage is
+// k = 128 E4M3 values, i.e. the same 128-byte rows, 32 KB operand halves,
+// swizzle, buffer loads and barrier schedule as gemm_dl_kernel, and two steps
+// of the 32x32x64 fp8 MFMA.  In step t (0, 1) lane half h takes logical chunks
+// 4t + h and 4t + 2 + h of a row (32 bytes); A and W use the same split, so
+// each MFMA sums over 64 distinct k of the super-stage.  128-byte rows keep
+// the loads at whole lines: 64-byte row pieces (one k64 step per stage) cap
+// the global -> LDS rate below what the fp8 MFMAs consume (measured on
+// MI355X).  Tiles t = blockIdx.x, + gridDim.x, ...; epilogue and the per-block
+// output amax as gemm_fp8_kernel.
+// ---------------------------------------------------------------------------
+template <int EPI>
+__global__ void __launch_bounds__(256, 1) gemm_fp8r_kernel(GemmBatch bt) {
+  constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
+  __shared__ __attribute__((aligned(1024))) char smem[kHalfSlots * kHalf];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int fs = ss_swz(frow);
+  // fragment offsets in an operand half: step t, chunk kk (0: 4t + h, 1: 4t + 2 + h)
+  int aoff[2][2], boff[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      aoff[t][kk] = (wm * WM + frow) * 128 + (((4 * t + 2 * kk + fhalf) ^ fs) << 4);
+      boff[t][kk] = (wn * WN + frow) * 128 + (((4 * t + 2 * kk + fhalf) ^ fs) << 4);
+    }
+  const int lrow8 = lane >> 3;
+  const int lchunk = (lane & 7) ^ ss_swz(wave * 8 + lrow8);
+
+  int prob = 0, m0 = 0, n0 = 0, NSS = 0;   // NSS: super-stages of the tile (K / 128)
+  __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000), rsrc_w = rsrc_a;
+  uint32_t soff[16];   // 0..7 A rows, 8..15 W rows (byte offsets; one byte per element)
+  auto setup = [&](int t) {
+    const TileCoord tc = decode_tile_id(bt, t, BM, BN);
+    GemmProblem p = bt.p[0];
+    if (tc.prob) p = bt.p[1];
+    prob = tc.prob;
+    m0 = tc.tm * BM;
+    n0 = tc.tn * BN;
+    NSS = p.K / 128;
+    rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), 0, -1, 0x00020000);
+    rsrc_w = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.W), 0, -1, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int r = ((wave + 4 * u) & 31) * 8 + lrow8;
+      if (u < 8) {
+        int gr = m0 + r;
+        gr = gr < p.M ? gr : p.M - 1;
+        soff[u] = (uint32_t)((int64_t)(gr / p.amap.seg) * p.amap.bstride + (int64_t)(gr % p.amap.seg) * p.amap.ld +
+                             lchunk * 16);
+      } else {
+        int gr = n0 + r;
+        gr = gr < p.N ? gr : p.N - 1;
+        soff[u] = (uint32_t)((int64_t)gr * p.ldw + lchunk * 16);
+      }
+    }
+  };
+  auto slot_of = [&](int h) { return smem + (h % kHalfSlots) * kHalf; };
+  auto dma_one = [&](int h, int ss, bool w, int u) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(w ? rsrc_w : rsrc_a,
+                                             (lds_void_t*)(slot_of(h) + ((wave + 4 * u) & 31) * 1024), 16,
+                                             (int)soff[(w ? 8 : 0) + u], ss * 128, 0, 0);
+  };
+
+  f32x16_t acc[TM][TN];
+  u32x4_t fa[2][TM][2], fb[2][TN][2];   // [set][tile][chunk]
+  // read q (0..15) of step t of super-stage j into set s: fragment q >> 1 (0..3 A,
+  // 4..7 W), chunk q & 1
+  auto frag_one = [&](int j, int t, int s, int q) {
+    const int n = q >> 1, kk = q & 1;
+    if (n < TM)
+      fa[s][n][kk] = *reinterpret_cast<const u32x4_t*>(slot_of(2 * j) + aoff[t][kk] + n * 32 * 128);
+    else
+      fb[s][n - TM][kk] = *reinterpret_cast<const u32x4_t*>(slot_of(2 * j + 1) + boff[t][kk] + (n - TM) * 32 * 128);
+  };
+  auto mfma_one = [&](int s, int idx) {
+    const int j = idx >> 2, i = idx & 3;
+    const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[s][j][0], fb[s][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[s][i][0], fa[s][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
+  // Super-stage j: step 0 (set 0) under the reads of step 1 into set 1 and
+  // (ISSUE) the loads of A of j + 2, at every other MFMA; then (NEXT) the
+  // barrier once j + 1 has landed (VM loads left in flight: A of j + 2);
+  // step 1 (set 1) under the reads of step 0 of j + 1 into set 0 and
+  // (ISSUE) the loads of W of j + 2 into the slot of A of j.
+  auto super_stage = [&](int j, auto issue, auto vm, auto next) __attribute__((always_inline)) {
+    constexpr bool ISSUE = decltype(issue)::value, NEXT = decltype(next)::value;
+    constexpr int VM = decltype(vm)::value;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one(0, idx);
+      frag_one(j, 1, 1, idx);
+      if (ISSUE && (idx & 1) == 1) dma_one(2 * j + 4, j + 2, false, idx >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) {
+      if constexpr (VM == 8) DL_WAIT_VM(8);
+      else DL_WAIT_VM(0);
+      lds_barrier();
+    }
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one(1, idx);
+      if (NEXT) frag_one(j + 1, 0, 0, idx);
+      if (ISSUE && (idx & 1) == 1) dma_one(2 * j + 5, j + 2, true, idx >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using V8 = std::integral_constant<int, 8>;
+  using V0 = std::integral_constant<int, 0>;
+  // halves 0..3 (A, W of super-stages 0 and 1) of the current tile
+  auto prologue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dma_one(h, h >> 1, (h & 1) != 0, u);
+  };
+  // all NSS (>= 2) super-stages of the current tile into acc, its prologue
+  // issued (settled: no global memory operation after it); on return every
+  // load has landed and every wave has read its last fragments
+  auto run_stages = [&](bool settled) __attribute__((always_inline)) {
+    if (settled) DL_WAIT_VM(16);
+    else DL_WAIT_VM(0);
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) frag_one(0, 0, 0, q);
+    int j = 0;
+    for (; j + 2 < NSS; ++j) super_stage(j, T_{}, V8{}, T_{});
+    super_stage(j, F_{}, V0{}, T_{});
+    super_stage(j + 1, F_{}, V0{}, F_{});
+    __syncthreads();
+  };
+
+  int t = blockIdx.x;
+  if (t >= bt.total_tiles) return;   // block-uniform
+  setup(t);
+  prologue();
+  // amax of each problem's E4M3 output over the block's tiles, raised once
+  // per block (as gemm_fp8_kernel)
+  uint32_t mxp[2] = {0u, 0u};
+  for (bool first = true; t < bt.total_tiles; t += gridDim.x, first = false) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    run_stages(first);
+    const int cprob = prob, cm0 = m0, cn0 = n0;
+    if (t + (int)gridDim.x < bt.total_tiles) {
+      setup(t + gridDim.x);
+      prologue();
+    }
+    // epilogue through slot 4, which the next tile's prologue leaves alone
+    GemmProblem pc = bt.p[0];
+    if (cprob) pc = bt.p[1];
+    uint32_t mx = 0;
+    tile_epilogue<EPI>(pc, acc, reinterpret_cast<float*>(smem + 4 * kHalf) + wave * 32 * 64, cm0 + wm * WM,
+                       cn0 + wn * WN, lane, epi_dequant(pc), epi_out_scale(pc), mx);
+    if (cprob) mxp[1] = max(mxp[1], mx);
+    else mxp[0] = max(mxp[0], mx);
+  }
+  if (bt.p[0].qo || (bt.count > 1 && bt.p[1].qo)) {   // block-uniform
+    // slot 0 is idle: the last tile's barrier has passed and no prologue followed it
+    __syncthreads();
+    uint32_t* red = reinterpret_cast<uint32_t*>(smem);   // [2][4]
+    const uint32_t m0w = wave_max_u32(mxp[0]), m1w = wave_max_u32(mxp[1]);
+    if (lane == 0) {
+      red[wave] = m0w;
+      red[4 + wave] = m1w;
+    }
+    __syncthreads();
+    if (tid < 2 && (tid == 0 || bt.count > 1)) {
+      const uint32_t m = max(max(red[4 * tid], red[4 * tid + 1]), max(red[4 * tid + 2], red[4 * tid + 3]));
+      if (bt.p[tid].qo && m) fp8_amax_raise(bt.p[tid].qo, __uint_as_float(m));
+    }
+  }
+}
+
 // Split-K reduction: out = epilogue(sum over splits s = 0..ksplit-1 in order
 // of partials[s]), four consecutive columns per thread; the accumulator
 // scale of E4M3 operands was applied when the partials were written.
@@ -1609,7 +1794,7 @@ static bool fp8_span_ok(const GemmProblem& q) {
 template <int OP, int EPI>
 static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream) {
   if constexpr (OP == kFP8)
-    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtE4M3>), dim3(grid), dim3(256), 0, stream, big);
+    hipLaunchKernelGGL((gemm_fp8r_kernel<EPI>), dim3(grid), dim3(256), 0, stream, big);
   else if constexpr (OP == kMXFP8)
     hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtMx8>), dim3(grid), dim3(256), 0, stream, big);
   else if constexpr (OP == kMXFP4)
