@@ -1514,9 +1514,11 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmBatch bt) {
 // MI355X).  Tiles t = blockIdx.x, + gridDim.x, ...; epilogue and the per-block
 // output amax as gemm_fp8_kernel.
 // ---------------------------------------------------------------------------
-template <int EPI>
+template <int EPI, int FMT>
 __global__ void __launch_bounds__(256, 1) gemm_fp8r_kernel(GemmBatch bt) {
+  constexpr bool MX = FMT != kFmtE4M3, FP4 = FMT == kFmtMx4;
   constexpr int BM = kDlRows, BN = kDlRows, WM = 128, WN = 128, TM = 4, TN = 4;
+  constexpr int SCS = FP4 ? 512 : 256;   // MX: scale bytes of one 64-byte step for a wave's 128 rows
   __shared__ __attribute__((aligned(1024))) char smem[kHalfSlots * kHalf];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -1534,7 +1536,15 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8r_kernel(GemmBatch bt) {
   const int lrow8 = lane >> 3;
   const int lchunk = (lane & 7) ^ ss_swz(wave * 8 + lrow8);
 
-  int prob = 0, m0 = 0, n0 = 0, NSS = 0;   // NSS: super-stages of the tile (K / 128)
+  int prob = 0, m0 = 0, n0 = 0, NSS = 0;   // NSS: super-stages of the tile (K bytes / 128)
+  // MX: the lane's scale word of 64-byte step kc at sca + kc * SCS (A rows of
+  // the wave) and scb + kc * SCS (W rows), as gemm_fp8_kernel reads them;
+  // step t of super-stage j is kc = 2 j + t.  Two register sets, super-stage
+  // j in set j % 2, loaded two super-stages ahead (MXFP8 uses .x only).
+  const uint8_t* sca = nullptr;
+  const uint8_t* scb = nullptr;
+  const int sc_lane = FP4 ? fhalf * 256 + frow * 8 : fhalf * 128 + frow * 4;
+  uint2 scl_a[2][2], scl_b[2][2];   // [set][step]
   __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000), rsrc_w = rsrc_a;
   uint32_t soff[16];   // 0..7 A rows, 8..15 W rows (byte offsets; one byte per element)
   auto setup = [&](int t) {
@@ -1544,7 +1554,11 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8r_kernel(GemmBatch bt) {
     prob = tc.prob;
     m0 = tc.tm * BM;
     n0 = tc.tn * BN;
-    NSS = p.K / 128;
+    NSS = (FP4 ? p.K / 2 : p.K) / 128;
+    if constexpr (MX) {
+      sca = p.sa + (size_t)(m0 / 128 + wm) * (2 * NSS) * SCS;
+      scb = p.sb + (size_t)(n0 / 128 + wn) * (2 * NSS) * SCS;
+    }
     rsrc_a = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), 0, -1, 0x00020000);
     rsrc_w = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.W), 0, -1, 0x00020000);
 #pragma unroll
@@ -1580,23 +1594,86 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8r_kernel(GemmBatch bt) {
     else
       fb[s][n - TM][kk] = *reinterpret_cast<const u32x4_t*>(slot_of(2 * j + 1) + boff[t][kk] + (n - TM) * 32 * 128);
   };
-  auto mfma_one = [&](int s, int idx) {
-    const int j = idx >> 2, i = idx & 3;
-    const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[s][j][0], fb[s][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-    const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[s][i][0], fa[s][i][1], 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+  // MX: the scale words of super-stage j into set Q
+  auto ld_scales = [&](int j, auto set) __attribute__((always_inline)) {
+    constexpr int Q = decltype(set)::value;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const size_t kc = (size_t)(2 * j + t) * SCS + sc_lane;
+      if constexpr (FP4) {
+        scl_a[Q][t] = *reinterpret_cast<const uint2*>(sca + kc);
+        scl_b[Q][t] = *reinterpret_cast<const uint2*>(scb + kc);
+      } else {
+        scl_a[Q][t].x = *reinterpret_cast<const uint32_t*>(sca + kc);
+        scl_b[Q][t].x = *reinterpret_cast<const uint32_t*>(scb + kc);
+      }
+    }
   };
+  // MFMA of tile (I, J) in step T with fragments in set s and MX scales of
+  // set Q: one E4M3 / MXFP8 MFMA over both chunks, or (MXFP4) one fp4 MFMA
+  // per chunk; the scale of A fragment I is byte I of the lane's A word, that
+  // of W fragment J byte J of its W word (the byte selectors are immediates,
+  // hence the tile as a type)
+  auto mfma_ij = [&](int s, auto ic, auto jc, auto step, auto set) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value, J = decltype(jc)::value;
+    constexpr int T = decltype(step)::value, Q = decltype(set)::value;
+    if constexpr (FP4) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[s][J][c], fb[s][J][c], 0, 1, 2, 3, -1, -1, -1, -1));
+        const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[s][I][c], fa[s][I][c], 0, 1, 2, 3, -1, -1, -1, -1));
+        const uint32_t sa_w = c ? scl_a[Q][T].y : scl_a[Q][T].x, sb_w = c ? scl_b[Q][T].y : scl_b[Q][T].x;
+        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[I][J], 4, 4, I, (int)sa_w, J, (int)sb_w);
+      }
+    } else {
+      const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fb[s][J][0], fb[s][J][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(fa[s][I][0], fa[s][I][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      if constexpr (MX)
+        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[I][J], 0, 0, I, (int)scl_a[Q][T].x, J,
+                                                                   (int)scl_b[Q][T].x);
+      else
+        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[I][J], 0, 0, 0, 0, 0, 0);
+    }
+  };
+  // MFMA slot idx: tile (idx & 3, idx >> 2)
+  auto mfma_one = [&](int s, int idx, auto step, auto set) __attribute__((always_inline)) {
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    switch (idx) {
+      case 0: mfma_ij(s, C0{}, C0{}, step, set); break;
+      case 1: mfma_ij(s, C1{}, C0{}, step, set); break;
+      case 2: mfma_ij(s, C2{}, C0{}, step, set); break;
+      case 3: mfma_ij(s, C3{}, C0{}, step, set); break;
+      case 4: mfma_ij(s, C0{}, C1{}, step, set); break;
+      case 5: mfma_ij(s, C1{}, C1{}, step, set); break;
+      case 6: mfma_ij(s, C2{}, C1{}, step, set); break;
+      case 7: mfma_ij(s, C3{}, C1{}, step, set); break;
+      case 8: mfma_ij(s, C0{}, C2{}, step, set); break;
+      case 9: mfma_ij(s, C1{}, C2{}, step, set); break;
+      case 10: mfma_ij(s, C2{}, C2{}, step, set); break;
+      case 11: mfma_ij(s, C3{}, C2{}, step, set); break;
+      case 12: mfma_ij(s, C0{}, C3{}, step, set); break;
+      case 13: mfma_ij(s, C1{}, C3{}, step, set); break;
+      case 14: mfma_ij(s, C2{}, C3{}, step, set); break;
+      default: mfma_ij(s, C3{}, C3{}, step, set); break;
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   // Super-stage j: step 0 (set 0) under the reads of step 1 into set 1 and
   // (ISSUE) the loads of A of j + 2, at every other MFMA; then (NEXT) the
   // barrier once j + 1 has landed (VM loads left in flight: A of j + 2);
   // step 1 (set 1) under the reads of step 0 of j + 1 into set 0 and
   // (ISSUE) the loads of W of j + 2 into the slot of A of j.
-  auto super_stage = [&](int j, auto issue, auto vm, auto next) __attribute__((always_inline)) {
+  auto super_stage = [&](int j, auto issue, auto vm, auto next, auto set, auto lscale) __attribute__((always_inline)) {
     constexpr bool ISSUE = decltype(issue)::value, NEXT = decltype(next)::value;
+    constexpr bool LSCALE = decltype(lscale)::value;
     constexpr int VM = decltype(vm)::value;
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
-      mfma_one(0, idx);
+      mfma_one(0, idx, S0{}, set);
       frag_one(j, 1, 1, idx);
       if (ISSUE && (idx & 1) == 1) dma_one(2 * j + 4, j + 2, false, idx >> 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -1608,18 +1685,28 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8r_kernel(GemmBatch bt) {
     }
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
-      mfma_one(1, idx);
+      mfma_one(1, idx, S1{}, set);
       if (NEXT) frag_one(j + 1, 0, 0, idx);
       if (ISSUE && (idx & 1) == 1) dma_one(2 * j + 5, j + 2, true, idx >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // MX: the scales of super-stage j + 2 into this set, free once its MFMAs
+    // are issued; they precede the A loads of j + 3, so the barrier of j + 1
+    // (which leaves only those in flight) finds them landed
+    if constexpr (MX && LSCALE) ld_scales(j + 2, set);
+    __builtin_amdgcn_sched_barrier(0);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   using V8 = std::integral_constant<int, 8>;
   using V0 = std::integral_constant<int, 0>;
-  // halves 0..3 (A, W of super-stages 0 and 1) of the current tile
+  // halves 0..3 (A, W of super-stages 0 and 1) of the current tile, after
+  // (MX) the scales of super-stages 0 and 1
   auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (MX) {
+      ld_scales(0, S0{});
+      ld_scales(1, S1{});
+    }
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
@@ -1635,9 +1722,18 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8r_kernel(GemmBatch bt) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) frag_one(0, 0, 0, q);
     int j = 0;
-    for (; j + 2 < NSS; ++j) super_stage(j, T_{}, V8{}, T_{});
-    super_stage(j, F_{}, V0{}, T_{});
-    super_stage(j + 1, F_{}, V0{}, F_{});
+    if constexpr (MX) {
+      // pairs, so super-stage j's scale set j % 2 is fixed at compile time
+      // (NSS is even for MX launches)
+      for (; j + 2 < NSS; j += 2) {
+        super_stage(j, T_{}, V8{}, T_{}, S0{}, T_{});
+        super_stage(j + 1, T_{}, V8{}, T_{}, S1{}, T_{});
+      }
+    } else {
+      for (; j + 2 < NSS; ++j) super_stage(j, T_{}, V8{}, T_{}, S0{}, F_{});
+    }
+    super_stage(j, F_{}, V0{}, T_{}, S0{}, F_{});
+    super_stage(j + 1, F_{}, V0{}, F_{}, S1{}, F_{});
     __syncthreads();
   };
 
@@ -1793,12 +1889,20 @@ static bool fp8_span_ok(const GemmProblem& q) {
 
 template <int OP, int EPI>
 static void launch_persistent(const GemmBatch& big, int grid, hipStream_t stream) {
+  // MX on the ring needs an even number of 128-byte super-stages (its scale
+  // registers alternate between two sets); other K keep gemm_fp8_kernel
+  bool even = true;
+  for (int i = 0; i < big.count; ++i)
+    even = even && ((OP == kMXFP4 ? big.p[i].K / 2 : big.p[i].K) / 128) % 2 == 0;
   if constexpr (OP == kFP8)
-    hipLaunchKernelGGL((gemm_fp8r_kernel<EPI>), dim3(grid), dim3(256), 0, stream, big);
-  else if constexpr (OP == kMXFP8)
-    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtMx8>), dim3(grid), dim3(256), 0, stream, big);
-  else if constexpr (OP == kMXFP4)
-    hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtMx4>), dim3(grid), dim3(256), 0, stream, big);
+    hipLaunchKernelGGL((gemm_fp8r_kernel<EPI, kFmtE4M3>), dim3(grid), dim3(256), 0, stream, big);
+  else if constexpr (OP == kMXFP8) {
+    if (even) hipLaunchKernelGGL((gemm_fp8r_kernel<EPI, kFmtMx8>), dim3(grid), dim3(256), 0, stream, big);
+    else hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtMx8>), dim3(grid), dim3(256), 0, stream, big);
+  } else if constexpr (OP == kMXFP4) {
+    if (even) hipLaunchKernelGGL((gemm_fp8r_kernel<EPI, kFmtMx4>), dim3(grid), dim3(256), 0, stream, big);
+    else hipLaunchKernelGGL((gemm_fp8_kernel<EPI, kFmtMx4>), dim3(grid), dim3(256), 0, stream, big);
+  }
   else
     hipLaunchKernelGGL((gemm_dl_kernel<OP, EPI>), dim3(grid), dim3(256), 0, stream, big);
 }
