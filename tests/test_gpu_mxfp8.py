@@ -97,7 +97,9 @@ def _linear_gpu(xq, xs, wq, ws, b, m, n, k):
     return y.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (300, 132, 512)])
+# k = 384 and 1152 give an odd number of 128-wide k super-stages: the GEMM then
+# runs on the 64-byte-stage kernel instead of the ring of operand halves
+@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (300, 132, 512), (300, 132, 384)])
 def test_mxfp8_linear_exact_on_small_integers(m, n, k):
     # codes of integers |v| <= 8 with block exponents in [-1, 1]: every product
     # and every partial sum (at most 2^17 in steps of 2^-2) is an exactly
@@ -119,7 +121,7 @@ def test_mxfp8_linear_exact_on_small_integers(m, n, k):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("m,n,k", [(512, 768, 3072), (4608 + 97, 3072 + 4, 3072), (1000, 12288, 256)])
+@pytest.mark.parametrize("m,n,k", [(512, 768, 3072), (4608 + 97, 3072 + 4, 3072), (1000, 12288, 256), (520, 256, 1152)])
 def test_mxfp8_linear(m, n, k):
     _say(f"MXFP8 linear m={m} n={n} k={k}")
     rng = np.random.default_rng(m * 3 + n + k)
