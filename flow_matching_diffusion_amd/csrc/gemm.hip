@@ -9,7 +9,7 @@
 // small E4M3 problems on the 128 x 128 kernel after an exact widening to fp16.  A and W are both K-contiguous (torch
 // Linear layout).  Several problems (the image and text streams of a double
 // block) share one grid; the tile order keeps each XCD on a contiguous tile
-// range and walks tiles in groups of 8 tile rows so A and W panels are reused
+// range and walks tiles in groups of 4 tile rows so A and W panels are reused
 // from L2.
 //  * large problems: gemm_dl_kernel, persistent (one 256-thread block per CU),
 //    256 x 256 tiles; operands loaded global -> LDS directly in k = 64
@@ -190,7 +190,7 @@ __device__ __forceinline__ TileCoord tile_coord(const GemmBatch& bt, int id, int
   const int local = id - (c.prob ? bt.p[1].tile_begin : bt.p[0].tile_begin);
   const int tiles_m = (int)ceil_div(c.prob ? bt.p[1].M : bt.p[0].M, BM);
   const int tiles_n = c.prob ? bt.p[1].tiles_n : bt.p[0].tiles_n;
-  constexpr int kGroupM = 8;
+  constexpr int kGroupM = 4;
   const int group = kGroupM * tiles_n;
   const int g = local / group;
   const int first_m = g * kGroupM;
