@@ -25,6 +25,15 @@
 // relative rounding) and the 64 multiplies of O are skipped on almost every
 // tile.  The result is the same softmax; only the reference point of the
 // exponentials differs.
+// K and V^T tiles reach LDS by direct global -> LDS loads (16 bytes per lane,
+// no register round trip) into a ring of four slots each: iteration t reads
+// K(t + 1) and V(t) while V(t + 3) and K(t + 4) load, so every load has two
+// iterations to land, and the one barrier per tile waits only for the loads
+// the next iteration reads (counted vmcnt; __syncthreads() would wait for
+// all).  Against K / V staged through registers with two LDS buffers each:
+// 328 -> 300 us at B=1, L=4608, 24 heads on MI355X, bit-identical results.
+// All slots are one LDS array: with one array per tile kind the compiler
+// adds a wait for every load in flight before each fragment read.
 // Inputs come from launch_prep: Q, K head-major [B, H, Lp, Dh] and V
 // transposed [B, H, Dh, Lp], Lp = seq rounded up to 256, zero padded.  The
 // output is written as bf16, fp16 or E4M3 (the operand type of the next
@@ -49,17 +58,22 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   constexpr int DCH = DH / 8;     // 16-byte chunks per K row
   constexpr int KS = DH / 16;     // MFMA k-steps of S^T
   constexpr int DT = DH / 32;     // 32-row tiles of O^T
-  constexpr int LK = KT * DCH / NT;
-  constexpr int LV = DH * 8 / NT;
   constexpr float kLazy = 8.0f;   // rescale when a tile max exceeds the running max by this (log2)
-  // LDS rows padded by 16 bytes: a 16-byte read of 32 consecutive rows at one
-  // chunk then touches each 4-bank group once per 16-lane cycle (gfx950 serves
-  // a 16-byte-per-lane read in four such cycles), and every read address is a
-  // per-lane base plus an immediate offset
-  constexpr int KLD = DH + 8;     // K tile row stride (elements)
-  constexpr int VLD = KT + 8;     // V^T tile row stride (elements)
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][DH * VLD];
+  constexpr int KSL = 4;                      // ring slots of K and of V^T tiles
+  constexpr int KRB = DH * 2;                 // K row bytes (256 or 128); V^T rows are 128
+  constexpr int TB = KT * DH * 2;             // bytes of one K or V^T tile
+  constexpr int NKD = TB / 1024 / NW;         // 1 KB loads per wave and tile, K
+  constexpr int NVD = TB / 1024 / NW;         // and V^T
+  constexpr int VMW = 2 * (NKD + NVD);        // loads left in flight at the end of an iteration
+  // Rows unpadded; 16-byte chunk c of row r at physical chunk c ^ swz(r), with
+  // swz(r) = r & 15 for 256-byte rows and (r >> 1) & 7 for 128-byte rows.
+  // gfx950 serves a 16-byte-per-lane read in four cycles of 16 lanes, those of
+  // a cycle having equal lane bit 5 and equal (bit 4 xor bit 2) (measured with
+  // the bank-conflict counter); a fragment read of 32 consecutive rows at one
+  // logical chunk then hits each 4-bank group once per cycle.
+  __shared__ __attribute__((aligned(1024))) char ring[2 * KSL * TB];
+  auto kslot = [&](int j) { return ring + (j % KSL) * TB; };
+  auto vslot = [&](int j) { return ring + (KSL + j % KSL) * TB; };
 
   // work item of this block: XCD x (blocks are dispatched round-robin over the
   // 8 XCDs) takes the contiguous item range [x * per, (x + 1) * per), so the
@@ -74,6 +88,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   const int b = (int)(bh / a.heads), h = (int)(bh % a.heads);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
+  const int kswz = KRB == 256 ? (l32 & 15) : ((l32 >> 1) & 7);   // swz of the lane's fragment rows
+  const int vswz = (l32 >> 1) & 7;
   const bf16_t* Qh = reinterpret_cast<const bf16_t*>(a.qh) + bh * a.seq_pad * DH;
   const bf16_t* Kh = reinterpret_cast<const bf16_t*>(a.kh) + bh * a.seq_pad * DH;
   const bf16_t* Vt = reinterpret_cast<const bf16_t*>(a.vt) + bh * DH * a.seq_pad;
@@ -83,7 +99,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(Qh + (int64_t)q * DH + ks * 16 + half * 8);
 
-  u32x4_t rk[LK], rv[LV];
   f32x16_t o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
@@ -92,7 +107,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = a.scale_log2;
 
-  // S^T of tile t (64 keys x 32 queries, two 32 x 32 tiles) from K buffer t % 2
+  // S^T of tile t (64 keys x 32 queries, two 32 x 32 tiles)
   auto s_tile = [&](int t, f32x16_t (&sv)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -101,7 +116,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
       const int rho = u * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[t & 1][rho * KLD + (ks * 2 + half) * 8]);
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(kslot(t) + rho * KRB + (((ks * 2 + half) ^ kswz) << 4));
         sv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sv[u], 0, 0, 0);
       }
     }
@@ -141,14 +157,50 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
       m_run = m_new;
     }
   };
-  // O^T += V^T P^T over the 4 16-key steps of tile t (V buffer t % 2), the
-  // V^T fragment reads three MFMAs ahead
+  // Direct global -> LDS loads, 1 KB per instruction (lane l writes bytes
+  // 16 l .. 16 l + 15 of it).  Lane l of a K load fills LDS row r at physical
+  // chunk p, so it loads logical chunk p ^ swz(r) of the key stored in row r
+  // (rows hold keys in the permuted order, swap23 being its own inverse); a
+  // V^T load fills 8 rows of 128 bytes the same way.  A tile index past the
+  // last tile loads the last tile again (into a slot no one reads), so every
+  // iteration issues the same number of loads.  Offsets: per lane (fixed),
+  // plus the tile's (a scalar).
+  const int ntl = (a.seq + KT - 1) / KT;
+  __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Kh), 0, -1, 0x00020000);
+  __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Vt), 0, -1, 0x00020000);
+  int koff[NKD], voff[NVD];
+#pragma unroll
+  for (int u = 0; u < NKD; ++u) {
+    const int r = (wave * NKD + u) * (1024 / KRB) + lane / (KRB / 16);
+    const int c = (lane % (KRB / 16)) ^ (KRB == 256 ? (r & 15) : ((r >> 1) & 7));
+    koff[u] = ((r & 32) | swap23(r & 31)) * KRB + c * 16;
+  }
+#pragma unroll
+  for (int u = 0; u < NVD; ++u) {
+    const int d = (wave * NVD + u) * 8 + (lane >> 3);
+    voff[u] = d * a.seq_pad * 2 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+  }
+  auto dma_k = [&](int j, int u) {
+    const int jj = j < ntl ? j : ntl - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_k, (lds_void_t*)(kslot(j) + (wave * NKD + u) * 1024), 16,
+                                             (int)koff[u], (int)(jj * KT * KRB), 0, 0);
+  };
+  auto dma_v = [&](int j, int u) {
+    const int jj = j < ntl ? j : ntl - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, (lds_void_t*)(vslot(j) + (wave * NVD + u) * 1024), 16,
+                                             (int)voff[u], (int)(jj * KT * 2), 0, 0);
+  };
+
+  // O^T += V^T P^T over the 4 16-key steps of tile t, the V^T fragment reads
+  // three MFMAs ahead; the loads of V(t + 3) and K(t + 4) are spread over
+  // the MFMAs
   auto pv_tile = [&](int t) {
     constexpr int NP = DT * 4, AH = 3;
-    const bf16_t* vb = &Vs[t & 1][0];
+    const char* vb = vslot(t);
     // step m: output tile i = m % DT, key step kb = m / DT (chains alternate)
     auto vfrag = [&](int m) {
-      return *reinterpret_cast<const bf16x8_t*>(vb + ((m % DT) * 32 + l32) * VLD + ((m / DT) * 2 + half) * 8);
+      return *reinterpret_cast<const bf16x8_t*>(vb + ((m % DT) * 32 + l32) * 128 +
+                                                ((((m / DT) * 2 + half) ^ vswz) << 4));
     };
     bf16x8_t vq[NP];
 #pragma unroll
@@ -157,62 +209,37 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
     for (int m = 0; m < NP; ++m) {
       if (m + AH < NP) vq[m + AH] = vfrag(m + AH);
       o[m % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[m], pf[m / DT], o[m % DT], 0, 0, 0);
+      if ((m & 3) == 1) {
+        const int d = m >> 2;
+        if (d < NVD) dma_v(t + 3, d);
+        else if (d < NVD + NKD) dma_k(t + 4, d - NVD);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Software pipeline, one barrier per tile: iteration t computes S(t + 1)
   // while the softmax of S(t) runs (the MFMAs do not depend on it, so the
-  // SIMD executes both at once), then O += V(t) P(t).  LDS: K(t + 1) and
-  // V(t) are resident during iteration t; K(t + 2) goes to K(t)'s buffer and
-  // V(t + 1) to V(t - 1)'s, both read for the last time in iteration t - 1.
-  const int ntiles = (a.seq + KT - 1) / KT;
-  // prologue: K(0), V(0), K(1) in LDS; S(0); tiles K(2), V(1) in registers
-  auto gload_k = [&](int j) {
+  // SIMD executes both at once), then O += V(t) P(t).  Loads in issue order:
+  // K(0) V(0) K(1) V(1) K(2) V(2) K(3) before the loop, V(t + 3) K(t + 4) in
+  // iteration t, into the slots of V(t - 1) and K(t), last read in iteration
+  // t - 1.  At the end of iteration t, K(t + 2) and V(t + 1) must have landed:
+  // the four tiles issued after them may still be in flight (VMW loads).
+  const int ntiles = ntl;
 #pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
-      rk[i] = *reinterpret_cast<const u32x4_t*>(Kh + (int64_t)(j * KT + kr) * DH + c * 8);
-    }
-  };
-  auto gload_v = [&](int j) {
+  for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int g = tid + NT * i, d = g >> 3, c = g & 7;
-      rv[i] = *reinterpret_cast<const u32x4_t*>(Vt + (int64_t)d * a.seq_pad + j * KT + c * 8);
-    }
-  };
-  auto lstore_k = [&](int j) {
+    for (int u = 0; u < NKD; ++u) dma_k(j, u);
+    if (j < 3) {
 #pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      const int g = tid + NT * i, kr = g / DCH, c = g % DCH;
-      const int rho = (kr & 32) | swap23(kr & 31);
-      *reinterpret_cast<u32x4_t*>(&Ks[j & 1][rho * KLD + c * 8]) = rk[i];
+      for (int u = 0; u < NVD; ++u) dma_v(j, u);
     }
-  };
-  auto lstore_v = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int g = tid + NT * i, d = g >> 3, c = g & 7;
-      *reinterpret_cast<u32x4_t*>(&Vs[j & 1][d * VLD + c * 8]) = rv[i];
-    }
-  };
-  gload_k(0);
-  gload_v(0);
-  lstore_k(0);
-  lstore_v(0);
-  if (ntiles > 1) {
-    gload_k(1);
-    lstore_k(1);
   }
-  if (ntiles > 2) gload_k(2);
-  if (ntiles > 1) gload_v(1);
-  // the barriers publish LDS stores; K(2) and V(1) stay in flight in registers
+  DL_WAIT_VM(VMW);   // K(0), V(0), K(1)
   lds_barrier();
   f32x16_t sc_cur[2], sc_nxt[2];
   s_tile(0, sc_cur);
-  // iteration 0 overwrites K(0)'s buffer with K(2): every wave must have read
-  // K(0) first
+  // iteration 0 loads K(4) into K(0)'s slot: every wave must have read K(0)
   lds_barrier();
   for (int t = 0; t < ntiles; ++t) {
     softmax_max(t, sc_cur);
@@ -224,11 +251,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
     {
       constexpr int NM = 2 * KS, PP = 16 / NM;   // MFMA steps, probability pairs per step
       constexpr int AH = 3;                      // fragment reads run this many steps ahead
-      const bf16_t* kb = &Ks[(t + 1) & 1][0];
+      const char* kb = kslot(t + 1);
       // step m: score tile u = m % 2, k step ks = m / 2 (the two accumulation
       // chains alternate, so consecutive MFMAs are independent)
       auto kfrag = [&](int m) {
-        return *reinterpret_cast<const bf16x8_t*>(kb + ((m & 1) * 32 + l32) * KLD + ((m >> 1) * 2 + half) * 8);
+        return *reinterpret_cast<const bf16x8_t*>(kb + ((m & 1) * 32 + l32) * KRB +
+                                                  ((((m >> 1) * 2 + half) ^ kswz) << 4));
       };
       bf16x8_t kq[NM];
 #pragma unroll
@@ -263,17 +291,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
       l_run += psum;
     }
     pv_tile(t);
-    // next tiles: K(t + 2), V(t + 1) to LDS, K(t + 3), V(t + 2) loaded
-    if (t + 2 < ntiles) lstore_k(t + 2);
-    if (t + 1 < ntiles) lstore_v(t + 1);
-    if (t + 3 < ntiles) gload_k(t + 3);
-    if (t + 2 < ntiles) gload_v(t + 2);
 #pragma unroll
     for (int u = 0; u < 2; ++u) sc_cur[u] = sc_nxt[u];
-    // K(t + 3) and V(t + 2) are only stored to LDS in the next iteration:
-    // the barrier waits for the LDS stores, not for these loads
+    DL_WAIT_VM(VMW);   // K(t + 2), V(t + 1)
     lds_barrier();
   }
+  DL_WAIT_VM(0);       // no load into LDS outlives the loop
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   // training: P = exp2(s * sc - m_run) / l_tot = exp2(s * sc - lse)

@@ -109,6 +109,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// s_waitcnt vmcnt(n) leaving expcnt / lgkmcnt unconstrained (gfx9 encoding)
+#define DL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// LDS and global address-space pointers of the direct global -> LDS loads.
+// Their integer operands are passed as plain int expressions: an operand of a
+// template-dependent type keeps the host compiler from emitting the kernel's
+// launch stub.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
 // ---- wave reductions (fixed butterfly order -> deterministic) ---------------
 template <int WIDTH = kWave>
 __device__ __forceinline__ float wave_sum(float v) {

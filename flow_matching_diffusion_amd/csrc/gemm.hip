@@ -416,9 +416,6 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmBatch bt) {
 // ---------------------------------------------------------------------------
 // 256 x 256 tile, 4-stage LDS ring fed by direct global->LDS loads
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
 constexpr int kDlBK = 32;                 // k per stage
 constexpr int kDlStages = 5;
 constexpr int kDlRows = 256;              // BM = BN
@@ -435,9 +432,6 @@ constexpr int kDlStageBytes = 2 * kDlRows * kDlBK * 2;   // A + B, 32 KB
 // row l / 4, a whole 64-byte row per 4 lanes) is conflict-free for any
 // in-row permutation.
 __device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
-
-// s_waitcnt vmcnt(n) leaving expcnt / lgkmcnt unconstrained (gfx9 encoding)
-#define DL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 // Epilogue of one 256 x 256 tile of the persistent kernels.  Each wave owns a
 // 128 x 128 block of 4 x 4 accumulator tiles; its 8 quarters (32 rows x 64
