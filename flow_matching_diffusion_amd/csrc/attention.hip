@@ -142,7 +142,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[u][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      // with lane l ^ 32, through the VALU: the swap leaves lane l holding its
+      // own max and its partner's in the two results (no LDS round trip)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     // lazy max: move the reference point only when the tile max exceeds it
     // by more than kLazy (always on the first tile, where m_run = -inf)
     const float m_tile = mx * sc;
@@ -191,23 +196,26 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
                                              (int)voff[u], (int)(jj * KT * 2), 0, 0);
   };
 
-  // O^T += V^T P^T over the 4 16-key steps of tile t, the V^T fragment reads
-  // three MFMAs ahead; the loads of V(t + 3) and K(t + 4) are spread over
-  // the MFMAs
+  // Fragment reads run AH MFMAs ahead of their use.  V^T fragment m of tile
+  // t: output tile i = m % DT, key step m / DT (the chains alternate); K
+  // fragment m: score tile m % 2, k step m / 2.
+  constexpr int NP = DT * 4, NM = 2 * KS, AH = 3;
+  bf16x8_t vq[NP], kq[NM];
+  auto vfrag = [&](int t, int m) {
+    return *reinterpret_cast<const bf16x8_t*>(vslot(t) + ((m % DT) * 32 + l32) * 128 +
+                                              ((((m / DT) * 2 + half) ^ vswz) << 4));
+  };
+  auto kfrag = [&](int t, int m) {
+    return *reinterpret_cast<const bf16x8_t*>(kslot(t) + ((m & 1) * 32 + l32) * KRB +
+                                              ((((m >> 1) * 2 + half) ^ kswz) << 4));
+  };
+  // O^T += V^T P^T over the 4 16-key steps of tile t (its first AH fragments
+  // already read); the loads of V(t + 3) and K(t + 4) are spread over the
+  // MFMAs
   auto pv_tile = [&](int t) {
-    constexpr int NP = DT * 4, AH = 3;
-    const char* vb = vslot(t);
-    // step m: output tile i = m % DT, key step kb = m / DT (chains alternate)
-    auto vfrag = [&](int m) {
-      return *reinterpret_cast<const bf16x8_t*>(vb + ((m % DT) * 32 + l32) * 128 +
-                                                ((((m / DT) * 2 + half) ^ vswz) << 4));
-    };
-    bf16x8_t vq[NP];
-#pragma unroll
-    for (int m = 0; m < AH; ++m) vq[m] = vfrag(m);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-      if (m + AH < NP) vq[m + AH] = vfrag(m + AH);
+      if (m + AH < NP) vq[m + AH] = vfrag(t, m + AH);
       o[m % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[m], pf[m / DT], o[m % DT], 0, 0, 0);
       if ((m & 3) == 1) {
         const int d = m >> 2;
@@ -242,25 +250,20 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   // iteration 0 loads K(4) into K(0)'s slot: every wave must have read K(0)
   lds_barrier();
   for (int t = 0; t < ntiles; ++t) {
+    // the first K fragments of S(t + 1) (K(t + 1) landed before the last
+    // barrier): their latency hides under the row max
+#pragma unroll
+    for (int m = 0; m < AH; ++m) kq[m] = kfrag(t + 1, m);
     softmax_max(t, sc_cur);
     // S(t + 1) with the exponentials of tile t in its MFMA shadow: step m
-    // (of 2 KS) issues one MFMA, the K fragment read of step m + 3 and
-    // 16 / (2 KS) probability pairs of tile t, fenced so
-    // the compiler keeps the interleave.  On the last tile the product is of
-    // a resident buffer and is discarded (no branch in the interleaved code).
+    // (of 2 KS) issues one MFMA, the K fragment read of step m + 3 (in the
+    // last steps, the first V^T fragments of P V(t)) and 16 / (2 KS)
+    // probability pairs of tile t, fenced so the compiler keeps the
+    // interleave.  On the last tile the product is of a resident buffer and
+    // is discarded (no branch in the interleaved code).  The two
+    // accumulation chains alternate, so consecutive MFMAs are independent.
     {
-      constexpr int NM = 2 * KS, PP = 16 / NM;   // MFMA steps, probability pairs per step
-      constexpr int AH = 3;                      // fragment reads run this many steps ahead
-      const char* kb = kslot(t + 1);
-      // step m: score tile u = m % 2, k step ks = m / 2 (the two accumulation
-      // chains alternate, so consecutive MFMAs are independent)
-      auto kfrag = [&](int m) {
-        return *reinterpret_cast<const bf16x8_t*>(kb + ((m & 1) * 32 + l32) * KRB +
-                                                  ((((m >> 1) * 2 + half) ^ kswz) << 4));
-      };
-      bf16x8_t kq[NM];
-#pragma unroll
-      for (int m = 0; m < AH; ++m) kq[m] = kfrag(m);
+      constexpr int PP = 16 / NM;   // probability pairs per step
       float psum = 0.f;
       uint32_t w[4];
 #pragma unroll
@@ -270,7 +273,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const int u = m & 1, ks = m >> 1;
-        if (m + AH < NM) kq[m + AH] = kfrag(m + AH);
+        if (m + AH < NM) kq[m + AH] = kfrag(t + 1, m + AH);
+        else vq[m + AH - NM] = vfrag(t, m + AH - NM);
         sc_nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[m], qf[ks], sc_nxt[u], 0, 0, 0);
 #pragma unroll
         for (int pp = 0; pp < PP; ++pp) {
