@@ -947,6 +947,8 @@ flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, in
   REQUIRE(batch >= 1 && seq >= 1 && heads >= 1, "batch, seq and heads must be >= 1");
   if (head_dim != 64 && head_dim != 128)
     return fail(FLUX_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  if (seq_pad_of(seq) * head_dim * 2 >= (int64_t)1 << 31)
+    return fail(FLUX_ERR_UNSUPPORTED, "seq %d too long (one head's keys must stay under 2 GiB)", seq);
   REQUIRE(q && k && v && o, "q, k, v and o are required");
   REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o), "pointers must be 16-byte aligned");
   const int64_t D = (int64_t)heads * head_dim;

@@ -95,6 +95,9 @@ inline flux_status check_dims(const flux_dims* d) {
   REQUIRE(d->weights_f16 == 0 || (d->weights_f16 == 1 && d->precision == FLUX_PREC_BF16),
           "weights_f16 must be 0, or 1 with FLUX_PREC_BF16");
   const int64_t L = (int64_t)d->l_img + d->l_txt;
+  if ((L + 255) / 256 * 256 * d->head_dim * 2 >= (int64_t)1 << 31)
+    return fail(FLUX_ERR_UNSUPPORTED, "l_img + l_txt = %lld too long (one head's keys must stay under 2 GiB)",
+                (long long)L);
   REQUIRE(L * d->batch < (int64_t)1 << 31 && (int64_t)d->batch * L * (3 * d->hidden + d->mlp_hidden) < (int64_t)1 << 40,
           "problem too large");
   return FLUX_OK;

@@ -592,6 +592,8 @@ hipError_t launch_attention(const AttnArgs& a, int dtype, int out_dtype, hipStre
     return hipGetLastError();
   }
   if (dtype == kBF16) {
+    // K and V^T of one (batch, head) are addressed by 32-bit byte offsets
+    if ((int64_t)a.seq_pad * a.head_dim * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     // one block per 256 queries of a (batch, head), rounded up to whole XCD
     // groups (blocks past the work exit at once)
     const int items = a.batch * a.heads * (a.seq_pad / 256);

@@ -785,6 +785,8 @@ flux_status flux_attention_fwd_train(int32_t batch, int32_t seq, int32_t heads, 
                                      size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   REQUIRE(batch >= 1 && seq >= 1 && heads >= 1, "batch, seq and heads must be >= 1");
+  if (seq_pad_of(seq) * 128 * 2 >= (int64_t)1 << 31)
+    return fail(FLUX_ERR_UNSUPPORTED, "seq %d too long (one head's keys must stay under 2 GiB)", seq);
   REQUIRE(q && k && v && o && lse && aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(lse),
           "q, k, v, o and lse must be non-NULL and 16-byte aligned");
   REQUIRE(ld >= heads * 128 && ld % 8 == 0 && ldo >= heads * 128 && ldo % 8 == 0, "ld, ldo >= heads*128, multiples of 8");

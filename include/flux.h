@@ -414,6 +414,9 @@ flux_status flux_linear_fwd(int32_t precision, int32_t m, int32_t n, int32_t k, 
  *  q, k, v [B, L, heads*head_dim] of element type `precision`, row stride ld_in;
  *  o [B, L, heads*head_dim] same type, row stride ld_out.
  *  workspace >= flux_attention_workspace_bytes(...) bytes.
+ *  FLUX_ERR_UNSUPPORTED when round_up(seq, 256) * head_dim * 2 bytes (one
+ *  head's keys) reach 2 GiB; the block calls apply the same limit to
+ *  l_img + l_txt.
  */
 flux_status flux_attention_fwd(int32_t precision, int32_t batch, int32_t seq, int32_t heads, int32_t head_dim,
                                const void* q, const void* k, const void* v, int64_t ld_in, void* o,

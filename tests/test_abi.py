@@ -53,6 +53,7 @@ def _dims(**kw):
     (dict(l_img=0), F.FLUX_ERR_INVALID_ARGUMENT),
     (dict(mlp_hidden=100), F.FLUX_ERR_UNSUPPORTED),
     (dict(precision=7), F.FLUX_ERR_INVALID_ARGUMENT),
+    (dict(l_img=(1 << 23) - 16, heads=2, head_dim=128, axes_dim=(16, 56, 56)), F.FLUX_ERR_UNSUPPORTED),
 ])
 def test_bad_dims_rejected(kw, status):
     L = F.lib()
@@ -156,6 +157,11 @@ def test_linear_and_attention_argument_checks():
         F.FLUX_ERR_UNSUPPORTED                                                  # N % 4
     assert L.flux_attention_fwd(F.FLUX_PREC_BF16, 1, 80, 4, 96, fake, fake, fake, 384, fake, 384, fake, 1 << 30,
                                 None) == F.FLUX_ERR_UNSUPPORTED                # head_dim 96
+    # one head's keys reach 2 GiB: the attention loads use 32-bit byte offsets
+    assert L.flux_attention_fwd(F.FLUX_PREC_BF16, 1, 1 << 23, 1, 128, fake, fake, fake, 128, fake, 128, fake,
+                                1 << 40, None) == F.FLUX_ERR_UNSUPPORTED
+    assert L.flux_attention_fwd_train(1, 1 << 23, 1, fake, fake, fake, 128, fake, 128, fake, fake, 1 << 40,
+                                      None) == F.FLUX_ERR_UNSUPPORTED
     need = F.flux_attention_workspace_bytes(F.FLUX_PREC_BF16, 1, 80, 4, 64)
     assert L.flux_attention_fwd(F.FLUX_PREC_BF16, 1, 80, 4, 64, fake, fake, fake, 256, fake, 256, fake, need - 1,
                                 None) == F.FLUX_ERR_WORKSPACE_TOO_SMALL
