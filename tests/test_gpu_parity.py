@@ -167,7 +167,9 @@ def test_linear(prec, m, n, k):
 # attention
 # --------------------------------------------------------------------------- #
 @pytest.mark.parametrize("prec,B,L,H,dh", [("bf16", 1, 80, 4, 64), ("bf16", 2, 200, 2, 128), ("bf16", 1, 1536, 24, 128),
-                                           ("bf16", 1, 4608, 24, 128), ("f32", 1, 80, 4, 64), ("f32", 2, 130, 2, 128)])
+                                           ("bf16", 1, 4608, 24, 128), ("bf16", 1, 40, 2, 64), ("bf16", 2, 40, 2, 128),
+                                           ("bf16", 1, 257, 3, 128),
+                                           ("f32", 1, 80, 4, 64), ("f32", 2, 130, 2, 128)])
 def test_attention(prec, B, L, H, dh):
     _say(f"attention {prec} B={B} L={L} H={H} dh={dh}")
     rng = np.random.default_rng(L + H)
