@@ -34,8 +34,9 @@
 // 328 -> 300 us at B=1, L=4608, 24 heads on MI355X, bit-identical results.
 // All slots are one LDS array: with one array per tile kind the compiler
 // adds a wait for every load in flight before each fragment read.
-// Inputs come from launch_prep: Q, K head-major [B, H, Lp, Dh] and V
-// transposed [B, H, Dh, Lp], Lp = seq rounded up to 256, zero padded.  The
+// Inputs, as the q|k|v GEMM epilogue or launch_prep write them: Q, K
+// head-major [B, H, Lp, Dh] and V transposed [B, H, Dh, Lp], Lp = seq
+// rounded up to 256, zero padded.  The
 // output is written as bf16, fp16 or E4M3 (the operand type of the next
 // linear; E4M3 with the delayed scale of the row's stream).
 #include <math.h>
@@ -54,8 +55,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_kernel(AttnArgs a) {
   constexpr int QW = 32;          // queries per wave
   constexpr int NW = 8;           // waves per block
   constexpr int QB = NW * QW;     // queries per block
-  constexpr int NT = NW * 64;     // threads
-  constexpr int DCH = DH / 8;     // 16-byte chunks per K row
   constexpr int KS = DH / 16;     // MFMA k-steps of S^T
   constexpr int DT = DH / 32;     // 32-row tiles of O^T
   constexpr float kLazy = 8.0f;   // rescale when a tile max exceeds the running max by this (log2)
@@ -408,7 +407,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
 typedef int i32x8a_t __attribute__((ext_vector_type(8)));
 
 __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
-  constexpr int DH = 128, KT = 64, QW = 32, NW = 8, QB = NW * QW, NT = NW * 64, DT = DH / 32;
+  constexpr int DH = 128, KT = 64, QW = 32, NW = 8, QB = NW * QW, DT = DH / 32;
   constexpr int KLD = DH + 16;    // K tile row stride (bytes): 16 lanes of a read hit distinct bank groups
   constexpr int VLD = KT + 16;    // V^T tile row stride (bytes)
   constexpr float kLazy = 8.0f;

@@ -672,7 +672,6 @@ flux_status flux_block_bwd(const flux_dims* d, const flux_stream_weights* iw, co
   auto linear_bwd = [&](const void* dyv, int64_t N, const void* x, int64_t K, const void* const* W, int wsel,
                         void* dxv, bool dx_f32) -> flux_status {
     for (int i = 0; i < ns; ++i) {
-      float* gw = wsel == 0 ? gs[i]->qkv_w : wsel == 1 ? gs[i]->proj_w : wsel == 2 ? gs[i]->fc1_w : gs[i]->fc2_w;
       float* gb = wsel == 0 ? gs[i]->qkv_b : wsel == 1 ? gs[i]->proj_b : wsel == 2 ? gs[i]->fc1_b : gs[i]->fc2_b;
       const void* dyi = elem_ptr(dyv, off[i] * N, 2);
       FLUX_HIP(colsum(dyi, kBF16, jrow(i, N), nullptr, none, B * seg[i], N, 1, gb, 0, w.pt.col, st), "bias gradient");
