@@ -970,8 +970,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
   // MFMAs, the fragments of slice n + 1 read during slice n.  ISSUE: the A
   // half of j + 2 loads during slices 0-1, at every other MFMA (into the slot
   // of W of j - 1, free since the previous barrier), and its W half during
-  // slice 3, one load per MFMA (into the slot of A of j, free after this
-  // super-stage's barrier); denser load issue stalls the wave's MFMAs.  NEXT: the barrier
+  // slice 3, also at every other MFMA (into the slot of A of j, free after
+  // this super-stage's barrier); denser load issue stalls the wave's MFMAs
+  // (the W half one per MFMA over the last 8 of slice 3: 0.4-1.2 % slower).  NEXT: the barrier
   // between slices 2 and 3 waits until j + 1 has landed for every wave (VM:
   // loads left in flight, those of A of j + 2), and slice 3 reads the first
   // fragments of j + 1.  Flags are compile-time, so the k loop has no branches.
@@ -1007,7 +1008,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dl_kernel(GemmBatch bt) {
     for (int idx = 0; idx < 16; ++idx) {
       mfma_one(1, idx);
       if (NEXT && idx < 8) frag_one(j + 1, 0, 0, idx);
-      else if (ISSUE && idx >= 8) dma_one(2 * j + 5, ss0 + j + 2, true, idx - 8);
+      if (ISSUE && (idx & 1) == 1) dma_one(2 * j + 5, ss0 + j + 2, true, idx >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
