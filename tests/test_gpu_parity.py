@@ -141,8 +141,12 @@ def test_timestep_embed(batch, dim):
 # --------------------------------------------------------------------------- #
 # linear (GEMM)
 # --------------------------------------------------------------------------- #
+# the 4608 x 9216 and the two 4096-wide cases run on the persistent ring
+# kernel (>= 128 tiles of 256 x 256): K = 3072, and its smallest K (512, four
+# k units) and an odd number of k units (640) with a partly filled last tile row
 @pytest.mark.parametrize("prec,m,n,k", [("bf16", 80, 768, 256), ("bf16", 333, 1284, 512), ("bf16", 1536, 3072, 3072),
-                                        ("bf16", 4608, 9216, 3072), ("f32", 80, 768, 256), ("f32", 77, 36, 40)])
+                                        ("bf16", 4608, 9216, 3072), ("bf16", 2100, 4096, 640),
+                                        ("bf16", 2304, 4096, 512), ("f32", 80, 768, 256), ("f32", 77, 36, 40)])
 def test_linear(prec, m, n, k):
     _say(f"linear {prec} m={m} n={n} k={k}")
     rng = np.random.default_rng(m * 7 + n)
@@ -154,8 +158,16 @@ def test_linear(prec, m, n, k):
         x, w, b = synth.round_to_bf16(x), synth.round_to_bf16(w), synth.round_to_bf16(b)
     y = torch.empty((m, n), device="cuda")
     p = F().FLUX_PREC_BF16 if bf else F().FLUX_PREC_F32
-    F().flux_linear_fwd(p, m, n, k, dev(x, bf), k, dev(w, bf), dev(b, bf), y, n)
+    xd, wd, bd = dev(x, bf), dev(w, bf), dev(b, bf)
     torch.cuda.synchronize()
+    F().flux_timing_read()   # clears the counts of earlier launches
+    F().flux_timing_enable(True)
+    F().flux_linear_fwd(p, m, n, k, xd, k, wd, bd, y, n)
+    torch.cuda.synchronize()
+    launches = {c: v[1] for c, v in F().flux_timing_read().items() if v[1]}
+    F().flux_timing_enable(False)
+    if bf and m * n >= 128 * 256 * 256 and k >= 512:
+        assert "gemm_256_bf16" in launches, launches   # the persistent ring kernel ran
     rows = np.arange(m) if m <= 512 else np.unique(np.r_[rng.choice(m, 96, replace=False), 0, m - 1])
     ref = O.linear(x[rows], w, b)
     g = y.cpu().numpy()[rows]
